@@ -1,0 +1,81 @@
+"""Routed MoE layer with intra-expert activation sparsity, in fp64.
+
+Test infrastructure only (see the package docstring).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .teal import silu, dense_mlp
+from .topk import value_topk
+
+
+def router(x, Wr, top: int):
+    """Router of one token: logits = x Wr; the ``top`` experts with the largest
+    logits (ties to the smaller expert index); weights = softmax over the
+    selected logits.
+
+    Intra-expert summary, method section: routed experts are chosen by the
+    router, shared experts are always active; the router logic is kept as is.
+    Reading taken (the pages do not print the router): softmax renormalised over
+    the selected experts.  Returns (ids in descending-logit order, weights).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    logits = x @ np.asarray(Wr, dtype=np.float64)
+    sel = value_topk(logits, top)
+    order = sel[np.lexsort((sel, -logits[sel]))]          # descending logit, ties by index
+    z = logits[order]
+    e = np.exp(z - z.max())
+    return order, e / e.sum(), logits
+
+
+def expert_sparse(x, Wgu_e, Wd_e, keep: int):
+    """One routed expert on one token with intra-expert sparsity.
+
+    Intra-expert summary, system implementation: the gate projection is run
+    densely to score the neurons, the low-scoring neurons are skipped and only
+    the active neurons' weights are gathered for the up/down work.  Reading
+    taken (workload definition): gate and up are both dense, the score is
+    |silu(g) * u|, and the ``keep`` largest (ties to the smaller index) reach
+    the down projection.
+
+    Wgu_e: ``[d_ff_e, 2, d_model]`` neuron-major; Wd_e: ``[d_ff_e, d_model]``.
+    Returns (y_e, h, keep_idx).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(Wgu_e, dtype=np.float64)
+    g = W[:, 0, :] @ x
+    u = W[:, 1, :] @ x
+    h = silu(g) * u
+    kidx = value_topk(np.abs(h), keep)
+    y = h[kidx] @ np.asarray(Wd_e, dtype=np.float64)[kidx]
+    return y, h, kidx
+
+
+def moe_layer(x, w: dict, top: int, keep: int):
+    """``y_t = sum_j w_tj * expert_{e_tj}(x_t) + shared(x_t)`` for every token t.
+
+    Intra-expert summary, method section: routed experts are sparsified inside,
+    shared experts stay dense and are added unweighted.  ``w`` holds numpy fp64
+    arrays: w_router [d, E], w_gate_up [E, d_ff_e, 2, d], w_down [E, d_ff_e, d],
+    s_gate_up [d, 2, d_ff_s] (input-major), s_down [d_ff_s, d].
+    """
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    T = x.shape[0]
+    d = x.shape[1]
+    out = np.zeros((T, d))
+    info = []
+    for t in range(T):
+        ids, wts, logits = router(x[t], w["w_router"], top)
+        y = np.zeros(d)
+        hs, ks = [], []
+        for e, we in zip(ids, wts):
+            ye, h, kidx = expert_sparse(x[t], w["w_gate_up"][e], w["w_down"][e], keep)
+            y += we * ye
+            hs.append(h)
+            ks.append(kidx)
+        sgu = np.asarray(w["s_gate_up"], dtype=np.float64)
+        y += dense_mlp(x[t], sgu[:, 0, :], sgu[:, 1, :], w["s_down"])
+        out[t] = y
+        info.append(dict(ids=ids, weights=wts, logits=logits, h=hs, keep=ks))
+    return out, info
