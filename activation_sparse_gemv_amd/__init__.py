@@ -1,0 +1,11 @@
+"""libactsparse: activation-sparse GEMV for LLM decode on MI355X (gfx950).
+
+The compute lives in the HIP library ``libactsparse.so`` (C ABI declared in
+``include/actsparse.h``); ``api`` is a thin tensor-level binding with the same
+entry-point names, and ``datagen`` draws the seeded synthetic inputs.
+"""
+from . import _lib  # noqa: F401
+from .api import (  # noqa: F401
+    MLPWeights, as_bench_flush, as_calibrate_threshold, as_dense_gemv, as_sparse_swiglu_mlp,
+    as_threshold_gemv, as_version, nearest_rank, unpack_bits, workspace,
+)

@@ -1,0 +1,131 @@
+"""ctypes declarations of libactsparse's C ABI (include/actsparse.h).
+
+Loading fails loudly: there is no fallback implementation of any entry point.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int, c_int64, c_size_t, c_uint, c_void_p, c_char_p
+
+LIB_PATH = os.environ.get("ACTSPARSE_LIB",
+                          os.path.join(os.path.dirname(os.path.abspath(__file__)), "libactsparse.so"))
+
+AS_OK, AS_ERR_INVALID_ARG, AS_ERR_UNSUPPORTED, AS_ERR_WORKSPACE, AS_ERR_HIP = range(5)
+AS_F16, AS_BF16, AS_F32 = 0, 1, 2
+AS_FLAG_ACCUMULATE = 1 << 0
+AS_FLAG_NO_NT_LOADS = 1 << 2
+AS_FLAG_FORCE_DENSE = 1 << 3
+AS_MLP_THRESHOLD, AS_MLP_NEURON_SET = 0, 1
+AS_TOPK_VALUE, AS_TOPK_RANK_BLEND = 0, 1
+
+
+class ASMaskOut(ctypes.Structure):
+    _fields_ = [("bits", c_void_p), ("idx", c_void_p), ("nnz", c_void_p)]
+
+
+class ASMlpWeights(ctypes.Structure):
+    _fields_ = [("w_gate_up", c_void_p), ("w_down", c_void_p), ("w_dt", c_int),
+                ("d_model", c_int), ("d_ff", c_int)]
+
+
+class ASMlpDebug(ctypes.Structure):
+    _fields_ = [("h", c_void_p), ("x_mask", ASMaskOut), ("h_mask", ASMaskOut), ("ev", c_void_p * 3)]
+
+
+# name -> (restype, argtypes); every symbol declared in include/actsparse.h
+SIGNATURES = {
+    "as_version": (c_int, []),
+    "as_status_string": (c_char_p, [c_int]),
+    "as_last_error": (c_char_p, []),
+    "as_workspace_init": (c_int, [c_void_p, c_size_t, c_void_p]),
+    "as_calibrate_threshold": (c_int, [c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p]),
+    "as_threshold_gemv_ws_size": (c_size_t, [c_int, c_int, c_int]),
+    "as_threshold_gemv": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_float,
+                                  c_void_p, c_int, c_uint, POINTER(ASMaskOut), c_void_p, c_size_t, c_void_p]),
+    "as_dense_gemv": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int,
+                              c_void_p, c_int, c_uint, c_void_p, c_size_t, c_void_p]),
+    "as_sparse_swiglu_mlp_ws_size": (c_size_t, [c_int, POINTER(ASMlpWeights), c_int]),
+    "as_sparse_swiglu_mlp": (c_int, [c_void_p, c_int, c_int, POINTER(ASMlpWeights), c_int, c_float, c_float,
+                                     c_void_p, c_int, c_void_p, c_int, c_uint, POINTER(ASMlpDebug),
+                                     c_void_p, c_size_t, c_void_p]),
+    "as_bench_flush": (c_int, [c_void_p, c_size_t, c_void_p]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libactsparse.so (built in-tree by ``python -m activation_sparse_gemv_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libactsparse.so not found at {LIB_PATH}; build it with "
+                          f"`python -m activation_sparse_gemv_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class ASError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        lib = load()
+        self.status = status
+        msg = lib.as_last_error().decode(errors="replace")
+        super().__init__(f"{fn} -> {lib.as_status_string(status).decode()}: {msg}")
+
+
+def check(status: int, fn: str):
+    if status != AS_OK:
+        raise ASError(status, fn)
+
+
+# ---------------------------------------------------------------- HIP events
+_hip = None
+
+
+def hip():
+    """libamdhip64 for raw HIP events (recorded on the stream the kernels run on)."""
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [POINTER(c_void_p)]
+        h.hipEventRecord.argtypes = [c_void_p, c_void_p]
+        h.hipEventSynchronize.argtypes = [c_void_p]
+        h.hipEventElapsedTime.argtypes = [POINTER(c_float), c_void_p, c_void_p]
+        h.hipEventDestroy.argtypes = [c_void_p]
+        _hip = h
+    return _hip
+
+
+class HipEvent:
+    def __init__(self):
+        self.ev = c_void_p()
+        r = hip().hipEventCreate(ctypes.byref(self.ev))
+        if r != 0:
+            raise RuntimeError(f"hipEventCreate failed ({r})")
+
+    def record(self, stream: int):
+        r = hip().hipEventRecord(self.ev, c_void_p(stream))
+        if r != 0:
+            raise RuntimeError(f"hipEventRecord failed ({r})")
+
+    def elapsed_ms(self, later: "HipEvent") -> float:
+        hip().hipEventSynchronize(later.ev)
+        ms = c_float()
+        r = hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, later.ev)
+        if r != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({r})")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self.ev:
+                hip().hipEventDestroy(self.ev)
+        except Exception:
+            pass

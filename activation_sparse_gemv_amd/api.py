@@ -1,0 +1,247 @@
+"""Tensor-level binding of libactsparse: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks tensor placement, allocates outputs and the
+workspace with torch (device memory is torch's), and passes raw pointers and
+torch's current HIP stream to the library.  Workspaces are cached per
+(entry point, shape) and device, zero-filled once; the library leaves their
+counters at zero after every call, so reuse on one stream is safe.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from fractions import Fraction
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float16: L.AS_F16, torch.bfloat16: L.AS_BF16, torch.float32: L.AS_F32}
+_WS: dict = {}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libactsparse operates on device tensors only (no CPU path exists)")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def workspace(key, nbytes: int, device: torch.device) -> torch.Tensor:
+    k = (key, nbytes, str(device))
+    ws = _WS.get(k)
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _WS[k] = ws
+    return ws
+
+
+def as_version() -> int:
+    return L.load().as_version()
+
+
+def nearest_rank(p: float, n: int) -> int:
+    """1-based rank ceil(p * n) of the decimal p (argument of as_calibrate_threshold)."""
+    if p <= 0:
+        return 0
+    return min(n, max(1, math.ceil(Fraction(repr(float(p))) * n)))
+
+
+def as_calibrate_threshold(pool: torch.Tensor, p: float | None = None, rank: int | None = None) -> torch.Tensor:
+    """Threshold for target sparsity p (or an explicit 1-based rank) from a
+    calibration pool; returns a 1-element fp32 device tensor."""
+    _need_cuda(pool)
+    n = pool.numel()
+    if rank is None:
+        rank = nearest_rank(p, n)
+    out = torch.empty(1, dtype=torch.float32, device=pool.device)
+    L.check(L.load().as_calibrate_threshold(_ptr(pool), _dt(pool), n, rank, _ptr(out), _stream(pool.device)),
+            "as_calibrate_threshold")
+    return out
+
+
+def _mask_bufs(M: int, n: int, device, want_idx: bool):
+    nw = (n + 63) // 64
+    bits = torch.zeros((M, nw), dtype=torch.int64, device=device)
+    nnz = torch.zeros(M, dtype=torch.int32, device=device)
+    idx = torch.full((M, n), -1, dtype=torch.int32, device=device) if want_idx else None
+    return dict(bits=bits, nnz=nnz, idx=idx)
+
+
+def _mask_struct(d) -> L.ASMaskOut:
+    if d is None:
+        return L.ASMaskOut(None, None, None)
+    return L.ASMaskOut(_ptr(d.get("bits")), _ptr(d.get("idx")), _ptr(d.get("nnz")))
+
+
+def as_threshold_gemv(X: torch.Tensor, W: torch.Tensor, t: float, y_dtype=torch.float32,
+                      flags: int = 0, mask_out: bool = False, Y: torch.Tensor | None = None):
+    """Y[m] = sum_{i: |X[m,i]| > t} X[m,i] W[i,:].  X [M,K] or [K]; W [K,N]."""
+    squeeze = X.dim() == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    _need_cuda(X2, W, Y)
+    M, K = X2.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError(f"X has K={K} but W has {K2} rows")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype, device=X.device)
+    lib = L.load()
+    nb = lib.as_threshold_gemv_ws_size(M, K, N)
+    ws = workspace(("gemv", M, K, N), nb, X.device)
+    md = _mask_bufs(M, K, X.device, M == 1) if mask_out else None
+    ms = _mask_struct(md)
+    L.check(lib.as_threshold_gemv(_ptr(X2), _dt(X2), M, K, _ptr(W), _dt(W), N, float(t), _ptr(Y), _dt(Y),
+                                  flags, ctypes.byref(ms) if md else None, _ptr(ws), ws.numel(),
+                                  _stream(X.device)), "as_threshold_gemv")
+    out = Y[0] if squeeze else Y
+    return (out, md) if mask_out else out
+
+
+def as_dense_gemv(X: torch.Tensor, W: torch.Tensor, y_dtype=torch.float32, flags: int = 0,
+                  Y: torch.Tensor | None = None):
+    squeeze = X.dim() == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    _need_cuda(X2, W, Y)
+    M, K = X2.shape
+    N = W.shape[1]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype, device=X.device)
+    lib = L.load()
+    nb = lib.as_threshold_gemv_ws_size(M, K, N)
+    ws = workspace(("gemv", M, K, N), nb, X.device)
+    L.check(lib.as_dense_gemv(_ptr(X2), _dt(X2), M, K, _ptr(W), _dt(W), N, _ptr(Y), _dt(Y), flags,
+                              _ptr(ws), ws.numel(), _stream(X.device)), "as_dense_gemv")
+    return Y[0] if squeeze else Y
+
+
+@dataclass
+class MLPWeights:
+    """THRESHOLD: w_gate_up [d_model, 2, d_ff], w_down [d_ff, d_model].
+    NEURON_SET: w_gate_up [d_ff, 3, d_model] (gate, up, down rows per neuron), w_down None."""
+    w_gate_up: torch.Tensor
+    w_down: Optional[torch.Tensor]
+    mode: int = L.AS_MLP_THRESHOLD
+
+    @property
+    def d_model(self):
+        return self.w_gate_up.shape[0] if self.mode == L.AS_MLP_THRESHOLD else self.w_gate_up.shape[2]
+
+    @property
+    def d_ff(self):
+        return self.w_gate_up.shape[2] if self.mode == L.AS_MLP_THRESHOLD else self.w_gate_up.shape[0]
+
+    def struct(self) -> L.ASMlpWeights:
+        return L.ASMlpWeights(_ptr(self.w_gate_up), _ptr(self.w_down), _dt(self.w_gate_up),
+                              self.d_model, self.d_ff)
+
+
+def as_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float = float("-inf"), t_h: float = float("-inf"),
+                         neuron_idx: torch.Tensor | None = None, y_dtype=torch.float32, flags: int = 0,
+                         debug: bool = False, events=None, Y: torch.Tensor | None = None):
+    """Sparse SwiGLU MLP (THRESHOLD or NEURON_SET per ``w.mode``).  With ``debug``
+    returns (Y, dict(h=..., x_mask=..., h_mask=...))."""
+    squeeze = X.dim() == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    _need_cuda(X2, w.w_gate_up, w.w_down, neuron_idx, Y)
+    M = X2.shape[0]
+    d, f = w.d_model, w.d_ff
+    if X2.shape[1] != d:
+        raise ValueError(f"X has {X2.shape[1]} features, weights have d_model={d}")
+    if Y is None:
+        Y = torch.empty((M, d), dtype=y_dtype, device=X.device)
+    lib = L.load()
+    ws_ = w.struct()
+    nb = lib.as_sparse_swiglu_mlp_ws_size(M, ctypes.byref(ws_), w.mode)
+    ws = workspace(("mlp", w.mode, M, d, f), nb, X.device)
+    n_active = 0 if neuron_idx is None else neuron_idx.numel()
+    dbg = None
+    dd = None
+    if debug or events is not None:
+        dbg = L.ASMlpDebug()
+        if debug:
+            dense = bool(flags & L.AS_FLAG_FORCE_DENSE)
+            nh = f if (w.mode == L.AS_MLP_THRESHOLD) else (f if dense else n_active)
+            dd = dict(h=torch.zeros((M, max(nh, 1)), dtype=torch.float32, device=X.device))
+            dbg.h = _ptr(dd["h"])
+            if w.mode == L.AS_MLP_THRESHOLD:
+                dd["x_mask"] = _mask_bufs(M, d, X.device, M == 1)
+                dd["h_mask"] = dict(bits=torch.zeros((M, (f + 63) // 64), dtype=torch.int64, device=X.device))
+                dbg.x_mask = _mask_struct(dd["x_mask"])
+                dbg.h_mask = _mask_struct(dd["h_mask"])
+        if events is not None:
+            for i, e in enumerate(events):
+                dbg.ev[i] = e.ev if e is not None else None
+    L.check(lib.as_sparse_swiglu_mlp(_ptr(X2), _dt(X2), M, ctypes.byref(ws_), w.mode, float(t_x), float(t_h),
+                                     _ptr(neuron_idx), n_active, _ptr(Y), _dt(Y), flags,
+                                     ctypes.byref(dbg) if dbg is not None else None,
+                                     _ptr(ws), ws.numel(), _stream(X.device)), "as_sparse_swiglu_mlp")
+    out = Y[0] if squeeze else Y
+    return (out, dd) if debug else out
+
+
+def as_bench_flush(buf: torch.Tensor):
+    _need_cuda(buf)
+    L.check(L.load().as_bench_flush(_ptr(buf), buf.numel() * buf.element_size(), _stream(buf.device)),
+            "as_bench_flush")
+
+
+def unpack_bits(bits: torch.Tensor, n: int) -> torch.Tensor:
+    """[M, words] int64 bitmask -> [M, n] bool (bit i%64 of word i//64)."""
+    b = bits.cpu().view(torch.int64)
+    shifts = torch.arange(64, dtype=torch.int64)
+    m = ((b.unsqueeze(-1) >> shifts) & 1).bool().reshape(b.shape[0], -1)
+    return m[:, :n]
+
+
+class PreparedCall:
+    """A library call with every argument resolved once, for tight launch loops
+    (benchmarks, decode loops): calling it performs only the C call."""
+
+    def __init__(self, fn, args, name, keep):
+        self._fn, self._args, self._name, self._keep = fn, args, name, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != L.AS_OK:
+            L.check(st, self._name)
+
+
+def prepare_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float, t_h: float, Y: torch.Tensor,
+                              neuron_idx: torch.Tensor | None = None, flags: int = 0, events=None) -> PreparedCall:
+    X2 = X.reshape(1, -1) if X.dim() == 1 else X
+    _need_cuda(X2, w.w_gate_up, w.w_down, neuron_idx, Y)
+    M = X2.shape[0]
+    lib = L.load()
+    ws_ = w.struct()
+    nb = lib.as_sparse_swiglu_mlp_ws_size(M, ctypes.byref(ws_), w.mode)
+    ws = workspace(("mlp", w.mode, M, w.d_model, w.d_ff), nb, X.device)
+    dbg = None
+    if events is not None:
+        dbg = L.ASMlpDebug()
+        for i, e in enumerate(events):
+            dbg.ev[i] = e.ev if e is not None else None
+    n_active = 0 if neuron_idx is None else neuron_idx.numel()
+    args = (_ptr(X2), _dt(X2), M, ctypes.byref(ws_), w.mode, ctypes.c_float(t_x), ctypes.c_float(t_h),
+            _ptr(neuron_idx), n_active, _ptr(Y), _dt(Y), flags,
+            ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream(X.device))
+    return PreparedCall(lib.as_sparse_swiglu_mlp, args, "as_sparse_swiglu_mlp", (ws_, dbg, ws, X2, Y))

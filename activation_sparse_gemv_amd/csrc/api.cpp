@@ -1,0 +1,383 @@
+// C ABI of libactsparse: argument validation, workspace layout, launch planning.
+#include "../../include/actsparse.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "internal.hpp"
+
+using namespace as;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+as_status fail(as_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+as_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return AS_OK;
+  return fail(AS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is_wdt(as_dtype d) { return d == AS_F16 || d == AS_BF16; }
+bool is_dt(as_dtype d) { return d == AS_F16 || d == AS_BF16 || d == AS_F32; }
+int mt_for(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+
+int num_cus() {
+  static int cus = -1;
+  if (cus < 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      cus = prop.multiProcessorCount;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// Launch plan of one row-gather GEMV over at most `rows` rows and `cols` output
+// columns (paired gate/up: `cols` neurons, 2*cols columns).
+struct Plan {
+  int lpr, n_tiles, S, cap;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : dflt;
+}
+
+Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix) {
+  // Tile width: lanes_per_row * 8 columns.  Wider tiles give longer bursts per
+  // row; narrower tiles give more tiles (less split-K, cheaper final combine).
+  const long tot_cols = gu ? 2L * cols : cols;
+  int lpr;
+  if (tot_cols >= 512L * 48) lpr = 64;
+  else if (gu) lpr = 32;
+  else lpr = 16;
+  char key[64];
+  snprintf(key, sizeof key, "%s_LPR", env_prefix);
+  lpr = env_int(key, lpr);
+  if (gu && lpr < 32) lpr = 32;
+  const int tn = lpr * 8;
+  const int n_tiles = gu ? (cols + tn / 2 - 1) / (tn / 2) : (cols + tn - 1) / tn;
+  // Slices: about 1.75 workgroups per CU in total, at least ~24 rows per slice.
+  // Every workgroup pays a fixed chain of round trips (input compaction, partial
+  // store, tile counter, final combine), so fewer, longer workgroups win as long
+  // as every CU has work (measured on MI355X for the 4096 -> 2x14336 and
+  // 14336 -> 4096 shapes).
+  const int target = (7 * num_cus()) / 4;
+  int S = (target + n_tiles - 1) / n_tiles;
+  int smax = rows / 24;
+  if (smax < 1) smax = 1;
+  if (S > smax) S = smax;
+  if (S > 256) S = 256;
+  if (S < 1) S = 1;
+  snprintf(key, sizeof key, "%s_S", env_prefix);
+  S = env_int(key, S);
+  if (S < 1) S = 1;
+  const int cap = (rows + S - 1) / S;
+  return Plan{lpr, n_tiles, S, cap};
+}
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off += up256(count * sizeof(T));
+    return p;
+  }
+};
+
+// Workspace of one GEMV: counters, partials.
+struct GemvWs {
+  unsigned* counters;
+  float* partials;
+};
+GemvWs carve_gemv(Carver& c, const Plan& pl, int M, long part_ld) {
+  GemvWs w;
+  w.counters = c.take<unsigned>(pl.n_tiles);
+  w.partials = c.take<float>(size_t(pl.S) * M * part_ld);
+  return w;
+}
+
+// Workspace of a two-stage MLP.
+struct MlpWs {
+  GemvWs g1, g2;
+  float* h;
+  int* l_cnt;
+  int* l_idx;
+  float* l_val;
+};
+
+struct MlpPlan {
+  Plan p1, p2;
+  int n_lt, lt_stride;
+};
+
+MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
+  MlpPlan mp;
+  if (mode == AS_MLP_THRESHOLD) {
+    mp.p1 = plan_gemv(w->d_model, w->d_ff, true, "AS_GU");
+    mp.n_lt = mp.p1.n_tiles;
+    mp.lt_stride = mp.p1.lpr * 4;   // tile neurons = tile columns / 2
+  } else {
+    mp.p1 = Plan{0, 0, 1, 0};
+    mp.n_lt = 1;
+    mp.lt_stride = w->d_ff;
+  }
+  (void)dense;
+  mp.p2 = plan_gemv(w->d_ff, w->d_model, false, "AS_DN");
+  (void)M;
+  return mp;
+}
+
+MlpWs carve_mlp(Carver& c, const MlpPlan& mp, int M, const as_mlp_weights* w, as_mlp_mode mode) {
+  MlpWs ws;
+  if (mode == AS_MLP_THRESHOLD) ws.g1 = carve_gemv(c, mp.p1, M, 2L * w->d_ff);
+  else ws.g1 = GemvWs{nullptr, nullptr};
+  ws.g2 = carve_gemv(c, mp.p2, M, w->d_model);
+  ws.h = c.take<float>(size_t(M) * w->d_ff);
+  ws.l_cnt = c.take<int>(mp.n_lt);
+  ws.l_idx = c.take<int>(w->d_ff);
+  ws.l_val = c.take<float>(size_t(w->d_ff) * M);
+  return ws;
+}
+
+GemvParams base_params() {
+  GemvParams p;
+  memset(&p, 0, sizeof p);
+  return p;
+}
+
+as_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need > 0 && ws == nullptr) return fail(AS_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (ws_bytes < need) return fail(AS_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if (ws && !aligned16(ws)) return fail(AS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  return AS_OK;
+}
+
+}  // namespace
+
+// =====================================================================================
+extern "C" {
+
+int as_version(void) { return AS_VERSION; }
+
+const char* as_status_string(as_status s) {
+  switch (s) {
+    case AS_OK: return "AS_OK";
+    case AS_ERR_INVALID_ARG: return "AS_ERR_INVALID_ARG";
+    case AS_ERR_UNSUPPORTED: return "AS_ERR_UNSUPPORTED";
+    case AS_ERR_WORKSPACE: return "AS_ERR_WORKSPACE";
+    case AS_ERR_HIP: return "AS_ERR_HIP";
+  }
+  return "AS_ERR_UNKNOWN";
+}
+
+const char* as_last_error(void) { return g_last_error.c_str(); }
+
+as_status as_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return AS_OK;
+  if (!ws) return fail(AS_ERR_INVALID_ARG, "as_workspace_init: ws is NULL");
+  return hip_check(launch_fill_zero(ws, bytes, stream), "as_workspace_init");
+}
+
+as_status as_bench_flush(void* buf, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return AS_OK;
+  if (!buf) return fail(AS_ERR_INVALID_ARG, "as_bench_flush: buf is NULL");
+  static uint32_t salt = 1;
+  return hip_check(launch_fill_pattern(buf, bytes, 0x9e3779b9u * salt++, stream), "as_bench_flush");
+}
+
+as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64_t rank, float* t_out,
+                                 hipStream_t stream) {
+  if (!pool || !t_out) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: NULL pointer");
+  if (!is_dt(dt)) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: bad dtype %d", int(dt));
+  if (n < 1 || rank < 0 || rank > n)
+    return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: n=%lld rank=%lld", (long long)n, (long long)rank);
+  return hip_check(launch_calibrate(pool, int(dt), n, rank, t_out, stream), "as_calibrate_threshold");
+}
+
+// ------------------------------------------------------------------ GEMV
+size_t as_threshold_gemv_ws_size(int M, int K, int N) {
+  if (M < 1 || K < 1 || N < 1) return 0;
+  const Plan pl = plan_gemv(K, N, false, "AS_GV");
+  Carver c{nullptr};
+  carve_gemv(c, pl, M, N);
+  return c.off;
+}
+
+static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N,
+                             float t, void* Y, as_dtype y_dt, unsigned flags, as_mask_out* mo, void* ws,
+                             size_t ws_bytes, hipStream_t stream, bool dense, const char* fn) {
+  if (!X || !W || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, W or Y", fn);
+  if (!is_dt(x_dt) || !is_wdt(w_dt) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (M < 1 || M > 8) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..8", fn, M);
+  if (K < 1 || N < 8 || N % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: K=%d N=%d (N must be a multiple of 8)", fn, K, N);
+  if (!aligned16(W)) return fail(AS_ERR_INVALID_ARG, "%s: W not 16-byte aligned", fn);
+  if (mo && mo->idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: mask idx export needs M == 1", fn);
+  const Plan pl = plan_gemv(K, N, false, "AS_GV");
+  Carver c{reinterpret_cast<char*>(ws)};
+  GemvWs gw = carve_gemv(c, pl, M, N);
+  as_status st = check_ws(ws, ws_bytes, c.off);
+  if (st != AS_OK) return st;
+
+  GemvParams p = base_params();
+  p.x = X; p.x_dt = int(x_dt); p.M = M; p.K = K; p.ldx = K; p.t = t;
+  p.W = reinterpret_cast<const uint16_t*>(W); p.ldw = N; p.N = N;
+  p.n_tiles = pl.n_tiles; p.S = pl.S; p.cap = pl.cap;
+  p.partials = gw.partials; p.counters = gw.counters; p.part_ld = N;
+  p.y = Y; p.y_dt = int(y_dt); p.ldy = N; p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
+  if (mo && !dense) {
+    p.x_bits = mo->bits; p.x_bits_ld = (K + 63) / 64; p.x_idx = mo->idx; p.x_nnz = mo->nnz;
+  }
+  GemvConfig cfg{int(w_dt), mt_for(M), pl.lpr, dense ? IN_ALL : IN_THRESH, OUT_Y, false,
+                 (flags & AS_FLAG_NO_NT_LOADS) == 0};
+  return hip_check(launch_gather_gemv(cfg, p, stream), fn);
+}
+
+as_status as_threshold_gemv(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N,
+                            float t, void* Y, as_dtype y_dt, unsigned flags, as_mask_out* mask_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
+  return gemv_common(X, x_dt, M, K, W, w_dt, N, t, Y, y_dt, flags, mask_out, ws, ws_bytes, stream, dense,
+                     "as_threshold_gemv");
+}
+
+as_status as_dense_gemv(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N, void* Y,
+                        as_dtype y_dt, unsigned flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return gemv_common(X, x_dt, M, K, W, w_dt, N, -INFINITY, Y, y_dt, flags, nullptr, ws, ws_bytes, stream, true,
+                     "as_dense_gemv");
+}
+
+// ------------------------------------------------------------------ MLP
+static as_status check_mlp_weights(const as_mlp_weights* w, as_mlp_mode mode, const char* fn) {
+  if (!w) return fail(AS_ERR_INVALID_ARG, "%s: weights struct is NULL", fn);
+  if (!w->w_gate_up) return fail(AS_ERR_INVALID_ARG, "%s: w_gate_up is NULL", fn);
+  if (!is_wdt(w->w_dt)) return fail(AS_ERR_INVALID_ARG, "%s: weight dtype must be f16 or bf16", fn);
+  if (w->d_model < 8 || w->d_model % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: d_model=%d not a multiple of 8", fn, w->d_model);
+  if (w->d_ff < 64 || w->d_ff % 64 != 0) return fail(AS_ERR_INVALID_ARG, "%s: d_ff=%d not a multiple of 64", fn, w->d_ff);
+  if (!aligned16(w->w_gate_up)) return fail(AS_ERR_INVALID_ARG, "%s: w_gate_up not 16-byte aligned", fn);
+  if (mode == AS_MLP_THRESHOLD) {
+    if (!w->w_down) return fail(AS_ERR_INVALID_ARG, "%s: w_down is NULL", fn);
+    if (!aligned16(w->w_down)) return fail(AS_ERR_INVALID_ARG, "%s: w_down not 16-byte aligned", fn);
+  } else if (mode != AS_MLP_NEURON_SET) {
+    return fail(AS_ERR_INVALID_ARG, "%s: bad mode %d", fn, int(mode));
+  }
+  return AS_OK;
+}
+
+size_t as_sparse_swiglu_mlp_ws_size(int M, const as_mlp_weights* w, as_mlp_mode mode) {
+  if (M < 1 || !w || w->d_model < 1 || w->d_ff < 1) return 0;
+  const MlpPlan mp = plan_mlp(M, w, mode, false);
+  Carver c{nullptr};
+  carve_mlp(c, mp, M, w, mode);
+  return c.off;
+}
+
+as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp_weights* w, as_mlp_mode mode,
+                               float t_x, float t_h, const int32_t* neuron_idx, int n_active, void* Y,
+                               as_dtype y_dt, unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  const char* fn = "as_sparse_swiglu_mlp";
+  as_status st = check_mlp_weights(w, mode, fn);
+  if (st != AS_OK) return st;
+  if (!X || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X or Y", fn);
+  if (!is_dt(x_dt) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (M < 1 || M > 8) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..8", fn, M);
+  const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
+  if (mode == AS_MLP_NEURON_SET && !dense) {
+    if (n_active < 0 || n_active > w->d_ff) return fail(AS_ERR_INVALID_ARG, "%s: n_active=%d", fn, n_active);
+    if (n_active > 0 && !neuron_idx) return fail(AS_ERR_INVALID_ARG, "%s: neuron_idx is NULL", fn);
+  }
+  if (dbg && (dbg->h_mask.idx || dbg->h_mask.nnz))
+    return fail(AS_ERR_UNSUPPORTED, "%s: h mask exports bits only", fn);
+  if (dbg && dbg->x_mask.idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: x mask idx export needs M == 1", fn);
+  if (dbg && mode == AS_MLP_NEURON_SET && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz || dbg->h_mask.bits))
+    return fail(AS_ERR_UNSUPPORTED, "%s: mask exports exist in THRESHOLD mode only", fn);
+
+  const MlpPlan mp = plan_mlp(M, w, mode, dense);
+  Carver c{reinterpret_cast<char*>(ws)};
+  MlpWs mw = carve_mlp(c, mp, M, w, mode);
+  st = check_ws(ws, ws_bytes, c.off);
+  if (st != AS_OK) return st;
+
+  const int d = w->d_model, f = w->d_ff;
+  const int mt = mt_for(M);
+  const bool nt = (flags & AS_FLAG_NO_NT_LOADS) == 0;
+  hipEvent_t* ev = dbg ? dbg->ev : nullptr;
+  auto rec = [&](int i) -> as_status {
+    if (ev && ev[i]) return hip_check(hipEventRecord(ev[i], stream), "hipEventRecord");
+    return AS_OK;
+  };
+  if ((st = rec(0)) != AS_OK) return st;
+
+  float* hbuf = (dbg && dbg->h && mode == AS_MLP_THRESHOLD) ? dbg->h : mw.h;
+  GemvParams p2 = base_params();
+  GemvConfig c2{int(w->w_dt), mt, mp.p2.lpr, IN_LISTS, OUT_Y, false, nt};
+
+  if (mode == AS_MLP_THRESHOLD) {
+    // stage 1: x mask -> gate/up gather GEMV -> SwiGLU -> h mask -> per-tile lists
+    GemvParams p = base_params();
+    p.x = X; p.x_dt = int(x_dt); p.M = M; p.K = d; p.ldx = d; p.t = t_x;
+    p.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.ldw = 2L * f; p.N = f; p.gu_off = f;
+    p.n_tiles = mp.p1.n_tiles; p.S = mp.p1.S; p.cap = mp.p1.cap;
+    p.partials = mw.g1.partials; p.counters = mw.g1.counters; p.part_ld = 2L * f;
+    p.t_h = dense ? -INFINITY : t_h; p.h = hbuf; p.ldh = f;
+    if (!dense) { p.o_cnt = mw.l_cnt; p.o_idx = mw.l_idx; p.o_val = mw.l_val; }
+    if (dbg && !dense) {
+      p.h_bits = dbg->h_mask.bits; p.h_bits_ld = (f + 63) / 64;
+      p.x_bits = dbg->x_mask.bits; p.x_bits_ld = (d + 63) / 64; p.x_idx = dbg->x_mask.idx; p.x_nnz = dbg->x_mask.nnz;
+    }
+    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : IN_THRESH, OUT_SWIGLU, true, nt};
+    if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
+    if ((st = rec(1)) != AS_OK) return st;
+    // stage 2: down projection over the surviving h rows
+    p2.W = reinterpret_cast<const uint16_t*>(w->w_down); p2.ldw = d;
+    if (dense) {
+      c2.in = IN_ALL;
+      p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = -INFINITY;
+    }
+  } else {
+    // stage 1: gate/up dot products of the listed neurons (neuron-major rows)
+    NeuronGuParams q;
+    memset(&q, 0, sizeof q);
+    q.x = X; q.x_dt = int(x_dt); q.M = M; q.ldx = d; q.d_model = d;
+    q.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); q.ld_neuron = 3L * d; q.up_off = d;
+    q.idx = dense ? nullptr : neuron_idx; q.n_active = dense ? f : n_active;
+    q.h_dbg = dbg ? dbg->h : nullptr; q.ld_hdbg = q.n_active;
+    q.o_cnt = mw.l_cnt; q.o_idx = mw.l_idx; q.o_val = mw.l_val;
+    q.neurons_per_wave = env_int("AS_NS_NPW", 2);
+    if ((st = hip_check(launch_neuron_gu(int(w->w_dt), mt, nt, q, stream), fn)) != AS_OK) return st;
+    if ((st = rec(1)) != AS_OK) return st;
+    p2.W = reinterpret_cast<const uint16_t*>(w->w_gate_up) + 2L * d; p2.ldw = 3L * d;
+  }
+  p2.M = M;
+  p2.list_cnt = mw.l_cnt; p2.list_idx = mw.l_idx; p2.list_val = mw.l_val;
+  p2.n_lt = mp.n_lt; p2.lt_stride = mp.lt_stride;
+  p2.N = d;
+  p2.n_tiles = mp.p2.n_tiles; p2.S = mp.p2.S; p2.cap = mp.p2.cap;
+  p2.partials = mw.g2.partials; p2.counters = mw.g2.counters; p2.part_ld = d;
+  p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
+  if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;
+  return rec(2);
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Device helpers shared by the gfx950 kernels: dtype conversion, 16-byte weight
+// loads, wave64 / workgroup scans, and the internal launch interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace as {
+
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)b);
+  return (float)h;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                                                  // RNE
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Element i of a vector stored in dtype dt, as fp32 (exact for f16/bf16).
+__device__ __forceinline__ float load_elem(const void* p, int dt, long i) {
+  if (dt == DT_F32) return reinterpret_cast<const float*>(p)[i];
+  uint32_t b = reinterpret_cast<const uint16_t*>(p)[i];
+  return dt == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+__device__ __forceinline__ void store_elem(void* p, int dt, long i, float v) {
+  if (dt == DT_F32) reinterpret_cast<float*>(p)[i] = v;
+  else if (dt == DT_BF16) reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+  else reinterpret_cast<uint16_t*>(p)[i] = f32_to_f16_bits(v);
+}
+
+// 16-byte weight load (8 x 16-bit), nontemporal when nt is set: the rows are
+// streamed once per call, so they should not displace x, h and the partials.
+__device__ __forceinline__ u32x4 load_w16(const uint16_t* p, bool nt) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  return nt ? __builtin_nontemporal_load(q) : *q;
+}
+
+// Unpack 8 weights (two per dword, low half first) to fp32.
+template <int WDT>
+__device__ __forceinline__ void unpack8(const u32x4 v, float w[8]) {
+  if constexpr (WDT == DT_BF16) {
+    w[0] = __uint_as_float(v.x << 16); w[1] = __uint_as_float(v.x & 0xffff0000u);
+    w[2] = __uint_as_float(v.y << 16); w[3] = __uint_as_float(v.y & 0xffff0000u);
+    w[4] = __uint_as_float(v.z << 16); w[5] = __uint_as_float(v.z & 0xffff0000u);
+    w[6] = __uint_as_float(v.w << 16); w[7] = __uint_as_float(v.w & 0xffff0000u);
+  } else {
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[2 * k] = f16_bits_to_f32(q[k] & 0xffffu);
+      w[2 * k + 1] = f16_bits_to_f32(q[k] >> 16);
+    }
+  }
+}
+
+// CE consecutive elements of a vector (dtype dt) starting at element `off`, as fp32.
+// n == CE: vector loads (the caller guarantees 16-byte alignment); otherwise the
+// first n elements are loaded one by one and the rest are zero.
+template <int CE>
+__device__ __forceinline__ void load_chunk(const void* x, int dt, long off, int n, float v[CE]) {
+  static_assert(CE % 8 == 0, "chunk of whole 16-byte vectors");
+  if (n == CE) {
+    if (dt == DT_F32) {
+      const float4* q = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
+      float4 f[CE / 4];
+#pragma unroll
+      for (int k = 0; k < CE / 4; ++k) f[k] = q[k];
+#pragma unroll
+      for (int k = 0; k < CE / 4; ++k) {
+        v[4 * k] = f[k].x; v[4 * k + 1] = f[k].y; v[4 * k + 2] = f[k].z; v[4 * k + 3] = f[k].w;
+      }
+    } else {
+      const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
+      u32x4 raw[CE / 8];
+#pragma unroll
+      for (int k = 0; k < CE / 8; ++k) raw[k] = q[k];
+#pragma unroll
+      for (int k = 0; k < CE / 8; ++k) {
+        if (dt == DT_BF16) unpack8<DT_BF16>(raw[k], v + 8 * k);
+        else unpack8<DT_F16>(raw[k], v + 8 * k);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < CE; ++e) v[e] = e < n ? load_elem(x, dt, off + e) : 0.f;
+  }
+}
+
+// Wait until every vector-memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt/lgkmcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Device-coherent (agent scope) store / load: written through to, or read from,
+// the level shared by every XCD, so no L2 writeback or invalidate is needed.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------- wave64 helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` in lanes below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan over a workgroup of NT threads (NT a multiple of 64, <= 1024).
+// `sm` needs NT/64 + 1 ints.  Returns the exclusive prefix; *total = the sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* sm, int* total) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  int inc = wave_incl_scan(v);
+  if (l == 63) sm[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < NW; ++i) { int c = sm[i]; sm[i] = run; run += c; }
+    sm[NW] = run;
+  }
+  __syncthreads();
+  int r = sm[w] + inc - v;
+  *total = sm[NW];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace as

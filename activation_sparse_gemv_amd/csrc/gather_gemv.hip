@@ -1,0 +1,56 @@
+// Row-gather GEMV launch entry: picks the instantiation (weights dtype, tokens) and
+// the threshold-prologue chunk width.  The kernel itself is in gather_gemv_impl.hpp.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace as {
+
+constexpr int kThreadsHost = 256;
+
+size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
+  const int nslot = 4 * (64 / c.lpr), tn = c.lpr * 8;
+  size_t b = ((size_t(cap) * 4 + 15) & ~size_t(15)) + ((size_t(cap) * c.mt * 4 + 15) & ~size_t(15));
+  b += (size_t(nslot > c.mt ? nslot : c.mt) * tn * 4 + 15) & ~size_t(15);
+  if (c.in == IN_LISTS) b += (size_t(n_lt + 1) * 4 + 15) & ~size_t(15);
+  return b;
+}
+
+hipError_t launch_gemv_bf16_m1(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+hipError_t launch_gemv_bf16_m2(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+hipError_t launch_gemv_bf16_m4(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+hipError_t launch_gemv_bf16_m8(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+hipError_t launch_gemv_f16_m1(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+hipError_t launch_gemv_f16_m2(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+hipError_t launch_gemv_f16_m4(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+hipError_t launch_gemv_f16_m8(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
+
+// Chunk width (16-byte vectors of 8 inputs per thread) of the vectorised
+// threshold prologue, or 0 for the general element-wise prologue.
+int pick_chunk_vectors(const void* x, int x_dt, int K, long ldx) {
+  const int es = x_dt == DT_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0 || (ldx * es) % 16 != 0) return 0;
+  const int per = (K + kThreadsHost - 1) / kThreadsHost;
+  if (per <= 16) return 2;
+  if (per <= 64) return 8;
+  return 0;
+}
+
+hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s) {
+  const size_t smem = gemv_smem_bytes(c, p.cap, p.n_lt);
+  if (c.gu && c.lpr == 16) return hipErrorInvalidValue;
+  GemvConfig cc = c;
+  if (cc.in == IN_THRESH && cc.nv < 0) {
+    cc.nv = pick_chunk_vectors(p.x, p.x_dt, p.K, p.ldx);
+    if (cc.mt > 1 && cc.nv > 2) cc.nv = 0;     // wide register chunks only for one token
+  }
+  const bool bf = cc.wdt == DT_BF16;
+  switch (cc.mt) {
+    case 1: return bf ? launch_gemv_bf16_m1(cc, p, smem, s) : launch_gemv_f16_m1(cc, p, smem, s);
+    case 2: return bf ? launch_gemv_bf16_m2(cc, p, smem, s) : launch_gemv_f16_m2(cc, p, smem, s);
+    case 4: return bf ? launch_gemv_bf16_m4(cc, p, smem, s) : launch_gemv_f16_m4(cc, p, smem, s);
+    case 8: return bf ? launch_gemv_bf16_m8(cc, p, smem, s) : launch_gemv_f16_m8(cc, p, smem, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace as

@@ -1,0 +1,494 @@
+// Row-gather GEMV for activation-sparse decode on gfx950.
+//
+// TEAL slides, slide 11 (Hardware-Aware Acceleration): the mask is generated
+// inside the sparse kernel and only the weight rows of surviving inputs are
+// loaded; the mask itself is never stored.  Here W is input-major ([K, N]
+// row-major), so the weights of one surviving input neuron are one contiguous
+// row and every load below is a coalesced 16-byte-per-lane burst.
+//
+// Work decomposition (one launch):
+//   * every workgroup rebuilds the compacted list of surviving rows from the
+//     8 KB input vector (wave64 ballots + a workgroup scan), keeping only the
+//     slice of the list it owns: slices split the list evenly, so work is
+//     balanced whatever the mask looks like;
+//   * the grid is n_tiles column tiles x S slices; a workgroup streams its
+//     slice of rows for its tile's columns and accumulates in fp32 registers;
+//   * the S partial tiles are combined by the last workgroup to finish a tile
+//     (device-coherent partial stores and a per-tile counter), always in slice
+//     order so the result is bitwise reproducible, and that workgroup runs the
+//     epilogue: store y, or the SwiGLU step h = silu(g) * u, the |h| > t_h mask
+//     and a per-tile compacted list that feeds the down projection.
+#pragma once
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace as {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+
+template <int LPR>
+struct TileShape {
+  static constexpr int RPW = 64 / LPR;     // rows per wave instruction
+  static constexpr int NSLOT = 4 * RPW;    // row slots per workgroup
+  static constexpr int TN = LPR * 8;       // tile width in columns
+};
+
+__host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~size_t(15); }
+
+
+// Verification exports of the per-token input masks (bits and nnz by workgroup 0;
+// the ascending index list, M == 1 only, by the workgroups of column tile 0).
+template <int MT>
+__device__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_scan, int tid, int tile, int lo,
+                               int cnt) {
+  const int K = p.K;
+  const float t = p.t;
+  const int M = p.M;
+  const int C = (K + kThreads - 1) / kThreads;
+  const int i0 = min(tid * C, K), i1 = min(i0 + C, K);
+  if (p.x_bits != nullptr && blockIdx.x == 0) {
+    const int nw = (K + 63) / 64;
+    for (int m = 0; m < M; ++m)
+      for (int w = tid; w < nw; w += kThreads) {
+        uint64_t bits = 0;
+        for (int b = 0; b < 64; ++b) {
+          int i = w * 64 + b;
+          if (i < K && fabsf(load_elem(p.x, p.x_dt, m * p.ldx + i)) > t) bits |= (uint64_t)1 << b;
+        }
+        p.x_bits[m * p.x_bits_ld + w] = bits;
+      }
+  }
+  if (p.x_nnz != nullptr && blockIdx.x == 0) {
+    for (int m = 0; m < M; ++m) {
+      int cm = 0;
+      for (int i = i0; i < i1; ++i) cm += fabsf(load_elem(p.x, p.x_dt, m * p.ldx + i)) > t;
+      int tot;
+      (void)block_excl_scan<kThreads>(cm, s_scan, &tot);
+      if (tid == 0) p.x_nnz[m] = tot;
+    }
+  }
+  if (p.x_idx != nullptr && tile == 0) {
+    __syncthreads();
+    for (int r = tid; r < cnt; r += kThreads) p.x_idx[lo + r] = s_idx[r];
+  }
+}
+
+template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
+__global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams p) {
+  using TS = TileShape<LPR>;
+  constexpr int RPW = TS::RPW, NSLOT = TS::NSLOT, TN = TS::TN, TB = TN / 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int cap = p.cap;
+  int* s_idx = reinterpret_cast<int*>(smem);
+  float* s_val = reinterpret_cast<float*>(smem + align16(size_t(cap) * 4));
+  float* s_red = reinterpret_cast<float*>(smem + align16(size_t(cap) * 4) + align16(size_t(cap) * MT * 4));
+  int* s_pref = reinterpret_cast<int*>(reinterpret_cast<unsigned char*>(s_red) +
+                                       align16(size_t(NSLOT > MT ? NSLOT : MT) * TN * 4));
+  __shared__ int s_scan[kThreads / 64 + 1];
+  __shared__ int s_flag;
+
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x % p.n_tiles;
+  const int sl = blockIdx.x / p.n_tiles;
+  const int S = p.S;
+  const int M = p.M;
+
+  // ------------------------------------------------------------ prologue
+  int cnt = 0;
+  if constexpr (IN == IN_THRESH && NV > 0) {
+    // Each thread owns CE = 8*NV consecutive inputs, loaded with 16-byte vector
+    // loads issued together; the union mask over tokens stays in a 64-bit word,
+    // so the whole compaction costs one L2 round trip and one workgroup scan.
+    constexpr int CE = 8 * NV;
+    const int K = p.K;
+    const float t = p.t;
+    const int i0 = tid * CE;
+    const int n = max(0, min(CE, K - i0));
+    float v0[CE];
+    uint64_t ubits = 0;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < M) {
+        float v[CE];
+        load_chunk<CE>(p.x, p.x_dt, (long)m * p.ldx + i0, n, v);
+        uint64_t b = 0;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) b |= (uint64_t)(e < n && fabsf(v[e]) > t) << e;
+        ubits |= b;
+        if (m == 0)
+#pragma unroll
+          for (int e = 0; e < CE; ++e) v0[e] = v[e];
+      }
+    }
+    const int c = __popcll(ubits);
+    int nnz;
+    const int off = block_excl_scan<kThreads>(c, s_scan, &nnz);
+    const int lo = int((long)sl * nnz / S), hi = int((long)(sl + 1) * nnz / S);
+    cnt = hi - lo;
+    if (off < hi && off + c > lo) {
+#pragma unroll
+      for (int e = 0; e < CE; ++e) {
+        if ((ubits >> e) & 1) {
+          const int r = off + __popcll(ubits & ((((uint64_t)1) << e) - 1));
+          if (r >= lo && r < hi) {
+            s_idx[r - lo] = i0 + e;
+            s_val[r - lo] = fabsf(v0[e]) > t ? v0[e] : 0.f;
+#pragma unroll
+            for (int m = 1; m < MT; ++m) {
+              float xv = 0.f;
+              if (m < M) {
+                xv = load_elem(p.x, p.x_dt, (long)m * p.ldx + i0 + e);
+                xv = fabsf(xv) > t ? xv : 0.f;
+              }
+              s_val[m * cap + (r - lo)] = xv;
+            }
+          }
+        }
+      }
+    }
+    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt);
+  } else if constexpr (IN == IN_THRESH) {
+    const int K = p.K;
+    const float t = p.t;
+    const int C = (K + kThreads - 1) / kThreads;
+    const int i0 = min(tid * C, K), i1 = min(i0 + C, K);
+    int c = 0;
+    for (int i = i0; i < i1; ++i) {
+      bool a = false;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < M) a |= fabsf(load_elem(p.x, p.x_dt, m * p.ldx + i)) > t;
+      c += a;
+    }
+    int nnz;
+    const int off = block_excl_scan<kThreads>(c, s_scan, &nnz);
+    const int lo = int((long)sl * nnz / S), hi = int((long)(sl + 1) * nnz / S);
+    cnt = hi - lo;
+    if (off < hi && off + c > lo) {
+      int r = off;
+      for (int i = i0; i < i1 && r < hi; ++i) {
+        float xv[MT];
+        bool a = false;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float v = m < M ? load_elem(p.x, p.x_dt, m * p.ldx + i) : 0.f;
+          bool k = fabsf(v) > t;
+          a |= k;
+          xv[m] = k ? v : 0.f;
+        }
+        if (a) {
+          if (r >= lo) {
+            s_idx[r - lo] = i;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) s_val[m * cap + (r - lo)] = xv[m];
+          }
+          ++r;
+        }
+      }
+    }
+    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt);
+  } else if constexpr (IN == IN_LISTS) {
+    const int n_lt = p.n_lt;
+    int run = 0;
+    for (int base = 0; base < n_lt; base += kThreads) {
+      const int q = base + tid;
+      const int v = q < n_lt ? p.list_cnt[q] : 0;
+      int tot;
+      const int off = block_excl_scan<kThreads>(v, s_scan, &tot);
+      if (q < n_lt) s_pref[q] = run + off;
+      run += tot;
+    }
+    if (tid == 0) s_pref[n_lt] = run;
+    __syncthreads();
+    const int nnz = run;
+    const int lo = int((long)sl * nnz / S), hi = int((long)(sl + 1) * nnz / S);
+    cnt = hi - lo;
+    for (int r = tid; r < cnt; r += kThreads) {
+      const int g = lo + r;
+      int a = 0, b = n_lt;            // largest q with s_pref[q] <= g
+      while (b - a > 1) {
+        const int mid = (a + b) >> 1;
+        if (s_pref[mid] <= g) a = mid; else b = mid;
+      }
+      const long e = (long)a * p.lt_stride + (g - s_pref[a]);
+      s_idx[r] = p.list_idx[e];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? p.list_val[e * M + m] : 0.f;
+    }
+  } else {  // IN_ALL: every row, no mask (dense baseline)
+    const int K = p.K;
+    const int lo = int((long)sl * K / S), hi = int((long)(sl + 1) * K / S);
+    cnt = hi - lo;
+    for (int r = tid; r < cnt; r += kThreads) {
+      s_idx[r] = lo + r;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        s_val[m * cap + r] = m < M ? load_elem(p.x, p.x_dt, m * p.ldx + lo + r) : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------ main loop
+  const int lane = tid & 63, wave = tid >> 6;
+  const int sub = lane / LPR, l = lane % LPR;
+  const int slot = wave * RPW + sub;
+  long wcol;
+  bool valid;
+  if constexpr (GU) {
+    const int nb = tile * TB + (l % (LPR / 2)) * 8;
+    valid = nb < p.N;
+    wcol = (l < LPR / 2) ? nb : p.gu_off + nb;
+  } else {
+    const int c0 = tile * TN + l * 8;
+    valid = c0 < p.N;
+    wcol = c0;
+  }
+  // Lanes past a ragged column edge read column 0 of the same rows (their sums are
+  // discarded), and rows past the end of the slice repeat its last row with x = 0,
+  // so every load below is unconditional and all kUnroll loads issue back to back.
+  const uint16_t* Wc = p.W + (valid ? wcol : 0);
+  const long ldw = p.ldw;
+
+  float acc[MT][8];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = 0.f;
+
+  for (int r = slot; r < cnt; r += NSLOT * kUnroll) {
+    int row[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) row[u] = s_idx[min(r + u * NSLOT, cnt - 1)];
+    u32x4 w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) w[u] = load_w16(Wc + (long)row[u] * ldw, NT);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int rr = r + u * NSLOT;
+      float wf[8];
+      unpack8<WDT>(w[u], wf);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float xv = rr < cnt ? s_val[m * cap + rr] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[m][j] = fmaf(xv, wf[j], acc[m][j]);
+      }
+    }
+  }
+
+  // ------------------------------------------------------------ slot reduction
+  constexpr int CPT = (TN + kThreads - 1) / kThreads;   // tile columns per thread
+  float res[MT][CPT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_red[slot * TN + l * 8 + j] = acc[m][j];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kThreads;
+      float v = 0.f;
+      if (c < TN)
+#pragma unroll
+        for (int s2 = 0; s2 < NSLOT; ++s2) v += s_red[s2 * TN + c];
+      res[m][q] = v;
+    }
+  }
+
+  // tile-local column c -> (validity, partial/output column)
+  auto col_of = [&](int c, bool& ok) -> long {
+    if constexpr (GU) {
+      const int n = tile * TB + (c % TB);
+      ok = n < p.N;
+      return c < TB ? (long)n : (long)p.N + n;
+    } else {
+      const int n = tile * TN + c;
+      ok = n < p.N;
+      return n;
+    }
+  };
+
+  // ------------------------------------------------------------ split-K combine
+  if (S > 1) {
+    // Partials are written through to the device-coherent level (relaxed agent-scope
+    // atomic stores) and the wave waits for their completion before the counter
+    // increment; the last workgroup reads them back with coherent loads.  No
+    // L2 writeback/invalidate fence is needed on any workgroup.
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kThreads;
+      bool ok;
+      const long pc = col_of(c, ok);
+      if (c < TN && ok)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < M) store_coherent(p.partials + ((long)sl * M + m) * p.part_ld + pc, res[m][q]);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = (prev == unsigned(S - 1));
+    }
+    __syncthreads();
+    if (!s_flag) return;
+    if (tid == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Batches of kBatch slices are loaded together (one round trip per batch),
+    // then summed in slice order.
+    constexpr int kBatch = 16;
+    long pcs[CPT];
+    bool oks[CPT];
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kThreads;
+      bool ok;
+      pcs[q] = col_of(c, ok);
+      oks[q] = c < TN && ok;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= M) break;
+      float v[CPT];
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) v[q] = 0.f;
+      for (int s0 = 0; s0 < S; s0 += kBatch) {
+        float tmp[CPT][kBatch];
+#pragma unroll
+        for (int q = 0; q < CPT; ++q)
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k) {
+            const int s2 = min(s0 + k, S - 1);
+            tmp[q][k] = oks[q] ? load_coherent(p.partials + ((long)s2 * M + m) * p.part_ld + pcs[q]) : 0.f;
+          }
+#pragma unroll
+        for (int q = 0; q < CPT; ++q)
+#pragma unroll
+          for (int k = 0; k < kBatch; ++k)
+            if (s0 + k < S) v[q] += tmp[q][k];
+      }
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) res[m][q] = v[q];
+    }
+  }
+
+  // ------------------------------------------------------------ epilogues
+  if constexpr (OUT == OUT_Y) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kThreads;
+      bool ok;
+      const long gc = col_of(c, ok);
+      if (c < TN && ok)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < M) {
+            float v = res[m][q];
+            if (p.accumulate) v += load_elem(p.y, p.y_dt, m * p.ldy + gc);
+            store_elem(p.y, p.y_dt, m * p.ldy + gc, v);
+          }
+    }
+  } else {
+    static_assert(GU, "the SwiGLU epilogue needs paired gate/up columns");
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kThreads;
+      if (c < TN)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) s_red[m * TN + c] = res[m][q];
+    }
+    __syncthreads();
+    const int n = tile * TB + tid;
+    const bool nvalid = tid < TB && n < p.N;
+    float hv[MT];
+    bool any = false;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      hv[m] = 0.f;
+      if (nvalid && m < M) {
+        const float g = s_red[m * TN + tid], u = s_red[m * TN + TB + tid];
+        hv[m] = silu_f32(g) * u;
+        any |= fabsf(hv[m]) > p.t_h;
+        p.h[m * p.ldh + n] = hv[m];
+      }
+    }
+    if (p.h_bits != nullptr && tid < TB) {
+      for (int m = 0; m < M; ++m) {
+        const uint64_t bits = __ballot(nvalid && fabsf(hv[m]) > p.t_h);
+        if ((tid & 63) == 0 && tile * TB + tid < p.N) p.h_bits[m * p.h_bits_ld + (tile * TB + tid) / 64] = bits;
+      }
+    }
+    if (p.o_cnt != nullptr) {
+      const int flag = (nvalid && any) ? 1 : 0;
+      int tot;
+      const int pos = block_excl_scan<kThreads>(flag, s_scan, &tot);
+      if (flag) {
+        const long e = (long)tile * TB + pos;
+        p.o_idx[e] = n;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < M) p.o_val[e * M + m] = fabsf(hv[m]) > p.t_h ? hv[m] : 0.f;
+      }
+      if (tid == 0) p.o_cnt[tile] = tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
+hipError_t launch_one(const GemvParams& p, size_t smem, hipStream_t s) {
+  auto k = gather_gemv_kernel<WDT, MT, LPR, IN, OUT, GU, NT, NV>;
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, dim3(p.n_tiles * p.S), dim3(kThreads), smem, s, p);
+  return hipGetLastError();
+}
+
+template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT>
+hipError_t pick_nv(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
+  if constexpr (IN == IN_THRESH) {
+    if (c.nv == 2) return launch_one<WDT, MT, LPR, IN, OUT, GU, NT, 2>(p, smem, s);
+    if constexpr (MT == 1) {
+      if (c.nv == 8) return launch_one<WDT, MT, LPR, IN, OUT, GU, NT, 8>(p, smem, s);
+    }
+  }
+  return launch_one<WDT, MT, LPR, IN, OUT, GU, NT, 0>(p, smem, s);
+}
+
+template <int WDT, int MT, int LPR, int IN, int OUT, bool GU>
+hipError_t pick_nt(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
+  return c.nt ? pick_nv<WDT, MT, LPR, IN, OUT, GU, true>(c, p, smem, s)
+              : pick_nv<WDT, MT, LPR, IN, OUT, GU, false>(c, p, smem, s);
+}
+
+template <int WDT, int MT, int LPR>
+hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
+  if (c.gu) {
+    if (c.out != OUT_SWIGLU) return hipErrorInvalidValue;
+    if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_SWIGLU, true>(c, p, smem, s);
+    if (c.in == IN_ALL) return pick_nt<WDT, MT, LPR, IN_ALL, OUT_SWIGLU, true>(c, p, smem, s);
+    return hipErrorInvalidValue;
+  }
+  if (c.out != OUT_Y) return hipErrorInvalidValue;
+  if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_Y, false>(c, p, smem, s);
+  if (c.in == IN_LISTS) return pick_nt<WDT, MT, LPR, IN_LISTS, OUT_Y, false>(c, p, smem, s);
+  return pick_nt<WDT, MT, LPR, IN_ALL, OUT_Y, false>(c, p, smem, s);
+}
+
+template <int WDT, int MT>
+hipError_t pick_lpr(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
+  switch (c.lpr) {
+    case 16: return pick_mode<WDT, MT, 16>(c, p, smem, s);
+    case 32: return pick_mode<WDT, MT, 32>(c, p, smem, s);
+    case 64: return pick_mode<WDT, MT, 64>(c, p, smem, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace as

@@ -1,0 +1,67 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace as {
+
+enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2 };
+enum { OUT_Y = 0, OUT_SWIGLU = 1 };
+
+// One row-gather GEMV launch: Y[m, c] = sum over listed rows i of xv[m, i] * W[i, c].
+// The rows come from a magnitude mask of a vector (IN_THRESH), from per-tile
+// compacted lists written by an earlier stage (IN_LISTS) or are all rows (IN_ALL).
+// The grid is n_tiles column tiles x S slices of the row list (split-K); the
+// last workgroup of a tile sums the S partials in slice order and runs the
+// epilogue (OUT_Y: store y; OUT_SWIGLU: h = silu(g) * u, |h| > t_h, per-tile list).
+struct GemvParams {
+  // input vector (IN_THRESH, IN_ALL): x[m * ldx + i], i < K
+  const void* x; int x_dt; int M; int K; long ldx; float t;
+  // input lists (IN_LISTS): tile q holds list_cnt[q] entries at (q * lt_stride + e)
+  const int* list_cnt; const int* list_idx; const float* list_val; int n_lt; int lt_stride;
+  // weights: row i, column c at W[i * ldw + c]; GU: gate column n, up column gu_off + n
+  const uint16_t* W; long ldw; int N; long gu_off;
+  // split
+  int n_tiles; int S; int cap;
+  float* partials; unsigned* counters; long part_ld;
+  // OUT_Y
+  void* y; int y_dt; long ldy; int accumulate;
+  // OUT_SWIGLU
+  float t_h; float* h; long ldh; int* o_cnt; int* o_idx; float* o_val; uint64_t* h_bits; long h_bits_ld;
+  // input-mask verification exports (IN_THRESH)
+  uint64_t* x_bits; long x_bits_ld; int* x_idx; int* x_nnz;
+};
+
+struct GemvConfig {
+  int wdt;   // DT_F16 / DT_BF16
+  int mt;    // template token count (1, 2, 4, 8) >= M
+  int lpr;   // lanes per row segment (16, 32, 64): tile width lpr * 8 columns
+  int in;    // IN_*
+  int out;   // OUT_*
+  bool gu;   // paired gate/up columns
+  bool nt;   // nontemporal weight loads
+  int nv = -1;  // threshold prologue chunk (16-byte vectors per thread); -1 = choose, 0 = general
+};
+
+size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt);
+hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s);
+
+// Neuron-major gate/up dot products for a neuron list (static neuron set).
+struct NeuronGuParams {
+  const void* x; int x_dt; int M; long ldx; int d_model;
+  const uint16_t* W; long ld_neuron; long up_off;   // gate row of neuron j at W + j*ld_neuron, up at + up_off
+  const int* idx; int n_active;                       // idx == nullptr: neuron p is p
+  float* h_dbg; long ld_hdbg;                         // optional [M, n_active]
+  int* o_cnt; int* o_idx; float* o_val;               // single-tile list for the down stage
+  int neurons_per_wave;
+};
+hipError_t launch_neuron_gu(int wdt, int mt, bool nt, const NeuronGuParams& p, hipStream_t s);
+
+// Misc kernels.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);
+hipError_t launch_calibrate(const void* pool, int dt, int64_t n, int64_t rank, float* t_out, hipStream_t s);
+
+}  // namespace as

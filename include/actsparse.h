@@ -1,0 +1,177 @@
+/*
+ * actsparse.h -- C ABI of libactsparse: activation-sparse GEMV for LLM decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library implements training-free activation sparsity at decode time:
+ * the input of a projection is thresholded by magnitude (|x| > t), or reduced
+ * to a top-k neuron set, and only the weight rows of the surviving input
+ * neurons are streamed from HBM into an fp32-accumulated GEMV.
+ *
+ * Sources of the operations (web pages; cited by title and section):
+ *  - TEAL slides: "【DL輪読会】Training-Free Activation Sparsity in Large
+ *    Language Models" -- magnitude thresholding of every projection input
+ *    (method slide), thresholds from calibration data (method slide, setup
+ *    slide), fused mask + sparse GEMV that loads only the needed weights
+ *    (slide 11, Hardware-Aware Acceleration).
+ *  - GLASS summary: "技術概要：GLASS – LLM の推論時スパース化のための
+ *    グローバル・ローカル集約" -- rank aggregation of a local and a global
+ *    importance signal and top-k selection of a static FFN mask (section 2.2).
+ *  - Intra-expert summary: "Uncovering Intra-expert Activation Sparsity for
+ *    Efficient Mixture-of-Expert Model Execution" -- dense gate scoring,
+ *    masking, and gathered up/down projections inside routed experts, shared
+ *    experts and router unchanged (method section, system implementation).
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless stated otherwise, 16-byte aligned.
+ *    Tensors are row-major and contiguous.  The caller owns every buffer,
+ *    including the workspace; the library allocates nothing, never copies
+ *    between host and device and never synchronises: each call only enqueues
+ *    kernels on `stream` (0 = the default stream).
+ *  - Inputs are never written.  Outputs are fully overwritten unless
+ *    AS_FLAG_ACCUMULATE is set (then Y += result).
+ *  - Workspace: `ws` must hold at least the size returned by the matching
+ *    *_ws_size query and must be zero-filled before its first use (any zero
+ *    fill, or as_workspace_init).  Every call leaves the counters it uses at
+ *    zero again, so a workspace is reusable by later calls on the same stream.
+ *    Calls that may run concurrently need distinct workspaces.
+ *  - Errors: arguments are validated on the host before anything is enqueued
+ *    (AS_ERR_INVALID_ARG / AS_ERR_UNSUPPORTED / AS_ERR_WORKSPACE); a launch
+ *    failure returns AS_ERR_HIP.  as_last_error() gives the message of the last
+ *    failure on the calling thread.  Device faults surface at the caller's next
+ *    synchronisation.  NaN, Inf, all-masked and k = n inputs are defined
+ *    semantics, not errors.
+ *  - Determinism: for fixed inputs, sizes and flags every output is bitwise
+ *    reproducible (split-K partial sums are combined in a fixed order).
+ *  - Accumulation is fp32; bf16 x bf16 and fp16 x fp16 products are exact in fp32.
+ */
+#ifndef ACTSPARSE_H
+#define ACTSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AS_VERSION 100
+
+typedef enum {
+  AS_OK = 0,
+  AS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer          */
+  AS_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement         */
+  AS_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the size query    */
+  AS_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed          */
+} as_status;
+
+typedef enum { AS_F16 = 0, AS_BF16 = 1, AS_F32 = 2 } as_dtype;
+
+enum {
+  AS_FLAG_ACCUMULATE = 1u << 0,   /* Y += result instead of Y = result                   */
+  AS_FLAG_NO_NT_LOADS = 1u << 2,  /* plain (cached) weight loads instead of nontemporal  */
+  AS_FLAG_FORCE_DENSE = 1u << 3   /* ignore thresholds / neuron lists: dense baseline   */
+};
+
+/* Verification exports of a mask (every field may be NULL).
+   bits: [M, ceil(n/64)] uint64, bit i%64 of word i/64 set when element i is kept.
+   idx:  [M, n] int32, kept indices ascending; the first nnz[m] entries are valid.
+   nnz:  [M] int32. */
+typedef struct {
+  uint64_t *bits;
+  int32_t *idx;
+  int32_t *nnz;
+} as_mask_out;
+
+/* ------------------------------------------------------------------ library */
+int as_version(void);
+const char *as_status_string(as_status s);
+const char *as_last_error(void);
+/* Zero-fill `bytes` of device memory at `ws` with a kernel (no memset node). */
+as_status as_workspace_init(void *ws, size_t bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ calibration
+ * TEAL slides, method slide: the threshold t_p of a projection input is fixed
+ * from calibration data for the target sparsity p.  Reading: t is the
+ * nearest-rank order statistic of the pooled magnitudes:
+ *   *t_out = the rank-th smallest |pool[i]| (1-based), as fp32;
+ *   rank = 0 gives -INFINITY (sparsity 0 keeps every input).
+ * The caller computes rank = ceil(p * n).  NaN magnitudes order above +inf.
+ * pool: [n] of dtype dt (f16/bf16/f32).  t_out: one device float.
+ * Errors: INVALID_ARG if pool/t_out is NULL, n < 1, rank < 0 or rank > n. */
+as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64_t rank,
+                                 float *t_out, hipStream_t stream);
+
+/* ------------------------------------------------------------ threshold GEMV
+ * TEAL slides, slide 11: mask generation fused with the sparse product,
+ * loading only the weight rows whose input survives:
+ *   Y[m, :] = sum over i with |X[m, i]| > t of X[m, i] * W[i, :]
+ * X: [M, K] (f16/bf16/f32), 1 <= M <= 8.  W: [K, N] input-major (f16/bf16),
+ * N % 8 == 0.  Y: [M, N] (f16/bf16/f32).  t is compared in fp32 with strict
+ * '>': t = -INFINITY keeps every row; NaN inputs are dropped.  A weight row is
+ * read once for all M tokens if any token keeps it; each token still uses only
+ * its own kept inputs.
+ * mask_out (nullable): the per-token input masks (bits and nnz for any M,
+ * idx only for M == 1).
+ * AS_FLAG_FORCE_DENSE runs the dense baseline (every row, t ignored). */
+size_t as_threshold_gemv_ws_size(int M, int K, int N);
+as_status as_threshold_gemv(const void *X, as_dtype x_dt, int M, int K,
+                            const void *W, as_dtype w_dt, int N, float t,
+                            void *Y, as_dtype y_dt, unsigned flags, as_mask_out *mask_out,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dense GEMV baseline Y = X W over every row (the speedup denominator): the
+ * same kernel and launch shape as as_threshold_gemv without the mask. */
+as_status as_dense_gemv(const void *X, as_dtype x_dt, int M, int K,
+                        const void *W, as_dtype w_dt, int N,
+                        void *Y, as_dtype y_dt, unsigned flags,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ sparse SwiGLU MLP */
+typedef enum { AS_MLP_THRESHOLD = 0, AS_MLP_NEURON_SET = 1 } as_mlp_mode;
+
+typedef struct {
+  const void *w_gate_up;  /* THRESHOLD: [d_model, 2, d_ff] input-major (row i = gate row i
+                             then up row i).  NEURON_SET: [d_ff, 3, d_model] neuron-major
+                             (gate row, up row, down row of neuron j adjacent). */
+  const void *w_down;     /* THRESHOLD: [d_ff, d_model] input-major.  NEURON_SET: NULL. */
+  as_dtype w_dt;          /* AS_F16 or AS_BF16 */
+  int d_model;            /* multiple of 8 */
+  int d_ff;               /* multiple of 64 */
+} as_mlp_weights;
+
+typedef struct {
+  float *h;               /* THRESHOLD: [M, d_ff] fp32 intermediate silu(g)*u of every
+                             neuron.  NEURON_SET: [M, n_active] for the listed neurons. */
+  as_mask_out x_mask;     /* input mask |X| > t_x (THRESHOLD only; see as_threshold_gemv) */
+  as_mask_out h_mask;     /* |h| > t_h (THRESHOLD only): bits only, idx/nnz must be NULL */
+  hipEvent_t ev[3];       /* if non-NULL: recorded before stage 1, between the stages,
+                             and after stage 2 (per-kernel timing) */
+} as_mlp_debug;
+
+/* THRESHOLD (TEAL slides, method slide; every projection input thresholded):
+ *   x~ = X * [|X| > t_x];  g = x~ Wg;  u = x~ Wu;  h = silu(g) * u  (fp32)
+ *   Y = (h * [|h| > t_h]) Wd
+ * NEURON_SET (GLASS summary, section 2.2: a static top-k neuron mask applied
+ * through decode): the same SwiGLU restricted to neurons
+ * neuron_idx[0 .. n_active) (int32, device, ascending, distinct, < d_ff);
+ * t_x and t_h are ignored.
+ * X: [M, d_model] (f16/bf16/f32), 1 <= M <= 8; Y: [M, d_model].
+ * silu(z) = z / (1 + exp(-z)).  AS_FLAG_FORCE_DENSE: dense SwiGLU over all
+ * neurons and inputs (the baseline).  dbg is nullable. */
+size_t as_sparse_swiglu_mlp_ws_size(int M, const as_mlp_weights *w, as_mlp_mode mode);
+as_status as_sparse_swiglu_mlp(const void *X, as_dtype x_dt, int M, const as_mlp_weights *w,
+                               as_mlp_mode mode, float t_x, float t_h,
+                               const int32_t *neuron_idx, int n_active,
+                               void *Y, as_dtype y_dt, unsigned flags, as_mlp_debug *dbg,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ benchmark support
+ * Overwrite `bytes` of device memory at `buf` with a kernel, evicting the
+ * Infinity Cache and L2 between timed calls. */
+as_status as_bench_flush(void *buf, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ACTSPARSE_H */

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every declared symbol and validates arguments
+on the host (CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from activation_sparse_gemv_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "actsparse.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(as_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libactsparse.so is not built: run `python -m activation_sparse_gemv_amd.build`")
+    return L.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in actsparse.h but not exported"
+        assert n in L.SIGNATURES, f"{n} has no ctypes signature in the binding"
+    for n in L.SIGNATURES:
+        assert n in names, f"binding declares {n}, header does not"
+
+
+def test_version_and_strings(lib):
+    assert lib.as_version() == 100
+    assert lib.as_status_string(L.AS_ERR_WORKSPACE) == b"AS_ERR_WORKSPACE"
+
+
+def _p(v=4096):
+    return ctypes.c_void_p(v)
+
+
+def test_gemv_validation(lib):
+    st = lib.as_threshold_gemv(None, L.AS_BF16, 1, 64, _p(), L.AS_BF16, 64, 0.5, _p(), L.AS_F32, 0, None,
+                               None, 0, None)
+    assert st == L.AS_ERR_INVALID_ARG and b"NULL" in lib.as_last_error()
+    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 9, 64, _p(), L.AS_BF16, 64, 0.5, _p(), L.AS_F32, 0, None,
+                               None, 0, None)
+    assert st == L.AS_ERR_UNSUPPORTED
+    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 1, 64, _p(), L.AS_BF16, 60, 0.5, _p(), L.AS_F32, 0, None,
+                               None, 0, None)
+    assert st == L.AS_ERR_INVALID_ARG
+    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 1, 64, _p(4100), L.AS_BF16, 64, 0.5, _p(), L.AS_F32, 0, None,
+                               None, 0, None)
+    assert st == L.AS_ERR_INVALID_ARG and b"aligned" in lib.as_last_error()
+    st = lib.as_threshold_gemv(_p(), L.AS_F32, 1, 64, _p(), L.AS_F32, 64, 0.5, _p(), L.AS_F32, 0, None,
+                               None, 0, None)
+    assert st == L.AS_ERR_INVALID_ARG     # fp32 weights are not a supported storage type
+    need = lib.as_threshold_gemv_ws_size(1, 4096, 4096)
+    assert need > 0
+    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 1, 4096, _p(), L.AS_BF16, 4096, 0.5, _p(), L.AS_F32, 0, None,
+                               _p(), need - 1, None)
+    assert st == L.AS_ERR_WORKSPACE
+    st = lib.as_dense_gemv(_p(), L.AS_BF16, 1, 4096, _p(), L.AS_BF16, 4096, _p(), L.AS_F32, 0, None, 0, None)
+    assert st == L.AS_ERR_WORKSPACE
+
+
+def test_mlp_validation(lib):
+    w = L.ASMlpWeights(_p(), _p(), L.AS_BF16, 4096, 14336)
+    need = lib.as_sparse_swiglu_mlp_ws_size(1, ctypes.byref(w), L.AS_MLP_THRESHOLD)
+    assert need > 14336 * 4
+    st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(w), L.AS_MLP_THRESHOLD, 0.5, 0.5, None, 0,
+                                  _p(), L.AS_F32, 0, None, _p(), need - 16, None)
+    assert st == L.AS_ERR_WORKSPACE
+    bad = L.ASMlpWeights(_p(), _p(), L.AS_BF16, 4096, 14300)
+    st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(bad), L.AS_MLP_THRESHOLD, 0.5, 0.5, None, 0,
+                                  _p(), L.AS_F32, 0, None, _p(), 1 << 30, None)
+    assert st == L.AS_ERR_INVALID_ARG and b"d_ff" in lib.as_last_error()
+    nodown = L.ASMlpWeights(_p(), None, L.AS_BF16, 4096, 14336)
+    st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(nodown), L.AS_MLP_THRESHOLD, 0.5, 0.5, None,
+                                  0, _p(), L.AS_F32, 0, None, _p(), 1 << 30, None)
+    assert st == L.AS_ERR_INVALID_ARG
+    st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(nodown), L.AS_MLP_NEURON_SET, 0, 0, None,
+                                  5, _p(), L.AS_F32, 0, None, _p(), 1 << 30, None)
+    assert st == L.AS_ERR_INVALID_ARG and b"neuron_idx" in lib.as_last_error()
+    st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(nodown), L.AS_MLP_NEURON_SET, 0, 0, _p(),
+                                  20000, _p(), L.AS_F32, 0, None, _p(), 1 << 30, None)
+    assert st == L.AS_ERR_INVALID_ARG
+
+
+def test_calibrate_validation(lib):
+    assert lib.as_calibrate_threshold(None, L.AS_F32, 10, 5, _p(), None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 11, _p(), None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 0, 0, _p(), None) == L.AS_ERR_INVALID_ARG
+
+
+def test_workspace_init_and_flush_validation(lib):
+    assert lib.as_workspace_init(None, 64, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_workspace_init(None, 0, None) == L.AS_OK
+    assert lib.as_bench_flush(None, 64, None) == L.AS_ERR_INVALID_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from activation_sparse_gemv_amd import api
+    with pytest.raises(ValueError, match="device tensors"):
+        api.as_threshold_gemv(torch.zeros(64, dtype=torch.bfloat16), torch.zeros(64, 64, dtype=torch.bfloat16), 0.5)

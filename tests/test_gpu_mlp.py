@@ -1,0 +1,149 @@
+"""GPU parity of the sparse SwiGLU MLP (threshold and static neuron-set modes),
+checked stage by stage against the fp64 oracle (run on an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_gemv_amd as asg
+from activation_sparse_gemv_amd import _lib as L
+from activation_sparse_gemv_amd import datagen
+from oracle import teal, glass
+from helpers import TOL, f64, rel_err, bits_to_bool, announce
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+_CACHE = {}
+
+
+def _mlp(cfg, shape):
+    key = (cfg, shape)
+    if key not in _CACHE:
+        wgu, wd = datagen.mlp_weights_input_major(cfg, 0, shape)
+        _CACHE.clear()
+        _CACHE[key] = dict(wgu=wgu, wd=wd, Wg=f64(wgu[:, 0, :]), Wu=f64(wgu[:, 1, :]), Wd=f64(wd),
+                           dev=asg.MLPWeights(wgu.to(DEV), wd.to(DEV)))
+    return _CACHE[key]
+
+
+def _check_stagewise(x, w, t_x, t_h, M):
+    """Stage-wise parity: x mask exact; h within tolerance; h mask exact on the GPU's h;
+    y within tolerance of the oracle's down stage fed the GPU's h."""
+    y, dbg = asg.as_sparse_swiglu_mlp(x.to(DEV), w["dev"], t_x, t_h, debug=True)
+    X = f64(x)
+    d = X.shape[1]
+    f = w["Wg"].shape[1]
+    m1 = teal.magnitude_mask(X, t_x)
+    assert np.array_equal(bits_to_bool(dbg["x_mask"]["bits"], d), m1)
+    assert dbg["x_mask"]["nnz"].cpu().numpy().tolist() == m1.sum(axis=1).tolist()
+    r = teal.swiglu_mlp_threshold(X, w["Wg"], w["Wu"], w["Wd"], t_x, t_h)
+    h_gpu = f64(dbg["h"])
+    assert rel_err(h_gpu, r["h"]) < TOL
+    m2 = teal.magnitude_mask(h_gpu, t_h)
+    assert np.array_equal(bits_to_bool(dbg["h_mask"]["bits"], f), m2)
+    y_ref = teal.down_stage(h_gpu, w["Wd"], t_h)
+    err = rel_err(y, y_ref)
+    assert err < TOL, err
+    flips = int((m2 != r["m2"]).sum())
+    e2e = rel_err(y, r["y"])
+    if flips == 0:
+        assert e2e < TOL
+    return dict(err=err, e2e=e2e, flips=flips, sparsity_x=1 - m1.mean(), sparsity_h=1 - m2.mean())
+
+
+def test_mlp_small_fp16_workload():
+    """SwiGLU 512 -> 2048 -> 512, fp16 weights, Laplace inputs, 50% thresholds from 256
+    calibration vectors, 64 decode tokens one at a time and batched by 8."""
+    shape = datagen.CFG1
+    w = _mlp(1, shape)
+    calib = datagen.laplace((256, shape.d_model), datagen.seed_for(1, 0, "calib"), dtype="f16")
+    t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], 0.5, 0.5)
+    toks = datagen.laplace((64, shape.d_model), datagen.seed_for(1, 0, "decode"), dtype="f16")
+    for i in range(64):
+        announce(f"mlp small token {i}")
+        _check_stagewise(toks[i:i + 1], w, float(t_x), float(t_h), 1)
+    for b in range(0, 64, 8):
+        announce(f"mlp small batch {b}")
+        _check_stagewise(toks[b:b + 8], w, float(t_x), float(t_h), 8)
+
+
+@pytest.mark.parametrize("s", datagen.CFG2_SWEEP)
+def test_mlp_llama_sweep(s):
+    """Llama-3-8B-shaped MLP (4096 -> 14336 -> 4096, bf16), Student-t(3) inputs, thresholds
+    calibrated at sparsity s on both inputs, in the launch configuration the benchmark times."""
+    shape = datagen.CFG2
+    w = _mlp(2, shape)
+    calib = datagen.student_t((256, shape.d_model), datagen.seed_for(2, 0, "calib"))
+    t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], s, s)
+    toks = datagen.student_t((4, shape.d_model), datagen.seed_for(2, 0, "decode"))
+    for i in range(4):
+        announce(f"mlp llama s={s} token {i}")
+        r = _check_stagewise(toks[i:i + 1], w, float(t_x), float(t_h), 1)
+        print(r, flush=True)
+
+
+def test_mlp_dense_baseline_matches_dense_oracle():
+    announce("mlp dense baseline")
+    shape = datagen.CFG2
+    w = _mlp(2, shape)
+    x = datagen.student_t((1, shape.d_model), 77)
+    y = asg.as_sparse_swiglu_mlp(x.to(DEV), w["dev"], 5.0, 5.0, flags=L.AS_FLAG_FORCE_DENSE)
+    ref = teal.dense_mlp(f64(x), w["Wg"], w["Wu"], w["Wd"])
+    assert rel_err(y, ref) < TOL
+    # sparsity 0 (t = -inf on both inputs) computes the same function
+    y0 = asg.as_sparse_swiglu_mlp(x.to(DEV), w["dev"], float("-inf"), float("-inf"))
+    assert rel_err(y0, ref) < TOL
+
+
+def test_mlp_determinism_and_edges():
+    announce("mlp determinism")
+    shape = datagen.CFG1
+    w = _mlp(1, shape)
+    x = datagen.laplace((1, shape.d_model), 91, dtype="f16").to(DEV)
+    y1 = asg.as_sparse_swiglu_mlp(x, w["dev"], 0.7, 0.01)
+    y2 = asg.as_sparse_swiglu_mlp(x, w["dev"], 0.7, 0.01)
+    assert torch.equal(y1, y2)
+    # everything masked at the input: y == 0
+    y = asg.as_sparse_swiglu_mlp(x, w["dev"], 1e30, 0.0)
+    assert torch.count_nonzero(y).item() == 0
+    # everything masked at h: y == 0
+    y = asg.as_sparse_swiglu_mlp(x, w["dev"], 0.5, 1e30)
+    assert torch.count_nonzero(y).item() == 0
+
+
+def _neuron_major(d, f, seed):
+    W = datagen.mlp_weights_neuron_major(4, seed, d, f)
+    return W, f64(W[:, 0]), f64(W[:, 1]), f64(W[:, 2])
+
+
+@pytest.mark.parametrize("d,f,n_act,M", [(512, 2048, 1024, 1), (512, 2048, 777, 3), (4096, 14336, 7168, 1),
+                                         (4096, 14336, 1, 1), (4096, 14336, 0, 1)])
+def test_neuron_set_mlp(d, f, n_act, M):
+    announce(f"neuron-set d={d} f={f} n={n_act} M={M}")
+    W, Wg, Wu, Wd = _neuron_major(d, f, d + n_act)
+    rng = np.random.default_rng(n_act + 1)
+    idx = np.sort(rng.choice(f, size=n_act, replace=False)).astype(np.int32)
+    x = datagen.student_t((M, d), 55 + M)
+    w = asg.MLPWeights(W.to(DEV), None, L.AS_MLP_NEURON_SET)
+    y, dbg = asg.as_sparse_swiglu_mlp(x.to(DEV), w, neuron_idx=torch.from_numpy(idx).to(DEV), debug=True)
+    X = f64(x)
+    h_ref = teal.silu(X @ Wg[idx].T) * (X @ Wu[idx].T)
+    if n_act:
+        assert rel_err(f64(dbg["h"])[:, :n_act], h_ref) < TOL
+    ref = glass.neuron_set_mlp(X, Wg, Wu, Wd, idx)
+    assert rel_err(y, ref) < TOL
+    if n_act == 0:
+        assert torch.count_nonzero(y).item() == 0
+
+
+def test_neuron_set_full_equals_dense():
+    announce("neuron-set full")
+    d, f = 512, 2048
+    W, Wg, Wu, Wd = _neuron_major(d, f, 3)
+    x = datagen.student_t((1, d), 56)
+    w = asg.MLPWeights(W.to(DEV), None, L.AS_MLP_NEURON_SET)
+    y = asg.as_sparse_swiglu_mlp(x.to(DEV), w, flags=L.AS_FLAG_FORCE_DENSE)
+    ref = glass.neuron_set_mlp(f64(x), Wg, Wu, Wd, np.arange(f))
+    assert rel_err(y, ref) < TOL
+    y2 = asg.as_sparse_swiglu_mlp(x.to(DEV), w, neuron_idx=torch.arange(f, dtype=torch.int32, device=DEV))
+    assert rel_err(y2, ref) < TOL
