@@ -29,6 +29,11 @@ class ASMlpWeights(ctypes.Structure):
                 ("d_model", c_int), ("d_ff", c_int)]
 
 
+class ASMoeWeights(ctypes.Structure):
+    _fields_ = [("w_gate_up", c_void_p), ("w_down", c_void_p), ("w_dt", c_int), ("n_experts", c_int),
+                ("d_model", c_int), ("d_ff_e", c_int)]
+
+
 class ASMlpDebug(ctypes.Structure):
     _fields_ = [("h", c_void_p), ("x_mask", ASMaskOut), ("h_mask", ASMaskOut), ("ev", c_void_p * 3)]
 
@@ -49,6 +54,14 @@ SIGNATURES = {
     "as_sparse_swiglu_mlp": (c_int, [c_void_p, c_int, c_int, POINTER(ASMlpWeights), c_int, c_float, c_float,
                                      c_void_p, c_int, c_void_p, c_int, c_uint, POINTER(ASMlpDebug),
                                      c_void_p, c_size_t, c_void_p]),
+    "as_topk_mask_ws_size": (c_size_t, [c_int, c_int, c_int]),
+    "as_topk_mask": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
+                             c_void_p, c_size_t, c_void_p]),
+    "as_moe_router": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "as_sparse_moe_expert_ws_size": (c_size_t, [c_int, c_int, POINTER(ASMoeWeights)]),
+    "as_sparse_moe_expert": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, POINTER(ASMoeWeights),
+                                     c_int, c_void_p, c_int, c_uint, c_void_p, c_void_p, c_void_p, c_size_t,
+                                     c_void_p]),
     "as_bench_flush": (c_int, [c_void_p, c_size_t, c_void_p]),
 }
 

@@ -199,6 +199,101 @@ def as_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float = float("-in
     return (out, dd) if debug else out
 
 
+def as_topk_mask(score: torch.Tensor, k: int, prior: torch.Tensor | None = None, lam: float = 0.5,
+                 mode: int | None = None, want_mask: bool = True, want_idx: bool = True):
+    """Exact top-k per row (value mode, or the GLASS rank blend when ``prior`` is
+    given).  score/prior: [rows, n] or [n] fp32.  Returns (mask words, idx)."""
+    squeeze = score.dim() == 1
+    s2 = score.reshape(1, -1) if squeeze else score
+    p2 = None if prior is None else (prior.reshape(1, -1) if prior.dim() == 1 else prior)
+    if p2 is not None and p2.shape != s2.shape:
+        p2 = p2.expand_as(s2).contiguous()
+    _need_cuda(s2, p2)
+    if s2.dtype != torch.float32 or (p2 is not None and p2.dtype != torch.float32):
+        raise TypeError("scores must be float32")
+    rows, n = s2.shape
+    if mode is None:
+        mode = L.AS_TOPK_VALUE if p2 is None else L.AS_TOPK_RANK_BLEND
+    dev = s2.device
+    mask = torch.zeros((rows, (n + 63) // 64), dtype=torch.int64, device=dev) if want_mask else None
+    idx = torch.zeros((rows, k), dtype=torch.int32, device=dev) if want_idx else None
+    lib = L.load()
+    nb = lib.as_topk_mask_ws_size(rows, n, mode)
+    ws = workspace(("topk", rows, n, mode), nb, dev) if nb else None
+    L.check(lib.as_topk_mask(_ptr(s2), _ptr(p2), rows, n, k, mode, float(lam), _ptr(mask), _ptr(idx),
+                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)), "as_topk_mask")
+    if squeeze:
+        return (mask[0] if mask is not None else None), (idx[0] if idx is not None else None)
+    return mask, idx
+
+
+def as_moe_router(logits: torch.Tensor, top_k: int):
+    """logits [T, E] fp32 -> (ids [T, top_k] int32 in descending-logit order, weights [T, top_k])."""
+    _need_cuda(logits)
+    T, E = logits.shape
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    wts = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    L.check(L.load().as_moe_router(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(wts), _stream(logits.device)),
+            "as_moe_router")
+    return ids, wts
+
+
+@dataclass
+class MoEWeights:
+    """Routed experts (gate/up [E, d_ff_e, 2, d] neuron-major, down [E, d_ff_e, d]),
+    router [d, E] and the dense shared expert (input-major gate/up [d, 2, d_ff_s],
+    down [d_ff_s, d])."""
+    w_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    w_router: Optional[torch.Tensor] = None
+    shared: Optional[MLPWeights] = None
+
+    def struct(self) -> L.ASMoeWeights:
+        E, f, _, d = self.w_gate_up.shape
+        return L.ASMoeWeights(_ptr(self.w_gate_up), _ptr(self.w_down), _dt(self.w_gate_up), E, d, f)
+
+
+def as_sparse_moe_expert(X: torch.Tensor, w: MoEWeights, ids: torch.Tensor, wts: torch.Tensor, keep_k: int,
+                         y_dtype=torch.float32, flags: int = 0, Y: torch.Tensor | None = None, debug: bool = False):
+    """Routed experts with intra-expert top-k; Y (+)= sum_j wts[t,j] * expert_{ids[t,j]}(X[t])."""
+    _need_cuda(X, w.w_gate_up, w.w_down, ids, wts, Y)
+    T, d = X.shape
+    top = ids.shape[1]
+    E, f = w.w_gate_up.shape[0], w.w_gate_up.shape[1]
+    if Y is None:
+        Y = torch.empty((T, d), dtype=y_dtype, device=X.device)
+    lib = L.load()
+    st = w.struct()
+    nb = lib.as_sparse_moe_expert_ws_size(T, top, ctypes.byref(st))
+    ws = workspace(("moe", T, top, E, d, f), nb, X.device)
+    h = keep = None
+    if debug:
+        h = torch.zeros((T, top, f), dtype=torch.float32, device=X.device)
+        keep = torch.full((T, top, max(keep_k, 1)), -1, dtype=torch.int32, device=X.device)
+    L.check(lib.as_sparse_moe_expert(_ptr(X), _dt(X), T, _ptr(ids), _ptr(wts), top, ctypes.byref(st), keep_k,
+                                     _ptr(Y), _dt(Y), flags, _ptr(h), _ptr(keep), _ptr(ws), ws.numel(),
+                                     _stream(X.device)), "as_sparse_moe_expert")
+    return (Y, dict(h=h, keep=keep)) if debug else Y
+
+
+def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: int = 0, debug: bool = False):
+    """One MoE layer from the library's entry points: router logits (dense GEMV),
+    router top-k + softmax, the dense shared expert, then the routed experts
+    accumulated on top.  Returns Y [T, d] fp32 (and intermediates when debug)."""
+    T, d = X.shape
+    logits = torch.empty((T, w.w_router.shape[1]), dtype=torch.float32, device=X.device)
+    for t0 in range(0, T, 8):
+        as_dense_gemv(X[t0:t0 + 8], w.w_router, Y=logits[t0:t0 + 8])
+    ids, wts = as_moe_router(logits, top_k)
+    Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
+    for t0 in range(0, T, 8):
+        as_sparse_swiglu_mlp(X[t0:t0 + 8], w.shared, flags=L.AS_FLAG_FORCE_DENSE, Y=Y[t0:t0 + 8])
+    r = as_sparse_moe_expert(X, w, ids, wts, keep_k, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug)
+    if debug:
+        return Y, dict(logits=logits, ids=ids, wts=wts, **r[1])
+    return Y
+
+
 def as_bench_flush(buf: torch.Tensor):
     _need_cuda(buf)
     L.check(L.load().as_bench_flush(_ptr(buf), buf.numel() * buf.element_size(), _stream(buf.device)),

@@ -380,4 +380,97 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   return rec(2);
 }
 
+// ------------------------------------------------------------------ top-k
+size_t as_topk_mask_ws_size(int rows, int n, as_topk_mode mode) {
+  if (mode != AS_TOPK_RANK_BLEND || rows < 1 || n < 1) return 0;
+  return up256(size_t(rows) * 2 * n * sizeof(unsigned));
+}
+
+as_status as_topk_mask(const float* score, const float* prior, int rows, int n, int k, as_topk_mode mode,
+                       float lambda, uint64_t* mask, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "as_topk_mask";
+  if (!score) return fail(AS_ERR_INVALID_ARG, "%s: score is NULL", fn);
+  if (!mask && !idx) return fail(AS_ERR_INVALID_ARG, "%s: both outputs are NULL", fn);
+  if (rows < 1 || n < 1) return fail(AS_ERR_INVALID_ARG, "%s: rows=%d n=%d", fn, rows, n);
+  if (k < 0 || k > n) return fail(AS_ERR_INVALID_ARG, "%s: k=%d outside 0..n=%d", fn, k, n);
+  if (mode == AS_TOPK_VALUE) return hip_check(launch_topk_value(score, rows, n, k, mask, idx, stream), fn);
+  if (mode != AS_TOPK_RANK_BLEND) return fail(AS_ERR_INVALID_ARG, "%s: bad mode %d", fn, int(mode));
+  if (!prior) return fail(AS_ERR_INVALID_ARG, "%s: prior is NULL", fn);
+  if (!(lambda >= 0.f && lambda <= 1.f)) return fail(AS_ERR_INVALID_ARG, "%s: lambda=%g outside [0, 1]", fn, lambda);
+  if (n > 65535) return fail(AS_ERR_UNSUPPORTED, "%s: RANK_BLEND needs n <= 65535 (n=%d)", fn, n);
+  as_status st = check_ws(ws, ws_bytes, as_topk_mask_ws_size(rows, n, mode));
+  if (st != AS_OK) return st;
+  const uint32_t lq = (uint32_t)floor((double)lambda * 65536.0 + 0.5);
+  return hip_check(launch_topk_blend(score, prior, rows, n, k, lq, mask, idx, reinterpret_cast<unsigned*>(ws),
+                                     stream), fn);
+}
+
+// ------------------------------------------------------------------ MoE
+as_status as_moe_router(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
+                        hipStream_t stream) {
+  const char* fn = "as_moe_router";
+  if (!logits || !ids || !weights) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (T < 1 || E < 1 || E > 1024) return fail(AS_ERR_INVALID_ARG, "%s: T=%d E=%d", fn, T, E);
+  if (top_k < 1 || top_k > E || top_k > 64) return fail(AS_ERR_INVALID_ARG, "%s: top_k=%d", fn, top_k);
+  return hip_check(launch_router(logits, T, E, top_k, ids, weights, stream), fn);
+}
+
+namespace {
+struct MoeWs {
+  int* grp;
+  float* h;
+  float* partials;
+  unsigned* counters;
+};
+MoeWs carve_moe(Carver& c, int T, int top, const as_moe_weights* w) {
+  MoeWs m;
+  m.grp = c.take<int>(size_t(2 + 2 * w->n_experts + T * top));
+  m.h = c.take<float>(size_t(T) * top * w->d_ff_e);
+  m.partials = c.take<float>(size_t(T) * top * w->d_model);
+  m.counters = c.take<unsigned>(size_t(T) * moe_down_tiles(w->d_model));
+  return m;
+}
+}  // namespace
+
+size_t as_sparse_moe_expert_ws_size(int T, int top_k, const as_moe_weights* w) {
+  if (!w || T < 1 || top_k < 1 || w->n_experts < 1 || w->d_model < 1 || w->d_ff_e < 1) return 0;
+  Carver c{nullptr};
+  carve_moe(c, T, top_k, w);
+  return c.off;
+}
+
+as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_t* expert_ids,
+                               const float* expert_w, int top_k, const as_moe_weights* w, int keep_k, void* Y,
+                               as_dtype y_dt, unsigned flags, float* h_dbg, int32_t* keep_dbg, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "as_sparse_moe_expert";
+  if (!X || !expert_ids || !expert_w || !w || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!w->w_gate_up || !w->w_down) return fail(AS_ERR_INVALID_ARG, "%s: NULL weights", fn);
+  if (!is_dt(x_dt) || !is_dt(y_dt) || !is_wdt(w->w_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (T < 1 || top_k < 1 || top_k > 32 || T * top_k > 256)
+    return fail(AS_ERR_INVALID_ARG, "%s: T=%d top_k=%d (top_k <= 32, T*top_k <= 256)", fn, T, top_k);
+  if (w->n_experts < 1 || w->n_experts > 1024) return fail(AS_ERR_INVALID_ARG, "%s: E=%d", fn, w->n_experts);
+  if (w->d_model < 8 || w->d_model % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: d_model=%d", fn, w->d_model);
+  if (w->d_ff_e < 1) return fail(AS_ERR_INVALID_ARG, "%s: d_ff_e=%d", fn, w->d_ff_e);
+  if (keep_k < 0 || keep_k > w->d_ff_e) return fail(AS_ERR_INVALID_ARG, "%s: keep_k=%d", fn, keep_k);
+  if (!aligned16(w->w_gate_up) || !aligned16(w->w_down)) return fail(AS_ERR_INVALID_ARG, "%s: weights not 16-byte aligned", fn);
+  Carver c{reinterpret_cast<char*>(ws)};
+  MoeWs m = carve_moe(c, T, top_k, w);
+  as_status st = check_ws(ws, ws_bytes, c.off);
+  if (st != AS_OK) return st;
+  MoeParams p;
+  memset(&p, 0, sizeof p);
+  p.x = X; p.x_dt = int(x_dt); p.ldx = w->d_model; p.T = T; p.top = top_k; p.E = w->n_experts;
+  p.d_model = w->d_model; p.d_ff = w->d_ff_e;
+  p.keep_k = (flags & AS_FLAG_FORCE_DENSE) ? w->d_ff_e : keep_k;
+  p.ids = expert_ids; p.wts = expert_w;
+  p.w_gu = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.w_down = reinterpret_cast<const uint16_t*>(w->w_down);
+  p.grp = m.grp; p.h = m.h; p.h_dbg = h_dbg; p.keep_dbg = (flags & AS_FLAG_FORCE_DENSE) ? nullptr : keep_dbg;
+  p.partials = m.partials; p.counters = m.counters; p.n_tiles = moe_down_tiles(w->d_model);
+  p.y = Y; p.y_dt = int(y_dt); p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
+  p.neurons_per_block = env_int("AS_MOE_NPB", 16);
+  const int max_unique = T * top_k < w->n_experts ? T * top_k : w->n_experts;
+  return hip_check(launch_moe(int(w->w_dt), p, max_unique, stream), fn);
+}
+
 }  // extern "C"

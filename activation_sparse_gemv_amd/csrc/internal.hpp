@@ -59,6 +59,23 @@ struct NeuronGuParams {
 };
 hipError_t launch_neuron_gu(int wdt, int mt, bool nt, const NeuronGuParams& p, hipStream_t s);
 
+// Top-k masks.
+hipError_t launch_topk_value(const float* score, int rows, int n, int k, uint64_t* mask, int* idx, hipStream_t s);
+hipError_t launch_topk_blend(const float* score, const float* prior, int rows, int n, int k, uint32_t lq,
+                             uint64_t* mask, int* idx, unsigned* cnt, hipStream_t s);
+
+// Routed MoE experts with intra-expert top-k (see moe.hip).
+struct MoeParams {
+  const void* x; int x_dt; long ldx; int T; int top; int E; int d_model; int d_ff; int keep_k;
+  const int* ids; const float* wts;
+  const uint16_t* w_gu; const uint16_t* w_down;     // [E, d_ff, 2, d_model], [E, d_ff, d_model]
+  int* grp; float* h; float* h_dbg; int* keep_dbg; float* partials; unsigned* counters; int n_tiles;
+  void* y; int y_dt; int accumulate; int neurons_per_block;
+};
+hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s);
+hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s);
+int moe_down_tiles(int d_model);
+
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);

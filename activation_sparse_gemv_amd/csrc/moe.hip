@@ -1,0 +1,312 @@
+// Routed MoE experts with intra-expert activation sparsity.
+//
+// Intra-expert summary, system implementation: the router and the shared
+// expert are kept as they are; inside each routed expert the gate projection is
+// run densely to score the neurons, the low-scoring neurons are masked, and the
+// remaining neurons' weights are gathered for the rest of the expert.  Here the
+// score of neuron n is |silu(g_n) * u_n| (gate and up dense), the keep_k best
+// neurons (ties to the smaller index) reach the down projection, and only their
+// down rows (one contiguous d_model row each) are read.
+//
+// Kernels (one call):
+//   group:   one workgroup sorts the (token, slot) assignments by expert, so the
+//            weights of an expert are read once for all tokens routed to it;
+//   gate/up: (touched expert, neuron block) workgroups; one wave per neuron
+//            computes both dot products for up to 4 tokens at a time;
+//   down:    (token, slot, column tile) workgroups: exact top-k of |h|, gathered
+//            down rows, weight w_tj; the last slot to finish a (token, tile)
+//            sums the slots in slot order into Y (deterministic).
+#include "topk.hpp"
+#include "internal.hpp"
+
+namespace as {
+
+// ---------------------------------------------------------------- router
+constexpr int kRouterThreads = 128;
+
+__global__ __launch_bounds__(kRouterThreads) void router_kernel(const float* logits, int E, int top, int* ids,
+                                                                float* wts) {
+  __shared__ TopkSmem sm;
+  __shared__ int sel[64];
+  const long t = blockIdx.x;
+  const float* z = logits + t * E;
+  block_topk<kRouterThreads>([=](int i) { return float_key(z[i]); }, E, top, nullptr, sel, sm);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // order the selection by (logit desc, index asc), then softmax over it
+    for (int a = 1; a < top; ++a) {
+      const int v = sel[a];
+      const uint32_t kv = float_key(z[v]);
+      int b = a - 1;
+      while (b >= 0 && (float_key(z[sel[b]]) < kv || (float_key(z[sel[b]]) == kv && sel[b] > v))) {
+        sel[b + 1] = sel[b];
+        --b;
+      }
+      sel[b + 1] = v;
+    }
+    const float zmax = z[sel[0]];
+    float sum = 0.f;
+    for (int a = 0; a < top; ++a) sum += expf(z[sel[a]] - zmax);
+    for (int a = 0; a < top; ++a) {
+      ids[t * top + a] = sel[a];
+      wts[t * top + a] = expf(z[sel[a]] - zmax) / sum;
+    }
+  }
+}
+
+hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s) {
+  hipLaunchKernelGGL(router_kernel, dim3(T), dim3(kRouterThreads), 0, s, logits, E, top, ids, wts);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- grouping
+// Counting sort of the (token, slot) items by expert, in one workgroup.
+// grp[0] = number of touched experts U; grp[1 .. 1+U) = their ids ascending;
+// grp[1+E .. 1+E+U] = start offsets; grp[2+2E ..) = items (t*top + j), grouped
+// by expert, ascending within a group.  Items with an id outside [0, E) are
+// dropped (they contribute nothing).
+constexpr int kGrpThreads = 256;
+
+__global__ __launch_bounds__(kGrpThreads) void group_kernel(const int* ids, int n_items, int E, int* grp) {
+  __shared__ int s_ids[kGrpThreads];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1024];
+  __shared__ int s_scan[kGrpThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kGrpThreads) s_cnt[e] = 0;
+  int my = -1;
+  if (tid < n_items) {
+    my = ids[tid];
+    if (my < 0 || my >= E) my = -1;
+  }
+  s_ids[tid] = my;
+  __syncthreads();
+  if (my >= 0) atomicAdd(&s_cnt[my], 1);
+  __syncthreads();
+  // exclusive scans over experts: item offsets and touched-expert ranks
+  const int per = (E + kGrpThreads - 1) / kGrpThreads;
+  int c_items = 0, c_touch = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) { c_items += s_cnt[e]; c_touch += s_cnt[e] > 0; }
+  }
+  int tot_items, tot_touch;
+  int off_items = block_excl_scan<kGrpThreads>(c_items, s_scan, &tot_items);
+  int off_touch = block_excl_scan<kGrpThreads>(c_touch, s_scan, &tot_touch);
+  int* uexp = grp + 1;
+  int* start = grp + 1 + E;
+  int* items = grp + 2 + 2 * E;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      s_off[e] = off_items;
+      if (s_cnt[e] > 0) {
+        uexp[off_touch] = e;
+        start[off_touch] = off_items;
+        ++off_touch;
+      }
+      off_items += s_cnt[e];
+    }
+  }
+  if (tid == 0) {
+    grp[0] = tot_touch;
+    start[tot_touch] = tot_items;
+  }
+  __syncthreads();
+  if (my >= 0) {
+    int before = 0;
+    for (int q = 0; q < tid; ++q) before += s_ids[q] == my;
+    items[s_off[my] + before] = tid;
+  }
+}
+
+// ---------------------------------------------------------------- gate / up
+constexpr int kGuThreads = 256;
+constexpr int kGuTok = 4;   // tokens per pass
+
+template <int WDT>
+__global__ __launch_bounds__(kGuThreads) void expert_gu_kernel(const MoeParams p) {
+  extern __shared__ __align__(16) float xs[];   // [kGuTok][d]
+  const int u = blockIdx.x;
+  const int* grp = p.grp;
+  if (u >= grp[0]) return;
+  const int E = p.E, d = p.d_model, f = p.d_ff;
+  const int e = grp[1 + u];
+  const int st = grp[1 + E + u], en = grp[1 + E + u + 1];
+  const int* items = grp + 2 + 2 * E;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.y * p.neurons_per_block;
+  const int n1 = min(n0 + p.neurons_per_block, f);
+  const uint16_t* W = p.w_gu + (long)e * f * 2 * d;
+  for (int g0 = st; g0 < en; g0 += kGuTok) {
+    const int ng = min(kGuTok, en - g0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kGuTok * d; i += kGuThreads) {
+      const int m = i / d, c = i % d;
+      float v = 0.f;
+      if (m < ng) v = load_elem(p.x, p.x_dt, (long)(items[g0 + m] / p.top) * p.ldx + c);
+      xs[i] = v;
+    }
+    __syncthreads();
+    for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
+      const uint16_t* wg = W + (long)n * 2 * d;
+      const uint16_t* wu = wg + d;
+      float g[kGuTok], uu[kGuTok];
+#pragma unroll
+      for (int m = 0; m < kGuTok; ++m) { g[m] = 0.f; uu[m] = 0.f; }
+      for (int c0 = lane * 8; c0 < d; c0 += 64 * 8 * 4) {
+        u32x4 vg[4], vu[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = min(c0 + k * 512, d - 8);
+          vg[k] = load_w16(wg + c, true);
+          vu[k] = load_w16(wu + c, true);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = c0 + k * 512;
+          if (c < d) {
+            float fg[8], fu[8];
+            unpack8<WDT>(vg[k], fg);
+            unpack8<WDT>(vu[k], fu);
+#pragma unroll
+            for (int m = 0; m < kGuTok; ++m) {
+              const float4 xa = *reinterpret_cast<const float4*>(xs + m * d + c);
+              const float4 xb = *reinterpret_cast<const float4*>(xs + m * d + c + 4);
+              const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                g[m] = fmaf(xv[q], fg[q], g[m]);
+                uu[m] = fmaf(xv[q], fu[q], uu[m]);
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < kGuTok; ++m) {
+        const float gs = wave_sum(g[m]);
+        const float us = wave_sum(uu[m]);
+        if (lane == 0 && m < ng) {
+          const int it = items[g0 + m];
+          const float h = silu_f32(gs) * us;
+          p.h[(long)it * f + n] = h;
+          if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down
+constexpr int kDnThreads = 256;
+constexpr int kDnLpr = 64;                 // one wave covers 512 columns of one row
+constexpr int kDnTile = kDnLpr * 8;
+
+template <int WDT>
+__global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* keep = reinterpret_cast<int*>(smem);                        // [keep_k]
+  float* kval = reinterpret_cast<float*>(smem + 4 * ((p.keep_k + 3) & ~3));
+  float* red = kval + ((p.keep_k + 3) & ~3);                       // [4][kDnTile]
+  __shared__ TopkSmem sm;
+  __shared__ int s_last;
+  const int item = blockIdx.x;                  // t * top + j
+  const int tile = blockIdx.y;
+  const int t = item / p.top, j = item % p.top;
+  const int f = p.d_ff, d = p.d_model;
+  int e = p.ids[item];
+  const bool valid_e = e >= 0 && e < p.E;
+  if (!valid_e) e = 0;
+  const float* h = p.h + (long)item * f;
+  const int kk = valid_e ? p.keep_k : 0;
+  block_topk<kDnThreads>([=](int i) { return float_key(fabsf(h[i])); }, f, kk, nullptr, keep, sm);
+  __syncthreads();
+  for (int r = threadIdx.x; r < kk; r += kDnThreads) kval[r] = h[keep[r]];
+  if (p.keep_dbg != nullptr && tile == 0)
+    for (int r = threadIdx.x; r < p.keep_k; r += kDnThreads) p.keep_dbg[(long)item * p.keep_k + r] = kk ? keep[r] : -1;
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = tile * kDnTile + lane * 8;
+  const bool cvalid = c0 < d;
+  const uint16_t* Wd = p.w_down + (long)e * f * d + (cvalid ? c0 : 0);
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  constexpr int U = 8;
+  for (int r = wave; r < kk; r += 4 * U) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = load_w16(Wd + (long)keep[min(r + 4 * u, kk - 1)] * d, true);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rr = r + 4 * u;
+      const float hv = rr < kk ? kval[rr] : 0.f;
+      float wf[8];
+      unpack8<WDT>(w[u], wf);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(hv, wf[q], acc[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[wave * kDnTile + lane * 8 + q] = acc[q];
+  __syncthreads();
+  const float wt = valid_e ? p.wts[item] : 0.f;
+  // partial of this (token, slot): w_tj * sum over kept neurons, coherent store
+  for (int c = threadIdx.x; c < kDnTile; c += kDnThreads) {
+    const int gc = tile * kDnTile + c;
+    if (gc < d) {
+      const float v = red[c] + red[kDnTile + c] + red[2 * kDnTile + c] + red[3 * kDnTile + c];
+      store_coherent(p.partials + (long)item * d + gc, wt * v);
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = p.counters + (long)t * p.n_tiles + tile;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == unsigned(p.top - 1);
+    if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  (void)j;
+  for (int c = threadIdx.x; c < kDnTile; c += kDnThreads) {
+    const int gc = tile * kDnTile + c;
+    if (gc < d) {
+      float tmp[32];
+      const int top = p.top;
+#pragma unroll
+      for (int q = 0; q < 32; ++q)
+        tmp[q] = q < top ? load_coherent(p.partials + ((long)t * top + q) * d + gc) : 0.f;
+      float v = 0.f;
+      for (int q = 0; q < top; ++q) v += tmp[q];
+      if (p.accumulate) v += load_elem(p.y, p.y_dt, (long)t * d + gc);
+      store_elem(p.y, p.y_dt, (long)t * d + gc, v);
+    }
+  }
+}
+
+hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s) {
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGrpThreads), 0, s, p.ids, p.T * p.top, p.E, p.grp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nblk = (p.d_ff + p.neurons_per_block - 1) / p.neurons_per_block;
+  const size_t sm1 = size_t(kGuTok) * p.d_model * 4;
+  auto k1 = wdt == DT_BF16 ? expert_gu_kernel<DT_BF16> : expert_gu_kernel<DT_F16>;
+  if (sm1 > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, int(sm1));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k1, dim3(max_unique, nblk), dim3(kGuThreads), sm1, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t sm2 = size_t(8) * ((p.keep_k + 3) & ~3) + size_t(4) * kDnTile * 4;
+  auto k2 = wdt == DT_BF16 ? expert_down_kernel<DT_BF16> : expert_down_kernel<DT_F16>;
+  hipLaunchKernelGGL(k2, dim3(p.T * p.top, p.n_tiles), dim3(kDnThreads), sm2, s, p);
+  return hipGetLastError();
+}
+
+int moe_down_tiles(int d_model) { return (d_model + kDnTile - 1) / kDnTile; }
+
+}  // namespace as

@@ -1,0 +1,118 @@
+// Exact top-k selection with index tie-break, as a workgroup-level device routine.
+//
+// GLASS summary, section 2.2 (selection): the k neurons with the highest score
+// form the mask.  Intra-expert summary, method section: the lowest-scoring
+// neurons of a routed expert are skipped.  Both need an exact order statistic:
+// here every score is mapped to an order-preserving 32-bit key, an MSB-first
+// radix select over four 8-bit digits (LDS histogram) finds the k-th largest key
+// T and how many keys equal to T must be taken, and a final pass in index order
+// keeps every key above T plus the first such keys equal to T, so ties go to the
+// smaller index.  Output: an ascending index list and a 64-bit-word bitmask.
+#pragma once
+#include "common.hpp"
+
+namespace as {
+
+// Order-preserving key of a float: larger value -> larger key; -0.0 == +0.0;
+// NaN maps to 0, below every number (-inf maps to 0x007fffff).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  if (f != f) return 0u;
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct TopkSmem {
+  unsigned hist[256];
+  int wave_cnt[32];
+  uint32_t prefix;
+  int krem;
+  int run_eq, run_sel;
+};
+
+// Select the k largest of n keys (key(i) for i < n), ties to the smaller index.
+// NT threads (multiple of 64, <= 1024).  Writes idx[0..k) ascending (if idx) and
+// ceil(n/64) mask words (if mask).  Every thread of the workgroup must call it.
+template <int NT, class KeyFn>
+__device__ void block_topk(KeyFn key, int n, int k, uint64_t* mask, int* idx, TopkSmem& sm) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (k > n) k = n;
+  uint32_t T = 0u;
+  int take_eq = 0;
+  bool all = k >= n, none = k <= 0;
+  if (!all && !none) {
+    if (tid == 0) { sm.prefix = 0u; sm.krem = k; }
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+      for (int b = tid; b < 256; b += NT) sm.hist[b] = 0u;
+      __syncthreads();
+      const uint32_t prefix = sm.prefix;
+      for (int i = tid; i < n; i += NT) {
+        const uint32_t kk = key(i);
+        if ((kk & hi_mask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & 0xffu], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int krem = sm.krem;
+        int b = 255;
+        for (; b > 0; --b) {
+          if ((int)sm.hist[b] >= krem) break;
+          krem -= (int)sm.hist[b];
+        }
+        sm.prefix = prefix | ((uint32_t)b << shift);
+        sm.krem = krem;
+      }
+      __syncthreads();
+    }
+    T = sm.prefix;
+    take_eq = sm.krem;
+  }
+  if (tid == 0) { sm.run_eq = 0; sm.run_sel = 0; }
+  __syncthreads();
+  for (int base = 0; base < n; base += NT) {
+    const int i = base + tid;
+    bool sel = false, eq = false;
+    if (i < n) {
+      if (all) sel = true;
+      else if (!none) {
+        const uint32_t kk = key(i);
+        sel = kk > T;
+        eq = kk == T;
+      }
+    }
+    // rank of this key among the keys equal to T, in index order
+    const uint64_t eqb = __ballot(eq);
+    if (lane == 0) sm.wave_cnt[w] = __popcll(eqb);
+    __syncthreads();
+    int eq_before = sm.run_eq;
+    for (int v = 0; v < w; ++v) eq_before += sm.wave_cnt[v];
+    eq_before += lanes_below(eqb);
+    if (eq && eq_before < take_eq) sel = true;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int v = 0; v < NW; ++v) tot += sm.wave_cnt[v];
+      sm.run_eq += tot;
+    }
+    const uint64_t sb = __ballot(sel);
+    if (mask != nullptr && lane == 0 && (base + w * 64) < n) mask[(base + w * 64) >> 6] = sb;
+    __syncthreads();
+    if (lane == 0) sm.wave_cnt[w] = __popcll(sb);
+    __syncthreads();
+    int pos = sm.run_sel;
+    for (int v = 0; v < w; ++v) pos += sm.wave_cnt[v];
+    pos += lanes_below(sb);
+    if (sel && idx != nullptr) idx[pos] = i;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int v = 0; v < NW; ++v) tot += sm.wave_cnt[v];
+      sm.run_sel += tot;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace as

@@ -166,6 +166,72 @@ as_status as_sparse_swiglu_mlp(const void *X, as_dtype x_dt, int M, const as_mlp
                                void *Y, as_dtype y_dt, unsigned flags, as_mlp_debug *dbg,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------ top-k neuron masks */
+typedef enum { AS_TOPK_VALUE = 0, AS_TOPK_RANK_BLEND = 1 } as_topk_mode;
+
+/* Exact top-k per row, ties broken by index (the smaller index wins).
+ * VALUE (intra-expert summary, method section: the lowest-scoring neurons are
+ * skipped; GLASS summary, section 2.2: the top-k neurons form the mask): the k
+ * largest score[r, :], comparing -0.0 == +0.0, NaN below every number.
+ * RANK_BLEND (GLASS summary, section 2.2: GLASS_j = (1 - lambda) R^(l)_j +
+ * lambda R^(g)_j): ordinal ranks R^(l) of score[r, :] and R^(g) of prior[r, :]
+ * (largest value -> n; equal values: the smaller index ranks higher), blended in
+ * 16-bit fixed point, S_j = (65536 - lq) R^(l)_j + lq R^(g)_j with
+ * lq = floor(lambda * 65536 + 0.5), then the k largest S.
+ * score, prior: [rows, n] fp32 (prior only for RANK_BLEND, else may be NULL).
+ * Outputs (either may be NULL, not both): mask [rows, ceil(n/64)] uint64 (bit
+ * i%64 of word i/64 = kept), idx [rows, k] int32 ascending.
+ * Errors: INVALID_ARG for k < 0, k > n, n < 1, rows < 1, lambda outside [0, 1];
+ * UNSUPPORTED for RANK_BLEND with n > 65535.  VALUE needs no workspace. */
+size_t as_topk_mask_ws_size(int rows, int n, as_topk_mode mode);
+as_status as_topk_mask(const float *score, const float *prior, int rows, int n, int k,
+                       as_topk_mode mode, float lambda, uint64_t *mask, int32_t *idx,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------ MoE: router and routed experts */
+typedef struct {
+  const void *w_gate_up;  /* [E, d_ff_e, 2, d_model] neuron-major: gate row then up row of
+                             every neuron of every expert, contiguous */
+  const void *w_down;     /* [E, d_ff_e, d_model]: row n = neuron n's output weights */
+  as_dtype w_dt;          /* AS_F16 or AS_BF16 */
+  int n_experts;          /* E, 1..1024 */
+  int d_model;            /* multiple of 8 */
+  int d_ff_e;             /* neurons per expert */
+} as_moe_weights;
+
+/* Router (intra-expert summary, method section: routed experts are chosen by the
+ * router, whose logic is unchanged).  Reading: per token t, the top_k experts
+ * with the largest logits[t, :] (ties to the smaller index), in descending
+ * logit order, weights = softmax over the selected logits.
+ * logits: [T, E] fp32.  ids: [T, top_k] int32.  weights: [T, top_k] fp32.
+ * Errors: INVALID_ARG for T < 1, E < 1 or > 1024, top_k < 1 or > min(E, 64). */
+as_status as_moe_router(const float *logits, int T, int E, int top_k,
+                        int32_t *ids, float *weights, hipStream_t stream);
+
+/* Routed experts with intra-expert activation sparsity (intra-expert summary,
+ * system implementation: dense gate scoring, low-scoring neurons masked, only
+ * the active neurons' weights gathered):
+ *   Y[t, :] (+)= sum_j expert_w[t, j] * y_{t,j},
+ *   y_{t,j} = sum over n in keep(t, j) of h_n * Wd_e[n, :],   e = expert_ids[t, j],
+ *   h = silu(x_t Wg_e^T) * (x_t Wu_e^T) over all d_ff_e neurons (fp32),
+ *   keep(t, j) = the keep_k neurons with the largest |h_n| (ties to the smaller n).
+ * X: [T, d_model] (f16/bf16/f32); expert_ids [T, top_k] int32 (ids outside
+ * [0, E) contribute nothing); expert_w [T, top_k] fp32; Y [T, d_model].
+ * Gate/up weights of an expert are read once per call for all tokens routed to
+ * it.  Shared experts are not part of this call (run them densely and combine
+ * with AS_FLAG_ACCUMULATE).  AS_FLAG_FORCE_DENSE keeps every neuron.
+ * Debug exports (nullable): h_dbg [T, top_k, d_ff_e] fp32, keep_dbg
+ * [T, top_k, keep_k] int32 ascending.
+ * Errors: INVALID_ARG for T < 1, top_k < 1 or > 32, T * top_k > 256,
+ * keep_k < 0 or > d_ff_e. */
+size_t as_sparse_moe_expert_ws_size(int T, int top_k, const as_moe_weights *w);
+as_status as_sparse_moe_expert(const void *X, as_dtype x_dt, int T,
+                               const int32_t *expert_ids, const float *expert_w, int top_k,
+                               const as_moe_weights *w, int keep_k,
+                               void *Y, as_dtype y_dt, unsigned flags,
+                               float *h_dbg, int32_t *keep_dbg,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ benchmark support
  * Overwrite `bytes` of device memory at `buf` with a kernel, evicting the
  * Infinity Cache and L2 between timed calls. */

@@ -1,0 +1,113 @@
+"""GPU parity of the MoE router and the routed experts with intra-expert top-k,
+checked stage by stage against the fp64 oracle (run on an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_gemv_amd as asg
+from activation_sparse_gemv_amd import _lib as L
+from activation_sparse_gemv_amd import datagen
+from oracle import moe, teal, topk
+from helpers import TOL, f64, rel_err, announce
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+_W = {}
+
+
+def _weights(E, d, f, fs):
+    key = (E, d, f, fs)
+    if key not in _W:
+        _W.clear()
+        w = datagen.moe_weights(5, 0, n_experts=E, d_model=d, d_ff_e=f, d_ff_shared=fs)
+        dw = asg.MoEWeights(w["w_gate_up"].to(DEV), w["w_down"].to(DEV), w["w_router"].to(DEV),
+                            asg.MLPWeights(w["s_gate_up"].to(DEV), w["s_down"].to(DEV)))
+        _W[key] = (w, dw)
+    return _W[key]
+
+
+def _check_layer(E, d, f, fs, T, top, keep, seed):
+    w, dw = _weights(E, d, f, fs)
+    X = datagen.student_t((T, d), seed)
+    Y, dbg = asg.moe_layer(X.to(DEV), dw, top, keep, debug=True)
+    Xd = f64(X)
+    Wr = f64(w["w_router"])
+    # router: GPU logits within tolerance; selection and weights from the GPU's logits
+    lg = f64(dbg["logits"])
+    assert rel_err(lg, Xd @ Wr) < TOL
+    ids = dbg["ids"].cpu().numpy()
+    wts = f64(dbg["wts"])
+    for t in range(T):
+        sel = topk.value_topk(lg[t], top)
+        order = sel[np.lexsort((sel, -lg[t][sel]))]
+        assert ids[t].tolist() == order.tolist()
+        z = lg[t][order]
+        p = np.exp(z - z.max())
+        np.testing.assert_allclose(wts[t], p / p.sum(), rtol=1e-5, atol=1e-7)
+    # routed experts, stage by stage
+    h = f64(dbg["h"])
+    kp = dbg["keep"].cpu().numpy()
+    sgu = f64(w["s_gate_up"])
+    y_ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(top):
+            e = int(ids[t, j])
+            Wgu = f64(w["w_gate_up"][e])
+            Wd = f64(w["w_down"][e])
+            h_ref = teal.silu(Wgu[:, 0, :] @ Xd[t]) * (Wgu[:, 1, :] @ Xd[t])
+            assert rel_err(h[t, j], h_ref) < TOL
+            kidx = topk.value_topk(np.abs(h[t, j]), keep)            # exact on the GPU's h
+            assert kp[t, j, :keep].tolist() == kidx.tolist()
+            y_ref[t] += wts[t, j] * (h[t, j][kidx] @ Wd[kidx])
+        y_ref[t] += teal.dense_mlp(Xd[t], sgu[:, 0, :], sgu[:, 1, :], f64(w["s_down"]))
+    err = rel_err(Y, y_ref)
+    assert err < TOL, err
+    return ids
+
+
+def test_moe_small_all_token_counts():
+    for T in (1, 3, 8, 16):
+        announce(f"moe small T={T}")
+        _check_layer(8, 64, 48, 128, T, 2, 5, 100 + T)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_moe_workload(T):
+    """128 experts, d_model 2048, d_ff_e 768, top-8 routing, keep the top 10% (77) of each
+    routed expert's neurons, dense shared expert with d_ff 4096."""
+    announce(f"moe workload T={T}")
+    c = datagen.CFG5
+    _check_layer(c["n_experts"], c["d_model"], c["d_ff_e"], c["d_ff_shared"], T, c["top"], c["keep"],
+                 datagen.seed_for(5, T, "decode"))
+
+
+def test_moe_keep_all_is_dense_moe():
+    announce("moe keep-all")
+    E, d, f, fs, T, top = 8, 64, 48, 128, 4, 2
+    w, dw = _weights(E, d, f, fs)
+    X = datagen.student_t((T, d), 7)
+    Y = asg.moe_layer(X.to(DEV), dw, top, f)
+    ref, _ = moe.moe_layer(f64(X), {k: f64(v) for k, v in w.items()}, top, f)
+    assert rel_err(Y, ref) < TOL
+    Y2 = asg.moe_layer(X.to(DEV), dw, top, 3, flags=L.AS_FLAG_FORCE_DENSE)
+    assert rel_err(Y2, ref) < TOL
+
+
+def test_moe_invalid_ids_and_determinism():
+    announce("moe invalid ids")
+    E, d, f, fs = 8, 64, 48, 128
+    w, dw = _weights(E, d, f, fs)
+    X = datagen.student_t((2, d), 8).to(DEV)
+    ids = torch.tensor([[1, -1], [E, 3]], dtype=torch.int32, device=DEV)
+    wts = torch.tensor([[0.5, 0.5], [0.25, 0.75]], dtype=torch.float32, device=DEV)
+    Y, dbg = asg.as_sparse_moe_expert(X, dw, ids, wts, 5, debug=True)
+    h = f64(dbg["h"])
+    ref = np.zeros((2, d))
+    for t, j, e, wt in ((0, 0, 1, 0.5), (1, 1, 3, 0.75)):
+        kidx = topk.value_topk(np.abs(h[t, j]), 5)
+        assert dbg["keep"][t, j].cpu().numpy().tolist() == kidx.tolist()
+        ref[t] = wt * (h[t, j][kidx] @ f64(w["w_down"][e])[kidx])
+    assert rel_err(Y, ref) < TOL
+    assert dbg["keep"][0, 1].cpu().numpy().tolist() == [-1] * 5      # invalid expert: nothing kept
+    Y2 = asg.as_sparse_moe_expert(X, dw, ids, wts, 5)
+    assert torch.equal(Y, Y2)
