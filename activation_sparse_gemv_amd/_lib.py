@@ -34,6 +34,20 @@ class ASMoeWeights(ctypes.Structure):
                 ("d_model", c_int), ("d_ff_e", c_int)]
 
 
+class ASBlockWeights(ctypes.Structure):
+    _fields_ = [("w_qkv", c_void_p), ("w_o", c_void_p), ("mlp", ASMlpWeights), ("n_q", c_int), ("n_kv", c_int),
+                ("head_dim", c_int)]
+
+
+class ASBlockThresholds(ctypes.Structure):
+    _fields_ = [("qkv", c_float), ("o", c_float), ("gate_up", c_float), ("down", c_float)]
+
+
+class ASBlockDebug(ctypes.Structure):
+    _fields_ = [("xn", c_void_p), ("qkv", c_void_p), ("o", c_void_p), ("h1", c_void_p), ("xn2", c_void_p),
+                ("h", c_void_p)]
+
+
 class ASMlpDebug(ctypes.Structure):
     _fields_ = [("h", c_void_p), ("x_mask", ASMaskOut), ("h_mask", ASMaskOut), ("ev", c_void_p * 3)]
 
@@ -62,6 +76,14 @@ SIGNATURES = {
     "as_sparse_moe_expert": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, POINTER(ASMoeWeights),
                                      c_int, c_void_p, c_int, c_uint, c_void_p, c_void_p, c_void_p, c_size_t,
                                      c_void_p]),
+    "as_rmsnorm": (c_int, [c_void_p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p]),
+    "as_gqa_decode_attention_ws_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "as_gqa_decode_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                                        c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "as_decoder_block_ws_size": (c_size_t, [POINTER(ASBlockWeights), c_int]),
+    "as_decoder_block": (c_int, [c_void_p, c_int, POINTER(ASBlockWeights), c_void_p, c_void_p, c_int,
+                                 POINTER(ASBlockThresholds), c_void_p, c_uint, POINTER(ASBlockDebug), c_void_p,
+                                 c_size_t, c_void_p]),
     "as_bench_flush": (c_int, [c_void_p, c_size_t, c_void_p]),
 }
 

@@ -294,6 +294,76 @@ def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: in
     return Y
 
 
+def as_rmsnorm(X: torch.Tensor, eps: float = 1e-5, copy: bool = False):
+    X2 = X.reshape(1, -1) if X.dim() == 1 else X
+    _need_cuda(X2)
+    rows, d = X2.shape
+    Y = torch.empty((rows, d), dtype=torch.float32, device=X.device)
+    C = torch.empty((rows, d), dtype=torch.float32, device=X.device) if copy else None
+    L.check(L.load().as_rmsnorm(_ptr(X2), _dt(X2), rows, d, float(eps), _ptr(Y), _ptr(C), _stream(X.device)),
+            "as_rmsnorm")
+    Y = Y.reshape(X.shape)
+    return (Y, C.reshape(X.shape)) if copy else Y
+
+
+def as_gqa_decode_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor):
+    """q [n_q, hd] fp32, k_new/v_new [n_kv, hd] fp32, caches [n_ctx, n_kv, hd] bf16 -> o [n_q, hd]."""
+    _need_cuda(q, k_new, v_new, k_cache, v_cache)
+    n_q, hd = q.shape
+    n_ctx, n_kv, _ = k_cache.shape
+    o = torch.empty((n_q, hd), dtype=torch.float32, device=q.device)
+    lib = L.load()
+    nb = lib.as_gqa_decode_attention_ws_size(n_ctx, n_q, n_kv, hd)
+    ws = workspace(("attn", n_ctx, n_q, n_kv, hd), nb, q.device)
+    L.check(lib.as_gqa_decode_attention(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                        _dt(k_cache), n_ctx, n_q, n_kv, hd, _ptr(o), _ptr(ws), ws.numel(),
+                                        _stream(q.device)), "as_gqa_decode_attention")
+    return o
+
+
+@dataclass
+class BlockWeights:
+    """w_qkv [d, (n_q + 2 n_kv) hd], w_o [n_q hd, d], mlp (THRESHOLD layout)."""
+    w_qkv: torch.Tensor
+    w_o: torch.Tensor
+    mlp: MLPWeights
+    n_q: int = 32
+    n_kv: int = 8
+    head_dim: int = 128
+
+    def struct(self) -> L.ASBlockWeights:
+        return L.ASBlockWeights(_ptr(self.w_qkv), _ptr(self.w_o), self.mlp.struct(), self.n_q, self.n_kv,
+                                self.head_dim)
+
+
+def as_decoder_block(X: torch.Tensor, w: BlockWeights, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     t: dict, flags: int = 0, debug: bool = False, Y: torch.Tensor | None = None):
+    """One decode token through a thresholded decoder block; t = dict(qkv=, o=, gate_up=, down=)."""
+    X1 = X.reshape(-1)
+    _need_cuda(X1, w.w_qkv, w.w_o, k_cache, v_cache, Y)
+    d = X1.numel()
+    if Y is None:
+        Y = torch.empty(d, dtype=torch.float32, device=X.device)
+    lib = L.load()
+    st = w.struct()
+    n_ctx = k_cache.shape[0]
+    nb = lib.as_decoder_block_ws_size(ctypes.byref(st), n_ctx)
+    ws = workspace(("block", d, w.mlp.d_ff, n_ctx, w.n_q, w.n_kv, w.head_dim), nb, X.device)
+    th = L.ASBlockThresholds(float(t["qkv"]), float(t["o"]), float(t["gate_up"]), float(t["down"]))
+    dd = None
+    dbg = None
+    if debug:
+        nqkv = (w.n_q + 2 * w.n_kv) * w.head_dim
+        z = lambda n: torch.zeros(n, dtype=torch.float32, device=X.device)  # noqa: E731
+        dd = dict(xn=z(d), qkv=z(nqkv), o=z(w.n_q * w.head_dim), h1=z(d), xn2=z(d), h=z(w.mlp.d_ff))
+        dbg = L.ASBlockDebug(*(_ptr(dd[k]) for k in ("xn", "qkv", "o", "h1", "xn2", "h")))
+    L.check(lib.as_decoder_block(_ptr(X1), _dt(X1), ctypes.byref(st), _ptr(k_cache), _ptr(v_cache), n_ctx,
+                                 ctypes.byref(th), _ptr(Y), flags, ctypes.byref(dbg) if dbg is not None else None,
+                                 _ptr(ws), ws.numel(), _stream(X.device)), "as_decoder_block")
+    return (Y, dd) if debug else Y
+
+
 def as_bench_flush(buf: torch.Tensor):
     _need_cuda(buf)
     L.check(L.load().as_bench_flush(_ptr(buf), buf.numel() * buf.element_size(), _stream(buf.device)),

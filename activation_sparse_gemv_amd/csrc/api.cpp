@@ -473,4 +473,139 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   return hip_check(launch_moe(int(w->w_dt), p, max_unique, stream), fn);
 }
 
+// ------------------------------------------------------------------ block glue
+as_status as_rmsnorm(const void* X, as_dtype x_dt, int rows, int d, float eps, float* Y, float* copy,
+                     hipStream_t stream) {
+  const char* fn = "as_rmsnorm";
+  if (!X || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!is_dt(x_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (rows < 1 || d < 1 || !(eps >= 0.f)) return fail(AS_ERR_INVALID_ARG, "%s: rows=%d d=%d", fn, rows, d);
+  return hip_check(launch_rmsnorm(X, int(x_dt), rows, d, eps, Y, copy, stream), fn);
+}
+
+namespace {
+int attn_chunks(int n_ctx, int n_kv) {
+  int c = (n_ctx + 1 + 63) / 64;
+  const int max_c = (2 * num_cus() + n_kv - 1) / n_kv;
+  if (c > max_c) c = max_c;
+  if (c < 1) c = 1;
+  return c;
+}
+struct AttnWs {
+  float* part_o;
+  float* part_ml;
+  unsigned* counters;
+};
+AttnWs carve_attn(Carver& c, int n_ctx, int n_q, int n_kv, int hd) {
+  AttnWs a;
+  const int C = attn_chunks(n_ctx, n_kv);
+  const int grp = n_q / n_kv;
+  a.part_o = c.take<float>(size_t(n_kv) * C * grp * hd);
+  a.part_ml = c.take<float>(size_t(n_kv) * C * grp * 2);
+  a.counters = c.take<unsigned>(size_t(n_kv));
+  return a;
+}
+}  // namespace
+
+size_t as_gqa_decode_attention_ws_size(int n_ctx, int n_q, int n_kv, int head_dim) {
+  if (n_ctx < 0 || n_q < 1 || n_kv < 1 || head_dim < 1 || n_q % n_kv) return 0;
+  Carver c{nullptr};
+  carve_attn(c, n_ctx, n_q, n_kv, head_dim);
+  return c.off;
+}
+
+as_status as_gqa_decode_attention(const float* q, const float* k_new, const float* v_new, const void* k_cache,
+                                  const void* v_cache, as_dtype kv_dt, int n_ctx, int n_q, int n_kv, int head_dim,
+                                  float* o, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "as_gqa_decode_attention";
+  if (!q || !k_new || !v_new || !o) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (n_ctx > 0 && (!k_cache || !v_cache)) return fail(AS_ERR_INVALID_ARG, "%s: NULL cache", fn);
+  if (kv_dt != AS_BF16) return fail(AS_ERR_UNSUPPORTED, "%s: caches must be bf16", fn);
+  if (n_ctx < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv || head_dim < 1)
+    return fail(AS_ERR_INVALID_ARG, "%s: n_ctx=%d n_q=%d n_kv=%d hd=%d", fn, n_ctx, n_q, n_kv, head_dim);
+  if (n_q / n_kv > attention_max_group() || head_dim > attention_max_head_dim())
+    return fail(AS_ERR_UNSUPPORTED, "%s: group %d or head_dim %d too large", fn, n_q / n_kv, head_dim);
+  Carver c{reinterpret_cast<char*>(ws)};
+  AttnWs a = carve_attn(c, n_ctx, n_q, n_kv, head_dim);
+  as_status st = check_ws(ws, ws_bytes, c.off);
+  if (st != AS_OK) return st;
+  AttnParams p;
+  p.q = q; p.k_new = k_new; p.v_new = v_new;
+  p.k_cache = reinterpret_cast<const uint16_t*>(k_cache); p.v_cache = reinterpret_cast<const uint16_t*>(v_cache);
+  p.n_ctx = n_ctx; p.n_q = n_q; p.n_kv = n_kv; p.head_dim = head_dim;
+  p.o = o; p.part_o = a.part_o; p.part_ml = a.part_ml; p.counters = a.counters;
+  return hip_check(launch_attention(p, attn_chunks(n_ctx, n_kv), stream), fn);
+}
+
+namespace {
+struct BlockWs {
+  float *xn, *qkv, *o, *h1, *xn2;
+  void *ws_qkv, *ws_o, *ws_attn, *ws_mlp;
+  size_t n_qkv, n_o, n_attn, n_mlp;
+};
+BlockWs carve_block(Carver& c, const as_block_weights* w, int n_ctx) {
+  BlockWs b;
+  const int d = w->mlp.d_model;
+  const int nqkv = (w->n_q + 2 * w->n_kv) * w->head_dim, no = w->n_q * w->head_dim;
+  b.xn = c.take<float>(d);
+  b.qkv = c.take<float>(nqkv);
+  b.o = c.take<float>(no);
+  b.h1 = c.take<float>(d);
+  b.xn2 = c.take<float>(d);
+  b.n_qkv = as_threshold_gemv_ws_size(1, d, nqkv);
+  b.n_o = as_threshold_gemv_ws_size(1, no, d);
+  b.n_attn = as_gqa_decode_attention_ws_size(n_ctx, w->n_q, w->n_kv, w->head_dim);
+  b.n_mlp = as_sparse_swiglu_mlp_ws_size(1, &w->mlp, AS_MLP_THRESHOLD);
+  b.ws_qkv = c.take<char>(b.n_qkv);
+  b.ws_o = c.take<char>(b.n_o);
+  b.ws_attn = c.take<char>(b.n_attn);
+  b.ws_mlp = c.take<char>(b.n_mlp);
+  return b;
+}
+}  // namespace
+
+size_t as_decoder_block_ws_size(const as_block_weights* w, int n_ctx) {
+  if (!w || w->n_q < 1 || w->n_kv < 1 || w->head_dim < 1 || w->mlp.d_model < 1 || w->mlp.d_ff < 1) return 0;
+  Carver c{nullptr};
+  carve_block(c, w, n_ctx);
+  return c.off;
+}
+
+as_status as_decoder_block(const void* X, as_dtype x_dt, const as_block_weights* w, const void* k_cache,
+                           const void* v_cache, int n_ctx, const as_block_thresholds* t, float* Y, unsigned flags,
+                           as_block_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "as_decoder_block";
+  if (!X || !w || !t || !Y || !w->w_qkv || !w->w_o) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  as_status st = check_mlp_weights(&w->mlp, AS_MLP_THRESHOLD, fn);
+  if (st != AS_OK) return st;
+  if (w->n_q < 1 || w->n_kv < 1 || w->head_dim < 1 || w->n_q % w->n_kv)
+    return fail(AS_ERR_INVALID_ARG, "%s: heads %d/%d hd %d", fn, w->n_q, w->n_kv, w->head_dim);
+  Carver c{reinterpret_cast<char*>(ws)};
+  BlockWs b = carve_block(c, w, n_ctx);
+  if ((st = check_ws(ws, ws_bytes, c.off)) != AS_OK) return st;
+  const int d = w->mlp.d_model, hd = w->head_dim;
+  const int nqkv = (w->n_q + 2 * w->n_kv) * hd, no = w->n_q * hd;
+  const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
+  const unsigned pass = flags & (AS_FLAG_NO_NT_LOADS | AS_FLAG_FORCE_DENSE);
+  float* xn = dbg && dbg->xn ? dbg->xn : b.xn;
+  float* qkv = dbg && dbg->qkv ? dbg->qkv : b.qkv;
+  float* o = dbg && dbg->o ? dbg->o : b.o;
+  float* h1 = dbg && dbg->h1 ? dbg->h1 : b.h1;
+  float* xn2 = dbg && dbg->xn2 ? dbg->xn2 : b.xn2;
+  const float inf = -INFINITY;
+  if ((st = as_rmsnorm(X, x_dt, 1, d, 1e-5f, xn, h1, stream)) != AS_OK) return st;
+  if ((st = as_threshold_gemv(xn, AS_F32, 1, d, w->w_qkv, w->mlp.w_dt, nqkv, dense ? inf : t->qkv, qkv, AS_F32,
+                              pass, nullptr, b.ws_qkv, b.n_qkv, stream)) != AS_OK) return st;
+  if ((st = as_gqa_decode_attention(qkv, qkv + no, qkv + no + w->n_kv * hd, k_cache, v_cache, AS_BF16, n_ctx,
+                                    w->n_q, w->n_kv, hd, o, b.ws_attn, b.n_attn, stream)) != AS_OK) return st;
+  if ((st = as_threshold_gemv(o, AS_F32, 1, no, w->w_o, w->mlp.w_dt, d, dense ? inf : t->o, h1, AS_F32,
+                              pass | AS_FLAG_ACCUMULATE, nullptr, b.ws_o, b.n_o, stream)) != AS_OK) return st;
+  if ((st = as_rmsnorm(h1, AS_F32, 1, d, 1e-5f, xn2, Y, stream)) != AS_OK) return st;
+  as_mlp_debug md;
+  memset(&md, 0, sizeof md);
+  md.h = dbg ? dbg->h : nullptr;
+  return as_sparse_swiglu_mlp(xn2, AS_F32, 1, &w->mlp, AS_MLP_THRESHOLD, t->gate_up, t->down, nullptr, 0, Y,
+                              AS_F32, pass | AS_FLAG_ACCUMULATE, md.h ? &md : nullptr, b.ws_mlp, b.n_mlp, stream);
+}
+
 }  // extern "C"

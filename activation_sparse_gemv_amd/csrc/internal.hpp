@@ -76,6 +76,18 @@ hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, f
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s);
 int moe_down_tiles(int d_model);
 
+// Decoder-block glue (see glue.hip).
+struct AttnParams {
+  const float* q; const float* k_new; const float* v_new;     // fp32 projections of the current token
+  const uint16_t* k_cache; const uint16_t* v_cache;            // bf16 [n_ctx, n_kv, head_dim]
+  int n_ctx, n_q, n_kv, head_dim;
+  float* o; float* part_o; float* part_ml; unsigned* counters;
+};
+hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, float* y, float* copy, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s);
+int attention_max_group();
+int attention_max_head_dim();
+
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);

@@ -232,6 +232,59 @@ as_status as_sparse_moe_expert(const void *X, as_dtype x_dt, int T,
                                float *h_dbg, int32_t *keep_dbg,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------ decoder-block glue
+ * TEAL slides, method slide: every projection input of the attention and MLP
+ * blocks is thresholded; the attention core stays dense.  Readings (the pages
+ * give no block): pre-norm RMSNorm with unit gain, no rotary embedding, query
+ * head h reads key/value head h / (n_q / n_kv), keys = cached context + the
+ * current token. */
+
+/* Y[r, :] = X[r, :] / sqrt(mean(X[r, :]^2) + eps) in fp32; copy[r, :] = X[r, :]
+ * as fp32 when copy is non-NULL (the residual branch).  X: [rows, d]. */
+as_status as_rmsnorm(const void *X, as_dtype x_dt, int rows, int d, float eps,
+                     float *Y, float *copy, hipStream_t stream);
+
+/* Dense softmax attention of one decode token, scale 1/sqrt(head_dim):
+ * o[h, :] = sum_j softmax_j(q[h] . K_j / sqrt(hd)) V_j over the n_ctx cached keys
+ * of kv head h / (n_q / n_kv) followed by the current token's k_new / v_new.
+ * q: [n_q, hd] fp32; k_new, v_new: [n_kv, hd] fp32; caches: [n_ctx, n_kv, hd]
+ * (AS_BF16 only); o: [n_q, hd] fp32.  n_q % n_kv == 0, n_q / n_kv <= 8,
+ * head_dim <= 256, n_ctx >= 0. */
+size_t as_gqa_decode_attention_ws_size(int n_ctx, int n_q, int n_kv, int head_dim);
+as_status as_gqa_decode_attention(const float *q, const float *k_new, const float *v_new,
+                                  const void *k_cache, const void *v_cache, as_dtype kv_dt,
+                                  int n_ctx, int n_q, int n_kv, int head_dim, float *o,
+                                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+typedef struct {
+  const void *w_qkv;      /* [d_model, (n_q + 2 n_kv) * head_dim] input-major, columns q | k | v */
+  const void *w_o;        /* [n_q * head_dim, d_model] input-major */
+  as_mlp_weights mlp;     /* THRESHOLD layout (gate/up [d_model, 2, d_ff], down [d_ff, d_model]) */
+  int n_q, n_kv, head_dim;
+} as_block_weights;
+
+typedef struct { float qkv, o, gate_up, down; } as_block_thresholds;
+
+typedef struct {          /* every field nullable; fp32 intermediates of one call */
+  float *xn;              /* [d_model] rmsnorm(x) */
+  float *qkv;             /* [(n_q + 2 n_kv) * head_dim] */
+  float *o;               /* [n_q * head_dim] attention output (o-proj input) */
+  float *h1;              /* [d_model] x + o-proj */
+  float *xn2;             /* [d_model] rmsnorm(h1) */
+  float *h;               /* [d_ff] MLP intermediate */
+} as_block_debug;
+
+/* One decoder block for one decode token, every projection input thresholded:
+ *   xn = rmsnorm(x); qkv = (xn * [|xn| > t.qkv]) Wqkv; o = attention(q, caches + k, v)
+ *   h1 = x + (o * [|o| > t.o]) Wo;  Y = h1 + MLP(rmsnorm(h1)) with t.gate_up, t.down.
+ * X: [d_model] (f16/bf16/f32); Y: [d_model] fp32.  AS_FLAG_FORCE_DENSE ignores
+ * every threshold (the dense block). */
+size_t as_decoder_block_ws_size(const as_block_weights *w, int n_ctx);
+as_status as_decoder_block(const void *X, as_dtype x_dt, const as_block_weights *w,
+                           const void *k_cache, const void *v_cache, int n_ctx,
+                           const as_block_thresholds *t, float *Y, unsigned flags,
+                           as_block_debug *dbg, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ benchmark support
  * Overwrite `bytes` of device memory at `buf` with a kernel, evicting the
  * Infinity Cache and L2 between timed calls. */
