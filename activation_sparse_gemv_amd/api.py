@@ -282,12 +282,12 @@ def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: in
     accumulated on top.  Returns Y [T, d] fp32 (and intermediates when debug)."""
     T, d = X.shape
     logits = torch.empty((T, w.w_router.shape[1]), dtype=torch.float32, device=X.device)
-    for t0 in range(0, T, 8):
-        as_dense_gemv(X[t0:t0 + 8], w.w_router, Y=logits[t0:t0 + 8])
+    for t0 in range(0, T, 16):
+        as_dense_gemv(X[t0:t0 + 16], w.w_router, Y=logits[t0:t0 + 16])
     ids, wts = as_moe_router(logits, top_k)
     Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
-    for t0 in range(0, T, 8):
-        as_sparse_swiglu_mlp(X[t0:t0 + 8], w.shared, flags=L.AS_FLAG_FORCE_DENSE, Y=Y[t0:t0 + 8])
+    for t0 in range(0, T, 16):
+        as_sparse_swiglu_mlp(X[t0:t0 + 16], w.shared, flags=L.AS_FLAG_FORCE_DENSE, Y=Y[t0:t0 + 16])
     r = as_sparse_moe_expert(X, w, ids, wts, keep_k, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug)
     if debug:
         return Y, dict(logits=logits, ids=ids, wts=wts, **r[1])

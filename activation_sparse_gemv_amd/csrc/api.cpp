@@ -34,7 +34,7 @@ as_status hip_check(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool is_wdt(as_dtype d) { return d == AS_F16 || d == AS_BF16; }
 bool is_dt(as_dtype d) { return d == AS_F16 || d == AS_BF16 || d == AS_F32; }
-int mt_for(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+int mt_for(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 
 int num_cus() {
@@ -229,7 +229,8 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
                              size_t ws_bytes, hipStream_t stream, bool dense, const char* fn) {
   if (!X || !W || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, W or Y", fn);
   if (!is_dt(x_dt) || !is_wdt(w_dt) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
-  if (M < 1 || M > 8) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..8", fn, M);
+  if (M < 1 || M > 16) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..16", fn, M);
+  if (M > 8 && w_dt != AS_BF16) return fail(AS_ERR_UNSUPPORTED, "%s: M > 8 (MFMA path) needs bf16 weights", fn);
   if (K < 1 || N < 8 || N % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: K=%d N=%d (N must be a multiple of 8)", fn, K, N);
   if (!aligned16(W)) return fail(AS_ERR_INVALID_ARG, "%s: W not 16-byte aligned", fn);
   if (mo && mo->idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: mask idx export needs M == 1", fn);
@@ -301,7 +302,9 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   if (st != AS_OK) return st;
   if (!X || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X or Y", fn);
   if (!is_dt(x_dt) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
-  if (M < 1 || M > 8) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..8", fn, M);
+  if (M < 1 || M > 16) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..16", fn, M);
+  if (M > 8 && (w->w_dt != AS_BF16 || mode != AS_MLP_THRESHOLD))
+    return fail(AS_ERR_UNSUPPORTED, "%s: M > 8 (MFMA path) needs bf16 weights in THRESHOLD mode", fn);
   const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
   if (mode == AS_MLP_NEURON_SET && !dense) {
     if (n_active < 0 || n_active > w->d_ff) return fail(AS_ERR_INVALID_ARG, "%s: n_active=%d", fn, n_active);

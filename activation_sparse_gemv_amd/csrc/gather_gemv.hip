@@ -12,9 +12,11 @@ size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
   size_t b = ((size_t(cap) * 4 + 15) & ~size_t(15)) + ((size_t(cap) * c.mt * 4 + 15) & ~size_t(15));
   b += (size_t(nslot > c.mt ? nslot : c.mt) * tn * 4 + 15) & ~size_t(15);
   if (c.in == IN_LISTS) b += (size_t(n_lt + 1) * 4 + 15) & ~size_t(15);
+  if (c.mt == 16) b += size_t(32) * (tn + 4) * 2;     // staged bf16 weight chunk of the MFMA loop
   return b;
 }
 
+hipError_t launch_gemv_bf16_m16(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
 hipError_t launch_gemv_bf16_m1(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
 hipError_t launch_gemv_bf16_m2(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
 hipError_t launch_gemv_bf16_m4(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
@@ -49,6 +51,7 @@ hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStrea
     case 2: return bf ? launch_gemv_bf16_m2(cc, p, smem, s) : launch_gemv_f16_m2(cc, p, smem, s);
     case 4: return bf ? launch_gemv_bf16_m4(cc, p, smem, s) : launch_gemv_f16_m4(cc, p, smem, s);
     case 8: return bf ? launch_gemv_bf16_m8(cc, p, smem, s) : launch_gemv_f16_m8(cc, p, smem, s);
+    case 16: return bf ? launch_gemv_bf16_m16(cc, p, smem, s) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -74,6 +74,103 @@ __device__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_sca
   }
 }
 
+// ---------------------------------------------------------------- MFMA main loop
+// Batches of 9..16 tokens: the per-row FMA count outgrows the VALU, so the
+// contraction runs on the matrix cores (v_mfma_f32_16x16x32_bf16).  MFMA wants
+// the reduction (row) index contiguous per lane, while input-major rows are
+// contiguous along the output columns, so each 32-row chunk of the tile is
+// staged through LDS (rows padded by 4 elements, which spreads the four lane
+// groups of a transposed read over distinct banks) and read back column-wise.
+// Activations are fp32 in LDS; each is split into bf16 hi + bf16 lo (x - hi),
+// two MFMAs per fragment, which keeps fp32 inputs (h, normalised x) to ~2^-16
+// relative precision while bf16 inputs stay exact.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int LPR, bool GU, bool NT>
+__device__ void mfma_main_loop(const GemvParams& p, const int* s_idx, const float* s_val, uint16_t* s_w, int cap,
+                               int cnt, int tile, float* s_out /* [16][TN] */) {
+  constexpr int TN = LPR * 8, TB = TN / 2, LDW = TN + 4;
+  constexpr int NB = TN / 16;              // 16-column blocks in the tile
+  constexpr int NBW = NB / 4;              // blocks per wave
+  constexpr int VPT = TN / 64;             // 16-byte vectors per thread per 32-row chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  f32x4_t acc[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // global source of each of this thread's vectors: tile row (0..31) and tile column (multiple of 8)
+  int vrow[VPT], vcol[VPT];
+  long vsrc[VPT];
+#pragma unroll
+  for (int q = 0; q < VPT; ++q) {
+    const int v = tid + q * kThreads;
+    vrow[q] = v / (TN / 8);
+    vcol[q] = (v % (TN / 8)) * 8;
+    long gc;
+    bool ok;
+    if constexpr (GU) {
+      const int n = tile * TB + (vcol[q] % TB);
+      ok = n < p.N;
+      gc = vcol[q] < TB ? (long)n : p.gu_off + n;
+    } else {
+      const int n = tile * TN + vcol[q];
+      ok = n < p.N;
+      gc = n;
+    }
+    vsrc[q] = ok ? gc : 0;
+  }
+  const int nchunks = (cnt + 31) / 32;
+  u32x4 buf[VPT];
+  auto fetch = [&](int ch) {
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+      const int row = s_idx[min(ch * 32 + vrow[q], cnt - 1)];
+      buf[q] = load_w16(p.W + (long)row * p.ldw + vsrc[q], NT);
+    }
+  };
+  if (nchunks > 0) fetch(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < VPT; ++q) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(s_w + vrow[q] * LDW + vcol[q]);
+      dst[0] = buf[q].x; dst[1] = buf[q].y; dst[2] = buf[q].z; dst[3] = buf[q].w;
+    }
+    __syncthreads();
+    if (ch + 1 < nchunks) fetch(ch + 1);
+    // A fragments: token li, rows 8g .. 8g+7 of the chunk, split into hi + lo
+    bf16x8_t ahi, alo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = ch * 32 + 8 * g + e;
+      const float x = r < cnt ? s_val[li * cap + r] : 0.f;
+      const uint16_t hb = f32_to_bf16_bits(x);
+      const float hf = bf16_bits_to_f32(hb);
+      const uint16_t lb = f32_to_bf16_bits(x - hf);
+      ahi[e] = __builtin_bit_cast(__bf16, hb);
+      alo[e] = __builtin_bit_cast(__bf16, lb);
+    }
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      const int col = (wave * NBW + b) * 16 + li;
+      bf16x8_t bw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bw[e] = __builtin_bit_cast(__bf16, s_w[(8 * g + e) * LDW + col]);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bw, acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bw, acc[b], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int col = (wave * NBW + b) * 16 + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_out[(4 * g + e) * TN + col] = acc[b][e];
+  }
+  __syncthreads();
+}
+
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
 __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams p) {
   using TS = TileShape<LPR>;
@@ -85,6 +182,9 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
   float* s_red = reinterpret_cast<float*>(smem + align16(size_t(cap) * 4) + align16(size_t(cap) * MT * 4));
   int* s_pref = reinterpret_cast<int*>(reinterpret_cast<unsigned char*>(s_red) +
                                        align16(size_t(NSLOT > MT ? NSLOT : MT) * TN * 4));
+  // MT == 16 only: the bf16 weight chunk staged for the MFMA loop, after s_pref
+  uint16_t* s_w = reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(s_pref) +
+                                              (IN == IN_LISTS ? align16(size_t(p.n_lt + 1) * 4) : 0));
   __shared__ int s_scan[kThreads / 64 + 1];
   __shared__ int s_flag;
 
@@ -229,6 +329,19 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
   }
   __syncthreads();
 
+  constexpr int CPT = (TN + kThreads - 1) / kThreads;   // tile columns per thread
+  float res[MT][CPT];
+  if constexpr (MT == 16) {
+    static_assert(WDT == DT_BF16, "the MFMA path takes bf16 weights");
+    mfma_main_loop<LPR, GU, NT>(p, s_idx, s_val, s_w, cap, cnt, tile, s_red);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + q * kThreads;
+        res[m][q] = c < TN ? s_red[m * TN + c] : 0.f;
+      }
+  } else {
   // ------------------------------------------------------------ main loop
   const int lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPR, l = lane % LPR;
@@ -278,8 +391,6 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
   }
 
   // ------------------------------------------------------------ slot reduction
-  constexpr int CPT = (TN + kThreads - 1) / kThreads;   // tile columns per thread
-  float res[MT][CPT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     __syncthreads();
@@ -295,6 +406,8 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
         for (int s2 = 0; s2 < NSLOT; ++s2) v += s_red[s2 * TN + c];
       res[m][q] = v;
     }
+  }
+
   }
 
   // tile-local column c -> (validity, partial/output column)

@@ -106,7 +106,8 @@ as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64
  * TEAL slides, slide 11: mask generation fused with the sparse product,
  * loading only the weight rows whose input survives:
  *   Y[m, :] = sum over i with |X[m, i]| > t of X[m, i] * W[i, :]
- * X: [M, K] (f16/bf16/f32), 1 <= M <= 8.  W: [K, N] input-major (f16/bf16),
+ * X: [M, K] (f16/bf16/f32), 1 <= M <= 16 (M > 8 runs on the matrix cores and
+ * needs bf16 weights).  W: [K, N] input-major (f16/bf16),
  * N % 8 == 0.  Y: [M, N] (f16/bf16/f32).  t is compared in fp32 with strict
  * '>': t = -INFINITY keeps every row; NaN inputs are dropped.  A weight row is
  * read once for all M tokens if any token keeps it; each token still uses only
@@ -156,7 +157,8 @@ typedef struct {
  * through decode): the same SwiGLU restricted to neurons
  * neuron_idx[0 .. n_active) (int32, device, ascending, distinct, < d_ff);
  * t_x and t_h are ignored.
- * X: [M, d_model] (f16/bf16/f32), 1 <= M <= 8; Y: [M, d_model].
+ * X: [M, d_model] (f16/bf16/f32), 1 <= M <= 16 (M > 8: THRESHOLD mode with bf16
+ * weights, on the matrix cores); Y: [M, d_model].
  * silu(z) = z / (1 + exp(-z)).  AS_FLAG_FORCE_DENSE: dense SwiGLU over all
  * neurons and inputs (the baseline).  dbg is nullable. */
 size_t as_sparse_swiglu_mlp_ws_size(int M, const as_mlp_weights *w, as_mlp_mode mode);

@@ -70,6 +70,36 @@ def test_gemv_parity_shapes(M, wdt, xdt):
         assert m["idx"][0, :nnz].cpu().numpy().tolist() == np.flatnonzero(mask[0]).tolist()
 
 
+@pytest.mark.parametrize("M", [9, 12, 16])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_gemv_mfma_batches(M, xdt):
+    """9..16 tokens run on the matrix cores (bf16 weights); fp32 inputs go through the
+    hi/lo bf16 split."""
+    K, N = 1000, 1352
+    announce(f"gemv mfma M={M} x={xdt}")
+    x = datagen.student_t((M, K), 900 + M, dtype=xdt)
+    W = datagen.normal((K, N), 901)
+    t = float(teal.calibrate_threshold(f64(x), 0.5))
+    y, m = _run(x, W, t, mask_out=True)
+    assert rel_err(y, teal.masked_gemv(f64(x), f64(W), t)) < TOL * 1e-2
+    assert np.array_equal(bits_to_bool(m["bits"], K), teal.magnitude_mask(f64(x), t))
+    yd = asg.as_dense_gemv(_dev(x), _dev(W))
+    assert rel_err(yd, f64(x) @ f64(W)) < TOL * 1e-2
+    # Llama down-projection shape, batched
+    x2 = datagen.student_t((M, 14336), 902 + M, dtype=xdt)
+    W2 = datagen.normal((14336, 4096), 903)
+    t2 = float(teal.calibrate_threshold(f64(x2), 0.5))
+    assert rel_err(_run(x2, W2, t2), teal.masked_gemv(f64(x2), f64(W2), t2)) < TOL * 1e-2
+
+
+def test_gemv_mfma_integer_bit_exact():
+    announce("gemv mfma integer")
+    K, N = 4096, 4096
+    x = datagen.int_valued((16, K), 77, -8, 8)
+    W = datagen.int_valued((K, N), 78, -4, 4)
+    assert np.array_equal(f64(_run(x, W, 3.0)), teal.masked_gemv(f64(x), f64(W), 3.0))
+
+
 @pytest.mark.parametrize("s", datagen.CFG2_SWEEP)
 def test_gemv_llama_shapes_sweep(s):
     """Llama-3-8B-shaped projections (down: 14336 -> 4096, o: 4096 -> 4096) at each sparsity."""

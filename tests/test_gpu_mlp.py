@@ -82,6 +82,21 @@ def test_mlp_llama_sweep(s):
         print(r, flush=True)
 
 
+@pytest.mark.parametrize("M", [9, 16])
+def test_mlp_batched_mfma(M):
+    """Threshold MLP for 9..16 tokens on the matrix cores (Llama-3-8B shape, 50%)."""
+    announce(f"mlp mfma M={M}")
+    shape = datagen.CFG2
+    w = _mlp(2, shape)
+    calib = datagen.student_t((256, shape.d_model), datagen.seed_for(2, 0, "calib"))
+    t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], 0.5, 0.5)
+    toks = datagen.student_t((M, shape.d_model), datagen.seed_for(2, 1, "decode"))
+    r = _check_stagewise(toks, w, float(t_x), float(t_h), M)
+    print(r, flush=True)
+    y = asg.as_sparse_swiglu_mlp(toks.to(DEV), w["dev"], 5.0, 5.0, flags=L.AS_FLAG_FORCE_DENSE)
+    assert rel_err(y, teal.dense_mlp(f64(toks), w["Wg"], w["Wu"], w["Wd"])) < TOL
+
+
 def test_mlp_dense_baseline_matches_dense_oracle():
     announce("mlp dense baseline")
     shape = datagen.CFG2
