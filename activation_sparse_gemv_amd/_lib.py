@@ -84,6 +84,7 @@ SIGNATURES = {
     "as_decoder_block": (c_int, [c_void_p, c_int, POINTER(ASBlockWeights), c_void_p, c_void_p, c_int,
                                  POINTER(ASBlockThresholds), c_void_p, c_uint, POINTER(ASBlockDebug), c_void_p,
                                  c_size_t, c_void_p]),
+    "as_glass_local_signal": (c_int, [c_void_p, c_int, c_int, POINTER(ASMlpWeights), c_void_p, c_void_p]),
     "as_bench_flush": (c_int, [c_void_p, c_size_t, c_void_p]),
 }
 

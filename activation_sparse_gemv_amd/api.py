@@ -364,6 +364,17 @@ def as_decoder_block(X: torch.Tensor, w: BlockWeights, k_cache: torch.Tensor, v_
     return (Y, dd) if debug else Y
 
 
+def as_glass_local_signal(X: torch.Tensor, w: MLPWeights) -> torch.Tensor:
+    """Mean |h| of every FFN neuron over the prompt tokens X [P, d] (bf16); w neuron-major."""
+    _need_cuda(X, w.w_gate_up)
+    P = X.shape[0]
+    local = torch.empty(w.d_ff, dtype=torch.float32, device=X.device)
+    st = w.struct()
+    L.check(L.load().as_glass_local_signal(_ptr(X), _dt(X), P, ctypes.byref(st), _ptr(local), _stream(X.device)),
+            "as_glass_local_signal")
+    return local
+
+
 def as_bench_flush(buf: torch.Tensor):
     _need_cuda(buf)
     L.check(L.load().as_bench_flush(_ptr(buf), buf.numel() * buf.element_size(), _stream(buf.device)),

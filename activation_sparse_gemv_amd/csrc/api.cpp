@@ -611,4 +611,19 @@ as_status as_decoder_block(const void* X, as_dtype x_dt, const as_block_weights*
                               AS_F32, pass | AS_FLAG_ACCUMULATE, md.h ? &md : nullptr, b.ws_mlp, b.n_mlp, stream);
 }
 
+// ------------------------------------------------------------------ GLASS local signal
+as_status as_glass_local_signal(const void* X, as_dtype x_dt, int P, const as_mlp_weights* w, float* local,
+                                hipStream_t stream) {
+  const char* fn = "as_glass_local_signal";
+  if (!X || !w || !w->w_gate_up || !local) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (P < 1 || w->d_model < 32 || w->d_ff < 16) return fail(AS_ERR_INVALID_ARG, "%s: P=%d d=%d d_ff=%d", fn, P, w->d_model, w->d_ff);
+  if (x_dt != AS_BF16 || w->w_dt != AS_BF16 || w->d_model % 32 != 0)
+    return fail(AS_ERR_UNSUPPORTED, "%s: needs bf16 X and weights and d_model %% 32 == 0", fn);
+  if (!aligned16(X) || !aligned16(w->w_gate_up)) return fail(AS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  const int d = w->d_model;
+  return hip_check(launch_local_signal(reinterpret_cast<const uint16_t*>(X), P, d,
+                                       reinterpret_cast<const uint16_t*>(w->w_gate_up), 3L * d, d, w->d_ff, local,
+                                       stream), fn);
+}
+
 }  // extern "C"

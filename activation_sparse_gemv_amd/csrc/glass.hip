@@ -1,0 +1,84 @@
+// GLASS local signal: mean |h| of every FFN neuron over the prompt tokens.
+//
+// GLASS summary, section 1 and 2.2: the local importance signal comes from the
+// prefill-stage activations of the prompt.  Reading: local_j = (1/P) sum_t
+// |silu(x_t . Wg_j) * (x_t . Wu_j)|, the magnitude of the down-projection input.
+// This is a dense prefill GEMM, run once per prompt, on the matrix cores: with
+// the FFN stored neuron-major a neuron's gate (and up) row is contiguous along
+// the reduction dimension, so both MFMA operands are K-contiguous: the weight
+// fragment of a lane is one 16-byte load, and the prompt tile (32 columns of
+// every token) is staged in LDS once per k-step for the four waves.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace as {
+
+typedef __bf16 g_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float g_f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLsThreads = 256;
+constexpr int kLsTokBlock = 128;          // tokens per pass (8 MFMA row tiles)
+constexpr int kLsLd = 40;                 // LDS row stride (elements) of the prompt tile
+
+__global__ __launch_bounds__(kLsThreads) void local_signal_kernel(const uint16_t* X, int P, int d,
+                                                                  const uint16_t* W, long ld_neuron, long up_off,
+                                                                  int d_ff, float* local) {
+  __shared__ __align__(16) uint16_t xt[kLsTokBlock * kLsLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int j = (blockIdx.x * 4 + wave) * 16 + li;          // this lane's neuron (B column)
+  const bool jvalid = j < d_ff;
+  const uint16_t* wg = W + (long)(jvalid ? j : 0) * ld_neuron;
+  const uint16_t* wu = wg + up_off;
+  float asum = 0.f;
+  for (int t0 = 0; t0 < P; t0 += kLsTokBlock) {
+    g_f32x4 accg[8], accu[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) { accg[m] = g_f32x4{0.f, 0.f, 0.f, 0.f}; accu[m] = accg[m]; }
+    for (int k0 = 0; k0 < d; k0 += 32) {
+      __syncthreads();
+      // prompt tile: 128 tokens x 32 columns, two 16-byte vectors per thread
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int v = tid + q * kLsThreads;               // 0..511
+        const int t = v >> 2, c = (v & 3) * 8;
+        u32x4 val = u32x4{0u, 0u, 0u, 0u};
+        if (t0 + t < P) val = *reinterpret_cast<const u32x4*>(X + (long)(t0 + t) * d + k0 + c);
+        *reinterpret_cast<u32x4*>(xt + t * kLsLd + c) = val;
+      }
+      __syncthreads();
+      const u32x4 bg = load_w16(wg + k0 + 8 * g, true);
+      const u32x4 bu = load_w16(wu + k0 + 8 * g, true);
+      const g_bf16x8 fg = __builtin_bit_cast(g_bf16x8, bg);
+      const g_bf16x8 fu = __builtin_bit_cast(g_bf16x8, bu);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(xt + (m * 16 + li) * kLsLd + 8 * g);
+        const g_bf16x8 fa = __builtin_bit_cast(g_bf16x8, a);
+        accg[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fg, accg[m], 0, 0, 0);
+        accu[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fu, accu[m], 0, 0, 0);
+      }
+    }
+    // lane holds D[token 4g+e of each row tile][neuron li]
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + m * 16 + 4 * g + e;
+        if (t < P) asum += fabsf(silu_f32(accg[m][e]) * accu[m][e]);
+      }
+  }
+  // combine the four lane groups (tokens 4g..4g+3 of every tile) of neuron li, in a fixed order
+  const float s1 = __shfl(asum, li + 16, 64), s2 = __shfl(asum, li + 32, 64), s3 = __shfl(asum, li + 48, 64);
+  if (g == 0 && jvalid) local[j] = ((asum + s1) + (s2 + s3)) / (float)P;
+}
+
+hipError_t launch_local_signal(const uint16_t* X, int P, int d, const uint16_t* W, long ld_neuron, long up_off,
+                               int d_ff, float* local, hipStream_t s) {
+  const int blocks = (d_ff + 63) / 64;
+  hipLaunchKernelGGL(local_signal_kernel, dim3(blocks), dim3(kLsThreads), 0, s, X, P, d, W, ld_neuron, up_off, d_ff,
+                     local);
+  return hipGetLastError();
+}
+
+}  // namespace as

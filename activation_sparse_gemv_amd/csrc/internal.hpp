@@ -88,6 +88,10 @@ hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s);
 int attention_max_group();
 int attention_max_head_dim();
 
+// GLASS local signal (see glass.hip).
+hipError_t launch_local_signal(const uint16_t* X, int P, int d, const uint16_t* W, long ld_neuron, long up_off,
+                               int d_ff, float* local, hipStream_t s);
+
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);

@@ -190,6 +190,18 @@ as_status as_topk_mask(const float *score, const float *prior, int rows, int n, 
                        as_topk_mode mode, float lambda, uint64_t *mask, int32_t *idx,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* GLASS local signal (GLASS summary, sections 1 and 2.2: the local importance
+ * of a neuron comes from the prompt's prefill activations).  Reading:
+ *   local[j] = (1/P) sum_t |silu(X[t] . Wg_j) * (X[t] . Wu_j)|,
+ * the mean magnitude of the down-projection input over the P prompt tokens,
+ * computed on the matrix cores (fp32 accumulation).  It is the score argument
+ * of as_topk_mask in RANK_BLEND mode.
+ * X: [P, d_model] bf16; w: NEURON_SET layout [d_ff, 3, d_model] bf16
+ * (w->w_down unused); local: [d_ff] fp32.
+ * Errors: UNSUPPORTED unless X and the weights are bf16 and d_model % 32 == 0. */
+as_status as_glass_local_signal(const void *X, as_dtype x_dt, int P, const as_mlp_weights *w,
+                                float *local, hipStream_t stream);
+
 /* ------------------------------------------------------------ MoE: router and routed experts */
 typedef struct {
   const void *w_gate_up;  /* [E, d_ff_e, 2, d_model] neuron-major: gate row then up row of

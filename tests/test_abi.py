@@ -48,9 +48,12 @@ def test_gemv_validation(lib):
     st = lib.as_threshold_gemv(None, L.AS_BF16, 1, 64, _p(), L.AS_BF16, 64, 0.5, _p(), L.AS_F32, 0, None,
                                None, 0, None)
     assert st == L.AS_ERR_INVALID_ARG and b"NULL" in lib.as_last_error()
-    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 9, 64, _p(), L.AS_BF16, 64, 0.5, _p(), L.AS_F32, 0, None,
+    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 17, 64, _p(), L.AS_BF16, 64, 0.5, _p(), L.AS_F32, 0, None,
                                None, 0, None)
     assert st == L.AS_ERR_UNSUPPORTED
+    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 9, 64, _p(), L.AS_F16, 64, 0.5, _p(), L.AS_F32, 0, None,
+                               None, 0, None)
+    assert st == L.AS_ERR_UNSUPPORTED and b"MFMA" in lib.as_last_error()
     st = lib.as_threshold_gemv(_p(), L.AS_BF16, 1, 64, _p(), L.AS_BF16, 60, 0.5, _p(), L.AS_F32, 0, None,
                                None, 0, None)
     assert st == L.AS_ERR_INVALID_ARG
@@ -96,6 +99,42 @@ def test_calibrate_validation(lib):
     assert lib.as_calibrate_threshold(None, L.AS_F32, 10, 5, _p(), None) == L.AS_ERR_INVALID_ARG
     assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 11, _p(), None) == L.AS_ERR_INVALID_ARG
     assert lib.as_calibrate_threshold(_p(), L.AS_F32, 0, 0, _p(), None) == L.AS_ERR_INVALID_ARG
+
+
+def test_topk_moe_block_validation(lib):
+    assert lib.as_topk_mask(None, None, 1, 10, 3, L.AS_TOPK_VALUE, 0.5, _p(), None, None, 0, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_topk_mask(_p(), None, 1, 10, 11, L.AS_TOPK_VALUE, 0.5, _p(), None, None, 0, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_topk_mask(_p(), None, 1, 10, 3, L.AS_TOPK_VALUE, 0.5, None, None, None, 0, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_topk_mask(_p(), None, 1, 10, 3, L.AS_TOPK_RANK_BLEND, 0.5, _p(), None, _p(), 1 << 20, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_topk_mask(_p(), _p(), 1, 10, 3, L.AS_TOPK_RANK_BLEND, 1.5, _p(), None, _p(), 1 << 20, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_topk_mask(_p(), _p(), 1, 70000, 3, L.AS_TOPK_RANK_BLEND, 0.5, _p(), None, _p(), 1 << 30, None) == L.AS_ERR_UNSUPPORTED
+    assert lib.as_topk_mask(_p(), _p(), 2, 100, 3, L.AS_TOPK_RANK_BLEND, 0.5, _p(), None, _p(), 16, None) == L.AS_ERR_WORKSPACE
+    assert lib.as_topk_mask_ws_size(1, 14336, L.AS_TOPK_VALUE) == 0
+    assert lib.as_moe_router(_p(), 1, 128, 0, _p(), _p(), None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_moe_router(_p(), 1, 2000, 8, _p(), _p(), None) == L.AS_ERR_INVALID_ARG
+    mw = L.ASMoeWeights(_p(), _p(), L.AS_BF16, 128, 2048, 768)
+    assert lib.as_sparse_moe_expert_ws_size(16, 8, ctypes.byref(mw)) > 0
+    st = lib.as_sparse_moe_expert(_p(), L.AS_BF16, 64, _p(), _p(), 8, ctypes.byref(mw), 77, _p(), L.AS_F32, 0,
+                                  None, None, _p(), 1 << 30, None)
+    assert st == L.AS_ERR_INVALID_ARG          # T * top_k > 256
+    st = lib.as_sparse_moe_expert(_p(), L.AS_BF16, 1, _p(), _p(), 8, ctypes.byref(mw), 800, _p(), L.AS_F32, 0,
+                                  None, None, _p(), 1 << 30, None)
+    assert st == L.AS_ERR_INVALID_ARG          # keep_k > d_ff_e
+    assert lib.as_gqa_decode_attention(_p(), _p(), _p(), _p(), _p(), L.AS_F16, 16, 32, 8, 128, _p(), _p(), 1 << 30,
+                                       None) == L.AS_ERR_UNSUPPORTED
+    assert lib.as_gqa_decode_attention(_p(), _p(), _p(), _p(), _p(), L.AS_BF16, 16, 32, 3, 128, _p(), _p(), 1 << 30,
+                                       None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_gqa_decode_attention(_p(), _p(), _p(), _p(), _p(), L.AS_BF16, 16, 64, 4, 128, _p(), _p(), 1 << 30,
+                                       None) == L.AS_ERR_UNSUPPORTED       # group of 16 > 8
+    assert lib.as_rmsnorm(None, L.AS_F32, 1, 64, 1e-5, _p(), None, None) == L.AS_ERR_INVALID_ARG
+    w = L.ASMlpWeights(_p(), None, L.AS_F16, 4096, 14336)
+    assert lib.as_glass_local_signal(_p(), L.AS_BF16, 128, ctypes.byref(w), _p(), None) == L.AS_ERR_UNSUPPORTED
+    bw = L.ASBlockWeights(_p(), _p(), L.ASMlpWeights(_p(), _p(), L.AS_BF16, 4096, 14336), 32, 8, 128)
+    need = lib.as_decoder_block_ws_size(ctypes.byref(bw), 2048)
+    assert need > 0
+    th = L.ASBlockThresholds(0.5, 0.5, 0.5, 0.5)
+    assert lib.as_decoder_block(_p(), L.AS_BF16, ctypes.byref(bw), _p(), _p(), 2048, ctypes.byref(th), _p(), 0,
+                                None, _p(), need - 256, None) == L.AS_ERR_WORKSPACE
 
 
 def test_workspace_init_and_flush_validation(lib):
