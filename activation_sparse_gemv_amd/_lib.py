@@ -16,6 +16,7 @@ AS_F16, AS_BF16, AS_F32 = 0, 1, 2
 AS_FLAG_ACCUMULATE = 1 << 0
 AS_FLAG_NO_NT_LOADS = 1 << 2
 AS_FLAG_FORCE_DENSE = 1 << 3
+AS_FLAG_NO_FUSION = 1 << 4
 AS_MLP_THRESHOLD, AS_MLP_NEURON_SET = 0, 1
 AS_TOPK_VALUE, AS_TOPK_RANK_BLEND = 0, 1
 

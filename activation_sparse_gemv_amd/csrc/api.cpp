@@ -124,11 +124,15 @@ struct MlpWs {
   int* l_cnt;
   int* l_idx;
   float* l_val;
+  unsigned* queue;        // [0] next item, [1] exit count, [2] error flag (persistent kernel)
+  unsigned* tile_done;    // [n_lt]
 };
 
 struct MlpPlan {
   Plan p1, p2;
   int n_lt, lt_stride;
+  int parts2;             // partial slots of the down stage (max of its split and the h-tiles)
+  int s2_tiles, cap2_tiles;  // down stage over whole h-tiles: slices and their max list entries
 };
 
 MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
@@ -144,6 +148,16 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
   }
   (void)dense;
   mp.p2 = plan_gemv(w->d_ff, w->d_model, false, "AS_DN");
+  mp.parts2 = mp.p2.S > mp.n_lt ? mp.p2.S : mp.n_lt;
+  {
+    // threshold mode: each down slice owns whole h-tiles (about 1.75 workgroups per CU)
+    const int target = (7 * num_cus()) / 4;
+    int tpw = (int)((long)mp.n_lt * mp.p2.n_tiles / (target > 0 ? target : 1));
+    tpw = env_int("AS_DN_TPW", tpw < 1 ? 1 : tpw);
+    if (tpw < 1) tpw = 1;
+    mp.s2_tiles = (mp.n_lt + tpw - 1) / tpw;
+    mp.cap2_tiles = ((mp.n_lt + mp.s2_tiles - 1) / mp.s2_tiles) * mp.lt_stride;
+  }
   (void)M;
   return mp;
 }
@@ -152,11 +166,15 @@ MlpWs carve_mlp(Carver& c, const MlpPlan& mp, int M, const as_mlp_weights* w, as
   MlpWs ws;
   if (mode == AS_MLP_THRESHOLD) ws.g1 = carve_gemv(c, mp.p1, M, 2L * w->d_ff);
   else ws.g1 = GemvWs{nullptr, nullptr};
-  ws.g2 = carve_gemv(c, mp.p2, M, w->d_model);
+  Plan p2 = mp.p2;
+  p2.S = mp.parts2;
+  ws.g2 = carve_gemv(c, p2, M, w->d_model);
   ws.h = c.take<float>(size_t(M) * w->d_ff);
   ws.l_cnt = c.take<int>(mp.n_lt);
   ws.l_idx = c.take<int>(w->d_ff);
   ws.l_val = c.take<float>(size_t(w->d_ff) * M);
+  ws.queue = c.take<unsigned>(4);
+  ws.tile_done = c.take<unsigned>(mp.n_lt);
   return ws;
 }
 
@@ -336,6 +354,44 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   GemvParams p2 = base_params();
   GemvConfig c2{int(w->w_dt), mt, mp.p2.lpr, IN_LISTS, OUT_Y, false, nt};
 
+  const bool fused = mode == AS_MLP_THRESHOLD && mt <= 8 && nt && (flags & AS_FLAG_NO_FUSION) == 0 &&
+                     env_int("AS_FUSED", 0) != 0 && (mp.p1.lpr == 32 || mp.p1.lpr == 64) &&
+                     (mp.p2.lpr == 16 || mp.p2.lpr == 64);
+  if (fused) {
+    // one persistent launch: gate/up items, then down items as their h-tiles complete
+    FusedMlpParams fz;
+    memset(&fz, 0, sizeof fz);
+    GemvParams& q1 = fz.p1;
+    q1.x = X; q1.x_dt = int(x_dt); q1.M = M; q1.K = d; q1.ldx = d; q1.t = dense ? -INFINITY : t_x;
+    q1.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); q1.ldw = 2L * f; q1.N = f; q1.gu_off = f;
+    q1.n_tiles = mp.p1.n_tiles; q1.S = mp.p1.S; q1.cap = mp.p1.cap;
+    q1.partials = mw.g1.partials; q1.counters = mw.g1.counters; q1.part_ld = 2L * f;
+    q1.t_h = dense ? -INFINITY : t_h; q1.h = hbuf; q1.ldh = f;
+    q1.o_cnt = mw.l_cnt; q1.o_idx = mw.l_idx; q1.o_val = mw.l_val; q1.tile_done = mw.tile_done;
+    if (dbg && !dense) {
+      q1.h_bits = dbg->h_mask.bits; q1.h_bits_ld = (f + 63) / 64;
+      q1.x_bits = dbg->x_mask.bits; q1.x_bits_ld = (d + 63) / 64; q1.x_idx = dbg->x_mask.idx; q1.x_nnz = dbg->x_mask.nnz;
+    }
+    GemvParams& q2 = fz.p2;
+    q2.M = M; q2.W = reinterpret_cast<const uint16_t*>(w->w_down); q2.ldw = d; q2.N = d;
+    q2.list_cnt = mw.l_cnt; q2.list_idx = mw.l_idx; q2.list_val = mw.l_val;
+    q2.n_lt = 1; q2.lt_stride = mp.lt_stride; q2.coherent_lists = 1;
+    q2.n_tiles = mp.p2.n_tiles; q2.S = 1; q2.cap = mp.lt_stride;
+    q2.partials = mw.g2.partials; q2.counters = mw.g2.counters; q2.part_ld = d;
+    q2.y = Y; q2.y_dt = int(y_dt); q2.ldy = d; q2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
+    fz.n_tiles1 = mp.p1.n_tiles; fz.S1 = mp.p1.S; fz.items1 = fz.n_tiles1 * fz.S1; fz.n_ct2 = mp.p2.n_tiles;
+    fz.next = mw.queue; fz.exit_cnt = mw.queue + 1; fz.err = mw.queue + 2; fz.tile_done = mw.tile_done;
+    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : IN_THRESH, OUT_SWIGLU, true, true};
+    GemvConfig c2q{int(w->w_dt), mt, mp.p2.lpr, IN_LISTS, OUT_Y, false, true};
+    const size_t sm1 = gemv_smem_bytes(c1, q1.cap, 0), sm2 = gemv_smem_bytes(c2q, q2.cap, 1);
+    FusedCfg fc{int(w->w_dt), mt, mp.p1.lpr, mp.p2.lpr, dense ? IN_ALL : IN_THRESH,
+                dense ? 0 : pick_chunk_vectors(X, int(x_dt), d, d), env_int("AS_FUSED_WPC", 0), num_cus()};
+    if (mt > 1 && fc.nv > 2) fc.nv = 0;
+    if ((st = hip_check(launch_fused_mlp(fc, fz, sm1 > sm2 ? sm1 : sm2, stream), fn)) != AS_OK) return st;
+    if ((st = rec(1)) != AS_OK) return st;
+    return rec(2);
+  }
+
   if (mode == AS_MLP_THRESHOLD) {
     // stage 1: x mask -> gate/up gather GEMV -> SwiGLU -> h mask -> per-tile lists
     GemvParams p = base_params();
@@ -357,6 +413,8 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
     if (dense) {
       c2.in = IN_ALL;
       p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = -INFINITY;
+    } else if (env_int("AS_DN_TILES", 1)) {
+      c2.in = IN_TILES;
     }
   } else {
     // stage 1: gate/up dot products of the listed neurons (neuron-major rows)
@@ -377,6 +435,7 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   p2.n_lt = mp.n_lt; p2.lt_stride = mp.lt_stride;
   p2.N = d;
   p2.n_tiles = mp.p2.n_tiles; p2.S = mp.p2.S; p2.cap = mp.p2.cap;
+  if (c2.in == IN_TILES) { p2.S = mp.s2_tiles; p2.cap = mp.cap2_tiles; }
   p2.partials = mw.g2.partials; p2.counters = mw.g2.counters; p2.part_ld = d;
   p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;

@@ -11,7 +11,9 @@ size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
   const int nslot = 4 * (64 / c.lpr), tn = c.lpr * 8;
   size_t b = ((size_t(cap) * 4 + 15) & ~size_t(15)) + ((size_t(cap) * c.mt * 4 + 15) & ~size_t(15));
   b += (size_t(nslot > c.mt ? nslot : c.mt) * tn * 4 + 15) & ~size_t(15);
-  if (c.in == IN_LISTS) b += (size_t(n_lt + 1) * 4 + 15) & ~size_t(15);
+  if (c.in == IN_LISTS || c.in == IN_TILES) b += (size_t(n_lt + 1) * 4 + 15) & ~size_t(15);
+  // IN_TILES: raw candidate entries (index + M values) of the slice's tiles, cap of them
+  if (c.in == IN_TILES) b += size_t(cap) * (1 + c.mt) * 4;
   if (c.mt == 16) b += size_t(32) * (tn + 4) * 2;     // staged bf16 weight chunk of the MFMA loop
   return b;
 }
@@ -35,6 +37,26 @@ int pick_chunk_vectors(const void* x, int x_dt, int K, long ldx) {
   if (per <= 16) return 2;
   if (per <= 64) return 8;
   return 0;
+}
+
+hipError_t launch_fused_bf16_m1(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+hipError_t launch_fused_bf16_m2(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+hipError_t launch_fused_bf16_m4(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+hipError_t launch_fused_bf16_m8(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+hipError_t launch_fused_f16_m1(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+hipError_t launch_fused_f16_m2(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+hipError_t launch_fused_f16_m4(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+hipError_t launch_fused_f16_m8(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
+
+hipError_t launch_fused_mlp(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
+  const bool bf = c.wdt == DT_BF16;
+  switch (c.mt) {
+    case 1: return bf ? launch_fused_bf16_m1(c, f, smem, s) : launch_fused_f16_m1(c, f, smem, s);
+    case 2: return bf ? launch_fused_bf16_m2(c, f, smem, s) : launch_fused_f16_m2(c, f, smem, s);
+    case 4: return bf ? launch_fused_bf16_m4(c, f, smem, s) : launch_fused_f16_m4(c, f, smem, s);
+    case 8: return bf ? launch_fused_bf16_m8(c, f, smem, s) : launch_fused_f16_m8(c, f, smem, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s) {

@@ -41,13 +41,13 @@ __host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~size_t(
 // the ascending index list, M == 1 only, by the workgroups of column tile 0).
 template <int MT>
 __device__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_scan, int tid, int tile, int lo,
-                               int cnt) {
+                               int cnt, bool first) {
   const int K = p.K;
   const float t = p.t;
   const int M = p.M;
   const int C = (K + kThreads - 1) / kThreads;
   const int i0 = min(tid * C, K), i1 = min(i0 + C, K);
-  if (p.x_bits != nullptr && blockIdx.x == 0) {
+  if (p.x_bits != nullptr && first) {
     const int nw = (K + 63) / 64;
     for (int m = 0; m < M; ++m)
       for (int w = tid; w < nw; w += kThreads) {
@@ -59,7 +59,7 @@ __device__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_sca
         p.x_bits[m * p.x_bits_ld + w] = bits;
       }
   }
-  if (p.x_nnz != nullptr && blockIdx.x == 0) {
+  if (p.x_nnz != nullptr && first) {
     for (int m = 0; m < M; ++m) {
       int cm = 0;
       for (int i = i0; i < i1; ++i) cm += fabsf(load_elem(p.x, p.x_dt, m * p.ldx + i)) > t;
@@ -171,11 +171,16 @@ __device__ void mfma_main_loop(const GemvParams& p, const int* s_idx, const floa
   __syncthreads();
 }
 
+// One work item: column tile `tile`, row slice `sl` of S (p.S) equal parts of the
+// compacted row list; its partial tile is slot `part` of `n_parts` combined by
+// the last item of the tile to finish.  IN_LISTS reads list tiles
+// [lt0, lt0 + n_lt).  Used by the one-launch kernel below (items = blocks) and
+// by the persistent MLP kernel (items from a work queue).
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
-__global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams p) {
+__device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n_parts, int lt0, int n_lt,
+                          unsigned char* smem) {
   using TS = TileShape<LPR>;
   constexpr int RPW = TS::RPW, NSLOT = TS::NSLOT, TN = TS::TN, TB = TN / 2;
-  extern __shared__ __align__(16) unsigned char smem[];
   const int cap = p.cap;
   int* s_idx = reinterpret_cast<int*>(smem);
   float* s_val = reinterpret_cast<float*>(smem + align16(size_t(cap) * 4));
@@ -184,13 +189,12 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
                                        align16(size_t(NSLOT > MT ? NSLOT : MT) * TN * 4));
   // MT == 16 only: the bf16 weight chunk staged for the MFMA loop, after s_pref
   uint16_t* s_w = reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(s_pref) +
-                                              (IN == IN_LISTS ? align16(size_t(p.n_lt + 1) * 4) : 0));
+                                              ((IN == IN_LISTS || IN == IN_TILES) ? align16(size_t(p.n_lt + 1) * 4) : 0));
+  (void)n_lt;
   __shared__ int s_scan[kThreads / 64 + 1];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x % p.n_tiles;
-  const int sl = blockIdx.x / p.n_tiles;
   const int S = p.S;
   const int M = p.M;
 
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
         }
       }
     }
-    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt);
+    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
   } else if constexpr (IN == IN_THRESH) {
     const int K = p.K;
     const float t = p.t;
@@ -287,13 +291,12 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
         }
       }
     }
-    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt);
+    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
   } else if constexpr (IN == IN_LISTS) {
-    const int n_lt = p.n_lt;
     int run = 0;
     for (int base = 0; base < n_lt; base += kThreads) {
       const int q = base + tid;
-      const int v = q < n_lt ? p.list_cnt[q] : 0;
+      const int v = q < n_lt ? (p.coherent_lists ? load_coherent_i32(p.list_cnt + lt0 + q) : p.list_cnt[lt0 + q]) : 0;
       int tot;
       const int off = block_excl_scan<kThreads>(v, s_scan, &tot);
       if (q < n_lt) s_pref[q] = run + off;
@@ -311,10 +314,52 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
         const int mid = (a + b) >> 1;
         if (s_pref[mid] <= g) a = mid; else b = mid;
       }
-      const long e = (long)a * p.lt_stride + (g - s_pref[a]);
-      s_idx[r] = p.list_idx[e];
+      const long e = (long)(lt0 + a) * p.lt_stride + (g - s_pref[a]);
+      if (p.coherent_lists) {
+        s_idx[r] = load_coherent_i32(p.list_idx + e);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? p.list_val[e * M + m] : 0.f;
+        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? load_coherent(p.list_val + e * M + m) : 0.f;
+      } else {
+        s_idx[r] = p.list_idx[e];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? p.list_val[e * M + m] : 0.f;
+      }
+    }
+  } else if constexpr (IN == IN_TILES) {
+    // Slice sl owns whole list tiles [t0, t1).  Counts and every candidate entry of
+    // those tiles are loaded together (one round trip; entries past a tile's count
+    // are ignored), staged in LDS, then compacted in tile order.
+    const int t0 = (int)((long)sl * n_lt / S), t1 = (int)((long)(sl + 1) * n_lt / S);
+    const int nt = t1 - t0;
+    const int stride = p.lt_stride;
+    const int tot_e = nt * stride;
+    int* s_cnt = s_pref;                                   // [nt + 1]
+    int* r_idx = reinterpret_cast<int*>(s_w);              // [tot_e] raw candidates
+    float* r_val = reinterpret_cast<float*>(r_idx + tot_e);  // [tot_e][M]
+    if (tid < nt) s_cnt[tid] = p.list_cnt[lt0 + t0 + tid];
+    for (int e = tid; e < tot_e; e += kThreads) {
+      const long ge = (long)(lt0 + t0) * stride + e;
+      r_idx[e] = p.list_idx[ge];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        if (m < M) r_val[e * M + m] = p.list_val[ge * M + m];
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int q = 0; q < nt; ++q) { const int c = s_cnt[q]; s_cnt[q] = run; run += c; }
+      s_cnt[nt] = run;
+    }
+    __syncthreads();
+    cnt = s_cnt[nt];
+    for (int e = tid; e < tot_e; e += kThreads) {
+      const int q = e / stride, k = e % stride;
+      if (s_cnt[q] + k < s_cnt[q + 1]) {
+        const int r = s_cnt[q] + k;
+        s_idx[r] = r_idx[e];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? r_val[e * M + m] : 0.f;
+      }
     }
   } else {  // IN_ALL: every row, no mask (dense baseline)
     const int K = p.K;
@@ -424,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
   };
 
   // ------------------------------------------------------------ split-K combine
-  if (S > 1) {
+  if (n_parts > 1) {
     // Partials are written through to the device-coherent level (relaxed agent-scope
     // atomic stores) and the wave waits for their completion before the counter
     // increment; the last workgroup reads them back with coherent loads.  No
@@ -437,14 +482,14 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
       if (c < TN && ok)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (m < M) store_coherent(p.partials + ((long)sl * M + m) * p.part_ld + pc, res[m][q]);
+          if (m < M) store_coherent(p.partials + ((long)part * M + m) * p.part_ld + pc, res[m][q]);
     }
     wait_vmem();
     __syncthreads();
     if (tid == 0) {
       const unsigned prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
-      s_flag = (prev == unsigned(S - 1));
+      s_flag = (prev == unsigned(n_parts - 1));
     }
     __syncthreads();
     if (!s_flag) return;
@@ -467,20 +512,20 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
       float v[CPT];
 #pragma unroll
       for (int q = 0; q < CPT; ++q) v[q] = 0.f;
-      for (int s0 = 0; s0 < S; s0 += kBatch) {
+      for (int s0 = 0; s0 < n_parts; s0 += kBatch) {
         float tmp[CPT][kBatch];
 #pragma unroll
         for (int q = 0; q < CPT; ++q)
 #pragma unroll
           for (int k = 0; k < kBatch; ++k) {
-            const int s2 = min(s0 + k, S - 1);
+            const int s2 = min(s0 + k, n_parts - 1);
             tmp[q][k] = oks[q] ? load_coherent(p.partials + ((long)s2 * M + m) * p.part_ld + pcs[q]) : 0.f;
           }
 #pragma unroll
         for (int q = 0; q < CPT; ++q)
 #pragma unroll
           for (int k = 0; k < kBatch; ++k)
-            if (s0 + k < S) v[q] += tmp[q][k];
+            if (s0 + k < n_parts) v[q] += tmp[q][k];
       }
 #pragma unroll
       for (int q = 0; q < CPT; ++q) res[m][q] = v[q];
@@ -540,14 +585,121 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
       const int pos = block_excl_scan<kThreads>(flag, s_scan, &tot);
       if (flag) {
         const long e = (long)tile * TB + pos;
-        p.o_idx[e] = n;
+        store_coherent_i32(p.o_idx + e, n);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          if (m < M) p.o_val[e * M + m] = fabsf(hv[m]) > p.t_h ? hv[m] : 0.f;
+          if (m < M) store_coherent(p.o_val + e * M + m, fabsf(hv[m]) > p.t_h ? hv[m] : 0.f);
       }
-      if (tid == 0) p.o_cnt[tile] = tot;
+      if (tid == 0) store_coherent_i32(p.o_cnt + tile, tot);
+      if (p.tile_done != nullptr) {
+        // publish: the tile's list is complete before its flag is raised
+        wait_vmem();
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(p.tile_done + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
+}
+
+template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
+__global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tile = blockIdx.x % p.n_tiles, sl = blockIdx.x / p.n_tiles;
+  gemv_item<WDT, MT, LPR, IN, OUT, GU, NT, NV>(p, tile, sl, sl, p.S, 0, p.n_lt, smem);
+}
+
+// ---------------------------------------------------------------- persistent MLP
+// One launch for both stages of the threshold-mode SwiGLU MLP.  Workgroups take
+// items from a queue: first the gate/up items (tile-major, so whole tiles finish
+// early), then the down items (h-tile q, down column tile).  A down item waits
+// only for its own h-tile: the last gate/up item of tile q publishes the tile's
+// compacted h list with device-coherent stores and raises tile_done[q], so the
+// down projection of early tiles streams while later gate/up tiles are still in
+// flight, and there is no second launch, ramp-up or tail.  Every item a down
+// item can wait for was handed out earlier to a workgroup that is running, so
+// the wait always ends; it is bounded anyway and a timeout raises *err.
+template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
+__global__ __launch_bounds__(kThreads) void mlp_fused_kernel(const FusedMlpParams f) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_item;
+  const int tid = threadIdx.x;
+  const int total = f.items1 + f.n_tiles1 * f.n_ct2;
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) s_item = (int)__hip_atomic_fetch_add(f.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= total) break;
+    if (item < f.items1) {
+      const int tile = item / f.S1, sl = item % f.S1;
+      gemv_item<WDT, MT, LPR1, IN1, OUT_SWIGLU, true, true, NV>(f.p1, tile, sl, sl, f.S1, 0, 0, smem);
+    } else {
+      const int k = item - f.items1;
+      const int q = k / f.n_ct2, ct = k % f.n_ct2;
+      if (tid == 0) {
+        unsigned spins = 0;
+        while (__hip_atomic_load(f.tile_done + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > (1u << 24)) {
+            __hip_atomic_store(f.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      gemv_item<WDT, MT, LPR2, IN_LISTS, OUT_Y, false, true, 0>(f.p2, ct, 0, q, f.n_tiles1, q, 1, smem);
+    }
+  }
+  if (tid == 0) {
+    wait_vmem();
+    const unsigned prev = __hip_atomic_fetch_add(f.exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      for (int q = 0; q < f.n_tiles1; ++q)
+        __hip_atomic_store(f.tile_done + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f.next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f.exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
+hipError_t launch_fused_one(const FusedMlpParams& f, size_t smem, int wg_per_cu, int cus, hipStream_t s) {
+  auto k = mlp_fused_kernel<WDT, MT, LPR1, LPR2, IN1, NV>;
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), kThreads, smem) !=
+          hipSuccess || occ < 1)
+    occ = 1;
+  int per = wg_per_cu > 0 ? (wg_per_cu < occ ? wg_per_cu : occ) : occ;
+  int grid = per * cus;
+  const int total = f.items1 + f.n_tiles1 * f.n_ct2;
+  if (grid > total) grid = total;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), smem, s, f);
+  return hipGetLastError();
+}
+
+template <int WDT, int MT, int LPR1, int LPR2>
+hipError_t fused_pick_in(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
+  if (c.in1 == IN_ALL) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_ALL, 0>(f, smem, c.wg_per_cu, c.cus, s);
+  if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 2>(f, smem, c.wg_per_cu, c.cus, s);
+  if constexpr (MT == 1) {
+    if (c.nv == 8) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 8>(f, smem, c.wg_per_cu, c.cus, s);
+  }
+  return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 0>(f, smem, c.wg_per_cu, c.cus, s);
+}
+
+template <int WDT, int MT>
+hipError_t fused_pick(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
+  if (c.lpr1 == 64 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 64, 16>(c, f, smem, s);
+  if (c.lpr1 == 64 && c.lpr2 == 64) return fused_pick_in<WDT, MT, 64, 64>(c, f, smem, s);
+  if (c.lpr1 == 32 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 32, 16>(c, f, smem, s);
+  if (c.lpr1 == 32 && c.lpr2 == 64) return fused_pick_in<WDT, MT, 32, 64>(c, f, smem, s);
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -591,6 +743,7 @@ hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipS
   if (c.out != OUT_Y) return hipErrorInvalidValue;
   if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_LISTS) return pick_nt<WDT, MT, LPR, IN_LISTS, OUT_Y, false>(c, p, smem, s);
+  if (c.in == IN_TILES) return pick_nt<WDT, MT, LPR, IN_TILES, OUT_Y, false>(c, p, smem, s);
   return pick_nt<WDT, MT, LPR, IN_ALL, OUT_Y, false>(c, p, smem, s);
 }
 

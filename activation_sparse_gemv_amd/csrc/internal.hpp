@@ -7,7 +7,7 @@
 
 namespace as {
 
-enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2 };
+enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_TILES = 3 };
 enum { OUT_Y = 0, OUT_SWIGLU = 1 };
 
 // One row-gather GEMV launch: Y[m, c] = sum over listed rows i of xv[m, i] * W[i, c].
@@ -32,6 +32,9 @@ struct GemvParams {
   float t_h; float* h; long ldh; int* o_cnt; int* o_idx; float* o_val; uint64_t* h_bits; long h_bits_ld;
   // input-mask verification exports (IN_THRESH)
   uint64_t* x_bits; long x_bits_ld; int* x_idx; int* x_nnz;
+  // persistent MLP kernel: per-tile "list published" flags raised by the SwiGLU epilogue
+  unsigned* tile_done;
+  int coherent_lists;      // lists written by the same launch: read them device-coherently
 };
 
 struct GemvConfig {
@@ -46,7 +49,22 @@ struct GemvConfig {
 };
 
 size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt);
+
+// Persistent two-stage threshold MLP (one launch; see mlp_fused_kernel).
+struct FusedMlpParams {
+  GemvParams p1, p2;       // p1: gate/up items (S = S1); p2: down items over single h-tiles (S = 1)
+  int items1, n_tiles1, S1, n_ct2;
+  unsigned* next;
+  unsigned* exit_cnt;
+  unsigned* tile_done;     // [n_tiles1]
+  unsigned* err;
+};
+struct FusedCfg {
+  int wdt, mt, lpr1, lpr2, in1, nv, wg_per_cu, cus;
+};
+hipError_t launch_fused_mlp(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s);
+int pick_chunk_vectors(const void* x, int x_dt, int K, long ldx);
 
 // Neuron-major gate/up dot products for a neuron list (static neuron set).
 struct NeuronGuParams {

@@ -70,7 +70,8 @@ typedef enum { AS_F16 = 0, AS_BF16 = 1, AS_F32 = 2 } as_dtype;
 enum {
   AS_FLAG_ACCUMULATE = 1u << 0,   /* Y += result instead of Y = result                   */
   AS_FLAG_NO_NT_LOADS = 1u << 2,  /* plain (cached) weight loads instead of nontemporal  */
-  AS_FLAG_FORCE_DENSE = 1u << 3   /* ignore thresholds / neuron lists: dense baseline   */
+  AS_FLAG_FORCE_DENSE = 1u << 3,  /* ignore thresholds / neuron lists: dense baseline   */
+  AS_FLAG_NO_FUSION = 1u << 4     /* threshold MLP: two launches instead of one persistent */
 };
 
 /* Verification exports of a mask (every field may be NULL).
