@@ -1,0 +1,55 @@
+"""HIP-graph capture of library calls (the benchmark times sub-steps as graph
+replays): every replay must reproduce the eager result bit for bit, with eager
+work and synchronisations between replays."""
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_gemv_amd as asg
+from activation_sparse_gemv_amd import _lib as L
+from activation_sparse_gemv_amd import datagen
+from helpers import announce
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _capture(fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+        out = fn()
+    return g, out
+
+
+def test_graph_replays_match_eager():
+    announce("graph replays")
+    shape = datagen.MLPShape(1024, 4096, "bf16")
+    wgu, wd = datagen.mlp_weights_input_major(7, 0, shape)
+    w = asg.MLPWeights(wgu.to(DEV), wd.to(DEV))
+    x = datagen.student_t((1, 1024), 5).to(DEV)
+    sc = torch.rand(4096, device=DEV)
+    pr = torch.rand(4096, device=DEV)
+    eager_y = asg.as_sparse_swiglu_mlp(x, w, 0.7, 0.01).clone()
+    eager_k = asg.as_topk_mask(sc, 1000, prior=pr, lam=0.5)[1].clone()
+    Y = torch.empty((1, 1024), dtype=torch.float32, device=DEV)
+
+    def step():
+        asg.as_sparse_swiglu_mlp(x, w, 0.7, 0.01, Y=Y)
+        return asg.as_topk_mask(sc, 1000, prior=pr, lam=0.5)[1]
+
+    g, kout = _capture(step)
+    for rep in range(4):
+        Y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, eager_y), rep
+        assert torch.equal(kout, eager_k), rep
+        # eager work between replays
+        asg.as_sparse_swiglu_mlp(x, w, 0.3, 0.0)
+        torch.cuda.synchronize()
