@@ -228,7 +228,7 @@ as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64
                                  hipStream_t stream) {
   if (!pool || !t_out) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: NULL pointer");
   if (!is_dt(dt)) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: bad dtype %d", int(dt));
-  if (n < 1 || rank < 0 || rank > n)
+  if (n < 1 || n > 2147483647LL || rank < 0 || rank > n)
     return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: n=%lld rank=%lld", (long long)n, (long long)rank);
   return hip_check(launch_calibrate(pool, int(dt), n, rank, t_out, stream), "as_calibrate_threshold");
 }
@@ -548,8 +548,9 @@ as_status as_rmsnorm(const void* X, as_dtype x_dt, int rows, int d, float eps, f
 namespace {
 int attn_chunks(int n_ctx, int n_kv) {
   int c = (n_ctx + 1 + 63) / 64;
-  const int max_c = (2 * num_cus() + n_kv - 1) / n_kv;
+  const int max_c = (num_cus() + n_kv - 1) / n_kv;       // about one workgroup per CU
   if (c > max_c) c = max_c;
+  if (c > attention_max_chunks()) c = attention_max_chunks();
   if (c < 1) c = 1;
   return c;
 }
@@ -585,8 +586,10 @@ as_status as_gqa_decode_attention(const float* q, const float* k_new, const floa
   if (kv_dt != AS_BF16) return fail(AS_ERR_UNSUPPORTED, "%s: caches must be bf16", fn);
   if (n_ctx < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv || head_dim < 1)
     return fail(AS_ERR_INVALID_ARG, "%s: n_ctx=%d n_q=%d n_kv=%d hd=%d", fn, n_ctx, n_q, n_kv, head_dim);
-  if (n_q / n_kv > attention_max_group() || head_dim > attention_max_head_dim())
-    return fail(AS_ERR_UNSUPPORTED, "%s: group %d or head_dim %d too large", fn, n_q / n_kv, head_dim);
+  if (n_q / n_kv > attention_max_group() || head_dim != attention_head_dim())
+    return fail(AS_ERR_UNSUPPORTED, "%s: group %d (max 8) or head_dim %d (must be 128)", fn, n_q / n_kv, head_dim);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(AS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   Carver c{reinterpret_cast<char*>(ws)};
   AttnWs a = carve_attn(c, n_ctx, n_q, n_kv, head_dim);
   as_status st = check_ws(ws, ws_bytes, c.off);

@@ -152,6 +152,37 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Radix-select step, run by one full wave: given a 256-bin histogram, find the
+// bin holding the krem-th key counted from the top (from_top) or from the bottom,
+// and the rank of that key inside the bin.  Lane l owns bins 4l..4l+3; the
+// counts above (below) a lane come from a wave suffix (prefix) scan, so the
+// search is a few shuffles instead of a 256-step serial walk.
+__device__ __forceinline__ void wave_select_bin(const unsigned* hist, int krem, bool from_top, int* bin_out,
+                                                int* krem_out) {
+  const int l = lane_id();
+  int c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c[q] = (int)hist[4 * l + q];
+  const int local = c[0] + c[1] + c[2] + c[3];
+  // inclusive scan in the direction of the walk
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = from_top ? __shfl_down(incl, o, 64) : __shfl_up(incl, o, 64);
+    if (from_top ? (l + o < 64) : (l >= o)) incl += t;
+  }
+  int run = incl - local;             // keys in bins strictly before this lane's bins (walk order)
+  int found = -1, rem = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int qq = from_top ? 3 - q : q;
+    const int b = 4 * l + qq;
+    if (found < 0 && run < krem && krem <= run + c[qq]) { found = b; rem = krem - run; }
+    run += c[qq];
+  }
+  if (found >= 0) { *bin_out = found; *krem_out = rem; }
+}
+
 // Exclusive scan over a workgroup of NT threads (NT a multiple of 64, <= 1024).
 // `sm` needs NT/64 + 1 ints.  Returns the exclusive prefix; *total = the sum.
 template <int NT>

@@ -45,50 +45,75 @@ hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, f
 // keys against the n_q / n_kv query heads of the group, keeps the chunk's
 // running max and exp-sum, and its unnormalised partial output; the last chunk
 // of a kv head to finish merges the chunks in chunk order (deterministic).
+// Loads are 16-byte: four lanes share one 256-byte key row for the scores, and
+// sixteen lanes one value row for the output.
 constexpr int kAttThreads = 256;
 constexpr int kMaxGroup = 8;      // query heads per kv head
-constexpr int kMaxHd = 256;
+constexpr int kAttHd = 128;       // head dimension of the vectorised path
+constexpr int kMaxChunks = 64;
+
+__device__ __forceinline__ void kv_row8(const uint16_t* cache, const float* fresh, bool from_cache, long off,
+                                        float v[8]) {
+  if (from_cache) {
+    unpack8<DT_BF16>(*reinterpret_cast<const u32x4*>(cache + off), v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fresh[off + e];
+  }
+}
 
 __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams p) {
   extern __shared__ __align__(16) float sm[];
-  const int hd = p.head_dim, grp = p.n_q / p.n_kv;
+  constexpr int hd = kAttHd;
+  const int grp = p.n_q / p.n_kv;
   const int g = blockIdx.x, c = blockIdx.y, C = gridDim.y;
   const int n_keys = p.n_ctx + 1;
   const int j0 = (int)((long)c * n_keys / C), j1 = (int)((long)(c + 1) * n_keys / C);
   const int nk = j1 - j0;
   float* qs = sm;                          // [grp][hd]  (pre-scaled)
-  float* sc = qs + grp * hd;               // [grp][chunk]
+  float* sc = qs + grp * hd;               // [grp][nk]
+  float* red = sc + grp * ((nk + 3) & ~3); // [16][grp][hd] output partials per key group
   __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
+  __shared__ float s_ml[kMaxChunks * kMaxGroup * 2];
   __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int i = threadIdx.x; i < grp * hd; i += kAttThreads) {
+  for (int i = tid; i < grp * hd; i += kAttThreads) {
     const int qh = g * grp + i / hd, dd = i % hd;
     qs[i] = p.q[(long)qh * hd + dd] * scale;
   }
   __syncthreads();
-  // scores: wave w takes keys j0 + w, j0 + w + 4, ...; lanes split the head dim
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int j = j0 + wave; j < j1; j += kAttThreads / 64) {
-    float part[kMaxGroup];
+  // scores: four lanes per key, 32 dimensions (four 16-byte loads) each
+  {
+    const int part = tid & 3, d0 = part * 32;
+    for (int jj = tid >> 2; jj < nk; jj += kAttThreads / 4) {
+      const int j = j0 + jj;
+      const bool fromc = j < p.n_ctx;
+      const long off = fromc ? ((long)j * p.n_kv + g) * hd + d0 : (long)g * hd + d0;
+      float acc[kMaxGroup];
 #pragma unroll
-    for (int a = 0; a < kMaxGroup; ++a) part[a] = 0.f;
-    for (int dd = lane; dd < hd; dd += 64) {
-      const float kv = j < p.n_ctx ? bf16_bits_to_f32(p.k_cache[((long)j * p.n_kv + g) * hd + dd])
-                                   : p.k_new[(long)g * hd + dd];
+      for (int a = 0; a < kMaxGroup; ++a) acc[a] = 0.f;
 #pragma unroll
-      for (int a = 0; a < kMaxGroup; ++a)
-        if (a < grp) part[a] = fmaf(qs[a * hd + dd], kv, part[a]);
-    }
+      for (int v8 = 0; v8 < 4; ++v8) {
+        float kv[8];
+        kv_row8(p.k_cache, p.k_new, fromc, off + v8 * 8, kv);
 #pragma unroll
-    for (int a = 0; a < kMaxGroup; ++a) {
-      if (a < grp) {
-        const float s = wave_sum(part[a]);
-        if (lane == 0) sc[a * nk + (j - j0)] = s;
+        for (int a = 0; a < kMaxGroup; ++a)
+          if (a < grp)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[a] = fmaf(qs[a * hd + d0 + v8 * 8 + e], kv[e], acc[a]);
+      }
+#pragma unroll
+      for (int a = 0; a < kMaxGroup; ++a) {
+        float v = acc[a];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        if (part == 0 && a < grp) sc[a * nk + jj] = v;
       }
     }
   }
   __syncthreads();
-  // chunk softmax statistics per query head (one wave per head, looping)
+  // chunk softmax statistics per query head (one wave per head)
   for (int a = wave; a < grp; a += kAttThreads / 64) {
     float m = -INFINITY;
     for (int t = lane; t < nk; t += 64) m = fmaxf(m, sc[a * nk + t]);
@@ -104,16 +129,39 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     if (lane == 0) { s_m[a] = m; s_l[a] = l; }
   }
   __syncthreads();
-  // unnormalised partial outputs: thread -> (head a, dim dd)
-  for (int i = threadIdx.x; i < grp * hd; i += kAttThreads) {
+  // unnormalised partial outputs: thread = (key group kg of 16, 8 dims dg of 16)
+  {
+    const int dg = tid & 15, kg = tid >> 4;
+    float acc[kMaxGroup][8];
+#pragma unroll
+    for (int a = 0; a < kMaxGroup; ++a)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
+    for (int jj = kg; jj < nk; jj += 16) {
+      const int j = j0 + jj;
+      const bool fromc = j < p.n_ctx;
+      const long off = fromc ? ((long)j * p.n_kv + g) * hd + dg * 8 : (long)g * hd + dg * 8;
+      float vv[8];
+      kv_row8(p.v_cache, p.v_new, fromc, off, vv);
+#pragma unroll
+      for (int a = 0; a < kMaxGroup; ++a)
+        if (a < grp) {
+          const float pa = sc[a * nk + jj];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(pa, vv[e], acc[a][e]);
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < kMaxGroup; ++a)
+      if (a < grp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[(kg * grp + a) * hd + dg * 8 + e] = acc[a][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < grp * hd; i += kAttThreads) {
     const int a = i / hd, dd = i % hd;
     float o = 0.f;
-    for (int t = 0; t < nk; ++t) {
-      const int j = j0 + t;
-      const float vv = j < p.n_ctx ? bf16_bits_to_f32(p.v_cache[((long)j * p.n_kv + g) * hd + dd])
-                                   : p.v_new[(long)g * hd + dd];
-      o = fmaf(sc[a * nk + t], vv, o);
-    }
+    for (int kg = 0; kg < 16; ++kg) o += red[(kg * grp + a) * hd + dd];
     const long base = ((long)g * C + c) * grp + a;          // partial record index
     store_coherent(p.part_o + base * hd + dd, o);
     if (dd == 0) {
@@ -123,24 +171,37 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   }
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(p.counters + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == unsigned(C - 1);
     if (s_last) __hip_atomic_store(p.counters + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last) return;
-  // merge: O = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c
-  for (int i = threadIdx.x; i < grp * hd; i += kAttThreads) {
+  // merge: O = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c, chunk statistics in one round trip
+  for (int i = tid; i < C * grp * 2; i += kAttThreads) s_ml[i] = load_coherent(p.part_ml + (long)g * C * grp * 2 + i);
+  __syncthreads();
+  for (int i = tid; i < grp * hd; i += kAttThreads) {
     const int a = i / hd, dd = i % hd;
     float M = -INFINITY;
-    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, load_coherent(p.part_ml + (((long)g * C + cc) * grp + a) * 2));
+    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, s_ml[(cc * grp + a) * 2]);
     float L = 0.f, O = 0.f;
-    for (int cc = 0; cc < C; ++cc) {
-      const long base = ((long)g * C + cc) * grp + a;
-      const float w = expf(load_coherent(p.part_ml + base * 2) - M);
-      L = fmaf(w, load_coherent(p.part_ml + base * 2 + 1), L);
-      O = fmaf(w, load_coherent(p.part_o + base * hd + dd), O);
+    for (int c0 = 0; c0 < C; c0 += 16) {
+      float ov[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int cc = min(c0 + k, C - 1);
+        ov[k] = load_coherent(p.part_o + (((long)g * C + cc) * grp + a) * hd + dd);
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int cc = c0 + k;
+        if (cc < C) {
+          const float w = expf(s_ml[(cc * grp + a) * 2] - M);
+          L = fmaf(w, s_ml[(cc * grp + a) * 2 + 1], L);
+          O = fmaf(w, ov[k], O);
+        }
+      }
     }
     p.o[(long)(g * grp + a) * hd + dd] = O / L;
   }
@@ -150,7 +211,8 @@ hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s) {
   const int grp = p.n_q / p.n_kv;
   const int n_keys = p.n_ctx + 1;
   const int max_chunk = (n_keys + chunks - 1) / chunks;
-  const size_t smem = size_t(grp) * p.head_dim * 4 + size_t(grp) * max_chunk * 4;
+  const size_t smem = size_t(grp) * kAttHd * 4 + size_t(grp) * ((max_chunk + 3) & ~3) * 4 +
+                      size_t(16) * grp * kAttHd * 4;
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
@@ -161,6 +223,7 @@ hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s) {
 }
 
 int attention_max_group() { return kMaxGroup; }
-int attention_max_head_dim() { return kMaxHd; }
+int attention_head_dim() { return kAttHd; }
+int attention_max_chunks() { return kMaxChunks; }
 
 }  // namespace as

@@ -104,7 +104,8 @@ struct AttnParams {
 hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, float* y, float* copy, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s);
 int attention_max_group();
-int attention_max_head_dim();
+int attention_head_dim();
+int attention_max_chunks();
 
 // GLASS local signal (see glass.hip).
 hipError_t launch_local_signal(const uint16_t* X, int P, int d, const uint16_t* W, long ld_neuron, long up_off,

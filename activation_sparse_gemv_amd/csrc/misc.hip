@@ -52,6 +52,7 @@ __global__ __launch_bounds__(kCalThreads) void calibrate_kernel(const void* pool
   __shared__ unsigned hist[256];
   __shared__ uint32_t s_prefix;
   __shared__ int64_t s_krem;
+  __shared__ int s_bin, s_binrem;
   if (rank == 0) {
     if (threadIdx.x == 0) *t_out = -INFINITY;
     return;
@@ -68,15 +69,11 @@ __global__ __launch_bounds__(kCalThreads) void calibrate_kernel(const void* pool
       if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
     }
     __syncthreads();
+    if (threadIdx.x < 64) wave_select_bin(hist, (int)s_krem, false, &s_bin, &s_binrem);
+    __syncthreads();
     if (threadIdx.x == 0) {
-      int64_t krem = s_krem;
-      int b = 0;
-      for (; b < 255; ++b) {
-        if ((int64_t)hist[b] >= krem) break;
-        krem -= hist[b];
-      }
-      s_prefix = prefix | ((uint32_t)b << shift);
-      s_krem = krem;
+      s_prefix = prefix | ((uint32_t)s_bin << shift);
+      s_krem = s_binrem;
     }
     __syncthreads();
   }

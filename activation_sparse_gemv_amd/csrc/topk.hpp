@@ -27,6 +27,7 @@ struct TopkSmem {
   int wave_cnt[32];
   uint32_t prefix;
   int krem;
+  int sel_bin, sel_krem;
   int run_eq, run_sel;
 };
 
@@ -54,15 +55,11 @@ __device__ void block_topk(KeyFn key, int n, int k, uint64_t* mask, int* idx, To
         if ((kk & hi_mask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & 0xffu], 1u);
       }
       __syncthreads();
+      if (w == 0) wave_select_bin(sm.hist, sm.krem, true, &sm.sel_bin, &sm.sel_krem);
+      __syncthreads();
       if (tid == 0) {
-        int krem = sm.krem;
-        int b = 255;
-        for (; b > 0; --b) {
-          if ((int)sm.hist[b] >= krem) break;
-          krem -= (int)sm.hist[b];
-        }
-        sm.prefix = prefix | ((uint32_t)b << shift);
-        sm.krem = krem;
+        sm.prefix = prefix | ((uint32_t)sm.sel_bin << shift);
+        sm.krem = sm.sel_krem;
       }
       __syncthreads();
     }

@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="counter run: a 256 MiB device copy (known bytes) then 16 headline sparse-MLP calls")
     return ap.parse_args()
 
 
@@ -557,6 +559,38 @@ def row_small(C, cpu):
     return r
 
 
+def traffic_run(C):
+    """For rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: one plain device copy of
+    256 MiB (the counters' scale reference), then 16 sparse MLP calls of the headline
+    workload rotating over 8 layer copies; prints the active bytes of each call."""
+    torch, asg, datagen = C.torch, C.asg, C.datagen
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=C.dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    shape = datagen.CFG2
+    d, f = shape.d_model, shape.d_ff
+    wgu, wd = datagen.mlp_weights_input_major(2, 0, shape)
+    w0 = asg.MLPWeights(wgu.to(C.dev), wd.to(C.dev))
+    layers = [w0] + [asg.MLPWeights(w0.w_gate_up.clone(), w0.w_down.clone()) for _ in range(7)]
+    calib = datagen.student_t((256, d), datagen.seed_for(2, 0, "calib")).to(C.dev)
+    toks = datagen.student_t((64, d), datagen.seed_for(2, 0, "decode")).to(C.dev)
+    t_x = float(asg.as_calibrate_threshold(calib, 0.5).item())
+    hs = [asg.as_sparse_swiglu_mlp(calib[b:b + 16], w0, t_x, float("-inf"), debug=True)[1]["h"].clone()
+          for b in range(0, 256, 16)]
+    t_h = float(asg.as_calibrate_threshold(torch.cat(hs), 0.5).item())
+    torch.cuda.synchronize()
+    for i in range(16):
+        y, dbg = asg.as_sparse_swiglu_mlp(toks[i], layers[i % 8], t_x, t_h, debug=True)
+        torch.cuda.synchronize()
+        nx = int((toks[i].float().abs() > t_x).sum().item())
+        nh = int((dbg["h"][0].abs() > t_h).sum().item())
+        print(json.dumps({"call": i, "gate_up_active_bytes": nx * 2 * f * 2, "down_active_bytes": nh * d * 2}),
+              flush=True)
+    print(json.dumps({"copy_bytes": src.numel(), "kernel_source_sha256": kernel_source_hash()}), flush=True)
+
+
 # ============================================================================ main
 def main():
     a = parse()
@@ -573,6 +607,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     C = Ctx(torch, asg, L, datagen, dev)
+    if a.traffic_run:
+        traffic_run(C)
+        return
     out, t_x, t_h = headline(a, C)
     cpu = not a.no_cpu_baseline
     if not a.headline_only:

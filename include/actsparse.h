@@ -99,7 +99,8 @@ as_status as_workspace_init(void *ws, size_t bytes, hipStream_t stream);
  *   rank = 0 gives -INFINITY (sparsity 0 keeps every input).
  * The caller computes rank = ceil(p * n).  NaN magnitudes order above +inf.
  * pool: [n] of dtype dt (f16/bf16/f32).  t_out: one device float.
- * Errors: INVALID_ARG if pool/t_out is NULL, n < 1, rank < 0 or rank > n. */
+ * Errors: INVALID_ARG if pool/t_out is NULL, n < 1 or n >= 2^31, rank < 0 or
+ * rank > n. */
 as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64_t rank,
                                  float *t_out, hipStream_t stream);
 
@@ -264,7 +265,7 @@ as_status as_rmsnorm(const void *X, as_dtype x_dt, int rows, int d, float eps,
  * of kv head h / (n_q / n_kv) followed by the current token's k_new / v_new.
  * q: [n_q, hd] fp32; k_new, v_new: [n_kv, hd] fp32; caches: [n_ctx, n_kv, hd]
  * (AS_BF16 only); o: [n_q, hd] fp32.  n_q % n_kv == 0, n_q / n_kv <= 8,
- * head_dim <= 256, n_ctx >= 0. */
+ * head_dim == 128, n_ctx >= 0. */
 size_t as_gqa_decode_attention_ws_size(int n_ctx, int n_q, int n_kv, int head_dim);
 as_status as_gqa_decode_attention(const float *q, const float *k_new, const float *v_new,
                                   const void *k_cache, const void *v_cache, as_dtype kv_dt,

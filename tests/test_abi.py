@@ -126,6 +126,8 @@ def test_topk_moe_block_validation(lib):
                                        None) == L.AS_ERR_INVALID_ARG
     assert lib.as_gqa_decode_attention(_p(), _p(), _p(), _p(), _p(), L.AS_BF16, 16, 64, 4, 128, _p(), _p(), 1 << 30,
                                        None) == L.AS_ERR_UNSUPPORTED       # group of 16 > 8
+    assert lib.as_gqa_decode_attention(_p(), _p(), _p(), _p(), _p(), L.AS_BF16, 16, 32, 8, 64, _p(), _p(), 1 << 30,
+                                       None) == L.AS_ERR_UNSUPPORTED       # head_dim != 128
     assert lib.as_rmsnorm(None, L.AS_F32, 1, 64, 1e-5, _p(), None, None) == L.AS_ERR_INVALID_ARG
     w = L.ASMlpWeights(_p(), None, L.AS_F16, 4096, 14336)
     assert lib.as_glass_local_signal(_p(), L.AS_BF16, 128, ctypes.byref(w), _p(), None) == L.AS_ERR_UNSUPPORTED

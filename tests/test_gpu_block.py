@@ -23,8 +23,8 @@ def test_rmsnorm():
         assert np.array_equal(f64(c), f64(x))
 
 
-@pytest.mark.parametrize("n_ctx,n_q,n_kv,hd", [(2048, 32, 8, 128), (0, 4, 2, 64), (1, 8, 8, 128),
-                                               (300, 16, 2, 64), (5000, 32, 8, 128)])
+@pytest.mark.parametrize("n_ctx,n_q,n_kv,hd", [(2048, 32, 8, 128), (0, 4, 2, 128), (1, 8, 8, 128),
+                                               (300, 16, 2, 128), (5000, 32, 8, 128), (70, 8, 1, 128)])
 def test_attention(n_ctx, n_q, n_kv, hd):
     announce(f"attention n_ctx={n_ctx}")
     rng = np.random.default_rng(n_ctx + n_q)
