@@ -61,7 +61,12 @@ int env_int(const char* name, int dflt) {
   return v && *v ? atoi(v) : dflt;
 }
 
-Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix) {
+// LDS per workgroup on gfx950, and what a plan keeps free of it beyond the row list
+// and its activations (slot reduction or staged MFMA chunk, list prefix sums).
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kLdsReserve = 40 * 1024;
+
+Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
   // Tile width: lanes_per_row * 8 columns.  Wider tiles give longer bursts per
   // row; narrower tiles give more tiles (less split-K, cheaper final combine).
   const long tot_cols = gu ? 2L * cols : cols;
@@ -72,7 +77,6 @@ Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix) {
   char key[64];
   snprintf(key, sizeof key, "%s_LPR", env_prefix);
   lpr = env_int(key, lpr);
-  if (gu && lpr < 32) lpr = 32;
   const int tn = lpr * 8;
   const int n_tiles = gu ? (cols + tn / 2 - 1) / (tn / 2) : (cols + tn - 1) / tn;
   // Slices: about 1.75 workgroups per CU in total, at least ~24 rows per slice.
@@ -87,10 +91,20 @@ Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix) {
   if (S > smax) S = smax;
   if (S > 256) S = 256;
   if (S < 1) S = 1;
+  // The row list and its activations ([mt][cap] fp32) sit in LDS: the matrix-core
+  // path (mt 16) keeps slices at <= 512 rows so two workgroups share a CU, and every
+  // plan, forced ones included, stays within the LDS of one workgroup.
+  const int hard_cap = (kLdsBytes - kLdsReserve) / (4 + 4 * mt);
+  if (mt >= 16) {
+    const int s16 = (rows + 511) / 512;
+    if (S < s16) S = s16;
+  }
   snprintf(key, sizeof key, "%s_S", env_prefix);
   S = env_int(key, S);
   if (S < 1) S = 1;
-  const int cap = (rows + S - 1) / S;
+  if ((rows + S - 1) / S > hard_cap) S = (rows + hard_cap - 1) / hard_cap;
+  // multiple of 8 rows: the MFMA loop reads activations as aligned 16-byte vectors
+  const int cap = (((rows + S - 1) / S) + 7) & ~7;
   return Plan{lpr, n_tiles, S, cap};
 }
 
@@ -138,7 +152,7 @@ struct MlpPlan {
 MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
   MlpPlan mp;
   if (mode == AS_MLP_THRESHOLD) {
-    mp.p1 = plan_gemv(w->d_model, w->d_ff, true, "AS_GU");
+    mp.p1 = plan_gemv(w->d_model, w->d_ff, true, "AS_GU", mt_for(M));
     mp.n_lt = mp.p1.n_tiles;
     mp.lt_stride = mp.p1.lpr * 4;   // tile neurons = tile columns / 2
   } else {
@@ -147,18 +161,23 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     mp.lt_stride = w->d_ff;
   }
   (void)dense;
-  mp.p2 = plan_gemv(w->d_ff, w->d_model, false, "AS_DN");
+  mp.p2 = plan_gemv(w->d_ff, w->d_model, false, "AS_DN", mt_for(M));
   mp.parts2 = mp.p2.S > mp.n_lt ? mp.p2.S : mp.n_lt;
   {
     // threshold mode: each down slice owns whole h-tiles (about 1.75 workgroups per CU)
     const int target = (7 * num_cus()) / 4;
     int tpw = (int)((long)mp.n_lt * mp.p2.n_tiles / (target > 0 ? target : 1));
+    // list entries per slice: index + activations in LDS twice (raw, then compacted)
+    const int mt = mt_for(M);
+    const int hard_e = (kLdsBytes - kLdsReserve) / (8 + 8 * mt);
+    const int pref_e = mt >= 16 ? 512 : hard_e;
+    if (tpw * mp.lt_stride > pref_e) tpw = pref_e / mp.lt_stride;
     tpw = env_int("AS_DN_TPW", tpw < 1 ? 1 : tpw);
+    if (tpw * mp.lt_stride > hard_e) tpw = hard_e / mp.lt_stride;
     if (tpw < 1) tpw = 1;
     mp.s2_tiles = (mp.n_lt + tpw - 1) / tpw;
     mp.cap2_tiles = ((mp.n_lt + mp.s2_tiles - 1) / mp.s2_tiles) * mp.lt_stride;
   }
-  (void)M;
   return mp;
 }
 
@@ -236,7 +255,7 @@ as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64
 // ------------------------------------------------------------------ GEMV
 size_t as_threshold_gemv_ws_size(int M, int K, int N) {
   if (M < 1 || K < 1 || N < 1) return 0;
-  const Plan pl = plan_gemv(K, N, false, "AS_GV");
+  const Plan pl = plan_gemv(K, N, false, "AS_GV", mt_for(M));
   Carver c{nullptr};
   carve_gemv(c, pl, M, N);
   return c.off;
@@ -252,7 +271,7 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   if (K < 1 || N < 8 || N % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: K=%d N=%d (N must be a multiple of 8)", fn, K, N);
   if (!aligned16(W)) return fail(AS_ERR_INVALID_ARG, "%s: W not 16-byte aligned", fn);
   if (mo && mo->idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: mask idx export needs M == 1", fn);
-  const Plan pl = plan_gemv(K, N, false, "AS_GV");
+  const Plan pl = plan_gemv(K, N, false, "AS_GV", mt_for(M));
   Carver c{reinterpret_cast<char*>(ws)};
   GemvWs gw = carve_gemv(c, pl, M, N);
   as_status st = check_ws(ws, ws_bytes, c.off);

@@ -44,11 +44,15 @@ __device__ __forceinline__ void store_elem(void* p, int dt, long i, float v) {
   else reinterpret_cast<uint16_t*>(p)[i] = f32_to_f16_bits(v);
 }
 
-// 16-byte weight load (8 x 16-bit), nontemporal when nt is set: the rows are
+// 16-byte weight load (8 x 16-bit), nontemporal when NT is set: the rows are
 // streamed once per call, so they should not displace x, h and the partials.
-__device__ __forceinline__ u32x4 load_w16(const uint16_t* p, bool nt) {
+// NT is a compile-time choice: a runtime select between the two forms gets merged
+// into one plain load by the optimizer, which drops the nontemporal hint.
+template <bool NT>
+__device__ __forceinline__ u32x4 load_w16(const uint16_t* p) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  return nt ? __builtin_nontemporal_load(q) : *q;
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
 }
 
 // Unpack 8 weights (two per dword, low half first) to fp32.
@@ -100,6 +104,33 @@ __device__ __forceinline__ void load_chunk(const void* x, int dt, long off, int 
 #pragma unroll
     for (int e = 0; e < CE; ++e) v[e] = e < n ? load_elem(x, dt, off + e) : 0.f;
   }
+}
+
+// Values at input index i of tokens 0..MT-1 (token rows at or past M re-read row
+// M - 1 and read as 0).  The dtype test sits outside the loads, so all MT loads
+// issue back to back instead of one round trip per token.
+template <int MT>
+__device__ __forceinline__ void load_tokens(const void* x, int dt, long ldx, long i, int M, float (&v)[MT]) {
+  if (dt == DT_F32) {
+    const float* q = reinterpret_cast<const float*>(x) + i;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) v[m] = q[(long)(m < M ? m : M - 1) * ldx];
+  } else {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(x) + i;
+    uint32_t b[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) b[m] = q[(long)(m < M ? m : M - 1) * ldx];
+    if (dt == DT_BF16) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) v[m] = bf16_bits_to_f32(b[m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) v[m] = f16_bits_to_f32(b[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    if (m >= M) v[m] = 0.f;
 }
 
 // Wait until every vector-memory operation this wave issued has completed.

@@ -8,14 +8,23 @@ namespace as {
 constexpr int kThreadsHost = 256;
 
 size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
+  auto a16 = [](size_t b) { return (b + 15) & ~size_t(15); };
   const int nslot = 4 * (64 / c.lpr), tn = c.lpr * 8;
-  size_t b = ((size_t(cap) * 4 + 15) & ~size_t(15)) + ((size_t(cap) * c.mt * 4 + 15) & ~size_t(15));
-  b += (size_t(nslot > c.mt ? nslot : c.mt) * tn * 4 + 15) & ~size_t(15);
-  if (c.in == IN_LISTS || c.in == IN_TILES) b += (size_t(n_lt + 1) * 4 + 15) & ~size_t(15);
-  // IN_TILES: raw candidate entries (index + M values) of the slice's tiles, cap of them
-  if (c.in == IN_TILES) b += size_t(cap) * (1 + c.mt) * 4;
-  if (c.mt == 16) b += size_t(32) * (tn + 4) * 2;     // staged bf16 weight chunk of the MFMA loop
-  return b;
+  size_t b = a16(size_t(cap) * 4) + a16(size_t(cap) * c.mt * 4);
+  // slot reduction of the VALU loop (the MFMA loop stages its output in the chunk buffer)
+  if (c.mt != 16) b += a16(size_t(nslot > c.mt ? nslot : c.mt) * tn * 4);
+  if (c.in == IN_LISTS || c.in == IN_TILES) b += a16(size_t(n_lt + 1) * 4);
+  // staging region: IN_TILES raw candidate entries (index + M values, cap of them)
+  // during the prologue; the MFMA weight chunk and output tile afterwards
+  size_t stage = 0;
+  if (c.in == IN_TILES) stage = size_t(cap) * (1 + c.mt) * 4;
+  if (c.mt == 16) {
+    const size_t rows = size_t(32) * (512 / tn);
+    const size_t chunk = rows * (tn + 4) * 2, out = size_t(16) * tn * 4;
+    const size_t m = chunk > out ? chunk : out;
+    if (m > stage) stage = m;
+  }
+  return b + stage;
 }
 
 hipError_t launch_gemv_bf16_m16(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
@@ -61,7 +70,6 @@ hipError_t launch_fused_mlp(const FusedCfg& c, const FusedMlpParams& f, size_t s
 
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s) {
   const size_t smem = gemv_smem_bytes(c, p.cap, p.n_lt);
-  if (c.gu && c.lpr == 16) return hipErrorInvalidValue;
   GemvConfig cc = c;
   if (cc.in == IN_THRESH && cc.nv < 0) {
     cc.nv = pick_chunk_vectors(p.x, p.x_dt, p.K, p.ldx);

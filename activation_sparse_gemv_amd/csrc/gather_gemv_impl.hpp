@@ -74,39 +74,68 @@ __device__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_sca
   }
 }
 
+// Plain global -> LDS copy by the whole workgroup with eight loads in flight per
+// thread (the stores to LDS would otherwise wait on each load in turn).
+template <class T>
+__device__ __forceinline__ void copy_to_lds(T* dst, const T* src, int n) {
+  int j = threadIdx.x;
+  for (; j + 7 * kThreads < n; j += 8 * kThreads) {
+    T v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[j + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[j + u * kThreads] = v[u];
+  }
+  for (; j < n; j += kThreads) dst[j] = src[j];
+}
+
 // ---------------------------------------------------------------- MFMA main loop
 // Batches of 9..16 tokens: the per-row FMA count outgrows the VALU, so the
 // contraction runs on the matrix cores (v_mfma_f32_16x16x32_bf16).  MFMA wants
 // the reduction (row) index contiguous per lane, while input-major rows are
-// contiguous along the output columns, so each 32-row chunk of the tile is
-// staged through LDS (rows padded by 4 elements, which spreads the four lane
-// groups of a transposed read over distinct banks) and read back column-wise.
+// contiguous along the output columns, so each chunk of CR rows (32 KB of bf16
+// weights whatever the tile width) is staged through LDS (rows padded by 4
+// elements, which spreads the four lane groups of a transposed read over
+// distinct banks) and read back column-wise.  Two chunks are in flight per
+// workgroup: the loads of chunk c + 2 are issued as soon as chunk c has been
+// written to LDS, into the register buffer chunk c came from.
 // Activations are fp32 in LDS; each is split into bf16 hi + bf16 lo (x - hi),
 // two MFMAs per fragment, which keeps fp32 inputs (h, normalised x) to ~2^-16
 // relative precision while bf16 inputs stay exact.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+template <int TN>
+struct MfmaShape {
+  static constexpr int CR = 32 * (512 / TN);          // rows per staged chunk
+  static constexpr int LDW = TN + 4;                   // LDS row pitch (elements)
+  static constexpr int KS = CR / 32;                   // MFMA k-steps per chunk
+  static constexpr int VPT = CR * TN / 8 / kThreads;   // 16-byte vectors per thread per chunk
+  static constexpr size_t kBytes = size_t(CR) * LDW * 2;
+};
+
 template <int LPR, bool GU, bool NT>
-__device__ void mfma_main_loop(const GemvParams& p, const int* s_idx, const float* s_val, uint16_t* s_w, int cap,
-                               int cnt, int tile, float* s_out /* [16][TN] */) {
-  constexpr int TN = LPR * 8, TB = TN / 2, LDW = TN + 4;
+__device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s_idx, const float* s_val, uint16_t* s_w, int cap,
+                               int cnt, int tile, float* s_out /* [16][TN], aliases s_w */) {
+  constexpr int TN = LPR * 8, TB = TN / 2;
+  using MS = MfmaShape<TN>;
+  constexpr int CR = MS::CR, LDW = MS::LDW, KS = MS::KS, VPT = MS::VPT, VPR = TN / 8;
   constexpr int NB = TN / 16;              // 16-column blocks in the tile
   constexpr int NBW = NB / 4;              // blocks per wave
-  constexpr int VPT = TN / 64;             // 16-byte vectors per thread per 32-row chunk
+  static_assert(VPT * kThreads * 8 == CR * TN, "chunk must split evenly over the threads");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   f32x4_t acc[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // global source of each of this thread's vectors: tile row (0..31) and tile column (multiple of 8)
+  // global source of each of this thread's vectors: chunk row and tile column (multiple of 8)
   int vrow[VPT], vcol[VPT];
   long vsrc[VPT];
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
     const int v = tid + q * kThreads;
-    vrow[q] = v / (TN / 8);
-    vcol[q] = (v % (TN / 8)) * 8;
+    vrow[q] = v / VPR;
+    vcol[q] = (v % VPR) * 8;
     long gc;
     bool ok;
     if constexpr (GU) {
@@ -120,45 +149,76 @@ __device__ void mfma_main_loop(const GemvParams& p, const int* s_idx, const floa
     }
     vsrc[q] = ok ? gc : 0;
   }
-  const int nchunks = (cnt + 31) / 32;
-  u32x4 buf[VPT];
-  auto fetch = [&](int ch) {
+  const int nch = (cnt + CR - 1) / CR;
+  // rows past the end of the list repeat its last row (their activations are 0)
+  auto fetch = [&](int ch, u32x4 (&buf)[VPT]) {
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      const int row = s_idx[min(ch * 32 + vrow[q], cnt - 1)];
-      buf[q] = load_w16(p.W + (long)row * p.ldw + vsrc[q], NT);
+      const int row = s_idx[min(ch * CR + vrow[q], cnt - 1)];
+      buf[q] = load_w16<NT>(p.W + (long)row * p.ldw + vsrc[q]);
     }
   };
-  if (nchunks > 0) fetch(0);
-  for (int ch = 0; ch < nchunks; ++ch) {
-    __syncthreads();
+  // refill: issue the loads of chunk ch + 2 into buf once chunk ch is in LDS
+  auto step = [&](int ch, u32x4 (&buf)[VPT], bool refill) {
+    __syncthreads();                       // every wave is done reading the previous chunk
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(s_w + vrow[q] * LDW + vcol[q]);
-      dst[0] = buf[q].x; dst[1] = buf[q].y; dst[2] = buf[q].z; dst[3] = buf[q].w;
+      uint64_t* dst = reinterpret_cast<uint64_t*>(s_w + vrow[q] * LDW + vcol[q]);
+      dst[0] = (uint64_t)buf[q].x | ((uint64_t)buf[q].y << 32);
+      dst[1] = (uint64_t)buf[q].z | ((uint64_t)buf[q].w << 32);
     }
     __syncthreads();
-    if (ch + 1 < nchunks) fetch(ch + 1);
-    // A fragments: token li, rows 8g .. 8g+7 of the chunk, split into hi + lo
-    bf16x8_t ahi, alo;
+    if (refill) fetch(ch + 2, buf);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = ch * 32 + 8 * g + e;
-      const float x = r < cnt ? s_val[li * cap + r] : 0.f;
-      const uint16_t hb = f32_to_bf16_bits(x);
-      const float hf = bf16_bits_to_f32(hb);
-      const uint16_t lb = f32_to_bf16_bits(x - hf);
-      ahi[e] = __builtin_bit_cast(__bf16, hb);
-      alo[e] = __builtin_bit_cast(__bf16, lb);
+    for (int ks = 0; ks < KS; ++ks) {
+      // A fragment: token li, rows 8g .. 8g+7 of this k-step, split into hi + lo
+      const int r0 = ch * CR + ks * 32 + 8 * g;
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(s_val + li * cap + r0);
+      const f32x4_t xa = src[0], xb = src[1];
+      bf16x8_t ahi, alo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = r0 + e < cnt ? (e < 4 ? xa[e] : xb[e - 4]) : 0.f;
+        const uint16_t hb = f32_to_bf16_bits(x);
+        const float hf = bf16_bits_to_f32(hb);
+        const uint16_t lb = f32_to_bf16_bits(x - hf);
+        ahi[e] = __builtin_bit_cast(__bf16, hb);
+        alo[e] = __builtin_bit_cast(__bf16, lb);
+      }
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        const int col = (wave * NBW + b) * 16 + li;
+        bf16x8_t bw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bw[e] = __builtin_bit_cast(__bf16, s_w[(ks * 32 + 8 * g + e) * LDW + col]);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bw, acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bw, acc[b], 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int b = 0; b < NBW; ++b) {
-      const int col = (wave * NBW + b) * 16 + li;
-      bf16x8_t bw;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bw[e] = __builtin_bit_cast(__bf16, s_w[(8 * g + e) * LDW + col]);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bw, acc[b], 0, 0, 0);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bw, acc[b], 0, 0, 0);
+  };
+  // The steady-state loop refills unconditionally, so the two buffers' loads are
+  // always outstanding in the same order and the wait before a buffer's LDS write
+  // leaves the other buffer's loads in flight; the last two or three chunks are
+  // peeled off.
+  u32x4 ba[VPT], bb[VPT];
+  if (nch == 1) {
+    fetch(0, ba);
+    step(0, ba, false);
+  } else if (nch >= 2) {
+    fetch(0, ba);
+    fetch(1, bb);
+    int ch = 0;
+    for (; ch + 3 < nch; ch += 2) {
+      step(ch, ba, true);
+      step(ch + 1, bb, true);
+    }
+    if (nch - ch == 3) {
+      step(ch, ba, true);
+      step(ch + 1, bb, false);
+      step(ch + 2, ba, false);
+    } else {
+      step(ch, ba, false);
+      step(ch + 1, bb, false);
     }
   }
   __syncthreads();
@@ -177,19 +237,23 @@ __device__ void mfma_main_loop(const GemvParams& p, const int* s_idx, const floa
 // [lt0, lt0 + n_lt).  Used by the one-launch kernel below (items = blocks) and
 // by the persistent MLP kernel (items from a work queue).
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
-__device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n_parts, int lt0, int n_lt,
+__device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n_parts, int lt0, int n_lt,
                           unsigned char* smem) {
   using TS = TileShape<LPR>;
   constexpr int RPW = TS::RPW, NSLOT = TS::NSLOT, TN = TS::TN, TB = TN / 2;
   const int cap = p.cap;
+  // LDS: row list | activations [MT][cap] | slot reduction (VALU loop) | list-tile
+  // prefix sums | staging region (IN_TILES raw entries during the prologue, then the
+  // MFMA weight chunk, whose buffer also holds the MFMA output tile).
+  constexpr bool kMfma = MT == 16;
   int* s_idx = reinterpret_cast<int*>(smem);
   float* s_val = reinterpret_cast<float*>(smem + align16(size_t(cap) * 4));
-  float* s_red = reinterpret_cast<float*>(smem + align16(size_t(cap) * 4) + align16(size_t(cap) * MT * 4));
-  int* s_pref = reinterpret_cast<int*>(reinterpret_cast<unsigned char*>(s_red) +
-                                       align16(size_t(NSLOT > MT ? NSLOT : MT) * TN * 4));
-  // MT == 16 only: the bf16 weight chunk staged for the MFMA loop, after s_pref
+  unsigned char* after_val = smem + align16(size_t(cap) * 4) + align16(size_t(cap) * MT * 4);
+  const size_t red_bytes = kMfma ? 0 : align16(size_t(NSLOT > MT ? NSLOT : MT) * TN * 4);
+  int* s_pref = reinterpret_cast<int*>(after_val + red_bytes);
   uint16_t* s_w = reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(s_pref) +
                                               ((IN == IN_LISTS || IN == IN_TILES) ? align16(size_t(p.n_lt + 1) * 4) : 0));
+  float* s_red = kMfma ? reinterpret_cast<float*>(s_w) : reinterpret_cast<float*>(after_val);
   (void)n_lt;
   __shared__ int s_scan[kThreads / 64 + 1];
   __shared__ int s_flag;
@@ -211,18 +275,55 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
     const int n = max(0, min(CE, K - i0));
     float v0[CE];
     uint64_t ubits = 0;
+    if (MT > 1 && n == CE && p.x_dt != DT_F32) {
+      // the chunks of up to 8 tokens are loaded before any is used (one round trip
+      // per 8 tokens, at most 64 registers of raw input)
+      constexpr int NVV = CE / 8;
+      constexpr int G = MT < 8 ? MT : 8;
+      const bool bf = p.x_dt == DT_BF16;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < M) {
-        float v[CE];
-        load_chunk<CE>(p.x, p.x_dt, (long)m * p.ldx + i0, n, v);
-        uint64_t b = 0;
+      for (int m0 = 0; m0 < MT; m0 += G) {
+        if (m0 < M) {
+          u32x4 raw[G][NVV];
 #pragma unroll
-        for (int e = 0; e < CE; ++e) b |= (uint64_t)(e < n && fabsf(v[e]) > t) << e;
-        ubits |= b;
-        if (m == 0)
+          for (int j = 0; j < G; ++j) {
+            const int m = m0 + j;
+            const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) +
+                                                            (long)(m < M ? m : M - 1) * p.ldx + i0);
 #pragma unroll
-          for (int e = 0; e < CE; ++e) v0[e] = v[e];
+            for (int k = 0; k < NVV; ++k) raw[j][k] = q[k];
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            uint64_t b = 0;
+#pragma unroll
+            for (int k = 0; k < NVV; ++k) {
+              const uint32_t w4[4] = {raw[j][k].x, raw[j][k].y, raw[j][k].z, raw[j][k].w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t hb = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
+                const float v = bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb);
+                b |= (uint64_t)(fabsf(v) > t) << (8 * k + e);
+              }
+            }
+            if (m0 + j < M) ubits |= b;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+          float v[CE];
+          load_chunk<CE>(p.x, p.x_dt, (long)m * p.ldx + i0, n, v);
+          uint64_t b = 0;
+#pragma unroll
+          for (int e = 0; e < CE; ++e) b |= (uint64_t)(e < n && fabsf(v[e]) > t) << e;
+          ubits |= b;
+          if (MT == 1 && m == 0)
+#pragma unroll
+            for (int e = 0; e < CE; ++e) v0[e] = v[e];
+        }
       }
     }
     const int c = __popcll(ubits);
@@ -237,18 +338,20 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
           const int r = off + __popcll(ubits & ((((uint64_t)1) << e) - 1));
           if (r >= lo && r < hi) {
             s_idx[r - lo] = i0 + e;
-            s_val[r - lo] = fabsf(v0[e]) > t ? v0[e] : 0.f;
-#pragma unroll
-            for (int m = 1; m < MT; ++m) {
-              float xv = 0.f;
-              if (m < M) {
-                xv = load_elem(p.x, p.x_dt, (long)m * p.ldx + i0 + e);
-                xv = fabsf(xv) > t ? xv : 0.f;
-              }
-              s_val[m * cap + (r - lo)] = xv;
-            }
+            if constexpr (MT == 1) s_val[r - lo] = fabsf(v0[e]) > t ? v0[e] : 0.f;
           }
         }
+      }
+    }
+    if constexpr (MT > 1) {
+      // Several tokens: the slice's rows are known, so every token's values are
+      // gathered in one pass of independent loads (x stays cache resident).
+      __syncthreads();
+      for (int r = tid; r < cnt; r += kThreads) {
+        float xv[MT];
+        load_tokens<MT>(p.x, p.x_dt, p.ldx, s_idx[r], M, xv);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = fabsf(xv[m]) > t ? xv[m] : 0.f;
       }
     }
     thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
@@ -259,10 +362,11 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
     const int i0 = min(tid * C, K), i1 = min(i0 + C, K);
     int c = 0;
     for (int i = i0; i < i1; ++i) {
+      float xv[MT];
+      load_tokens<MT>(p.x, p.x_dt, p.ldx, i, M, xv);
       bool a = false;
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) a |= fabsf(load_elem(p.x, p.x_dt, m * p.ldx + i)) > t;
+      for (int m = 0; m < MT; ++m) a |= fabsf(xv[m]) > t;
       c += a;
     }
     int nnz;
@@ -273,22 +377,30 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
       int r = off;
       for (int i = i0; i < i1 && r < hi; ++i) {
         float xv[MT];
+        load_tokens<MT>(p.x, p.x_dt, p.ldx, i, M, xv);
         bool a = false;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          float v = m < M ? load_elem(p.x, p.x_dt, m * p.ldx + i) : 0.f;
-          bool k = fabsf(v) > t;
+          const bool k = fabsf(xv[m]) > t;
           a |= k;
-          xv[m] = k ? v : 0.f;
+          xv[m] = k ? xv[m] : 0.f;
         }
         if (a) {
           if (r >= lo) {
             s_idx[r - lo] = i;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) s_val[m * cap + (r - lo)] = xv[m];
+            if constexpr (MT == 1) s_val[r - lo] = xv[0];
           }
           ++r;
         }
+      }
+    }
+    if constexpr (MT > 1) {
+      __syncthreads();
+      for (int r = tid; r < cnt; r += kThreads) {
+        float xv[MT];
+        load_tokens<MT>(p.x, p.x_dt, p.ldx, s_idx[r], M, xv);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = fabsf(xv[m]) > t ? xv[m] : 0.f;
       }
     }
     thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
@@ -315,15 +427,18 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
         if (s_pref[mid] <= g) a = mid; else b = mid;
       }
       const long e = (long)(lt0 + a) * p.lt_stride + (g - s_pref[a]);
+      float xv[MT];
       if (p.coherent_lists) {
         s_idx[r] = load_coherent_i32(p.list_idx + e);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? load_coherent(p.list_val + e * M + m) : 0.f;
+        for (int m = 0; m < MT; ++m) xv[m] = load_coherent(p.list_val + e * M + (m < M ? m : M - 1));
       } else {
         s_idx[r] = p.list_idx[e];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? p.list_val[e * M + m] : 0.f;
+        for (int m = 0; m < MT; ++m) xv[m] = p.list_val[e * M + (m < M ? m : M - 1)];
       }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? xv[m] : 0.f;
     }
   } else if constexpr (IN == IN_TILES) {
     // Slice sl owns whole list tiles [t0, t1).  Counts and every candidate entry of
@@ -337,13 +452,9 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
     int* r_idx = reinterpret_cast<int*>(s_w);              // [tot_e] raw candidates
     float* r_val = reinterpret_cast<float*>(r_idx + tot_e);  // [tot_e][M]
     if (tid < nt) s_cnt[tid] = p.list_cnt[lt0 + t0 + tid];
-    for (int e = tid; e < tot_e; e += kThreads) {
-      const long ge = (long)(lt0 + t0) * stride + e;
-      r_idx[e] = p.list_idx[ge];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) r_val[e * M + m] = p.list_val[ge * M + m];
-    }
+    const long gbase = (long)(lt0 + t0) * stride;
+    copy_to_lds(r_idx, p.list_idx + gbase, tot_e);
+    copy_to_lds(r_val, p.list_val + gbase * M, tot_e * M);
     __syncthreads();
     if (tid == 0) {
       int run = 0;
@@ -367,9 +478,10 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
     cnt = hi - lo;
     for (int r = tid; r < cnt; r += kThreads) {
       s_idx[r] = lo + r;
+      float xv[MT];
+      load_tokens<MT>(p.x, p.x_dt, p.ldx, lo + r, M, xv);
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        s_val[m * cap + r] = m < M ? load_elem(p.x, p.x_dt, m * p.ldx + lo + r) : 0.f;
+      for (int m = 0; m < MT; ++m) s_val[m * cap + r] = xv[m];
     }
   }
   __syncthreads();
@@ -420,7 +532,7 @@ __device__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n
     for (int u = 0; u < kUnroll; ++u) row[u] = s_idx[min(r + u * NSLOT, cnt - 1)];
     u32x4 w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) w[u] = load_w16(Wc + (long)row[u] * ldw, NT);
+    for (int u = 0; u < kUnroll; ++u) w[u] = load_w16<NT>(Wc + (long)row[u] * ldw);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int rr = r + u * NSLOT;

@@ -47,8 +47,8 @@ __global__ __launch_bounds__(kLsThreads) void local_signal_kernel(const uint16_t
         *reinterpret_cast<u32x4*>(xt + t * kLsLd + c) = val;
       }
       __syncthreads();
-      const u32x4 bg = load_w16(wg + k0 + 8 * g, true);
-      const u32x4 bu = load_w16(wu + k0 + 8 * g, true);
+      const u32x4 bg = load_w16<true>(wg + k0 + 8 * g);
+      const u32x4 bu = load_w16<true>(wu + k0 + 8 * g);
       const g_bf16x8 fg = __builtin_bit_cast(g_bf16x8, bg);
       const g_bf16x8 fu = __builtin_bit_cast(g_bf16x8, bu);
 #pragma unroll

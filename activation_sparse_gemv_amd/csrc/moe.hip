@@ -159,8 +159,8 @@ __global__ __launch_bounds__(kGuThreads) void expert_gu_kernel(const MoeParams p
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int c = min(c0 + k * 512, d - 8);
-          vg[k] = load_w16(wg + c, true);
-          vu[k] = load_w16(wu + c, true);
+          vg[k] = load_w16<true>(wg + c);
+          vu[k] = load_w16<true>(wu + c);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   for (int r = wave; r < kk; r += 4 * U) {
     u32x4 w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = load_w16(Wd + (long)keep[min(r + 4 * u, kk - 1)] * d, true);
+    for (int u = 0; u < U; ++u) w[u] = load_w16<true>(Wd + (long)keep[min(r + 4 * u, kk - 1)] * d);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rr = r + 4 * u;

@@ -45,8 +45,8 @@ __global__ __launch_bounds__(kNThreads) void neuron_gu_kernel(const NeuronGuPara
       for (int k = 0; k < kChunkUnroll; ++k) {
         const int c = c0 + k * 512;
         if (c < d) {
-          vg[k] = load_w16(wg + c, NT);
-          vu[k] = load_w16(wu + c, NT);
+          vg[k] = load_w16<NT>(wg + c);
+          vu[k] = load_w16<NT>(wu + c);
         } else {
           vg[k] = u32x4{0u, 0u, 0u, 0u};
           vu[k] = u32x4{0u, 0u, 0u, 0u};

@@ -162,3 +162,31 @@ def test_neuron_set_full_equals_dense():
     assert rel_err(y, ref) < TOL
     y2 = asg.as_sparse_swiglu_mlp(x.to(DEV), w, neuron_idx=torch.arange(f, dtype=torch.int32, device=DEV))
     assert rel_err(y2, ref) < TOL
+
+
+_PLANS = [dict(AS_GU_LPR=16, AS_GU_S=1), dict(AS_GU_LPR=16, AS_GU_S=2, AS_DN_TPW=1),
+          dict(AS_GU_LPR=32, AS_GU_S=3, AS_DN_LPR=32, AS_DN_TPW=2), dict(AS_DN_LPR=64, AS_DN_TPW=1),
+          dict(AS_GU_LPR=64, AS_GU_S=5, AS_DN_LPR=16, AS_DN_TPW=3)]
+
+
+@pytest.mark.parametrize("plan", range(len(_PLANS)))
+@pytest.mark.parametrize("cfg,M", [(1, 1), (1, 8), (2, 1), (2, 16)])
+def test_mlp_launch_plans(plan, cfg, M, monkeypatch):
+    """Other tile widths, split-K factors and down-stage tile groupings (set through the
+    launch-plan overrides) compute the same MLP: the small fp16 shape for 1 and 8 tokens,
+    the Llama shape for 1 and 16 tokens (matrix cores), 50% thresholds."""
+    for k, v in _PLANS[plan].items():
+        monkeypatch.setenv(k, str(v))
+    announce(f"mlp plan {_PLANS[plan]} cfg={cfg} M={M}")
+    shape = datagen.CFG1 if cfg == 1 else datagen.CFG2
+    w = _mlp(cfg, shape)
+    if cfg == 1:
+        calib = datagen.laplace((64, shape.d_model), datagen.seed_for(1, 0, "calib"), dtype="f16")
+        toks = datagen.laplace((M, shape.d_model), datagen.seed_for(1, 3, "decode"), dtype="f16")
+    else:
+        calib = datagen.student_t((64, shape.d_model), datagen.seed_for(2, 0, "calib"))
+        toks = datagen.student_t((M, shape.d_model), datagen.seed_for(2, 3, "decode"))
+    t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], 0.5, 0.5)
+    _check_stagewise(toks, w, float(t_x), float(t_h), M)
+    y = asg.as_sparse_swiglu_mlp(toks.to(DEV), w["dev"], 5.0, 5.0, flags=L.AS_FLAG_FORCE_DENSE)
+    assert rel_err(y, teal.dense_mlp(f64(toks), w["Wg"], w["Wu"], w["Wd"])) < TOL
