@@ -64,6 +64,8 @@ int env_int(const char* name, int dflt) {
 // LDS per workgroup on gfx950, and what a plan keeps free of it beyond the row list
 // and its activations (slot reduction or staged MFMA chunk, list prefix sums).
 constexpr int kLdsBytes = 160 * 1024;
+// Largest contraction length (rows of W): the kernels split row lists in 32-bit arithmetic.
+constexpr int kMaxRows = 1 << 24;
 constexpr int kLdsReserve = 40 * 1024;
 
 Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
@@ -138,7 +140,7 @@ struct MlpWs {
   int* l_cnt;
   int* l_idx;
   float* l_val;
-  unsigned* queue;        // [0] next item, [1] exit count, [2] error flag (persistent kernel)
+  unsigned* queue;        // [1] exit count, [2] error flag (one-launch MLP)
   unsigned* tile_done;    // [n_lt]
 };
 
@@ -146,7 +148,8 @@ struct MlpPlan {
   Plan p1, p2;
   int n_lt, lt_stride;
   int parts2;             // partial slots of the down stage (max of its split and the h-tiles)
-  int s2_tiles, cap2_tiles;  // down stage over whole h-tiles: slices and their max list entries
+  int s2_tiles, cap2_tiles;  // down stage over whole h-tiles (one-launch MLP): slices, max list entries
+  int s2_range, cap2_range;  // down stage masking h by range (two launches): slices, max range length
 };
 
 MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
@@ -162,9 +165,19 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
   }
   (void)dense;
   mp.p2 = plan_gemv(w->d_ff, w->d_model, false, "AS_DN", mt_for(M));
-  mp.parts2 = mp.p2.S > mp.n_lt ? mp.p2.S : mp.n_lt;
   {
-    // threshold mode: each down slice owns whole h-tiles (about 1.75 workgroups per CU)
+    // threshold mode, two launches: down slice s masks its own 64-aligned range of h
+    const int units = (w->d_ff + 63) / 64;
+    const int hard = (kLdsBytes - kLdsReserve) / (4 + 4 * mt_for(M));
+    int S = mp.p2.S;
+    while (S < units && ((units + S - 1) / S) * 64 > hard) ++S;
+    mp.s2_range = S;
+    mp.cap2_range = ((units + S - 1) / S) * 64;
+  }
+  mp.parts2 = mp.p2.S > mp.n_lt ? mp.p2.S : mp.n_lt;
+  if (mp.s2_range > mp.parts2) mp.parts2 = mp.s2_range;
+  {
+    // one-launch MLP: each down slice owns whole h-tiles (about 1.75 workgroups per CU)
     const int target = (7 * num_cus()) / 4;
     int tpw = (int)((long)mp.n_lt * mp.p2.n_tiles / (target > 0 ? target : 1));
     // list entries per slice: index + activations in LDS twice (raw, then compacted)
@@ -269,6 +282,7 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   if (M < 1 || M > 16) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..16", fn, M);
   if (M > 8 && w_dt != AS_BF16) return fail(AS_ERR_UNSUPPORTED, "%s: M > 8 (MFMA path) needs bf16 weights", fn);
   if (K < 1 || N < 8 || N % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: K=%d N=%d (N must be a multiple of 8)", fn, K, N);
+  if (K > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "%s: K=%d above %d", fn, K, kMaxRows);
   if (!aligned16(W)) return fail(AS_ERR_INVALID_ARG, "%s: W not 16-byte aligned", fn);
   if (mo && mo->idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: mask idx export needs M == 1", fn);
   const Plan pl = plan_gemv(K, N, false, "AS_GV", mt_for(M));
@@ -312,6 +326,8 @@ static as_status check_mlp_weights(const as_mlp_weights* w, as_mlp_mode mode, co
   if (!is_wdt(w->w_dt)) return fail(AS_ERR_INVALID_ARG, "%s: weight dtype must be f16 or bf16", fn);
   if (w->d_model < 8 || w->d_model % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: d_model=%d not a multiple of 8", fn, w->d_model);
   if (w->d_ff < 64 || w->d_ff % 64 != 0) return fail(AS_ERR_INVALID_ARG, "%s: d_ff=%d not a multiple of 64", fn, w->d_ff);
+  if (w->d_model > kMaxRows || w->d_ff > kMaxRows)
+    return fail(AS_ERR_UNSUPPORTED, "%s: d_model=%d or d_ff=%d above %d", fn, w->d_model, w->d_ff, kMaxRows);
   if (!aligned16(w->w_gate_up)) return fail(AS_ERR_INVALID_ARG, "%s: w_gate_up not 16-byte aligned", fn);
   if (mode == AS_MLP_THRESHOLD) {
     if (!w->w_down) return fail(AS_ERR_INVALID_ARG, "%s: w_down is NULL", fn);
@@ -373,14 +389,18 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   GemvParams p2 = base_params();
   GemvConfig c2{int(w->w_dt), mt, mp.p2.lpr, IN_LISTS, OUT_Y, false, nt};
 
-  const bool fused = mode == AS_MLP_THRESHOLD && mt <= 8 && nt && (flags & AS_FLAG_NO_FUSION) == 0 &&
-                     env_int("AS_FUSED", 0) != 0 && (mp.p1.lpr == 32 || mp.p1.lpr == 64) &&
-                     (mp.p2.lpr == 16 || mp.p2.lpr == 64);
-  if (fused) {
-    // one persistent launch: gate/up items, then down items as their h-tiles complete
+  // One launch for both stages (opt-in: measured slower than two launches on the
+  // Llama shape, since an h-tile completes only with its slowest slice) when every
+  // workgroup of it can be resident at once (the launcher checks occupancy and
+  // launches nothing otherwise).
+  const bool try_fused = mode == AS_MLP_THRESHOLD && mt <= 8 && nt && (flags & AS_FLAG_NO_FUSION) == 0 &&
+                         env_int("AS_FUSED", 0) != 0 && (mp.p1.lpr == 32 || mp.p1.lpr == 64) &&
+                         (mp.p2.lpr == 16 || mp.p2.lpr == 32);
+  if (try_fused) {
     FusedMlpParams fz;
     memset(&fz, 0, sizeof fz);
     GemvParams& q1 = fz.p1;
+    q1 = base_params();
     q1.x = X; q1.x_dt = int(x_dt); q1.M = M; q1.K = d; q1.ldx = d; q1.t = dense ? -INFINITY : t_x;
     q1.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); q1.ldw = 2L * f; q1.N = f; q1.gu_off = f;
     q1.n_tiles = mp.p1.n_tiles; q1.S = mp.p1.S; q1.cap = mp.p1.cap;
@@ -392,34 +412,41 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
       q1.x_bits = dbg->x_mask.bits; q1.x_bits_ld = (d + 63) / 64; q1.x_idx = dbg->x_mask.idx; q1.x_nnz = dbg->x_mask.nnz;
     }
     GemvParams& q2 = fz.p2;
+    q2 = base_params();
     q2.M = M; q2.W = reinterpret_cast<const uint16_t*>(w->w_down); q2.ldw = d; q2.N = d;
     q2.list_cnt = mw.l_cnt; q2.list_idx = mw.l_idx; q2.list_val = mw.l_val;
-    q2.n_lt = 1; q2.lt_stride = mp.lt_stride; q2.coherent_lists = 1;
-    q2.n_tiles = mp.p2.n_tiles; q2.S = 1; q2.cap = mp.lt_stride;
+    q2.n_lt = mp.n_lt; q2.lt_stride = mp.lt_stride; q2.coherent_lists = 1;
+    q2.n_tiles = mp.p2.n_tiles; q2.S = mp.s2_tiles; q2.cap = mp.cap2_tiles;
     q2.partials = mw.g2.partials; q2.counters = mw.g2.counters; q2.part_ld = d;
     q2.y = Y; q2.y_dt = int(y_dt); q2.ldy = d; q2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
-    fz.n_tiles1 = mp.p1.n_tiles; fz.S1 = mp.p1.S; fz.items1 = fz.n_tiles1 * fz.S1; fz.n_ct2 = mp.p2.n_tiles;
-    fz.next = mw.queue; fz.exit_cnt = mw.queue + 1; fz.err = mw.queue + 2; fz.tile_done = mw.tile_done;
+    fz.n_tiles1 = mp.p1.n_tiles; fz.S1 = mp.p1.S; fz.items1 = fz.n_tiles1 * fz.S1;
+    fz.n_ct2 = mp.p2.n_tiles; fz.S2 = mp.s2_tiles; fz.items2 = fz.n_ct2 * fz.S2; fz.n_lt = mp.n_lt;
+    fz.exit_cnt = mw.queue + 1; fz.err = mw.queue + 2; fz.tile_done = mw.tile_done;
     GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : IN_THRESH, OUT_SWIGLU, true, true};
-    GemvConfig c2q{int(w->w_dt), mt, mp.p2.lpr, IN_LISTS, OUT_Y, false, true};
-    const size_t sm1 = gemv_smem_bytes(c1, q1.cap, 0), sm2 = gemv_smem_bytes(c2q, q2.cap, 1);
+    GemvConfig c2t{int(w->w_dt), mt, mp.p2.lpr, IN_TILES, OUT_Y, false, true};
+    const size_t sm1 = gemv_smem_bytes(c1, q1.cap, 0), sm2 = gemv_smem_bytes(c2t, q2.cap, q2.n_lt);
     FusedCfg fc{int(w->w_dt), mt, mp.p1.lpr, mp.p2.lpr, dense ? IN_ALL : IN_THRESH,
-                dense ? 0 : pick_chunk_vectors(X, int(x_dt), d, d), env_int("AS_FUSED_WPC", 0), num_cus()};
+                dense ? 0 : pick_chunk_vectors(X, int(x_dt), d, d), num_cus()};
     if (mt > 1 && fc.nv > 2) fc.nv = 0;
-    if ((st = hip_check(launch_fused_mlp(fc, fz, sm1 > sm2 ? sm1 : sm2, stream), fn)) != AS_OK) return st;
-    if ((st = rec(1)) != AS_OK) return st;
-    return rec(2);
+    const hipError_t e = launch_fused_mlp(fc, fz, sm1 > sm2 ? sm1 : sm2, stream);
+    if (e != hipErrorCooperativeLaunchTooLarge) {
+      if ((st = hip_check(e, fn)) != AS_OK) return st;
+      if ((st = rec(1)) != AS_OK) return st;
+      return rec(2);
+    }
   }
 
   if (mode == AS_MLP_THRESHOLD) {
-    // stage 1: x mask -> gate/up gather GEMV -> SwiGLU -> h mask -> per-tile lists
+    // stage 1: x mask -> gate/up gather GEMV -> SwiGLU -> h (and, with the list-tile
+    // down stage, the h mask's per-tile lists)
+    const bool dn_tiles = !dense && env_int("AS_DN_TILES", 0) != 0;
     GemvParams p = base_params();
     p.x = X; p.x_dt = int(x_dt); p.M = M; p.K = d; p.ldx = d; p.t = t_x;
     p.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.ldw = 2L * f; p.N = f; p.gu_off = f;
     p.n_tiles = mp.p1.n_tiles; p.S = mp.p1.S; p.cap = mp.p1.cap;
     p.partials = mw.g1.partials; p.counters = mw.g1.counters; p.part_ld = 2L * f;
     p.t_h = dense ? -INFINITY : t_h; p.h = hbuf; p.ldh = f;
-    if (!dense) { p.o_cnt = mw.l_cnt; p.o_idx = mw.l_idx; p.o_val = mw.l_val; }
+    if (dn_tiles) { p.o_cnt = mw.l_cnt; p.o_idx = mw.l_idx; p.o_val = mw.l_val; }
     if (dbg && !dense) {
       p.h_bits = dbg->h_mask.bits; p.h_bits_ld = (f + 63) / 64;
       p.x_bits = dbg->x_mask.bits; p.x_bits_ld = (d + 63) / 64; p.x_idx = dbg->x_mask.idx; p.x_nnz = dbg->x_mask.nnz;
@@ -427,13 +454,17 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
     GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : IN_THRESH, OUT_SWIGLU, true, nt};
     if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
-    // stage 2: down projection over the surviving h rows
+    // stage 2: down projection over the surviving h rows; each slice masks its
+    // own range of h (or, opt-in, reads whole h-tile lists)
     p2.W = reinterpret_cast<const uint16_t*>(w->w_down); p2.ldw = d;
     if (dense) {
       c2.in = IN_ALL;
       p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = -INFINITY;
-    } else if (env_int("AS_DN_TILES", 1)) {
+    } else if (dn_tiles) {
       c2.in = IN_TILES;
+    } else {
+      c2.in = IN_RANGE;
+      p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = t_h;
     }
   } else {
     // stage 1: gate/up dot products of the listed neurons (neuron-major rows)
@@ -455,6 +486,7 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   p2.N = d;
   p2.n_tiles = mp.p2.n_tiles; p2.S = mp.p2.S; p2.cap = mp.p2.cap;
   if (c2.in == IN_TILES) { p2.S = mp.s2_tiles; p2.cap = mp.cap2_tiles; }
+  if (c2.in == IN_RANGE) { p2.S = mp.s2_range; p2.cap = mp.cap2_range; }
   p2.partials = mw.g2.partials; p2.counters = mw.g2.counters; p2.part_ld = d;
   p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;

@@ -133,6 +133,12 @@ __device__ __forceinline__ void load_tokens(const void* x, int dt, long ldx, lon
     if (m >= M) v[m] = 0.f;
 }
 
+// floor(a * b / c) in 32-bit unsigned arithmetic, for a * b < 2^32 (split points of
+// at most 2^24 items into parts): a 64-bit division is a long scalar sequence here.
+__device__ __forceinline__ int split_point(int a, int b, int c) {
+  return (int)((unsigned)a * (unsigned)b / (unsigned)c);
+}
+
 // Wait until every vector-memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

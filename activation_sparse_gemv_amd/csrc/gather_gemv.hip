@@ -38,11 +38,11 @@ hipError_t launch_gemv_f16_m4(const GemvConfig& c, const GemvParams& p, size_t s
 hipError_t launch_gemv_f16_m8(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
 
 // Chunk width (16-byte vectors of 8 inputs per thread) of the vectorised
-// threshold prologue, or 0 for the general element-wise prologue.
-int pick_chunk_vectors(const void* x, int x_dt, int K, long ldx) {
+// threshold prologue over `len` inputs, or 0 for the element-wise one.
+int pick_chunk_vectors(const void* x, int x_dt, int len, long ldx) {
   const int es = x_dt == DT_F32 ? 4 : 2;
   if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0 || (ldx * es) % 16 != 0) return 0;
-  const int per = (K + kThreadsHost - 1) / kThreadsHost;
+  const int per = (len + kThreadsHost - 1) / kThreadsHost;
   if (per <= 16) return 2;
   if (per <= 64) return 8;
   return 0;
@@ -71,8 +71,9 @@ hipError_t launch_fused_mlp(const FusedCfg& c, const FusedMlpParams& f, size_t s
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s) {
   const size_t smem = gemv_smem_bytes(c, p.cap, p.n_lt);
   GemvConfig cc = c;
-  if (cc.in == IN_THRESH && cc.nv < 0) {
-    cc.nv = pick_chunk_vectors(p.x, p.x_dt, p.K, p.ldx);
+  if ((cc.in == IN_THRESH || cc.in == IN_RANGE) && cc.nv < 0) {
+    // the chunk prologue covers the whole input (IN_THRESH) or one slice's range
+    cc.nv = pick_chunk_vectors(p.x, p.x_dt, cc.in == IN_RANGE ? p.cap : p.K, p.ldx);
     if (cc.mt > 1 && cc.nv > 2) cc.nv = 0;     // wide register chunks only for one token
   }
   const bool bf = cc.wdt == DT_BF16;

@@ -78,15 +78,44 @@ __device__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_sca
 // thread (the stores to LDS would otherwise wait on each load in turn).
 template <class T>
 __device__ __forceinline__ void copy_to_lds(T* dst, const T* src, int n) {
-  int j = threadIdx.x;
-  for (; j + 7 * kThreads < n; j += 8 * kThreads) {
+  // indices past n re-read element n - 1 (the loads stay unconditional and
+  // issue together); only the stores are predicated
+  for (int j = threadIdx.x; j < n; j += 8 * kThreads) {
     T v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[j + u * kThreads];
+    for (int u = 0; u < 8; ++u) v[u] = src[min(j + u * kThreads, n - 1)];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dst[j + u * kThreads] = v[u];
+    for (int u = 0; u < 8; ++u)
+      if (j + u * kThreads < n) dst[j + u * kThreads] = v[u];
   }
-  for (; j < n; j += kThreads) dst[j] = src[j];
+}
+
+// Two such copies with all of their loads in flight together; COH reads the
+// sources device-coherently (data written by other workgroups of the same launch).
+template <bool COH, class T>
+__device__ __forceinline__ T load_maybe_coherent(const T* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH, class T, class U>
+__device__ __forceinline__ void copy2_to_lds(T* d1, const T* s1, int n1, U* d2, const U* s2, int n2) {
+  const int n = n1 > n2 ? n1 : n2;
+  for (int j = threadIdx.x; j < n; j += 8 * kThreads) {
+    T a[8];
+    U b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int jj = j + u * kThreads;
+      a[u] = n1 > 0 ? load_maybe_coherent<COH>(s1 + min(jj, n1 - 1)) : T(0);
+      b[u] = n2 > 0 ? load_maybe_coherent<COH>(s2 + min(jj, n2 - 1)) : U(0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int jj = j + u * kThreads;
+      if (jj < n1) d1[jj] = a[u];
+      if (jj < n2) d2[jj] = b[u];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- MFMA main loop
@@ -231,11 +260,176 @@ __device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s
   __syncthreads();
 }
 
+// ---------------------------------------------------------------- input compaction
+// Both return the number of rows kept (entries [lo, lo + count) of the compacted
+// list, *lo_out = lo), with s_idx / s_val filled; the caller synchronises.
+// Entries are in ascending input order; with `split`, the workgroup keeps entries
+// [sl * nnz / S, (sl + 1) * nnz / S), so slices are equal whatever the mask.
+
+// Each thread owns a chunk of consecutive inputs of [i0, i1): 8 * NV of them
+// loaded as 16-byte vectors issued together (NV > 0, 16-byte aligned rows), or
+// ceil(len / threads) element by element (NV == 0).  A row is kept if any token
+// keeps it; a workgroup scan of the per-thread counts places the chunks.  One
+// token's values stay in registers; for several tokens every kept row's values
+// are gathered afterwards in one pass of independent loads.
+template <int MT, int NV>
+__device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i1, bool split, int sl, int S,
+                                              int* s_idx, float* s_val, int cap, int* s_scan, int* lo_out) {
+  const int tid = threadIdx.x;
+  const int M = p.M;
+  const float t = p.t;
+  const int L = max(0, i1 - i0);
+  constexpr int CEV = NV > 0 ? 8 * NV : 1;
+  const int CE = NV > 0 ? CEV : (L + kThreads - 1) / kThreads;
+  const int c0 = min(i0 + tid * CE, i1), n = max(0, min(CE, i1 - c0));
+  uint64_t ubits = 0;       // NV > 0: bit e for input c0 + e
+  float v0[CEV];            // MT == 1, NV > 0: the chunk's values
+  int c = 0;
+  if constexpr (NV > 0 && MT == 1) {
+    load_chunk<CEV>(p.x, p.x_dt, c0, n, v0);
+#pragma unroll
+    for (int e = 0; e < CEV; ++e) ubits |= (uint64_t)(e < n && fabsf(v0[e]) > t) << e;
+    c = __popcll(ubits);
+  } else if constexpr (NV > 0) {
+    if (n == CEV && p.x_dt != DT_F32) {
+      // the chunks of up to 8 tokens are loaded before any is used
+      constexpr int NVV = CEV / 8;
+      constexpr int G = MT < 8 ? MT : 8;
+      const bool bf = p.x_dt == DT_BF16;
+#pragma unroll
+      for (int m0 = 0; m0 < MT; m0 += G) {
+        if (m0 < M) {
+          u32x4 raw[G][NVV];
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const int m = m0 + j;
+            const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) +
+                                                            (long)(m < M ? m : M - 1) * p.ldx + c0);
+#pragma unroll
+            for (int k = 0; k < NVV; ++k) raw[j][k] = q[k];
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            uint64_t b = 0;
+#pragma unroll
+            for (int k = 0; k < NVV; ++k) {
+              const uint32_t w4[4] = {raw[j][k].x, raw[j][k].y, raw[j][k].z, raw[j][k].w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t hb = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
+                const float v = bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb);
+                b |= (uint64_t)(fabsf(v) > t) << (8 * k + e);
+              }
+            }
+            if (m0 + j < M) ubits |= b;
+          }
+        }
+      }
+    } else if (n == CEV) {
+      // fp32 rows: groups of 4 tokens
+      constexpr int NF = CEV / 4;
+      constexpr int G = MT < 4 ? MT : 4;
+#pragma unroll
+      for (int m0 = 0; m0 < MT; m0 += G) {
+        if (m0 < M) {
+          float4 raw[G][NF];
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const int m = m0 + j;
+            const float4* q = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.x) +
+                                                              (long)(m < M ? m : M - 1) * p.ldx + c0);
+#pragma unroll
+            for (int k = 0; k < NF; ++k) raw[j][k] = q[k];
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            uint64_t b = 0;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) {
+              b |= (uint64_t)(fabsf(raw[j][k].x) > t) << (4 * k);
+              b |= (uint64_t)(fabsf(raw[j][k].y) > t) << (4 * k + 1);
+              b |= (uint64_t)(fabsf(raw[j][k].z) > t) << (4 * k + 2);
+              b |= (uint64_t)(fabsf(raw[j][k].w) > t) << (4 * k + 3);
+            }
+            if (m0 + j < M) ubits |= b;
+          }
+        }
+      }
+    } else {
+      for (int e = 0; e < n; ++e) {
+        float xv[MT];
+        load_tokens<MT>(p.x, p.x_dt, p.ldx, c0 + e, M, xv);
+        bool a = false;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a |= fabsf(xv[m]) > t;
+        ubits |= (uint64_t)a << e;
+      }
+    }
+    c = __popcll(ubits);
+  } else {
+    for (int e = 0; e < n; ++e) {
+      float xv[MT];
+      load_tokens<MT>(p.x, p.x_dt, p.ldx, c0 + e, M, xv);
+      bool a = false;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) a |= fabsf(xv[m]) > t;
+      c += a;
+    }
+  }
+  int nnz;
+  const int off = block_excl_scan<kThreads>(c, s_scan, &nnz);
+  const int lo = split ? split_point(sl, nnz, S) : 0;
+  const int hi = split ? split_point(sl + 1, nnz, S) : nnz;
+  *lo_out = lo;
+  if (off < hi && off + c > lo) {
+    if constexpr (NV > 0) {
+      int r = off - lo;
+      const unsigned span = (unsigned)(hi - lo);
+#pragma unroll
+      for (int e = 0; e < CEV; ++e) {
+        const bool k = (ubits >> e) & 1;
+        if (k && (unsigned)r < span) {
+          s_idx[r] = c0 + e;
+          if constexpr (MT == 1) s_val[r] = v0[e];
+        }
+        r += k;
+      }
+    } else {
+      int r = off;
+      for (int e = 0; e < n && r < hi; ++e) {
+        float xv[MT];
+        load_tokens<MT>(p.x, p.x_dt, p.ldx, c0 + e, M, xv);
+        bool a = false;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a |= fabsf(xv[m]) > t;
+        if (a) {
+          if (r >= lo) {
+            s_idx[r - lo] = c0 + e;
+            if constexpr (MT == 1) s_val[r - lo] = xv[0];
+          }
+          ++r;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int cnt = hi - lo;
+  if constexpr (MT == 1) return cnt;
+  for (int r = tid; r < cnt; r += kThreads) {
+    float xv[MT];
+    load_tokens<MT>(p.x, p.x_dt, p.ldx, s_idx[r], M, xv);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) s_val[m * cap + r] = fabsf(xv[m]) > t ? xv[m] : 0.f;
+  }
+  return cnt;
+}
+
 // One work item: column tile `tile`, row slice `sl` of S (p.S) equal parts of the
 // compacted row list; its partial tile is slot `part` of `n_parts` combined by
 // the last item of the tile to finish.  IN_LISTS reads list tiles
-// [lt0, lt0 + n_lt).  Used by the one-launch kernel below (items = blocks) and
-// by the persistent MLP kernel (items from a work queue).
+// [lt0, lt0 + n_lt); IN_TILES gives slice sl whole list tiles of [lt0, lt0 + n_lt).
+// Used by the GEMV kernel below (one item per workgroup) and by the one-launch
+// MLP kernel (a gate/up item, then a down item, per workgroup).
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
 __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n_parts, int lt0, int n_lt,
                           unsigned char* smem) {
@@ -264,146 +458,20 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
 
   // ------------------------------------------------------------ prologue
   int cnt = 0;
-  if constexpr (IN == IN_THRESH && NV > 0) {
-    // Each thread owns CE = 8*NV consecutive inputs, loaded with 16-byte vector
-    // loads issued together; the union mask over tokens stays in a 64-bit word,
-    // so the whole compaction costs one L2 round trip and one workgroup scan.
-    constexpr int CE = 8 * NV;
-    const int K = p.K;
-    const float t = p.t;
-    const int i0 = tid * CE;
-    const int n = max(0, min(CE, K - i0));
-    float v0[CE];
-    uint64_t ubits = 0;
-    if (MT > 1 && n == CE && p.x_dt != DT_F32) {
-      // the chunks of up to 8 tokens are loaded before any is used (one round trip
-      // per 8 tokens, at most 64 registers of raw input)
-      constexpr int NVV = CE / 8;
-      constexpr int G = MT < 8 ? MT : 8;
-      const bool bf = p.x_dt == DT_BF16;
-#pragma unroll
-      for (int m0 = 0; m0 < MT; m0 += G) {
-        if (m0 < M) {
-          u32x4 raw[G][NVV];
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            const int m = m0 + j;
-            const u32x4* q = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) +
-                                                            (long)(m < M ? m : M - 1) * p.ldx + i0);
-#pragma unroll
-            for (int k = 0; k < NVV; ++k) raw[j][k] = q[k];
-          }
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            uint64_t b = 0;
-#pragma unroll
-            for (int k = 0; k < NVV; ++k) {
-              const uint32_t w4[4] = {raw[j][k].x, raw[j][k].y, raw[j][k].z, raw[j][k].w};
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t hb = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
-                const float v = bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb);
-                b |= (uint64_t)(fabsf(v) > t) << (8 * k + e);
-              }
-            }
-            if (m0 + j < M) ubits |= b;
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          float v[CE];
-          load_chunk<CE>(p.x, p.x_dt, (long)m * p.ldx + i0, n, v);
-          uint64_t b = 0;
-#pragma unroll
-          for (int e = 0; e < CE; ++e) b |= (uint64_t)(e < n && fabsf(v[e]) > t) << e;
-          ubits |= b;
-          if (MT == 1 && m == 0)
-#pragma unroll
-            for (int e = 0; e < CE; ++e) v0[e] = v[e];
-        }
-      }
+  if constexpr (IN == IN_THRESH || IN == IN_RANGE) {
+    // IN_THRESH: the whole input, split into S equal parts of the compacted list.
+    // IN_RANGE: slice sl owns the inputs of its 64-aligned range and keeps all of them.
+    const bool split = IN == IN_THRESH;
+    int r0 = 0, r1 = p.K;
+    if (!split) {
+      const int units = (p.K + 63) / 64;
+      r0 = min(p.K, split_point(sl, units, S) * 64);
+      r1 = min(p.K, split_point(sl + 1, units, S) * 64);
     }
-    const int c = __popcll(ubits);
-    int nnz;
-    const int off = block_excl_scan<kThreads>(c, s_scan, &nnz);
-    const int lo = int((long)sl * nnz / S), hi = int((long)(sl + 1) * nnz / S);
-    cnt = hi - lo;
-    if (off < hi && off + c > lo) {
-#pragma unroll
-      for (int e = 0; e < CE; ++e) {
-        if ((ubits >> e) & 1) {
-          const int r = off + __popcll(ubits & ((((uint64_t)1) << e) - 1));
-          if (r >= lo && r < hi) {
-            s_idx[r - lo] = i0 + e;
-            if constexpr (MT == 1) s_val[r - lo] = fabsf(v0[e]) > t ? v0[e] : 0.f;
-          }
-        }
-      }
-    }
-    if constexpr (MT > 1) {
-      // Several tokens: the slice's rows are known, so every token's values are
-      // gathered in one pass of independent loads (x stays cache resident).
-      __syncthreads();
-      for (int r = tid; r < cnt; r += kThreads) {
-        float xv[MT];
-        load_tokens<MT>(p.x, p.x_dt, p.ldx, s_idx[r], M, xv);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = fabsf(xv[m]) > t ? xv[m] : 0.f;
-      }
-    }
-    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
-  } else if constexpr (IN == IN_THRESH) {
-    const int K = p.K;
-    const float t = p.t;
-    const int C = (K + kThreads - 1) / kThreads;
-    const int i0 = min(tid * C, K), i1 = min(i0 + C, K);
-    int c = 0;
-    for (int i = i0; i < i1; ++i) {
-      float xv[MT];
-      load_tokens<MT>(p.x, p.x_dt, p.ldx, i, M, xv);
-      bool a = false;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) a |= fabsf(xv[m]) > t;
-      c += a;
-    }
-    int nnz;
-    const int off = block_excl_scan<kThreads>(c, s_scan, &nnz);
-    const int lo = int((long)sl * nnz / S), hi = int((long)(sl + 1) * nnz / S);
-    cnt = hi - lo;
-    if (off < hi && off + c > lo) {
-      int r = off;
-      for (int i = i0; i < i1 && r < hi; ++i) {
-        float xv[MT];
-        load_tokens<MT>(p.x, p.x_dt, p.ldx, i, M, xv);
-        bool a = false;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const bool k = fabsf(xv[m]) > t;
-          a |= k;
-          xv[m] = k ? xv[m] : 0.f;
-        }
-        if (a) {
-          if (r >= lo) {
-            s_idx[r - lo] = i;
-            if constexpr (MT == 1) s_val[r - lo] = xv[0];
-          }
-          ++r;
-        }
-      }
-    }
-    if constexpr (MT > 1) {
-      __syncthreads();
-      for (int r = tid; r < cnt; r += kThreads) {
-        float xv[MT];
-        load_tokens<MT>(p.x, p.x_dt, p.ldx, s_idx[r], M, xv);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = fabsf(xv[m]) > t ? xv[m] : 0.f;
-      }
-    }
-    thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
+    int lo;
+    cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo);
+    if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
+      thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
   } else if constexpr (IN == IN_LISTS) {
     int run = 0;
     for (int base = 0; base < n_lt; base += kThreads) {
@@ -417,7 +485,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     if (tid == 0) s_pref[n_lt] = run;
     __syncthreads();
     const int nnz = run;
-    const int lo = int((long)sl * nnz / S), hi = int((long)(sl + 1) * nnz / S);
+    const int lo = split_point(sl, nnz, S), hi = split_point(sl + 1, nnz, S);
     cnt = hi - lo;
     for (int r = tid; r < cnt; r += kThreads) {
       const int g = lo + r;
@@ -444,17 +512,21 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     // Slice sl owns whole list tiles [t0, t1).  Counts and every candidate entry of
     // those tiles are loaded together (one round trip; entries past a tile's count
     // are ignored), staged in LDS, then compacted in tile order.
-    const int t0 = (int)((long)sl * n_lt / S), t1 = (int)((long)(sl + 1) * n_lt / S);
+    const int t0 = split_point(sl, n_lt, S), t1 = split_point(sl + 1, n_lt, S);
     const int nt = t1 - t0;
     const int stride = p.lt_stride;
     const int tot_e = nt * stride;
     int* s_cnt = s_pref;                                   // [nt + 1]
     int* r_idx = reinterpret_cast<int*>(s_w);              // [tot_e] raw candidates
     float* r_val = reinterpret_cast<float*>(r_idx + tot_e);  // [tot_e][M]
-    if (tid < nt) s_cnt[tid] = p.list_cnt[lt0 + t0 + tid];
     const long gbase = (long)(lt0 + t0) * stride;
-    copy_to_lds(r_idx, p.list_idx + gbase, tot_e);
-    copy_to_lds(r_val, p.list_val + gbase * M, tot_e * M);
+    if (p.coherent_lists) {
+      if (tid < nt) s_cnt[tid] = load_coherent_i32(p.list_cnt + lt0 + t0 + tid);
+      copy2_to_lds<true>(r_idx, p.list_idx + gbase, tot_e, r_val, p.list_val + gbase * M, tot_e * M);
+    } else {
+      if (tid < nt) s_cnt[tid] = p.list_cnt[lt0 + t0 + tid];
+      copy2_to_lds<false>(r_idx, p.list_idx + gbase, tot_e, r_val, p.list_val + gbase * M, tot_e * M);
+    }
     __syncthreads();
     if (tid == 0) {
       int run = 0;
@@ -463,18 +535,18 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     }
     __syncthreads();
     cnt = s_cnt[nt];
-    for (int e = tid; e < tot_e; e += kThreads) {
-      const int q = e / stride, k = e % stride;
-      if (s_cnt[q] + k < s_cnt[q + 1]) {
-        const int r = s_cnt[q] + k;
-        s_idx[r] = r_idx[e];
+    for (int q = 0; q < nt; ++q) {
+      const int base = s_cnt[q], len = s_cnt[q + 1] - base;
+      for (int k = tid; k < len; k += kThreads) {
+        const int e = q * stride + k;
+        s_idx[base + k] = r_idx[e];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? r_val[e * M + m] : 0.f;
+        for (int m = 0; m < MT; ++m) s_val[m * cap + base + k] = m < M ? r_val[e * M + m] : 0.f;
       }
     }
   } else {  // IN_ALL: every row, no mask (dense baseline)
     const int K = p.K;
-    const int lo = int((long)sl * K / S), hi = int((long)(sl + 1) * K / S);
+    const int lo = split_point(sl, K, S), hi = split_point(sl + 1, K, S);
     cnt = hi - lo;
     for (int r = tid; r < cnt; r += kThreads) {
       s_idx[r] = lo + r;
@@ -720,62 +792,58 @@ __global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams 
   gemv_item<WDT, MT, LPR, IN, OUT, GU, NT, NV>(p, tile, sl, sl, p.S, 0, p.n_lt, smem);
 }
 
-// ---------------------------------------------------------------- persistent MLP
-// One launch for both stages of the threshold-mode SwiGLU MLP.  Workgroups take
-// items from a queue: first the gate/up items (tile-major, so whole tiles finish
-// early), then the down items (h-tile q, down column tile).  A down item waits
-// only for its own h-tile: the last gate/up item of tile q publishes the tile's
-// compacted h list with device-coherent stores and raises tile_done[q], so the
-// down projection of early tiles streams while later gate/up tiles are still in
-// flight, and there is no second launch, ramp-up or tail.  Every item a down
-// item can wait for was handed out earlier to a workgroup that is running, so
-// the wait always ends; it is bounded anyway and a timeout raises *err.
+// ---------------------------------------------------------------- one-launch MLP
+// Both stages of the threshold-mode SwiGLU MLP in one launch.  Workgroup w runs
+// gate/up item w (column tile, row slice), then down item w (down column tile,
+// group of whole h-tiles), so the grid is exactly as large as the larger stage
+// and the host only takes this path when every workgroup of it is resident at
+// once.  A down item waits only for the h-tiles it reads: the last gate/up
+// workgroup of a tile publishes the tile's compacted h list with device-coherent
+// stores, waits for them, and then raises the tile's flag, and the down item
+// reads the lists device-coherently.  So the down projection of early tiles
+// overlaps the tail of the gate/up stage, and the second launch, its ramp-up and
+// the gap between launches disappear.  The wait is bounded anyway; a timeout
+// raises *err.  The last workgroup to finish clears the flags for the next call.
 template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
 __global__ __launch_bounds__(kThreads) void mlp_fused_kernel(const FusedMlpParams f) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_item;
-  const int tid = threadIdx.x;
-  const int total = f.items1 + f.n_tiles1 * f.n_ct2;
-  for (;;) {
-    __syncthreads();
-    if (tid == 0) s_item = (int)__hip_atomic_fetch_add(f.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int item = s_item;
-    if (item >= total) break;
-    if (item < f.items1) {
-      const int tile = item / f.S1, sl = item % f.S1;
-      gemv_item<WDT, MT, LPR1, IN1, OUT_SWIGLU, true, true, NV>(f.p1, tile, sl, sl, f.S1, 0, 0, smem);
-    } else {
-      const int k = item - f.items1;
-      const int q = k / f.n_ct2, ct = k % f.n_ct2;
-      if (tid == 0) {
-        unsigned spins = 0;
-        while (__hip_atomic_load(f.tile_done + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > (1u << 24)) {
-            __hip_atomic_store(f.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
+  const int w = blockIdx.x, tid = threadIdx.x;
+  if (w < f.items1) {
+    const int tile = w % f.n_tiles1, sl = w / f.n_tiles1;
+    gemv_item<WDT, MT, LPR1, IN1, OUT_SWIGLU, true, true, NV>(f.p1, tile, sl, sl, f.S1, 0, 0, smem);
+  }
+  for (int item = w; item < f.items2; item += gridDim.x) {
+    const int ct = item % f.n_ct2, sl = item / f.n_ct2;
+    const int t0 = split_point(sl, f.n_lt, f.S2), t1 = split_point(sl + 1, f.n_lt, f.S2);
+    if (tid < t1 - t0) {
+      unsigned spins = 0;
+      while (__hip_atomic_load(f.tile_done + t0 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1u << 26)) {
+          __hip_atomic_store(f.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
         }
       }
-      __syncthreads();
-      gemv_item<WDT, MT, LPR2, IN_LISTS, OUT_Y, false, true, 0>(f.p2, ct, 0, q, f.n_tiles1, q, 1, smem);
     }
+    __syncthreads();
+    gemv_item<WDT, MT, LPR2, IN_TILES, OUT_Y, false, true, 0>(f.p2, ct, sl, sl, f.S2, 0, f.n_lt, smem);
+    __syncthreads();
   }
   if (tid == 0) {
     wait_vmem();
     const unsigned prev = __hip_atomic_fetch_add(f.exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == gridDim.x - 1) {
-      for (int q = 0; q < f.n_tiles1; ++q)
+      for (int q = 0; q < f.n_lt; ++q)
         __hip_atomic_store(f.tile_done + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(f.next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(f.exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
+// Launches the one-launch MLP if all of its workgroups fit on the device at once;
+// returns hipErrorCooperativeLaunchTooLarge (nothing launched) otherwise.
 template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
-hipError_t launch_fused_one(const FusedMlpParams& f, size_t smem, int wg_per_cu, int cus, hipStream_t s) {
+hipError_t launch_fused_one(const FusedMlpParams& f, size_t smem, int cus, hipStream_t s) {
   auto k = mlp_fused_kernel<WDT, MT, LPR1, LPR2, IN1, NV>;
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -784,33 +852,30 @@ hipError_t launch_fused_one(const FusedMlpParams& f, size_t smem, int wg_per_cu,
   }
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), kThreads, smem) !=
-          hipSuccess || occ < 1)
-    occ = 1;
-  int per = wg_per_cu > 0 ? (wg_per_cu < occ ? wg_per_cu : occ) : occ;
-  int grid = per * cus;
-  const int total = f.items1 + f.n_tiles1 * f.n_ct2;
-  if (grid > total) grid = total;
-  if (grid < 1) grid = 1;
+      hipSuccess)
+    return hipErrorCooperativeLaunchTooLarge;
+  const int grid = f.items1 > f.items2 ? f.items1 : f.items2;
+  if (grid < 1 || (long)occ * cus < grid) return hipErrorCooperativeLaunchTooLarge;
   hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), smem, s, f);
   return hipGetLastError();
 }
 
 template <int WDT, int MT, int LPR1, int LPR2>
 hipError_t fused_pick_in(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  if (c.in1 == IN_ALL) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_ALL, 0>(f, smem, c.wg_per_cu, c.cus, s);
-  if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 2>(f, smem, c.wg_per_cu, c.cus, s);
+  if (c.in1 == IN_ALL) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_ALL, 0>(f, smem, c.cus, s);
+  if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 2>(f, smem, c.cus, s);
   if constexpr (MT == 1) {
-    if (c.nv == 8) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 8>(f, smem, c.wg_per_cu, c.cus, s);
+    if (c.nv == 8) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 8>(f, smem, c.cus, s);
   }
-  return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 0>(f, smem, c.wg_per_cu, c.cus, s);
+  return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 0>(f, smem, c.cus, s);
 }
 
 template <int WDT, int MT>
 hipError_t fused_pick(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
   if (c.lpr1 == 64 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 64, 16>(c, f, smem, s);
-  if (c.lpr1 == 64 && c.lpr2 == 64) return fused_pick_in<WDT, MT, 64, 64>(c, f, smem, s);
+  if (c.lpr1 == 64 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 64, 32>(c, f, smem, s);
   if (c.lpr1 == 32 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 32, 16>(c, f, smem, s);
-  if (c.lpr1 == 32 && c.lpr2 == 64) return fused_pick_in<WDT, MT, 32, 64>(c, f, smem, s);
+  if (c.lpr1 == 32 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 32, 32>(c, f, smem, s);
   return hipErrorInvalidValue;
 }
 
@@ -829,7 +894,8 @@ hipError_t launch_one(const GemvParams& p, size_t smem, hipStream_t s) {
 
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT>
 hipError_t pick_nv(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
-  if constexpr (IN == IN_THRESH) {
+  // 16-byte chunk prologue: 2 vectors per thread, or 8 for one token
+  if constexpr (IN == IN_THRESH || IN == IN_RANGE) {
     if (c.nv == 2) return launch_one<WDT, MT, LPR, IN, OUT, GU, NT, 2>(p, smem, s);
     if constexpr (MT == 1) {
       if (c.nv == 8) return launch_one<WDT, MT, LPR, IN, OUT, GU, NT, 8>(p, smem, s);
@@ -854,6 +920,7 @@ hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipS
   }
   if (c.out != OUT_Y) return hipErrorInvalidValue;
   if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_Y, false>(c, p, smem, s);
+  if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_LISTS) return pick_nt<WDT, MT, LPR, IN_LISTS, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_TILES) return pick_nt<WDT, MT, LPR, IN_TILES, OUT_Y, false>(c, p, smem, s);
   return pick_nt<WDT, MT, LPR, IN_ALL, OUT_Y, false>(c, p, smem, s);

@@ -7,17 +7,19 @@
 
 namespace as {
 
-enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_TILES = 3 };
+enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_TILES = 3, IN_RANGE = 4 };
 enum { OUT_Y = 0, OUT_SWIGLU = 1 };
 
 // One row-gather GEMV launch: Y[m, c] = sum over listed rows i of xv[m, i] * W[i, c].
-// The rows come from a magnitude mask of a vector (IN_THRESH), from per-tile
-// compacted lists written by an earlier stage (IN_LISTS) or are all rows (IN_ALL).
+// The rows come from a magnitude mask of a vector (IN_THRESH: the whole vector,
+// split evenly over the slices; IN_RANGE: each slice masks its own range), from
+// per-tile compacted lists written by an earlier stage (IN_LISTS, IN_TILES) or
+// are all rows (IN_ALL).
 // The grid is n_tiles column tiles x S slices of the row list (split-K); the
 // last workgroup of a tile sums the S partials in slice order and runs the
 // epilogue (OUT_Y: store y; OUT_SWIGLU: h = silu(g) * u, |h| > t_h, per-tile list).
 struct GemvParams {
-  // input vector (IN_THRESH, IN_ALL): x[m * ldx + i], i < K
+  // input vector (IN_THRESH, IN_RANGE, IN_ALL): x[m * ldx + i], i < K
   const void* x; int x_dt; int M; int K; long ldx; float t;
   // input lists (IN_LISTS): tile q holds list_cnt[q] entries at (q * lt_stride + e)
   const int* list_cnt; const int* list_idx; const float* list_val; int n_lt; int lt_stride;
@@ -32,7 +34,7 @@ struct GemvParams {
   float t_h; float* h; long ldh; int* o_cnt; int* o_idx; float* o_val; uint64_t* h_bits; long h_bits_ld;
   // input-mask verification exports (IN_THRESH)
   uint64_t* x_bits; long x_bits_ld; int* x_idx; int* x_nnz;
-  // persistent MLP kernel: per-tile "list published" flags raised by the SwiGLU epilogue
+  // one-launch MLP: per-tile "list published" flags raised by the SwiGLU epilogue
   unsigned* tile_done;
   int coherent_lists;      // lists written by the same launch: read them device-coherently
 };
@@ -50,17 +52,17 @@ struct GemvConfig {
 
 size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt);
 
-// Persistent two-stage threshold MLP (one launch; see mlp_fused_kernel).
+// One-launch two-stage threshold MLP (see mlp_fused_kernel).
 struct FusedMlpParams {
-  GemvParams p1, p2;       // p1: gate/up items (S = S1); p2: down items over single h-tiles (S = 1)
-  int items1, n_tiles1, S1, n_ct2;
-  unsigned* next;
+  GemvParams p1, p2;       // p1: gate/up items (S1 slices); p2: down items over whole h-tiles (IN_TILES, S2 slices)
+  int items1, n_tiles1, S1;
+  int items2, n_ct2, S2, n_lt;
   unsigned* exit_cnt;
-  unsigned* tile_done;     // [n_tiles1]
+  unsigned* tile_done;     // [n_lt]
   unsigned* err;
 };
 struct FusedCfg {
-  int wdt, mt, lpr1, lpr2, in1, nv, wg_per_cu, cus;
+  int wdt, mt, lpr1, lpr2, in1, nv, cus;
 };
 hipError_t launch_fused_mlp(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s);

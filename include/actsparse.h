@@ -71,7 +71,7 @@ enum {
   AS_FLAG_ACCUMULATE = 1u << 0,   /* Y += result instead of Y = result                   */
   AS_FLAG_NO_NT_LOADS = 1u << 2,  /* plain (cached) weight loads instead of nontemporal  */
   AS_FLAG_FORCE_DENSE = 1u << 3,  /* ignore thresholds / neuron lists: dense baseline   */
-  AS_FLAG_NO_FUSION = 1u << 4     /* threshold MLP: two launches instead of one persistent */
+  AS_FLAG_NO_FUSION = 1u << 4     /* threshold MLP: two launches instead of one           */
 };
 
 /* Verification exports of a mask (every field may be NULL).
@@ -109,7 +109,7 @@ as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64
  * loading only the weight rows whose input survives:
  *   Y[m, :] = sum over i with |X[m, i]| > t of X[m, i] * W[i, :]
  * X: [M, K] (f16/bf16/f32), 1 <= M <= 16 (M > 8 runs on the matrix cores and
- * needs bf16 weights).  W: [K, N] input-major (f16/bf16),
+ * needs bf16 weights), 1 <= K <= 2^24.  W: [K, N] input-major (f16/bf16),
  * N % 8 == 0.  Y: [M, N] (f16/bf16/f32).  t is compared in fp32 with strict
  * '>': t = -INFINITY keeps every row; NaN inputs are dropped.  A weight row is
  * read once for all M tokens if any token keeps it; each token still uses only
@@ -139,8 +139,8 @@ typedef struct {
                              (gate row, up row, down row of neuron j adjacent). */
   const void *w_down;     /* THRESHOLD: [d_ff, d_model] input-major.  NEURON_SET: NULL. */
   as_dtype w_dt;          /* AS_F16 or AS_BF16 */
-  int d_model;            /* multiple of 8 */
-  int d_ff;               /* multiple of 64 */
+  int d_model;            /* multiple of 8, at most 2^24 */
+  int d_ff;               /* multiple of 64, at most 2^24 */
 } as_mlp_weights;
 
 typedef struct {

@@ -166,15 +166,17 @@ def test_neuron_set_full_equals_dense():
 
 _PLANS = [dict(AS_GU_LPR=16, AS_GU_S=1), dict(AS_GU_LPR=16, AS_GU_S=2, AS_DN_TPW=1),
           dict(AS_GU_LPR=32, AS_GU_S=3, AS_DN_LPR=32, AS_DN_TPW=2), dict(AS_DN_LPR=64, AS_DN_TPW=1),
-          dict(AS_GU_LPR=64, AS_GU_S=5, AS_DN_LPR=16, AS_DN_TPW=3)]
+          dict(AS_GU_LPR=64, AS_GU_S=5, AS_DN_LPR=16, AS_DN_TPW=3), dict(AS_DN_TILES=1),
+          dict(AS_FUSED=1), dict(AS_FUSED=1, AS_DN_TPW=2, AS_DN_LPR=32), dict(AS_DN_S=13)]
 
 
 @pytest.mark.parametrize("plan", range(len(_PLANS)))
 @pytest.mark.parametrize("cfg,M", [(1, 1), (1, 8), (2, 1), (2, 16)])
 def test_mlp_launch_plans(plan, cfg, M, monkeypatch):
-    """Other tile widths, split-K factors and down-stage tile groupings (set through the
-    launch-plan overrides) compute the same MLP: the small fp16 shape for 1 and 8 tokens,
-    the Llama shape for 1 and 16 tokens (matrix cores), 50% thresholds."""
+    """Other tile widths, split-K factors, down-stage input modes (h ranges, h-tile lists)
+    and the one-launch variant (set through the launch-plan overrides) compute the same
+    MLP: the small fp16 shape for 1 and 8 tokens, the Llama shape for 1 and 16 tokens
+    (matrix cores), 50% thresholds."""
     for k, v in _PLANS[plan].items():
         monkeypatch.setenv(k, str(v))
     announce(f"mlp plan {_PLANS[plan]} cfg={cfg} M={M}")
