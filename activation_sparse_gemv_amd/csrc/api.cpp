@@ -78,6 +78,17 @@ Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
   else lpr = 16;
   char key[64];
   snprintf(key, sizeof key, "%s_LPR", env_prefix);
+  if (mt >= 16 && env_int(key, 0) == 0) {
+    // matrix-core path: slices of <= 512 rows; widen the tile until the grid fits
+    // two workgroups per CU (a second round of workgroups would double the time)
+    const int s16 = (rows + 511) / 512;
+    while (lpr < 64) {
+      const int tn2 = lpr * 8;
+      const long nt2 = gu ? (cols + tn2 / 2 - 1) / (tn2 / 2) : (cols + tn2 - 1) / tn2;
+      if (nt2 * s16 <= 2L * num_cus()) break;
+      lpr *= 2;
+    }
+  }
   lpr = env_int(key, lpr);
   const int tn = lpr * 8;
   const int n_tiles = gu ? (cols + tn / 2 - 1) / (tn / 2) : (cols + tn - 1) / tn;
@@ -150,6 +161,7 @@ struct MlpPlan {
   int parts2;             // partial slots of the down stage (max of its split and the h-tiles)
   int s2_tiles, cap2_tiles;  // down stage over whole h-tiles (one-launch MLP): slices, max list entries
   int s2_range, cap2_range;  // down stage masking h by range (two launches): slices, max range length
+  int cap1_range;            // gate/up stage masking x by range (several tokens): max range length
 };
 
 MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
@@ -163,12 +175,18 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     mp.n_lt = 1;
     mp.lt_stride = w->d_ff;
   }
+  {
+    const int units = (w->d_model + 63) / 64;
+    mp.cap1_range = ((units + mp.p1.S - 1) / mp.p1.S) * 64;
+  }
   (void)dense;
   mp.p2 = plan_gemv(w->d_ff, w->d_model, false, "AS_DN", mt_for(M));
   {
     // threshold mode, two launches: down slice s masks its own 64-aligned range of h
+    // (several tokens also stage the range of every token in LDS)
     const int units = (w->d_ff + 63) / 64;
-    const int hard = (kLdsBytes - kLdsReserve) / (4 + 4 * mt_for(M));
+    const int mt = mt_for(M);
+    const int hard = (kLdsBytes - kLdsReserve) / (mt > 1 ? 4 + 8 * mt : 4 + 4 * mt);
     int S = mp.p2.S;
     while (S < units && ((units + S - 1) / S) * 64 > hard) ++S;
     mp.s2_range = S;
@@ -286,6 +304,8 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   if (!aligned16(W)) return fail(AS_ERR_INVALID_ARG, "%s: W not 16-byte aligned", fn);
   if (mo && mo->idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: mask idx export needs M == 1", fn);
   const Plan pl = plan_gemv(K, N, false, "AS_GV", mt_for(M));
+  if ((long)pl.S * M * N >= (1L << 31))
+    return fail(AS_ERR_UNSUPPORTED, "%s: split-K partials of %d x %d x %d exceed 2^31 elements", fn, pl.S, M, N);
   Carver c{reinterpret_cast<char*>(ws)};
   GemvWs gw = carve_gemv(c, pl, M, N);
   as_status st = check_ws(ws, ws_bytes, c.off);
@@ -370,6 +390,8 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
     return fail(AS_ERR_UNSUPPORTED, "%s: mask exports exist in THRESHOLD mode only", fn);
 
   const MlpPlan mp = plan_mlp(M, w, mode, dense);
+  if ((long)mp.p1.S * M * 2L * w->d_ff >= (1L << 31) || (long)mp.parts2 * M * w->d_model >= (1L << 31))
+    return fail(AS_ERR_UNSUPPORTED, "%s: split-K partials exceed 2^31 elements", fn);
   Carver c{reinterpret_cast<char*>(ws)};
   MlpWs mw = carve_mlp(c, mp, M, w, mode);
   st = check_ws(ws, ws_bytes, c.off);
@@ -440,6 +462,12 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
     // stage 1: x mask -> gate/up gather GEMV -> SwiGLU -> h (and, with the list-tile
     // down stage, the h mask's per-tile lists)
     const bool dn_tiles = !dense && env_int("AS_DN_TILES", 0) != 0;
+    // several tokens: each gate/up slice masks its own range of x (the union mask
+    // over tokens is nearly dense, so equal ranges are balanced); the x mask exports
+    // and one token use the evenly split compacted list
+    const bool x_exports = dbg && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz);
+    const bool gu_range = !dense && M > 1 && !x_exports && env_int("AS_GU_RANGE", 1) != 0 &&
+                          (long)mp.cap1_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
     GemvParams p = base_params();
     p.x = X; p.x_dt = int(x_dt); p.M = M; p.K = d; p.ldx = d; p.t = t_x;
     p.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.ldw = 2L * f; p.N = f; p.gu_off = f;
@@ -451,7 +479,8 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
       p.h_bits = dbg->h_mask.bits; p.h_bits_ld = (f + 63) / 64;
       p.x_bits = dbg->x_mask.bits; p.x_bits_ld = (d + 63) / 64; p.x_idx = dbg->x_mask.idx; p.x_nnz = dbg->x_mask.nnz;
     }
-    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : IN_THRESH, OUT_SWIGLU, true, nt};
+    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH), OUT_SWIGLU, true, nt};
+    if (gu_range) p.cap = mp.cap1_range;
     if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
     // stage 2: down projection over the surviving h rows; each slice masks its

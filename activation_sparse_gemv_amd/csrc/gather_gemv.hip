@@ -15,9 +15,12 @@ size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
   if (c.mt != 16) b += a16(size_t(nslot > c.mt ? nslot : c.mt) * tn * 4);
   if (c.in == IN_LISTS || c.in == IN_TILES) b += a16(size_t(n_lt + 1) * 4);
   // staging region: IN_TILES raw candidate entries (index + M values, cap of them)
-  // during the prologue; the MFMA weight chunk and output tile afterwards
+  // or the IN_RANGE input range during the prologue; the MFMA weight chunk and
+  // output tile afterwards
   size_t stage = 0;
   if (c.in == IN_TILES) stage = size_t(cap) * (1 + c.mt) * 4;
+  // IN_RANGE, several tokens: the slice's range of every token, fp32
+  if (c.in == IN_RANGE && c.mt > 1) stage = size_t(cap) * c.mt * 4;
   if (c.mt == 16) {
     const size_t rows = size_t(32) * (512 / tn);
     const size_t chunk = rows * (tn + 4) * 2, out = size_t(16) * tn * 4;
@@ -72,9 +75,14 @@ hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStrea
   const size_t smem = gemv_smem_bytes(c, p.cap, p.n_lt);
   GemvConfig cc = c;
   if ((cc.in == IN_THRESH || cc.in == IN_RANGE) && cc.nv < 0) {
-    // the chunk prologue covers the whole input (IN_THRESH) or one slice's range
-    cc.nv = pick_chunk_vectors(p.x, p.x_dt, cc.in == IN_RANGE ? p.cap : p.K, p.ldx);
-    if (cc.mt > 1 && cc.nv > 2) cc.nv = 0;     // wide register chunks only for one token
+    if (cc.in == IN_RANGE && cc.mt > 1) {
+      // staged range prologue: 16-byte vectors whenever rows are aligned
+      cc.nv = (p.K % 8 == 0 && pick_chunk_vectors(p.x, p.x_dt, 1, p.ldx) > 0) ? 2 : 0;
+    } else {
+      // the chunk prologue covers the whole input (IN_THRESH) or one slice's range
+      cc.nv = pick_chunk_vectors(p.x, p.x_dt, cc.in == IN_RANGE ? p.cap : p.K, p.ldx);
+      if (cc.mt > 1 && cc.nv > 2) cc.nv = 0;     // wide register chunks only for one token
+    }
   }
   const bool bf = cc.wdt == DT_BF16;
   switch (cc.mt) {

@@ -40,7 +40,7 @@ __host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~size_t(
 // Verification exports of the per-token input masks (bits and nnz by workgroup 0;
 // the ascending index list, M == 1 only, by the workgroups of column tile 0).
 template <int MT>
-__device__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_scan, int tid, int tile, int lo,
+__device__ __forceinline__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_scan, int tid, int tile, int lo,
                                int cnt, bool first) {
   const int K = p.K;
   const float t = p.t;
@@ -424,6 +424,97 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
   return cnt;
 }
 
+// Several tokens, one slice's own range [i0, i1): every token's values of the
+// range are staged in LDS (stage: [MT][len] fp32) with one round trip of
+// independent loads (16-byte vectors when NV > 0, i.e. aligned rows), then each
+// thread takes a contiguous chunk of the range for the union mask, a workgroup
+// scan places the chunks, and the kept rows' values are copied from the stage.
+template <int MT, int NV>
+__device__ __forceinline__ int compact_range_staged(const GemvParams& p, int i0, int i1, int* s_idx, float* s_val,
+                                                    int cap, float* stage, int* s_scan) {
+  const int tid = threadIdx.x, M = p.M;
+  const float t = p.t;
+  const int L = max(0, i1 - i0);
+  if constexpr (NV > 0) {
+    // vectors of 8 (16-bit) or 4 (fp32) inputs; L is a multiple of 64 except at the end
+    const bool f32 = p.x_dt == DT_F32, bf = p.x_dt == DT_BF16;
+    const int per = f32 ? 4 : 8;
+    const int nvec = (L + per - 1) / per;               // per token
+    const int tot = nvec * MT;
+    for (int j0 = tid; j0 < tot; j0 += 8 * kThreads) {
+      u32x4 raw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u * kThreads, tot - 1);
+        const int m = j / nvec, vi = j % nvec;
+        const int mm = m < M ? m : M - 1;
+        const long e = (long)mm * p.ldx + i0 + (long)vi * per;
+        raw[u] = f32 ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(p.x) + e)
+                     : *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) + e);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * kThreads;
+        if (j < tot) {
+          const int m = j / nvec, vi = j % nvec;
+          // L is a multiple of 8 (whole vectors), so each vector is one or two
+          // 16-byte LDS stores
+          f32x4_t* dst = reinterpret_cast<f32x4_t*>(stage + m * L + vi * per);
+          const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+          const bool live = m < M;
+          if (f32) {
+            dst[0] = live ? f32x4_t{__uint_as_float(w4[0]), __uint_as_float(w4[1]), __uint_as_float(w4[2]),
+                                    __uint_as_float(w4[3])}
+                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          } else {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t hb = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
+              f[e] = live ? (bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb)) : 0.f;
+            }
+            dst[0] = f32x4_t{f[0], f[1], f[2], f[3]};
+            dst[1] = f32x4_t{f[4], f[5], f[6], f[7]};
+          }
+        }
+      }
+    }
+  } else {
+    for (int j = tid; j < L * MT; j += kThreads) {
+      const int m = j / L, i = j % L;
+      stage[j] = m < M ? load_elem(p.x, p.x_dt, (long)m * p.ldx + i0 + i) : 0.f;
+    }
+  }
+  __syncthreads();
+  const int CE = (L + kThreads - 1) / kThreads;
+  const int c0 = min(tid * CE, L), n = max(0, min(CE, L - c0));
+  int c = 0;
+  for (int e = 0; e < n; ++e) {
+    bool a = false;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
+    c += a;
+  }
+  int nnz;
+  int r = block_excl_scan<kThreads>(c, s_scan, &nnz);
+  for (int e = 0; e < n; ++e) {
+    bool a = false;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
+    if (a) {
+      s_idx[r] = i0 + c0 + e;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float xv = stage[m * L + c0 + e];
+        s_val[m * cap + r] = fabsf(xv) > t ? xv : 0.f;
+      }
+      ++r;
+    }
+  }
+  __syncthreads();
+  return nnz;
+}
+
 // One work item: column tile `tile`, row slice `sl` of S (p.S) equal parts of the
 // compacted row list; its partial tile is slot `part` of `n_parts` combined by
 // the last item of the tile to finish.  IN_LISTS reads list tiles
@@ -468,8 +559,11 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       r0 = min(p.K, split_point(sl, units, S) * 64);
       r1 = min(p.K, split_point(sl + 1, units, S) * 64);
     }
-    int lo;
-    cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo);
+    int lo = 0;
+    if constexpr (IN == IN_RANGE && MT > 1)
+      cnt = compact_range_staged<MT, NV>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan);
+    else
+      cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo);
     if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
       thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
   } else if constexpr (IN == IN_LISTS) {
@@ -678,42 +772,53 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     __syncthreads();
     if (!s_flag) return;
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Batches of kBatch slices are loaded together (one round trip per batch),
-    // then summed in slice order.
-    constexpr int kBatch = 16;
-    long pcs[CPT];
+    // Batches of slices are loaded together for every token (one round trip per
+    // batch, at most 128 values in flight per thread), then summed in slice order.
+    constexpr int kBudget = 128 / (MT * CPT);
+    constexpr int kBatch = kBudget < 1 ? 1 : (kBudget > 16 ? 16 : kBudget);
+    // 32-bit element offsets (the partials buffer holds fewer than 2^31 floats);
+    // columns past the tile edge read column 0 and are dropped, so every load is
+    // unconditional.
+    int pcs[CPT];
     bool oks[CPT];
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int c = tid + q * kThreads;
       bool ok;
-      pcs[q] = col_of(c, ok);
+      const long pc = col_of(c, ok);
       oks[q] = c < TN && ok;
+      pcs[q] = oks[q] ? (int)pc : 0;
     }
+    const int slice_stride = M * (int)p.part_ld;
+    float v[MT][CPT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m >= M) break;
-      float v[CPT];
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int q = 0; q < CPT; ++q) v[q] = 0.f;
-      for (int s0 = 0; s0 < n_parts; s0 += kBatch) {
-        float tmp[CPT][kBatch];
+      for (int q = 0; q < CPT; ++q) v[m][q] = 0.f;
+    for (int s0 = 0; s0 < n_parts; s0 += kBatch) {
+      float tmp[MT][CPT][kBatch];
 #pragma unroll
-        for (int q = 0; q < CPT; ++q)
+      for (int k = 0; k < kBatch; ++k) {
+        const float* ps = p.partials + min(s0 + k, n_parts - 1) * slice_stride;
 #pragma unroll
-          for (int k = 0; k < kBatch; ++k) {
-            const int s2 = min(s0 + k, n_parts - 1);
-            tmp[q][k] = oks[q] ? load_coherent(p.partials + ((long)s2 * M + m) * p.part_ld + pcs[q]) : 0.f;
-          }
+        for (int m = 0; m < MT; ++m) {
+          const float* pm = ps + (m < M ? m : M - 1) * (int)p.part_ld;
+#pragma unroll
+          for (int q = 0; q < CPT; ++q) tmp[m][q][k] = load_coherent(pm + pcs[q]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int q = 0; q < CPT; ++q)
 #pragma unroll
           for (int k = 0; k < kBatch; ++k)
-            if (s0 + k < n_parts) v[q] += tmp[q][k];
-      }
-#pragma unroll
-      for (int q = 0; q < CPT; ++q) res[m][q] = v[q];
+            if (s0 + k < n_parts && oks[q]) v[m][q] += tmp[m][q][k];
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) res[m][q] = m < M ? v[m][q] : 0.f;
   }
 
   // ------------------------------------------------------------ epilogues
@@ -785,8 +890,10 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
   }
 }
 
+// At least two waves per SIMD (two workgroups per CU): the register budget of the
+// widest instantiations (16 tokens) must stay within 256 per lane.
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
-__global__ __launch_bounds__(kThreads) void gather_gemv_kernel(const GemvParams p) {
+__global__ __launch_bounds__(kThreads, 2) void gather_gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tile = blockIdx.x % p.n_tiles, sl = blockIdx.x / p.n_tiles;
   gemv_item<WDT, MT, LPR, IN, OUT, GU, NT, NV>(p, tile, sl, sl, p.S, 0, p.n_lt, smem);
@@ -915,6 +1022,9 @@ hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipS
   if (c.gu) {
     if (c.out != OUT_SWIGLU) return hipErrorInvalidValue;
     if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_SWIGLU, true>(c, p, smem, s);
+    if constexpr (MT > 1) {
+      if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_SWIGLU, true>(c, p, smem, s);
+    }
     if (c.in == IN_ALL) return pick_nt<WDT, MT, LPR, IN_ALL, OUT_SWIGLU, true>(c, p, smem, s);
     return hipErrorInvalidValue;
   }
