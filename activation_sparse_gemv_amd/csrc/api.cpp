@@ -188,6 +188,7 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     const int mt = mt_for(M);
     const int hard = (kLdsBytes - kLdsReserve) / (mt > 1 ? 4 + 8 * mt : 4 + 4 * mt);
     int S = mp.p2.S;
+    if (S > units / 2) S = units / 2 > 1 ? units / 2 : 1;      // ranges of at least 128 rows
     while (S < units && ((units + S - 1) / S) * 64 > hard) ++S;
     mp.s2_range = S;
     mp.cap2_range = ((units + S - 1) / S) * 64;
@@ -315,12 +316,28 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   p.x = X; p.x_dt = int(x_dt); p.M = M; p.K = K; p.ldx = K; p.t = t;
   p.W = reinterpret_cast<const uint16_t*>(W); p.ldw = N; p.N = N;
   p.n_tiles = pl.n_tiles; p.S = pl.S; p.cap = pl.cap;
+  // Without mask exports each slice masks its own 64-aligned range of x (no
+  // whole-vector scan per workgroup); ranges of at least 128 rows.
+  const bool exports = mo && (mo->bits || mo->idx || mo->nnz);
+  bool range = false;
+  if (!dense && !exports && env_int("AS_GV_RANGE", 1) != 0) {
+    const int units = (K + 63) / 64;
+    int S = pl.S;
+    if (S > units / 2) S = units / 2 > 1 ? units / 2 : 1;
+    const int cap = ((units + S - 1) / S) * 64;
+    const int mt = mt_for(M);
+    if ((long)cap * (mt > 1 ? 4 + 8 * mt : 4 + 4 * mt) <= kLdsBytes - kLdsReserve) {
+      range = true;
+      p.S = S;
+      p.cap = cap;
+    }
+  }
   p.partials = gw.partials; p.counters = gw.counters; p.part_ld = N;
   p.y = Y; p.y_dt = int(y_dt); p.ldy = N; p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   if (mo && !dense) {
     p.x_bits = mo->bits; p.x_bits_ld = (K + 63) / 64; p.x_idx = mo->idx; p.x_nnz = mo->nnz;
   }
-  GemvConfig cfg{int(w_dt), mt_for(M), pl.lpr, dense ? IN_ALL : IN_THRESH, OUT_Y, false,
+  GemvConfig cfg{int(w_dt), mt_for(M), pl.lpr, dense ? IN_ALL : (range ? IN_RANGE : IN_THRESH), OUT_Y, false,
                  (flags & AS_FLAG_NO_NT_LOADS) == 0};
   return hip_check(launch_gather_gemv(cfg, p, stream), fn);
 }
