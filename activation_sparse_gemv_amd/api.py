@@ -10,6 +10,7 @@ counters at zero after every call, so reuse on one stream is safe.
 from __future__ import annotations
 
 import ctypes
+import os
 import math
 from dataclasses import dataclass
 from fractions import Fraction
@@ -47,7 +48,12 @@ def _need_cuda(*ts):
 
 
 def workspace(key, nbytes: int, device: torch.device) -> torch.Tensor:
-    k = (key, nbytes, str(device))
+    """Zero-filled workspace cached per call shape.  The carve-up of a workspace
+    follows the launch plan, which the AS_* tuning variables can change, so they
+    are part of the key (a workspace reused under another plan could hold stale
+    bytes where the new plan keeps its counters)."""
+    plan_env = tuple(sorted((k, v) for k, v in os.environ.items() if k.startswith("AS_")))
+    k = (key, nbytes, str(device), plan_env)
     ws = _WS.get(k)
     if ws is None:
         ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)

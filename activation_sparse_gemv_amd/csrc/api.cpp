@@ -92,14 +92,15 @@ Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
   lpr = env_int(key, lpr);
   const int tn = lpr * 8;
   const int n_tiles = gu ? (cols + tn / 2 - 1) / (tn / 2) : (cols + tn - 1) / tn;
-  // Slices: about 1.75 workgroups per CU in total, at least ~24 rows per slice.
+  // Slices: about 1.75 workgroups per CU in total, at least 128 rows per slice
+  // (the last workgroup of a tile reads every slice's partial).
   // Every workgroup pays a fixed chain of round trips (input compaction, partial
   // store, tile counter, final combine), so fewer, longer workgroups win as long
   // as every CU has work (measured on MI355X for the 4096 -> 2x14336 and
   // 14336 -> 4096 shapes).
   const int target = (7 * num_cus()) / 4;
   int S = (target + n_tiles - 1) / n_tiles;
-  int smax = rows / 24;
+  int smax = rows / 128;
   if (smax < 1) smax = 1;
   if (S > smax) S = smax;
   if (S > 256) S = 256;
@@ -610,7 +611,7 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
     return fail(AS_ERR_INVALID_ARG, "%s: T=%d top_k=%d (top_k <= 32, T*top_k <= 256)", fn, T, top_k);
   if (w->n_experts < 1 || w->n_experts > 1024) return fail(AS_ERR_INVALID_ARG, "%s: E=%d", fn, w->n_experts);
   if (w->d_model < 8 || w->d_model % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: d_model=%d", fn, w->d_model);
-  if (w->d_ff_e < 1) return fail(AS_ERR_INVALID_ARG, "%s: d_ff_e=%d", fn, w->d_ff_e);
+  if (w->d_ff_e < 1 || w->d_ff_e > 8192) return fail(AS_ERR_UNSUPPORTED, "%s: d_ff_e=%d outside 1..8192", fn, w->d_ff_e);
   if (keep_k < 0 || keep_k > w->d_ff_e) return fail(AS_ERR_INVALID_ARG, "%s: keep_k=%d", fn, keep_k);
   if (!aligned16(w->w_gate_up) || !aligned16(w->w_down)) return fail(AS_ERR_INVALID_ARG, "%s: weights not 16-byte aligned", fn);
   Carver c{reinterpret_cast<char*>(ws)};
@@ -628,6 +629,10 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   p.partials = m.partials; p.counters = m.counters; p.n_tiles = moe_down_tiles(w->d_model);
   p.y = Y; p.y_dt = int(y_dt); p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   p.neurons_per_block = env_int("AS_MOE_NPB", 16);
+  {
+    const int es = x_dt == AS_F32 ? 4 : 2;
+    p.x_vec = aligned16(X) && (long(w->d_model) * es) % 16 == 0;
+  }
   const int max_unique = T * top_k < w->n_experts ? T * top_k : w->n_experts;
   return hip_check(launch_moe(int(w->w_dt), p, max_unique, stream), fn);
 }

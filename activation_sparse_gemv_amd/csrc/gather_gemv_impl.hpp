@@ -42,31 +42,41 @@ __host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~size_t(
 template <int MT>
 __device__ __forceinline__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_scan, int tid, int tile, int lo,
                                int cnt, bool first) {
+  (void)s_scan;
   const int K = p.K;
   const float t = p.t;
   const int M = p.M;
-  const int C = (K + kThreads - 1) / kThreads;
-  const int i0 = min(tid * C, K), i1 = min(i0 + C, K);
-  if (p.x_bits != nullptr && first) {
-    const int nw = (K + 63) / 64;
-    for (int m = 0; m < M; ++m)
-      for (int w = tid; w < nw; w += kThreads) {
-        uint64_t bits = 0;
-        for (int b = 0; b < 64; ++b) {
-          int i = w * 64 + b;
-          if (i < K && fabsf(load_elem(p.x, p.x_dt, m * p.ldx + i)) > t) bits |= (uint64_t)1 << b;
-        }
-        p.x_bits[m * p.x_bits_ld + w] = bits;
+  if ((p.x_bits != nullptr || p.x_nnz != nullptr) && first) {
+    // one 64-bit word of one token per wave and step: lane b tests input 64 w + b
+    // (coalesced loads, eight words in flight per wave), ballot, count
+    __shared__ int s_nnz[MT];
+    if (tid < MT) s_nnz[tid] = 0;
+    __syncthreads();
+    const int nw = (K + 63) / 64, lane = tid & 63, wave = tid >> 6;
+    constexpr int NWV = kThreads / 64;
+    for (int j0 = wave; j0 < M * nw; j0 += 8 * NWV) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u * NWV, M * nw - 1);
+        const int m = j / nw, i = min((j % nw) * 64 + lane, K - 1);
+        v[u] = load_elem(p.x, p.x_dt, (long)m * p.ldx + i);
       }
-  }
-  if (p.x_nnz != nullptr && first) {
-    for (int m = 0; m < M; ++m) {
-      int cm = 0;
-      for (int i = i0; i < i1; ++i) cm += fabsf(load_elem(p.x, p.x_dt, m * p.ldx + i)) > t;
-      int tot;
-      (void)block_excl_scan<kThreads>(cm, s_scan, &tot);
-      if (tid == 0) p.x_nnz[m] = tot;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * NWV;
+        if (j < M * nw) {
+          const int m = j / nw, w = j % nw;
+          const uint64_t bits = __ballot(w * 64 + lane < K && fabsf(v[u]) > t);
+          if (lane == 0) {
+            if (p.x_bits != nullptr) p.x_bits[m * p.x_bits_ld + w] = bits;
+            atomicAdd(&s_nnz[m], __popcll(bits));
+          }
+        }
+      }
     }
+    __syncthreads();
+    if (p.x_nnz != nullptr && tid < M) p.x_nnz[tid] = s_nnz[tid];
   }
   if (p.x_idx != nullptr && tile == 0) {
     __syncthreads();

@@ -91,6 +91,7 @@ struct MoeParams {
   const uint16_t* w_gu; const uint16_t* w_down;     // [E, d_ff, 2, d_model], [E, d_ff, d_model]
   int* grp; float* h; float* h_dbg; int* keep_dbg; float* partials; unsigned* counters; int n_tiles;
   void* y; int y_dt; int accumulate; int neurons_per_block;
+  int x_vec;               // token rows 16-byte aligned (vector staging of x)
 };
 hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s);
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s);

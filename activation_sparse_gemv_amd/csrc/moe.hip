@@ -22,35 +22,41 @@
 namespace as {
 
 // ---------------------------------------------------------------- router
-constexpr int kRouterThreads = 128;
+// One wave per token: exact top-k of the logits (wave radix select), the
+// selection ordered by (logit desc, index asc) through per-lane ranks, and the
+// softmax over the selected logits.
+constexpr int kRouterThreads = 64;
 
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(const float* logits, int E, int top, int* ids,
                                                                 float* wts) {
   __shared__ TopkSmem sm;
   __shared__ int sel[64];
   const long t = blockIdx.x;
+  const int lane = threadIdx.x;
   const float* z = logits + t * E;
-  block_topk<kRouterThreads>([=](int i) { return float_key(z[i]); }, E, top, nullptr, sel, sm);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // order the selection by (logit desc, index asc), then softmax over it
-    for (int a = 1; a < top; ++a) {
-      const int v = sel[a];
-      const uint32_t kv = float_key(z[v]);
-      int b = a - 1;
-      while (b >= 0 && (float_key(z[sel[b]]) < kv || (float_key(z[sel[b]]) == kv && sel[b] > v))) {
-        sel[b + 1] = sel[b];
-        --b;
-      }
-      sel[b + 1] = v;
+  wave_topk([=](int i) { return float_key(z[i]); }, E, top, sel, sm);
+  __builtin_amdgcn_wave_barrier();
+  // lane a < top holds selection a; its rank in (logit desc, index asc) order
+  int me = 0, rank = 0;
+  uint32_t km = 0u;
+  if (lane < top) {
+    me = sel[lane];
+    km = float_key(z[me]);
+    for (int b = 0; b < top; ++b) {
+      const int ob = sel[b];
+      const uint32_t kb = float_key(z[ob]);
+      rank += (kb > km) || (kb == km && ob < me);
     }
-    const float zmax = z[sel[0]];
-    float sum = 0.f;
-    for (int a = 0; a < top; ++a) sum += expf(z[sel[a]] - zmax);
-    for (int a = 0; a < top; ++a) {
-      ids[t * top + a] = sel[a];
-      wts[t * top + a] = expf(z[sel[a]] - zmax) / sum;
-    }
+  }
+  // softmax over the selected logits, shifted by their maximum
+  float m = lane < top ? z[me] : -INFINITY;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float ev = lane < top ? expf(z[me] - m) : 0.f;
+  const float sum = wave_sum(ev);
+  if (lane < top) {
+    ids[t * top + rank] = me;
+    wts[t * top + rank] = ev / sum;
   }
 }
 
@@ -124,7 +130,68 @@ __global__ __launch_bounds__(kGrpThreads) void group_kernel(const int* ids, int 
 constexpr int kGuThreads = 256;
 constexpr int kGuTok = 4;   // tokens per pass
 
-template <int WDT>
+// One or two tokens of an expert: the tokens' inputs stay in registers (lane l
+// holds inputs l*8 + 512 k .. +8, the columns its weight loads meet), so the
+// weight stream is not limited by LDS reads.  d_model <= 512 * NK, aligned rows.
+template <int WDT, int TK, int NK>
+__device__ __forceinline__ void expert_neurons_reg(const MoeParams& p, const uint16_t* W, const int* items, int g0,
+                                                   int ng, int n0, int n1) {
+  const int d = p.d_model, f = p.d_ff;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float xr[TK][NK][8];
+#pragma unroll
+  for (int m = 0; m < TK; ++m) {
+    const long row = (long)(items[g0 + (m < ng ? m : ng - 1)] / p.top) * p.ldx;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = lane * 8 + k * 512;
+      load_chunk<8>(p.x, p.x_dt, row + (c < d ? c : 0), (m < ng && c < d) ? 8 : 0, xr[m][k]);
+    }
+  }
+  for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
+    const uint16_t* wg = W + (long)n * 2 * d;
+    const uint16_t* wu = wg + d;
+    u32x4 vg[NK], vu[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = min(lane * 8 + k * 512, d - 8);
+      vg[k] = load_w16<true>(wg + c);
+      vu[k] = load_w16<true>(wu + c);
+    }
+    float g[TK], uu[TK];
+#pragma unroll
+    for (int m = 0; m < TK; ++m) { g[m] = 0.f; uu[m] = 0.f; }
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      if (lane * 8 + k * 512 < d) {
+        float fg[8], fu[8];
+        unpack8<WDT>(vg[k], fg);
+        unpack8<WDT>(vu[k], fu);
+#pragma unroll
+        for (int m = 0; m < TK; ++m)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            g[m] = fmaf(xr[m][k][q], fg[q], g[m]);
+            uu[m] = fmaf(xr[m][k][q], fu[q], uu[m]);
+          }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < TK; ++m) {
+      const float gs = wave_sum(g[m]);
+      const float us = wave_sum(uu[m]);
+      if (lane == 0 && m < ng) {
+        const int it = items[g0 + m];
+        const float h = silu_f32(gs) * us;
+        p.h[(long)it * f + n] = h;
+        if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
+      }
+    }
+  }
+}
+
+// NK > 0: groups of one or two tokens take the register path (d_model <= 512 NK).
+template <int WDT, int NK>
 __global__ __launch_bounds__(kGuThreads) void expert_gu_kernel(const MoeParams p) {
   extern __shared__ __align__(16) float xs[];   // [kGuTok][d]
   const int u = blockIdx.x;
@@ -140,12 +207,60 @@ __global__ __launch_bounds__(kGuThreads) void expert_gu_kernel(const MoeParams p
   const uint16_t* W = p.w_gu + (long)e * f * 2 * d;
   for (int g0 = st; g0 < en; g0 += kGuTok) {
     const int ng = min(kGuTok, en - g0);
+    if constexpr (NK > 0) {
+      if (ng <= 2) {
+        if (ng == 1) expert_neurons_reg<WDT, 1, NK>(p, W, items, g0, ng, n0, n1);
+        else expert_neurons_reg<WDT, 2, NK>(p, W, items, g0, ng, n0, n1);
+        continue;
+      }
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < kGuTok * d; i += kGuThreads) {
-      const int m = i / d, c = i % d;
-      float v = 0.f;
-      if (m < ng) v = load_elem(p.x, p.x_dt, (long)(items[g0 + m] / p.top) * p.ldx + c);
-      xs[i] = v;
+    if (p.x_vec) {
+      // 16-byte loads of the group's token rows, issued together, staged as fp32
+      const bool f32 = p.x_dt == DT_F32, bf = p.x_dt == DT_BF16;
+      const int per = f32 ? 4 : 8, nv = d / per, tot = kGuTok * nv;
+      for (int j0 = threadIdx.x; j0 < tot; j0 += 4 * kGuThreads) {
+        u32x4 raw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = min(j0 + q * kGuThreads, tot - 1);
+          const int m = min(j / nv, ng - 1), vi = j % nv;
+          const long e0 = (long)(items[g0 + m] / p.top) * p.ldx + (long)vi * per;
+          raw[q] = f32 ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(p.x) + e0)
+                       : *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) + e0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + q * kGuThreads;
+          if (j < tot) {
+            const int m = j / nv, vi = j % nv;
+            float4* dst = reinterpret_cast<float4*>(xs + m * d + vi * per);
+            const uint32_t w4[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+            const bool live = m < ng;
+            if (f32) {
+              dst[0] = live ? make_float4(__uint_as_float(w4[0]), __uint_as_float(w4[1]), __uint_as_float(w4[2]),
+                                          __uint_as_float(w4[3]))
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+              float fv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t hb = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
+                fv[e] = live ? (bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb)) : 0.f;
+              }
+              dst[0] = make_float4(fv[0], fv[1], fv[2], fv[3]);
+              dst[1] = make_float4(fv[4], fv[5], fv[6], fv[7]);
+            }
+          }
+        }
+      }
+    } else {
+      for (int i = threadIdx.x; i < kGuTok * d; i += kGuThreads) {
+        const int m = i / d, c = i % d;
+        float v = 0.f;
+        if (m < ng) v = load_elem(p.x, p.x_dt, (long)(items[g0 + m] / p.top) * p.ldx + c);
+        xs[i] = v;
+      }
     }
     __syncthreads();
     for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
@@ -203,12 +318,25 @@ constexpr int kDnThreads = 256;
 constexpr int kDnLpr = 64;                 // one wave covers 512 columns of one row
 constexpr int kDnTile = kDnLpr * 8;
 
+// Workgroup copy of n floats to LDS, eight loads in flight per thread.
+__device__ __forceinline__ void copy_to_lds_f32(float* dst, const float* src, int n) {
+  for (int j = threadIdx.x; j < n; j += 8 * kDnThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[min(j + u * kDnThreads, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j + u * kDnThreads < n) dst[j + u * kDnThreads] = v[u];
+  }
+}
+
 template <int WDT>
 __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   int* keep = reinterpret_cast<int*>(smem);                        // [keep_k]
   float* kval = reinterpret_cast<float*>(smem + 4 * ((p.keep_k + 3) & ~3));
   float* red = kval + ((p.keep_k + 3) & ~3);                       // [4][kDnTile]
+  float* hs = red + 4 * kDnTile;                                   // [d_ff] this item's h
   __shared__ TopkSmem sm;
   __shared__ int s_last;
   const int item = blockIdx.x;                  // t * top + j
@@ -220,9 +348,11 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   if (!valid_e) e = 0;
   const float* h = p.h + (long)item * f;
   const int kk = valid_e ? p.keep_k : 0;
-  block_topk<kDnThreads>([=](int i) { return float_key(fabsf(h[i])); }, f, kk, nullptr, keep, sm);
+  copy_to_lds_f32(hs, h, f);
   __syncthreads();
-  for (int r = threadIdx.x; r < kk; r += kDnThreads) kval[r] = h[keep[r]];
+  block_topk<kDnThreads>([=](int i) { return float_key(fabsf(hs[i])); }, f, kk, nullptr, keep, sm);
+  __syncthreads();
+  for (int r = threadIdx.x; r < kk; r += kDnThreads) kval[r] = hs[keep[r]];
   if (p.keep_dbg != nullptr && tile == 0)
     for (int r = threadIdx.x; r < p.keep_k; r += kDnThreads) p.keep_dbg[(long)item * p.keep_k + r] = kk ? keep[r] : -1;
   __syncthreads();
@@ -294,14 +424,21 @@ hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s
   if (e != hipSuccess) return e;
   const int nblk = (p.d_ff + p.neurons_per_block - 1) / p.neurons_per_block;
   const size_t sm1 = size_t(kGuTok) * p.d_model * 4;
-  auto k1 = wdt == DT_BF16 ? expert_gu_kernel<DT_BF16> : expert_gu_kernel<DT_F16>;
+  const int d = p.d_model;
+  const int nk = (!p.x_vec || d > 4096) ? 0 : d <= 512 ? 1 : d <= 1024 ? 2 : d <= 2048 ? 4 : 8;
+  auto pick = [&](auto kb, auto kf) { return wdt == DT_BF16 ? kb : kf; };
+  auto k1 = nk == 0   ? pick(expert_gu_kernel<DT_BF16, 0>, expert_gu_kernel<DT_F16, 0>)
+            : nk == 1 ? pick(expert_gu_kernel<DT_BF16, 1>, expert_gu_kernel<DT_F16, 1>)
+            : nk == 2 ? pick(expert_gu_kernel<DT_BF16, 2>, expert_gu_kernel<DT_F16, 2>)
+            : nk == 4 ? pick(expert_gu_kernel<DT_BF16, 4>, expert_gu_kernel<DT_F16, 4>)
+                      : pick(expert_gu_kernel<DT_BF16, 8>, expert_gu_kernel<DT_F16, 8>);
   if (sm1 > 64 * 1024) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize, int(sm1));
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k1, dim3(max_unique, nblk), dim3(kGuThreads), sm1, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t sm2 = size_t(8) * ((p.keep_k + 3) & ~3) + size_t(4) * kDnTile * 4;
+  const size_t sm2 = size_t(8) * ((p.keep_k + 3) & ~3) + size_t(4) * kDnTile * 4 + size_t(p.d_ff) * 4;
   auto k2 = wdt == DT_BF16 ? expert_down_kernel<DT_BF16> : expert_down_kernel<DT_F16>;
   hipLaunchKernelGGL(k2, dim3(p.T * p.top, p.n_tiles), dim3(kDnThreads), sm2, s, p);
   return hipGetLastError();

@@ -112,4 +112,59 @@ __device__ void block_topk(KeyFn key, int n, int k, uint64_t* mask, int* idx, To
   }
 }
 
+// The same selection by a single wave, without workgroup barriers (only the
+// calling wave may use `sm`; a wave's LDS operations complete in order).  For
+// small n, where the barriers of the workgroup version dominate: the router's
+// logits, one expert's neurons.  Writes idx[0..k) ascending.
+template <class KeyFn>
+__device__ void wave_topk(KeyFn key, int n, int k, int* idx, TopkSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  if (k > n) k = n;
+  if (k <= 0) return;
+  const bool all = k >= n;
+  uint32_t T = 0u;
+  int take_eq = 0;
+  if (!all) {
+    uint32_t prefix = 0u;
+    int krem = k;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+      for (int b = lane; b < 256; b += 64) sm.hist[b] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < n; i += 64) {
+        const uint32_t kk = key(i);
+        if ((kk & hi_mask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & 0xffu], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      wave_select_bin(sm.hist, krem, true, &sm.sel_bin, &sm.sel_krem);
+      __builtin_amdgcn_wave_barrier();
+      prefix |= (uint32_t)sm.sel_bin << shift;
+      krem = sm.sel_krem;
+      __builtin_amdgcn_wave_barrier();
+    }
+    T = prefix;
+    take_eq = krem;
+  }
+  int run_eq = 0, run_sel = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    bool sel = false, eq = false;
+    if (i < n) {
+      if (all) sel = true;
+      else {
+        const uint32_t kk = key(i);
+        sel = kk > T;
+        eq = kk == T;
+      }
+    }
+    const uint64_t eqb = __ballot(eq);
+    if (eq && run_eq + lanes_below(eqb) < take_eq) sel = true;
+    run_eq += __popcll(eqb);
+    const uint64_t sb = __ballot(sel);
+    if (sel && idx != nullptr) idx[run_sel + lanes_below(sb)] = i;
+    run_sel += __popcll(sb);
+  }
+}
+
 }  // namespace as

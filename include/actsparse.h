@@ -32,8 +32,11 @@
  *  - Workspace: `ws` must hold at least the size returned by the matching
  *    *_ws_size query and must be zero-filled before its first use (any zero
  *    fill, or as_workspace_init).  Every call leaves the counters it uses at
- *    zero again, so a workspace is reusable by later calls on the same stream.
- *    Calls that may run concurrently need distinct workspaces.
+ *    zero again, so a workspace is reusable by later calls on the same stream
+ *    with the same shapes.  The carve-up follows the call's launch plan; the
+ *    AS_* tuning environment variables (tile width, slices) change plans, so
+ *    re-zero a workspace after changing them.  Calls that may run concurrently
+ *    need distinct workspaces.
  *  - Errors: arguments are validated on the host before anything is enqueued
  *    (AS_ERR_INVALID_ARG / AS_ERR_UNSUPPORTED / AS_ERR_WORKSPACE); a launch
  *    failure returns AS_ERR_HIP.  as_last_error() gives the message of the last
@@ -212,7 +215,7 @@ typedef struct {
   as_dtype w_dt;          /* AS_F16 or AS_BF16 */
   int n_experts;          /* E, 1..1024 */
   int d_model;            /* multiple of 8 */
-  int d_ff_e;             /* neurons per expert */
+  int d_ff_e;             /* neurons per expert, at most 8192 */
 } as_moe_weights;
 
 /* Router (intra-expert summary, method section: routed experts are chosen by the
