@@ -282,18 +282,47 @@ def as_sparse_moe_expert(X: torch.Tensor, w: MoEWeights, ids: torch.Tensor, wts:
     return (Y, dict(h=h, keep=keep)) if debug else Y
 
 
-def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: int = 0, debug: bool = False):
+_SIDE = {}
+
+
+def _side_stream(device: torch.device) -> torch.cuda.Stream:
+    """A second stream (default priority) per device, for work that can overlap."""
+    k = str(device)
+    if k not in _SIDE:
+        _SIDE[k] = torch.cuda.Stream(device=device)
+    return _SIDE[k]
+
+
+def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: int = 0, debug: bool = False,
+              overlap: bool = True):
     """One MoE layer from the library's entry points: router logits (dense GEMV),
     router top-k + softmax, the dense shared expert, then the routed experts
-    accumulated on top.  Returns Y [T, d] fp32 (and intermediates when debug)."""
+    accumulated on top.  With `overlap`, the shared expert runs on a second stream
+    while the router runs (the routed experts then wait for it, since they
+    accumulate into its output).  Returns Y [T, d] fp32 (and intermediates when
+    debug)."""
     T, d = X.shape
+    Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
+    cur = torch.cuda.current_stream(X.device)
+
+    def shared():
+        for t0 in range(0, T, 16):
+            as_sparse_swiglu_mlp(X[t0:t0 + 16], w.shared, flags=L.AS_FLAG_FORCE_DENSE, Y=Y[t0:t0 + 16])
+
+    side = _side_stream(X.device) if overlap else None
+    if side is not None:
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            shared()
+        Y.record_stream(side)
     logits = torch.empty((T, w.w_router.shape[1]), dtype=torch.float32, device=X.device)
     for t0 in range(0, T, 16):
         as_dense_gemv(X[t0:t0 + 16], w.w_router, Y=logits[t0:t0 + 16])
     ids, wts = as_moe_router(logits, top_k)
-    Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
-    for t0 in range(0, T, 16):
-        as_sparse_swiglu_mlp(X[t0:t0 + 16], w.shared, flags=L.AS_FLAG_FORCE_DENSE, Y=Y[t0:t0 + 16])
+    if side is not None:
+        cur.wait_stream(side)
+    else:
+        shared()
     r = as_sparse_moe_expert(X, w, ids, wts, keep_k, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug)
     if debug:
         return Y, dict(logits=logits, ids=ids, wts=wts, **r[1])
