@@ -152,17 +152,20 @@ struct MlpWs {
   int* l_cnt;
   int* l_idx;
   float* l_val;
-  unsigned* queue;        // [1] exit count, [2] error flag (one-launch MLP)
-  unsigned* tile_done;    // [n_lt]
+  unsigned* queue;        // one-launch MLP: [1] exit count, [2] error flag, [3] ready-list length
+  unsigned* fx_cnt;       // one-launch MLP: finished gate/up slices per h range
+  unsigned* fx_ready;     // one-launch MLP: ready list of h ranges, kCntStride apart
 };
 
 struct MlpPlan {
   Plan p1, p2;
   int n_lt, lt_stride;
   int parts2;             // partial slots of the down stage (max of its split and the h-tiles)
-  int s2_tiles, cap2_tiles;  // down stage over whole h-tiles (one-launch MLP): slices, max list entries
+  int s2_tiles, cap2_tiles;  // down stage over whole h-tiles (AS_DN_TILES): slices, max list entries
   int s2_range, cap2_range;  // down stage masking h by range (two launches): slices, max range length
   int cap1_range;            // gate/up stage masking x by range (several tokens): max range length
+  int fx_groups, fx_k2, fx_ranges, cap2_fused;  // one-launch MLP: XCD groups, h ranges per group (at
+                                                // most) and in all, max range length
 };
 
 MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
@@ -187,17 +190,39 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     // (several tokens also stage the range of every token in LDS)
     const int units = (w->d_ff + 63) / 64;
     const int mt = mt_for(M);
-    const int hard = (kLdsBytes - kLdsReserve) / (mt > 1 ? 4 + 8 * mt : 4 + 4 * mt);
+    // per row: index, activations and the staged range (IN_RANGE with several
+    // tokens, IN_PARTS)
+    const int hard = (kLdsBytes - kLdsReserve) / (4 + 8 * mt);
     int S = mp.p2.S;
     if (S > units / 2) S = units / 2 > 1 ? units / 2 : 1;      // ranges of at least 128 rows
     while (S < units && ((units + S - 1) / S) * 64 > hard) ++S;
     mp.s2_range = S;
     mp.cap2_range = ((units + S - 1) / S) * 64;
   }
+  {
+    // one-launch MLP: group x (one per XCD) owns gate/up tiles and the h rows they
+    // produce, split into fx_k2 down ranges
+    mp.fx_groups = 8;
+    mp.fx_k2 = env_int("AS_FX_K2", 2);
+    if (mp.fx_k2 < 1) mp.fx_k2 = 1;
+    // ranges of whole gate/up tiles: min(k2, tiles of the group) per group
+    const int tb1 = mp.p1.lpr * 4;
+    const int G = mp.fx_groups;
+    mp.fx_ranges = 0;
+    for (int x = 0; x < G; ++x) {
+      const int nt = (int)(((long)(x + 1) * mp.p1.n_tiles) / G - ((long)x * mp.p1.n_tiles) / G);
+      mp.fx_ranges += nt < mp.fx_k2 ? nt : mp.fx_k2;
+    }
+    const int nt_max = (mp.p1.n_tiles + G - 1) / G;
+    const int nr_max = nt_max < mp.fx_k2 ? nt_max : mp.fx_k2;
+    const long rows = (long)((nt_max + nr_max - 1) / (nr_max > 0 ? nr_max : 1)) * tb1;
+    mp.cap2_fused = (int)(rows < w->d_ff ? rows : w->d_ff);
+  }
   mp.parts2 = mp.p2.S > mp.n_lt ? mp.p2.S : mp.n_lt;
   if (mp.s2_range > mp.parts2) mp.parts2 = mp.s2_range;
+  if (mp.fx_ranges > mp.parts2) mp.parts2 = mp.fx_ranges;
   {
-    // one-launch MLP: each down slice owns whole h-tiles (about 1.75 workgroups per CU)
+    // down stage over whole h-tiles: each slice owns whole h-tiles (about 1.75 workgroups per CU)
     const int target = (7 * num_cus()) / 4;
     int tpw = (int)((long)mp.n_lt * mp.p2.n_tiles / (target > 0 ? target : 1));
     // list entries per slice: index + activations in LDS twice (raw, then compacted)
@@ -226,7 +251,8 @@ MlpWs carve_mlp(Carver& c, const MlpPlan& mp, int M, const as_mlp_weights* w, as
   ws.l_idx = c.take<int>(w->d_ff);
   ws.l_val = c.take<float>(size_t(w->d_ff) * M);
   ws.queue = c.take<unsigned>(4);
-  ws.tile_done = c.take<unsigned>(mp.n_lt);
+  ws.fx_cnt = c.take<unsigned>(mode == AS_MLP_THRESHOLD ? size_t(mp.fx_ranges) : 0);
+  ws.fx_ready = c.take<unsigned>(mode == AS_MLP_THRESHOLD ? size_t(mp.fx_ranges) * kCntStride : 0);
   return ws;
 }
 
@@ -429,51 +455,66 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   GemvParams p2 = base_params();
   GemvConfig c2{int(w->w_dt), mt, mp.p2.lpr, IN_LISTS, OUT_Y, false, nt};
 
-  // One launch for both stages (opt-in: measured slower than two launches on the
-  // Llama shape, since an h-tile completes only with its slowest slice) when every
-  // workgroup of it can be resident at once (the launcher checks occupancy and
-  // launches nothing otherwise).
+  // One launch for both stages (threshold mode, up to 8 tokens): gate/up
+  // workgroups, then down workgroups that start on their range of h as soon as the
+  // gate/up tiles covering it are complete (grouped by XCD).
   const bool try_fused = mode == AS_MLP_THRESHOLD && mt <= 8 && nt && (flags & AS_FLAG_NO_FUSION) == 0 &&
                          env_int("AS_FUSED", 0) != 0 && (mp.p1.lpr == 32 || mp.p1.lpr == 64) &&
-                         (mp.p2.lpr == 16 || mp.p2.lpr == 32);
+                         (mp.p2.lpr == 16 || mp.p2.lpr == 32) &&
+                         (long)mp.cap2_fused * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
   if (try_fused) {
+    const bool x_exports = dbg && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz);
+    const bool gu_range = !dense && (M > 1 ? env_int("AS_GU_RANGE", 1) != 0 : env_int("AS_GU_RANGE", 1) == 2) &&
+                          !x_exports &&
+                          (long)mp.cap1_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
     FusedMlpParams fz;
     memset(&fz, 0, sizeof fz);
     GemvParams& q1 = fz.p1;
     q1 = base_params();
     q1.x = X; q1.x_dt = int(x_dt); q1.M = M; q1.K = d; q1.ldx = d; q1.t = dense ? -INFINITY : t_x;
     q1.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); q1.ldw = 2L * f; q1.N = f; q1.gu_off = f;
-    q1.n_tiles = mp.p1.n_tiles; q1.S = mp.p1.S; q1.cap = mp.p1.cap;
-    q1.partials = mw.g1.partials; q1.counters = mw.g1.counters; q1.part_ld = 2L * f;
-    q1.t_h = dense ? -INFINITY : t_h; q1.h = hbuf; q1.ldh = f;
-    q1.o_cnt = mw.l_cnt; q1.o_idx = mw.l_idx; q1.o_val = mw.l_val; q1.tile_done = mw.tile_done;
+    q1.n_tiles = mp.p1.n_tiles; q1.S = mp.p1.S; q1.cap = gu_range ? mp.cap1_range : mp.p1.cap;
+    q1.partials = mw.g1.partials; q1.part_ld = 2L * f;
     if (dbg && !dense) {
-      q1.h_bits = dbg->h_mask.bits; q1.h_bits_ld = (f + 63) / 64;
       q1.x_bits = dbg->x_mask.bits; q1.x_bits_ld = (d + 63) / 64; q1.x_idx = dbg->x_mask.idx; q1.x_nnz = dbg->x_mask.nnz;
     }
     GemvParams& q2 = fz.p2;
     q2 = base_params();
     q2.M = M; q2.W = reinterpret_cast<const uint16_t*>(w->w_down); q2.ldw = d; q2.N = d;
-    q2.list_cnt = mw.l_cnt; q2.list_idx = mw.l_idx; q2.list_val = mw.l_val;
-    q2.n_lt = mp.n_lt; q2.lt_stride = mp.lt_stride; q2.coherent_lists = 1;
-    q2.n_tiles = mp.p2.n_tiles; q2.S = mp.s2_tiles; q2.cap = mp.cap2_tiles;
+    q2.x = mw.g1.partials; q2.x_dt = AS_F32; q2.K = f; q2.ldx = 2L * f; q2.t = dense ? -INFINITY : t_h;
+    q2.x_parts = mp.p1.S; q2.x_up = f; q2.keep_all = dense ? 1 : 0;
+    q2.h = (dbg && dbg->h) ? dbg->h : nullptr; q2.ldh = f;
+    if (dbg && !dense) { q2.h_bits = dbg->h_mask.bits; q2.h_bits_ld = (f + 63) / 64; }
+    q2.n_tiles = mp.p2.n_tiles; q2.S = mp.fx_ranges; q2.cap = mp.cap2_fused;
     q2.partials = mw.g2.partials; q2.counters = mw.g2.counters; q2.part_ld = d;
     q2.y = Y; q2.y_dt = int(y_dt); q2.ldy = d; q2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
-    fz.n_tiles1 = mp.p1.n_tiles; fz.S1 = mp.p1.S; fz.items1 = fz.n_tiles1 * fz.S1;
-    fz.n_ct2 = mp.p2.n_tiles; fz.S2 = mp.s2_tiles; fz.items2 = fz.n_ct2 * fz.S2; fz.n_lt = mp.n_lt;
-    fz.exit_cnt = mw.queue + 1; fz.err = mw.queue + 2; fz.tile_done = mw.tile_done;
-    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : IN_THRESH, OUT_SWIGLU, true, true};
-    GemvConfig c2t{int(w->w_dt), mt, mp.p2.lpr, IN_TILES, OUT_Y, false, true};
-    const size_t sm1 = gemv_smem_bytes(c1, q1.cap, 0), sm2 = gemv_smem_bytes(c2t, q2.cap, q2.n_lt);
-    FusedCfg fc{int(w->w_dt), mt, mp.p1.lpr, mp.p2.lpr, dense ? IN_ALL : IN_THRESH,
-                dense ? 0 : pick_chunk_vectors(X, int(x_dt), d, d), num_cus()};
-    if (mt > 1 && fc.nv > 2) fc.nv = 0;
-    const hipError_t e = launch_fused_mlp(fc, fz, sm1 > sm2 ? sm1 : sm2, stream);
-    if (e != hipErrorCooperativeLaunchTooLarge) {
-      if ((st = hip_check(e, fn)) != AS_OK) return st;
-      if ((st = rec(1)) != AS_OK) return st;
-      return rec(2);
+    q2.err_flag = mw.queue + 2;
+    fz.n_tiles1 = mp.p1.n_tiles; fz.S1 = mp.p1.S; fz.tb1 = mp.p1.lpr * 4;
+    fz.n_ct2 = mp.p2.n_tiles; fz.k2 = mp.fx_k2; fz.groups = mp.fx_groups; fz.n_ranges = mp.fx_ranges;
+    fz.g1 = fz.groups * ((fz.n_tiles1 + fz.groups - 1) / fz.groups) * fz.S1;
+    fz.g2 = fz.n_ranges * fz.n_ct2;
+    fz.range_cnt = mw.fx_cnt; fz.ready = mw.fx_ready; fz.ready_tail = mw.queue + 3;
+    fz.exit_cnt = mw.queue + 1; fz.err = mw.queue + 2;
+    const int in1 = dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH);
+    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, in1, OUT_PARTS, true, true};
+    GemvConfig c2f{int(w->w_dt), mt, mp.p2.lpr, IN_PARTS, OUT_Y, false, true};
+    const size_t sm1 = gemv_smem_bytes(c1, q1.cap, 0), sm2 = gemv_smem_bytes(c2f, q2.cap, 0);
+    int nv = 0;
+    if (in1 == IN_THRESH) {
+      nv = pick_chunk_vectors(X, int(x_dt), d, d);
+      if (mt > 1 && nv > 2) nv = 0;
+    } else if (in1 == IN_RANGE) {
+      nv = (d % 8 == 0 && pick_chunk_vectors(X, int(x_dt), 1, d) > 0) ? 2 : 0;
     }
+    FusedCfg fc{int(w->w_dt), mt, mp.p1.lpr, mp.p2.lpr, in1, nv};
+    // LDS of at least a third of a CU's, so that at most two workgroups share a CU and
+    // most down workgroups are dispatched as gate/up workgroups of their XCD finish
+    size_t smem = sm1 > sm2 ? sm1 : sm2;
+    const size_t lds_min = size_t(env_int("AS_FX_LDS_KB", 56)) * 1024;
+    if (smem < lds_min) smem = lds_min;
+    if ((st = hip_check(launch_fused_mlp(fc, fz, smem, stream), fn)) != AS_OK) return st;
+    if ((st = rec(1)) != AS_OK) return st;
+    return rec(2);
   }
 
   if (mode == AS_MLP_THRESHOLD) {
@@ -484,8 +525,17 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
     // over tokens is nearly dense, so equal ranges are balanced); the x mask exports
     // and one token use the evenly split compacted list
     const bool x_exports = dbg && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz);
-    const bool gu_range = !dense && M > 1 && !x_exports && env_int("AS_GU_RANGE", 1) != 0 &&
+    const bool gu_range = !dense && (M > 1 ? env_int("AS_GU_RANGE", 1) != 0 : env_int("AS_GU_RANGE", 1) == 2) &&
+                          !x_exports &&
                           (long)mp.cap1_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
+    // The gate/up launch stores its split-K partials unsummed and the down launch
+    // sums them for its own range of h (SwiGLU, mask and compaction in its
+    // prologue): the gate/up launch then ends without the chain of partial store,
+    // tile counter and combine of its last workgroups.  One token by default (the
+    // down prologue reads every gate/up slice's partial of its range, which for
+    // several tokens costs more than the combine it replaces).
+    const bool dn_parts = !dn_tiles && mt <= 8 && env_int("AS_DN_PARTS", mt == 1 ? 1 : 0) != 0 &&
+                          (long)mp.cap2_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
     GemvParams p = base_params();
     p.x = X; p.x_dt = int(x_dt); p.M = M; p.K = d; p.ldx = d; p.t = t_x;
     p.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.ldw = 2L * f; p.N = f; p.gu_off = f;
@@ -497,14 +547,22 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
       p.h_bits = dbg->h_mask.bits; p.h_bits_ld = (f + 63) / 64;
       p.x_bits = dbg->x_mask.bits; p.x_bits_ld = (d + 63) / 64; p.x_idx = dbg->x_mask.idx; p.x_nnz = dbg->x_mask.nnz;
     }
-    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH), OUT_SWIGLU, true, nt};
+    if (dn_parts) { p.h = nullptr; p.h_bits = nullptr; }
+    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH),
+                  dn_parts ? OUT_PARTS : OUT_SWIGLU, true, nt};
     if (gu_range) p.cap = mp.cap1_range;
     if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
     // stage 2: down projection over the surviving h rows; each slice masks its
     // own range of h (or, opt-in, reads whole h-tile lists)
     p2.W = reinterpret_cast<const uint16_t*>(w->w_down); p2.ldw = d;
-    if (dense) {
+    if (dn_parts) {
+      c2.in = IN_PARTS;
+      p2.x = mw.g1.partials; p2.x_dt = AS_F32; p2.K = f; p2.ldx = 2L * f; p2.t = dense ? -INFINITY : t_h;
+      p2.x_parts = mp.p1.S; p2.x_up = f; p2.keep_all = dense ? 1 : 0;
+      p2.h = (dbg && dbg->h) ? dbg->h : nullptr; p2.ldh = f;
+      if (dbg && !dense) { p2.h_bits = dbg->h_mask.bits; p2.h_bits_ld = (f + 63) / 64; }
+    } else if (dense) {
       c2.in = IN_ALL;
       p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = -INFINITY;
     } else if (dn_tiles) {
@@ -533,7 +591,7 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   p2.N = d;
   p2.n_tiles = mp.p2.n_tiles; p2.S = mp.p2.S; p2.cap = mp.p2.cap;
   if (c2.in == IN_TILES) { p2.S = mp.s2_tiles; p2.cap = mp.cap2_tiles; }
-  if (c2.in == IN_RANGE) { p2.S = mp.s2_range; p2.cap = mp.cap2_range; }
+  if (c2.in == IN_RANGE || c2.in == IN_PARTS) { p2.S = mp.s2_range; p2.cap = mp.cap2_range; }
   p2.partials = mw.g2.partials; p2.counters = mw.g2.counters; p2.part_ld = d;
   p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;

@@ -19,8 +19,8 @@ size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
   // output tile afterwards
   size_t stage = 0;
   if (c.in == IN_TILES) stage = size_t(cap) * (1 + c.mt) * 4;
-  // IN_RANGE, several tokens: the slice's range of every token, fp32
-  if (c.in == IN_RANGE && c.mt > 1) stage = size_t(cap) * c.mt * 4;
+  // IN_RANGE, several tokens, and IN_PARTS: the slice's range of every token, fp32
+  if ((c.in == IN_RANGE && c.mt > 1) || c.in == IN_PARTS) stage = size_t(cap) * c.mt * 4;
   if (c.mt == 16) {
     const size_t rows = size_t(32) * (512 / tn);
     const size_t chunk = rows * (tn + 4) * 2, out = size_t(16) * tn * 4;

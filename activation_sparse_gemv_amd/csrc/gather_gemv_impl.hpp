@@ -434,6 +434,44 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
   return cnt;
 }
 
+// Compaction of a range [i0, i0 + L) whose values sit in LDS (stage: [MT][L]
+// fp32): each thread takes a contiguous chunk for the union mask over tokens
+// (|v| > t for any token, or every row with keep_all), a workgroup scan places the
+// chunks, and the kept rows' values are copied (a token's value is 0 where its own
+// |v| <= t).  Returns the number of kept rows; synchronises before returning.
+template <int MT>
+__device__ __forceinline__ int compact_stage(const float* stage, int L, int i0, float t, bool keep_all, int* s_idx,
+                                             float* s_val, int cap, int* s_scan) {
+  const int tid = threadIdx.x;
+  const int CE = (L + kThreads - 1) / kThreads;
+  const int c0 = min(tid * CE, L), n = max(0, min(CE, L - c0));
+  int c = 0;
+  for (int e = 0; e < n; ++e) {
+    bool a = keep_all;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
+    c += a;
+  }
+  int nnz;
+  int r = block_excl_scan<kThreads>(c, s_scan, &nnz);
+  for (int e = 0; e < n; ++e) {
+    bool a = keep_all;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
+    if (a) {
+      s_idx[r] = i0 + c0 + e;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float xv = stage[m * L + c0 + e];
+        s_val[m * cap + r] = (keep_all || fabsf(xv) > t) ? xv : 0.f;
+      }
+      ++r;
+    }
+  }
+  __syncthreads();
+  return nnz;
+}
+
 // Several tokens, one slice's own range [i0, i1): every token's values of the
 // range are staged in LDS (stage: [MT][len] fp32) with one round trip of
 // independent loads (16-byte vectors when NV > 0, i.e. aligned rows), then each
@@ -496,44 +534,84 @@ __device__ __forceinline__ int compact_range_staged(const GemvParams& p, int i0,
     }
   }
   __syncthreads();
-  const int CE = (L + kThreads - 1) / kThreads;
-  const int c0 = min(tid * CE, L), n = max(0, min(CE, L - c0));
-  int c = 0;
-  for (int e = 0; e < n; ++e) {
-    bool a = false;
+  return compact_stage<MT>(stage, L, i0, t, false, s_idx, s_val, cap, s_scan);
+}
+
+// The input of a down projection is h = silu(g) * u of a paired gate/up launch
+// that stored its split-K partials without summing them (OUT_PARTS).  Slice sl
+// owns the 64-aligned range [i0, i1) of h: for each token and each group of four
+// rows, the gate and up partials of every gate/up slice are loaded together (up
+// to 8 slices per round trip, 16-byte vectors) and summed in slice order starting
+// from 0, which is exactly the sum the gate/up launch's own combine would form;
+// h goes to the stage ([MT][L] fp32), then the range is masked and compacted.
+// With `exports`, h and its mask bits are also written out (one workgroup per
+// range does this).
+template <int MT>
+__device__ __forceinline__ int compact_parts(const GemvParams& p, int i0, int i1, int* s_idx, float* s_val, int cap,
+                                             float* stage, int* s_scan, bool exports) {
+  const int tid = threadIdx.x, M = p.M;
+  const float t = p.t;
+  const int L = max(0, i1 - i0);            // a multiple of 64 (K is)
+  const int nq = L / 4;                     // groups of four rows per token
+  const int tot = nq * MT;
+  const int S1 = p.x_parts;
+  const float* P = reinterpret_cast<const float*>(p.x);
+  // 32-bit offsets: the partials buffer holds fewer than 2^31 floats
+  const int tok_ld = (int)p.ldx, slice_ld = M * tok_ld, up = (int)p.x_up;
+  constexpr int kB = 8;
+  for (int j = tid; j < tot; j += kThreads) {
+    const int m = j / nq, q = j % nq;
+    const int off = (m < M ? m : M - 1) * tok_ld + i0 + 4 * q;
+    f32x4_t g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S1; s0 += kB) {
+      f32x4_t tg[kB], tu[kB];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
-    c += a;
-  }
-  int nnz;
-  int r = block_excl_scan<kThreads>(c, s_scan, &nnz);
-  for (int e = 0; e < n; ++e) {
-    bool a = false;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
-    if (a) {
-      s_idx[r] = i0 + c0 + e;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const float xv = stage[m * L + c0 + e];
-        s_val[m * cap + r] = fabsf(xv) > t ? xv : 0.f;
+      for (int k = 0; k < kB; ++k) {
+        const float* ps = P + min(s0 + k, S1 - 1) * slice_ld + off;
+        tg[k] = *reinterpret_cast<const f32x4_t*>(ps);
+        tu[k] = *reinterpret_cast<const f32x4_t*>(ps + up);
       }
-      ++r;
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        if (s0 + k < S1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g[e] += tg[k][e];
+            u[e] += tu[k][e];
+          }
+        }
     }
+    f32x4_t h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = m < M ? silu_f32(g[e]) * u[e] : 0.f;
+    *reinterpret_cast<f32x4_t*>(stage + m * L + 4 * q) = h;
   }
   __syncthreads();
-  return nnz;
+  if (exports) {
+    if (p.h != nullptr)
+      for (int j = tid; j < M * L; j += kThreads) p.h[(j / L) * p.ldh + i0 + j % L] = stage[j];
+    if (p.h_bits != nullptr) {
+      // one wave per 64-row word (words never straddle tokens: L is a multiple of 64)
+      const int lane = tid & 63;
+      for (int b = (tid >> 6) * 64; b < M * L; b += kThreads) {
+        const uint64_t bits = __ballot(fabsf(stage[b + lane]) > t);
+        if (lane == 0) p.h_bits[(b / L) * p.h_bits_ld + (i0 + b % L) / 64] = bits;
+      }
+    }
+  }
+  return compact_stage<MT>(stage, L, i0, t, p.keep_all != 0, s_idx, s_val, cap, s_scan);
 }
 
 // One work item: column tile `tile`, row slice `sl` of S (p.S) equal parts of the
-// compacted row list; its partial tile is slot `part` of `n_parts` combined by
-// the last item of the tile to finish.  IN_LISTS reads list tiles
+// compacted row list (IN_PARTS: the range [rr0, rr1) of h when rr1 >= 0); its
+// partial tile is slot `part` of `n_parts` combined by the last item of the tile to
+// finish.  IN_LISTS reads list tiles
 // [lt0, lt0 + n_lt); IN_TILES gives slice sl whole list tiles of [lt0, lt0 + n_lt).
 // Used by the GEMV kernel below (one item per workgroup) and by the one-launch
 // MLP kernel (a gate/up item, then a down item, per workgroup).
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
 __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n_parts, int lt0, int n_lt,
-                          unsigned char* smem) {
+                          unsigned char* smem, int rr0 = 0, int rr1 = -1) {
   using TS = TileShape<LPR>;
   constexpr int RPW = TS::RPW, NSLOT = TS::NSLOT, TN = TS::TN, TB = TN / 2;
   const int cap = p.cap;
@@ -576,11 +654,17 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo);
     if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
       thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
+  } else if constexpr (IN == IN_PARTS) {
+    // the range of h: explicit (one-launch MLP) or slice sl of S 64-aligned parts
+    const int units = (p.K + 63) / 64;
+    const int r0 = rr1 >= 0 ? rr0 : min(p.K, split_point(sl, units, S) * 64);
+    const int r1 = rr1 >= 0 ? rr1 : min(p.K, split_point(sl + 1, units, S) * 64);
+    cnt = compact_parts<MT>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan, tile == 0);
   } else if constexpr (IN == IN_LISTS) {
     int run = 0;
     for (int base = 0; base < n_lt; base += kThreads) {
       const int q = base + tid;
-      const int v = q < n_lt ? (p.coherent_lists ? load_coherent_i32(p.list_cnt + lt0 + q) : p.list_cnt[lt0 + q]) : 0;
+      const int v = q < n_lt ? p.list_cnt[lt0 + q] : 0;
       int tot;
       const int off = block_excl_scan<kThreads>(v, s_scan, &tot);
       if (q < n_lt) s_pref[q] = run + off;
@@ -600,15 +684,9 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       }
       const long e = (long)(lt0 + a) * p.lt_stride + (g - s_pref[a]);
       float xv[MT];
-      if (p.coherent_lists) {
-        s_idx[r] = load_coherent_i32(p.list_idx + e);
+      s_idx[r] = p.list_idx[e];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) xv[m] = load_coherent(p.list_val + e * M + (m < M ? m : M - 1));
-      } else {
-        s_idx[r] = p.list_idx[e];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) xv[m] = p.list_val[e * M + (m < M ? m : M - 1)];
-      }
+      for (int m = 0; m < MT; ++m) xv[m] = p.list_val[e * M + (m < M ? m : M - 1)];
 #pragma unroll
       for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? xv[m] : 0.f;
     }
@@ -624,13 +702,8 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     int* r_idx = reinterpret_cast<int*>(s_w);              // [tot_e] raw candidates
     float* r_val = reinterpret_cast<float*>(r_idx + tot_e);  // [tot_e][M]
     const long gbase = (long)(lt0 + t0) * stride;
-    if (p.coherent_lists) {
-      if (tid < nt) s_cnt[tid] = load_coherent_i32(p.list_cnt + lt0 + t0 + tid);
-      copy2_to_lds<true>(r_idx, p.list_idx + gbase, tot_e, r_val, p.list_val + gbase * M, tot_e * M);
-    } else {
-      if (tid < nt) s_cnt[tid] = p.list_cnt[lt0 + t0 + tid];
-      copy2_to_lds<false>(r_idx, p.list_idx + gbase, tot_e, r_val, p.list_val + gbase * M, tot_e * M);
-    }
+    if (tid < nt) s_cnt[tid] = p.list_cnt[lt0 + t0 + tid];
+    copy2_to_lds<false>(r_idx, p.list_idx + gbase, tot_e, r_val, p.list_val + gbase * M, tot_e * M);
     __syncthreads();
     if (tid == 0) {
       int run = 0;
@@ -756,6 +829,22 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     }
   };
 
+  // ------------------------------------------------------------ unsummed partials
+  if constexpr (OUT == OUT_PARTS) {
+    // the next launch sums the slices (its kernel boundary makes these stores visible)
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kThreads;
+      bool ok;
+      const long pc = col_of(c, ok);
+      if (c < TN && ok)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < M) store_coherent(p.partials + ((long)part * M + m) * p.part_ld + pc, res[m][q]);
+    }
+    return;
+  }
+
   // ------------------------------------------------------------ split-K combine
   if (n_parts > 1) {
     // Partials are written through to the device-coherent level (relaxed agent-scope
@@ -825,10 +914,12 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
           for (int k = 0; k < kBatch; ++k)
             if (s0 + k < n_parts && oks[q]) v[m][q] += tmp[m][q][k];
     }
+    // a producer wait of the one-launch MLP that timed out poisons the output
+    const float bad = (p.err_flag != nullptr && load_coherent_u32(p.err_flag) != 0u) ? __builtin_nanf("") : 0.f;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int q = 0; q < CPT; ++q) res[m][q] = m < M ? v[m][q] : 0.f;
+      for (int q = 0; q < CPT; ++q) res[m][q] = m < M ? v[m][q] + bad : 0.f;
   }
 
   // ------------------------------------------------------------ epilogues
@@ -847,7 +938,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
             store_elem(p.y, p.y_dt, m * p.ldy + gc, v);
           }
     }
-  } else {
+  } else if constexpr (OUT == OUT_SWIGLU) {
     static_assert(GU, "the SwiGLU epilogue needs paired gate/up columns");
     __syncthreads();
 #pragma unroll
@@ -890,12 +981,6 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
           if (m < M) store_coherent(p.o_val + e * M + m, fabsf(hv[m]) > p.t_h ? hv[m] : 0.f);
       }
       if (tid == 0) store_coherent_i32(p.o_cnt + tile, tot);
-      if (p.tile_done != nullptr) {
-        // publish: the tile's list is complete before its flag is raised
-        wait_vmem();
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(p.tile_done + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
     }
   }
 }
@@ -910,89 +995,161 @@ __global__ __launch_bounds__(kThreads, 2) void gather_gemv_kernel(const GemvPara
 }
 
 // ---------------------------------------------------------------- one-launch MLP
-// Both stages of the threshold-mode SwiGLU MLP in one launch.  Workgroup w runs
-// gate/up item w (column tile, row slice), then down item w (down column tile,
-// group of whole h-tiles), so the grid is exactly as large as the larger stage
-// and the host only takes this path when every workgroup of it is resident at
-// once.  A down item waits only for the h-tiles it reads: the last gate/up
-// workgroup of a tile publishes the tile's compacted h list with device-coherent
-// stores, waits for them, and then raises the tile's flag, and the down item
-// reads the lists device-coherently.  So the down projection of early tiles
-// overlaps the tail of the gate/up stage, and the second launch, its ramp-up and
-// the gap between launches disappear.  The wait is bounded anyway; a timeout
-// raises *err.  The last workgroup to finish clears the flags for the next call.
-template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
-__global__ __launch_bounds__(kThreads) void mlp_fused_kernel(const FusedMlpParams f) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int w = blockIdx.x, tid = threadIdx.x;
-  if (w < f.items1) {
-    const int tile = w % f.n_tiles1, sl = w / f.n_tiles1;
-    gemv_item<WDT, MT, LPR1, IN1, OUT_SWIGLU, true, true, NV>(f.p1, tile, sl, sl, f.S1, 0, 0, smem);
+// Both stages of the threshold-mode SwiGLU MLP in one launch, in two roles.  The
+// first g1 workgroups are gate/up items: each stores its split-K partial tile
+// unsummed and waits for the stores.  The gate/up tiles are grouped by XCD
+// (workgroup w runs on XCD w % 8 on this part), and each group's tiles are cut
+// into at most k2 h ranges of whole tiles; the item that completes the last slice
+// of a range appends the range to a ready list.  The other g2 workgroups are
+// down items: down workgroup n takes column tile n % n_ct2 of the (n / n_ct2)-th
+// range to become ready, waits for that list entry, then sums the range's
+// partials, applies SwiGLU and the h mask in its prologue (IN_PARTS) and streams
+// its rows; its partial goes to the range's slot, so the final combine is in
+// h-row order whatever the order ranges became ready in.  Down work thus starts
+// on whatever range is done first, on any XCD, while slower gate/up tiles are
+// still streaming, and the gap between two launches disappears.
+// Down items wait only on gate/up items, which never wait and come first in the
+// grid, and every XCD dispatches its workgroups in index order, so the waits end
+// whatever else occupies the device.  They are bounded anyway: a timeout raises
+// *err, which poisons the output with NaN.  The last workgroup to finish clears
+// the counters and the list for the next call.
+
+// Range q of group x (k2 ranges at most, never empty): tiles [*ta, *tb); returns
+// the global range index (ranges numbered in group order, i.e. h-row order).
+__device__ __forceinline__ int fused_range(const FusedMlpParams& f, int x, int q, int* ta, int* tb) {
+  int base = 0;
+  for (int y = 0; y < x; ++y) {
+    const int n = split_point(y + 1, f.n_tiles1, f.groups) - split_point(y, f.n_tiles1, f.groups);
+    base += n < f.k2 ? n : f.k2;
   }
-  for (int item = w; item < f.items2; item += gridDim.x) {
-    const int ct = item % f.n_ct2, sl = item / f.n_ct2;
-    const int t0 = split_point(sl, f.n_lt, f.S2), t1 = split_point(sl + 1, f.n_lt, f.S2);
-    if (tid < t1 - t0) {
-      unsigned spins = 0;
-      while (__hip_atomic_load(f.tile_done + t0 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > (1u << 26)) {
-          __hip_atomic_store(f.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+  const int t0 = split_point(x, f.n_tiles1, f.groups);
+  const int nt = split_point(x + 1, f.n_tiles1, f.groups) - t0;
+  const int nr = nt < f.k2 ? nt : f.k2;
+  *ta = t0 + split_point(q, nt, nr);
+  *tb = t0 + split_point(q + 1, nt, nr);
+  return base + q;
+}
+
+template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
+__global__ __launch_bounds__(kThreads, 2) void mlp_xcd_kernel(const FusedMlpParams f) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_range;
+  const int w = blockIdx.x, tid = threadIdx.x;
+  const int G = f.groups;
+  if (w < f.g1) {
+    const int x = w % G, i = w / G;
+    const int t0 = split_point(x, f.n_tiles1, G), nt = split_point(x + 1, f.n_tiles1, G) - t0;
+    if (i < nt * f.S1) {
+      const int lt = i % nt, sl = i / nt;
+      gemv_item<WDT, MT, LPR1, IN1, OUT_PARTS, true, true, NV>(f.p1, t0 + lt, sl, sl, f.S1, 0, 0, smem);
+      // publish: the partial tile is stored before the range's slice count rises
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0) {
+        const int nr = nt < f.k2 ? nt : f.k2;
+        int q = 0;
+        while (q + 1 < nr && split_point(q + 1, nt, nr) <= lt) ++q;
+        int ta, tb;
+        const int r = fused_range(f, x, q, &ta, &tb);
+        const unsigned need = (unsigned)((tb - ta) * f.S1);
+        const unsigned prev = __hip_atomic_fetch_add(f.range_cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + 1 == need) {
+          const unsigned pos = __hip_atomic_fetch_add(f.ready_tail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(f.ready + (long)pos * kCntStride, (unsigned)r + 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
-    __syncthreads();
-    gemv_item<WDT, MT, LPR2, IN_TILES, OUT_Y, false, true, 0>(f.p2, ct, sl, sl, f.S2, 0, f.n_lt, smem);
-    __syncthreads();
+  } else {
+    const int n = w - f.g1;
+    const int k = n / f.n_ct2, ct = n % f.n_ct2;
+    if (k < f.n_ranges) {
+      if (tid == 0) {
+        // one poller per workgroup, a few hundred cycles apart; list entries sit
+        // kCntStride apart so that polling does not load one memory channel
+        unsigned v, spins = 0;
+        while ((v = __hip_atomic_load(f.ready + (long)k * kCntStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+               0u) {
+          __builtin_amdgcn_s_sleep(8);
+          if (++spins > (1u << 24)) {
+            __hip_atomic_store(f.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v = (unsigned)k + 1u;
+            break;
+          }
+        }
+        s_range = (int)v - 1;
+      }
+      __syncthreads();
+      const int r = s_range;
+      // range r -> group and rows
+      int x = 0, base = 0;
+      for (;;) {
+        const int nt = split_point(x + 1, f.n_tiles1, G) - split_point(x, f.n_tiles1, G);
+        const int nr = nt < f.k2 ? nt : f.k2;
+        if (r < base + nr || x == G - 1) break;
+        base += nr;
+        ++x;
+      }
+      int ta, tb;
+      fused_range(f, x, r - base, &ta, &tb);
+      const int K = f.p2.K;
+      const int r0 = min(K, ta * f.tb1), r1 = min(K, tb * f.tb1);
+      gemv_item<WDT, MT, LPR2, IN_PARTS, OUT_Y, false, true, 0>(f.p2, ct, 0, r, f.n_ranges, 0, 0, smem, r0, r1);
+    }
   }
+  __syncthreads();
   if (tid == 0) {
     wait_vmem();
     const unsigned prev = __hip_atomic_fetch_add(f.exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == gridDim.x - 1) {
-      for (int q = 0; q < f.n_lt; ++q)
-        __hip_atomic_store(f.tile_done + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int q = 0; q < f.n_ranges; ++q) {
+        __hip_atomic_store(f.range_cnt + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(f.ready + (long)q * kCntStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(f.ready_tail, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f.err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(f.exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-// Launches the one-launch MLP if all of its workgroups fit on the device at once;
-// returns hipErrorCooperativeLaunchTooLarge (nothing launched) otherwise.
 template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
-hipError_t launch_fused_one(const FusedMlpParams& f, size_t smem, int cus, hipStream_t s) {
-  auto k = mlp_fused_kernel<WDT, MT, LPR1, LPR2, IN1, NV>;
+hipError_t launch_fused_one(const FusedMlpParams& f, size_t smem, hipStream_t s) {
+  auto k = mlp_xcd_kernel<WDT, MT, LPR1, LPR2, IN1, NV>;
   if (smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
   }
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), kThreads, smem) !=
-      hipSuccess)
-    return hipErrorCooperativeLaunchTooLarge;
-  const int grid = f.items1 > f.items2 ? f.items1 : f.items2;
-  if (grid < 1 || (long)occ * cus < grid) return hipErrorCooperativeLaunchTooLarge;
+  const int grid = f.g1 + f.g2;
+  if (grid < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), smem, s, f);
   return hipGetLastError();
 }
 
 template <int WDT, int MT, int LPR1, int LPR2>
 hipError_t fused_pick_in(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  if (c.in1 == IN_ALL) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_ALL, 0>(f, smem, c.cus, s);
-  if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 2>(f, smem, c.cus, s);
-  if constexpr (MT == 1) {
-    if (c.nv == 8) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 8>(f, smem, c.cus, s);
+  if (c.in1 == IN_ALL) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_ALL, 0>(f, smem, s);
+  if (c.in1 == IN_RANGE) {
+    if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_RANGE, 2>(f, smem, s);
+    return launch_fused_one<WDT, MT, LPR1, LPR2, IN_RANGE, 0>(f, smem, s);
   }
-  return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 0>(f, smem, c.cus, s);
+  if (c.in1 != IN_THRESH) return hipErrorInvalidValue;
+  if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 2>(f, smem, s);
+  if constexpr (MT == 1) {
+    if (c.nv == 8) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 8>(f, smem, s);
+  }
+  return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 0>(f, smem, s);
 }
 
 template <int WDT, int MT>
 hipError_t fused_pick(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  if (c.lpr1 == 64 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 64, 16>(c, f, smem, s);
-  if (c.lpr1 == 64 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 64, 32>(c, f, smem, s);
-  if (c.lpr1 == 32 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 32, 16>(c, f, smem, s);
-  if (c.lpr1 == 32 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 32, 32>(c, f, smem, s);
+  if constexpr (MT <= 8) {
+    if (c.lpr1 == 64 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 64, 16>(c, f, smem, s);
+    if (c.lpr1 == 64 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 64, 32>(c, f, smem, s);
+    if (c.lpr1 == 32 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 32, 16>(c, f, smem, s);
+    if (c.lpr1 == 32 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 32, 32>(c, f, smem, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -1030,11 +1187,17 @@ hipError_t pick_nt(const GemvConfig& c, const GemvParams& p, size_t smem, hipStr
 template <int WDT, int MT, int LPR>
 hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
   if (c.gu) {
+    if (c.out == OUT_PARTS) {
+      if constexpr (MT <= 8) {
+        if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_PARTS, true>(c, p, smem, s);
+        if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_PARTS, true>(c, p, smem, s);
+        if (c.in == IN_ALL) return pick_nt<WDT, MT, LPR, IN_ALL, OUT_PARTS, true>(c, p, smem, s);
+      }
+      return hipErrorInvalidValue;
+    }
     if (c.out != OUT_SWIGLU) return hipErrorInvalidValue;
     if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_SWIGLU, true>(c, p, smem, s);
-    if constexpr (MT > 1) {
-      if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_SWIGLU, true>(c, p, smem, s);
-    }
+    if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_SWIGLU, true>(c, p, smem, s);
     if (c.in == IN_ALL) return pick_nt<WDT, MT, LPR, IN_ALL, OUT_SWIGLU, true>(c, p, smem, s);
     return hipErrorInvalidValue;
   }
@@ -1043,6 +1206,10 @@ hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipS
   if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_LISTS) return pick_nt<WDT, MT, LPR, IN_LISTS, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_TILES) return pick_nt<WDT, MT, LPR, IN_TILES, OUT_Y, false>(c, p, smem, s);
+  if (c.in == IN_PARTS) {
+    if constexpr (MT <= 8) return pick_nt<WDT, MT, LPR, IN_PARTS, OUT_Y, false>(c, p, smem, s);
+    return hipErrorInvalidValue;
+  }
   return pick_nt<WDT, MT, LPR, IN_ALL, OUT_Y, false>(c, p, smem, s);
 }
 

@@ -113,6 +113,34 @@ def test_mlp_dense_baseline_matches_dense_oracle():
     assert rel_err(y0, ref) < TOL
 
 
+@pytest.mark.parametrize("cfg,M", [(1, 1), (2, 1), (1, 4)])
+def test_mlp_unsummed_partials_equal_summed(cfg, M, monkeypatch):
+    """The down stage that sums the gate/up split-K partials of its own h range in its
+    prologue forms the same h (same slice order, same SwiGLU) and so the same y, bit for
+    bit, as the gate/up launch's own combine followed by the range-masked down stage; the
+    one-launch MLP forms the same h and h mask too."""
+    announce(f"mlp unsummed partials cfg={cfg} M={M}")
+    shape = datagen.CFG1 if cfg == 1 else datagen.CFG2
+    w = _mlp(cfg, shape)
+    gen = datagen.laplace if cfg == 1 else datagen.student_t
+    kw = dict(dtype="f16") if cfg == 1 else {}
+    calib = gen((64, shape.d_model), datagen.seed_for(cfg, 0, "calib"), **kw)
+    x = gen((M, shape.d_model), datagen.seed_for(cfg, 5, "decode"), **kw).to(DEV)
+    t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], 0.5, 0.5)
+    out = {}
+    for mode in (0, 1, 2):
+        monkeypatch.setenv("AS_DN_PARTS", str(min(mode, 1)))
+        monkeypatch.setenv("AS_FUSED", "1" if mode == 2 else "0")
+        y, dbg = asg.as_sparse_swiglu_mlp(x, w["dev"], float(t_x), float(t_h), debug=True)
+        out[mode] = (y, dbg["h"].clone(), dbg["h_mask"]["bits"].clone())
+    for mode in (1, 2):
+        assert torch.equal(out[0][1], out[mode][1])
+        assert torch.equal(out[0][2], out[mode][2])
+    assert torch.equal(out[0][0], out[1][0])
+    # the one-launch MLP splits the down rows differently: same rows, other sum order
+    assert rel_err(out[2][0], f64(out[0][0])) < 1e-5
+
+
 def test_mlp_determinism_and_edges():
     announce("mlp determinism")
     shape = datagen.CFG1
@@ -170,7 +198,9 @@ def test_neuron_set_full_equals_dense():
 _PLANS = [dict(AS_GU_LPR=16, AS_GU_S=1), dict(AS_GU_LPR=16, AS_GU_S=2, AS_DN_TPW=1),
           dict(AS_GU_LPR=32, AS_GU_S=3, AS_DN_LPR=32, AS_DN_TPW=2), dict(AS_DN_LPR=64, AS_DN_TPW=1),
           dict(AS_GU_LPR=64, AS_GU_S=5, AS_DN_LPR=16, AS_DN_TPW=3), dict(AS_DN_TILES=1),
-          dict(AS_FUSED=1), dict(AS_FUSED=1, AS_DN_TPW=2, AS_DN_LPR=32), dict(AS_DN_S=13)]
+          dict(AS_FUSED=1), dict(AS_FUSED=1, AS_DN_TPW=2, AS_DN_LPR=32), dict(AS_DN_S=13),
+          dict(AS_DN_PARTS=0), dict(AS_DN_PARTS=1, AS_GU_S=11), dict(AS_DN_PARTS=1, AS_GU_S=1, AS_DN_LPR=32),
+          dict(AS_FUSED=1, AS_FX_K2=1), dict(AS_FUSED=1, AS_FX_K2=3, AS_GU_S=5), dict(AS_FUSED=1, AS_GU_S=11)]
 
 
 @pytest.mark.parametrize("plan", range(len(_PLANS)))
