@@ -59,7 +59,8 @@ SIGNATURES = {
     "as_status_string": (c_char_p, [c_int]),
     "as_last_error": (c_char_p, []),
     "as_workspace_init": (c_int, [c_void_p, c_size_t, c_void_p]),
-    "as_calibrate_threshold": (c_int, [c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p]),
+    "as_calibrate_threshold_ws_size": (c_size_t, [c_int64]),
+    "as_calibrate_threshold": (c_int, [c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
     "as_threshold_gemv_ws_size": (c_size_t, [c_int, c_int, c_int]),
     "as_threshold_gemv": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_float,
                                   c_void_p, c_int, c_uint, POINTER(ASMaskOut), c_void_p, c_size_t, c_void_p]),

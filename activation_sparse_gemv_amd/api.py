@@ -80,8 +80,11 @@ def as_calibrate_threshold(pool: torch.Tensor, p: float | None = None, rank: int
     if rank is None:
         rank = nearest_rank(p, n)
     out = torch.empty(1, dtype=torch.float32, device=pool.device)
-    L.check(L.load().as_calibrate_threshold(_ptr(pool), _dt(pool), n, rank, _ptr(out), _stream(pool.device)),
-            "as_calibrate_threshold")
+    lib = L.load()
+    nb = lib.as_calibrate_threshold_ws_size(n)
+    ws = workspace(("calibrate",), nb, pool.device)
+    L.check(lib.as_calibrate_threshold(_ptr(pool), _dt(pool), n, rank, _ptr(out), _ptr(ws), nb,
+                                       _stream(pool.device)), "as_calibrate_threshold")
     return out
 
 

@@ -302,13 +302,18 @@ as_status as_bench_flush(void* buf, size_t bytes, hipStream_t stream) {
   return hip_check(launch_fill_pattern(buf, bytes, 0x9e3779b9u * salt++, stream), "as_bench_flush");
 }
 
-as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64_t rank, float* t_out,
-                                 hipStream_t stream) {
+size_t as_calibrate_threshold_ws_size(int64_t n) { return n < 1 ? 0 : up256(calibrate_ws_bytes()); }
+
+as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64_t rank, float* t_out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
   if (!pool || !t_out) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: NULL pointer");
   if (!is_dt(dt)) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: bad dtype %d", int(dt));
   if (n < 1 || n > 2147483647LL || rank < 0 || rank > n)
     return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: n=%lld rank=%lld", (long long)n, (long long)rank);
-  return hip_check(launch_calibrate(pool, int(dt), n, rank, t_out, stream), "as_calibrate_threshold");
+  as_status st = check_ws(ws, ws_bytes, calibrate_ws_bytes());
+  if (st != AS_OK) return st;
+  return hip_check(launch_calibrate(pool, int(dt), n, rank, t_out, reinterpret_cast<unsigned*>(ws), stream),
+                   "as_calibrate_threshold");
 }
 
 // ------------------------------------------------------------------ GEMV

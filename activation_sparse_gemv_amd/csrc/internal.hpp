@@ -132,6 +132,8 @@ hipError_t launch_local_signal(const uint16_t* X, int P, int d, const uint16_t* 
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);
-hipError_t launch_calibrate(const void* pool, int dt, int64_t n, int64_t rank, float* t_out, hipStream_t s);
+size_t calibrate_ws_bytes();
+hipError_t launch_calibrate(const void* pool, int dt, int64_t n, int64_t rank, float* t_out, unsigned* ghist,
+                            hipStream_t s);
 
 }  // namespace as

@@ -39,49 +39,126 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) { return launc
 // TEAL slides, method slide: t_p is decided from calibration data for the target
 // sparsity.  Nearest-rank order statistic of |pool| by an MSB-first radix select
 // over the fp32 bit pattern of |v| (for non-negative floats the bit pattern
-// orders like the value; NaN patterns order above +inf).  One workgroup of 1024
-// threads, four 8-bit passes with an LDS histogram: an offline step, not timed.
-constexpr int kCalThreads = 1024;
+// orders like the value; NaN patterns order above +inf): four 8-bit passes, each
+// one launch over the whole pool.  A pass keeps the keys whose higher bytes equal
+// the prefix chosen so far, counts their next byte in per-wave LDS histograms and
+// adds them to the pass's global histogram; every workgroup of the next pass
+// re-derives the prefix and the remaining rank from the earlier histograms (the
+// same walk in every workgroup).  A last one-workgroup launch writes t and clears
+// the histograms for the next call.
+constexpr int kCalThreads = 256;
+constexpr int kCalVec = 4;   // 16-byte vectors per thread and step
 
-__device__ __forceinline__ uint32_t abs_key(const void* pool, int dt, int64_t i) {
-  return __float_as_uint(load_elem(pool, dt, i)) & 0x7fffffffu;
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+// Prefix (bytes of passes 0 .. npass-1) and the rank left inside it, from the
+// global histograms; run by one wave, results through shared memory.
+__device__ __forceinline__ void cal_walk(const unsigned* ghist, int npass, int64_t rank, unsigned* sh,
+                                         uint32_t* prefix_out, int* krem_out) {
+  // sh: [npass * 256] staging of the histograms + 2 ints
+  int* s_bin = reinterpret_cast<int*>(sh + npass * 256);
+  for (int i = threadIdx.x; i < npass * 256; i += kCalThreads) sh[i] = ghist[i];
+  __syncthreads();   // callers run this with every thread of the workgroup
+  uint32_t prefix = 0u;
+  int krem = (int)rank;
+  for (int q = 0; q < npass; ++q) {
+    if (threadIdx.x < 64) wave_select_bin(sh + q * 256, krem, false, &s_bin[0], &s_bin[1]);
+    __syncthreads();
+    prefix |= (uint32_t)s_bin[0] << (24 - 8 * q);
+    krem = s_bin[1];
+    __syncthreads();
+  }
+  *prefix_out = prefix;
+  *krem_out = krem;
 }
 
-__global__ __launch_bounds__(kCalThreads) void calibrate_kernel(const void* pool, int dt, int64_t n,
-                                                                int64_t rank, float* t_out) {
-  __shared__ unsigned hist[256];
-  __shared__ uint32_t s_prefix;
-  __shared__ int64_t s_krem;
-  __shared__ int s_bin, s_binrem;
+template <int PASS>
+__global__ __launch_bounds__(kCalThreads) void calibrate_hist_kernel(const void* pool, int dt, int64_t n, int64_t rank,
+                                                                     int vec, unsigned* ghist) {
+  __shared__ unsigned hist[4][256];
+  __shared__ unsigned stage[3 * 256 + 2];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t prefix = 0u;
+  if constexpr (PASS > 0) {
+    int krem;
+    cal_walk(ghist, PASS, rank, stage, &prefix, &krem);
+  }
+  const uint32_t hi_mask = PASS == 0 ? 0u : (0xffffffffu << (32 - 8 * PASS));
+  constexpr int shift = 24 - 8 * PASS;
+  for (int b = tid; b < 4 * 256; b += kCalThreads) (&hist[0][0])[b] = 0u;
+  __syncthreads();
+  unsigned* wh = hist[wave];
+  auto add = [&](float v) {
+    const uint32_t k = abs_bits(v);
+    if ((k & hi_mask) == prefix) atomicAdd(&wh[(k >> shift) & 0xffu], 1u);
+  };
+  // 16-byte vectors (8 half-width or 4 fp32 values) when the pool is aligned
+  const int per = dt == DT_F32 ? 4 : 8;
+  const int64_t nvec = vec ? n / per : 0;
+  const int64_t stride = (int64_t)gridDim.x * kCalThreads * kCalVec;
+  for (int64_t v0 = (int64_t)blockIdx.x * kCalThreads * kCalVec + tid; v0 < nvec; v0 += stride) {
+    u32x4 raw[kCalVec];
+#pragma unroll
+    for (int u = 0; u < kCalVec; ++u) {
+      const int64_t vi = v0 + (int64_t)u * kCalThreads;
+      raw[u] = vi < nvec ? reinterpret_cast<const u32x4*>(pool)[vi] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kCalVec; ++u) {
+      if (v0 + (int64_t)u * kCalThreads >= nvec) continue;
+      const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      if (dt == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) add(__uint_as_float(w4[e]));
+      } else {
+        const bool bf = dt == DT_BF16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hb = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
+          add(bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb));
+        }
+      }
+    }
+  }
+  // elements past the last whole vector (or all of them for an unaligned pool)
+  for (int64_t i = nvec * per + (int64_t)blockIdx.x * kCalThreads + tid; i < n; i += (int64_t)gridDim.x * kCalThreads)
+    add(load_elem(pool, dt, i));
+  __syncthreads();
+  const unsigned c = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
+  if (c) atomicAdd(ghist + PASS * 256 + tid, c);
+}
+
+__global__ __launch_bounds__(kCalThreads) void calibrate_final_kernel(int64_t rank, unsigned* ghist, float* t_out) {
+  __shared__ unsigned stage[4 * 256 + 2];
+  uint32_t prefix;
+  int krem;
   if (rank == 0) {
     if (threadIdx.x == 0) *t_out = -INFINITY;
     return;
   }
-  if (threadIdx.x == 0) { s_prefix = 0u; s_krem = rank; }
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
-    for (int b = threadIdx.x; b < 256; b += kCalThreads) hist[b] = 0u;
-    __syncthreads();
-    const uint32_t prefix = s_prefix;
-    for (int64_t i = threadIdx.x; i < n; i += kCalThreads) {
-      const uint32_t k = abs_key(pool, dt, i);
-      if ((k & hi_mask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) wave_select_bin(hist, (int)s_krem, false, &s_bin, &s_binrem);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      s_prefix = prefix | ((uint32_t)s_bin << shift);
-      s_krem = s_binrem;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *t_out = __uint_as_float(s_prefix);
+  cal_walk(ghist, 4, rank, stage, &prefix, &krem);
+  if (threadIdx.x == 0) *t_out = __uint_as_float(prefix);
+  for (int i = threadIdx.x; i < 4 * 256; i += kCalThreads) ghist[i] = 0u;
 }
 
-hipError_t launch_calibrate(const void* pool, int dt, int64_t n, int64_t rank, float* t_out, hipStream_t s) {
-  hipLaunchKernelGGL(calibrate_kernel, dim3(1), dim3(kCalThreads), 0, s, pool, dt, n, rank, t_out);
+size_t calibrate_ws_bytes() { return 4 * 256 * sizeof(unsigned); }
+
+hipError_t launch_calibrate(const void* pool, int dt, int64_t n, int64_t rank, float* t_out, unsigned* ghist,
+                            hipStream_t s) {
+  if (rank > 0) {
+    const int es = dt == DT_F32 ? 4 : 2;
+    const int vec = (reinterpret_cast<uintptr_t>(pool) & 15u) == 0 ? 1 : 0;
+    const int64_t per_wg = (int64_t)kCalThreads * kCalVec * (16 / es);
+    int64_t blocks = (n + per_wg - 1) / per_wg;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks < 1) blocks = 1;
+    const dim3 g((unsigned)blocks), b(kCalThreads);
+    hipLaunchKernelGGL(calibrate_hist_kernel<0>, g, b, 0, s, pool, dt, n, rank, vec, ghist);
+    hipLaunchKernelGGL(calibrate_hist_kernel<1>, g, b, 0, s, pool, dt, n, rank, vec, ghist);
+    hipLaunchKernelGGL(calibrate_hist_kernel<2>, g, b, 0, s, pool, dt, n, rank, vec, ghist);
+    hipLaunchKernelGGL(calibrate_hist_kernel<3>, g, b, 0, s, pool, dt, n, rank, vec, ghist);
+  }
+  hipLaunchKernelGGL(calibrate_final_kernel, dim3(1), dim3(kCalThreads), 0, s, rank, ghist, t_out);
   return hipGetLastError();
 }
 

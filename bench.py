@@ -288,9 +288,11 @@ def row_calibrate(C, cpu):
     pool = datagen.student_t((256, 14336), 7001).to(C.dev)
     fns = [lambda: asg.as_calibrate_threshold(pool, 0.5) for _ in range(4)]
     us = C.graph_us(fns, reps=5)
-    r = {"step": "a1 threshold calibration (nearest-rank order statistic, one workgroup radix select)",
-         "shape": "pool 256 x 14336 bf16", "us": r4(us), "pool_mb": pool.numel() * 2 / 1e6,
-         "note": "offline, once per model; a single workgroup (latency, not bandwidth bound)"}
+    mb = pool.numel() * 2 / 1e6
+    r = {"step": "a1 threshold calibration (nearest-rank order statistic, grid-wide 4-pass radix select)",
+         "shape": "pool 256 x 14336 bf16", "us": r4(us), "pool_mb": mb,
+         "gbs_4_passes": r4(4 * mb * 1e6 / (us * 1e-6) / 1e9),
+         "note": "offline, once per model; four histogram launches over the pool and one select launch"}
     if cpu:
         from oracle import teal
         P = pool.cpu().to(torch.float64).numpy()

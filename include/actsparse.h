@@ -102,10 +102,14 @@ as_status as_workspace_init(void *ws, size_t bytes, hipStream_t stream);
  *   rank = 0 gives -INFINITY (sparsity 0 keeps every input).
  * The caller computes rank = ceil(p * n).  NaN magnitudes order above +inf.
  * pool: [n] of dtype dt (f16/bf16/f32).  t_out: one device float.
+ * ws: caller-owned device workspace of as_calibrate_threshold_ws_size(n) bytes
+ * (zero-filled once; every call leaves it zeroed); calls sharing a workspace
+ * must be ordered on one stream.
  * Errors: INVALID_ARG if pool/t_out is NULL, n < 1 or n >= 2^31, rank < 0 or
- * rank > n. */
+ * rank > n; WORKSPACE if ws is NULL or too small. */
+size_t as_calibrate_threshold_ws_size(int64_t n);
 as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64_t rank,
-                                 float *t_out, hipStream_t stream);
+                                 float *t_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ threshold GEMV
  * TEAL slides, slide 11: mask generation fused with the sparse product,

@@ -96,9 +96,13 @@ def test_mlp_validation(lib):
 
 
 def test_calibrate_validation(lib):
-    assert lib.as_calibrate_threshold(None, L.AS_F32, 10, 5, _p(), None) == L.AS_ERR_INVALID_ARG
-    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 11, _p(), None) == L.AS_ERR_INVALID_ARG
-    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 0, 0, _p(), None) == L.AS_ERR_INVALID_ARG
+    nb = lib.as_calibrate_threshold_ws_size(10)
+    assert nb > 0
+    assert lib.as_calibrate_threshold(None, L.AS_F32, 10, 5, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 11, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 0, 0, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 5, _p(), None, nb, None) == L.AS_ERR_WORKSPACE
+    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 5, _p(), _p(), nb - 1, None) == L.AS_ERR_WORKSPACE
 
 
 def test_topk_moe_block_validation(lib):

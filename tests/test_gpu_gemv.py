@@ -225,3 +225,22 @@ def test_calibration_bit_exact(p):
     for q in (0.1, 0.3, 0.5, 0.7, 0.85):
         got = asg.as_calibrate_threshold(_dev(pool), q).cpu().numpy()[0]
         assert got == teal.calibrate_threshold(f64(pool), q)
+
+
+@pytest.mark.parametrize("n,dtype,offset", [(1000, "f16", 0), (1003, "f32", 1), (4099, "bf16", 3),
+                                            (256 * 14336, "bf16", 0), (20_000_000, "bf16", 0),
+                                            (3_000_001, "f32", 0), (777_777, "f16", 5)])
+def test_calibration_sizes_and_layouts(n, dtype, offset):
+    """The grid-wide radix select over pools of many workgroups (and more than the
+    grid covers in one sweep), vector tails and unaligned pools (element offsets, so
+    the element-wise path), against the sorted-pool oracle."""
+    announce(f"calibrate n={n} {dtype} offset={offset}")
+    buf = datagen.student_t((n + offset,), 950 + n % 97, dtype=dtype)
+    pool_dev = _dev(buf)[offset:]
+    ref_pool = f64(buf[offset:])
+    for p in (0.05, 0.5, 0.97):
+        got = asg.as_calibrate_threshold(pool_dev, p).cpu().numpy()[0]
+        assert got == teal.calibrate_threshold(ref_pool, p), (n, dtype, offset, p)
+    # the first and the last order statistic
+    assert asg.as_calibrate_threshold(pool_dev, rank=1).cpu().numpy()[0] == np.float32(np.abs(ref_pool).min())
+    assert asg.as_calibrate_threshold(pool_dev, rank=n).cpu().numpy()[0] == np.float32(np.abs(ref_pool).max())
