@@ -73,9 +73,135 @@ __global__ __launch_bounds__(kLsThreads) void local_signal_kernel(const uint16_t
   if (g == 0 && jvalid) local[j] = ((asum + s1) + (s2 + s3)) / (float)P;
 }
 
+// Streaming variant for d_model % 128 == 0 (the usual case).  At 128 tokens a
+// weight byte carries 128 flops, below the matrix cores' ridge, so the kernel is
+// bound by the weight stream and is written to keep it full: the reduction runs
+// in stages of 128 columns; each lane holds its gate and up fragments of three
+// stages in registers (two stages of loads stay in flight while one is
+// multiplied: 64 KB per workgroup), and the prompt tile of the next stage is
+// loaded into registers during the current one and written to the other half of
+// a double-buffered LDS tile.  The MFMA sequence of every accumulator (k-steps of
+// 32 in ascending order) is the same as in the kernel above, so both give the
+// same bits.
+constexpr int kLsKS = 128;                 // reduction columns per stage
+constexpr int kLsLdS = kLsKS + 8;          // LDS row stride (elements) of a stage tile
+constexpr int kLsTileElems = kLsTokBlock * kLsLdS;
+
+__global__ __launch_bounds__(kLsThreads, 1) void local_signal_stream_kernel(const uint16_t* X, int P, int d,
+                                                                            const uint16_t* W, long ld_neuron,
+                                                                            long up_off, int d_ff, float* local) {
+  extern __shared__ __align__(16) uint16_t xs[];       // [2][kLsTokBlock][kLsLdS]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int j = (blockIdx.x * 4 + wave) * 16 + li;
+  const bool jvalid = j < d_ff;
+  const uint16_t* wg = W + (long)(jvalid ? j : 0) * ld_neuron + 8 * g;
+  const uint16_t* wu = wg + up_off;
+  const int NS = d / kLsKS;
+  float asum = 0.f;
+  for (int t0 = 0; t0 < P; t0 += kLsTokBlock) {
+    g_f32x4 accg[8], accu[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) { accg[m] = g_f32x4{0.f, 0.f, 0.f, 0.f}; accu[m] = accg[m]; }
+    // stage st of the weights: 4 k-steps of gate and up (16 bytes each) for this lane
+    auto load_w = [&](int st, u32x4 (&b)[8]) {
+      const int k0 = (st < NS ? st : NS - 1) * kLsKS;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        b[q] = load_w16<true>(wg + k0 + 32 * q);
+        b[4 + q] = load_w16<true>(wu + k0 + 32 * q);
+      }
+    };
+    // stage st of the prompt tile: 128 tokens x 128 columns, 8 vectors per thread
+    // (tokens past P repeat the last one; their sums are not used)
+    auto load_x = [&](int st, u32x4 (&r)[8]) {
+      const int k0 = (st < NS ? st : NS - 1) * kLsKS;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int v = tid + q * kLsThreads;
+        const int t = v >> 4, c = (v & 15) * 8;
+        const int tt = t0 + t < P ? t0 + t : P - 1;
+        r[q] = *reinterpret_cast<const u32x4*>(X + (long)tt * d + k0 + c);
+      }
+    };
+    auto store_x = [&](int buf, const u32x4 (&r)[8]) {
+      uint16_t* dst = xs + buf * kLsTileElems;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int v = tid + q * kLsThreads;
+        const int t = v >> 4, c = (v & 15) * 8;
+        *reinterpret_cast<u32x4*>(dst + t * kLsLdS + c) = r[q];
+      }
+    };
+    auto compute = [&](int buf, const u32x4 (&b)[8]) {
+      const uint16_t* src = xs + buf * kLsTileElems;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const g_bf16x8 fg = __builtin_bit_cast(g_bf16x8, b[q]);
+        const g_bf16x8 fu = __builtin_bit_cast(g_bf16x8, b[4 + q]);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(src + (m * 16 + li) * kLsLdS + 32 * q + 8 * g);
+          const g_bf16x8 fa = __builtin_bit_cast(g_bf16x8, a);
+          accg[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fg, accg[m], 0, 0, 0);
+          accu[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fu, accu[m], 0, 0, 0);
+        }
+      }
+    };
+    u32x4 w0[8], w1[8], w2[8], xr[8];
+    __syncthreads();                       // the previous token block is done with both tiles
+    // loads outstanding at the loop head in the loop's own order: W(0), X(1), W(1)
+    load_x(0, xr);
+    load_w(0, w0);
+    store_x(0, xr);
+    load_x(1, xr);
+    load_w(1, w1);
+    __syncthreads();
+    // Stage st: hand the prompt tile of stage st + 1 (loaded during the previous
+    // stage) to LDS, fetch the tile of stage st + 2 and then the weights of stage
+    // st + 2 (unconditionally; past the end they reload the last stage), and
+    // multiply stage st.  Loads complete in issue order, so waiting for a tile
+    // never waits for the weights issued after it: two weight stages stay in
+    // flight while one is multiplied.
+    auto step = [&](int st, const u32x4 (&cur)[8], u32x4 (&refill)[8]) {
+      store_x((st + 1) & 1, xr);
+      load_x(st + 2, xr);
+      load_w(st + 2, refill);
+      compute(st & 1, cur);
+      __syncthreads();
+    };
+    int st = 0;
+    for (; st + 3 <= NS; st += 3) {
+      step(st, w0, w2);
+      step(st + 1, w1, w0);
+      step(st + 2, w2, w1);
+    }
+    if (st < NS) step(st, w0, w2);
+    if (st + 1 < NS) step(st + 1, w1, w0);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + m * 16 + 4 * g + e;
+        if (t < P) asum += fabsf(silu_f32(accg[m][e]) * accu[m][e]);
+      }
+  }
+  const float s1 = __shfl(asum, li + 16, 64), s2 = __shfl(asum, li + 32, 64), s3 = __shfl(asum, li + 48, 64);
+  if (g == 0 && jvalid) local[j] = ((asum + s1) + (s2 + s3)) / (float)P;
+}
+
 hipError_t launch_local_signal(const uint16_t* X, int P, int d, const uint16_t* W, long ld_neuron, long up_off,
                                int d_ff, float* local, hipStream_t s) {
   const int blocks = (d_ff + 63) / 64;
+  if (d % kLsKS == 0) {
+    const size_t smem = size_t(2) * kLsTileElems * sizeof(uint16_t);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(local_signal_stream_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(local_signal_stream_kernel, dim3(blocks), dim3(kLsThreads), smem, s, X, P, d, W, ld_neuron,
+                       up_off, d_ff, local);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(local_signal_kernel, dim3(blocks), dim3(kLsThreads), 0, s, X, P, d, W, ld_neuron, up_off, d_ff,
                      local);
   return hipGetLastError();

@@ -375,11 +375,18 @@ def row_glass(C, cpu):
     us, usd = C.graph_us(fs), C.graph_us(fd)
     ab = k * 3 * d * 2
     flops = 2 * c["prompt"] * d * 2 * f
+    lw = 2 * f * d * 2
     r = {"step": "a7 GLASS static neuron set: local signal (MFMA prefill) + rank-blend top-k + neuron-set SwiGLU",
          "shape": "d_model 4096, d_ff 14336, keep 7168, bf16, batch 1",
          "decode_us": r4(us), "dense_us": r4(usd), "speedup": r4(usd / us), "active_mb": r4(ab / 1e6),
          "gbs": r4(ab / (us * 1e-6) / 1e9), "frac_hbm": r4(ab / (us * 1e-6) / 8e12),
          "local_signal_us_128_tokens": r4(u_loc),
+         # 128 tokens: 128 flops per weight byte, below the bf16 ridge (~312), so the
+         # weight stream (gate + up rows of every neuron) bounds it
+         "local_signal_bound": "hbm",
+         "local_signal_weight_mb": r4(lw / 1e6),
+         "local_signal_gbs": r4(lw / (u_loc * 1e-6) / 1e9),
+         "local_signal_frac_hbm": r4(lw / (u_loc * 1e-6) / 8e12),
          "local_signal_tflops": r4(flops / (u_loc * 1e-6) / 1e12),
          "local_signal_frac_mfma_bf16": r4(flops / (u_loc * 1e-6) / 1e12 / PEAK_BF16_TFLOPS)}
     if cpu:

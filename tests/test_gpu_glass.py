@@ -14,8 +14,12 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("P,d,f", [(5, 64, 128), (130, 256, 448), (128, 512, 2048)])
+@pytest.mark.parametrize("P,d,f", [(5, 64, 128), (130, 256, 448), (128, 512, 2048), (1, 128, 64), (17, 384, 192),
+                                   (129, 640, 320), (40, 96, 80)])
 def test_local_signal_small(P, d, f):
+    """Small prompts through both local-signal kernels (d_model a multiple of 128: the
+    staged stream, with 1, 2, 3 and 5 stages; otherwise the single-step one), ragged
+    token blocks and neuron tiles."""
     announce(f"local signal P={P} d={d} f={f}")
     W = datagen.mlp_weights_neuron_major(4, P, d, f)
     X = datagen.student_t((P, d), 40 + P)
