@@ -606,7 +606,7 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
 // ------------------------------------------------------------------ top-k
 size_t as_topk_mask_ws_size(int rows, int n, as_topk_mode mode) {
   if (mode != AS_TOPK_RANK_BLEND || rows < 1 || n < 1) return 0;
-  return up256(size_t(rows) * 2 * n * sizeof(unsigned));
+  return up256(topk_blend_ws_bytes(rows, n));
 }
 
 as_status as_topk_mask(const float* score, const float* prior, int rows, int n, int k, as_topk_mode mode,

@@ -96,6 +96,7 @@ hipError_t launch_neuron_gu(int wdt, int mt, bool nt, const NeuronGuParams& p, h
 
 // Top-k masks.
 hipError_t launch_topk_value(const float* score, int rows, int n, int k, uint64_t* mask, int* idx, hipStream_t s);
+size_t topk_blend_ws_bytes(int rows, int n);
 hipError_t launch_topk_blend(const float* score, const float* prior, int rows, int n, int k, uint32_t lq,
                              uint64_t* mask, int* idx, unsigned* cnt, hipStream_t s);
 

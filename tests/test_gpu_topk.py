@@ -91,3 +91,19 @@ def test_blend_multi_row_and_ties():
     prior = rng.integers(0, 5, size=(4, 300)).astype(np.float32)
     for k in (0, 1, 150, 299, 300):
         _check_rows(local, k, prior, 0.5)
+
+
+@pytest.mark.parametrize("n", [16384, 20000, 40000])
+def test_blend_large_n(n):
+    """Rank blend past the GLASS size, up to scores staged outside LDS (n > 32768),
+    with ties, -0.0 / +0.0 and NaN, two rows, several k, called repeatedly (the rank
+    counts are cleared by each call for the next)."""
+    announce(f"topk blend n={n}")
+    rng = np.random.default_rng(n)
+    local = rng.integers(0, 50, size=(2, n)).astype(np.float32)
+    prior = rng.random((2, n), dtype=np.float32)
+    local[0, :7] = [np.nan, -0.0, 0.0, np.inf, -np.inf, np.nan, 0.0]
+    prior[1, 3:6] = prior[1, 2]
+    for k in (1, n // 2, n - 1):
+        _check_rows(local, k, prior, 0.5)
+    _check_rows(local, n // 3, prior, 0.25)
