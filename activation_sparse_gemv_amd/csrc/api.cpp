@@ -172,6 +172,18 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
   MlpPlan mp;
   if (mode == AS_MLP_THRESHOLD) {
     mp.p1 = plan_gemv(w->d_model, w->d_ff, true, "AS_GU", mt_for(M));
+    // One token with the down stage summing the unsummed gate/up partials: at most
+    // one gate/up workgroup per CU (fewer partials for the down prologue to read,
+    // and the workgroups finish together; measured on the Llama shape).
+    // (The dense baseline takes the same plan, and the workspace size does not
+    // depend on the flags.)
+    if (M == 1 && env_int("AS_DN_PARTS", 1) != 0 && getenv("AS_GU_S") == nullptr) {
+      const int per_cu = num_cus() / (mp.p1.n_tiles > 0 ? mp.p1.n_tiles : 1);
+      if (per_cu >= 2 && per_cu < mp.p1.S) {
+        mp.p1.S = per_cu;
+        mp.p1.cap = (((w->d_model + per_cu - 1) / per_cu) + 7) & ~7;
+      }
+    }
     mp.n_lt = mp.p1.n_tiles;
     mp.lt_stride = mp.p1.lpr * 4;   // tile neurons = tile columns / 2
   } else {

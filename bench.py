@@ -230,7 +230,7 @@ def headline(a, C):
         "frac_of_peak_layer": round(m["gbs"] / PEAK_HBM_GBS, 4),
         "stage_us": {"gate_up": round(m["stage1_us"], 3), "down": round(m["stage2_us"], 3),
                      "dense_gate_up": round(float(dk1.mean()), 3), "dense_down": round(float(dk2.mean()), 3)},
-        "roofline": {"bound": "hbm", "kernel": "gather_gemv_kernel: gate/up row gather + SwiGLU epilogue",
+        "roofline": {"bound": "hbm", "kernel": "gather_gemv_kernel: gate/up row gather (split-K partials left for the down prologue, which applies SwiGLU)",
                      "achieved": round(m["stage1_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(m["stage1_gbs"] / PEAK_HBM_GBS, 4),
                      "bytes_per_launch": m["stage1_bytes_per_launch"], "us_per_launch": round(m["stage1_us"], 3),
