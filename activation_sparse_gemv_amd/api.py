@@ -263,8 +263,11 @@ class MoEWeights:
 
 
 def as_sparse_moe_expert(X: torch.Tensor, w: MoEWeights, ids: torch.Tensor, wts: torch.Tensor, keep_k: int,
-                         y_dtype=torch.float32, flags: int = 0, Y: torch.Tensor | None = None, debug: bool = False):
-    """Routed experts with intra-expert top-k; Y (+)= sum_j wts[t,j] * expert_{ids[t,j]}(X[t])."""
+                         y_dtype=torch.float32, flags: int = 0, Y: torch.Tensor | None = None, debug: bool = False,
+                         y_ready: "L.HipEvent | None" = None):
+    """Routed experts with intra-expert top-k; Y (+)= sum_j wts[t,j] * expert_{ids[t,j]}(X[t]).
+    y_ready: event recorded after the producer of Y on another stream; only the down
+    stage waits for it."""
     _need_cuda(X, w.w_gate_up, w.w_down, ids, wts, Y)
     T, d = X.shape
     top = ids.shape[1]
@@ -280,7 +283,8 @@ def as_sparse_moe_expert(X: torch.Tensor, w: MoEWeights, ids: torch.Tensor, wts:
         h = torch.zeros((T, top, f), dtype=torch.float32, device=X.device)
         keep = torch.full((T, top, max(keep_k, 1)), -1, dtype=torch.int32, device=X.device)
     L.check(lib.as_sparse_moe_expert(_ptr(X), _dt(X), T, _ptr(ids), _ptr(wts), top, ctypes.byref(st), keep_k,
-                                     _ptr(Y), _dt(Y), flags, _ptr(h), _ptr(keep), _ptr(ws), ws.numel(),
+                                     _ptr(Y), _dt(Y), flags, _ptr(h), _ptr(keep),
+                                     y_ready.ev if y_ready is not None else None, _ptr(ws), ws.numel(),
                                      _stream(X.device)), "as_sparse_moe_expert")
     return (Y, dict(h=h, keep=keep)) if debug else Y
 
@@ -296,14 +300,25 @@ def _side_stream(device: torch.device) -> torch.cuda.Stream:
     return _SIDE[k]
 
 
+_SIDE_EV = {}
+
+
+def _side_event(device: torch.device) -> "L.HipEvent":
+    """An event per device marking the end of the side stream's work."""
+    k = str(device)
+    if k not in _SIDE_EV:
+        _SIDE_EV[k] = L.HipEvent()
+    return _SIDE_EV[k]
+
+
 def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: int = 0, debug: bool = False,
               overlap: bool = True):
     """One MoE layer from the library's entry points: router logits (dense GEMV),
     router top-k + softmax, the dense shared expert, then the routed experts
     accumulated on top.  With `overlap`, the shared expert runs on a second stream
-    while the router runs (the routed experts then wait for it, since they
-    accumulate into its output).  Returns Y [T, d] fp32 (and intermediates when
-    debug)."""
+    while the router and the routed experts' grouping and gate/up stage run; their
+    down stage waits for it, since it accumulates into its output.  Returns Y [T, d]
+    fp32 (and intermediates when debug)."""
     T, d = X.shape
     Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
     cur = torch.cuda.current_stream(X.device)
@@ -313,20 +328,24 @@ def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: in
             as_sparse_swiglu_mlp(X[t0:t0 + 16], w.shared, flags=L.AS_FLAG_FORCE_DENSE, Y=Y[t0:t0 + 16])
 
     side = _side_stream(X.device) if overlap else None
+    ready = None
     if side is not None:
         side.wait_stream(cur)
         with torch.cuda.stream(side):
             shared()
+        ready = _side_event(X.device)
+        ready.record(side.cuda_stream)
         Y.record_stream(side)
     logits = torch.empty((T, w.w_router.shape[1]), dtype=torch.float32, device=X.device)
     for t0 in range(0, T, 16):
         as_dense_gemv(X[t0:t0 + 16], w.w_router, Y=logits[t0:t0 + 16])
     ids, wts = as_moe_router(logits, top_k)
-    if side is not None:
-        cur.wait_stream(side)
-    else:
+    if side is None:
         shared()
-    r = as_sparse_moe_expert(X, w, ids, wts, keep_k, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug)
+    # the routed experts' down stage waits for the shared expert (it accumulates
+    # into Y); their grouping and gate/up stage overlap it
+    r = as_sparse_moe_expert(X, w, ids, wts, keep_k, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug,
+                             y_ready=ready)
     if debug:
         return Y, dict(logits=logits, ids=ids, wts=wts, **r[1])
     return Y

@@ -676,8 +676,8 @@ size_t as_sparse_moe_expert_ws_size(int T, int top_k, const as_moe_weights* w) {
 
 as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_t* expert_ids,
                                const float* expert_w, int top_k, const as_moe_weights* w, int keep_k, void* Y,
-                               as_dtype y_dt, unsigned flags, float* h_dbg, int32_t* keep_dbg, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+                               as_dtype y_dt, unsigned flags, float* h_dbg, int32_t* keep_dbg,
+                               hipEvent_t y_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
   const char* fn = "as_sparse_moe_expert";
   if (!X || !expert_ids || !expert_w || !w || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!w->w_gate_up || !w->w_down) return fail(AS_ERR_INVALID_ARG, "%s: NULL weights", fn);
@@ -709,7 +709,7 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
     p.x_vec = aligned16(X) && (long(w->d_model) * es) % 16 == 0;
   }
   const int max_unique = T * top_k < w->n_experts ? T * top_k : w->n_experts;
-  return hip_check(launch_moe(int(w->w_dt), p, max_unique, stream), fn);
+  return hip_check(launch_moe(int(w->w_dt), p, max_unique, y_ready, stream), fn);
 }
 
 // ------------------------------------------------------------------ block glue

@@ -110,7 +110,7 @@ struct MoeParams {
   int x_vec;               // token rows 16-byte aligned (vector staging of x)
 };
 hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s);
-hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s);
+hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s);
 int moe_down_tiles(int d_model);
 
 // Decoder-block glue (see glue.hip).

@@ -31,10 +31,19 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(const float* log
                                                                 float* wts) {
   __shared__ TopkSmem sm;
   __shared__ int sel[64];
+  __shared__ float z[1024];       // this token's logits (E <= 1024), read once
   const long t = blockIdx.x;
   const int lane = threadIdx.x;
-  const float* z = logits + t * E;
-  wave_topk([=](int i) { return float_key(z[i]); }, E, top, sel, sm);
+  for (int i = lane; i < E; i += kRouterThreads) z[i] = logits[t * E + i];
+  __syncthreads();
+  if (E <= 64 * 4) {
+    uint32_t kr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kr[q] = q * 64 + lane < E ? float_key(z[q * 64 + lane]) : 0u;
+    wave_topk_regs<4>(kr, E, top, sel, sm);
+  } else {
+    wave_topk([=](int i) { return float_key(z[i]); }, E, top, sel, sm);
+  }
   __builtin_amdgcn_wave_barrier();
   // lane a < top holds selection a; its rank in (logit desc, index asc) order
   int me = 0, rank = 0;
@@ -350,7 +359,21 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   const int kk = valid_e ? p.keep_k : 0;
   copy_to_lds_f32(hs, h, f);
   __syncthreads();
-  block_topk<kDnThreads>([=](int i) { return float_key(fabsf(hs[i])); }, f, kk, nullptr, keep, sm);
+  // the exact top-k of |h| by one wave over the staged row (no workgroup barriers
+  // inside the selection); the other waves wait at the barrier below
+  if (threadIdx.x < 64) {
+    if (f <= 64 * 16) {
+      uint32_t kr[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = q * 64 + threadIdx.x;
+        kr[q] = i < f ? float_key(fabsf(hs[i])) : 0u;
+      }
+      wave_topk_regs<16>(kr, f, kk, keep, sm);
+    } else {
+      wave_topk([=](int i) { return float_key(fabsf(hs[i])); }, f, kk, keep, sm);
+    }
+  }
   __syncthreads();
   for (int r = threadIdx.x; r < kk; r += kDnThreads) kval[r] = hs[keep[r]];
   if (p.keep_dbg != nullptr && tile == 0)
@@ -364,7 +387,9 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  constexpr int U = 8;
+  // up to 24 kept rows per wave in one batch of independent loads (77 rows: one
+  // round trip for the four waves)
+  constexpr int U = 24;
   for (int r = wave; r < kk; r += 4 * U) {
     u32x4 w[U];
 #pragma unroll
@@ -418,7 +443,7 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   }
 }
 
-hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s) {
+hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s) {
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGrpThreads), 0, s, p.ids, p.T * p.top, p.E, p.grp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -438,6 +463,9 @@ hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipStream_t s
   }
   hipLaunchKernelGGL(k1, dim3(max_unique, nblk), dim3(kGuThreads), sm1, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // only the down stage touches Y: the producer of Y (another stream) need not be
+  // done before the grouping and the gate/up stage
+  if (y_ready != nullptr && (e = hipStreamWaitEvent(s, y_ready, 0)) != hipSuccess) return e;
   const size_t sm2 = size_t(8) * ((p.keep_k + 3) & ~3) + size_t(4) * kDnTile * 4 + size_t(p.d_ff) * 4;
   auto k2 = wdt == DT_BF16 ? expert_down_kernel<DT_BF16> : expert_down_kernel<DT_F16>;
   hipLaunchKernelGGL(k2, dim3(p.T * p.top, p.n_tiles), dim3(kDnThreads), sm2, s, p);

@@ -167,4 +167,60 @@ __device__ void wave_topk(KeyFn key, int n, int k, int* idx, TopkSmem& sm) {
   }
 }
 
+// The same selection by one wave with the keys in registers: key[q] is the key of
+// index q * 64 + lane (n <= 64 * KPL; lanes past n hold anything).  Each radix pass
+// issues the lane's histogram atomics back to back (no LDS reads of the keys), and
+// the final pass walks the 64-index chunks in order with ballots.  Writes idx[0..k)
+// ascending.  Called by the 64 threads of one wave.
+template <int KPL>
+__device__ void wave_topk_regs(const uint32_t (&key)[KPL], int n, int k, int* idx, TopkSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  if (k > n) k = n;
+  if (k <= 0) return;
+  const bool all = k >= n;
+  uint32_t T = 0u;
+  int take_eq = 0;
+  if (!all) {
+    uint32_t prefix = 0u;
+    int krem = k;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+      for (int b = lane; b < 256; b += 64) sm.hist[b] = 0u;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < KPL; ++q)
+        if (q * 64 + lane < n && (key[q] & hi_mask) == prefix) atomicAdd(&sm.hist[(key[q] >> shift) & 0xffu], 1u);
+      __builtin_amdgcn_wave_barrier();
+      wave_select_bin(sm.hist, krem, true, &sm.sel_bin, &sm.sel_krem);
+      __builtin_amdgcn_wave_barrier();
+      prefix |= (uint32_t)sm.sel_bin << shift;
+      krem = sm.sel_krem;
+      __builtin_amdgcn_wave_barrier();
+    }
+    T = prefix;
+    take_eq = krem;
+  }
+  int run_eq = 0, run_sel = 0;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) {
+    if (q * 64 >= n) break;
+    const int i = q * 64 + lane;
+    bool sel = false, eq = false;
+    if (i < n) {
+      if (all) sel = true;
+      else {
+        sel = key[q] > T;
+        eq = key[q] == T;
+      }
+    }
+    const uint64_t eqb = __ballot(eq);
+    if (eq && run_eq + lanes_below(eqb) < take_eq) sel = true;
+    run_eq += __popcll(eqb);
+    const uint64_t sb = __ballot(sel);
+    if (sel && idx != nullptr) idx[run_sel + lanes_below(sb)] = i;
+    run_sel += __popcll(sb);
+  }
+}
+
 }  // namespace as

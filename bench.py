@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--rows", default="", help="comma-separated row names to run (default: all)")
     ap.add_argument("--traffic-run", action="store_true",
                     help="counter run: a 256 MiB device copy (known bytes) then 16 headline sparse-MLP calls")
     return ap.parse_args()
@@ -628,6 +629,8 @@ def main():
                          ("a8_a9_moe", lambda: row_moe(C, cpu)),
                          ("a10_batch16_mfma", lambda: row_batch16(C, cpu, t_x, t_h)),
                          ("a11_block", lambda: row_block(C, cpu)), ("small_mlp_fp16", lambda: row_small(C, cpu))):
+            if a.rows and name not in a.rows.split(","):
+                continue
             t0 = time.time()
             rows[name] = fn()
             log(f"row {name} done in {time.time() - t0:.1f}s")

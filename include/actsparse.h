@@ -245,6 +245,10 @@ as_status as_moe_router(const float *logits, int T, int E, int top_k,
  * with AS_FLAG_ACCUMULATE).  AS_FLAG_FORCE_DENSE keeps every neuron.
  * Debug exports (nullable): h_dbg [T, top_k, d_ff_e] fp32, keep_dbg
  * [T, top_k, keep_k] int32 ascending.
+ * y_ready (nullable): an event recorded after whatever produces Y on another
+ * stream (e.g. the shared expert, for AS_FLAG_ACCUMULATE); the stream waits for
+ * it only before the down stage, the only one that touches Y, so the grouping
+ * and the gate/up stage overlap that producer.
  * Errors: INVALID_ARG for T < 1, top_k < 1 or > 32, T * top_k > 256,
  * keep_k < 0 or > d_ff_e. */
 size_t as_sparse_moe_expert_ws_size(int T, int top_k, const as_moe_weights *w);
@@ -252,7 +256,7 @@ as_status as_sparse_moe_expert(const void *X, as_dtype x_dt, int T,
                                const int32_t *expert_ids, const float *expert_w, int top_k,
                                const as_moe_weights *w, int keep_k,
                                void *Y, as_dtype y_dt, unsigned flags,
-                               float *h_dbg, int32_t *keep_dbg,
+                               float *h_dbg, int32_t *keep_dbg, hipEvent_t y_ready,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ decoder-block glue

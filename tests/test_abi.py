@@ -119,10 +119,10 @@ def test_topk_moe_block_validation(lib):
     mw = L.ASMoeWeights(_p(), _p(), L.AS_BF16, 128, 2048, 768)
     assert lib.as_sparse_moe_expert_ws_size(16, 8, ctypes.byref(mw)) > 0
     st = lib.as_sparse_moe_expert(_p(), L.AS_BF16, 64, _p(), _p(), 8, ctypes.byref(mw), 77, _p(), L.AS_F32, 0,
-                                  None, None, _p(), 1 << 30, None)
+                                  None, None, None, _p(), 1 << 30, None)
     assert st == L.AS_ERR_INVALID_ARG          # T * top_k > 256
     st = lib.as_sparse_moe_expert(_p(), L.AS_BF16, 1, _p(), _p(), 8, ctypes.byref(mw), 800, _p(), L.AS_F32, 0,
-                                  None, None, _p(), 1 << 30, None)
+                                  None, None, None, _p(), 1 << 30, None)
     assert st == L.AS_ERR_INVALID_ARG          # keep_k > d_ff_e
     assert lib.as_gqa_decode_attention(_p(), _p(), _p(), _p(), _p(), L.AS_F16, 16, 32, 8, 128, _p(), _p(), 1 << 30,
                                        None) == L.AS_ERR_UNSUPPORTED

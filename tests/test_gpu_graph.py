@@ -53,3 +53,25 @@ def test_graph_replays_match_eager():
         # eager work between replays
         asg.as_sparse_swiglu_mlp(x, w, 0.3, 0.0)
         torch.cuda.synchronize()
+
+
+def test_graph_moe_layer_with_side_stream():
+    """The MoE layer as captured by the benchmark: the shared expert on a second
+    stream, joined by the event the routed experts' down stage waits for; each replay
+    equals the eager layer (and the non-overlapped one) bit for bit."""
+    announce("graph moe layer")
+    w = datagen.moe_weights(5, 3, n_experts=16, d_model=512, d_ff_e=256, d_ff_shared=1024)
+    dw = asg.MoEWeights(w["w_gate_up"].to(DEV), w["w_down"].to(DEV), w["w_router"].to(DEV),
+                        asg.MLPWeights(w["s_gate_up"].to(DEV), w["s_down"].to(DEV)))
+    X = datagen.student_t((2, 512), 12).to(DEV)
+    eager = asg.moe_layer(X, dw, 4, 26).clone()
+    serial = asg.moe_layer(X, dw, 4, 26, overlap=False)
+    torch.cuda.synchronize()
+    assert torch.equal(eager, serial)
+    g, out = _capture(lambda: asg.moe_layer(X, dw, 4, 26))
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        asg.moe_layer(X, dw, 4, 13)
+        torch.cuda.synchronize()
