@@ -652,14 +652,12 @@ as_status as_moe_router(const float* logits, int T, int E, int top_k, int32_t* i
 
 namespace {
 struct MoeWs {
-  int* grp;
   float* h;
   float* partials;
   unsigned* counters;
 };
 MoeWs carve_moe(Carver& c, int T, int top, const as_moe_weights* w) {
   MoeWs m;
-  m.grp = c.take<int>(size_t(2 + 2 * w->n_experts + T * top));
   m.h = c.take<float>(size_t(T) * top * w->d_ff_e);
   m.partials = c.take<float>(size_t(T) * top * w->d_model);
   m.counters = c.take<unsigned>(size_t(T) * moe_down_tiles(w->d_model));
@@ -700,7 +698,7 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   p.keep_k = (flags & AS_FLAG_FORCE_DENSE) ? w->d_ff_e : keep_k;
   p.ids = expert_ids; p.wts = expert_w;
   p.w_gu = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.w_down = reinterpret_cast<const uint16_t*>(w->w_down);
-  p.grp = m.grp; p.h = m.h; p.h_dbg = h_dbg; p.keep_dbg = (flags & AS_FLAG_FORCE_DENSE) ? nullptr : keep_dbg;
+  p.h = m.h; p.h_dbg = h_dbg; p.keep_dbg = (flags & AS_FLAG_FORCE_DENSE) ? nullptr : keep_dbg;
   p.partials = m.partials; p.counters = m.counters; p.n_tiles = moe_down_tiles(w->d_model);
   p.y = Y; p.y_dt = int(y_dt); p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   p.neurons_per_block = env_int("AS_MOE_NPB", 16);

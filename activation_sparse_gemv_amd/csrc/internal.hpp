@@ -105,7 +105,7 @@ struct MoeParams {
   const void* x; int x_dt; long ldx; int T; int top; int E; int d_model; int d_ff; int keep_k;
   const int* ids; const float* wts;
   const uint16_t* w_gu; const uint16_t* w_down;     // [E, d_ff, 2, d_model], [E, d_ff, d_model]
-  int* grp; float* h; float* h_dbg; int* keep_dbg; float* partials; unsigned* counters; int n_tiles;
+  float* h; float* h_dbg; int* keep_dbg; float* partials; unsigned* counters; int n_tiles;
   void* y; int y_dt; int accumulate; int neurons_per_block;
   int x_vec;               // token rows 16-byte aligned (vector staging of x)
 };

@@ -75,68 +75,58 @@ hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, f
 }
 
 // ---------------------------------------------------------------- grouping
-// Counting sort of the (token, slot) items by expert, in one workgroup.
-// grp[0] = number of touched experts U; grp[1 .. 1+U) = their ids ascending;
-// grp[1+E .. 1+E+U] = start offsets; grp[2+2E ..) = items (t*top + j), grouped
-// by expert, ascending within a group.  Items with an id outside [0, E) are
-// dropped (they contribute nothing).
-constexpr int kGrpThreads = 256;
+// The (token, slot) items routed to an expert, computed by every gate/up
+// workgroup for itself (at most 256 items and 1024 experts, so this is a few LDS
+// passes and cheaper than a launch of its own): the touched experts in ascending
+// order, the u-th of them, and its items in ascending item order (t * top + j).
+// Items with an id outside [0, E) are dropped (they contribute nothing).  Returns
+// the expert id, or -1 when fewer than u + 1 experts are touched.
+constexpr int kGuThreads = 256;
 
-__global__ __launch_bounds__(kGrpThreads) void group_kernel(const int* ids, int n_items, int E, int* grp) {
-  __shared__ int s_ids[kGrpThreads];
-  __shared__ int s_cnt[1024];
-  __shared__ int s_off[1024];
-  __shared__ int s_scan[kGrpThreads / 64 + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kGrpThreads) s_cnt[e] = 0;
+__device__ __forceinline__ int gu_group(const MoeParams& p, int u, int* s_items, int* s_mark, int* s_scan,
+                                        int* cnt_out) {
+  __shared__ int s_e;
+  const int tid = threadIdx.x, E = p.E, n = p.T * p.top;
+  for (int e = tid; e < E; e += kGuThreads) s_mark[e] = 0;
+  if (tid == 0) s_e = -1;
+  __syncthreads();
   int my = -1;
-  if (tid < n_items) {
-    my = ids[tid];
+  if (tid < n) {
+    my = p.ids[tid];
     if (my < 0 || my >= E) my = -1;
+    if (my >= 0) s_mark[my] = 1;
   }
-  s_ids[tid] = my;
   __syncthreads();
-  if (my >= 0) atomicAdd(&s_cnt[my], 1);
-  __syncthreads();
-  // exclusive scans over experts: item offsets and touched-expert ranks
-  const int per = (E + kGrpThreads - 1) / kGrpThreads;
-  int c_items = 0, c_touch = 0;
+  // u-th touched expert: thread tid owns experts [tid * per, tid * per + per)
+  const int per = (E + kGuThreads - 1) / kGuThreads;
+  int c = 0;
   for (int q = 0; q < per; ++q) {
     const int e = tid * per + q;
-    if (e < E) { c_items += s_cnt[e]; c_touch += s_cnt[e] > 0; }
+    if (e < E) c += s_mark[e];
   }
-  int tot_items, tot_touch;
-  int off_items = block_excl_scan<kGrpThreads>(c_items, s_scan, &tot_items);
-  int off_touch = block_excl_scan<kGrpThreads>(c_touch, s_scan, &tot_touch);
-  int* uexp = grp + 1;
-  int* start = grp + 1 + E;
-  int* items = grp + 2 + 2 * E;
-  for (int q = 0; q < per; ++q) {
-    const int e = tid * per + q;
-    if (e < E) {
-      s_off[e] = off_items;
-      if (s_cnt[e] > 0) {
-        uexp[off_touch] = e;
-        start[off_touch] = off_items;
-        ++off_touch;
+  int tot;
+  int off = block_excl_scan<kGuThreads>(c, s_scan, &tot);
+  if (u >= off && u < off + c) {
+    for (int q = 0; q < per; ++q) {
+      const int e = tid * per + q;
+      if (e < E && s_mark[e]) {
+        if (off == u) s_e = e;
+        ++off;
       }
-      off_items += s_cnt[e];
     }
   }
-  if (tid == 0) {
-    grp[0] = tot_touch;
-    start[tot_touch] = tot_items;
-  }
   __syncthreads();
-  if (my >= 0) {
-    int before = 0;
-    for (int q = 0; q < tid; ++q) before += s_ids[q] == my;
-    items[s_off[my] + before] = tid;
-  }
+  const int e = s_e;
+  if (e < 0) return -1;
+  const int flag = (my == e) ? 1 : 0;
+  int cnt;
+  const int pos = block_excl_scan<kGuThreads>(flag, s_scan, &cnt);
+  if (flag) s_items[pos] = tid;
+  __syncthreads();
+  *cnt_out = cnt;
+  return e;
 }
 
-// ---------------------------------------------------------------- gate / up
-constexpr int kGuThreads = 256;
 constexpr int kGuTok = 4;   // tokens per pass
 
 // One or two tokens of an expert: the tokens' inputs stay in registers (lane l
@@ -203,13 +193,16 @@ __device__ __forceinline__ void expert_neurons_reg(const MoeParams& p, const uin
 template <int WDT, int NK>
 __global__ __launch_bounds__(kGuThreads) void expert_gu_kernel(const MoeParams p) {
   extern __shared__ __align__(16) float xs[];   // [kGuTok][d]
+  __shared__ int s_items[256];
+  __shared__ int s_mark[1024];
+  __shared__ int s_gscan[kGuThreads / 64 + 1];
   const int u = blockIdx.x;
-  const int* grp = p.grp;
-  if (u >= grp[0]) return;
-  const int E = p.E, d = p.d_model, f = p.d_ff;
-  const int e = grp[1 + u];
-  const int st = grp[1 + E + u], en = grp[1 + E + u + 1];
-  const int* items = grp + 2 + 2 * E;
+  int cnt = 0;
+  const int e = gu_group(p, u, s_items, s_mark, s_gscan, &cnt);
+  if (e < 0) return;
+  const int d = p.d_model, f = p.d_ff;
+  const int st = 0, en = cnt;
+  const int* items = s_items;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.y * p.neurons_per_block;
   const int n1 = min(n0 + p.neurons_per_block, f);
@@ -444,9 +437,7 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
 }
 
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s) {
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGrpThreads), 0, s, p.ids, p.T * p.top, p.E, p.grp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   const int nblk = (p.d_ff + p.neurons_per_block - 1) / p.neurons_per_block;
   const size_t sm1 = size_t(kGuTok) * p.d_model * 4;
   const int d = p.d_model;
