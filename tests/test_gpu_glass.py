@@ -58,3 +58,18 @@ def test_glass_static_mask_pipeline():
         y = asg.as_sparse_swiglu_mlp(toks[i:i + 1].to(DEV), w, neuron_idx=idx)
         ref = glass.neuron_set_mlp(f64(toks[i:i + 1]), Wg, Wu, Wdn, ref_idx)
         assert rel_err(y, ref) < TOL
+
+
+@pytest.mark.parametrize("P,d,f", [(128, 512, 2048), (130, 384, 448), (3, 128, 64)])
+def test_local_signal_kernels_agree(P, d, f, monkeypatch):
+    """The two staged local-signal kernels (weights through LDS, or fragments loaded
+    per lane) run the same MFMA sequence per accumulator: the same bits."""
+    announce(f"local signal kernels P={P} d={d} f={f}")
+    W = datagen.mlp_weights_neuron_major(4, P + 1, d, f)
+    X = datagen.student_t((P, d), 41 + P).to(DEV)
+    w = asg.MLPWeights(W.to(DEV), None, L.AS_MLP_NEURON_SET)
+    monkeypatch.setenv("AS_LS_LDS", "1")
+    a = asg.as_glass_local_signal(X, w).clone()
+    monkeypatch.setenv("AS_LS_LDS", "0")
+    b = asg.as_glass_local_signal(X, w)
+    assert torch.equal(a, b)
