@@ -337,9 +337,27 @@ size_t as_threshold_gemv_ws_size(int M, int K, int N) {
   return c.off;
 }
 
+// Work a decoder block folds into a projection (not part of the public calls):
+// RMS normalisation of the input in the threshold prologue (one token, the whole
+// vector in 16-byte chunks; the normalised vector optionally exported), and a
+// residual added to the output.
+struct GemvFuse {
+  bool norm = false;
+  float eps = 1e-5f;
+  float* xn_out = nullptr;
+  const void* res = nullptr;
+  int res_dt = AS_F32;
+};
+
+// Whether the threshold prologue can normalise X itself (one token, 16-byte chunks).
+static bool can_norm_in_prologue(const void* X, as_dtype x_dt, int K) {
+  return pick_chunk_vectors(X, int(x_dt), K, K) > 0 && K % 8 == 0;
+}
+
 static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N,
                              float t, void* Y, as_dtype y_dt, unsigned flags, as_mask_out* mo, void* ws,
-                             size_t ws_bytes, hipStream_t stream, bool dense, const char* fn) {
+                             size_t ws_bytes, hipStream_t stream, bool dense, const char* fn,
+                             const GemvFuse* fz = nullptr) {
   if (!X || !W || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, W or Y", fn);
   if (!is_dt(x_dt) || !is_wdt(w_dt) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
   if (M < 1 || M > 16) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..16", fn, M);
@@ -364,7 +382,10 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   // whole-vector scan per workgroup); ranges of at least 128 rows.
   const bool exports = mo && (mo->bits || mo->idx || mo->nnz);
   bool range = false;
-  if (!dense && !exports && env_int("AS_GV_RANGE", 1) != 0) {
+  const bool norm = fz != nullptr && fz->norm;
+  if (norm && (M != 1 || !can_norm_in_prologue(X, x_dt, K)))
+    return fail(AS_ERR_UNSUPPORTED, "%s: input normalisation needs one aligned token", fn);
+  if (!dense && !exports && !norm && env_int("AS_GV_RANGE", 1) != 0) {
     const int units = (K + 63) / 64;
     int S = pl.S;
     if (S > units / 2) S = units / 2 > 1 ? units / 2 : 1;
@@ -381,8 +402,16 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   if (mo && !dense) {
     p.x_bits = mo->bits; p.x_bits_ld = (K + 63) / 64; p.x_idx = mo->idx; p.x_nnz = mo->nnz;
   }
-  GemvConfig cfg{int(w_dt), mt_for(M), pl.lpr, dense ? IN_ALL : (range ? IN_RANGE : IN_THRESH), OUT_Y, false,
-                 (flags & AS_FLAG_NO_NT_LOADS) == 0};
+  int in = dense ? IN_ALL : (range ? IN_RANGE : IN_THRESH);
+  if (fz != nullptr) {
+    if (norm) {
+      // the whole vector is read by every workgroup; the dense baseline keeps every row
+      in = IN_THRESH;
+      p.norm_x = 1; p.norm_eps = fz->eps; p.xn_out = fz->xn_out; p.keep_all = dense ? 1 : 0;
+    }
+    p.res = fz->res; p.res_dt = fz->res_dt; p.ldres = N;
+  }
+  GemvConfig cfg{int(w_dt), mt_for(M), pl.lpr, in, OUT_Y, false, (flags & AS_FLAG_NO_NT_LOADS) == 0};
   return hip_check(launch_gather_gemv(cfg, p, stream), fn);
 }
 
@@ -427,10 +456,25 @@ size_t as_sparse_swiglu_mlp_ws_size(int M, const as_mlp_weights* w, as_mlp_mode 
   return c.off;
 }
 
+static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weights* w, as_mlp_mode mode,
+                          float t_x, float t_h, const int32_t* neuron_idx, int n_active, void* Y, as_dtype y_dt,
+                          unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream,
+                          const GemvFuse* fz);
+
 as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp_weights* w, as_mlp_mode mode,
                                float t_x, float t_h, const int32_t* neuron_idx, int n_active, void* Y,
                                as_dtype y_dt, unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
+  return mlp_impl(X, x_dt, M, w, mode, t_x, t_h, neuron_idx, n_active, Y, y_dt, flags, dbg, ws, ws_bytes, stream,
+                  nullptr);
+}
+
+// fz (nullable): the input normalised in the gate/up prologue and/or a residual
+// added to y (threshold mode, two launches, one token for the normalisation).
+static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weights* w, as_mlp_mode mode,
+                          float t_x, float t_h, const int32_t* neuron_idx, int n_active, void* Y, as_dtype y_dt,
+                          unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream,
+                          const GemvFuse* fz) {
   const char* fn = "as_sparse_swiglu_mlp";
   as_status st = check_mlp_weights(w, mode, fn);
   if (st != AS_OK) return st;
@@ -475,7 +519,8 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   // One launch for both stages (threshold mode, up to 8 tokens): gate/up
   // workgroups, then down workgroups that start on their range of h as soon as the
   // gate/up tiles covering it are complete (grouped by XCD).
-  const bool try_fused = mode == AS_MLP_THRESHOLD && mt <= 8 && nt && (flags & AS_FLAG_NO_FUSION) == 0 &&
+  const bool try_fused = fz == nullptr && mode == AS_MLP_THRESHOLD && mt <= 8 && nt &&
+                         (flags & AS_FLAG_NO_FUSION) == 0 &&
                          env_int("AS_FUSED", 0) != 0 && (mp.p1.lpr == 32 || mp.p1.lpr == 64) &&
                          (mp.p2.lpr == 16 || mp.p2.lpr == 32) &&
                          (long)mp.cap2_fused * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
@@ -565,8 +610,15 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
       p.x_bits = dbg->x_mask.bits; p.x_bits_ld = (d + 63) / 64; p.x_idx = dbg->x_mask.idx; p.x_nnz = dbg->x_mask.nnz;
     }
     if (dn_parts) { p.h = nullptr; p.h_bits = nullptr; }
-    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH),
-                  dn_parts ? OUT_PARTS : OUT_SWIGLU, true, nt};
+    int in1 = dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH);
+    if (fz != nullptr && fz->norm) {
+      if (M != 1 || !can_norm_in_prologue(X, x_dt, d))
+        return fail(AS_ERR_UNSUPPORTED, "%s: input normalisation needs one aligned token", fn);
+      // the whole vector is read by every workgroup; the dense baseline keeps every row
+      in1 = IN_THRESH;
+      p.norm_x = 1; p.norm_eps = fz->eps; p.xn_out = fz->xn_out; p.keep_all = dense ? 1 : 0;
+    }
+    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, in1, dn_parts ? OUT_PARTS : OUT_SWIGLU, true, nt};
     if (gu_range) p.cap = mp.cap1_range;
     if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
@@ -611,6 +663,7 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
   if (c2.in == IN_RANGE || c2.in == IN_PARTS) { p2.S = mp.s2_range; p2.cap = mp.cap2_range; }
   p2.partials = mw.g2.partials; p2.counters = mw.g2.counters; p2.part_ld = d;
   p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
+  if (fz != nullptr) { p2.res = fz->res; p2.res_dt = fz->res_dt; p2.ldres = d; }
   if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;
   return rec(2);
 }
@@ -833,6 +886,35 @@ as_status as_decoder_block(const void* X, as_dtype x_dt, const as_block_weights*
   float* h1 = dbg && dbg->h1 ? dbg->h1 : b.h1;
   float* xn2 = dbg && dbg->xn2 ? dbg->xn2 : b.xn2;
   const float inf = -INFINITY;
+  if (can_norm_in_prologue(X, x_dt, d) && can_norm_in_prologue(h1, AS_F32, d) &&
+      env_int("AS_BLOCK_FUSE", 1) != 0) {
+    // The two RMS normalisations run in the prologues of the projections that read
+    // them (qkv, and the MLP's gate/up), and the residual adds in the epilogues of
+    // the o projection (h1 = X + o W_o) and of the MLP's down stage (Y = h1 + MLP):
+    // five launches instead of seven, the same arithmetic order for the sums.
+    GemvFuse f1;
+    f1.norm = true;
+    f1.xn_out = dbg ? dbg->xn : nullptr;
+    if ((st = gemv_common(X, x_dt, 1, d, w->w_qkv, w->mlp.w_dt, nqkv, dense ? inf : t->qkv, qkv, AS_F32, pass,
+                          nullptr, b.ws_qkv, b.n_qkv, stream, dense, fn, &f1)) != AS_OK) return st;
+    if ((st = as_gqa_decode_attention(qkv, qkv + no, qkv + no + w->n_kv * hd, k_cache, v_cache, AS_BF16, n_ctx,
+                                      w->n_q, w->n_kv, hd, o, b.ws_attn, b.n_attn, stream)) != AS_OK) return st;
+    GemvFuse f2;
+    f2.res = X;
+    f2.res_dt = int(x_dt);
+    if ((st = gemv_common(o, AS_F32, 1, no, w->w_o, w->mlp.w_dt, d, dense ? inf : t->o, h1, AS_F32, pass, nullptr,
+                          b.ws_o, b.n_o, stream, dense, fn, &f2)) != AS_OK) return st;
+    GemvFuse f3;
+    f3.norm = true;
+    f3.xn_out = dbg ? dbg->xn2 : nullptr;
+    f3.res = h1;
+    f3.res_dt = AS_F32;
+    as_mlp_debug md;
+    memset(&md, 0, sizeof md);
+    md.h = dbg ? dbg->h : nullptr;
+    return mlp_impl(h1, AS_F32, 1, &w->mlp, AS_MLP_THRESHOLD, t->gate_up, t->down, nullptr, 0, Y, AS_F32, pass,
+                    md.h ? &md : nullptr, b.ws_mlp, b.n_mlp, stream, &f3);
+  }
   if ((st = as_rmsnorm(X, x_dt, 1, d, 1e-5f, xn, h1, stream)) != AS_OK) return st;
   if ((st = as_threshold_gemv(xn, AS_F32, 1, d, w->w_qkv, w->mlp.w_dt, nqkv, dense ? inf : t->qkv, qkv, AS_F32,
                               pass, nullptr, b.ws_qkv, b.n_qkv, stream)) != AS_OK) return st;

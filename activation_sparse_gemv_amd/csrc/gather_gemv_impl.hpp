@@ -284,7 +284,8 @@ __device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s
 // are gathered afterwards in one pass of independent loads.
 template <int MT, int NV>
 __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i1, bool split, int sl, int S,
-                                              int* s_idx, float* s_val, int cap, int* s_scan, int* lo_out) {
+                                              int* s_idx, float* s_val, int cap, int* s_scan, int* lo_out,
+                                              bool export_xn) {
   const int tid = threadIdx.x;
   const int M = p.M;
   const float t = p.t;
@@ -297,8 +298,29 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
   int c = 0;
   if constexpr (NV > 0 && MT == 1) {
     load_chunk<CEV>(p.x, p.x_dt, c0, n, v0);
+    if (p.norm_x && split) {
+      // RMS of the whole input (the chunks of all threads cover it): per-thread sum
+      // of squares, wave sums, the four wave partials added in wave order
+      float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < CEV; ++e) ubits |= (uint64_t)(e < n && fabsf(v0[e]) > t) << e;
+      for (int e = 0; e < CEV; ++e) ss = fmaf(v0[e], v0[e], ss);
+      ss = wave_sum(ss);
+      float* s_part = reinterpret_cast<float*>(s_scan);
+      if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) tot += s_part[w];
+      __syncthreads();   // s_scan is reused by the scan below
+      const float inv = 1.0f / sqrtf(tot / (float)(i1 - i0) + p.norm_eps);
+#pragma unroll
+      for (int e = 0; e < CEV; ++e) v0[e] *= inv;
+      if (export_xn && p.xn_out != nullptr)
+        for (int e = 0; e < n; ++e) p.xn_out[c0 + e] = v0[e];
+    }
+    const bool keep_all = p.keep_all != 0;
+#pragma unroll
+    for (int e = 0; e < CEV; ++e) ubits |= (uint64_t)(e < n && (keep_all || fabsf(v0[e]) > t)) << e;
     c = __popcll(ubits);
   } else if constexpr (NV > 0) {
     if (n == CEV && p.x_dt != DT_F32) {
@@ -651,7 +673,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     if constexpr (IN == IN_RANGE && MT > 1)
       cnt = compact_range_staged<MT, NV>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan);
     else
-      cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo);
+      cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo, tile == 0 && sl == 0);
     if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
       thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
   } else if constexpr (IN == IN_PARTS) {
@@ -935,6 +957,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
           if (m < M) {
             float v = res[m][q];
             if (p.accumulate) v += load_elem(p.y, p.y_dt, m * p.ldy + gc);
+            if (p.res != nullptr) v += load_elem(p.res, p.res_dt, m * p.ldres + gc);
             store_elem(p.y, p.y_dt, m * p.ldy + gc, v);
           }
     }

@@ -45,6 +45,12 @@ struct GemvParams {
   int x_parts; long x_up;
   int keep_all;            // IN_PARTS: keep every row (dense baseline), no mask
   const unsigned* err_flag;  // when set and nonzero at the combine, the output is NaN
+  // RMS normalisation of the input in the threshold prologue (IN_THRESH, one token,
+  // 16-byte chunks): x is scaled by 1 / sqrt(sum x^2 / K + norm_eps) before the mask
+  // and the products; xn_out (nullable) receives the normalised vector
+  int norm_x; float norm_eps; float* xn_out;
+  // OUT_Y: a residual added after the split-K sum, res[m * ldres + c] (nullable)
+  const void* res; int res_dt; long ldres;
 };
 
 struct GemvConfig {

@@ -68,10 +68,13 @@ def _thresholds(b, calib, s):
     return t
 
 
-@pytest.mark.parametrize("layer", [0, 31])
-def test_decoder_block_stagewise(layer):
+@pytest.mark.parametrize("layer,fuse", [(0, 1), (31, 1), (0, 0)])
+def test_decoder_block_stagewise(layer, fuse, monkeypatch):
     """Llama-3-8B-shaped block (q/o 4096x4096, k/v 4096x1024, MLP 4096->14336, 32/8 heads,
-    2048 cached tokens) at the depth schedule's sparsity for this layer."""
+    2048 cached tokens) at the depth schedule's sparsity for this layer; with the RMS
+    normalisations and residual adds folded into the projections (fuse=1, the
+    default) and as separate launches (fuse=0)."""
+    monkeypatch.setenv("AS_BLOCK_FUSE", str(fuse))
     s = datagen.cfg3_sparsity(layer)
     announce(f"block layer={layer} s={s:.2f}")
     b = _block(layer)
@@ -99,8 +102,10 @@ def test_decoder_block_stagewise(layer):
     print("e2e rel err", rel_err(Y, ref["out"]), flush=True)
 
 
-def test_decoder_block_dense():
-    announce("block dense")
+@pytest.mark.parametrize("fuse", [1, 0])
+def test_decoder_block_dense(fuse, monkeypatch):
+    monkeypatch.setenv("AS_BLOCK_FUSE", str(fuse))
+    announce(f"block dense fuse={fuse}")
     b = _block(0)
     x = datagen.student_t((4096,), 12345)
     tt = dict(qkv=9.0, o=9.0, gate_up=9.0, down=9.0)
