@@ -74,6 +74,9 @@ SIGNATURES = {
     "as_topk_mask": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
                              c_void_p, c_size_t, c_void_p]),
     "as_moe_router": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "as_moe_router_gemv_ws_size": (c_size_t, [c_int, c_int, c_int]),
+    "as_moe_router_gemv": (c_int, [c_void_p, c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_size_t, c_void_p]),
     "as_sparse_moe_expert_ws_size": (c_size_t, [c_int, c_int, POINTER(ASMoeWeights)]),
     "as_sparse_moe_expert": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, POINTER(ASMoeWeights),
                                      c_int, c_void_p, c_int, c_uint, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -247,6 +247,24 @@ def as_moe_router(logits: torch.Tensor, top_k: int):
     return ids, wts
 
 
+def as_moe_router_gemv(X: torch.Tensor, w_router: torch.Tensor, top_k: int):
+    """Router logits X @ w_router and routing in one launch (T <= 8, E <= 512):
+    returns (logits [T, E] fp32, ids [T, top_k] int32, weights [T, top_k])."""
+    _need_cuda(X, w_router)
+    T, d = X.shape
+    E = w_router.shape[1]
+    logits = torch.empty((T, E), dtype=torch.float32, device=X.device)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=X.device)
+    wts = torch.empty((T, top_k), dtype=torch.float32, device=X.device)
+    lib = L.load()
+    nb = lib.as_moe_router_gemv_ws_size(T, d, E)
+    ws = workspace(("router", T, d, E), nb, X.device)
+    L.check(lib.as_moe_router_gemv(_ptr(X), _dt(X), T, _ptr(w_router), _dt(w_router), d, E, top_k, _ptr(logits),
+                                   _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(), _stream(X.device)),
+            "as_moe_router_gemv")
+    return logits, ids, wts
+
+
 @dataclass
 class MoEWeights:
     """Routed experts (gate/up [E, d_ff_e, 2, d] neuron-major, down [E, d_ff_e, d]),
@@ -336,10 +354,14 @@ def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: in
         ready = _side_event(X.device)
         ready.record(side.cuda_stream)
         Y.record_stream(side)
-    logits = torch.empty((T, w.w_router.shape[1]), dtype=torch.float32, device=X.device)
-    for t0 in range(0, T, 16):
-        as_dense_gemv(X[t0:t0 + 16], w.w_router, Y=logits[t0:t0 + 16])
-    ids, wts = as_moe_router(logits, top_k)
+    E = w.w_router.shape[1]
+    if T <= 8 and E <= 512 and E % 8 == 0 and top_k <= 64:
+        logits, ids, wts = as_moe_router_gemv(X, w.w_router, top_k)
+    else:
+        logits = torch.empty((T, E), dtype=torch.float32, device=X.device)
+        for t0 in range(0, T, 16):
+            as_dense_gemv(X[t0:t0 + 16], w.w_router, Y=logits[t0:t0 + 16])
+        ids, wts = as_moe_router(logits, top_k)
     if side is None:
         shared()
     # the routed experts' down stage waits for the shared expert (it accumulates

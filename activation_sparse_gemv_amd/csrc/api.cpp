@@ -703,6 +703,52 @@ as_status as_moe_router(const float* logits, int T, int E, int top_k, int32_t* i
   return hip_check(launch_router(logits, T, E, top_k, ids, weights, stream), fn);
 }
 
+// Router logits and routing in one launch: the dense logits GEMV whose single
+// column tile's last workgroup routes every token (OUT_ROUTER).  Same plan as the
+// dense GEMV of as_dense_gemv, so the logits are the same bits.
+static Plan router_plan(int d_model, int E, int T) {
+  Plan pl = plan_gemv(d_model, E, false, "AS_GV", mt_for(T));
+  const int lpr = E <= 128 ? 16 : E <= 256 ? 32 : 64;
+  if (pl.lpr < lpr) pl.lpr = lpr;
+  pl.n_tiles = 1;
+  return pl;
+}
+
+size_t as_moe_router_gemv_ws_size(int T, int d_model, int E) {
+  if (T < 1 || T > 8 || d_model < 1 || E < 8 || E > 512) return 0;
+  const Plan pl = router_plan(d_model, E, T);
+  Carver c{nullptr};
+  carve_gemv(c, pl, T, E);
+  return c.off;
+}
+
+as_status as_moe_router_gemv(const void* X, as_dtype x_dt, int T, const void* w_router, as_dtype w_dt, int d_model,
+                             int E, int top_k, float* logits, int32_t* ids, float* weights, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "as_moe_router_gemv";
+  if (!X || !w_router || !logits || !ids || !weights) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!is_dt(x_dt) || !is_wdt(w_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (T < 1 || d_model < 1 || E < 8 || E % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: T=%d d=%d E=%d", fn, T, d_model, E);
+  if (top_k < 1 || top_k > E || top_k > 64) return fail(AS_ERR_INVALID_ARG, "%s: top_k=%d", fn, top_k);
+  if (T > 8 || E > 512 || d_model > kMaxRows)
+    return fail(AS_ERR_UNSUPPORTED, "%s: T=%d (<= 8), E=%d (<= 512), d=%d", fn, T, E, d_model);
+  if (!aligned16(w_router)) return fail(AS_ERR_INVALID_ARG, "%s: w_router not 16-byte aligned", fn);
+  const Plan pl = router_plan(d_model, E, T);
+  Carver c{reinterpret_cast<char*>(ws)};
+  GemvWs gw = carve_gemv(c, pl, T, E);
+  as_status st = check_ws(ws, ws_bytes, c.off);
+  if (st != AS_OK) return st;
+  GemvParams p = base_params();
+  p.x = X; p.x_dt = int(x_dt); p.M = T; p.K = d_model; p.ldx = d_model; p.t = -INFINITY;
+  p.W = reinterpret_cast<const uint16_t*>(w_router); p.ldw = E; p.N = E;
+  p.n_tiles = 1; p.S = pl.S; p.cap = pl.cap;
+  p.partials = gw.partials; p.counters = gw.counters; p.part_ld = E;
+  p.y = logits; p.y_dt = AS_F32; p.ldy = E;
+  p.route_top = top_k; p.route_ids = ids; p.route_wts = weights;
+  GemvConfig cfg{int(w_dt), mt_for(T), pl.lpr, IN_ALL, OUT_ROUTER, false, true};
+  return hip_check(launch_gather_gemv(cfg, p, stream), fn);
+}
+
 namespace {
 struct MoeWs {
   float* h;

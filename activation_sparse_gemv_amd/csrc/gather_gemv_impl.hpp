@@ -21,6 +21,7 @@
 #pragma once
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk.hpp"
 
 namespace as {
 
@@ -961,6 +962,27 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
             store_elem(p.y, p.y_dt, m * p.ldy + gc, v);
           }
     }
+  } else if constexpr (OUT == OUT_ROUTER) {
+    // the logits of every token (the grid has this one column tile): stored, staged
+    // in LDS, and each token routed by one wave
+    __shared__ TopkSmem r_sm[kThreads / 64];
+    __shared__ int r_sel[kThreads / 64][64];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kThreads;
+      if (c < TN)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          s_red[m * TN + c] = res[m][q];
+          if (m < M && c < p.N) store_elem(p.y, p.y_dt, m * p.ldy + c, res[m][q]);
+        }
+    }
+    __syncthreads();
+    const int wave = tid >> 6;
+    for (int m = wave; m < M; m += kThreads / 64)
+      route_token(s_red + m * TN, p.N, p.route_top, p.route_ids + m * p.route_top, p.route_wts + m * p.route_top,
+                  r_sel[wave], r_sm[wave]);
   } else if constexpr (OUT == OUT_SWIGLU) {
     static_assert(GU, "the SwiGLU epilogue needs paired gate/up columns");
     __syncthreads();
@@ -1222,6 +1244,12 @@ hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipS
     if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_SWIGLU, true>(c, p, smem, s);
     if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_SWIGLU, true>(c, p, smem, s);
     if (c.in == IN_ALL) return pick_nt<WDT, MT, LPR, IN_ALL, OUT_SWIGLU, true>(c, p, smem, s);
+    return hipErrorInvalidValue;
+  }
+  if (c.out == OUT_ROUTER) {
+    if constexpr (MT <= 8) {
+      if (c.in == IN_ALL) return pick_nt<WDT, MT, LPR, IN_ALL, OUT_ROUTER, false>(c, p, smem, s);
+    }
     return hipErrorInvalidValue;
   }
   if (c.out != OUT_Y) return hipErrorInvalidValue;

@@ -8,7 +8,7 @@
 namespace as {
 
 enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_TILES = 3, IN_RANGE = 4, IN_PARTS = 5 };
-enum { OUT_Y = 0, OUT_SWIGLU = 1, OUT_PARTS = 2 };
+enum { OUT_Y = 0, OUT_SWIGLU = 1, OUT_PARTS = 2, OUT_ROUTER = 3 };
 
 // One row-gather GEMV launch: Y[m, c] = sum over listed rows i of xv[m, i] * W[i, c].
 // The rows come from a magnitude mask of a vector (IN_THRESH: the whole vector,
@@ -20,7 +20,8 @@ enum { OUT_Y = 0, OUT_SWIGLU = 1, OUT_PARTS = 2 };
 // mask |h| > t).
 // The grid is n_tiles column tiles x S slices of the row list (split-K); the
 // last workgroup of a tile sums the S partials in slice order and runs the
-// epilogue (OUT_Y: store y; OUT_SWIGLU: h = silu(g) * u, |h| > t_h, per-tile list),
+// epilogue (OUT_Y: store y; OUT_SWIGLU: h = silu(g) * u, |h| > t_h, per-tile list;
+// OUT_ROUTER: store the logits and route every token from them),
 // or every workgroup stores its partial and stops (OUT_PARTS: the next launch
 // sums them).
 struct GemvParams {
@@ -51,6 +52,9 @@ struct GemvParams {
   int norm_x; float norm_eps; float* xn_out;
   // OUT_Y: a residual added after the split-K sum, res[m * ldres + c] (nullable)
   const void* res; int res_dt; long ldres;
+  // OUT_ROUTER (one column tile holding all N logits): y = logits, then per token
+  // the top route_top experts and their softmax weights
+  int route_top; int* route_ids; float* route_wts;
 };
 
 struct GemvConfig {

@@ -22,9 +22,8 @@
 namespace as {
 
 // ---------------------------------------------------------------- router
-// One wave per token: exact top-k of the logits (wave radix select), the
-// selection ordered by (logit desc, index asc) through per-lane ranks, and the
-// softmax over the selected logits.
+// One wave per token (route_token, topk.hpp): the token's logits staged in LDS,
+// exact top-k, ordered by (logit desc, index asc), softmax over the selected.
 constexpr int kRouterThreads = 64;
 
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(const float* logits, int E, int top, int* ids,
@@ -36,37 +35,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(const float* log
   const int lane = threadIdx.x;
   for (int i = lane; i < E; i += kRouterThreads) z[i] = logits[t * E + i];
   __syncthreads();
-  if (E <= 64 * 4) {
-    uint32_t kr[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kr[q] = q * 64 + lane < E ? float_key(z[q * 64 + lane]) : 0u;
-    wave_topk_regs<4>(kr, E, top, sel, sm);
-  } else {
-    wave_topk([=](int i) { return float_key(z[i]); }, E, top, sel, sm);
-  }
-  __builtin_amdgcn_wave_barrier();
-  // lane a < top holds selection a; its rank in (logit desc, index asc) order
-  int me = 0, rank = 0;
-  uint32_t km = 0u;
-  if (lane < top) {
-    me = sel[lane];
-    km = float_key(z[me]);
-    for (int b = 0; b < top; ++b) {
-      const int ob = sel[b];
-      const uint32_t kb = float_key(z[ob]);
-      rank += (kb > km) || (kb == km && ob < me);
-    }
-  }
-  // softmax over the selected logits, shifted by their maximum
-  float m = lane < top ? z[me] : -INFINITY;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  const float ev = lane < top ? expf(z[me] - m) : 0.f;
-  const float sum = wave_sum(ev);
-  if (lane < top) {
-    ids[t * top + rank] = me;
-    wts[t * top + rank] = ev / sum;
-  }
+  route_token(z, E, top, ids + t * top, wts + t * top, sel, sm);
 }
 
 hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s) {

@@ -223,4 +223,46 @@ __device__ void wave_topk_regs(const uint32_t (&key)[KPL], int n, int k, int* id
   }
 }
 
+// Routing of one token by one wave (intra-expert summary, system implementation:
+// the router picks the top experts by logit and weights them by a softmax over
+// the picked logits): z = the token's E logits (LDS), the exact top-`top` by
+// logit (ties to the smaller expert), written in (logit desc, index asc) order to
+// ids[0..top) with weights softmax over the selected logits, shifted by their
+// maximum.  sel: [64] LDS scratch; E <= 1024, top <= 64.
+__device__ __forceinline__ void route_token(const float* z, int E, int top, int* ids, float* wts, int* sel,
+                                            TopkSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  if (E <= 64 * 4) {
+    uint32_t kr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kr[q] = q * 64 + lane < E ? float_key(z[q * 64 + lane]) : 0u;
+    wave_topk_regs<4>(kr, E, top, sel, sm);
+  } else {
+    wave_topk([=](int i) { return float_key(z[i]); }, E, top, sel, sm);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane a < top holds selection a; its rank in (logit desc, index asc) order
+  int me = 0, rank = 0;
+  uint32_t km = 0u;
+  if (lane < top) {
+    me = sel[lane];
+    km = float_key(z[me]);
+    for (int b = 0; b < top; ++b) {
+      const int ob = sel[b];
+      const uint32_t kb = float_key(z[ob]);
+      rank += (kb > km) || (kb == km && ob < me);
+    }
+  }
+  float m = lane < top ? z[me] : -INFINITY;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float ev = lane < top ? expf(z[me] - m) : 0.f;
+  const float sum = wave_sum(ev);
+  if (lane < top) {
+    ids[rank] = me;
+    wts[rank] = ev / sum;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 }  // namespace as

@@ -231,6 +231,21 @@ typedef struct {
 as_status as_moe_router(const float *logits, int T, int E, int top_k,
                         int32_t *ids, float *weights, hipStream_t stream);
 
+/* Router logits and routing in one launch: logits = X W_router (dense GEMV,
+ * fp32 accumulation), then exactly what as_moe_router does with them.  The
+ * logits are the same bits as as_dense_gemv's for E <= 128.
+ * X: [T, d_model] (f16/bf16/f32); w_router: [d_model, E] (f16/bf16, 16-byte
+ * aligned); logits: [T, E] fp32 (output); ids [T, top_k] int32 and weights
+ * [T, top_k] fp32 as for as_moe_router.  ws: as_moe_router_gemv_ws_size(T,
+ * d_model, E) bytes, zero-filled once, left zeroed.
+ * Errors: INVALID_ARG for NULL pointers, E not a multiple of 8, top_k outside
+ * 1..min(E, 64); UNSUPPORTED for T > 8 or E > 512 (use as_dense_gemv and
+ * as_moe_router); WORKSPACE if ws is too small. */
+size_t as_moe_router_gemv_ws_size(int T, int d_model, int E);
+as_status as_moe_router_gemv(const void *X, as_dtype x_dt, int T, const void *w_router, as_dtype w_dt,
+                             int d_model, int E, int top_k, float *logits, int32_t *ids, float *weights,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Routed experts with intra-expert activation sparsity (intra-expert summary,
  * system implementation: dense gate scoring, low-scoring neurons masked, only
  * the active neurons' weights gathered):

@@ -111,3 +111,29 @@ def test_moe_invalid_ids_and_determinism():
     assert dbg["keep"][0, 1].cpu().numpy().tolist() == [-1] * 5      # invalid expert: nothing kept
     Y2 = asg.as_sparse_moe_expert(X, dw, ids, wts, 5)
     assert torch.equal(Y, Y2)
+
+
+@pytest.mark.parametrize("T,E,top", [(1, 128, 8), (3, 128, 8), (8, 128, 8), (2, 256, 6), (5, 512, 16), (1, 64, 64)])
+def test_router_gemv_fused(T, E, top):
+    """Logits GEMV and routing in one launch: the logits equal as_dense_gemv's (bit for
+    bit up to 128 experts, the same plan), and the routing equals as_moe_router's on
+    those logits, bit for bit."""
+    announce(f"router gemv T={T} E={E} top={top}")
+    d = 2048
+    Wr = datagen.normal((d, E), 600 + E, std=0.02).to(DEV)
+    X = datagen.student_t((T, d), 601 + T).to(DEV)
+    logits, ids, wts = asg.as_moe_router_gemv(X, Wr, top)
+    ref_logits = asg.as_dense_gemv(X, Wr)
+    if E <= 128:
+        assert torch.equal(logits, ref_logits)
+    else:
+        assert rel_err(logits, f64(ref_logits)) < 1e-5
+    ids2, wts2 = asg.as_moe_router(logits, top)
+    assert torch.equal(ids, ids2)
+    assert torch.equal(wts, wts2)
+    # against the oracle router on the same logits
+    eye = np.eye(E)
+    for t in range(T):
+        ref_ids, ref_w, _ = moe.router(f64(logits[t]), eye, top)     # the oracle router on these logits
+        assert ids[t].cpu().numpy().tolist() == ref_ids.tolist()
+        assert rel_err(wts[t], ref_w) < 1e-5
