@@ -7,6 +7,6 @@ entry-point names, and ``datagen`` draws the seeded synthetic inputs.
 from . import _lib  # noqa: F401
 from .api import (  # noqa: F401
     BlockWeights, MLPWeights, MoEWeights, as_decoder_block, as_gqa_decode_attention, as_rmsnorm,
-    as_glass_local_signal, as_moe_router, as_moe_router_gemv, as_sparse_moe_expert, moe_layer, as_bench_flush, as_calibrate_threshold, as_dense_gemv, as_sparse_swiglu_mlp,
+    as_glass_local_signal, as_moe_router, as_moe_router_gemv, as_sparse_moe_expert, as_moe_layer, moe_layer, as_bench_flush, as_calibrate_threshold, as_dense_gemv, as_sparse_swiglu_mlp,
     as_threshold_gemv, as_topk_mask, as_version, nearest_rank, unpack_bits, workspace,
 )

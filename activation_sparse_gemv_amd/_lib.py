@@ -35,6 +35,10 @@ class ASMoeWeights(ctypes.Structure):
                 ("d_model", c_int), ("d_ff_e", c_int)]
 
 
+class ASMoeLayerWeights(ctypes.Structure):
+    _fields_ = [("w_router", c_void_p), ("experts", ASMoeWeights), ("shared", ASMlpWeights)]
+
+
 class ASBlockWeights(ctypes.Structure):
     _fields_ = [("w_qkv", c_void_p), ("w_o", c_void_p), ("mlp", ASMlpWeights), ("n_q", c_int), ("n_kv", c_int),
                 ("head_dim", c_int)]
@@ -81,6 +85,9 @@ SIGNATURES = {
     "as_sparse_moe_expert": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, POINTER(ASMoeWeights),
                                      c_int, c_void_p, c_int, c_uint, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),
+    "as_moe_layer_ws_size": (c_size_t, [c_int, c_int, POINTER(ASMoeLayerWeights)]),
+    "as_moe_layer": (c_int, [c_void_p, c_int, c_int, POINTER(ASMoeLayerWeights), c_int, c_int, c_void_p, c_uint,
+                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "as_rmsnorm": (c_int, [c_void_p, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p]),
     "as_gqa_decode_attention_ws_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "as_gqa_decode_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,

@@ -307,6 +307,51 @@ def as_sparse_moe_expert(X: torch.Tensor, w: MoEWeights, ids: torch.Tensor, wts:
     return (Y, dict(h=h, keep=keep)) if debug else Y
 
 
+def _moe_layer_struct(w: MoEWeights) -> "L.ASMoeLayerWeights | None":
+    if w.w_router is None or w.shared is None or w.w_router.dtype != torch.bfloat16:
+        return None
+    return L.ASMoeLayerWeights(_ptr(w.w_router), w.struct(), w.shared.struct())
+
+
+def as_moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: int = 0, debug: bool = False):
+    """The whole MoE layer on the current stream in three launches (C entry point
+    as_moe_layer): router logits + routing beside the shared expert's gate/up, the
+    routed gate/up beside the shared expert's down, then the routed down stage.
+    Up to 8 tokens, bf16 weights; raises ASError (UNSUPPORTED) outside the limits.
+    Returns Y [T, d] fp32 (and logits, ids, wts, h, keep when debug)."""
+    _need_cuda(X, w.w_gate_up, w.w_down, w.w_router)
+    T, d = X.shape
+    E, f = w.w_gate_up.shape[0], w.w_gate_up.shape[1]
+    lib = L.load()
+    st = _moe_layer_struct(w)
+    if st is None:
+        raise ValueError("as_moe_layer: needs a bf16 router and a shared expert")
+    nb = lib.as_moe_layer_ws_size(T, top_k, ctypes.byref(st))
+    ws = workspace(("moe_layer", T, top_k, E, d, f, w.shared.d_ff), nb, X.device)
+    Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=X.device)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=X.device)
+    wts = torch.empty((T, top_k), dtype=torch.float32, device=X.device)
+    h = keep = None
+    if debug:
+        h = torch.zeros((T, top_k, f), dtype=torch.float32, device=X.device)
+        keep = torch.full((T, top_k, max(keep_k, 1)), -1, dtype=torch.int32, device=X.device)
+    L.check(lib.as_moe_layer(_ptr(X), _dt(X), T, ctypes.byref(st), top_k, keep_k, _ptr(Y), flags, _ptr(logits),
+                             _ptr(ids), _ptr(wts), _ptr(h), _ptr(keep), _ptr(ws), ws.numel(), _stream(X.device)),
+            "as_moe_layer")
+    if debug:
+        return Y, dict(logits=logits, ids=ids, wts=wts, h=h, keep=keep)
+    return Y
+
+
+def moe_layer_one_stream_ok(X: torch.Tensor, w: MoEWeights, top_k: int, flags: int = 0) -> bool:
+    """Whether as_moe_layer takes this call (shapes within its limits, bf16 weights)."""
+    if flags & ~L.AS_FLAG_FORCE_DENSE:
+        return False
+    st = _moe_layer_struct(w)
+    return st is not None and L.load().as_moe_layer_ws_size(X.shape[0], top_k, ctypes.byref(st)) > 0
+
+
 _SIDE = {}
 
 
@@ -330,13 +375,17 @@ def _side_event(device: torch.device) -> "L.HipEvent":
 
 
 def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: int = 0, debug: bool = False,
-              overlap: bool = True):
-    """One MoE layer from the library's entry points: router logits (dense GEMV),
-    router top-k + softmax, the dense shared expert, then the routed experts
-    accumulated on top.  With `overlap`, the shared expert runs on a second stream
-    while the router and the routed experts' grouping and gate/up stage run; their
-    down stage waits for it, since it accumulates into its output.  Returns Y [T, d]
-    fp32 (and intermediates when debug)."""
+              overlap: bool = True, one_stream: bool = True):
+    """One MoE layer: router logits (dense GEMV), router top-k + softmax, the dense
+    shared expert, then the routed experts accumulated on top.  Where as_moe_layer
+    takes the shapes (and `one_stream`), the layer is that one call: three launches
+    on the current stream.  Otherwise it is composed from the separate entry points;
+    with `overlap`, the shared expert then runs on a second stream while the router
+    and the routed experts' gate/up stage run, and their down stage waits for it,
+    since it accumulates into its output.  Returns Y [T, d] fp32 (and intermediates
+    when debug)."""
+    if one_stream and moe_layer_one_stream_ok(X, w, top_k, flags):
+        return as_moe_layer(X, w, top_k, keep_k, flags=flags, debug=debug)
     T, d = X.shape
     Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
     cur = torch.cuda.current_stream(X.device)

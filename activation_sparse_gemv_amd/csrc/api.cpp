@@ -750,6 +750,11 @@ as_status as_moe_router_gemv(const void* X, as_dtype x_dt, int T, const void* w_
 }
 
 namespace {
+// Neurons per gate/up workgroup: 16 for one token's 8 items (more workgroups keep
+// every CU busy), 32 beyond (fewer, longer workgroups; measured on the 128-expert,
+// d_model 2048, d_ff_e 768 shape for 1 to 16 tokens).
+int moe_npb(int items) { return env_int("AS_MOE_NPB", items <= 8 ? 16 : 32); }
+
 struct MoeWs {
   float* h;
   float* partials;
@@ -800,13 +805,173 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   p.h = m.h; p.h_dbg = h_dbg; p.keep_dbg = (flags & AS_FLAG_FORCE_DENSE) ? nullptr : keep_dbg;
   p.partials = m.partials; p.counters = m.counters; p.n_tiles = moe_down_tiles(w->d_model);
   p.y = Y; p.y_dt = int(y_dt); p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
-  p.neurons_per_block = env_int("AS_MOE_NPB", 16);
+  p.neurons_per_block = moe_npb(T * top_k);
   {
     const int es = x_dt == AS_F32 ? 4 : 2;
     p.x_vec = aligned16(X) && (long(w->d_model) * es) % 16 == 0;
   }
   const int max_unique = T * top_k < w->n_experts ? T * top_k : w->n_experts;
   return hip_check(launch_moe(int(w->w_dt), p, max_unique, y_ready, stream), fn);
+}
+
+// ------------------------------------------------------------------ MoE layer (one stream)
+namespace {
+// Plans of the three pieces and the combined launches' shapes; ok = false when the
+// shapes are outside the combined launches' limits.
+struct MoeLayerPlan {
+  bool ok;
+  Plan router;
+  MlpPlan shared;
+  MoeLayerCfg cfg;    // nk filled in at the call (depends on X's alignment)
+};
+
+MoeLayerPlan moe_layer_plan(int T, int top_k, const as_moe_layer_weights* w) {
+  MoeLayerPlan lp;
+  memset(&lp, 0, sizeof lp);
+  if (!w || T < 1 || T > 8 || top_k < 1) return lp;
+  const as_moe_weights& e = w->experts;
+  const as_mlp_weights& sh = w->shared;
+  const int E = e.n_experts, d = e.d_model;
+  if (E < 8 || E > 512 || E % 8 != 0 || top_k > 32 || top_k > E || T * top_k > 256) return lp;
+  if (d < 8 || d % 8 != 0 || d > kMaxRows || e.d_ff_e < 1 || e.d_ff_e > 8192) return lp;
+  if (sh.d_model != d || sh.d_ff < 64 || sh.d_ff % 64 != 0 || sh.d_ff > kMaxRows) return lp;
+  if (e.w_dt != AS_BF16 || sh.w_dt != AS_BF16) return lp;
+  lp.router = router_plan(d, E, T);
+  lp.shared = plan_mlp(T, &sh, AS_MLP_THRESHOLD, true);
+  {
+    // The shared down stage shares its launch with the routed gate/up workgroups,
+    // which take most of the device: one row range per CU and column tile, so the
+    // launch fits one round of workgroups.
+    MlpPlan& mp = lp.shared;
+    const int units = (sh.d_ff + 63) / 64;
+    const int per = num_cus() / (mp.p2.n_tiles > 0 ? mp.p2.n_tiles : 1);
+    if (per >= 1 && per < mp.s2_range) {
+      mp.s2_range = per;
+      mp.cap2_range = ((units + per - 1) / per) * 64;
+    }
+  }
+  const int mt = mt_for(T);
+  lp.cfg = MoeLayerCfg{int(AS_BF16), mt, lp.router.lpr, lp.shared.p1.lpr, lp.shared.p2.lpr, 0};
+  if (!moe_layer_supported(lp.cfg)) return lp;
+  // the shared down stage stages its range of every token's partial sums in LDS
+  if ((long)lp.shared.cap2_range * (4 + 8 * mt) > kLdsBytes - kLdsReserve) return lp;
+  if ((long)lp.shared.p1.S * T * 2L * sh.d_ff >= (1L << 31) || (long)lp.shared.parts2 * T * d >= (1L << 31))
+    return lp;
+  lp.ok = true;
+  return lp;
+}
+
+struct MoeLayerWs {
+  GemvWs router;
+  MlpWs shared;
+  MoeWs moe;
+};
+MoeLayerWs carve_moe_layer(Carver& c, const MoeLayerPlan& lp, int T, int top_k, const as_moe_layer_weights* w) {
+  MoeLayerWs m;
+  m.router = carve_gemv(c, lp.router, T, w->experts.n_experts);
+  m.shared = carve_mlp(c, lp.shared, T, &w->shared, AS_MLP_THRESHOLD);
+  m.moe = carve_moe(c, T, top_k, &w->experts);
+  return m;
+}
+}  // namespace
+
+size_t as_moe_layer_ws_size(int T, int top_k, const as_moe_layer_weights* w) {
+  const MoeLayerPlan lp = moe_layer_plan(T, top_k, w);
+  if (!lp.ok) return 0;
+  Carver c{nullptr};
+  carve_moe_layer(c, lp, T, top_k, w);
+  return c.off;
+}
+
+as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_weights* w, int top_k, int keep_k,
+                       float* Y, unsigned flags, float* logits, int32_t* ids, float* weights, float* h_dbg,
+                       int32_t* keep_dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "as_moe_layer";
+  if (!X || !w || !Y || !logits || !ids || !weights) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!w->w_router || !w->experts.w_gate_up || !w->experts.w_down)
+    return fail(AS_ERR_INVALID_ARG, "%s: NULL router or expert weights", fn);
+  as_status st = check_mlp_weights(&w->shared, AS_MLP_THRESHOLD, fn);
+  if (st != AS_OK) return st;
+  if (!is_dt(x_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (T < 1 || top_k < 1) return fail(AS_ERR_INVALID_ARG, "%s: T=%d top_k=%d", fn, T, top_k);
+  const as_moe_weights& ew = w->experts;
+  if (keep_k < 0 || keep_k > ew.d_ff_e) return fail(AS_ERR_INVALID_ARG, "%s: keep_k=%d", fn, keep_k);
+  if ((flags & ~unsigned(AS_FLAG_FORCE_DENSE)) != 0) return fail(AS_ERR_UNSUPPORTED, "%s: flags 0x%x", fn, flags);
+  if (!aligned16(w->w_router) || !aligned16(ew.w_gate_up) || !aligned16(ew.w_down))
+    return fail(AS_ERR_INVALID_ARG, "%s: weights not 16-byte aligned", fn);
+  MoeLayerPlan lp = moe_layer_plan(T, top_k, w);
+  if (!lp.ok)
+    return fail(AS_ERR_UNSUPPORTED, "%s: T=%d E=%d top_k=%d d=%d d_ff_e=%d outside the one-stream layer's limits",
+                fn, T, ew.n_experts, top_k, ew.d_model, ew.d_ff_e);
+  Carver c{reinterpret_cast<char*>(ws)};
+  const MoeLayerWs m = carve_moe_layer(c, lp, T, top_k, w);
+  if ((st = check_ws(ws, ws_bytes, c.off)) != AS_OK) return st;
+
+  const int E = ew.n_experts, d = ew.d_model, f = w->shared.d_ff, mt = lp.cfg.mt;
+  const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
+  // launch 1, first piece: router logits GEMV, its last workgroup routes (as in as_moe_router_gemv)
+  GemvParams pr = base_params();
+  pr.x = X; pr.x_dt = int(x_dt); pr.M = T; pr.K = d; pr.ldx = d; pr.t = -INFINITY;
+  pr.W = reinterpret_cast<const uint16_t*>(w->w_router); pr.ldw = E; pr.N = E;
+  pr.n_tiles = 1; pr.S = lp.router.S; pr.cap = lp.router.cap;
+  pr.partials = m.router.partials; pr.counters = m.router.counters; pr.part_ld = E;
+  pr.y = logits; pr.y_dt = AS_F32; pr.ldy = E;
+  pr.route_top = top_k; pr.route_ids = ids; pr.route_wts = weights;
+  // second piece: the shared expert's gate/up, every row, partials unsummed (as the
+  // dense MLP's gate/up stage with the down stage summing the partials)
+  const MlpPlan& mp = lp.shared;
+  GemvParams pg = base_params();
+  pg.x = X; pg.x_dt = int(x_dt); pg.M = T; pg.K = d; pg.ldx = d; pg.t = -INFINITY; pg.t_h = -INFINITY;
+  pg.W = reinterpret_cast<const uint16_t*>(w->shared.w_gate_up); pg.ldw = 2L * f; pg.N = f; pg.gu_off = f;
+  pg.n_tiles = mp.p1.n_tiles; pg.S = mp.p1.S; pg.cap = mp.p1.cap;
+  pg.partials = m.shared.g1.partials; pg.counters = m.shared.g1.counters; pg.part_ld = 2L * f;
+  const GemvConfig cr{int(AS_BF16), mt, lp.router.lpr, IN_ALL, OUT_ROUTER, false, true};
+  const GemvConfig cg{int(AS_BF16), mt, mp.p1.lpr, IN_ALL, OUT_PARTS, true, true};
+  size_t sm1 = gemv_smem_bytes(cr, pr.cap, 0);
+  {
+    const size_t b = gemv_smem_bytes(cg, pg.cap, 0);
+    if (b > sm1) sm1 = b;
+  }
+  // launch 2, first piece: routed experts' gate/up (as in as_sparse_moe_expert)
+  MoeParams pm;
+  memset(&pm, 0, sizeof pm);
+  pm.x = X; pm.x_dt = int(x_dt); pm.ldx = d; pm.T = T; pm.top = top_k; pm.E = E;
+  pm.d_model = d; pm.d_ff = ew.d_ff_e;
+  pm.keep_k = dense ? ew.d_ff_e : keep_k;
+  pm.ids = ids; pm.wts = weights;
+  pm.w_gu = reinterpret_cast<const uint16_t*>(ew.w_gate_up); pm.w_down = reinterpret_cast<const uint16_t*>(ew.w_down);
+  pm.h = m.moe.h; pm.h_dbg = h_dbg; pm.keep_dbg = dense ? nullptr : keep_dbg;
+  pm.partials = m.moe.partials; pm.counters = m.moe.counters; pm.n_tiles = moe_down_tiles(d);
+  pm.y = Y; pm.y_dt = AS_F32; pm.accumulate = 1;
+  pm.neurons_per_block = moe_npb(T * top_k);
+  {
+    const int es = x_dt == AS_F32 ? 4 : 2;
+    pm.x_vec = aligned16(X) && (long(d) * es) % 16 == 0;
+  }
+  const int n_u = T * top_k < E ? T * top_k : E;
+  const int n_gu = n_u * moe_gu_blocks_of(pm);
+  lp.cfg.nk = moe_gu_nk_of(pm);
+  // second piece: the shared expert's down projection; sums the gate/up partials of
+  // its range of h, SwiGLU, every row kept; writes Y
+  GemvParams pd = base_params();
+  pd.M = T; pd.W = reinterpret_cast<const uint16_t*>(w->shared.w_down); pd.ldw = d;
+  pd.x = m.shared.g1.partials; pd.x_dt = AS_F32; pd.K = f; pd.ldx = 2L * f; pd.t = -INFINITY;
+  pd.x_parts = mp.p1.S; pd.x_up = f; pd.keep_all = 1;
+  pd.list_cnt = m.shared.l_cnt; pd.list_idx = m.shared.l_idx; pd.list_val = m.shared.l_val;
+  pd.n_lt = mp.n_lt; pd.lt_stride = mp.lt_stride;
+  pd.N = d; pd.n_tiles = mp.p2.n_tiles; pd.S = mp.s2_range; pd.cap = mp.cap2_range;
+  pd.partials = m.shared.g2.partials; pd.counters = m.shared.g2.counters; pd.part_ld = d;
+  pd.y = Y; pd.y_dt = AS_F32; pd.ldy = d; pd.accumulate = 0;
+  const GemvConfig cd{int(AS_BF16), mt, mp.p2.lpr, IN_PARTS, OUT_Y, false, true};
+  size_t sm2 = moe_gu_smem_of(pm);
+  {
+    const size_t b = gemv_smem_bytes(cd, pd.cap, 0);
+    if (b > sm2) sm2 = b;
+  }
+  if ((st = hip_check(launch_moe_route_gu(lp.cfg, pr, pg, sm1, stream), fn)) != AS_OK) return st;
+  if ((st = hip_check(launch_moe_gu_down(lp.cfg, pm, n_u, n_gu, pd, sm2, stream), fn)) != AS_OK) return st;
+  // launch 3: routed down stage, exact top keep_k per (token, slot), added onto Y
+  return hip_check(launch_moe_down(int(AS_BF16), pm, stream), fn);
 }
 
 // ------------------------------------------------------------------ block glue

@@ -176,19 +176,80 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Wave reductions without LDS: DPP moves within each row of 16 lanes (quad lane
+// swaps xor 1 and xor 2, then rotations by 4 and 8 lanes), after which every lane
+// holds its row's result; the four row results are read out with readlane and
+// combined as (row0 op row1) op (row2 op row3).  The result is the same in every
+// lane.  Called with the whole wave active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float dppf(float v, int ctrl_sel) {
+  switch (ctrl_sel) {
+    case 0: return __int_as_float(dpp_mov<0xB1>(__float_as_int(v)));    // quad_perm [1, 0, 3, 2]
+    case 1: return __int_as_float(dpp_mov<0x4E>(__float_as_int(v)));    // quad_perm [2, 3, 0, 1]
+    case 2: return __int_as_float(dpp_mov<0x124>(__float_as_int(v)));   // row_ror:4
+    default: return __int_as_float(dpp_mov<0x128>(__float_as_int(v)));  // row_ror:8
+  }
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (l >= o) v += t;
+  for (int s = 0; s < 4; ++s) v += dppf(v, s);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v = fmaxf(v, dppf(v, s));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t x = (uint32_t)__float_as_int(dppf(__int_as_float((int)v), s));
+    v = x > v ? x : v;
   }
+  uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+  for (int l = 16; l < 64; l += 16) {
+    const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+    r = x > r ? x : r;
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t x = (uint32_t)__float_as_int(dppf(__int_as_float((int)v), s));
+    v = x < v ? x : v;
+  }
+  uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+  for (int l = 16; l < 64; l += 16) {
+    const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+    r = x < r ? x : r;
+  }
+  return r;
+}
+
+// Inclusive prefix sum over the 64 lanes by DPP: shifts right by 1, 2, 4 and 8
+// lanes within each row of 16 (lanes without a source add 0), then the last lane
+// of row 0 is broadcast into rows 1 and 3 and the last lane of row 1 into rows 2
+// and 3.  Called with the whole wave active.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
   return v;
 }
 

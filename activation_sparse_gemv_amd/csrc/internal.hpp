@@ -121,7 +121,24 @@ struct MoeParams {
 };
 hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s);
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s);
+hipError_t launch_moe_down(int wdt, const MoeParams& p, hipStream_t s);
 int moe_down_tiles(int d_model);
+// Launch shape of the routed gate/up stage (register chunks NK, neuron blocks, LDS).
+int moe_gu_nk_of(const MoeParams& p);
+int moe_gu_blocks_of(const MoeParams& p);
+size_t moe_gu_smem_of(const MoeParams& p);
+
+// One-stream MoE layer (moe_layer_impl.hpp): launch 1 = router logits GEMV with
+// routing | shared expert gate/up (OUT_PARTS); launch 2 = routed gate/up | shared
+// expert down (IN_PARTS, OUT_Y); launch 3 = launch_moe_down.  bf16 weights, up to
+// 8 tokens; lpr_r in {16, 32, 64}, lpr_g in {32, 64}, lpr_d in {16, 64},
+// nk in {0, 1, 2, 4, 8}.
+struct MoeLayerCfg { int wdt, mt, lpr_r, lpr_g, lpr_d, nk; };
+bool moe_layer_supported(const MoeLayerCfg& c);
+hipError_t launch_moe_route_gu(const MoeLayerCfg& c, const GemvParams& pr, const GemvParams& pg, size_t smem,
+                               hipStream_t s);
+hipError_t launch_moe_gu_down(const MoeLayerCfg& c, const MoeParams& pm, int n_u, int n_gu, const GemvParams& pd,
+                              size_t smem, hipStream_t s);
 
 // Decoder-block glue (see glue.hip).
 struct AttnParams {

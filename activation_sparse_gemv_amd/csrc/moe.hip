@@ -9,15 +9,14 @@
 // down rows (one contiguous d_model row each) are read.
 //
 // Kernels (one call):
-//   group:   one workgroup sorts the (token, slot) assignments by expert, so the
-//            weights of an expert are read once for all tokens routed to it;
-//   gate/up: (touched expert, neuron block) workgroups; one wave per neuron
-//            computes both dot products for up to 4 tokens at a time;
-//   down:    (token, slot, column tile) workgroups: exact top-k of |h|, gathered
-//            down rows, weight w_tj; the last slot to finish a (token, tile)
-//            sums the slots in slot order into Y (deterministic).
-#include "topk.hpp"
-#include "internal.hpp"
+//   gate/up: (touched expert, neuron block) workgroups; each derives its expert's
+//            (token, slot) items itself, and one wave per neuron computes both dot
+//            products for the expert's tokens (up to 4 at a time);
+//   down:    (token, slot, column tile) workgroups: the exact top-k of |h| (one
+//            wave, h in registers), the kept neurons' down rows, weight w_tj; the
+//            last slot to finish a (token, tile) sums the slots in slot order into
+//            Y (deterministic).
+#include "moe_impl.hpp"
 
 namespace as {
 
@@ -43,262 +42,36 @@ hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, f
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- grouping
-// The (token, slot) items routed to an expert, computed by every gate/up
-// workgroup for itself (at most 256 items and 1024 experts, so this is a few LDS
-// passes and cheaper than a launch of its own): the touched experts in ascending
-// order, the u-th of them, and its items in ascending item order (t * top + j).
-// Items with an id outside [0, E) are dropped (they contribute nothing).  Returns
-// the expert id, or -1 when fewer than u + 1 experts are touched.
-constexpr int kGuThreads = 256;
-
-__device__ __forceinline__ int gu_group(const MoeParams& p, int u, int* s_items, int* s_mark, int* s_scan,
-                                        int* cnt_out) {
-  __shared__ int s_e;
-  const int tid = threadIdx.x, E = p.E, n = p.T * p.top;
-  for (int e = tid; e < E; e += kGuThreads) s_mark[e] = 0;
-  if (tid == 0) s_e = -1;
-  __syncthreads();
-  int my = -1;
-  if (tid < n) {
-    my = p.ids[tid];
-    if (my < 0 || my >= E) my = -1;
-    if (my >= 0) s_mark[my] = 1;
-  }
-  __syncthreads();
-  // u-th touched expert: thread tid owns experts [tid * per, tid * per + per)
-  const int per = (E + kGuThreads - 1) / kGuThreads;
-  int c = 0;
-  for (int q = 0; q < per; ++q) {
-    const int e = tid * per + q;
-    if (e < E) c += s_mark[e];
-  }
-  int tot;
-  int off = block_excl_scan<kGuThreads>(c, s_scan, &tot);
-  if (u >= off && u < off + c) {
-    for (int q = 0; q < per; ++q) {
-      const int e = tid * per + q;
-      if (e < E && s_mark[e]) {
-        if (off == u) s_e = e;
-        ++off;
-      }
-    }
-  }
-  __syncthreads();
-  const int e = s_e;
-  if (e < 0) return -1;
-  const int flag = (my == e) ? 1 : 0;
-  int cnt;
-  const int pos = block_excl_scan<kGuThreads>(flag, s_scan, &cnt);
-  if (flag) s_items[pos] = tid;
-  __syncthreads();
-  *cnt_out = cnt;
-  return e;
-}
-
-constexpr int kGuTok = 4;   // tokens per pass
-
-// One or two tokens of an expert: the tokens' inputs stay in registers (lane l
-// holds inputs l*8 + 512 k .. +8, the columns its weight loads meet), so the
-// weight stream is not limited by LDS reads.  d_model <= 512 * NK, aligned rows.
-template <int WDT, int TK, int NK>
-__device__ __forceinline__ void expert_neurons_reg(const MoeParams& p, const uint16_t* W, const int* items, int g0,
-                                                   int ng, int n0, int n1) {
-  const int d = p.d_model, f = p.d_ff;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float xr[TK][NK][8];
-#pragma unroll
-  for (int m = 0; m < TK; ++m) {
-    const long row = (long)(items[g0 + (m < ng ? m : ng - 1)] / p.top) * p.ldx;
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      const int c = lane * 8 + k * 512;
-      load_chunk<8>(p.x, p.x_dt, row + (c < d ? c : 0), (m < ng && c < d) ? 8 : 0, xr[m][k]);
-    }
-  }
-  for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
-    const uint16_t* wg = W + (long)n * 2 * d;
-    const uint16_t* wu = wg + d;
-    u32x4 vg[NK], vu[NK];
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      const int c = min(lane * 8 + k * 512, d - 8);
-      vg[k] = load_w16<true>(wg + c);
-      vu[k] = load_w16<true>(wu + c);
-    }
-    float g[TK], uu[TK];
-#pragma unroll
-    for (int m = 0; m < TK; ++m) { g[m] = 0.f; uu[m] = 0.f; }
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      if (lane * 8 + k * 512 < d) {
-        float fg[8], fu[8];
-        unpack8<WDT>(vg[k], fg);
-        unpack8<WDT>(vu[k], fu);
-#pragma unroll
-        for (int m = 0; m < TK; ++m)
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            g[m] = fmaf(xr[m][k][q], fg[q], g[m]);
-            uu[m] = fmaf(xr[m][k][q], fu[q], uu[m]);
-          }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < TK; ++m) {
-      const float gs = wave_sum(g[m]);
-      const float us = wave_sum(uu[m]);
-      if (lane == 0 && m < ng) {
-        const int it = items[g0 + m];
-        const float h = silu_f32(gs) * us;
-        p.h[(long)it * f + n] = h;
-        if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
-      }
-    }
-  }
-}
-
-// NK > 0: groups of one or two tokens take the register path (d_model <= 512 NK).
+// ---------------------------------------------------------------- gate/up
 template <int WDT, int NK>
 __global__ __launch_bounds__(kGuThreads) void expert_gu_kernel(const MoeParams p) {
   extern __shared__ __align__(16) float xs[];   // [kGuTok][d]
-  __shared__ int s_items[256];
-  __shared__ int s_mark[1024];
-  __shared__ int s_gscan[kGuThreads / 64 + 1];
-  const int u = blockIdx.x;
-  int cnt = 0;
-  const int e = gu_group(p, u, s_items, s_mark, s_gscan, &cnt);
-  if (e < 0) return;
-  const int d = p.d_model, f = p.d_ff;
-  const int st = 0, en = cnt;
-  const int* items = s_items;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.y * p.neurons_per_block;
-  const int n1 = min(n0 + p.neurons_per_block, f);
-  const uint16_t* W = p.w_gu + (long)e * f * 2 * d;
-  for (int g0 = st; g0 < en; g0 += kGuTok) {
-    const int ng = min(kGuTok, en - g0);
-    if constexpr (NK > 0) {
-      if (ng <= 2) {
-        if (ng == 1) expert_neurons_reg<WDT, 1, NK>(p, W, items, g0, ng, n0, n1);
-        else expert_neurons_reg<WDT, 2, NK>(p, W, items, g0, ng, n0, n1);
-        continue;
-      }
-    }
-    __syncthreads();
-    if (p.x_vec) {
-      // 16-byte loads of the group's token rows, issued together, staged as fp32
-      const bool f32 = p.x_dt == DT_F32, bf = p.x_dt == DT_BF16;
-      const int per = f32 ? 4 : 8, nv = d / per, tot = kGuTok * nv;
-      for (int j0 = threadIdx.x; j0 < tot; j0 += 4 * kGuThreads) {
-        u32x4 raw[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = min(j0 + q * kGuThreads, tot - 1);
-          const int m = min(j / nv, ng - 1), vi = j % nv;
-          const long e0 = (long)(items[g0 + m] / p.top) * p.ldx + (long)vi * per;
-          raw[q] = f32 ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(p.x) + e0)
-                       : *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.x) + e0);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = j0 + q * kGuThreads;
-          if (j < tot) {
-            const int m = j / nv, vi = j % nv;
-            float4* dst = reinterpret_cast<float4*>(xs + m * d + vi * per);
-            const uint32_t w4[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
-            const bool live = m < ng;
-            if (f32) {
-              dst[0] = live ? make_float4(__uint_as_float(w4[0]), __uint_as_float(w4[1]), __uint_as_float(w4[2]),
-                                          __uint_as_float(w4[3]))
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-            } else {
-              float fv[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t hb = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
-                fv[e] = live ? (bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb)) : 0.f;
-              }
-              dst[0] = make_float4(fv[0], fv[1], fv[2], fv[3]);
-              dst[1] = make_float4(fv[4], fv[5], fv[6], fv[7]);
-            }
-          }
-        }
-      }
-    } else {
-      for (int i = threadIdx.x; i < kGuTok * d; i += kGuThreads) {
-        const int m = i / d, c = i % d;
-        float v = 0.f;
-        if (m < ng) v = load_elem(p.x, p.x_dt, (long)(items[g0 + m] / p.top) * p.ldx + c);
-        xs[i] = v;
-      }
-    }
-    __syncthreads();
-    for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
-      const uint16_t* wg = W + (long)n * 2 * d;
-      const uint16_t* wu = wg + d;
-      float g[kGuTok], uu[kGuTok];
-#pragma unroll
-      for (int m = 0; m < kGuTok; ++m) { g[m] = 0.f; uu[m] = 0.f; }
-      for (int c0 = lane * 8; c0 < d; c0 += 64 * 8 * 4) {
-        u32x4 vg[4], vu[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = min(c0 + k * 512, d - 8);
-          vg[k] = load_w16<true>(wg + c);
-          vu[k] = load_w16<true>(wu + c);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = c0 + k * 512;
-          if (c < d) {
-            float fg[8], fu[8];
-            unpack8<WDT>(vg[k], fg);
-            unpack8<WDT>(vu[k], fu);
-#pragma unroll
-            for (int m = 0; m < kGuTok; ++m) {
-              const float4 xa = *reinterpret_cast<const float4*>(xs + m * d + c);
-              const float4 xb = *reinterpret_cast<const float4*>(xs + m * d + c + 4);
-              const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-#pragma unroll
-              for (int q = 0; q < 8; ++q) {
-                g[m] = fmaf(xv[q], fg[q], g[m]);
-                uu[m] = fmaf(xv[q], fu[q], uu[m]);
-              }
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < kGuTok; ++m) {
-        const float gs = wave_sum(g[m]);
-        const float us = wave_sum(uu[m]);
-        if (lane == 0 && m < ng) {
-          const int it = items[g0 + m];
-          const float h = silu_f32(gs) * us;
-          p.h[(long)it * f + n] = h;
-          if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
-        }
-      }
-    }
-  }
+  expert_gu_block<WDT, NK>(p, blockIdx.x, blockIdx.y, xs);
 }
 
 // ---------------------------------------------------------------- down
 constexpr int kDnThreads = 256;
 constexpr int kDnLpr = 64;                 // one wave covers 512 columns of one row
 constexpr int kDnTile = kDnLpr * 8;
+static_assert(kDnTile % 256 == 0, "the combine takes whole columns per thread");
 
-// Workgroup copy of n floats to LDS, eight loads in flight per thread.
-__device__ __forceinline__ void copy_to_lds_f32(float* dst, const float* src, int n) {
-  for (int j = threadIdx.x; j < n; j += 8 * kDnThreads) {
-    float v[8];
+// Keep set of one item by one wave: h read straight into registers (one load per
+// lane and 64 neurons), the exact top-k of |h| (ties to the smaller index), the
+// kept indices and their h written to LDS in ascending index order.
+template <int KPL>
+__device__ __forceinline__ void down_keep_regs(const float* h, int f, int k, int* keep, float* kval, int* dbg) {
+  const int lane = threadIdx.x & 63;
+  float v[KPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[min(j + u * kDnThreads, n - 1)];
+  for (int q = 0; q < KPL; ++q) v[q] = h[min(q * 64 + lane, f - 1)];
+  uint32_t key[KPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (j + u * kDnThreads < n) dst[j + u * kDnThreads] = v[u];
-  }
+  for (int q = 0; q < KPL; ++q) key[q] = float_key(fabsf(v[q]));     // lanes past f: ignored
+  wave_topk_regs_emit<KPL>(key, f, k, [&](int pos, int q, int i) {
+    keep[pos] = i;
+    kval[pos] = v[q];
+    if (dbg != nullptr) dbg[pos] = i;
+  });
 }
 
 template <int WDT>
@@ -307,7 +80,7 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   int* keep = reinterpret_cast<int*>(smem);                        // [keep_k]
   float* kval = reinterpret_cast<float*>(smem + 4 * ((p.keep_k + 3) & ~3));
   float* red = kval + ((p.keep_k + 3) & ~3);                       // [4][kDnTile]
-  float* hs = red + 4 * kDnTile;                                   // [d_ff] this item's h
+  float* hs = red + 4 * kDnTile;                                   // [d_ff] when d_ff > 1024
   __shared__ TopkSmem sm;
   __shared__ int s_last;
   const int item = blockIdx.x;                  // t * top + j
@@ -317,29 +90,30 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   int e = p.ids[item];
   const bool valid_e = e >= 0 && e < p.E;
   if (!valid_e) e = 0;
-  const float* h = p.h + (long)item * f;
   const int kk = valid_e ? p.keep_k : 0;
-  copy_to_lds_f32(hs, h, f);
-  __syncthreads();
-  // the exact top-k of |h| by one wave over the staged row (no workgroup barriers
-  // inside the selection); the other waves wait at the barrier below
-  if (threadIdx.x < 64) {
-    if (f <= 64 * 16) {
-      uint32_t kr[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int i = q * 64 + threadIdx.x;
-        kr[q] = i < f ? float_key(fabsf(hs[i])) : 0u;
-      }
-      wave_topk_regs<16>(kr, f, kk, keep, sm);
-    } else {
+  // the item's keep set by wave 0 (every tile's workgroup selects the same set);
+  // an item with an invalid expert keeps nothing
+  int* dbg = (p.keep_dbg != nullptr && tile == 0) ? p.keep_dbg + (long)item * p.keep_k : nullptr;
+  if (threadIdx.x < 64 && kk > 0) {
+    const float* h = p.h + (long)item * f;
+    if (f <= 256) down_keep_regs<4>(h, f, kk, keep, kval, dbg);
+    else if (f <= 512) down_keep_regs<8>(h, f, kk, keep, kval, dbg);
+    else if (f <= 768) down_keep_regs<12>(h, f, kk, keep, kval, dbg);
+    else if (f <= 1024) down_keep_regs<16>(h, f, kk, keep, kval, dbg);
+    else {
+      // long rows: staged in LDS by this wave, radix selection over the copy
+      for (int i = threadIdx.x; i < f; i += 64) hs[i] = h[i];
+      __builtin_amdgcn_wave_barrier();
       wave_topk([=](int i) { return float_key(fabsf(hs[i])); }, f, kk, keep, sm);
+      __builtin_amdgcn_wave_barrier();
+      for (int r = threadIdx.x; r < kk; r += 64) {
+        kval[r] = hs[keep[r]];
+        if (dbg != nullptr) dbg[r] = keep[r];
+      }
     }
   }
-  __syncthreads();
-  for (int r = threadIdx.x; r < kk; r += kDnThreads) kval[r] = hs[keep[r]];
-  if (p.keep_dbg != nullptr && tile == 0)
-    for (int r = threadIdx.x; r < p.keep_k; r += kDnThreads) p.keep_dbg[(long)item * p.keep_k + r] = kk ? keep[r] : -1;
+  if (dbg != nullptr && !valid_e)
+    for (int r = threadIdx.x; r < p.keep_k; r += kDnThreads) dbg[r] = -1;
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -389,28 +163,52 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   __syncthreads();
   if (!s_last) return;
   (void)j;
-  for (int c = threadIdx.x; c < kDnTile; c += kDnThreads) {
-    const int gc = tile * kDnTile + c;
-    if (gc < d) {
-      float tmp[32];
-      const int top = p.top;
+  // both columns of a thread at once: the y values and eight slots' partials of
+  // each column are loaded before any is added (one round trip for eight slots)
+  constexpr int kCols = kDnTile / kDnThreads;
+  const int top = p.top;
+  int gcs[kCols];
+  float v[kCols], yv[kCols];
 #pragma unroll
-      for (int q = 0; q < 32; ++q)
-        tmp[q] = q < top ? load_coherent(p.partials + ((long)t * top + q) * d + gc) : 0.f;
-      float v = 0.f;
-      for (int q = 0; q < top; ++q) v += tmp[q];
-      if (p.accumulate) v += load_elem(p.y, p.y_dt, (long)t * d + gc);
-      store_elem(p.y, p.y_dt, (long)t * d + gc, v);
-    }
+  for (int u = 0; u < kCols; ++u) {
+    gcs[u] = tile * kDnTile + threadIdx.x + u * kDnThreads;
+    v[u] = 0.f;
+    yv[u] = p.accumulate ? load_elem(p.y, p.y_dt, (long)t * d + (gcs[u] < d ? gcs[u] : 0)) : 0.f;
   }
+  for (int q0 = 0; q0 < top; q0 += 8) {
+    // unconditional loads: slots past top re-read the last slot, columns past d
+    // read column 0; both are dropped below
+    float tmp[kCols][8];
+#pragma unroll
+    for (int u = 0; u < kCols; ++u)
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq)
+        tmp[u][qq] = load_coherent(p.partials + ((long)t * top + min(q0 + qq, top - 1)) * d +
+                                   (gcs[u] < d ? gcs[u] : 0));
+#pragma unroll
+    for (int u = 0; u < kCols; ++u)
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq)
+        if (q0 + qq < top && gcs[u] < d) v[u] += tmp[u][qq];      // slot order
+  }
+#pragma unroll
+  for (int u = 0; u < kCols; ++u)
+    if (gcs[u] < d) store_elem(p.y, p.y_dt, (long)t * d + gcs[u], p.accumulate ? v[u] + yv[u] : v[u]);
+}
+
+hipError_t launch_moe_down(int wdt, const MoeParams& p, hipStream_t s) {
+  const size_t sm2 = size_t(8) * ((p.keep_k + 3) & ~3) + size_t(4) * kDnTile * 4 +
+                     (p.d_ff > 1024 ? size_t(p.d_ff) * 4 : 0);
+  auto k2 = wdt == DT_BF16 ? expert_down_kernel<DT_BF16> : expert_down_kernel<DT_F16>;
+  hipLaunchKernelGGL(k2, dim3(p.T * p.top, p.n_tiles), dim3(kDnThreads), sm2, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s) {
   hipError_t e;
-  const int nblk = (p.d_ff + p.neurons_per_block - 1) / p.neurons_per_block;
-  const size_t sm1 = size_t(kGuTok) * p.d_model * 4;
-  const int d = p.d_model;
-  const int nk = (!p.x_vec || d > 4096) ? 0 : d <= 512 ? 1 : d <= 1024 ? 2 : d <= 2048 ? 4 : 8;
+  const int nblk = moe_gu_blocks(p);
+  const size_t sm1 = moe_gu_smem(p);
+  const int nk = moe_gu_nk(p);
   auto pick = [&](auto kb, auto kf) { return wdt == DT_BF16 ? kb : kf; };
   auto k1 = nk == 0   ? pick(expert_gu_kernel<DT_BF16, 0>, expert_gu_kernel<DT_F16, 0>)
             : nk == 1 ? pick(expert_gu_kernel<DT_BF16, 1>, expert_gu_kernel<DT_F16, 1>)
@@ -426,12 +224,53 @@ hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_
   // only the down stage touches Y: the producer of Y (another stream) need not be
   // done before the grouping and the gate/up stage
   if (y_ready != nullptr && (e = hipStreamWaitEvent(s, y_ready, 0)) != hipSuccess) return e;
-  const size_t sm2 = size_t(8) * ((p.keep_k + 3) & ~3) + size_t(4) * kDnTile * 4 + size_t(p.d_ff) * 4;
-  auto k2 = wdt == DT_BF16 ? expert_down_kernel<DT_BF16> : expert_down_kernel<DT_F16>;
-  hipLaunchKernelGGL(k2, dim3(p.T * p.top, p.n_tiles), dim3(kDnThreads), sm2, s, p);
-  return hipGetLastError();
+  return launch_moe_down(wdt, p, s);
 }
 
 int moe_down_tiles(int d_model) { return (d_model + kDnTile - 1) / kDnTile; }
+int moe_gu_nk_of(const MoeParams& p) { return moe_gu_nk(p); }
+int moe_gu_blocks_of(const MoeParams& p) { return moe_gu_blocks(p); }
+size_t moe_gu_smem_of(const MoeParams& p) { return moe_gu_smem(p); }
+
+// ---------------------------------------------------------------- one-stream layer
+// The combined launches are instantiated per token tile in moe_layer_bf16_m*.hip.
+#define AS_MOE_LAYER_DECL(MT)                                                                            \
+  hipError_t launch_moe_route_gu_m##MT(const MoeLayerCfg&, const GemvParams&, const GemvParams&, size_t, \
+                                       hipStream_t);                                                     \
+  hipError_t launch_moe_gu_down_m##MT(const MoeLayerCfg&, const MoeParams&, int, int, const GemvParams&, \
+                                      size_t, hipStream_t);
+AS_MOE_LAYER_DECL(1)
+AS_MOE_LAYER_DECL(2)
+AS_MOE_LAYER_DECL(4)
+AS_MOE_LAYER_DECL(8)
+#undef AS_MOE_LAYER_DECL
+
+bool moe_layer_supported(const MoeLayerCfg& c) {
+  return c.wdt == DT_BF16 && (c.mt == 1 || c.mt == 2 || c.mt == 4 || c.mt == 8) &&
+         (c.lpr_r == 16 || c.lpr_r == 32 || c.lpr_r == 64) && (c.lpr_g == 32 || c.lpr_g == 64) &&
+         (c.lpr_d == 16 || c.lpr_d == 64) && (c.nk == 0 || c.nk == 1 || c.nk == 2 || c.nk == 4 || c.nk == 8);
+}
+
+hipError_t launch_moe_route_gu(const MoeLayerCfg& c, const GemvParams& pr, const GemvParams& pg, size_t smem,
+                               hipStream_t s) {
+  if (!moe_layer_supported(c)) return hipErrorInvalidValue;
+  switch (c.mt) {
+    case 1: return launch_moe_route_gu_m1(c, pr, pg, smem, s);
+    case 2: return launch_moe_route_gu_m2(c, pr, pg, smem, s);
+    case 4: return launch_moe_route_gu_m4(c, pr, pg, smem, s);
+    default: return launch_moe_route_gu_m8(c, pr, pg, smem, s);
+  }
+}
+
+hipError_t launch_moe_gu_down(const MoeLayerCfg& c, const MoeParams& pm, int n_u, int n_gu, const GemvParams& pd,
+                              size_t smem, hipStream_t s) {
+  if (!moe_layer_supported(c)) return hipErrorInvalidValue;
+  switch (c.mt) {
+    case 1: return launch_moe_gu_down_m1(c, pm, n_u, n_gu, pd, smem, s);
+    case 2: return launch_moe_gu_down_m2(c, pm, n_u, n_gu, pd, smem, s);
+    case 4: return launch_moe_gu_down_m4(c, pm, n_u, n_gu, pd, smem, s);
+    default: return launch_moe_gu_down_m8(c, pm, n_u, n_gu, pd, smem, s);
+  }
+}
 
 }  // namespace as

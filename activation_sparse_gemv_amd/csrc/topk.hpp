@@ -168,59 +168,116 @@ __device__ void wave_topk(KeyFn key, int n, int k, int* idx, TopkSmem& sm) {
 }
 
 // The same selection by one wave with the keys in registers: key[q] is the key of
-// index q * 64 + lane (n <= 64 * KPL; lanes past n hold anything).  Each radix pass
-// issues the lane's histogram atomics back to back (no LDS reads of the keys), and
-// the final pass walks the 64-index chunks in order with ballots.  Writes idx[0..k)
-// ascending.  Called by the 64 threads of one wave.
-template <int KPL>
-__device__ void wave_topk_regs(const uint32_t (&key)[KPL], int n, int k, int* idx, TopkSmem& sm) {
+// index q * 64 + lane (n <= 64 * KPL; lanes past n hold anything).  The k-th
+// largest key T is bracketed: at least k keys are >= a, fewer than k are >= b.
+// Each step counts the keys >= a candidate c in (a, b) (one ballot per 64 keys, no
+// LDS or memory) and moves a or b to c.  Candidates alternate between a guess
+// interpolated from the two counts and the midpoint, so the search takes at most
+// twice the steps of bisection over 32 bits and, on smooth score distributions,
+// far fewer.  When exactly k keys are >= a candidate, T is the smallest of them
+// and the kept keys are those >= T; otherwise (ties at T) the final pass walks the
+// 64-index chunks in order with ballots (keys above T, then the first keys equal
+// to T).  Either pass calls emit(pos, q, i) for the pos-th
+// selected index i = q * 64 + lane, in ascending order of i.  Called by the 64
+// threads of one wave (a single wave issues one instruction per four cycles, so
+// the steps are kept short and branch-free).
+template <int KPL, class Emit>
+__device__ void wave_topk_regs_emit(const uint32_t (&key_in)[KPL], int n, int k, Emit emit) {
   const int lane = threadIdx.x & 63;
   if (k > n) k = n;
   if (k <= 0) return;
   const bool all = k >= n;
+  // lanes past n take key 0, which no candidate of the search counts (all are >= 1)
+  // and no count of keys above T includes, so the counting loops need no bounds
+  uint32_t key[KPL];
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) key[q] = q * 64 + lane < n ? key_in[q] : 0u;
   uint32_t T = 0u;
   int take_eq = 0;
   if (!all) {
-    uint32_t prefix = 0u;
-    int krem = k;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
-      for (int b = lane; b < 256; b += 64) sm.hist[b] = 0u;
-      __builtin_amdgcn_wave_barrier();
+    uint32_t mx = 0u;
 #pragma unroll
-      for (int q = 0; q < KPL; ++q)
-        if (q * 64 + lane < n && (key[q] & hi_mask) == prefix) atomicAdd(&sm.hist[(key[q] >> shift) & 0xffu], 1u);
-      __builtin_amdgcn_wave_barrier();
-      wave_select_bin(sm.hist, krem, true, &sm.sel_bin, &sm.sel_krem);
-      __builtin_amdgcn_wave_barrier();
-      prefix |= (uint32_t)sm.sel_bin << shift;
-      krem = sm.sel_krem;
-      __builtin_amdgcn_wave_barrier();
+    for (int q = 0; q < KPL; ++q) mx = key[q] > mx ? key[q] : mx;
+    // the largest key is at most that of +inf (0xff800000), so b does not wrap
+    uint32_t a = 0u, b = wave_max_u32(mx) + 1u;
+    int ca = n, cb = 0;                         // keys >= a, keys >= b
+    bool exact = false;
+    for (int it = 0; it < 72; ++it) {           // bisection every other step: w <= 1 before 72
+      const uint32_t w = b - a;
+      if (w <= 1u) break;
+      uint32_t off;
+      if (it & 1) {
+        off = w >> 1;
+      } else {
+        const float fr = __fdividef((float)(ca - k), (float)(ca - cb));
+        off = (uint32_t)((float)w * fr);
+        off = off < 1u ? 1u : (off > w - 1u ? w - 1u : off);
+      }
+      const uint32_t c = a + off;
+      // per-lane counts (VALU only), then one wave sum (exact: at most 1024 in fp32)
+      int lc = 0;
+#pragma unroll
+      for (int q = 0; q < KPL; ++q) lc += key[q] >= c ? 1 : 0;
+      const int cnt = (int)wave_sum((float)lc);
+      if (cnt >= k) {
+        a = c;
+        ca = cnt;
+        if (cnt == k) {
+          exact = true;
+          break;
+        }
+      } else {
+        b = c;
+        cb = cnt;
+      }
     }
-    T = prefix;
-    take_eq = krem;
+    if (exact) {
+      uint32_t m = 0xffffffffu;
+#pragma unroll
+      for (int q = 0; q < KPL; ++q) m = (key[q] >= a && key[q] < m) ? key[q] : m;
+      T = wave_min_u32(m);
+    } else {
+      T = a;                                    // b = a + 1: a is the k-th largest key
+    }
+    int gt = 0;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) gt += __popcll(__ballot(key[q] > T));
+    take_eq = k - gt;
+    // an exact count (k keys >= T) keeps every key equal to T: a plain threshold
+    if (exact) {
+      int run = 0;
+#pragma unroll
+      for (int q = 0; q < KPL; ++q) {
+        const bool sel = key[q] >= T;                // lanes past n hold 0 < T
+        const uint64_t sb = __ballot(sel);
+        if (sel) emit(run + lanes_below(sb), q, q * 64 + lane);
+        run += __popcll(sb);
+      }
+      return;
+    }
   }
   int run_eq = 0, run_sel = 0;
 #pragma unroll
   for (int q = 0; q < KPL; ++q) {
-    if (q * 64 >= n) break;
-    const int i = q * 64 + lane;
-    bool sel = false, eq = false;
-    if (i < n) {
-      if (all) sel = true;
-      else {
-        sel = key[q] > T;
-        eq = key[q] == T;
-      }
-    }
+    const bool valid = q * 64 + lane < n;
+    bool sel = valid && (all || key[q] > T);
+    const bool eq = valid && !all && key[q] == T;
     const uint64_t eqb = __ballot(eq);
     if (eq && run_eq + lanes_below(eqb) < take_eq) sel = true;
     run_eq += __popcll(eqb);
     const uint64_t sb = __ballot(sel);
-    if (sel && idx != nullptr) idx[run_sel + lanes_below(sb)] = i;
+    if (sel) emit(run_sel + lanes_below(sb), q, q * 64 + lane);
     run_sel += __popcll(sb);
   }
+}
+
+// The selection above writing idx[0..k) (ascending indices).  `sm` is not used.
+template <int KPL>
+__device__ __forceinline__ void wave_topk_regs(const uint32_t (&key)[KPL], int n, int k, int* idx, TopkSmem& sm) {
+  (void)sm;
+  wave_topk_regs_emit<KPL>(key, n, k, [&](int pos, int, int i) {
+    if (idx != nullptr) idx[pos] = i;
+  });
 }
 
 // Routing of one token by one wave (intra-expert summary, system implementation:
@@ -232,13 +289,21 @@ __device__ void wave_topk_regs(const uint32_t (&key)[KPL], int n, int k, int* id
 __device__ __forceinline__ void route_token(const float* z, int E, int top, int* ids, float* wts, int* sel,
                                             TopkSmem& sm) {
   const int lane = threadIdx.x & 63;
-  if (E <= 64 * 4) {
+  if (E <= 64 * 2) {
+    uint32_t kr[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) kr[q] = float_key(z[min(q * 64 + lane, E - 1)]);
+    wave_topk_regs<2>(kr, E, top, sel, sm);
+  } else if (E <= 64 * 4) {
     uint32_t kr[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) kr[q] = q * 64 + lane < E ? float_key(z[q * 64 + lane]) : 0u;
+    for (int q = 0; q < 4; ++q) kr[q] = float_key(z[min(q * 64 + lane, E - 1)]);
     wave_topk_regs<4>(kr, E, top, sel, sm);
   } else {
-    wave_topk([=](int i) { return float_key(z[i]); }, E, top, sel, sm);
+    uint32_t kr[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) kr[q] = float_key(z[min(q * 64 + lane, E - 1)]);
+    wave_topk_regs<16>(kr, E, top, sel, sm);
   }
   __builtin_amdgcn_wave_barrier();
   // lane a < top holds selection a; its rank in (logit desc, index asc) order
@@ -247,15 +312,15 @@ __device__ __forceinline__ void route_token(const float* z, int E, int top, int*
   if (lane < top) {
     me = sel[lane];
     km = float_key(z[me]);
-    for (int b = 0; b < top; ++b) {
-      const int ob = sel[b];
-      const uint32_t kb = float_key(z[ob]);
-      rank += (kb > km) || (kb == km && ob < me);
-    }
+  }
+  // the other selections' (index, key) from their lanes by readlane (no LDS)
+  for (int b = 0; b < top; ++b) {
+    const int ob = __builtin_amdgcn_readlane(me, b);
+    const uint32_t kb = (uint32_t)__builtin_amdgcn_readlane((int)km, b);
+    rank += (kb > km) || (kb == km && ob < me);
   }
   float m = lane < top ? z[me] : -INFINITY;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  m = wave_max(m);
   const float ev = lane < top ? expf(z[me] - m) : 0.f;
   const float sum = wave_sum(ev);
   if (lane < top) {

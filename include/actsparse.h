@@ -274,6 +274,47 @@ as_status as_sparse_moe_expert(const void *X, as_dtype x_dt, int T,
                                float *h_dbg, int32_t *keep_dbg, hipEvent_t y_ready,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* One MoE layer for up to 8 tokens on `stream` alone, in three launches
+ * (intra-expert summary, system implementation: the router and the shared expert
+ * are unchanged; the routed experts score their neurons densely and read only the
+ * kept neurons' down rows):
+ *   logits = X Wr;  (ids, weights) = the routing of as_moe_router;
+ *   Y = dense shared-expert SwiGLU MLP of X
+ *       + sum_j weights[t, j] * expert_{ids[t, j]}(X[t]) with the exact top keep_k
+ *         neurons of each (token, slot), as in as_sparse_moe_expert.
+ * Launch 1 runs the router logits GEMV (its last workgroup routes every token)
+ * beside the shared expert's gate/up; launch 2 the routed experts' gate/up beside
+ * the shared expert's down projection (which writes Y); launch 3 the routed down
+ * stage, added onto Y.  No piece waits on another stream.  logits, ids, weights,
+ * h and the keep sets are the bits of as_moe_router_gemv and as_sparse_moe_expert;
+ * Y is the composition with as_sparse_swiglu_mlp (AS_FLAG_FORCE_DENSE, gate/up
+ * partials summed in the down stage) up to the split of the shared expert's down
+ * stage, which here takes one row range per CU and column tile (another fp32
+ * summation order of the same terms).
+ * X: [T, d_model] (f16/bf16/f32).  Y: [T, d_model] fp32.  logits: [T, E] fp32,
+ * ids: [T, top_k] int32, weights: [T, top_k] fp32 (outputs, device).
+ * h_dbg [T * top_k, d_ff_e] and keep_dbg [T * top_k, keep_k]: optional, as in
+ * as_sparse_moe_expert.  flags: AS_FLAG_FORCE_DENSE (every routed neuron kept);
+ * any other flag is AS_ERR_UNSUPPORTED.
+ * Weights: bf16 throughout; w_router [d_model, E] input-major, 16-byte aligned;
+ * the shared expert in THRESHOLD layout with the experts' d_model.
+ * Limits: 1 <= T <= 8, E % 8 == 0, 8 <= E <= 512, 1 <= top_k <= min(32, E),
+ * T * top_k <= 256, d_ff_e <= 8192.  as_moe_layer_ws_size returns 0 where the
+ * shapes are outside these limits (then use the separate entry points);
+ * as_moe_layer returns AS_ERR_UNSUPPORTED there. */
+typedef struct {
+  const void *w_router;   /* [d_model, E] input-major */
+  as_moe_weights experts; /* routed experts */
+  as_mlp_weights shared;  /* shared expert, THRESHOLD layout, used densely */
+} as_moe_layer_weights;
+
+size_t as_moe_layer_ws_size(int T, int top_k, const as_moe_layer_weights *w);
+as_status as_moe_layer(const void *X, as_dtype x_dt, int T, const as_moe_layer_weights *w,
+                       int top_k, int keep_k, float *Y, unsigned flags,
+                       float *logits, int32_t *ids, float *weights,
+                       float *h_dbg, int32_t *keep_dbg,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------ decoder-block glue
  * TEAL slides, method slide: every projection input of the attention and MLP
  * blocks is thresholded; the attention core stays dense.  Readings (the pages

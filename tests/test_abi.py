@@ -154,3 +154,34 @@ def test_binding_refuses_cpu_tensors():
     from activation_sparse_gemv_amd import api
     with pytest.raises(ValueError, match="device tensors"):
         api.as_threshold_gemv(torch.zeros(64, dtype=torch.bfloat16), torch.zeros(64, 64, dtype=torch.bfloat16), 0.5)
+
+
+def test_moe_layer_limits_and_validation(lib):
+    """as_moe_layer: the one-stream layer's shape limits (workspace size 0 outside
+    them) and its argument checks, all returned before any launch."""
+    mw = L.ASMoeWeights(_p(), _p(), L.AS_BF16, 128, 2048, 768)
+    sw = L.ASMlpWeights(_p(), _p(), L.AS_BF16, 2048, 4096)
+    lw = L.ASMoeLayerWeights(_p(), mw, sw)
+    for T in (1, 2, 3, 4, 8):
+        assert lib.as_moe_layer_ws_size(T, 8, ctypes.byref(lw)) > 0
+    nb = lib.as_moe_layer_ws_size(1, 8, ctypes.byref(lw))
+    assert lib.as_moe_layer_ws_size(9, 8, ctypes.byref(lw)) == 0                 # more than 8 tokens
+    assert lib.as_moe_layer_ws_size(1, 33, ctypes.byref(lw)) == 0                # top_k above 32
+    bad = [L.ASMoeLayerWeights(_p(), L.ASMoeWeights(_p(), _p(), L.AS_BF16, 100, 2048, 768), sw),   # E % 8
+           L.ASMoeLayerWeights(_p(), L.ASMoeWeights(_p(), _p(), L.AS_BF16, 1024, 2048, 768), sw),  # E > 512
+           L.ASMoeLayerWeights(_p(), L.ASMoeWeights(_p(), _p(), L.AS_F16, 128, 2048, 768),
+                               L.ASMlpWeights(_p(), _p(), L.AS_F16, 2048, 4096)),                 # fp16
+           L.ASMoeLayerWeights(_p(), mw, L.ASMlpWeights(_p(), _p(), L.AS_BF16, 1024, 4096))]      # d_model
+    for b in bad:
+        assert lib.as_moe_layer_ws_size(1, 8, ctypes.byref(b)) == 0
+
+    def call(T=1, top=8, keep=77, flags=0, ws_bytes=1 << 30, logits=_p(), w=lw):
+        return lib.as_moe_layer(_p(), L.AS_BF16, T, ctypes.byref(w), top, keep, _p(), flags, logits, _p(), _p(),
+                                None, None, _p(), ws_bytes, None)
+    assert call(T=9) == L.AS_ERR_UNSUPPORTED
+    assert call(w=bad[0]) == L.AS_ERR_UNSUPPORTED
+    assert call(keep=800) == L.AS_ERR_INVALID_ARG                 # keep_k > d_ff_e
+    assert call(top=0) == L.AS_ERR_INVALID_ARG
+    assert call(flags=L.AS_FLAG_NO_NT_LOADS) == L.AS_ERR_UNSUPPORTED
+    assert call(logits=None) == L.AS_ERR_INVALID_ARG
+    assert call(ws_bytes=nb - 1) == L.AS_ERR_WORKSPACE

@@ -64,14 +64,34 @@ def test_graph_moe_layer_with_side_stream():
     dw = asg.MoEWeights(w["w_gate_up"].to(DEV), w["w_down"].to(DEV), w["w_router"].to(DEV),
                         asg.MLPWeights(w["s_gate_up"].to(DEV), w["s_down"].to(DEV)))
     X = datagen.student_t((2, 512), 12).to(DEV)
-    eager = asg.moe_layer(X, dw, 4, 26).clone()
-    serial = asg.moe_layer(X, dw, 4, 26, overlap=False)
+    eager = asg.moe_layer(X, dw, 4, 26, one_stream=False).clone()
+    serial = asg.moe_layer(X, dw, 4, 26, overlap=False, one_stream=False)
     torch.cuda.synchronize()
     assert torch.equal(eager, serial)
-    g, out = _capture(lambda: asg.moe_layer(X, dw, 4, 26))
+    g, out = _capture(lambda: asg.moe_layer(X, dw, 4, 26, one_stream=False))
     for rep in range(4):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), rep
-        asg.moe_layer(X, dw, 4, 13)
+        asg.moe_layer(X, dw, 4, 13, one_stream=False)
+        torch.cuda.synchronize()
+
+
+def test_graph_moe_layer_one_stream():
+    """The one-stream MoE layer (as_moe_layer) captured and replayed, with eager calls
+    of other keep counts between the replays: every replay equals the eager call."""
+    announce("graph moe layer one stream")
+    w = datagen.moe_weights(5, 3, n_experts=16, d_model=512, d_ff_e=256, d_ff_shared=1024)
+    dw = asg.MoEWeights(w["w_gate_up"].to(DEV), w["w_down"].to(DEV), w["w_router"].to(DEV),
+                        asg.MLPWeights(w["s_gate_up"].to(DEV), w["s_down"].to(DEV)))
+    X = datagen.student_t((2, 512), 12).to(DEV)
+    eager = asg.as_moe_layer(X, dw, 4, 26).clone()
+    torch.cuda.synchronize()
+    g, out = _capture(lambda: asg.as_moe_layer(X, dw, 4, 26))
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        asg.as_moe_layer(X, dw, 4, 13)
+        asg.moe_layer(X, dw, 4, 26, one_stream=False)
         torch.cuda.synchronize()

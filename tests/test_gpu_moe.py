@@ -137,3 +137,123 @@ def test_router_gemv_fused(T, E, top):
         ref_ids, ref_w, _ = moe.router(f64(logits[t]), eye, top)     # the oracle router on these logits
         assert ids[t].cpu().numpy().tolist() == ref_ids.tolist()
         assert rel_err(wts[t], ref_w) < 1e-5
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+@pytest.mark.parametrize("dense", [0, 1])
+def test_moe_layer_one_stream_equals_composition(T, dense, monkeypatch):
+    """as_moe_layer (three launches on one stream, independent pieces side by side in
+    one launch) gives the bits of the layer composed from the separate entry points
+    (router GEMV with routing, dense shared MLP whose down stage sums the gate/up
+    partials, routed experts accumulated), intermediates included, when the composed
+    shared MLP takes the layer's split of its down stage (one row range per CU and
+    column tile: 2048 columns in tiles of 128)."""
+    monkeypatch.setenv("AS_DN_PARTS", "1")
+    monkeypatch.setenv("AS_DN_S", str(torch.cuda.get_device_properties(0).multi_processor_count // 16))
+    announce(f"moe one-stream T={T} dense={dense}")
+    c = datagen.CFG5
+    w, dw = _weights(c["n_experts"], c["d_model"], c["d_ff_e"], c["d_ff_shared"])
+    X = datagen.student_t((T, c["d_model"]), datagen.seed_for(5, T, "decode")).to(DEV)
+    flags = L.AS_FLAG_FORCE_DENSE if dense else 0
+    assert asg.api.moe_layer_one_stream_ok(X, dw, c["top"], flags)
+    Y1, d1 = asg.as_moe_layer(X, dw, c["top"], c["keep"], flags=flags, debug=True)
+    Y2, d2 = asg.moe_layer(X, dw, c["top"], c["keep"], flags=flags, debug=True, one_stream=False)
+    torch.cuda.synchronize()
+    for k in ("logits", "ids", "wts", "h"):
+        assert torch.equal(d1[k], d2[k]), k
+    if not dense:
+        assert torch.equal(d1["keep"], d2["keep"])
+    assert torch.equal(Y1, Y2)
+    Y3 = asg.as_moe_layer(X, dw, c["top"], c["keep"], flags=flags)     # workspace reuse
+    assert torch.equal(Y3, Y1)
+
+
+def test_moe_layer_one_stream_small_shapes():
+    """Odd shapes through the one-stream layer against the oracle (E = 8, d_model 64,
+    d_ff_e 48, shared d_ff 128; unaligned token rows take the LDS staging path)."""
+    E, d, f, fs = 8, 64, 48, 128
+    w, dw = _weights(E, d, f, fs)
+    for T, top, keep in ((1, 2, 5), (3, 3, 1), (8, 8, 48), (5, 1, 0)):
+        announce(f"moe one-stream small T={T} top={top} keep={keep}")
+        X = datagen.student_t((T, d), 300 + T)
+        assert asg.api.moe_layer_one_stream_ok(X.to(DEV), dw, top)
+        Y, dbg = asg.as_moe_layer(X.to(DEV), dw, top, keep, debug=True)
+        ref, _ = moe.moe_layer(f64(X), {k: f64(v) for k, v in w.items()}, top, keep)
+        # the oracle's own routing and keep sets could differ from the GPU's on a near
+        # tie; these seeds have none, so the whole layer is compared
+        assert rel_err(Y, ref) < TOL
+        # unaligned rows (one-element offset into a larger buffer)
+        Xb = torch.zeros((T * d + 1,), dtype=X.dtype)
+        Xb[1:] = X.reshape(-1)
+        Xu = Xb.to(DEV)[1:].view(T, d)
+        Yu = asg.as_moe_layer(Xu, dw, top, keep)
+        assert torch.equal(Yu, Y)
+
+
+def _router_ref(lg_t, top):
+    """Oracle routing of one token's logits: ids in (logit desc, index asc) order, NaN last."""
+    v = lg_t.astype(np.float64)
+    sel = topk.value_topk(v, top)
+    nan = np.isnan(v[sel])
+    return sel[np.lexsort((sel, np.where(nan, 0.0, -v[sel]), nan))]
+
+
+@pytest.mark.parametrize("E,top", [(128, 8), (256, 64), (512, 16), (1024, 8), (8, 8), (100, 7), (960, 33)])
+def test_router_ties_and_special_values(E, top):
+    """Exact routing (register top-k of the router) under heavy ties, +-0, NaN and
+    infinities: ids equal the oracle's selection and order; weights where finite."""
+    announce(f"router ties E={E} top={top}")
+    rng = np.random.default_rng(E * 100 + top)
+    T = 7
+    lg = rng.integers(-3, 4, size=(T, E)).astype(np.float32)              # few values: ties
+    lg[1] = 0.0
+    lg[1, ::3] = -0.0                                                     # all equal, both zeros
+    lg[2] = rng.standard_normal(E).astype(np.float32)
+    lg[2, min(5, E - 1)] = np.nan
+    lg[2, min(6, E - 1)] = np.inf
+    lg[2, min(3, E - 1)] = -np.inf
+    lg[3] = -np.inf
+    lg[3, E // 2] = np.nan                                                # NaN ranks below -inf
+    lg[4] = 1.0
+    lg[4, E - 1] = np.nextafter(np.float32(1.0), np.float32(2.0))
+    lg[5] = rng.standard_normal(E).astype(np.float32)
+    lg[6] = np.round(rng.standard_normal(E) * 4).astype(np.float32) / 4
+    ids, wts = asg.as_moe_router(torch.from_numpy(lg).to(DEV), top)
+    ids = ids.cpu().numpy()
+    wts = f64(wts)
+    for t in range(T):
+        ref = _router_ref(lg[t], top)
+        assert ids[t].tolist() == ref.tolist(), t
+        z = lg[t][ref].astype(np.float64)
+        if np.all(np.isfinite(z)):
+            p = np.exp(z - z.max())
+            np.testing.assert_allclose(wts[t], p / p.sum(), rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("f,keep", [(300, 37), (768, 77), (1024, 500), (1100, 90)])
+def test_expert_keep_sets_under_ties(f, keep):
+    """Routed experts whose neurons repeat in a period of 5 (and every 7th neuron all
+    zero, giving h = +-0): massive ties in |h|, which the keep sets must break toward
+    the smaller neuron index, exactly as the oracle's top-k on the GPU's h."""
+    announce(f"expert ties f={f} keep={keep}")
+    E, d, T, top = 8, 64, 3, 2
+    w = datagen.moe_weights(5, 9, n_experts=E, d_model=d, d_ff_e=f, d_ff_shared=128)
+    gu = w["w_gate_up"].clone()
+    gu[:, :, :, :] = gu[:, torch.arange(f) % 5, :, :]
+    gu[:, ::7, :, :] = 0
+    dw = asg.MoEWeights(gu.to(DEV), w["w_down"].to(DEV), w["w_router"].to(DEV),
+                        asg.MLPWeights(w["s_gate_up"].to(DEV), w["s_down"].to(DEV)))
+    X = datagen.student_t((T, d), 77).to(DEV)
+    ids = torch.tensor([[0, 3], [3, 5], [7, 0]], dtype=torch.int32, device=DEV)
+    wts = torch.tensor([[0.6, 0.4], [0.5, 0.5], [0.9, 0.1]], dtype=torch.float32, device=DEV)
+    Y, dbg = asg.as_sparse_moe_expert(X, dw, ids, wts, keep, debug=True)
+    h = f64(dbg["h"])
+    kp = dbg["keep"].cpu().numpy()
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(top):
+            e = int(ids[t, j])
+            kidx = topk.value_topk(np.abs(h[t, j]), keep)
+            assert kp[t, j, :keep].tolist() == kidx.tolist(), (t, j)
+            ref[t] += float(wts[t, j]) * (h[t, j][kidx] @ f64(w["w_down"][e])[kidx])
+    assert rel_err(Y, ref) < TOL
