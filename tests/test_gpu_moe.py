@@ -26,8 +26,8 @@ def _weights(E, d, f, fs):
     return _W[key]
 
 
-def _check_layer(E, d, f, fs, T, top, keep, seed):
-    w, dw = _weights(E, d, f, fs)
+def _check_layer(E, d, f, fs, T, top, keep, seed, weights=None):
+    w, dw = weights if weights is not None else _weights(E, d, f, fs)
     X = datagen.student_t((T, d), seed)
     Y, dbg = asg.moe_layer(X.to(DEV), dw, top, keep, debug=True)
     Xd = f64(X)
@@ -257,3 +257,22 @@ def test_expert_keep_sets_under_ties(f, keep):
             assert kp[t, j, :keep].tolist() == kidx.tolist(), (t, j)
             ref[t] += float(wts[t, j]) * (h[t, j][kidx] @ f64(w["w_down"][e])[kidx])
     assert rel_err(Y, ref) < TOL
+
+
+def test_moe_layer_fp16_and_composed_paths():
+    """fp16 weights (outside the one-stream layer's bf16 instantiations) and 12 tokens
+    (above its 8) take the composed path; both still match the oracle layer, and the
+    binding reports which path a call takes."""
+    E, d, f, fs = 16, 256, 96, 256
+    w = datagen.moe_weights(5, 11, n_experts=E, d_model=d, d_ff_e=f, d_ff_shared=fs, dtype="f16")
+    dw = asg.MoEWeights(w["w_gate_up"].to(DEV), w["w_down"].to(DEV), w["w_router"].to(DEV),
+                        asg.MLPWeights(w["s_gate_up"].to(DEV), w["s_down"].to(DEV)))
+    wb = datagen.moe_weights(5, 11, n_experts=E, d_model=d, d_ff_e=f, d_ff_shared=fs)
+    dwb = asg.MoEWeights(wb["w_gate_up"].to(DEV), wb["w_down"].to(DEV), wb["w_router"].to(DEV),
+                         asg.MLPWeights(wb["s_gate_up"].to(DEV), wb["s_down"].to(DEV)))
+    for T, ww, src, one in ((3, dw, w, False), (12, dwb, wb, False), (3, dwb, wb, True)):
+        announce(f"moe paths T={T} one_stream={one}")
+        X = datagen.student_t((T, d), 500 + T)
+        assert asg.api.moe_layer_one_stream_ok(X.to(DEV), ww, 4) == one
+        # stage by stage against the oracle (selections on the GPU's logits and h)
+        _check_layer(E, d, f, fs, T, 4, 20, 500 + T, weights=(src, ww))
