@@ -118,6 +118,10 @@ struct MoeParams {
   float* h; float* h_dbg; int* keep_dbg; float* partials; unsigned* counters; int n_tiles;
   void* y; int y_dt; int accumulate; int neurons_per_block;
   int x_vec;               // token rows 16-byte aligned (vector staging of x)
+  // keep sets chosen at the end of the gate/up stage (keep != nullptr, d_ff <= 1024):
+  // finished neuron blocks per touched expert [256], kept indices and their h
+  // [T * top][keep_k]; else the down stage selects them itself
+  unsigned* gu_cnt; int* keep; float* kval;
 };
 hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s);
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s);

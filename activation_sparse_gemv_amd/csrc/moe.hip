@@ -13,7 +13,8 @@
 //            (token, slot) items itself, and one wave per neuron computes both dot
 //            products for the expert's tokens (up to 4 at a time);
 //   down:    (token, slot, column tile) workgroups: the exact top-k of |h| (one
-//            wave, h in registers), the kept neurons' down rows, weight w_tj; the
+//            wave, h in registers; or, for many items, chosen by the last gate/up
+//            block of each expert), the kept neurons' down rows, weight w_tj; the
 //            last slot to finish a (token, tile) sums the slots in slot order into
 //            Y (deterministic).
 #include "moe_impl.hpp"
@@ -55,25 +56,6 @@ constexpr int kDnLpr = 64;                 // one wave covers 512 columns of one
 constexpr int kDnTile = kDnLpr * 8;
 static_assert(kDnTile % 256 == 0, "the combine takes whole columns per thread");
 
-// Keep set of one item by one wave: h read straight into registers (one load per
-// lane and 64 neurons), the exact top-k of |h| (ties to the smaller index), the
-// kept indices and their h written to LDS in ascending index order.
-template <int KPL>
-__device__ __forceinline__ void down_keep_regs(const float* h, int f, int k, int* keep, float* kval, int* dbg) {
-  const int lane = threadIdx.x & 63;
-  float v[KPL];
-#pragma unroll
-  for (int q = 0; q < KPL; ++q) v[q] = h[min(q * 64 + lane, f - 1)];
-  uint32_t key[KPL];
-#pragma unroll
-  for (int q = 0; q < KPL; ++q) key[q] = float_key(fabsf(v[q]));     // lanes past f: ignored
-  wave_topk_regs_emit<KPL>(key, f, k, [&](int pos, int q, int i) {
-    keep[pos] = i;
-    kval[pos] = v[q];
-    if (dbg != nullptr) dbg[pos] = i;
-  });
-}
-
 template <int WDT>
 __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -94,12 +76,15 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   // the item's keep set by wave 0 (every tile's workgroup selects the same set);
   // an item with an invalid expert keeps nothing
   int* dbg = (p.keep_dbg != nullptr && tile == 0) ? p.keep_dbg + (long)item * p.keep_k : nullptr;
-  if (threadIdx.x < 64 && kk > 0) {
+  if (p.keep != nullptr) {
+    // chosen by the gate/up stage
+    for (int r = threadIdx.x; r < kk; r += kDnThreads) {
+      keep[r] = p.keep[(long)item * p.keep_k + r];
+      kval[r] = p.kval[(long)item * p.keep_k + r];
+    }
+  } else if (threadIdx.x < 64 && kk > 0) {
     const float* h = p.h + (long)item * f;
-    if (f <= 256) down_keep_regs<4>(h, f, kk, keep, kval, dbg);
-    else if (f <= 512) down_keep_regs<8>(h, f, kk, keep, kval, dbg);
-    else if (f <= 768) down_keep_regs<12>(h, f, kk, keep, kval, dbg);
-    else if (f <= 1024) down_keep_regs<16>(h, f, kk, keep, kval, dbg);
+    if (f <= 1024) item_keep_small<false>(h, f, kk, keep, kval, dbg);
     else {
       // long rows: staged in LDS by this wave, radix selection over the copy
       for (int i = threadIdx.x; i < f; i += 64) hs[i] = h[i];

@@ -119,7 +119,7 @@ __device__ __forceinline__ void expert_neurons_reg(const MoeParams& p, const uin
       if (lane == 0 && m < ng) {
         const int it = items[g0 + m];
         const float h = silu_f32(gs) * us;
-        p.h[(long)it * f + n] = h;
+        store_coherent(p.h + (long)it * f + n, h);
         if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
       }
     }
@@ -127,6 +127,38 @@ __device__ __forceinline__ void expert_neurons_reg(const MoeParams& p, const uin
 }
 
 // NK > 0: groups of one or two tokens take the register path (d_model <= 512 NK).
+// Keep set of one (token, slot) item by one wave: the item's h (d_ff <= 64 * KPL)
+// read straight into registers (coherent loads when other workgroups of the same
+// launch wrote it), the exact top-k of |h| (ties to the smaller index;
+// intra-expert summary, method section: the lowest-scoring neurons are skipped),
+// the kept indices and their h written in ascending index order.
+template <int KPL, bool COH>
+__device__ __forceinline__ void item_keep_regs(const float* h, int f, int k, int* keep, float* kval, int* dbg) {
+  const int lane = threadIdx.x & 63;
+  float v[KPL];
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) {
+    const int i = min(q * 64 + lane, f - 1);
+    v[q] = COH ? load_coherent(h + i) : h[i];
+  }
+  uint32_t key[KPL];
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) key[q] = float_key(fabsf(v[q]));     // lanes past f: ignored
+  wave_topk_regs_emit<KPL>(key, f, k, [&](int pos, int q, int i) {
+    keep[pos] = i;
+    kval[pos] = v[q];
+    if (dbg != nullptr) dbg[pos] = i;
+  });
+}
+
+template <bool COH>
+__device__ __forceinline__ void item_keep_small(const float* h, int f, int k, int* keep, float* kval, int* dbg) {
+  if (f <= 256) item_keep_regs<4, COH>(h, f, k, keep, kval, dbg);
+  else if (f <= 512) item_keep_regs<8, COH>(h, f, k, keep, kval, dbg);
+  else if (f <= 768) item_keep_regs<12, COH>(h, f, k, keep, kval, dbg);
+  else item_keep_regs<16, COH>(h, f, k, keep, kval, dbg);
+}
+
 // Workgroup (u, nb): the u-th touched expert's neurons [nb * neurons_per_block, ...).
 // xs: [kGuTok][d_model] fp32 of dynamic LDS.
 template <int WDT, int NK>
@@ -244,11 +276,32 @@ __device__ __forceinline__ void expert_gu_block(const MoeParams& p, int u, int n
         if (lane == 0 && m < ng) {
           const int it = items[g0 + m];
           const float h = silu_f32(gs) * us;
-          p.h[(long)it * f + n] = h;
+          store_coherent(p.h + (long)it * f + n, h);
           if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
         }
       }
     }
+  }
+  if (p.keep == nullptr) return;
+  // The last neuron block of the expert to finish chooses every item's keep set:
+  // the h stores above are device-coherent and complete before the counter
+  // increment (the protocol of the split-K combine).
+  __shared__ int s_last;
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned nblk = (unsigned)((f + p.neurons_per_block - 1) / p.neurons_per_block);
+    const unsigned prev = __hip_atomic_fetch_add(p.gu_cnt + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == nblk - 1;
+    if (s_last) __hip_atomic_store(p.gu_cnt + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last || p.keep_k <= 0) return;
+  for (int m = wave; m < en; m += kGuThreads / 64) {
+    const int it = items[m];
+    const long o = (long)it * p.keep_k;
+    item_keep_small<true>(p.h + (long)it * f, f, p.keep_k, p.keep + o, p.kval + o,
+                          p.keep_dbg != nullptr ? p.keep_dbg + o : nullptr);
   }
 }
 

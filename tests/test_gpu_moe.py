@@ -276,3 +276,24 @@ def test_moe_layer_fp16_and_composed_paths():
         assert asg.api.moe_layer_one_stream_ok(X.to(DEV), ww, 4) == one
         # stage by stage against the oracle (selections on the GPU's logits and h)
         _check_layer(E, d, f, fs, T, 4, 20, 500 + T, weights=(src, ww))
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_keep_sets_chosen_in_either_stage(T, monkeypatch):
+    """The keep sets chosen at the end of the gate/up stage (last neuron block of each
+    expert) or at the start of the down stage give the same bits (same selection on
+    the same h)."""
+    announce(f"moe selection placement T={T}")
+    c = datagen.CFG5
+    w, dw = _weights(c["n_experts"], c["d_model"], c["d_ff_e"], c["d_ff_shared"])
+    X = datagen.student_t((T, c["d_model"]), 900 + T).to(DEV)
+    logits, ids, wts = asg.as_moe_router_gemv(X, dw.w_router, c["top"])
+    out = {}
+    for v in ("0", "1"):
+        monkeypatch.setenv("AS_MOE_SEL_GU", v)
+        Y, dbg = asg.as_sparse_moe_expert(X, dw, ids, wts, c["keep"], debug=True)
+        Y2 = asg.as_moe_layer(X, dw, c["top"], c["keep"])
+        torch.cuda.synchronize()
+        out[v] = (Y.clone(), dbg["h"].clone(), dbg["keep"].clone(), Y2.clone())
+    for a, b in zip(out["0"], out["1"]):
+        assert torch.equal(a, b)
