@@ -178,32 +178,68 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   }
   __syncthreads();
   if (!s_last) return;
-  // merge: O = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c, chunk statistics in one round trip
-  for (int i = tid; i < C * grp * 2; i += kAttThreads) s_ml[i] = load_coherent(p.part_ml + (long)g * C * grp * 2 + i);
-  __syncthreads();
-  for (int i = tid; i < grp * hd; i += kAttThreads) {
-    const int a = i / hd, dd = i % hd;
-    float M = -INFINITY;
-    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, s_ml[(cc * grp + a) * 2]);
-    float L = 0.f, O = 0.f;
-    for (int c0 = 0; c0 < C; c0 += 16) {
-      float ov[16];
+  // merge: O = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c.  The partial outputs
+  // of 32 chunks of every output of this thread are loaded together, issued before
+  // the chunk statistics are waited for; the weights exp(m_c - M) and the sums L
+  // depend on (chunk, head) only and are formed once in LDS.  Chunks are merged in
+  // chunk order.
+  constexpr int kOut = kMaxGroup * kAttHd / kAttThreads;
+  const int n_out = (grp * hd + kAttThreads - 1) / kAttThreads;      // in use (uniform)
+  float ov[kOut][32];
+  auto load_ov = [&](int c0) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int cc = min(c0 + k, C - 1);
-        ov[k] = load_coherent(p.part_o + (((long)g * C + cc) * grp + a) * hd + dd);
-      }
+    for (int u = 0; u < kOut; ++u) {
+      if (u < n_out) {
+        const int i = min(tid + u * kAttThreads, grp * hd - 1), a = i / hd, dd = i % hd;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int cc = c0 + k;
-        if (cc < C) {
-          const float w = expf(s_ml[(cc * grp + a) * 2] - M);
-          L = fmaf(w, s_ml[(cc * grp + a) * 2 + 1], L);
-          O = fmaf(w, ov[k], O);
+        for (int k = 0; k < 32; ++k) {
+          const int cc = min(c0 + k, C - 1);
+          ov[u][k] = load_coherent(p.part_o + (((long)g * C + cc) * grp + a) * hd + dd);
         }
       }
     }
-    p.o[(long)(g * grp + a) * hd + dd] = O / L;
+  };
+  load_ov(0);
+  for (int i = tid; i < C * grp * 2; i += kAttThreads) s_ml[i] = load_coherent(p.part_ml + (long)g * C * grp * 2 + i);
+  __syncthreads();
+  __shared__ float s_M[kMaxGroup], s_L[kMaxGroup];
+  __shared__ float s_w[kMaxChunks * kMaxGroup];                     // [C][grp] merge weights
+  if (tid < grp) {
+    float M = -INFINITY;
+    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, s_ml[(cc * grp + tid) * 2]);
+    s_M[tid] = M;
+  }
+  __syncthreads();
+  for (int i = tid; i < C * grp; i += kAttThreads) s_w[i] = expf(s_ml[i * 2] - s_M[i % grp]);
+  __syncthreads();
+  if (tid < grp) {
+    float L = 0.f;
+    for (int cc = 0; cc < C; ++cc) L = fmaf(s_w[cc * grp + tid], s_ml[(cc * grp + tid) * 2 + 1], L);
+    s_L[tid] = L;
+  }
+  __syncthreads();
+  float O[kOut];
+#pragma unroll
+  for (int u = 0; u < kOut; ++u) O[u] = 0.f;
+  for (int c0 = 0; c0 < C; c0 += 32) {
+    if (c0 > 0) load_ov(c0);
+#pragma unroll
+    for (int u = 0; u < kOut; ++u) {
+      if (u < n_out) {
+        const int a = min(tid + u * kAttThreads, grp * hd - 1) / hd;
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+          if (c0 + k < C) O[u] = fmaf(s_w[(c0 + k) * grp + a], ov[u][k], O[u]);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kOut; ++u) {
+    const int i = tid + u * kAttThreads;
+    if (u < n_out && i < grp * hd) {
+      const int a = i / hd;
+      p.o[(long)(g * grp + a) * hd + i % hd] = O[u] / s_L[a];
+    }
   }
 }
 
