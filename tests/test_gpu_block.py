@@ -24,8 +24,11 @@ def test_rmsnorm():
 
 
 @pytest.mark.parametrize("n_ctx,n_q,n_kv,hd", [(2048, 32, 8, 128), (0, 4, 2, 128), (1, 8, 8, 128),
-                                               (300, 16, 2, 128), (5000, 32, 8, 128), (70, 8, 1, 128)])
+                                               (300, 16, 2, 128), (5000, 32, 8, 128), (70, 8, 1, 128),
+                                               (5000, 8, 1, 128), (2100, 16, 2, 128)])
 def test_attention(n_ctx, n_q, n_kv, hd):
+    """Decode attention against the fp64 oracle; the shapes cover 1 to 64 key chunks per kv
+    head (64 with one kv head and 5001 keys; 33 with two and 2101) and groups of 1 to 8."""
     announce(f"attention n_ctx={n_ctx}")
     rng = np.random.default_rng(n_ctx + n_q)
     q = torch.from_numpy(rng.standard_normal((n_q, hd)).astype(np.float32))
