@@ -495,6 +495,47 @@ __device__ __forceinline__ int compact_stage(const float* stage, int L, int i0, 
   return nnz;
 }
 
+// Several tokens, a range [i0, i1) of at most 2 * kThreads inputs: each thread owns
+// two consecutive inputs and loads every token's value of them into registers (no
+// LDS staging), forms their union mask (|v| > t for any token), and after a
+// workgroup scan writes the kept rows in input order, a token's value being 0 where
+// its own |v| <= t.  The same rows and values as the staged version below.
+template <int MT>
+__device__ __forceinline__ int compact_range_regs(const GemvParams& p, int i0, int i1, int* s_idx, float* s_val,
+                                                  int cap, int* s_scan) {
+  const int tid = threadIdx.x, M = p.M;
+  const float t = p.t;
+  const int L = max(0, i1 - i0);
+  const int c0 = 2 * tid;
+  float xv[2][MT];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const long row = L > 0 ? (long)i0 + min(c0 + e, L - 1) : 0;    // past L: a row in range, dropped
+    load_tokens<MT>(p.x, p.x_dt, p.ldx, row, M, xv[e]);
+  }
+  bool a[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    bool any = false;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) any |= m < M && fabsf(xv[e][m]) > t;
+    a[e] = c0 + e < L && any;
+  }
+  int nnz;
+  int r = block_excl_scan<kThreads>((int)a[0] + (int)a[1], s_scan, &nnz);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (a[e]) {
+      s_idx[r] = i0 + c0 + e;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s_val[m * cap + r] = (m < M && fabsf(xv[e][m]) > t) ? xv[e][m] : 0.f;
+      ++r;
+    }
+  }
+  __syncthreads();
+  return nnz;
+}
+
 // Several tokens, one slice's own range [i0, i1): every token's values of the
 // range are staged in LDS (stage: [MT][len] fp32) with one round trip of
 // independent loads (16-byte vectors when NV > 0, i.e. aligned rows), then each
@@ -672,7 +713,9 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     }
     int lo = 0;
     if constexpr (IN == IN_RANGE && MT > 1)
-      cnt = compact_range_staged<MT, NV>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan);
+      cnt = r1 - r0 <= 2 * kThreads
+                ? compact_range_regs<MT>(p, r0, r1, s_idx, s_val, cap, s_scan)
+                : compact_range_staged<MT, NV>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan);
     else
       cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo, tile == 0 && sl == 0);
     if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
