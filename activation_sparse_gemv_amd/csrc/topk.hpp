@@ -3,11 +3,13 @@
 // GLASS summary, section 2.2 (selection): the k neurons with the highest score
 // form the mask.  Intra-expert summary, method section: the lowest-scoring
 // neurons of a routed expert are skipped.  Both need an exact order statistic:
-// here every score is mapped to an order-preserving 32-bit key, an MSB-first
-// radix select over four 8-bit digits (LDS histogram) finds the k-th largest key
-// T and how many keys equal to T must be taken, and a final pass in index order
-// keeps every key above T plus the first such keys equal to T, so ties go to the
-// smaller index.  Output: an ascending index list and a 64-bit-word bitmask.
+// here every score is mapped to an order-preserving 32-bit key, the k-th largest
+// key T is found (an MSB-first radix select over four 8-bit digits with an LDS
+// histogram for the workgroup and long-row forms; a bracketed count search over
+// keys held in registers for one wave and at most 1024 keys), and a final pass in
+// index order keeps every key above T plus the first keys equal to T, so ties go
+// to the smaller index.  Output: an ascending index list (and, for the workgroup
+// form, a 64-bit-word bitmask).
 #pragma once
 #include "common.hpp"
 
