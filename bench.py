@@ -277,10 +277,20 @@ def cpu_baseline_headline(t_x, t_h, seconds):
                   wd.to(torch.float64).numpy())
     del wgu, wd
     toks = datagen.student_t((64, shape.d_model), datagen.seed_for(2, 0, "decode")).to(torch.float64).numpy()
-    us, n, el = cpu_time(lambda i: teal.swiglu_mlp_threshold(toks[i % 64], Wg, Wu, Wd, t_x, t_h), seconds)
-    return {"value": round(us, 1), "unit": "µs/layer", "cores": cores(), "kind": "oracle",
+    active = [0]
+
+    def one(i):
+        r = teal.swiglu_mlp_threshold(toks[i % 64], Wg, Wu, Wd, t_x, t_h)
+        # the active-row bytes of this token, counted as the GPU path counts them (bf16 rows)
+        active[0] += int(r["m1"].sum()) * 2 * shape.d_ff * 2 + int(r["m2"].sum()) * shape.d_model * 2
+
+    us, n, el = cpu_time(one, seconds, max_n=100000)
+    return {"value": round(active[0] / el / 1e9, 3), "unit": "GB/s", "cores": cores(), "kind": "oracle",
+            "us_per_layer": round(us, 1),
             "sample": f"{n} decode tokens through one 4096->14336->4096 threshold MLP (fp64 numpy, same "
-                      f"thresholds), {el:.1f} s; fp64 weight conversion not timed"}
+                      f"thresholds and tokens as the GPU run), {el:.1f} s; value = the active-row bytes "
+                      f"(bf16 rows of the kept inputs) of those tokens per second; fp64 weight conversion "
+                      f"not timed"}
 
 
 # ============================================================================ per-row sub-benchmarks
