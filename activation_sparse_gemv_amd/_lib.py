@@ -14,6 +14,7 @@ LIB_PATH = os.environ.get("ACTSPARSE_LIB",
 AS_OK, AS_ERR_INVALID_ARG, AS_ERR_UNSUPPORTED, AS_ERR_WORKSPACE, AS_ERR_HIP = range(5)
 AS_F16, AS_BF16, AS_F32 = 0, 1, 2
 AS_FLAG_ACCUMULATE = 1 << 0
+AS_FLAG_ATOMIC_SPLITK = 1 << 1
 AS_FLAG_NO_NT_LOADS = 1 << 2
 AS_FLAG_FORCE_DENSE = 1 << 3
 AS_FLAG_NO_FUSION = 1 << 4

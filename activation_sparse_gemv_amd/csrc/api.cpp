@@ -412,6 +412,14 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
     p.res = fz->res; p.res_dt = fz->res_dt; p.ldres = N;
   }
   GemvConfig cfg{int(w_dt), mt_for(M), pl.lpr, in, OUT_Y, false, (flags & AS_FLAG_NO_NT_LOADS) == 0};
+  if (flags & AS_FLAG_ATOMIC_SPLITK) {
+    if (y_dt != AS_F32) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_ATOMIC_SPLITK needs an fp32 Y", fn);
+    p.atomic_y = 1;
+    if (!p.accumulate) {
+      as_status st2 = hip_check(launch_fill_zero(Y, size_t(M) * N * sizeof(float), stream), fn);
+      if (st2 != AS_OK) return st2;
+    }
+  }
   return hip_check(launch_gather_gemv(cfg, p, stream), fn);
 }
 
@@ -484,6 +492,9 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   if (M > 8 && (w->w_dt != AS_BF16 || mode != AS_MLP_THRESHOLD))
     return fail(AS_ERR_UNSUPPORTED, "%s: M > 8 (MFMA path) needs bf16 weights in THRESHOLD mode", fn);
   const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
+  const bool atomic = (flags & AS_FLAG_ATOMIC_SPLITK) != 0;
+  const bool clear_y = atomic && (flags & AS_FLAG_ACCUMULATE) == 0;
+  if (atomic && y_dt != AS_F32) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_ATOMIC_SPLITK needs an fp32 Y", fn);
   if (mode == AS_MLP_NEURON_SET && !dense) {
     if (n_active < 0 || n_active > w->d_ff) return fail(AS_ERR_INVALID_ARG, "%s: n_active=%d", fn, n_active);
     if (n_active > 0 && !neuron_idx) return fail(AS_ERR_INVALID_ARG, "%s: neuron_idx is NULL", fn);
@@ -520,7 +531,7 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   // workgroups, then down workgroups that start on their range of h as soon as the
   // gate/up tiles covering it are complete (grouped by XCD).
   const bool try_fused = fz == nullptr && mode == AS_MLP_THRESHOLD && mt <= 8 && nt &&
-                         (flags & AS_FLAG_NO_FUSION) == 0 &&
+                         (flags & AS_FLAG_NO_FUSION) == 0 && !atomic &&
                          env_int("AS_FUSED", 0) != 0 && (mp.p1.lpr == 32 || mp.p1.lpr == 64) &&
                          (mp.p2.lpr == 16 || mp.p2.lpr == 32) &&
                          (long)mp.cap2_fused * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
@@ -620,6 +631,8 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
     }
     GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, in1, dn_parts ? OUT_PARTS : OUT_SWIGLU, true, nt};
     if (gu_range) p.cap = mp.cap1_range;
+    // the down stage adds into Y: the gate/up launch clears it (Y does not alias X)
+    if (clear_y) { p.zero_y = reinterpret_cast<float*>(Y); p.zero_n = long(M) * d; }
     if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
     // stage 2: down projection over the surviving h rows; each slice masks its
@@ -642,6 +655,8 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
     }
   } else {
     // stage 1: gate/up dot products of the listed neurons (neuron-major rows)
+    if (clear_y && (st = hip_check(launch_fill_zero(Y, size_t(M) * d * sizeof(float), stream), fn)) != AS_OK)
+      return st;
     NeuronGuParams q;
     memset(&q, 0, sizeof q);
     q.x = X; q.x_dt = int(x_dt); q.M = M; q.ldx = d; q.d_model = d;
@@ -663,6 +678,7 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   if (c2.in == IN_RANGE || c2.in == IN_PARTS) { p2.S = mp.s2_range; p2.cap = mp.cap2_range; }
   p2.partials = mw.g2.partials; p2.counters = mw.g2.counters; p2.part_ld = d;
   p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
+  p2.atomic_y = atomic ? 1 : 0;
   if (fz != nullptr) { p2.res = fz->res; p2.res_dt = fz->res_dt; p2.ldres = d; }
   if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;
   return rec(2);

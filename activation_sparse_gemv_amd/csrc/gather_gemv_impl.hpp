@@ -908,10 +908,34 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
         for (int m = 0; m < MT; ++m)
           if (m < M) store_coherent(p.partials + ((long)part * M + m) * p.part_ld + pc, res[m][q]);
     }
+    // one workgroup clears the y that the next launch adds into
+    if (p.zero_y != nullptr && tile == 0 && part == 0)
+      for (long i = tid; i < p.zero_n; i += kThreads) p.zero_y[i] = 0.f;
     return;
   }
 
   // ------------------------------------------------------------ split-K combine
+  if constexpr (OUT == OUT_Y) {
+    if (n_parts > 1 && p.atomic_y) {
+      // every slice adds its partial tile into y (fp32, cleared by the host or the
+      // previous launch unless accumulating); slice 0 adds the residual
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + q * kThreads;
+        bool ok;
+        const long gc = col_of(c, ok);
+        if (c < TN && ok)
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            if (m < M) {
+              float v = res[m][q];
+              if (part == 0 && p.res != nullptr) v += load_elem(p.res, p.res_dt, m * p.ldres + gc);
+              unsafeAtomicAdd(reinterpret_cast<float*>(p.y) + m * p.ldy + gc, v);
+            }
+      }
+      return;
+    }
+  }
   if (n_parts > 1) {
     // Partials are written through to the device-coherent level (relaxed agent-scope
     // atomic stores) and the wave waits for their completion before the counter
@@ -1028,6 +1052,9 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
                   r_sel[wave], r_sm[wave]);
   } else if constexpr (OUT == OUT_SWIGLU) {
     static_assert(GU, "the SwiGLU epilogue needs paired gate/up columns");
+    // the one workgroup finishing tile 0 clears the y that the next launch adds into
+    if (p.zero_y != nullptr && tile == 0)
+      for (long i = tid; i < p.zero_n; i += kThreads) p.zero_y[i] = 0.f;
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {

@@ -36,6 +36,12 @@ struct GemvParams {
   float* partials; unsigned* counters; long part_ld;
   // OUT_Y
   void* y; int y_dt; long ldy; int accumulate;
+  // OUT_Y with split rows: each slice adds its partial tile into y (fp32) with
+  // atomic adds (slice 0 also adds res) instead of the last-workgroup combine
+  int atomic_y;
+  // OUT_PARTS / OUT_SWIGLU: when set, one workgroup (column tile 0) clears zero_n
+  // floats at zero_y (the y that the next launch adds into)
+  float* zero_y; long zero_n;
   // OUT_SWIGLU
   float t_h; float* h; long ldh; int* o_cnt; int* o_idx; float* o_val; uint64_t* h_bits; long h_bits_ld;
   // input-mask verification exports (IN_THRESH)

@@ -199,6 +199,11 @@ def headline(a, C):
             r["stage1_us"], r["stage2_us"] = float(k1.mean()), float(k2.mean())
             r["stage1_gbs"] = float(b1.sum() / (k1.sum() * 1e-6) / 1e9)
             r["stage1_bytes_per_launch"] = float(b1.mean())
+            # the same step with the down stage's slices adding into Y atomically (no
+            # deterministic combine); reported beside the headline, not as it
+            at_ms, _, _, _ = run(t_x, t_h, a.flags | L.AS_FLAG_ATOMIC_SPLITK, a.steps, a.warmup, per_kernel=False)
+            r["atomic_us_per_layer"] = at_ms * 1e3 / calls
+            r["atomic_gbs"] = bytes_tot / (at_ms * 1e-3) / 1e9
         res[s] = r
         log(f"s={s:.2f} {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s (active {r['active_mb_per_layer']:.1f} MB)")
     dense_ms, _, _, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE, a.steps, a.warmup, per_kernel=False)
@@ -229,6 +234,9 @@ def headline(a, C):
         "dense_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
         "speedup_vs_dense": round(dense_us / m["us_per_layer"], 3),
         "frac_of_peak_layer": round(m["gbs"] / PEAK_HBM_GBS, 4),
+        "atomic_splitk": {"us_per_layer": round(m["atomic_us_per_layer"], 3), "gbs": round(m["atomic_gbs"], 1),
+                          "note": "AS_FLAG_ATOMIC_SPLITK: down-stage slices add into fp32 Y with atomics "
+                                  "(not bitwise reproducible); value above is the deterministic path"},
         "stage_us": {"gate_up": round(m["stage1_us"], 3), "down": round(m["stage2_us"], 3),
                      "dense_gate_up": round(float(dk1.mean()), 3), "dense_down": round(float(dk2.mean()), 3)},
         "roofline": {"bound": "hbm", "kernel": "gather_gemv_kernel: gate/up row gather (split-K partials left for the down prologue, which applies SwiGLU)",

@@ -72,6 +72,9 @@ typedef enum { AS_F16 = 0, AS_BF16 = 1, AS_F32 = 2 } as_dtype;
 
 enum {
   AS_FLAG_ACCUMULATE = 1u << 0,   /* Y += result instead of Y = result                   */
+  AS_FLAG_ATOMIC_SPLITK = 1u << 1, /* row slices add into fp32 Y with atomics: no partial
+                                      round trip or last-workgroup combine, not bitwise
+                                      reproducible (see the GEMV and MLP calls)           */
   AS_FLAG_NO_NT_LOADS = 1u << 2,  /* plain (cached) weight loads instead of nontemporal  */
   AS_FLAG_FORCE_DENSE = 1u << 3,  /* ignore thresholds / neuron lists: dense baseline   */
   AS_FLAG_NO_FUSION = 1u << 4     /* threshold MLP: two launches instead of one           */
@@ -123,7 +126,13 @@ as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64
  * its own kept inputs.
  * mask_out (nullable): the per-token input masks (bits and nnz for any M,
  * idx only for M == 1).
- * AS_FLAG_FORCE_DENSE runs the dense baseline (every row, t ignored). */
+ * AS_FLAG_FORCE_DENSE runs the dense baseline (every row, t ignored).
+ * AS_FLAG_ATOMIC_SPLITK (Y fp32 only, else UNSUPPORTED): where the launch plan
+ * splits the rows of a column tile over several workgroups, each adds its
+ * partial tile into Y with fp32 atomic adds instead of the deterministic
+ * store / count / last-workgroup sum (same terms, order of the additions
+ * unspecified).  Without AS_FLAG_ACCUMULATE, Y is cleared by an extra fill
+ * launch first.  Also taken by as_dense_gemv. */
 size_t as_threshold_gemv_ws_size(int M, int K, int N);
 as_status as_threshold_gemv(const void *X, as_dtype x_dt, int M, int K,
                             const void *W, as_dtype w_dt, int N, float t,
@@ -169,7 +178,11 @@ typedef struct {
  * X: [M, d_model] (f16/bf16/f32), 1 <= M <= 16 (M > 8: THRESHOLD mode with bf16
  * weights, on the matrix cores); Y: [M, d_model].
  * silu(z) = z / (1 + exp(-z)).  AS_FLAG_FORCE_DENSE: dense SwiGLU over all
- * neurons and inputs (the baseline).  dbg is nullable. */
+ * neurons and inputs (the baseline).  AS_FLAG_ATOMIC_SPLITK (fp32 Y only): the
+ * down projection's row slices add into Y with fp32 atomic adds (as in
+ * as_threshold_gemv); without AS_FLAG_ACCUMULATE, Y is cleared by the first
+ * launch, so Y must not alias X; the one-launch variant is not used.  dbg is
+ * nullable. */
 size_t as_sparse_swiglu_mlp_ws_size(int M, const as_mlp_weights *w, as_mlp_mode mode);
 as_status as_sparse_swiglu_mlp(const void *X, as_dtype x_dt, int M, const as_mlp_weights *w,
                                as_mlp_mode mode, float t_x, float t_h,

@@ -70,6 +70,10 @@ def test_gemv_validation(lib):
     assert st == L.AS_ERR_WORKSPACE
     st = lib.as_dense_gemv(_p(), L.AS_BF16, 1, 4096, _p(), L.AS_BF16, 4096, _p(), L.AS_F32, 0, None, 0, None)
     assert st == L.AS_ERR_WORKSPACE
+    # atomic split-K adds into fp32 only
+    st = lib.as_threshold_gemv(_p(), L.AS_BF16, 1, 4096, _p(), L.AS_BF16, 4096, 0.5, _p(), L.AS_BF16,
+                               L.AS_FLAG_ATOMIC_SPLITK, None, _p(), need, None)
+    assert st == L.AS_ERR_UNSUPPORTED and b"fp32" in lib.as_last_error()
 
 
 def test_mlp_validation(lib):
@@ -83,6 +87,9 @@ def test_mlp_validation(lib):
     st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(bad), L.AS_MLP_THRESHOLD, 0.5, 0.5, None, 0,
                                   _p(), L.AS_F32, 0, None, _p(), 1 << 30, None)
     assert st == L.AS_ERR_INVALID_ARG and b"d_ff" in lib.as_last_error()
+    st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(w), L.AS_MLP_THRESHOLD, 0.5, 0.5, None, 0,
+                                  _p(), L.AS_F16, L.AS_FLAG_ATOMIC_SPLITK, None, _p(), need, None)
+    assert st == L.AS_ERR_UNSUPPORTED and b"fp32" in lib.as_last_error()
     nodown = L.ASMlpWeights(_p(), None, L.AS_BF16, 4096, 14336)
     st = lib.as_sparse_swiglu_mlp(_p(), L.AS_BF16, 1, ctypes.byref(nodown), L.AS_MLP_THRESHOLD, 0.5, 0.5, None,
                                   0, _p(), L.AS_F32, 0, None, _p(), 1 << 30, None)

@@ -175,6 +175,33 @@ def test_gemv_unaligned_and_long_inputs(K):
     assert rel_err(y2, f64(y)) < 1e-5
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 14336, 4096), (3, 4096, 6144), (16, 4096, 4096), (1, 777, 200)])
+def test_gemv_atomic_splitk(M, K, N):
+    """AS_FLAG_ATOMIC_SPLITK: the row slices add into fp32 Y with atomics.  Integer-valued
+    inputs sum exactly in any order, so Y is bit-exact (a NaN-filled Y is overwritten, and
+    with AS_FLAG_ACCUMULATE the sum lands on Y's contents); real-valued inputs agree with
+    the deterministic combine and the oracle."""
+    announce(f"gemv atomic split-K M={M} K={K} N={N}")
+    x = datagen.int_valued((M, K), 1300 + M, -8, 8)
+    W = _dev(datagen.int_valued((K, N), 1301, -4, 4))
+    ref = teal.masked_gemv(f64(x), f64(W.cpu()), 3.0)
+    Y = torch.full((M, N), float("nan"), device=DEV)
+    asg.as_threshold_gemv(_dev(x), W, 3.0, flags=L.AS_FLAG_ATOMIC_SPLITK, Y=Y)
+    assert np.array_equal(f64(Y), ref)
+    Y0 = datagen.int_valued((M, N), 1302, -100, 100).float().to(DEV)
+    Y1 = Y0.clone()
+    asg.as_threshold_gemv(_dev(x), W, 3.0, flags=L.AS_FLAG_ATOMIC_SPLITK | L.AS_FLAG_ACCUMULATE, Y=Y1)
+    assert np.array_equal(f64(Y1), f64(Y0) + ref)
+    xr = datagen.student_t((M, K), 1303)
+    Wr = datagen.normal((K, N), 1304)
+    ya = asg.as_threshold_gemv(_dev(xr), _dev(Wr), 1.0, flags=L.AS_FLAG_ATOMIC_SPLITK)
+    yd = asg.as_threshold_gemv(_dev(xr), _dev(Wr), 1.0)
+    assert rel_err(ya, f64(yd)) < 1e-5
+    assert rel_err(ya, teal.masked_gemv(f64(xr), f64(Wr), 1.0)) < TOL * 1e-2
+    yda = asg.as_dense_gemv(_dev(xr), _dev(Wr), flags=L.AS_FLAG_ATOMIC_SPLITK)
+    assert rel_err(yda, f64(xr) @ f64(Wr)) < TOL * 1e-2
+
+
 def test_gemv_determinism_and_nt_flag():
     announce("gemv determinism")
     K, N = 14336, 4096

@@ -142,6 +142,53 @@ def test_mlp_unsummed_partials_equal_summed(cfg, M, monkeypatch):
     assert rel_err(out[2][0], f64(out[0][0])) < 1e-5
 
 
+@pytest.mark.parametrize("cfg,M", [(2, 1), (2, 4), (2, 16), (1, 1), (1, 3)])
+def test_mlp_atomic_splitk(cfg, M):
+    """AS_FLAG_ATOMIC_SPLITK in the threshold MLP: the down stage adds into fp32 Y with
+    atomics (the gate/up launch clears Y first, so a NaN-filled Y is overwritten).  y is
+    checked against the oracle's down stage fed the GPU's h, and against the
+    deterministic path; with AS_FLAG_ACCUMULATE it lands on Y's contents."""
+    announce(f"mlp atomic split-K cfg={cfg} M={M}")
+    shape = datagen.CFG1 if cfg == 1 else datagen.CFG2
+    w = _mlp(cfg, shape)
+    if cfg == 1:
+        calib = datagen.laplace((64, shape.d_model), datagen.seed_for(1, 0, "calib"), dtype="f16")
+        toks = datagen.laplace((M, shape.d_model), datagen.seed_for(1, 4, "decode"), dtype="f16")
+    else:
+        calib = datagen.student_t((64, shape.d_model), datagen.seed_for(2, 0, "calib"))
+        toks = datagen.student_t((M, shape.d_model), datagen.seed_for(2, 4, "decode"))
+    t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], 0.5, 0.5)
+    t_x, t_h = float(t_x), float(t_h)
+    xd = toks.to(DEV)
+    Y = torch.full((M, shape.d_model), float("nan"), device=DEV)
+    _, dbg = asg.as_sparse_swiglu_mlp(xd, w["dev"], t_x, t_h, flags=L.AS_FLAG_ATOMIC_SPLITK, Y=Y, debug=True)
+    y_ref = teal.down_stage(f64(dbg["h"]), w["Wd"], t_h)
+    assert rel_err(Y, y_ref) < TOL
+    Y2 = torch.full((M, shape.d_model), float("nan"), device=DEV)
+    asg.as_sparse_swiglu_mlp(xd, w["dev"], t_x, t_h, flags=L.AS_FLAG_ATOMIC_SPLITK, Y=Y2)
+    y_det = asg.as_sparse_swiglu_mlp(xd, w["dev"], t_x, t_h)
+    assert rel_err(Y2, f64(y_det)) < 1e-5
+    Y0 = torch.randn(M, shape.d_model, device=DEV)
+    Y1 = Y0.clone()
+    asg.as_sparse_swiglu_mlp(xd, w["dev"], t_x, t_h, flags=L.AS_FLAG_ATOMIC_SPLITK | L.AS_FLAG_ACCUMULATE, Y=Y1)
+    assert rel_err(Y1, f64(Y0) + f64(y_det)) < 1e-5
+    yd = asg.as_sparse_swiglu_mlp(xd, w["dev"], flags=L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK)
+    assert rel_err(yd, teal.dense_mlp(f64(toks), w["Wg"], w["Wu"], w["Wd"])) < TOL
+
+
+def test_neuron_set_atomic_splitk():
+    announce("neuron-set atomic split-K")
+    d, f, n_act = 512, 2048, 777
+    W, Wg, Wu, Wd = _neuron_major(d, f, 9)
+    idx = np.sort(np.random.default_rng(5).choice(f, size=n_act, replace=False)).astype(np.int32)
+    x = datagen.student_t((2, d), 57)
+    w = asg.MLPWeights(W.to(DEV), None, L.AS_MLP_NEURON_SET)
+    Y = torch.full((2, d), float("nan"), device=DEV)
+    asg.as_sparse_swiglu_mlp(x.to(DEV), w, neuron_idx=torch.from_numpy(idx).to(DEV),
+                             flags=L.AS_FLAG_ATOMIC_SPLITK, Y=Y)
+    assert rel_err(Y, glass.neuron_set_mlp(f64(x), Wg, Wu, Wd, idx)) < TOL
+
+
 def test_mlp_determinism_and_edges():
     announce("mlp determinism")
     shape = datagen.CFG1
