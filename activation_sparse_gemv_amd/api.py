@@ -346,7 +346,7 @@ def as_moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags:
 
 def moe_layer_one_stream_ok(X: torch.Tensor, w: MoEWeights, top_k: int, flags: int = 0) -> bool:
     """Whether as_moe_layer takes this call (shapes within its limits, bf16 weights)."""
-    if flags & ~L.AS_FLAG_FORCE_DENSE:
+    if flags & ~(L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK):
         return False
     st = _moe_layer_struct(w)
     return st is not None and L.load().as_moe_layer_ws_size(X.shape[0], top_k, ctypes.byref(st)) > 0

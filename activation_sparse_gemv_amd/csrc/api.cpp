@@ -842,6 +842,12 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   if (moe_select_in_gu(T * top_k, w->d_ff_e, false)) { p.gu_cnt = m.gu_cnt; p.keep = m.keep; p.kval = m.kval; }
   p.y = Y; p.y_dt = int(y_dt); p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   p.neurons_per_block = moe_npb(T * top_k);
+  if (flags & AS_FLAG_ATOMIC_SPLITK) {
+    if (y_dt != AS_F32) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_ATOMIC_SPLITK needs an fp32 Y", fn);
+    p.atomic_y = 1;
+    if (!p.accumulate && (st = hip_check(launch_fill_zero(Y, size_t(T) * w->d_model * sizeof(float), stream), fn)) != AS_OK)
+      return st;
+  }
   {
     const int es = x_dt == AS_F32 ? 4 : 2;
     p.x_vec = aligned16(X) && (long(w->d_model) * es) % 16 == 0;
@@ -932,7 +938,8 @@ as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_w
   if (T < 1 || top_k < 1) return fail(AS_ERR_INVALID_ARG, "%s: T=%d top_k=%d", fn, T, top_k);
   const as_moe_weights& ew = w->experts;
   if (keep_k < 0 || keep_k > ew.d_ff_e) return fail(AS_ERR_INVALID_ARG, "%s: keep_k=%d", fn, keep_k);
-  if ((flags & ~unsigned(AS_FLAG_FORCE_DENSE)) != 0) return fail(AS_ERR_UNSUPPORTED, "%s: flags 0x%x", fn, flags);
+  if ((flags & ~unsigned(AS_FLAG_FORCE_DENSE | AS_FLAG_ATOMIC_SPLITK)) != 0)
+    return fail(AS_ERR_UNSUPPORTED, "%s: flags 0x%x", fn, flags);
   if (!aligned16(w->w_router) || !aligned16(ew.w_gate_up) || !aligned16(ew.w_down))
     return fail(AS_ERR_INVALID_ARG, "%s: weights not 16-byte aligned", fn);
   MoeLayerPlan lp = moe_layer_plan(T, top_k, w);
@@ -980,6 +987,7 @@ as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_w
   pm.partials = m.moe.partials; pm.counters = m.moe.counters; pm.n_tiles = moe_down_tiles(d);
   if (moe_select_in_gu(T * top_k, ew.d_ff_e, true)) { pm.gu_cnt = m.moe.gu_cnt; pm.keep = m.moe.keep; pm.kval = m.moe.kval; }
   pm.y = Y; pm.y_dt = AS_F32; pm.accumulate = 1;
+  pm.atomic_y = (flags & AS_FLAG_ATOMIC_SPLITK) ? 1 : 0;
   pm.neurons_per_block = moe_npb(T * top_k);
   {
     const int es = x_dt == AS_F32 ? 4 : 2;

@@ -123,6 +123,7 @@ struct MoeParams {
   const uint16_t* w_gu; const uint16_t* w_down;     // [E, d_ff, 2, d_model], [E, d_ff, d_model]
   float* h; float* h_dbg; int* keep_dbg; float* partials; unsigned* counters; int n_tiles;
   void* y; int y_dt; int accumulate; int neurons_per_block;
+  int atomic_y;            // down stage: each (token, slot) adds its weighted tile into y (fp32) atomically
   int x_vec;               // token rows 16-byte aligned (vector staging of x)
   // keep sets chosen at the end of the gate/up stage (keep != nullptr, d_ff <= 1024):
   // finished neuron blocks per touched expert [256], kept indices and their h

@@ -129,6 +129,19 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   for (int q = 0; q < 8; ++q) red[wave * kDnTile + lane * 8 + q] = acc[q];
   __syncthreads();
   const float wt = valid_e ? p.wts[item] : 0.f;
+  if (p.atomic_y) {
+    // w_tj * sum over kept neurons added straight into y (fp32, written or cleared
+    // before this launch); no slot partials, no counter, no combine
+    if (valid_e)
+      for (int c = threadIdx.x; c < kDnTile; c += kDnThreads) {
+        const int gc = tile * kDnTile + c;
+        if (gc < d) {
+          const float v = red[c] + red[kDnTile + c] + red[2 * kDnTile + c] + red[3 * kDnTile + c];
+          unsafeAtomicAdd(reinterpret_cast<float*>(p.y) + (long)t * d + gc, wt * v);
+        }
+      }
+    return;
+  }
   // partial of this (token, slot): w_tj * sum over kept neurons, coherent store
   for (int c = threadIdx.x; c < kDnTile; c += kDnThreads) {
     const int gc = tile * kDnTile + c;

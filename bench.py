@@ -451,7 +451,10 @@ def row_moe(C, cpu):
         fs = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"]) for ww in copies * 2]
         fd = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"], flags=L.AS_FLAG_FORCE_DENSE)
               for ww in copies * 2]
+        fa = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"], flags=L.AS_FLAG_ATOMIC_SPLITK)
+              for ww in copies * 2]
         us, usd = C.graph_us(fs, reps=10), C.graph_us(fd, reps=10)
+        usa = C.graph_us(fa, reps=10)
         _, dbg = asg.moe_layer(X, copies[0], c["top"], c["keep"], debug=True)
         ids = dbg["ids"].cpu().numpy()
         touched = len(np.unique(ids))
@@ -463,9 +466,10 @@ def row_moe(C, cpu):
             d * c["n_experts"] * 2
         dense_b = touched * (e_gu + c["d_ff_e"] * d * 2) + (3 * d * c["d_ff_shared"]) * 2 + d * c["n_experts"] * 2
         cases.append({"tokens": T, "experts_touched": touched, "us": r4(us), "dense_us": r4(usd),
-                      "speedup": r4(usd / us), "active_mb": r4(ab / 1e6), "dense_mb": r4(dense_b / 1e6),
+                      "speedup": r4(usd / us), "atomic_splitk_us": r4(usa),
+                      "active_mb": r4(ab / 1e6), "dense_mb": r4(dense_b / 1e6),
                       "gbs": r4(ab / (us * 1e-6) / 1e9), "frac_hbm": r4(ab / (us * 1e-6) / 8e12)})
-        log(f"moe T={T}: {us:.1f} us (dense {usd:.1f})")
+        log(f"moe T={T}: {us:.1f} us (dense {usd:.1f}, atomic split-K {usa:.1f})")
     r = {"step": "a8+a9 MoE layer: router GEMV + top-8/softmax, dense shared expert, routed experts "
                  "(dense gate/up scoring, exact top-77 of 768, gathered down rows)",
          "shape": "128 experts, d_model 2048, d_ff_e 768, shared d_ff 4096, bf16", "cases": cases}

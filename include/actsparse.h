@@ -271,6 +271,11 @@ as_status as_moe_router_gemv(const void *X, as_dtype x_dt, int T, const void *w_
  * Gate/up weights of an expert are read once per call for all tokens routed to
  * it.  Shared experts are not part of this call (run them densely and combine
  * with AS_FLAG_ACCUMULATE).  AS_FLAG_FORCE_DENSE keeps every neuron.
+ * AS_FLAG_ATOMIC_SPLITK (fp32 Y only, else UNSUPPORTED): each (token, slot)
+ * adds its weighted rows' sum into Y with fp32 atomic adds instead of the
+ * slot-order sum by the last slot to finish (order of the additions
+ * unspecified); without AS_FLAG_ACCUMULATE, Y is cleared by a fill launch
+ * first (which does not wait for y_ready).
  * Debug exports (nullable): h_dbg [T, top_k, d_ff_e] fp32, keep_dbg
  * [T, top_k, keep_k] int32 ascending.
  * y_ready (nullable): an event recorded after whatever produces Y on another
@@ -307,8 +312,9 @@ as_status as_sparse_moe_expert(const void *X, as_dtype x_dt, int T,
  * X: [T, d_model] (f16/bf16/f32).  Y: [T, d_model] fp32.  logits: [T, E] fp32,
  * ids: [T, top_k] int32, weights: [T, top_k] fp32 (outputs, device).
  * h_dbg [T * top_k, d_ff_e] and keep_dbg [T * top_k, keep_k]: optional, as in
- * as_sparse_moe_expert.  flags: AS_FLAG_FORCE_DENSE (every routed neuron kept);
- * any other flag is AS_ERR_UNSUPPORTED.
+ * as_sparse_moe_expert.  flags: AS_FLAG_FORCE_DENSE (every routed neuron kept),
+ * AS_FLAG_ATOMIC_SPLITK (the routed down stage adds into Y atomically, as in
+ * as_sparse_moe_expert); any other flag is AS_ERR_UNSUPPORTED.
  * Weights: bf16 throughout; w_router [d_model, E] input-major, 16-byte aligned;
  * the shared expert in THRESHOLD layout with the experts' d_model.
  * Limits: 1 <= T <= 8, E % 8 == 0, 8 <= E <= 512, 1 <= top_k <= min(32, E),

@@ -168,6 +168,37 @@ def test_moe_layer_one_stream_equals_composition(T, dense, monkeypatch):
     assert torch.equal(Y3, Y1)
 
 
+@pytest.mark.parametrize("T", [1, 4, 12])
+def test_moe_atomic_splitk(T):
+    """AS_FLAG_ATOMIC_SPLITK: each (token, slot) adds its weighted rows' sum into Y with
+    atomics.  The layer (one stream up to 8 tokens, composed above) keeps the
+    intermediates bit for bit and agrees with the deterministic layer to 1e-5 (same
+    terms, another order of additions) and with the oracle; the routed experts alone
+    overwrite a NaN-filled Y without AS_FLAG_ACCUMULATE and add onto it with it."""
+    announce(f"moe atomic split-K T={T}")
+    c = datagen.CFG5
+    w, dw = _weights(c["n_experts"], c["d_model"], c["d_ff_e"], c["d_ff_shared"])
+    X = datagen.student_t((T, c["d_model"]), datagen.seed_for(5, T, "decode")).to(DEV)
+    Y1, d1 = asg.moe_layer(X, dw, c["top"], c["keep"], flags=L.AS_FLAG_ATOMIC_SPLITK, debug=True)
+    Y2, d2 = asg.moe_layer(X, dw, c["top"], c["keep"], debug=True)
+    torch.cuda.synchronize()
+    for k in ("logits", "ids", "wts", "h", "keep"):
+        assert torch.equal(d1[k], d2[k]), k
+    assert rel_err(Y1, f64(Y2)) < 1e-5
+    if T <= 4:
+        _check_layer(c["n_experts"], c["d_model"], c["d_ff_e"], c["d_ff_shared"], T, c["top"], c["keep"],
+                     datagen.seed_for(5, T, "decode"))
+    Yn = torch.full((T, c["d_model"]), float("nan"), device=DEV)
+    asg.as_sparse_moe_expert(X, dw, d2["ids"], d2["wts"], c["keep"], flags=L.AS_FLAG_ATOMIC_SPLITK, Y=Yn)
+    Yr = asg.as_sparse_moe_expert(X, dw, d2["ids"], d2["wts"], c["keep"])
+    assert rel_err(Yn, f64(Yr)) < 1e-5
+    Y0 = torch.randn(T, c["d_model"], device=DEV)
+    Ya = Y0.clone()
+    asg.as_sparse_moe_expert(X, dw, d2["ids"], d2["wts"], c["keep"],
+                             flags=L.AS_FLAG_ATOMIC_SPLITK | L.AS_FLAG_ACCUMULATE, Y=Ya)
+    assert rel_err(Ya, f64(Y0) + f64(Yr)) < 1e-5
+
+
 def test_moe_layer_one_stream_small_shapes():
     """Odd shapes through the one-stream layer against the oracle (E = 8, d_model 64,
     d_ff_e 48, shared d_ff 128; unaligned token rows take the LDS staging path)."""
