@@ -209,6 +209,9 @@ def headline(a, C):
     dense_ms, _, _, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE, a.steps, a.warmup, per_kernel=False)
     _, dk1, dk2, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE, a.steps, 2, per_kernel=True)
     dense_us = dense_ms * 1e3 / (a.steps * a.layers)
+    dense_at_ms, _, _, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK, a.steps, a.warmup,
+                               per_kernel=False)
+    dense_at_us = dense_at_ms * 1e3 / (a.steps * a.layers)
     dense_bytes = d * row_gu + f * row_d
     log(f"dense {dense_us:.2f} us/layer {dense_bytes / (dense_us * 1e-6) / 1e9:.0f} GB/s")
     m = res[a.sparsity]
@@ -235,6 +238,8 @@ def headline(a, C):
         "speedup_vs_dense": round(dense_us / m["us_per_layer"], 3),
         "frac_of_peak_layer": round(m["gbs"] / PEAK_HBM_GBS, 4),
         "atomic_splitk": {"us_per_layer": round(m["atomic_us_per_layer"], 3), "gbs": round(m["atomic_gbs"], 1),
+                          "dense_us_per_layer": round(dense_at_us, 3),
+                          "speedup_vs_dense": round(dense_at_us / m["atomic_us_per_layer"], 3),
                           "note": "AS_FLAG_ATOMIC_SPLITK: down-stage slices add into fp32 Y with atomics "
                                   "(not bitwise reproducible); value above is the deterministic path"},
         "stage_us": {"gate_up": round(m["stage1_us"], 3), "down": round(m["stage2_us"], 3),
@@ -454,7 +459,10 @@ def row_moe(C, cpu):
         fa = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"], flags=L.AS_FLAG_ATOMIC_SPLITK)
               for ww in copies * 2]
         us, usd = C.graph_us(fs, reps=10), C.graph_us(fd, reps=10)
-        usa = C.graph_us(fa, reps=10)
+        fda = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"],
+                                           flags=L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK)
+               for ww in copies * 2]
+        usa, usda = C.graph_us(fa, reps=10), C.graph_us(fda, reps=10)
         _, dbg = asg.moe_layer(X, copies[0], c["top"], c["keep"], debug=True)
         ids = dbg["ids"].cpu().numpy()
         touched = len(np.unique(ids))
@@ -466,10 +474,11 @@ def row_moe(C, cpu):
             d * c["n_experts"] * 2
         dense_b = touched * (e_gu + c["d_ff_e"] * d * 2) + (3 * d * c["d_ff_shared"]) * 2 + d * c["n_experts"] * 2
         cases.append({"tokens": T, "experts_touched": touched, "us": r4(us), "dense_us": r4(usd),
-                      "speedup": r4(usd / us), "atomic_splitk_us": r4(usa),
+                      "speedup": r4(usd / us),
+                      "atomic_splitk": {"us": r4(usa), "dense_us": r4(usda), "speedup": r4(usda / usa)},
                       "active_mb": r4(ab / 1e6), "dense_mb": r4(dense_b / 1e6),
                       "gbs": r4(ab / (us * 1e-6) / 1e9), "frac_hbm": r4(ab / (us * 1e-6) / 8e12)})
-        log(f"moe T={T}: {us:.1f} us (dense {usd:.1f}, atomic split-K {usa:.1f})")
+        log(f"moe T={T}: {us:.1f} us (dense {usd:.1f}); atomic split-K {usa:.1f} (dense {usda:.1f})")
     r = {"step": "a8+a9 MoE layer: router GEMV + top-8/softmax, dense shared expert, routed experts "
                  "(dense gate/up scoring, exact top-77 of 768, gathered down rows)",
          "shape": "128 experts, d_model 2048, d_ff_e 768, shared d_ff 4096, bf16", "cases": cases}
@@ -498,6 +507,10 @@ def row_batch16(C, cpu, t_x, t_h):
     us = C.graph_us([lambda w=w: asg.as_sparse_swiglu_mlp(X, w, t_x, t_h, Y=Y) for w in copies * 2])
     usd = C.graph_us([lambda w=w: asg.as_sparse_swiglu_mlp(X, w, flags=L.AS_FLAG_FORCE_DENSE, Y=Y)
                       for w in copies * 2])
+    usa = C.graph_us([lambda w=w: asg.as_sparse_swiglu_mlp(X, w, t_x, t_h, flags=L.AS_FLAG_ATOMIC_SPLITK, Y=Y)
+                      for w in copies * 2])
+    usda = C.graph_us([lambda w=w: asg.as_sparse_swiglu_mlp(X, w, flags=L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK,
+                                                            Y=Y) for w in copies * 2])
     _, dbg = asg.as_sparse_swiglu_mlp(X, w0, t_x, t_h, debug=True)
     ux = int((X.float().abs() > t_x).any(dim=0).sum().item())
     uh = int((dbg["h"].abs() > t_h).any(dim=0).sum().item())
@@ -506,6 +519,7 @@ def row_batch16(C, cpu, t_x, t_h):
     torch.cuda.empty_cache()
     return {"step": "a10 16-token batch on the matrix cores (MFMA gathered skinny GEMM), Llama MLP, 50% thresholds",
             "us": r4(us), "dense_us": r4(usd), "speedup": r4(usd / us),
+            "atomic_splitk": {"us": r4(usa), "dense_us": r4(usda), "speedup": r4(usda / usa)},
             "union_rows_x": ux, "union_rows_h": uh, "active_mb": r4(ab / 1e6),
             "gbs": r4(ab / (us * 1e-6) / 1e9), "frac_hbm": r4(ab / (us * 1e-6) / 8e12),
             "note": "with per-token thresholds the union of active rows over 16 tokens covers nearly every row"}
