@@ -95,3 +95,50 @@ def test_graph_moe_layer_one_stream():
         asg.as_moe_layer(X, dw, 4, 13)
         asg.moe_layer(X, dw, 4, 26, one_stream=False)
         torch.cuda.synchronize()
+
+
+def test_graph_atomic_splitk_replays():
+    """AS_FLAG_ATOMIC_SPLITK under graph replay: the GEMV clears Y with a fill kernel
+    (no memset node), the MLP with its gate/up launch, the MoE layer adds onto the
+    shared expert's Y; every replay lands within 1e-5 of the eager result (atomic
+    additions in any order), with NaN in Y beforehand and eager work in between."""
+    announce("graph atomic split-K")
+    shape = datagen.MLPShape(1024, 4096, "bf16")
+    wgu, wd = datagen.mlp_weights_input_major(7, 0, shape)
+    w = asg.MLPWeights(wgu.to(DEV), wd.to(DEV))
+    x = datagen.student_t((4, 1024), 6).to(DEV)
+    Wg = datagen.normal((4096, 2048), 8).to(DEV)
+    xg = datagen.student_t((2, 4096), 9).to(DEV)
+    c = datagen.CFG5
+    mw = datagen.moe_weights(5, 0, n_experts=c["n_experts"], d_model=c["d_model"], d_ff_e=c["d_ff_e"],
+                             d_ff_shared=c["d_ff_shared"])
+    dw = asg.MoEWeights(mw["w_gate_up"].to(DEV), mw["w_down"].to(DEV), mw["w_router"].to(DEV),
+                        asg.MLPWeights(mw["s_gate_up"].to(DEV), mw["s_down"].to(DEV)))
+    xm = datagen.student_t((2, c["d_model"]), 10).to(DEV)
+    A = L.AS_FLAG_ATOMIC_SPLITK
+    ref_y = asg.as_sparse_swiglu_mlp(x, w, 0.7, 0.01, flags=A).clone()
+    ref_g = asg.as_threshold_gemv(xg, Wg, 1.0, flags=A).clone()
+    ref_m = asg.moe_layer(xm, dw, c["top"], c["keep"], flags=A).clone()
+    Y = torch.empty((4, 1024), dtype=torch.float32, device=DEV)
+    G = torch.empty((2, 2048), dtype=torch.float32, device=DEV)
+
+    def step():
+        asg.as_sparse_swiglu_mlp(x, w, 0.7, 0.01, flags=A, Y=Y)
+        asg.as_threshold_gemv(xg, Wg, 1.0, flags=A, Y=G)
+        return asg.moe_layer(xm, dw, c["top"], c["keep"], flags=A)
+
+    g, mout = _capture(step)
+
+    def close(a, b):
+        return float((a - b).abs().max()) <= 1e-5 * float(b.abs().max())
+
+    for rep in range(4):
+        Y.fill_(float("nan"))
+        G.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert close(Y, ref_y), rep
+        assert close(G, ref_g), rep
+        assert close(mout, ref_m), rep
+        asg.as_sparse_swiglu_mlp(x, w, 0.3, 0.0)
+        torch.cuda.synchronize()
