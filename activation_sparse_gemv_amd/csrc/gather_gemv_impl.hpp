@@ -17,7 +17,9 @@
 //     (device-coherent partial stores and a per-tile counter), always in slice
 //     order so the result is bitwise reproducible, and that workgroup runs the
 //     epilogue: store y, or the SwiGLU step h = silu(g) * u, the |h| > t_h mask
-//     and a per-tile compacted list that feeds the down projection.
+//     and a per-tile compacted list that feeds the down projection.  On request
+//     (atomic_y) a y-storing launch skips that combine instead: every slice adds
+//     its tile into an fp32 y with atomic adds, in no fixed order.
 #pragma once
 #include "common.hpp"
 #include "internal.hpp"
