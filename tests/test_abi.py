@@ -35,6 +35,19 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
         assert n in names, f"binding declares {n}, header does not"
 
 
+def test_enum_values_match_the_header():
+    """Every enumerator of actsparse.h (status codes, dtypes, flags, modes) has the same
+    value in the binding, so a flag or code added on one side cannot drift."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    found = {}
+    for name, expr in re.findall(r"\b(AS_[A-Z0-9_]+)\s*=\s*([0-9]+u?(?:\s*<<\s*[0-9]+)?)", src):
+        m = re.fullmatch(r"([0-9]+)u?(?:\s*<<\s*([0-9]+))?", expr.strip())
+        found[name] = int(m.group(1)) << int(m.group(2) or 0)
+    assert {"AS_OK", "AS_ERR_HIP", "AS_BF16", "AS_FLAG_ATOMIC_SPLITK", "AS_TOPK_RANK_BLEND"} <= set(found)
+    for name, v in found.items():
+        assert getattr(L, name) == v, name
+
+
 def test_version_and_strings(lib):
     assert lib.as_version() == 100
     assert lib.as_status_string(L.AS_ERR_WORKSPACE) == b"AS_ERR_WORKSPACE"
