@@ -51,7 +51,8 @@ class ASBlockThresholds(ctypes.Structure):
 
 class ASBlockDebug(ctypes.Structure):
     _fields_ = [("xn", c_void_p), ("qkv", c_void_p), ("o", c_void_p), ("h1", c_void_p), ("xn2", c_void_p),
-                ("h", c_void_p)]
+                ("h", c_void_p), ("qkv_in", ASMaskOut), ("o_in", ASMaskOut), ("gate_up_in", ASMaskOut),
+                ("down_in", ASMaskOut)]
 
 
 class ASMlpDebug(ctypes.Structure):
@@ -65,7 +66,8 @@ SIGNATURES = {
     "as_last_error": (c_char_p, []),
     "as_workspace_init": (c_int, [c_void_p, c_size_t, c_void_p]),
     "as_calibrate_threshold_ws_size": (c_size_t, [c_int64]),
-    "as_calibrate_threshold": (c_int, [c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "as_calibrate_threshold": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_size_t,
+                                       c_void_p]),
     "as_threshold_gemv_ws_size": (c_size_t, [c_int, c_int, c_int]),
     "as_threshold_gemv": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_float,
                                   c_void_p, c_int, c_uint, POINTER(ASMaskOut), c_void_p, c_size_t, c_void_p]),

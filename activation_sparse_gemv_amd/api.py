@@ -10,8 +10,6 @@ counters at zero after every call, so reuse on one stream is safe.
 from __future__ import annotations
 
 import ctypes
-import os
-import math
 from dataclasses import dataclass
 from fractions import Fraction
 from typing import Optional
@@ -48,12 +46,9 @@ def _need_cuda(*ts):
 
 
 def workspace(key, nbytes: int, device: torch.device) -> torch.Tensor:
-    """Zero-filled workspace cached per call shape.  The carve-up of a workspace
-    follows the launch plan, which the AS_* tuning variables can change, so they
-    are part of the key (a workspace reused under another plan could hold stale
-    bytes where the new plan keeps its counters)."""
-    plan_env = tuple(sorted((k, v) for k, v in os.environ.items() if k.startswith("AS_")))
-    k = (key, nbytes, str(device), plan_env)
+    """Zero-filled workspace cached per call shape (the library's launch plan, and so
+    the workspace's carve-up, is a function of the shapes alone)."""
+    k = (key, nbytes, str(device))
     ws = _WS.get(k)
     if ws is None:
         ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
@@ -65,25 +60,18 @@ def as_version() -> int:
     return L.load().as_version()
 
 
-def nearest_rank(p: float, n: int) -> int:
-    """1-based rank ceil(p * n) of the decimal p (argument of as_calibrate_threshold)."""
-    if p <= 0:
-        return 0
-    return min(n, max(1, math.ceil(Fraction(repr(float(p))) * n)))
-
-
 def as_calibrate_threshold(pool: torch.Tensor, p: float | None = None, rank: int | None = None) -> torch.Tensor:
-    """Threshold for target sparsity p (or an explicit 1-based rank) from a
-    calibration pool; returns a 1-element fp32 device tensor."""
+    """Threshold for target sparsity p (the decimal p is passed to the library as the
+    exact rational it prints as) or for an explicit 1-based rank (passed as the
+    rational rank / n) from a calibration pool; returns a 1-element fp32 device tensor."""
     _need_cuda(pool)
     n = pool.numel()
-    if rank is None:
-        rank = nearest_rank(p, n)
+    q = Fraction(int(rank), n) if rank is not None else Fraction(repr(float(p))) if p > 0 else Fraction(0)
     out = torch.empty(1, dtype=torch.float32, device=pool.device)
     lib = L.load()
     nb = lib.as_calibrate_threshold_ws_size(n)
     ws = workspace(("calibrate",), nb, pool.device)
-    L.check(lib.as_calibrate_threshold(_ptr(pool), _dt(pool), n, rank, _ptr(out), _ptr(ws), nb,
+    L.check(lib.as_calibrate_threshold(_ptr(pool), _dt(pool), n, q.numerator, q.denominator, _ptr(out), _ptr(ws), nb,
                                        _stream(pool.device)), "as_calibrate_threshold")
     return out
 
@@ -194,7 +182,8 @@ def as_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float = float("-in
             dbg.h = _ptr(dd["h"])
             if w.mode == L.AS_MLP_THRESHOLD:
                 dd["x_mask"] = _mask_bufs(M, d, X.device, M == 1)
-                dd["h_mask"] = dict(bits=torch.zeros((M, (f + 63) // 64), dtype=torch.int64, device=X.device))
+                dd["h_mask"] = dict(bits=torch.zeros((M, (f + 63) // 64), dtype=torch.int64, device=X.device),
+                                    nnz=torch.zeros(M, dtype=torch.int32, device=X.device))
                 dbg.x_mask = _mask_struct(dd["x_mask"])
                 dbg.h_mask = _mask_struct(dd["h_mask"])
         if events is not None:
@@ -483,13 +472,42 @@ def as_decoder_block(X: torch.Tensor, w: BlockWeights, k_cache: torch.Tensor, v_
     dbg = None
     if debug:
         nqkv = (w.n_q + 2 * w.n_kv) * w.head_dim
+        no = w.n_q * w.head_dim
         z = lambda n: torch.zeros(n, dtype=torch.float32, device=X.device)  # noqa: E731
-        dd = dict(xn=z(d), qkv=z(nqkv), o=z(w.n_q * w.head_dim), h1=z(d), xn2=z(d), h=z(w.mlp.d_ff))
-        dbg = L.ASBlockDebug(*(_ptr(dd[k]) for k in ("xn", "qkv", "o", "h1", "xn2", "h")))
+        dd = dict(xn=z(d), qkv=z(nqkv), o=z(no), h1=z(d), xn2=z(d), h=z(w.mlp.d_ff))
+        masks = dict(qkv_in=_mask_bufs(1, d, X.device, True), o_in=_mask_bufs(1, no, X.device, True),
+                     gate_up_in=_mask_bufs(1, d, X.device, True), down_in=_mask_bufs(1, w.mlp.d_ff, X.device, False))
+        dd.update(masks)
+        dbg = L.ASBlockDebug(*(_ptr(dd[k]) for k in ("xn", "qkv", "o", "h1", "xn2", "h")),
+                             *(_mask_struct(masks[k]) for k in ("qkv_in", "o_in", "gate_up_in", "down_in")))
     L.check(lib.as_decoder_block(_ptr(X1), _dt(X1), ctypes.byref(st), _ptr(k_cache), _ptr(v_cache), n_ctx,
                                  ctypes.byref(th), _ptr(Y), flags, ctypes.byref(dbg) if dbg is not None else None,
                                  _ptr(ws), ws.numel(), _stream(X.device)), "as_decoder_block")
     return (Y, dd) if debug else Y
+
+
+def calibrate_decoder_block(Xc: torch.Tensor, w: BlockWeights, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            p: float, flags: int = 0, keep_pools: bool = False):
+    """Thresholds of one block's four thresholded inputs (qkv, o, gate_up, down) at
+    target sparsity p from calibration vectors Xc [n, d] (the block's inputs).
+
+    The pools are taken in input order, each with the thresholds of the earlier
+    inputs applied (TEAL slides, method slide: thresholds from calibration data for
+    the target sparsity); every pool and threshold is computed by the library
+    (as_decoder_block's exported intermediates, as_calibrate_threshold).  Returns
+    (thresholds, Y [n, d] fp32 = the block's outputs, which are the next block's
+    calibration inputs, and the pools when keep_pools)."""
+    inf = float("-inf")
+    t = dict(qkv=inf, o=inf, gate_up=inf, down=inf)
+    pools = {}
+    for key, src in (("qkv", "xn"), ("o", "o"), ("gate_up", "xn2"), ("down", "h")):
+        pool = torch.stack([as_decoder_block(Xc[i], w, k_cache, v_cache, t, flags=flags, debug=True)[1][src]
+                            for i in range(Xc.shape[0])])
+        t[key] = float(as_calibrate_threshold(pool, p).item())
+        if keep_pools:
+            pools[key] = pool
+    Y = torch.stack([as_decoder_block(Xc[i], w, k_cache, v_cache, t, flags=flags) for i in range(Xc.shape[0])])
+    return t, Y, (pools if keep_pools else None)
 
 
 def as_glass_local_signal(X: torch.Tensor, w: MLPWeights) -> torch.Tensor:

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <string>
 
 #include "internal.hpp"
@@ -36,6 +37,12 @@ bool is_wdt(as_dtype d) { return d == AS_F16 || d == AS_BF16; }
 bool is_dt(as_dtype d) { return d == AS_F16 || d == AS_BF16 || d == AS_F32; }
 int mt_for(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+size_t dt_bytes(as_dtype d) { return d == AS_F32 ? 4 : 2; }
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
 
 int num_cus() {
   static int cus = -1;
@@ -56,11 +63,6 @@ struct Plan {
   int lpr, n_tiles, S, cap;
 };
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
 // LDS per workgroup on gfx950, and what a plan keeps free of it beyond the row list
 // and its activations (slot reduction or staged MFMA chunk, list prefix sums).
 constexpr int kLdsBytes = 160 * 1024;
@@ -68,7 +70,9 @@ constexpr int kLdsBytes = 160 * 1024;
 constexpr int kMaxRows = 1 << 24;
 constexpr int kLdsReserve = 40 * 1024;
 
-Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
+// The plan is a function of the shapes (and the device's CU count) only, so the
+// workspace size a query returns always matches the call.
+Plan plan_gemv(int rows, int cols, bool gu, int mt) {
   // Tile width: lanes_per_row * 8 columns.  Wider tiles give longer bursts per
   // row; narrower tiles give more tiles (less split-K, cheaper final combine).
   const long tot_cols = gu ? 2L * cols : cols;
@@ -76,9 +80,7 @@ Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
   if (tot_cols >= 512L * 48) lpr = 64;
   else if (gu) lpr = 32;
   else lpr = 16;
-  char key[64];
-  snprintf(key, sizeof key, "%s_LPR", env_prefix);
-  if (mt >= 16 && env_int(key, 0) == 0) {
+  if (mt >= 16) {
     // matrix-core path: slices of <= 512 rows; widen the tile until the grid fits
     // two workgroups per CU (a second round of workgroups would double the time)
     const int s16 = (rows + 511) / 512;
@@ -89,7 +91,6 @@ Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
       lpr *= 2;
     }
   }
-  lpr = env_int(key, lpr);
   const int tn = lpr * 8;
   const int n_tiles = gu ? (cols + tn / 2 - 1) / (tn / 2) : (cols + tn - 1) / tn;
   // Slices: about 1.75 workgroups per CU in total, at least 128 rows per slice
@@ -113,9 +114,6 @@ Plan plan_gemv(int rows, int cols, bool gu, const char* env_prefix, int mt) {
     const int s16 = (rows + 511) / 512;
     if (S < s16) S = s16;
   }
-  snprintf(key, sizeof key, "%s_S", env_prefix);
-  S = env_int(key, S);
-  if (S < 1) S = 1;
   if ((rows + S - 1) / S > hard_cap) S = (rows + hard_cap - 1) / hard_cap;
   // multiple of 8 rows: the MFMA loop reads activations as aligned 16-byte vectors
   const int cap = (((rows + S - 1) / S) + 7) & ~7;
@@ -152,32 +150,26 @@ struct MlpWs {
   int* l_cnt;
   int* l_idx;
   float* l_val;
-  unsigned* queue;        // one-launch MLP: [1] exit count, [2] error flag, [3] ready-list length
-  unsigned* fx_cnt;       // one-launch MLP: finished gate/up slices per h range
-  unsigned* fx_ready;     // one-launch MLP: ready list of h ranges, kCntStride apart
 };
 
 struct MlpPlan {
   Plan p1, p2;
   int n_lt, lt_stride;
-  int parts2;             // partial slots of the down stage (max of its split and the h-tiles)
-  int s2_tiles, cap2_tiles;  // down stage over whole h-tiles (AS_DN_TILES): slices, max list entries
-  int s2_range, cap2_range;  // down stage masking h by range (two launches): slices, max range length
+  int parts2;             // partial slots of the down stage (max of its split and the ranges)
+  int s2_range, cap2_range;  // down stage masking h by range: slices, max range length
   int cap1_range;            // gate/up stage masking x by range (several tokens): max range length
-  int fx_groups, fx_k2, fx_ranges, cap2_fused;  // one-launch MLP: XCD groups, h ranges per group (at
-                                                // most) and in all, max range length
 };
 
 MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
   MlpPlan mp;
   if (mode == AS_MLP_THRESHOLD) {
-    mp.p1 = plan_gemv(w->d_model, w->d_ff, true, "AS_GU", mt_for(M));
+    mp.p1 = plan_gemv(w->d_model, w->d_ff, true, mt_for(M));
     // One token with the down stage summing the unsummed gate/up partials: at most
     // one gate/up workgroup per CU (fewer partials for the down prologue to read,
     // and the workgroups finish together; measured on the Llama shape).
     // (The dense baseline takes the same plan, and the workspace size does not
     // depend on the flags.)
-    if (M == 1 && env_int("AS_DN_PARTS", 1) != 0 && getenv("AS_GU_S") == nullptr) {
+    if (M == 1) {
       const int per_cu = num_cus() / (mp.p1.n_tiles > 0 ? mp.p1.n_tiles : 1);
       if (per_cu >= 2 && per_cu < mp.p1.S) {
         mp.p1.S = per_cu;
@@ -196,7 +188,7 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     mp.cap1_range = ((units + mp.p1.S - 1) / mp.p1.S) * 64;
   }
   (void)dense;
-  mp.p2 = plan_gemv(w->d_ff, w->d_model, false, "AS_DN", mt_for(M));
+  mp.p2 = plan_gemv(w->d_ff, w->d_model, false, mt_for(M));
   {
     // threshold mode, two launches: down slice s masks its own 64-aligned range of h
     // (several tokens also stage the range of every token in LDS)
@@ -211,43 +203,8 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     mp.s2_range = S;
     mp.cap2_range = ((units + S - 1) / S) * 64;
   }
-  {
-    // one-launch MLP: group x (one per XCD) owns gate/up tiles and the h rows they
-    // produce, split into fx_k2 down ranges
-    mp.fx_groups = 8;
-    mp.fx_k2 = env_int("AS_FX_K2", 2);
-    if (mp.fx_k2 < 1) mp.fx_k2 = 1;
-    // ranges of whole gate/up tiles: min(k2, tiles of the group) per group
-    const int tb1 = mp.p1.lpr * 4;
-    const int G = mp.fx_groups;
-    mp.fx_ranges = 0;
-    for (int x = 0; x < G; ++x) {
-      const int nt = (int)(((long)(x + 1) * mp.p1.n_tiles) / G - ((long)x * mp.p1.n_tiles) / G);
-      mp.fx_ranges += nt < mp.fx_k2 ? nt : mp.fx_k2;
-    }
-    const int nt_max = (mp.p1.n_tiles + G - 1) / G;
-    const int nr_max = nt_max < mp.fx_k2 ? nt_max : mp.fx_k2;
-    const long rows = (long)((nt_max + nr_max - 1) / (nr_max > 0 ? nr_max : 1)) * tb1;
-    mp.cap2_fused = (int)(rows < w->d_ff ? rows : w->d_ff);
-  }
   mp.parts2 = mp.p2.S > mp.n_lt ? mp.p2.S : mp.n_lt;
   if (mp.s2_range > mp.parts2) mp.parts2 = mp.s2_range;
-  if (mp.fx_ranges > mp.parts2) mp.parts2 = mp.fx_ranges;
-  {
-    // down stage over whole h-tiles: each slice owns whole h-tiles (about 1.75 workgroups per CU)
-    const int target = (7 * num_cus()) / 4;
-    int tpw = (int)((long)mp.n_lt * mp.p2.n_tiles / (target > 0 ? target : 1));
-    // list entries per slice: index + activations in LDS twice (raw, then compacted)
-    const int mt = mt_for(M);
-    const int hard_e = (kLdsBytes - kLdsReserve) / (8 + 8 * mt);
-    const int pref_e = mt >= 16 ? 512 : hard_e;
-    if (tpw * mp.lt_stride > pref_e) tpw = pref_e / mp.lt_stride;
-    tpw = env_int("AS_DN_TPW", tpw < 1 ? 1 : tpw);
-    if (tpw * mp.lt_stride > hard_e) tpw = hard_e / mp.lt_stride;
-    if (tpw < 1) tpw = 1;
-    mp.s2_tiles = (mp.n_lt + tpw - 1) / tpw;
-    mp.cap2_tiles = ((mp.n_lt + mp.s2_tiles - 1) / mp.s2_tiles) * mp.lt_stride;
-  }
   return mp;
 }
 
@@ -262,9 +219,6 @@ MlpWs carve_mlp(Carver& c, const MlpPlan& mp, int M, const as_mlp_weights* w, as
   ws.l_cnt = c.take<int>(mp.n_lt);
   ws.l_idx = c.take<int>(w->d_ff);
   ws.l_val = c.take<float>(size_t(w->d_ff) * M);
-  ws.queue = c.take<unsigned>(4);
-  ws.fx_cnt = c.take<unsigned>(mode == AS_MLP_THRESHOLD ? size_t(mp.fx_ranges) : 0);
-  ws.fx_ready = c.take<unsigned>(mode == AS_MLP_THRESHOLD ? size_t(mp.fx_ranges) * kCntStride : 0);
   return ws;
 }
 
@@ -310,18 +264,22 @@ as_status as_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
 as_status as_bench_flush(void* buf, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return AS_OK;
   if (!buf) return fail(AS_ERR_INVALID_ARG, "as_bench_flush: buf is NULL");
-  static uint32_t salt = 1;
-  return hip_check(launch_fill_pattern(buf, bytes, 0x9e3779b9u * salt++, stream), "as_bench_flush");
+  static std::atomic<uint32_t> salt{1};
+  return hip_check(launch_fill_pattern(buf, bytes, 0x9e3779b9u * salt.fetch_add(1u), stream), "as_bench_flush");
 }
 
 size_t as_calibrate_threshold_ws_size(int64_t n) { return n < 1 ? 0 : up256(calibrate_ws_bytes()); }
 
-as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64_t rank, float* t_out, void* ws,
-                                 size_t ws_bytes, hipStream_t stream) {
+as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64_t p_num, int64_t p_den,
+                                 float* t_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!pool || !t_out) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: NULL pointer");
   if (!is_dt(dt)) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: bad dtype %d", int(dt));
-  if (n < 1 || n > 2147483647LL || rank < 0 || rank > n)
-    return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: n=%lld rank=%lld", (long long)n, (long long)rank);
+  if (n < 1 || n > 2147483647LL || p_den < 1 || p_num < 0 || p_num > p_den)
+    return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: n=%lld p=%lld/%lld", (long long)n, (long long)p_num,
+                (long long)p_den);
+  // nearest rank ceil(p n), exact in 128-bit integers; p = 0 keeps every input
+  const unsigned __int128 num = (unsigned __int128)(uint64_t)p_num * (uint64_t)n;
+  const int64_t rank = p_num == 0 ? 0 : (int64_t)((num + (uint64_t)p_den - 1) / (uint64_t)p_den);
   as_status st = check_ws(ws, ws_bytes, calibrate_ws_bytes());
   if (st != AS_OK) return st;
   return hip_check(launch_calibrate(pool, int(dt), n, rank, t_out, reinterpret_cast<unsigned*>(ws), stream),
@@ -331,7 +289,7 @@ as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64
 // ------------------------------------------------------------------ GEMV
 size_t as_threshold_gemv_ws_size(int M, int K, int N) {
   if (M < 1 || K < 1 || N < 1) return 0;
-  const Plan pl = plan_gemv(K, N, false, "AS_GV", mt_for(M));
+  const Plan pl = plan_gemv(K, N, false, mt_for(M));
   Carver c{nullptr};
   carve_gemv(c, pl, M, N);
   return c.off;
@@ -366,7 +324,7 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   if (K > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "%s: K=%d above %d", fn, K, kMaxRows);
   if (!aligned16(W)) return fail(AS_ERR_INVALID_ARG, "%s: W not 16-byte aligned", fn);
   if (mo && mo->idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: mask idx export needs M == 1", fn);
-  const Plan pl = plan_gemv(K, N, false, "AS_GV", mt_for(M));
+  const Plan pl = plan_gemv(K, N, false, mt_for(M));
   if ((long)pl.S * M * N >= (1L << 31))
     return fail(AS_ERR_UNSUPPORTED, "%s: split-K partials of %d x %d x %d exceed 2^31 elements", fn, pl.S, M, N);
   Carver c{reinterpret_cast<char*>(ws)};
@@ -385,7 +343,7 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   const bool norm = fz != nullptr && fz->norm;
   if (norm && (M != 1 || !can_norm_in_prologue(X, x_dt, K)))
     return fail(AS_ERR_UNSUPPORTED, "%s: input normalisation needs one aligned token", fn);
-  if (!dense && !exports && !norm && env_int("AS_GV_RANGE", 1) != 0) {
+  if (!dense && !exports && !norm) {
     const int units = (K + 63) / 64;
     int S = pl.S;
     if (S > units / 2) S = units / 2 > 1 ? units / 2 : 1;
@@ -415,6 +373,9 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   if (flags & AS_FLAG_ATOMIC_SPLITK) {
     if (y_dt != AS_F32) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_ATOMIC_SPLITK needs an fp32 Y", fn);
     p.atomic_y = 1;
+    // the fill launch clears Y before X is read: they must not overlap
+    if (!p.accumulate && overlaps(X, size_t(M) * K * dt_bytes(x_dt), Y, size_t(M) * N * 4))
+      return fail(AS_ERR_INVALID_ARG, "%s: AS_FLAG_ATOMIC_SPLITK without AS_FLAG_ACCUMULATE needs Y apart from X", fn);
     if (!p.accumulate) {
       as_status st2 = hip_check(launch_fill_zero(Y, size_t(M) * N * sizeof(float), stream), fn);
       if (st2 != AS_OK) return st2;
@@ -495,12 +456,14 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   const bool atomic = (flags & AS_FLAG_ATOMIC_SPLITK) != 0;
   const bool clear_y = atomic && (flags & AS_FLAG_ACCUMULATE) == 0;
   if (atomic && y_dt != AS_F32) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_ATOMIC_SPLITK needs an fp32 Y", fn);
+  // with the atomic down stage, Y is cleared by the first launch while X may still be read
+  if (clear_y && overlaps(X, size_t(M) * w->d_model * dt_bytes(x_dt), Y, size_t(M) * w->d_model * 4))
+    return fail(AS_ERR_INVALID_ARG, "%s: AS_FLAG_ATOMIC_SPLITK without AS_FLAG_ACCUMULATE needs Y apart from X", fn);
   if (mode == AS_MLP_NEURON_SET && !dense) {
     if (n_active < 0 || n_active > w->d_ff) return fail(AS_ERR_INVALID_ARG, "%s: n_active=%d", fn, n_active);
     if (n_active > 0 && !neuron_idx) return fail(AS_ERR_INVALID_ARG, "%s: neuron_idx is NULL", fn);
   }
-  if (dbg && (dbg->h_mask.idx || dbg->h_mask.nnz))
-    return fail(AS_ERR_UNSUPPORTED, "%s: h mask exports bits only", fn);
+  if (dbg && dbg->h_mask.idx) return fail(AS_ERR_UNSUPPORTED, "%s: the h mask exports bits and nnz only", fn);
   if (dbg && dbg->x_mask.idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: x mask idx export needs M == 1", fn);
   if (dbg && mode == AS_MLP_NEURON_SET && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz || dbg->h_mask.bits))
     return fail(AS_ERR_UNSUPPORTED, "%s: mask exports exist in THRESHOLD mode only", fn);
@@ -527,79 +490,14 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   GemvParams p2 = base_params();
   GemvConfig c2{int(w->w_dt), mt, mp.p2.lpr, IN_LISTS, OUT_Y, false, nt};
 
-  // One launch for both stages (threshold mode, up to 8 tokens): gate/up
-  // workgroups, then down workgroups that start on their range of h as soon as the
-  // gate/up tiles covering it are complete (grouped by XCD).
-  const bool try_fused = fz == nullptr && mode == AS_MLP_THRESHOLD && mt <= 8 && nt &&
-                         (flags & AS_FLAG_NO_FUSION) == 0 && !atomic &&
-                         env_int("AS_FUSED", 0) != 0 && (mp.p1.lpr == 32 || mp.p1.lpr == 64) &&
-                         (mp.p2.lpr == 16 || mp.p2.lpr == 32) &&
-                         (long)mp.cap2_fused * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
-  if (try_fused) {
-    const bool x_exports = dbg && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz);
-    const bool gu_range = !dense && (M > 1 ? env_int("AS_GU_RANGE", 1) != 0 : env_int("AS_GU_RANGE", 1) == 2) &&
-                          !x_exports &&
-                          (long)mp.cap1_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
-    FusedMlpParams fz;
-    memset(&fz, 0, sizeof fz);
-    GemvParams& q1 = fz.p1;
-    q1 = base_params();
-    q1.x = X; q1.x_dt = int(x_dt); q1.M = M; q1.K = d; q1.ldx = d; q1.t = dense ? -INFINITY : t_x;
-    q1.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); q1.ldw = 2L * f; q1.N = f; q1.gu_off = f;
-    q1.n_tiles = mp.p1.n_tiles; q1.S = mp.p1.S; q1.cap = gu_range ? mp.cap1_range : mp.p1.cap;
-    q1.partials = mw.g1.partials; q1.part_ld = 2L * f;
-    if (dbg && !dense) {
-      q1.x_bits = dbg->x_mask.bits; q1.x_bits_ld = (d + 63) / 64; q1.x_idx = dbg->x_mask.idx; q1.x_nnz = dbg->x_mask.nnz;
-    }
-    GemvParams& q2 = fz.p2;
-    q2 = base_params();
-    q2.M = M; q2.W = reinterpret_cast<const uint16_t*>(w->w_down); q2.ldw = d; q2.N = d;
-    q2.x = mw.g1.partials; q2.x_dt = AS_F32; q2.K = f; q2.ldx = 2L * f; q2.t = dense ? -INFINITY : t_h;
-    q2.x_parts = mp.p1.S; q2.x_up = f; q2.keep_all = dense ? 1 : 0;
-    q2.h = (dbg && dbg->h) ? dbg->h : nullptr; q2.ldh = f;
-    if (dbg && !dense) { q2.h_bits = dbg->h_mask.bits; q2.h_bits_ld = (f + 63) / 64; }
-    q2.n_tiles = mp.p2.n_tiles; q2.S = mp.fx_ranges; q2.cap = mp.cap2_fused;
-    q2.partials = mw.g2.partials; q2.counters = mw.g2.counters; q2.part_ld = d;
-    q2.y = Y; q2.y_dt = int(y_dt); q2.ldy = d; q2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
-    q2.err_flag = mw.queue + 2;
-    fz.n_tiles1 = mp.p1.n_tiles; fz.S1 = mp.p1.S; fz.tb1 = mp.p1.lpr * 4;
-    fz.n_ct2 = mp.p2.n_tiles; fz.k2 = mp.fx_k2; fz.groups = mp.fx_groups; fz.n_ranges = mp.fx_ranges;
-    fz.g1 = fz.groups * ((fz.n_tiles1 + fz.groups - 1) / fz.groups) * fz.S1;
-    fz.g2 = fz.n_ranges * fz.n_ct2;
-    fz.range_cnt = mw.fx_cnt; fz.ready = mw.fx_ready; fz.ready_tail = mw.queue + 3;
-    fz.exit_cnt = mw.queue + 1; fz.err = mw.queue + 2;
-    const int in1 = dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH);
-    GemvConfig c1{int(w->w_dt), mt, mp.p1.lpr, in1, OUT_PARTS, true, true};
-    GemvConfig c2f{int(w->w_dt), mt, mp.p2.lpr, IN_PARTS, OUT_Y, false, true};
-    const size_t sm1 = gemv_smem_bytes(c1, q1.cap, 0), sm2 = gemv_smem_bytes(c2f, q2.cap, 0);
-    int nv = 0;
-    if (in1 == IN_THRESH) {
-      nv = pick_chunk_vectors(X, int(x_dt), d, d);
-      if (mt > 1 && nv > 2) nv = 0;
-    } else if (in1 == IN_RANGE) {
-      nv = (d % 8 == 0 && pick_chunk_vectors(X, int(x_dt), 1, d) > 0) ? 2 : 0;
-    }
-    FusedCfg fc{int(w->w_dt), mt, mp.p1.lpr, mp.p2.lpr, in1, nv};
-    // LDS of at least a third of a CU's, so that at most two workgroups share a CU and
-    // most down workgroups are dispatched as gate/up workgroups of their XCD finish
-    size_t smem = sm1 > sm2 ? sm1 : sm2;
-    const size_t lds_min = size_t(env_int("AS_FX_LDS_KB", 56)) * 1024;
-    if (smem < lds_min) smem = lds_min;
-    if ((st = hip_check(launch_fused_mlp(fc, fz, smem, stream), fn)) != AS_OK) return st;
-    if ((st = rec(1)) != AS_OK) return st;
-    return rec(2);
-  }
-
   if (mode == AS_MLP_THRESHOLD) {
-    // stage 1: x mask -> gate/up gather GEMV -> SwiGLU -> h (and, with the list-tile
-    // down stage, the h mask's per-tile lists)
-    const bool dn_tiles = !dense && env_int("AS_DN_TILES", 0) != 0;
+    // stage 1: x mask -> gate/up gather GEMV -> split-K partials, or the combined
+    // g and u -> SwiGLU -> h
     // several tokens: each gate/up slice masks its own range of x (the union mask
     // over tokens is nearly dense, so equal ranges are balanced); the x mask exports
     // and one token use the evenly split compacted list
     const bool x_exports = dbg && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz);
-    const bool gu_range = !dense && (M > 1 ? env_int("AS_GU_RANGE", 1) != 0 : env_int("AS_GU_RANGE", 1) == 2) &&
-                          !x_exports &&
+    const bool gu_range = !dense && M > 1 && !x_exports &&
                           (long)mp.cap1_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
     // The gate/up launch stores its split-K partials unsummed and the down launch
     // sums them for its own range of h (SwiGLU, mask and compaction in its
@@ -607,20 +505,23 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
     // tile counter and combine of its last workgroups.  One token by default (the
     // down prologue reads every gate/up slice's partial of its range, which for
     // several tokens costs more than the combine it replaces).
-    const bool dn_parts = !dn_tiles && mt <= 8 && env_int("AS_DN_PARTS", mt == 1 ? 1 : 0) != 0 &&
-                          (long)mp.cap2_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
+    const bool dn_parts = mt == 1 && (long)mp.cap2_range * (4 + 8 * mt) <= kLdsBytes - kLdsReserve;
     GemvParams p = base_params();
     p.x = X; p.x_dt = int(x_dt); p.M = M; p.K = d; p.ldx = d; p.t = t_x;
     p.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.ldw = 2L * f; p.N = f; p.gu_off = f;
     p.n_tiles = mp.p1.n_tiles; p.S = mp.p1.S; p.cap = mp.p1.cap;
     p.partials = mw.g1.partials; p.counters = mw.g1.counters; p.part_ld = 2L * f;
     p.t_h = dense ? -INFINITY : t_h; p.h = hbuf; p.ldh = f;
-    if (dn_tiles) { p.o_cnt = mw.l_cnt; p.o_idx = mw.l_idx; p.o_val = mw.l_val; }
     if (dbg && !dense) {
       p.h_bits = dbg->h_mask.bits; p.h_bits_ld = (f + 63) / 64;
       p.x_bits = dbg->x_mask.bits; p.x_bits_ld = (d + 63) / 64; p.x_idx = dbg->x_mask.idx; p.x_nnz = dbg->x_mask.nnz;
     }
-    if (dn_parts) { p.h = nullptr; p.h_bits = nullptr; }
+    int* h_nnz = (dbg && !dense) ? dbg->h_mask.nnz : nullptr;
+    if (h_nnz != nullptr) {
+      // the count is accumulated with atomics by the stage that masks h
+      if ((st = hip_check(launch_fill_zero(h_nnz, size_t(M) * sizeof(int), stream), fn)) != AS_OK) return st;
+    }
+    if (dn_parts) { p.h = nullptr; p.h_bits = nullptr; } else { p.h_nnz = h_nnz; }
     int in1 = dense ? IN_ALL : (gu_range ? IN_RANGE : IN_THRESH);
     if (fz != nullptr && fz->norm) {
       if (M != 1 || !can_norm_in_prologue(X, x_dt, d))
@@ -636,19 +537,17 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
     if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
     // stage 2: down projection over the surviving h rows; each slice masks its
-    // own range of h (or, opt-in, reads whole h-tile lists)
+    // own range of h
     p2.W = reinterpret_cast<const uint16_t*>(w->w_down); p2.ldw = d;
     if (dn_parts) {
       c2.in = IN_PARTS;
       p2.x = mw.g1.partials; p2.x_dt = AS_F32; p2.K = f; p2.ldx = 2L * f; p2.t = dense ? -INFINITY : t_h;
       p2.x_parts = mp.p1.S; p2.x_up = f; p2.keep_all = dense ? 1 : 0;
       p2.h = (dbg && dbg->h) ? dbg->h : nullptr; p2.ldh = f;
-      if (dbg && !dense) { p2.h_bits = dbg->h_mask.bits; p2.h_bits_ld = (f + 63) / 64; }
+      if (dbg && !dense) { p2.h_bits = dbg->h_mask.bits; p2.h_bits_ld = (f + 63) / 64; p2.h_nnz = h_nnz; }
     } else if (dense) {
       c2.in = IN_ALL;
       p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = -INFINITY;
-    } else if (dn_tiles) {
-      c2.in = IN_TILES;
     } else {
       c2.in = IN_RANGE;
       p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = t_h;
@@ -664,7 +563,7 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
     q.idx = dense ? nullptr : neuron_idx; q.n_active = dense ? f : n_active;
     q.h_dbg = dbg ? dbg->h : nullptr; q.ld_hdbg = q.n_active;
     q.o_cnt = mw.l_cnt; q.o_idx = mw.l_idx; q.o_val = mw.l_val;
-    q.neurons_per_wave = env_int("AS_NS_NPW", 2);
+    q.neurons_per_wave = 2;
     if ((st = hip_check(launch_neuron_gu(int(w->w_dt), mt, nt, q, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
     p2.W = reinterpret_cast<const uint16_t*>(w->w_gate_up) + 2L * d; p2.ldw = 3L * d;
@@ -674,7 +573,6 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   p2.n_lt = mp.n_lt; p2.lt_stride = mp.lt_stride;
   p2.N = d;
   p2.n_tiles = mp.p2.n_tiles; p2.S = mp.p2.S; p2.cap = mp.p2.cap;
-  if (c2.in == IN_TILES) { p2.S = mp.s2_tiles; p2.cap = mp.cap2_tiles; }
   if (c2.in == IN_RANGE || c2.in == IN_PARTS) { p2.S = mp.s2_range; p2.cap = mp.cap2_range; }
   p2.partials = mw.g2.partials; p2.counters = mw.g2.counters; p2.part_ld = d;
   p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
@@ -723,7 +621,7 @@ as_status as_moe_router(const float* logits, int T, int E, int top_k, int32_t* i
 // column tile's last workgroup routes every token (OUT_ROUTER).  Same plan as the
 // dense GEMV of as_dense_gemv, so the logits are the same bits.
 static Plan router_plan(int d_model, int E, int T) {
-  Plan pl = plan_gemv(d_model, E, false, "AS_GV", mt_for(T));
+  Plan pl = plan_gemv(d_model, E, false, mt_for(T));
   const int lpr = E <= 128 ? 16 : E <= 256 ? 32 : 64;
   if (pl.lpr < lpr) pl.lpr = lpr;
   pl.n_tiles = 1;
@@ -769,7 +667,7 @@ namespace {
 // Neurons per gate/up workgroup: 16 for one token's 8 items (more workgroups keep
 // every CU busy), 32 beyond (fewer, longer workgroups; measured on the 128-expert,
 // d_model 2048, d_ff_e 768 shape for 1 to 16 tokens).
-int moe_npb(int items) { return env_int("AS_MOE_NPB", items <= 8 ? 16 : 32); }
+int moe_npb(int items) { return items <= 8 ? 16 : 32; }
 
 struct MoeWs {
   float* h;
@@ -798,8 +696,6 @@ MoeWs carve_moe(Carver& c, int T, int top, const as_moe_weights* w) {
 // vs 68.5.  Rows longer than 1024 neurons always select in the down stage.
 bool moe_select_in_gu(int items, int d_ff_e, bool layer) {
   if (d_ff_e > 1024) return false;
-  const int v = env_int("AS_MOE_SEL_GU", -1);
-  if (v >= 0) return v != 0;
   return layer && items > 8;
 }
 }  // namespace
@@ -845,6 +741,8 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   if (flags & AS_FLAG_ATOMIC_SPLITK) {
     if (y_dt != AS_F32) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_ATOMIC_SPLITK needs an fp32 Y", fn);
     p.atomic_y = 1;
+    if (!p.accumulate && overlaps(X, size_t(T) * w->d_model * dt_bytes(x_dt), Y, size_t(T) * w->d_model * 4))
+      return fail(AS_ERR_INVALID_ARG, "%s: AS_FLAG_ATOMIC_SPLITK without AS_FLAG_ACCUMULATE needs Y apart from X", fn);
     if (!p.accumulate && (st = hip_check(launch_fill_zero(Y, size_t(T) * w->d_model * sizeof(float), stream), fn)) != AS_OK)
       return st;
   }
@@ -1136,14 +1034,27 @@ as_status as_decoder_block(const void* X, as_dtype x_dt, const as_block_weights*
   const int nqkv = (w->n_q + 2 * w->n_kv) * hd, no = w->n_q * hd;
   const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
   const unsigned pass = flags & (AS_FLAG_NO_NT_LOADS | AS_FLAG_FORCE_DENSE);
+  if (dbg && dbg->down_in.idx) return fail(AS_ERR_UNSUPPORTED, "%s: the down-input mask exports bits and nnz only", fn);
+  // mask exports of the four thresholded inputs (nullable)
+  as_mask_out* m_qkv = dbg ? &dbg->qkv_in : nullptr;
+  as_mask_out* m_o = dbg ? &dbg->o_in : nullptr;
   float* xn = dbg && dbg->xn ? dbg->xn : b.xn;
   float* qkv = dbg && dbg->qkv ? dbg->qkv : b.qkv;
   float* o = dbg && dbg->o ? dbg->o : b.o;
   float* h1 = dbg && dbg->h1 ? dbg->h1 : b.h1;
   float* xn2 = dbg && dbg->xn2 ? dbg->xn2 : b.xn2;
   const float inf = -INFINITY;
+  as_mlp_debug md;
+  memset(&md, 0, sizeof md);
+  if (dbg) {
+    md.h = dbg->h;
+    md.x_mask = dbg->gate_up_in;
+    md.h_mask = dbg->down_in;
+  }
+  const bool want_md = dbg && (md.h || md.x_mask.bits || md.x_mask.idx || md.x_mask.nnz || md.h_mask.bits ||
+                               md.h_mask.nnz);
   if (can_norm_in_prologue(X, x_dt, d) && can_norm_in_prologue(h1, AS_F32, d) &&
-      env_int("AS_BLOCK_FUSE", 1) != 0) {
+      (flags & AS_FLAG_NO_FUSION) == 0) {
     // The two RMS normalisations run in the prologues of the projections that read
     // them (qkv, and the MLP's gate/up), and the residual adds in the epilogues of
     // the o projection (h1 = X + o W_o) and of the MLP's down stage (Y = h1 + MLP):
@@ -1152,38 +1063,33 @@ as_status as_decoder_block(const void* X, as_dtype x_dt, const as_block_weights*
     f1.norm = true;
     f1.xn_out = dbg ? dbg->xn : nullptr;
     if ((st = gemv_common(X, x_dt, 1, d, w->w_qkv, w->mlp.w_dt, nqkv, dense ? inf : t->qkv, qkv, AS_F32, pass,
-                          nullptr, b.ws_qkv, b.n_qkv, stream, dense, fn, &f1)) != AS_OK) return st;
+                          m_qkv, b.ws_qkv, b.n_qkv, stream, dense, fn, &f1)) != AS_OK) return st;
     if ((st = as_gqa_decode_attention(qkv, qkv + no, qkv + no + w->n_kv * hd, k_cache, v_cache, AS_BF16, n_ctx,
                                       w->n_q, w->n_kv, hd, o, b.ws_attn, b.n_attn, stream)) != AS_OK) return st;
     GemvFuse f2;
     f2.res = X;
     f2.res_dt = int(x_dt);
-    if ((st = gemv_common(o, AS_F32, 1, no, w->w_o, w->mlp.w_dt, d, dense ? inf : t->o, h1, AS_F32, pass, nullptr,
+    if ((st = gemv_common(o, AS_F32, 1, no, w->w_o, w->mlp.w_dt, d, dense ? inf : t->o, h1, AS_F32, pass, m_o,
                           b.ws_o, b.n_o, stream, dense, fn, &f2)) != AS_OK) return st;
     GemvFuse f3;
     f3.norm = true;
     f3.xn_out = dbg ? dbg->xn2 : nullptr;
     f3.res = h1;
     f3.res_dt = AS_F32;
-    as_mlp_debug md;
-    memset(&md, 0, sizeof md);
-    md.h = dbg ? dbg->h : nullptr;
     return mlp_impl(h1, AS_F32, 1, &w->mlp, AS_MLP_THRESHOLD, t->gate_up, t->down, nullptr, 0, Y, AS_F32, pass,
-                    md.h ? &md : nullptr, b.ws_mlp, b.n_mlp, stream, &f3);
+                    want_md ? &md : nullptr, b.ws_mlp, b.n_mlp, stream, &f3);
   }
+  // AS_FLAG_NO_FUSION (or inputs the prologues cannot normalise): seven launches
   if ((st = as_rmsnorm(X, x_dt, 1, d, 1e-5f, xn, h1, stream)) != AS_OK) return st;
   if ((st = as_threshold_gemv(xn, AS_F32, 1, d, w->w_qkv, w->mlp.w_dt, nqkv, dense ? inf : t->qkv, qkv, AS_F32,
-                              pass, nullptr, b.ws_qkv, b.n_qkv, stream)) != AS_OK) return st;
+                              pass, m_qkv, b.ws_qkv, b.n_qkv, stream)) != AS_OK) return st;
   if ((st = as_gqa_decode_attention(qkv, qkv + no, qkv + no + w->n_kv * hd, k_cache, v_cache, AS_BF16, n_ctx,
                                     w->n_q, w->n_kv, hd, o, b.ws_attn, b.n_attn, stream)) != AS_OK) return st;
   if ((st = as_threshold_gemv(o, AS_F32, 1, no, w->w_o, w->mlp.w_dt, d, dense ? inf : t->o, h1, AS_F32,
-                              pass | AS_FLAG_ACCUMULATE, nullptr, b.ws_o, b.n_o, stream)) != AS_OK) return st;
+                              pass | AS_FLAG_ACCUMULATE, m_o, b.ws_o, b.n_o, stream)) != AS_OK) return st;
   if ((st = as_rmsnorm(h1, AS_F32, 1, d, 1e-5f, xn2, Y, stream)) != AS_OK) return st;
-  as_mlp_debug md;
-  memset(&md, 0, sizeof md);
-  md.h = dbg ? dbg->h : nullptr;
   return as_sparse_swiglu_mlp(xn2, AS_F32, 1, &w->mlp, AS_MLP_THRESHOLD, t->gate_up, t->down, nullptr, 0, Y,
-                              AS_F32, pass | AS_FLAG_ACCUMULATE, md.h ? &md : nullptr, b.ws_mlp, b.n_mlp, stream);
+                              AS_F32, pass | AS_FLAG_ACCUMULATE, want_md ? &md : nullptr, b.ws_mlp, b.n_mlp, stream);
 }
 
 // ------------------------------------------------------------------ GLASS local signal

@@ -13,12 +13,10 @@ size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
   size_t b = a16(size_t(cap) * 4) + a16(size_t(cap) * c.mt * 4);
   // slot reduction of the VALU loop (the MFMA loop stages its output in the chunk buffer)
   if (c.mt != 16) b += a16(size_t(nslot > c.mt ? nslot : c.mt) * tn * 4);
-  if (c.in == IN_LISTS || c.in == IN_TILES) b += a16(size_t(n_lt + 1) * 4);
-  // staging region: IN_TILES raw candidate entries (index + M values, cap of them)
-  // or the IN_RANGE input range during the prologue; the MFMA weight chunk and
-  // output tile afterwards
+  if (c.in == IN_LISTS) b += a16(size_t(n_lt + 1) * 4);
+  // staging region: the IN_RANGE / IN_PARTS input range during the prologue; the
+  // MFMA weight chunk and output tile afterwards
   size_t stage = 0;
-  if (c.in == IN_TILES) stage = size_t(cap) * (1 + c.mt) * 4;
   // IN_RANGE, several tokens, and IN_PARTS: the slice's range of every token, fp32
   if ((c.in == IN_RANGE && c.mt > 1) || c.in == IN_PARTS) stage = size_t(cap) * c.mt * 4;
   if (c.mt == 16) {
@@ -51,25 +49,6 @@ int pick_chunk_vectors(const void* x, int x_dt, int len, long ldx) {
   return 0;
 }
 
-hipError_t launch_fused_bf16_m1(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-hipError_t launch_fused_bf16_m2(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-hipError_t launch_fused_bf16_m4(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-hipError_t launch_fused_bf16_m8(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-hipError_t launch_fused_f16_m1(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-hipError_t launch_fused_f16_m2(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-hipError_t launch_fused_f16_m4(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-hipError_t launch_fused_f16_m8(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
-
-hipError_t launch_fused_mlp(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  const bool bf = c.wdt == DT_BF16;
-  switch (c.mt) {
-    case 1: return bf ? launch_fused_bf16_m1(c, f, smem, s) : launch_fused_f16_m1(c, f, smem, s);
-    case 2: return bf ? launch_fused_bf16_m2(c, f, smem, s) : launch_fused_f16_m2(c, f, smem, s);
-    case 4: return bf ? launch_fused_bf16_m4(c, f, smem, s) : launch_fused_f16_m4(c, f, smem, s);
-    case 8: return bf ? launch_fused_bf16_m8(c, f, smem, s) : launch_fused_f16_m8(c, f, smem, s);
-    default: return hipErrorInvalidValue;
-  }
-}
 
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s) {
   const size_t smem = gemv_smem_bytes(c, p.cap, p.n_lt);

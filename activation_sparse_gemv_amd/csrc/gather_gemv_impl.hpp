@@ -42,9 +42,12 @@ __host__ __device__ inline size_t align16(size_t b) { return (b + 15) & ~size_t(
 
 // Verification exports of the per-token input masks (bits and nnz by workgroup 0;
 // the ascending index list, M == 1 only, by the workgroups of column tile 0).
+// With the input normalised in the prologue (norm_x), the bits are those of the
+// normalised values: each value is scaled by the same fp32 factor the prologue
+// applied (inv_scale), so the comparison sees exactly the value that was masked.
 template <int MT>
 __device__ __forceinline__ void thresh_exports(const GemvParams& p, const int* s_idx, int* s_scan, int tid, int tile, int lo,
-                               int cnt, bool first) {
+                               int cnt, bool first, float inv_scale) {
   (void)s_scan;
   const int K = p.K;
   const float t = p.t;
@@ -64,6 +67,7 @@ __device__ __forceinline__ void thresh_exports(const GemvParams& p, const int* s
         const int j = min(j0 + u * NWV, M * nw - 1);
         const int m = j / nw, i = min((j % nw) * 64 + lane, K - 1);
         v[u] = load_elem(p.x, p.x_dt, (long)m * p.ldx + i);
+        if (p.norm_x) v[u] *= inv_scale;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -288,7 +292,7 @@ __device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s
 template <int MT, int NV>
 __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i1, bool split, int sl, int S,
                                               int* s_idx, float* s_val, int cap, int* s_scan, int* lo_out,
-                                              bool export_xn) {
+                                              bool export_xn, float* inv_out) {
   const int tid = threadIdx.x;
   const int M = p.M;
   const float t = p.t;
@@ -316,6 +320,7 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
       for (int w = 0; w < kThreads / 64; ++w) tot += s_part[w];
       __syncthreads();   // s_scan is reused by the scan below
       const float inv = 1.0f / sqrtf(tot / (float)(i1 - i0) + p.norm_eps);
+      *inv_out = inv;
 #pragma unroll
       for (int e = 0; e < CEV; ++e) v0[e] *= inv;
       if (export_xn && p.xn_out != nullptr)
@@ -656,12 +661,16 @@ __device__ __forceinline__ int compact_parts(const GemvParams& p, int i0, int i1
   if (exports) {
     if (p.h != nullptr)
       for (int j = tid; j < M * L; j += kThreads) p.h[(j / L) * p.ldh + i0 + j % L] = stage[j];
-    if (p.h_bits != nullptr) {
-      // one wave per 64-row word (words never straddle tokens: L is a multiple of 64)
+    if (p.h_bits != nullptr || p.h_nnz != nullptr) {
+      // one wave per 64-row word (words never straddle tokens: L is a multiple of 64);
+      // the count is accumulated with integer atomics (exact in any order)
       const int lane = tid & 63;
       for (int b = (tid >> 6) * 64; b < M * L; b += kThreads) {
         const uint64_t bits = __ballot(fabsf(stage[b + lane]) > t);
-        if (lane == 0) p.h_bits[(b / L) * p.h_bits_ld + (i0 + b % L) / 64] = bits;
+        if (lane == 0) {
+          if (p.h_bits != nullptr) p.h_bits[(b / L) * p.h_bits_ld + (i0 + b % L) / 64] = bits;
+          if (p.h_nnz != nullptr && bits) atomicAdd(p.h_nnz + b / L, (int)__popcll(bits));
+        }
       }
     }
   }
@@ -671,10 +680,8 @@ __device__ __forceinline__ int compact_parts(const GemvParams& p, int i0, int i1
 // One work item: column tile `tile`, row slice `sl` of S (p.S) equal parts of the
 // compacted row list (IN_PARTS: the range [rr0, rr1) of h when rr1 >= 0); its
 // partial tile is slot `part` of `n_parts` combined by the last item of the tile to
-// finish.  IN_LISTS reads list tiles
-// [lt0, lt0 + n_lt); IN_TILES gives slice sl whole list tiles of [lt0, lt0 + n_lt).
-// Used by the GEMV kernel below (one item per workgroup) and by the one-launch
-// MLP kernel (a gate/up item, then a down item, per workgroup).
+// finish.  IN_LISTS reads list tiles [lt0, lt0 + n_lt).  Used by the GEMV kernel
+// below (one item per workgroup) and by the one-stream MoE layer's launches.
 template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
 __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl, int part, int n_parts, int lt0, int n_lt,
                           unsigned char* smem, int rr0 = 0, int rr1 = -1) {
@@ -682,8 +689,9 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
   constexpr int RPW = TS::RPW, NSLOT = TS::NSLOT, TN = TS::TN, TB = TN / 2;
   const int cap = p.cap;
   // LDS: row list | activations [MT][cap] | slot reduction (VALU loop) | list-tile
-  // prefix sums | staging region (IN_TILES raw entries during the prologue, then the
-  // MFMA weight chunk, whose buffer also holds the MFMA output tile).
+  // prefix sums | staging region (the input range during an IN_RANGE / IN_PARTS
+  // prologue, then the MFMA weight chunk, whose buffer also holds the MFMA output
+  // tile).
   constexpr bool kMfma = MT == 16;
   int* s_idx = reinterpret_cast<int*>(smem);
   float* s_val = reinterpret_cast<float*>(smem + align16(size_t(cap) * 4));
@@ -691,7 +699,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
   const size_t red_bytes = kMfma ? 0 : align16(size_t(NSLOT > MT ? NSLOT : MT) * TN * 4);
   int* s_pref = reinterpret_cast<int*>(after_val + red_bytes);
   uint16_t* s_w = reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(s_pref) +
-                                              ((IN == IN_LISTS || IN == IN_TILES) ? align16(size_t(p.n_lt + 1) * 4) : 0));
+                                              (IN == IN_LISTS ? align16(size_t(p.n_lt + 1) * 4) : 0));
   float* s_red = kMfma ? reinterpret_cast<float*>(s_w) : reinterpret_cast<float*>(after_val);
   (void)n_lt;
   __shared__ int s_scan[kThreads / 64 + 1];
@@ -714,14 +722,16 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       r1 = min(p.K, split_point(sl + 1, units, S) * 64);
     }
     int lo = 0;
+    float inv_scale = 1.0f;     // the normalisation factor (norm_x), the same in every thread
     if constexpr (IN == IN_RANGE && MT > 1)
       cnt = r1 - r0 <= 2 * kThreads
                 ? compact_range_regs<MT>(p, r0, r1, s_idx, s_val, cap, s_scan)
                 : compact_range_staged<MT, NV>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan);
     else
-      cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo, tile == 0 && sl == 0);
+      cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo, tile == 0 && sl == 0,
+                                   &inv_scale);
     if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
-      thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0);
+      thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0, inv_scale);
   } else if constexpr (IN == IN_PARTS) {
     // the range of h: explicit (one-launch MLP) or slice sl of S 64-aligned parts
     const int units = (p.K + 63) / 64;
@@ -757,37 +767,6 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       for (int m = 0; m < MT; ++m) xv[m] = p.list_val[e * M + (m < M ? m : M - 1)];
 #pragma unroll
       for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? xv[m] : 0.f;
-    }
-  } else if constexpr (IN == IN_TILES) {
-    // Slice sl owns whole list tiles [t0, t1).  Counts and every candidate entry of
-    // those tiles are loaded together (one round trip; entries past a tile's count
-    // are ignored), staged in LDS, then compacted in tile order.
-    const int t0 = split_point(sl, n_lt, S), t1 = split_point(sl + 1, n_lt, S);
-    const int nt = t1 - t0;
-    const int stride = p.lt_stride;
-    const int tot_e = nt * stride;
-    int* s_cnt = s_pref;                                   // [nt + 1]
-    int* r_idx = reinterpret_cast<int*>(s_w);              // [tot_e] raw candidates
-    float* r_val = reinterpret_cast<float*>(r_idx + tot_e);  // [tot_e][M]
-    const long gbase = (long)(lt0 + t0) * stride;
-    if (tid < nt) s_cnt[tid] = p.list_cnt[lt0 + t0 + tid];
-    copy2_to_lds<false>(r_idx, p.list_idx + gbase, tot_e, r_val, p.list_val + gbase * M, tot_e * M);
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int q = 0; q < nt; ++q) { const int c = s_cnt[q]; s_cnt[q] = run; run += c; }
-      s_cnt[nt] = run;
-    }
-    __syncthreads();
-    cnt = s_cnt[nt];
-    for (int q = 0; q < nt; ++q) {
-      const int base = s_cnt[q], len = s_cnt[q + 1] - base;
-      for (int k = tid; k < len; k += kThreads) {
-        const int e = q * stride + k;
-        s_idx[base + k] = r_idx[e];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) s_val[m * cap + base + k] = m < M ? r_val[e * M + m] : 0.f;
-      }
     }
   } else {  // IN_ALL: every row, no mask (dense baseline)
     const int K = p.K;
@@ -1006,12 +985,10 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
           for (int k = 0; k < kBatch; ++k)
             if (s0 + k < n_parts && oks[q]) v[m][q] += tmp[m][q][k];
     }
-    // a producer wait of the one-launch MLP that timed out poisons the output
-    const float bad = (p.err_flag != nullptr && load_coherent_u32(p.err_flag) != 0u) ? __builtin_nanf("") : 0.f;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int q = 0; q < CPT; ++q) res[m][q] = m < M ? v[m][q] + bad : 0.f;
+      for (int q = 0; q < CPT; ++q) res[m][q] = m < M ? v[m][q] : 0.f;
   }
 
   // ------------------------------------------------------------ epilogues
@@ -1080,10 +1057,14 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
         p.h[m * p.ldh + n] = hv[m];
       }
     }
-    if (p.h_bits != nullptr && tid < TB) {
+    if ((p.h_bits != nullptr || p.h_nnz != nullptr) && tid < TB) {
       for (int m = 0; m < M; ++m) {
         const uint64_t bits = __ballot(nvalid && fabsf(hv[m]) > p.t_h);
-        if ((tid & 63) == 0 && tile * TB + tid < p.N) p.h_bits[m * p.h_bits_ld + (tile * TB + tid) / 64] = bits;
+        if ((tid & 63) == 0 && tile * TB + tid < p.N) {
+          if (p.h_bits != nullptr) p.h_bits[m * p.h_bits_ld + (tile * TB + tid) / 64] = bits;
+          // the mask's count: integer adds, exact in any order (cleared by the host)
+          if (p.h_nnz != nullptr && bits) atomicAdd(p.h_nnz + m, (int)__popcll(bits));
+        }
       }
     }
     if (p.o_cnt != nullptr) {
@@ -1109,165 +1090,6 @@ __global__ __launch_bounds__(kThreads, 2) void gather_gemv_kernel(const GemvPara
   extern __shared__ __align__(16) unsigned char smem[];
   const int tile = blockIdx.x % p.n_tiles, sl = blockIdx.x / p.n_tiles;
   gemv_item<WDT, MT, LPR, IN, OUT, GU, NT, NV>(p, tile, sl, sl, p.S, 0, p.n_lt, smem);
-}
-
-// ---------------------------------------------------------------- one-launch MLP
-// Both stages of the threshold-mode SwiGLU MLP in one launch, in two roles.  The
-// first g1 workgroups are gate/up items: each stores its split-K partial tile
-// unsummed and waits for the stores.  The gate/up tiles are grouped by XCD
-// (workgroup w runs on XCD w % 8 on this part), and each group's tiles are cut
-// into at most k2 h ranges of whole tiles; the item that completes the last slice
-// of a range appends the range to a ready list.  The other g2 workgroups are
-// down items: down workgroup n takes column tile n % n_ct2 of the (n / n_ct2)-th
-// range to become ready, waits for that list entry, then sums the range's
-// partials, applies SwiGLU and the h mask in its prologue (IN_PARTS) and streams
-// its rows; its partial goes to the range's slot, so the final combine is in
-// h-row order whatever the order ranges became ready in.  Down work thus starts
-// on whatever range is done first, on any XCD, while slower gate/up tiles are
-// still streaming, and the gap between two launches disappears.
-// Down items wait only on gate/up items, which never wait and come first in the
-// grid, and every XCD dispatches its workgroups in index order, so the waits end
-// whatever else occupies the device.  They are bounded anyway: a timeout raises
-// *err, which poisons the output with NaN.  The last workgroup to finish clears
-// the counters and the list for the next call.
-
-// Range q of group x (k2 ranges at most, never empty): tiles [*ta, *tb); returns
-// the global range index (ranges numbered in group order, i.e. h-row order).
-__device__ __forceinline__ int fused_range(const FusedMlpParams& f, int x, int q, int* ta, int* tb) {
-  int base = 0;
-  for (int y = 0; y < x; ++y) {
-    const int n = split_point(y + 1, f.n_tiles1, f.groups) - split_point(y, f.n_tiles1, f.groups);
-    base += n < f.k2 ? n : f.k2;
-  }
-  const int t0 = split_point(x, f.n_tiles1, f.groups);
-  const int nt = split_point(x + 1, f.n_tiles1, f.groups) - t0;
-  const int nr = nt < f.k2 ? nt : f.k2;
-  *ta = t0 + split_point(q, nt, nr);
-  *tb = t0 + split_point(q + 1, nt, nr);
-  return base + q;
-}
-
-template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
-__global__ __launch_bounds__(kThreads, 2) void mlp_xcd_kernel(const FusedMlpParams f) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_range;
-  const int w = blockIdx.x, tid = threadIdx.x;
-  const int G = f.groups;
-  if (w < f.g1) {
-    const int x = w % G, i = w / G;
-    const int t0 = split_point(x, f.n_tiles1, G), nt = split_point(x + 1, f.n_tiles1, G) - t0;
-    if (i < nt * f.S1) {
-      const int lt = i % nt, sl = i / nt;
-      gemv_item<WDT, MT, LPR1, IN1, OUT_PARTS, true, true, NV>(f.p1, t0 + lt, sl, sl, f.S1, 0, 0, smem);
-      // publish: the partial tile is stored before the range's slice count rises
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0) {
-        const int nr = nt < f.k2 ? nt : f.k2;
-        int q = 0;
-        while (q + 1 < nr && split_point(q + 1, nt, nr) <= lt) ++q;
-        int ta, tb;
-        const int r = fused_range(f, x, q, &ta, &tb);
-        const unsigned need = (unsigned)((tb - ta) * f.S1);
-        const unsigned prev = __hip_atomic_fetch_add(f.range_cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev + 1 == need) {
-          const unsigned pos = __hip_atomic_fetch_add(f.ready_tail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(f.ready + (long)pos * kCntStride, (unsigned)r + 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-  } else {
-    const int n = w - f.g1;
-    const int k = n / f.n_ct2, ct = n % f.n_ct2;
-    if (k < f.n_ranges) {
-      if (tid == 0) {
-        // one poller per workgroup, a few hundred cycles apart; list entries sit
-        // kCntStride apart so that polling does not load one memory channel
-        unsigned v, spins = 0;
-        while ((v = __hip_atomic_load(f.ready + (long)k * kCntStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
-               0u) {
-          __builtin_amdgcn_s_sleep(8);
-          if (++spins > (1u << 24)) {
-            __hip_atomic_store(f.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v = (unsigned)k + 1u;
-            break;
-          }
-        }
-        s_range = (int)v - 1;
-      }
-      __syncthreads();
-      const int r = s_range;
-      // range r -> group and rows
-      int x = 0, base = 0;
-      for (;;) {
-        const int nt = split_point(x + 1, f.n_tiles1, G) - split_point(x, f.n_tiles1, G);
-        const int nr = nt < f.k2 ? nt : f.k2;
-        if (r < base + nr || x == G - 1) break;
-        base += nr;
-        ++x;
-      }
-      int ta, tb;
-      fused_range(f, x, r - base, &ta, &tb);
-      const int K = f.p2.K;
-      const int r0 = min(K, ta * f.tb1), r1 = min(K, tb * f.tb1);
-      gemv_item<WDT, MT, LPR2, IN_PARTS, OUT_Y, false, true, 0>(f.p2, ct, 0, r, f.n_ranges, 0, 0, smem, r0, r1);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    wait_vmem();
-    const unsigned prev = __hip_atomic_fetch_add(f.exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == gridDim.x - 1) {
-      for (int q = 0; q < f.n_ranges; ++q) {
-        __hip_atomic_store(f.range_cnt + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(f.ready + (long)q * kCntStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __hip_atomic_store(f.ready_tail, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(f.err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(f.exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
-template <int WDT, int MT, int LPR1, int LPR2, int IN1, int NV>
-hipError_t launch_fused_one(const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  auto k = mlp_xcd_kernel<WDT, MT, LPR1, LPR2, IN1, NV>;
-  if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-    if (e != hipSuccess) return e;
-  }
-  const int grid = f.g1 + f.g2;
-  if (grid < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), smem, s, f);
-  return hipGetLastError();
-}
-
-template <int WDT, int MT, int LPR1, int LPR2>
-hipError_t fused_pick_in(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  if (c.in1 == IN_ALL) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_ALL, 0>(f, smem, s);
-  if (c.in1 == IN_RANGE) {
-    if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_RANGE, 2>(f, smem, s);
-    return launch_fused_one<WDT, MT, LPR1, LPR2, IN_RANGE, 0>(f, smem, s);
-  }
-  if (c.in1 != IN_THRESH) return hipErrorInvalidValue;
-  if (c.nv == 2) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 2>(f, smem, s);
-  if constexpr (MT == 1) {
-    if (c.nv == 8) return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 8>(f, smem, s);
-  }
-  return launch_fused_one<WDT, MT, LPR1, LPR2, IN_THRESH, 0>(f, smem, s);
-}
-
-template <int WDT, int MT>
-hipError_t fused_pick(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  if constexpr (MT <= 8) {
-    if (c.lpr1 == 64 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 64, 16>(c, f, smem, s);
-    if (c.lpr1 == 64 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 64, 32>(c, f, smem, s);
-    if (c.lpr1 == 32 && c.lpr2 == 16) return fused_pick_in<WDT, MT, 32, 16>(c, f, smem, s);
-    if (c.lpr1 == 32 && c.lpr2 == 32) return fused_pick_in<WDT, MT, 32, 32>(c, f, smem, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -1328,7 +1150,6 @@ hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipS
   if (c.in == IN_THRESH) return pick_nt<WDT, MT, LPR, IN_THRESH, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_RANGE) return pick_nt<WDT, MT, LPR, IN_RANGE, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_LISTS) return pick_nt<WDT, MT, LPR, IN_LISTS, OUT_Y, false>(c, p, smem, s);
-  if (c.in == IN_TILES) return pick_nt<WDT, MT, LPR, IN_TILES, OUT_Y, false>(c, p, smem, s);
   if (c.in == IN_PARTS) {
     if constexpr (MT <= 8) return pick_nt<WDT, MT, LPR, IN_PARTS, OUT_Y, false>(c, p, smem, s);
     return hipErrorInvalidValue;

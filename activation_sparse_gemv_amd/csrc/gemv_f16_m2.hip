@@ -5,7 +5,4 @@ namespace as {
 hipError_t launch_gemv_f16_m2(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
   return pick_lpr<DT_F16, 2>(c, p, smem, s);
 }
-hipError_t launch_fused_f16_m2(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s) {
-  return fused_pick<DT_F16, 2>(c, f, smem, s);
-}
 }  // namespace as

@@ -7,13 +7,13 @@
 
 namespace as {
 
-enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_TILES = 3, IN_RANGE = 4, IN_PARTS = 5 };
+enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_RANGE = 4, IN_PARTS = 5 };
 enum { OUT_Y = 0, OUT_SWIGLU = 1, OUT_PARTS = 2, OUT_ROUTER = 3 };
 
 // One row-gather GEMV launch: Y[m, c] = sum over listed rows i of xv[m, i] * W[i, c].
 // The rows come from a magnitude mask of a vector (IN_THRESH: the whole vector,
 // split evenly over the slices; IN_RANGE: each slice masks its own range), from
-// per-tile compacted lists written by an earlier stage (IN_LISTS, IN_TILES) or
+// per-tile compacted lists written by an earlier stage (IN_LISTS) or
 // are all rows (IN_ALL); or the input is h = silu(g) * u of an earlier paired
 // gate/up launch that left its split-K partials unsummed (IN_PARTS: each slice
 // sums the partials of its own range of h in slice order, applies SwiGLU and the
@@ -44,6 +44,7 @@ struct GemvParams {
   float* zero_y; long zero_n;
   // OUT_SWIGLU
   float t_h; float* h; long ldh; int* o_cnt; int* o_idx; float* o_val; uint64_t* h_bits; long h_bits_ld;
+  int* h_nnz;              // per-token count of the h mask (IN_PARTS, OUT_SWIGLU; cleared by the host)
   // input-mask verification exports (IN_THRESH)
   uint64_t* x_bits; long x_bits_ld; int* x_idx; int* x_nnz;
   // IN_PARTS: x = gate/up partials [x_parts][M][ldx] fp32 (gate column i at i, up at
@@ -51,7 +52,6 @@ struct GemvParams {
   // (written by the workgroups of column tile 0 only)
   int x_parts; long x_up;
   int keep_all;            // IN_PARTS: keep every row (dense baseline), no mask
-  const unsigned* err_flag;  // when set and nonzero at the combine, the output is NaN
   // RMS normalisation of the input in the threshold prologue (IN_THRESH, one token,
   // 16-byte chunks): x is scaled by 1 / sqrt(sum x^2 / K + norm_eps) before the mask
   // and the products; xn_out (nullable) receives the normalised vector
@@ -76,26 +76,6 @@ struct GemvConfig {
 
 size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt);
 
-// One-launch two-stage threshold MLP (see mlp_xcd_kernel): g1 gate/up workgroups
-// (OUT_PARTS) followed by g2 down workgroups (IN_PARTS) over h ranges published in a
-// ready list.
-constexpr int kCntStride = 1024;   // 4 KB between polled words
-struct FusedMlpParams {
-  GemvParams p1, p2;       // p1: gate/up (S1 slices, unsummed partials); p2: down (h ranges)
-  int n_tiles1, S1, tb1;   // gate/up column tiles, slices, h rows per tile
-  int n_ct2, k2;           // down column tiles; h ranges per group at most
-  int groups, n_ranges;    // XCD groups; h ranges in all
-  int g1, g2;              // workgroups of each role; grid = g1 + g2 (g2 = n_ranges * n_ct2)
-  unsigned* range_cnt;     // [n_ranges] finished gate/up slices per range
-  unsigned* ready;         // ready list: entry k (range + 1, 0 = not yet) at ready[k * kCntStride]
-  unsigned* ready_tail;    // entries appended so far
-  unsigned* exit_cnt;
-  unsigned* err;
-};
-struct FusedCfg {
-  int wdt, mt, lpr1, lpr2, in1, nv;
-};
-hipError_t launch_fused_mlp(const FusedCfg& c, const FusedMlpParams& f, size_t smem, hipStream_t s);
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s);
 int pick_chunk_vectors(const void* x, int x_dt, int K, long ldx);
 

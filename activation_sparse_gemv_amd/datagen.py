@@ -9,7 +9,9 @@ Generation rules
 ----------------
 * RNG: ``numpy.random.Generator(PCG64(seed))``; draws are cast to bf16/fp16
   through torch CPU tensors (round-to-nearest-even) and the cast bits are what
-  every consumer sees.
+  every consumer sees.  Normal draws of more than 2^22 values take chunk k of
+  2^22 values from the seed's stream advanced by k jumps (generated on threads;
+  the values do not depend on the thread count).
 * Seeds: ``seed = 10000*cfg + 100*layer + tag`` with the tags below.
 * Weights: N(0, 0.02^2) drawn directly in the layout the kernels read.
 * Activations: heavy-tailed (Laplace(0,1) or Student-t with 3 degrees of
@@ -20,7 +22,9 @@ Generation rules
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -47,10 +51,34 @@ def _cast(a: np.ndarray, dtype: str) -> torch.Tensor:
     return t.to(_TORCH_DT[dtype]).contiguous()
 
 
+# Large draws are split into chunks of _CHUNK values; chunk k comes from the PCG64
+# stream of the seed advanced by k jumps (PCG64.jumped(k)), so the values do not
+# depend on how many threads generate them (chunk 0 is the plain stream).
+_CHUNK = 1 << 22
+
+
+def _workers() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def normal(shape, seed: int, std: float = 0.02, dtype: str = "bf16") -> torch.Tensor:
     """N(0, std^2) in the requested storage dtype (float32 draws, RNE cast)."""
     n = int(np.prod(shape))
-    a = _rng(seed).standard_normal(n, dtype=np.float32)
+    a = np.empty(n, dtype=np.float32)
+    nch = max(1, (n + _CHUNK - 1) // _CHUNK)
+    base = np.random.PCG64(seed)
+    # every chunk's stream is set up before any draw (jumped() copies the state)
+    gens = [np.random.Generator(base.jumped(k) if k else np.random.PCG64(seed)) for k in range(nch)]
+
+    def fill(k: int) -> None:
+        lo, hi = k * _CHUNK, min(n, (k + 1) * _CHUNK)
+        gens[k].standard_normal(hi - lo, dtype=np.float32, out=a[lo:hi])
+
+    if nch <= 1:
+        fill(0)
+    else:
+        with cf.ThreadPoolExecutor(min(_workers(), nch)) as ex:
+            list(ex.map(fill, range(nch)))
     a *= np.float32(std)
     return _cast(a.reshape(shape), dtype)
 

@@ -33,10 +33,10 @@
  *    *_ws_size query and must be zero-filled before its first use (any zero
  *    fill, or as_workspace_init).  Every call leaves the counters it uses at
  *    zero again, so a workspace is reusable by later calls on the same stream
- *    with the same shapes.  The carve-up follows the call's launch plan; the
- *    AS_* tuning environment variables (tile width, slices) change plans, so
- *    re-zero a workspace after changing them.  Calls that may run concurrently
- *    need distinct workspaces.
+ *    with the same shapes.  The carve-up follows the call's launch plan, which
+ *    depends only on the shapes, the flags passed and the device's CU count
+ *    (the library reads no environment variables).  Calls that may run
+ *    concurrently need distinct workspaces.
  *  - Errors: arguments are validated on the host before anything is enqueued
  *    (AS_ERR_INVALID_ARG / AS_ERR_UNSUPPORTED / AS_ERR_WORKSPACE); a launch
  *    failure returns AS_ERR_HIP.  as_last_error() gives the message of the last
@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AS_VERSION 100
+#define AS_VERSION 200
 
 typedef enum {
   AS_OK = 0,
@@ -77,7 +77,8 @@ enum {
                                       reproducible (see the GEMV and MLP calls)           */
   AS_FLAG_NO_NT_LOADS = 1u << 2,  /* plain (cached) weight loads instead of nontemporal  */
   AS_FLAG_FORCE_DENSE = 1u << 3,  /* ignore thresholds / neuron lists: dense baseline   */
-  AS_FLAG_NO_FUSION = 1u << 4     /* threshold MLP: two launches instead of one           */
+  AS_FLAG_NO_FUSION = 1u << 4     /* decoder block: RMS normalisations and residual adds as
+                                     launches of their own (seven instead of five)       */
 };
 
 /* Verification exports of a mask (every field may be NULL).
@@ -101,17 +102,18 @@ as_status as_workspace_init(void *ws, size_t bytes, hipStream_t stream);
  * TEAL slides, method slide: the threshold t_p of a projection input is fixed
  * from calibration data for the target sparsity p.  Reading: t is the
  * nearest-rank order statistic of the pooled magnitudes:
+ *   rank = ceil(p * n) with p = p_num / p_den exactly (integer arithmetic);
  *   *t_out = the rank-th smallest |pool[i]| (1-based), as fp32;
- *   rank = 0 gives -INFINITY (sparsity 0 keeps every input).
- * The caller computes rank = ceil(p * n).  NaN magnitudes order above +inf.
+ *   p = 0 (p_num = 0) gives -INFINITY (sparsity 0 keeps every input).
+ * NaN magnitudes order above +inf.
  * pool: [n] of dtype dt (f16/bf16/f32).  t_out: one device float.
  * ws: caller-owned device workspace of as_calibrate_threshold_ws_size(n) bytes
  * (zero-filled once; every call leaves it zeroed); calls sharing a workspace
  * must be ordered on one stream.
- * Errors: INVALID_ARG if pool/t_out is NULL, n < 1 or n >= 2^31, rank < 0 or
- * rank > n; WORKSPACE if ws is NULL or too small. */
+ * Errors: INVALID_ARG if pool/t_out is NULL, n < 1 or n >= 2^31, p_den < 1,
+ * p_num < 0 or p_num > p_den; WORKSPACE if ws is NULL or too small. */
 size_t as_calibrate_threshold_ws_size(int64_t n);
-as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64_t rank,
+as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64_t p_num, int64_t p_den,
                                  float *t_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ threshold GEMV
@@ -126,6 +128,8 @@ as_status as_calibrate_threshold(const void *pool, as_dtype dt, int64_t n, int64
  * its own kept inputs.
  * mask_out (nullable): the per-token input masks (bits and nnz for any M,
  * idx only for M == 1).
+ * AS_FLAG_ATOMIC_SPLITK without AS_FLAG_ACCUMULATE clears Y before X is read, so
+ * there X and Y must not overlap (INVALID_ARG otherwise).
  * AS_FLAG_FORCE_DENSE runs the dense baseline (every row, t ignored).
  * AS_FLAG_ATOMIC_SPLITK (Y fp32 only, else UNSUPPORTED): where the launch plan
  * splits the rows of a column tile over several workgroups, each adds its
@@ -163,7 +167,8 @@ typedef struct {
   float *h;               /* THRESHOLD: [M, d_ff] fp32 intermediate silu(g)*u of every
                              neuron.  NEURON_SET: [M, n_active] for the listed neurons. */
   as_mask_out x_mask;     /* input mask |X| > t_x (THRESHOLD only; see as_threshold_gemv) */
-  as_mask_out h_mask;     /* |h| > t_h (THRESHOLD only): bits only, idx/nnz must be NULL */
+  as_mask_out h_mask;     /* |h| > t_h (THRESHOLD only): bits [M, ceil(d_ff/64)] and nnz [M];
+                             idx must be NULL */
   hipEvent_t ev[3];       /* if non-NULL: recorded before stage 1, between the stages,
                              and after stage 2 (per-kernel timing) */
 } as_mlp_debug;
@@ -181,8 +186,9 @@ typedef struct {
  * neurons and inputs (the baseline).  AS_FLAG_ATOMIC_SPLITK (fp32 Y only): the
  * down projection's row slices add into Y with fp32 atomic adds (as in
  * as_threshold_gemv); without AS_FLAG_ACCUMULATE, Y is cleared by the first
- * launch, so Y must not alias X; the one-launch variant is not used.  dbg is
- * nullable. */
+ * launch, so Y must not overlap X (INVALID_ARG otherwise).  dbg is nullable;
+ * the masks it exports are those of the masked tensors as the kernels computed
+ * them (h in fp32). */
 size_t as_sparse_swiglu_mlp_ws_size(int M, const as_mlp_weights *w, as_mlp_mode mode);
 as_status as_sparse_swiglu_mlp(const void *X, as_dtype x_dt, int M, const as_mlp_weights *w,
                                as_mlp_mode mode, float t_x, float t_h,
@@ -275,7 +281,8 @@ as_status as_moe_router_gemv(const void *X, as_dtype x_dt, int T, const void *w_
  * adds its weighted rows' sum into Y with fp32 atomic adds instead of the
  * slot-order sum by the last slot to finish (order of the additions
  * unspecified); without AS_FLAG_ACCUMULATE, Y is cleared by a fill launch
- * first (which does not wait for y_ready).
+ * first (which does not wait for y_ready), so Y must not overlap X
+ * (INVALID_ARG otherwise).
  * Debug exports (nullable): h_dbg [T, top_k, d_ff_e] fp32, keep_dbg
  * [T, top_k, keep_k] int32 ascending.
  * y_ready (nullable): an event recorded after whatever produces Y on another
@@ -374,13 +381,20 @@ typedef struct {          /* every field nullable; fp32 intermediates of one cal
   float *h1;              /* [d_model] x + o-proj */
   float *xn2;             /* [d_model] rmsnorm(h1) */
   float *h;               /* [d_ff] MLP intermediate */
+  /* masks of the four thresholded inputs, as the kernels applied them (see
+     as_mask_out; M = 1): |xn| > t.qkv, |o| > t.o, |xn2| > t.gate_up (bits, idx,
+     nnz), |h| > t.down (bits and nnz; idx must be NULL) */
+  as_mask_out qkv_in, o_in, gate_up_in, down_in;
 } as_block_debug;
 
 /* One decoder block for one decode token, every projection input thresholded:
  *   xn = rmsnorm(x); qkv = (xn * [|xn| > t.qkv]) Wqkv; o = attention(q, caches + k, v)
  *   h1 = x + (o * [|o| > t.o]) Wo;  Y = h1 + MLP(rmsnorm(h1)) with t.gate_up, t.down.
  * X: [d_model] (f16/bf16/f32); Y: [d_model] fp32.  AS_FLAG_FORCE_DENSE ignores
- * every threshold (the dense block). */
+ * every threshold (the dense block).  By default the two normalisations run in
+ * the prologues of the projections that read them and the residual adds in the
+ * epilogues of the projections that produce them (five launches);
+ * AS_FLAG_NO_FUSION runs them as launches of their own (seven). */
 size_t as_decoder_block_ws_size(const as_block_weights *w, int n_ctx);
 as_status as_decoder_block(const void *X, as_dtype x_dt, const as_block_weights *w,
                            const void *k_cache, const void *v_cache, int n_ctx,

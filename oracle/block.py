@@ -46,22 +46,28 @@ def gqa_decode_attention(q, k_cache, v_cache, k_new, v_new):
 
 
 def decoder_block(x, wqkv, wo, wgu, wd, k_cache, v_cache, t, n_q=32, n_kv=8, hd=128):
-    """One decode token through one block with thresholded projection inputs.
+    """Decode tokens through one block with thresholded projection inputs.
 
     TEAL slides, method slide: the inputs of the attention and MLP blocks' linear
     layers are magnitude-thresholded; the attention core stays dense.
+    ``x`` is one token ``[d]`` or independent tokens ``[T, d]`` (each token is the
+    same computation; the rows only share the matrix products).
     ``t`` = dict(qkv=, o=, gu=, d=) fp32 thresholds.  Weights input-major:
     wqkv [d, (n_q + 2 n_kv) hd], wo [n_q hd, d], wgu [d, 2, d_ff], wd [d_ff, d].
-    Returns a dict of every intermediate and ``out``.
+    Returns a dict of every intermediate and ``out`` (rows = tokens).
     """
     x = np.asarray(x, dtype=np.float64)
     xn = rmsnorm(x)
     xs = sparsify(xn, t["qkv"])
     qkv = xs @ np.asarray(wqkv, np.float64)
-    q = qkv[: n_q * hd].reshape(n_q, hd)
-    kn = qkv[n_q * hd: (n_q + n_kv) * hd].reshape(n_kv, hd)
-    vn = qkv[(n_q + n_kv) * hd:].reshape(n_kv, hd)
-    o = gqa_decode_attention(q, k_cache, v_cache, kn, vn)
+
+    def attend(row):
+        q = row[: n_q * hd].reshape(n_q, hd)
+        kn = row[n_q * hd: (n_q + n_kv) * hd].reshape(n_kv, hd)
+        vn = row[(n_q + n_kv) * hd:].reshape(n_kv, hd)
+        return gqa_decode_attention(q, k_cache, v_cache, kn, vn)
+
+    o = attend(qkv) if qkv.ndim == 1 else np.stack([attend(r) for r in qkv])
     y_att = sparsify(o, t["o"]) @ np.asarray(wo, np.float64)
     h1 = x + y_att
     xn2 = rmsnorm(h1)

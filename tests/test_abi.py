@@ -49,7 +49,7 @@ def test_enum_values_match_the_header():
 
 
 def test_version_and_strings(lib):
-    assert lib.as_version() == 100
+    assert lib.as_version() == 200
     assert lib.as_status_string(L.AS_ERR_WORKSPACE) == b"AS_ERR_WORKSPACE"
 
 
@@ -116,13 +116,46 @@ def test_mlp_validation(lib):
 
 
 def test_calibrate_validation(lib):
+    """The target sparsity is an exact rational p_num / p_den in [0, 1]."""
     nb = lib.as_calibrate_threshold_ws_size(10)
     assert nb > 0
-    assert lib.as_calibrate_threshold(None, L.AS_F32, 10, 5, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG
-    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 11, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG
-    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 0, 0, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG
-    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 5, _p(), None, nb, None) == L.AS_ERR_WORKSPACE
-    assert lib.as_calibrate_threshold(_p(), L.AS_F32, 10, 5, _p(), _p(), nb - 1, None) == L.AS_ERR_WORKSPACE
+    cal = lib.as_calibrate_threshold
+    assert cal(None, L.AS_F32, 10, 1, 2, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG
+    assert cal(_p(), L.AS_F32, 10, 11, 10, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG    # p > 1
+    assert cal(_p(), L.AS_F32, 10, -1, 10, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG    # p < 0
+    assert cal(_p(), L.AS_F32, 10, 1, 0, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG      # p_den < 1
+    assert cal(_p(), L.AS_F32, 0, 0, 1, _p(), _p(), nb, None) == L.AS_ERR_INVALID_ARG       # n < 1
+    assert cal(_p(), L.AS_F32, 10, 1, 2, _p(), None, nb, None) == L.AS_ERR_WORKSPACE
+    assert cal(_p(), L.AS_F32, 10, 1, 2, _p(), _p(), nb - 1, None) == L.AS_ERR_WORKSPACE
+
+
+def test_atomic_splitk_rejects_overlapping_output(lib):
+    """Without AS_FLAG_ACCUMULATE the atomic split-K paths clear Y before X is read, so
+    an overlapping Y is refused on the host (nothing is launched)."""
+    X = 1 << 20
+    need = lib.as_threshold_gemv_ws_size(1, 4096, 4096)
+    st = lib.as_threshold_gemv(_p(X), L.AS_BF16, 1, 4096, _p(), L.AS_BF16, 4096, 0.5, _p(X + 4096), L.AS_F32,
+                               L.AS_FLAG_ATOMIC_SPLITK, None, _p(), need, None)
+    assert st == L.AS_ERR_INVALID_ARG and b"apart from X" in lib.as_last_error()
+    w = L.ASMlpWeights(_p(), _p(), L.AS_BF16, 4096, 14336)
+    nm = lib.as_sparse_swiglu_mlp_ws_size(1, ctypes.byref(w), L.AS_MLP_THRESHOLD)
+    st = lib.as_sparse_swiglu_mlp(_p(X), L.AS_F32, 1, ctypes.byref(w), L.AS_MLP_THRESHOLD, 0.5, 0.5, None, 0,
+                                  _p(X), L.AS_F32, L.AS_FLAG_ATOMIC_SPLITK, None, _p(), nm, None)
+    assert st == L.AS_ERR_INVALID_ARG and b"apart from X" in lib.as_last_error()
+    mw = L.ASMoeWeights(_p(), _p(), L.AS_BF16, 128, 2048, 768)
+    ne = lib.as_sparse_moe_expert_ws_size(1, 8, ctypes.byref(mw))
+    st = lib.as_sparse_moe_expert(_p(X), L.AS_BF16, 1, _p(), _p(), 8, ctypes.byref(mw), 77, _p(X - 1024), L.AS_F32,
+                                  L.AS_FLAG_ATOMIC_SPLITK, None, None, None, _p(), ne, None)
+    assert st == L.AS_ERR_INVALID_ARG and b"apart from X" in lib.as_last_error()
+
+
+def test_library_reads_no_environment():
+    """The launch plans (and so the workspace carve-ups) depend on the shapes only:
+    no library source reads an environment variable."""
+    csrc = os.path.join(ROOT, "activation_sparse_gemv_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        src = open(os.path.join(csrc, f)).read()
+        assert "getenv" not in src and "environ" not in src, f
 
 
 def test_topk_moe_block_validation(lib):
@@ -161,6 +194,11 @@ def test_topk_moe_block_validation(lib):
     th = L.ASBlockThresholds(0.5, 0.5, 0.5, 0.5)
     assert lib.as_decoder_block(_p(), L.AS_BF16, ctypes.byref(bw), _p(), _p(), 2048, ctypes.byref(th), _p(), 0,
                                 None, _p(), need - 256, None) == L.AS_ERR_WORKSPACE
+    # the down-input mask exports bits and nnz, never an index list
+    dbg = L.ASBlockDebug()
+    dbg.down_in = L.ASMaskOut(None, _p(), None)
+    assert lib.as_decoder_block(_p(), L.AS_BF16, ctypes.byref(bw), _p(), _p(), 2048, ctypes.byref(th), _p(), 0,
+                                ctypes.byref(dbg), _p(), need, None) == L.AS_ERR_UNSUPPORTED
 
 
 def test_workspace_init_and_flush_validation(lib):

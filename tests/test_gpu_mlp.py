@@ -38,12 +38,18 @@ def _check_stagewise(x, w, t_x, t_h, M):
     assert dbg["x_mask"]["nnz"].cpu().numpy().tolist() == m1.sum(axis=1).tolist()
     r = teal.swiglu_mlp_threshold(X, w["Wg"], w["Wu"], w["Wd"], t_x, t_h)
     h_gpu = f64(dbg["h"])
-    assert rel_err(h_gpu, r["h"]) < TOL
+    # h: exact products, fp32 sums, fp32 SwiGLU; y: a plain GEMV of the GPU's h, whose
+    # matrix-core path (more than 8 tokens) carries each fp32 activation as bf16 hi +
+    # lo (2^-17 relative per term)
+    tol_y = 2e-5 if M <= 8 else 2e-4
+    eh = rel_err(h_gpu, r["h"])
+    assert eh < 1e-5, eh
     m2 = teal.magnitude_mask(h_gpu, t_h)
     assert np.array_equal(bits_to_bool(dbg["h_mask"]["bits"], f), m2)
+    assert dbg["h_mask"]["nnz"].cpu().numpy().tolist() == m2.sum(axis=1).tolist()
     y_ref = teal.down_stage(h_gpu, w["Wd"], t_h)
     err = rel_err(y, y_ref)
-    assert err < TOL, err
+    assert err < tol_y, err
     flips = int((m2 != r["m2"]).sum())
     e2e = rel_err(y, r["y"])
     if flips == 0:
@@ -113,13 +119,14 @@ def test_mlp_dense_baseline_matches_dense_oracle():
     assert rel_err(y0, ref) < TOL
 
 
-@pytest.mark.parametrize("cfg,M", [(1, 1), (2, 1), (1, 4)])
-def test_mlp_unsummed_partials_equal_summed(cfg, M, monkeypatch):
-    """The down stage that sums the gate/up split-K partials of its own h range in its
-    prologue forms the same h (same slice order, same SwiGLU) and so the same y, bit for
-    bit, as the gate/up launch's own combine followed by the range-masked down stage; the
-    one-launch MLP forms the same h and h mask too."""
-    announce(f"mlp unsummed partials cfg={cfg} M={M}")
+@pytest.mark.parametrize("cfg,M", [(1, 1), (2, 1), (1, 4), (2, 8), (2, 16)])
+def test_mlp_h_mask_count_and_reproducibility(cfg, M):
+    """The h-mask count export equals the popcount of the exported bits (and the
+    oracle's count on the GPU's h), and the whole call is bitwise reproducible: the
+    same y, h and masks on a second call with the same workspace (the one-token path
+    sums the unsummed gate/up partials in the down prologue; several tokens combine
+    in the gate/up launch; 16 tokens run on the matrix cores)."""
+    announce(f"mlp h nnz + run twice cfg={cfg} M={M}")
     shape = datagen.CFG1 if cfg == 1 else datagen.CFG2
     w = _mlp(cfg, shape)
     gen = datagen.laplace if cfg == 1 else datagen.student_t
@@ -127,19 +134,17 @@ def test_mlp_unsummed_partials_equal_summed(cfg, M, monkeypatch):
     calib = gen((64, shape.d_model), datagen.seed_for(cfg, 0, "calib"), **kw)
     x = gen((M, shape.d_model), datagen.seed_for(cfg, 5, "decode"), **kw).to(DEV)
     t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], 0.5, 0.5)
-    out = {}
-    monkeypatch.setenv("AS_GU_S", "5")     # the same gate/up split (so the same sums) in every mode
-    for mode in (0, 1, 2):
-        monkeypatch.setenv("AS_DN_PARTS", str(min(mode, 1)))
-        monkeypatch.setenv("AS_FUSED", "1" if mode == 2 else "0")
-        y, dbg = asg.as_sparse_swiglu_mlp(x, w["dev"], float(t_x), float(t_h), debug=True)
-        out[mode] = (y, dbg["h"].clone(), dbg["h_mask"]["bits"].clone())
-    for mode in (1, 2):
-        assert torch.equal(out[0][1], out[mode][1])
-        assert torch.equal(out[0][2], out[mode][2])
-    assert torch.equal(out[0][0], out[1][0])
-    # the one-launch MLP splits the down rows differently: same rows, other sum order
-    assert rel_err(out[2][0], f64(out[0][0])) < 1e-5
+    y1, d1 = asg.as_sparse_swiglu_mlp(x, w["dev"], float(t_x), float(t_h), debug=True)
+    y2, d2 = asg.as_sparse_swiglu_mlp(x, w["dev"], float(t_x), float(t_h), debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(d1["h"], d2["h"])
+    for k in ("bits", "nnz"):
+        assert torch.equal(d1["h_mask"][k], d2["h_mask"][k])
+        assert torch.equal(d1["x_mask"][k], d2["x_mask"][k])
+    f = shape.d_ff
+    m2 = teal.magnitude_mask(f64(d1["h"]), t_h)
+    assert np.array_equal(bits_to_bool(d1["h_mask"]["bits"], f), m2)
+    assert d1["h_mask"]["nnz"].cpu().numpy().tolist() == m2.sum(axis=1).tolist()
 
 
 @pytest.mark.parametrize("cfg,M", [(2, 1), (2, 4), (2, 16), (1, 1), (1, 3)])
@@ -241,35 +246,3 @@ def test_neuron_set_full_equals_dense():
     assert rel_err(y, ref) < TOL
     y2 = asg.as_sparse_swiglu_mlp(x.to(DEV), w, neuron_idx=torch.arange(f, dtype=torch.int32, device=DEV))
     assert rel_err(y2, ref) < TOL
-
-
-_PLANS = [dict(AS_GU_LPR=16, AS_GU_S=1), dict(AS_GU_LPR=16, AS_GU_S=2, AS_DN_TPW=1),
-          dict(AS_GU_LPR=32, AS_GU_S=3, AS_DN_LPR=32, AS_DN_TPW=2), dict(AS_DN_LPR=64, AS_DN_TPW=1),
-          dict(AS_GU_LPR=64, AS_GU_S=5, AS_DN_LPR=16, AS_DN_TPW=3), dict(AS_DN_TILES=1),
-          dict(AS_FUSED=1), dict(AS_FUSED=1, AS_DN_TPW=2, AS_DN_LPR=32), dict(AS_DN_S=13),
-          dict(AS_DN_PARTS=0), dict(AS_DN_PARTS=1, AS_GU_S=11), dict(AS_DN_PARTS=1, AS_GU_S=1, AS_DN_LPR=32),
-          dict(AS_FUSED=1, AS_FX_K2=1), dict(AS_FUSED=1, AS_FX_K2=3, AS_GU_S=5), dict(AS_FUSED=1, AS_GU_S=11)]
-
-
-@pytest.mark.parametrize("plan", range(len(_PLANS)))
-@pytest.mark.parametrize("cfg,M", [(1, 1), (1, 8), (2, 1), (2, 16)])
-def test_mlp_launch_plans(plan, cfg, M, monkeypatch):
-    """Other tile widths, split-K factors, down-stage input modes (h ranges, h-tile lists)
-    and the one-launch variant (set through the launch-plan overrides) compute the same
-    MLP: the small fp16 shape for 1 and 8 tokens, the Llama shape for 1 and 16 tokens
-    (matrix cores), 50% thresholds."""
-    for k, v in _PLANS[plan].items():
-        monkeypatch.setenv(k, str(v))
-    announce(f"mlp plan {_PLANS[plan]} cfg={cfg} M={M}")
-    shape = datagen.CFG1 if cfg == 1 else datagen.CFG2
-    w = _mlp(cfg, shape)
-    if cfg == 1:
-        calib = datagen.laplace((64, shape.d_model), datagen.seed_for(1, 0, "calib"), dtype="f16")
-        toks = datagen.laplace((M, shape.d_model), datagen.seed_for(1, 3, "decode"), dtype="f16")
-    else:
-        calib = datagen.student_t((64, shape.d_model), datagen.seed_for(2, 0, "calib"))
-        toks = datagen.student_t((M, shape.d_model), datagen.seed_for(2, 3, "decode"))
-    t_x, t_h, _ = teal.calibrate_mlp(f64(calib), w["Wg"], w["Wu"], 0.5, 0.5)
-    _check_stagewise(toks, w, float(t_x), float(t_h), M)
-    y = asg.as_sparse_swiglu_mlp(toks.to(DEV), w["dev"], 5.0, 5.0, flags=L.AS_FLAG_FORCE_DENSE)
-    assert rel_err(y, teal.dense_mlp(f64(toks), w["Wg"], w["Wu"], w["Wd"])) < TOL

@@ -141,15 +141,13 @@ def test_router_gemv_fused(T, E, top):
 
 @pytest.mark.parametrize("T", [1, 2, 4, 8])
 @pytest.mark.parametrize("dense", [0, 1])
-def test_moe_layer_one_stream_equals_composition(T, dense, monkeypatch):
+def test_moe_layer_one_stream_equals_composition(T, dense):
     """as_moe_layer (three launches on one stream, independent pieces side by side in
     one launch) gives the bits of the layer composed from the separate entry points
-    (router GEMV with routing, dense shared MLP whose down stage sums the gate/up
-    partials, routed experts accumulated), intermediates included, when the composed
-    shared MLP takes the layer's split of its down stage (one row range per CU and
-    column tile: 2048 columns in tiles of 128)."""
-    monkeypatch.setenv("AS_DN_PARTS", "1")
-    monkeypatch.setenv("AS_DN_S", str(torch.cuda.get_device_properties(0).multi_processor_count // 16))
+    (router GEMV with routing, dense shared MLP, routed experts accumulated) for every
+    intermediate (logits, routing, h, keep sets); Y agrees to 1e-5 (the layer splits
+    the shared expert's down stage one row range per CU and column tile, another
+    fp32 summation order of the same terms)."""
     announce(f"moe one-stream T={T} dense={dense}")
     c = datagen.CFG5
     w, dw = _weights(c["n_experts"], c["d_model"], c["d_ff_e"], c["d_ff_shared"])
@@ -163,8 +161,8 @@ def test_moe_layer_one_stream_equals_composition(T, dense, monkeypatch):
         assert torch.equal(d1[k], d2[k]), k
     if not dense:
         assert torch.equal(d1["keep"], d2["keep"])
-    assert torch.equal(Y1, Y2)
-    Y3 = asg.as_moe_layer(X, dw, c["top"], c["keep"], flags=flags)     # workspace reuse
+    assert rel_err(Y1, f64(Y2)) < 1e-5
+    Y3 = asg.as_moe_layer(X, dw, c["top"], c["keep"], flags=flags)     # workspace reuse: the same bits
     assert torch.equal(Y3, Y1)
 
 
@@ -310,21 +308,19 @@ def test_moe_layer_fp16_and_composed_paths():
 
 
 @pytest.mark.parametrize("T", [1, 3])
-def test_keep_sets_chosen_in_either_stage(T, monkeypatch):
-    """The keep sets chosen at the end of the gate/up stage (last neuron block of each
-    expert) or at the start of the down stage give the same bits (same selection on
-    the same h)."""
+def test_keep_sets_chosen_in_either_stage(T):
+    """The keep sets are chosen at the end of the gate/up stage (the one-stream layer
+    with more than 8 (token, slot) items: its last neuron block of each expert) or at
+    the start of the down stage (the routed-expert entry point; the layer with at most
+    8 items): the same selection on the same h gives the same bits either way."""
     announce(f"moe selection placement T={T}")
     c = datagen.CFG5
     w, dw = _weights(c["n_experts"], c["d_model"], c["d_ff_e"], c["d_ff_shared"])
     X = datagen.student_t((T, c["d_model"]), 900 + T).to(DEV)
     logits, ids, wts = asg.as_moe_router_gemv(X, dw.w_router, c["top"])
-    out = {}
-    for v in ("0", "1"):
-        monkeypatch.setenv("AS_MOE_SEL_GU", v)
-        Y, dbg = asg.as_sparse_moe_expert(X, dw, ids, wts, c["keep"], debug=True)
-        Y2 = asg.as_moe_layer(X, dw, c["top"], c["keep"])
-        torch.cuda.synchronize()
-        out[v] = (Y.clone(), dbg["h"].clone(), dbg["keep"].clone(), Y2.clone())
-    for a, b in zip(out["0"], out["1"]):
-        assert torch.equal(a, b)
+    Ye, de = asg.as_sparse_moe_expert(X, dw, ids, wts, c["keep"], debug=True)
+    Yl, dl = asg.as_moe_layer(X, dw, c["top"], c["keep"], debug=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dl["ids"], ids) and torch.equal(dl["wts"], wts)
+    assert torch.equal(de["h"], dl["h"])
+    assert torch.equal(de["keep"], dl["keep"])

@@ -170,3 +170,22 @@ def test_decoder_block_dense_special_case():
     t = dict(qkv=np.float32(0.5), o=np.float32(0.3), gu=np.float32(0.5), d=np.float32(0.01))
     r2 = block.decoder_block(x, wqkv, wo, wgu, wd, K, V, t, nq, nkv, hd)
     np.testing.assert_allclose(r2["y_att"], teal.masked_gemv(r2["o"], wo, t["o"]), rtol=1e-13)
+
+
+def test_decoder_block_rows_are_independent_tokens():
+    """Tokens passed together [T, d] give row by row the results of one-token calls
+    (the rows only share the matrix products), with thresholds on."""
+    d, nq, nkv, hd, f, n = 64, 4, 2, 16, 96, 10
+    rng = np.random.default_rng(16)
+    wqkv = rng.standard_normal((d, (nq + 2 * nkv) * hd)) * 0.1
+    wo = rng.standard_normal((nq * hd, d)) * 0.1
+    wgu = rng.standard_normal((d, 2, f)) * 0.1
+    wd = rng.standard_normal((f, d)) * 0.1
+    K, V = rng.standard_normal((n, nkv, hd)), rng.standard_normal((n, nkv, hd))
+    X = rng.standard_normal((3, d))
+    t = dict(qkv=np.float32(0.5), o=np.float32(0.3), gu=np.float32(0.5), d=np.float32(0.01))
+    rb = block.decoder_block(X, wqkv, wo, wgu, wd, K, V, t, nq, nkv, hd)
+    for i in range(3):
+        r1 = block.decoder_block(X[i], wqkv, wo, wgu, wd, K, V, t, nq, nkv, hd)
+        for k in ("xn", "qkv", "o", "h1", "xn2", "h", "out"):
+            np.testing.assert_allclose(rb[k][i], r1[k], rtol=1e-13, atol=1e-15, err_msg=k)

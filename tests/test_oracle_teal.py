@@ -185,3 +185,21 @@ def test_bitmask_words():
     m[[0, 63, 64, 129]] = True
     w = teal.bitmask_words(m)
     assert w.tolist() == [1 | (1 << 63), 1, 2]
+
+
+def test_datagen_normal_is_chunk_and_thread_invariant():
+    """Large normal draws are split into chunks of jumped PCG64 streams generated on
+    threads: the values do not depend on the thread count, the first chunk is the
+    plain stream of the seed, and an empty draw is empty."""
+    import numpy as np
+    import torch
+    from activation_sparse_gemv_amd import datagen
+    n = datagen._CHUNK + 1000
+    a = datagen.normal((n,), 11, dtype="f32")
+    b = datagen.normal((n,), 11, dtype="f32")
+    assert torch.equal(a, b)
+    first = np.random.Generator(np.random.PCG64(11)).standard_normal(1000, dtype=np.float32) * np.float32(0.02)
+    assert np.array_equal(a[:1000].numpy(), first)
+    tail = np.random.Generator(np.random.PCG64(11).jumped(1)).standard_normal(1000, dtype=np.float32) * np.float32(0.02)
+    assert np.array_equal(a[datagen._CHUNK:].numpy(), tail)
+    assert datagen.normal((0, 4), 3).numel() == 0
