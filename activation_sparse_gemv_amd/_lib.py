@@ -77,6 +77,9 @@ SIGNATURES = {
     "as_sparse_swiglu_mlp": (c_int, [c_void_p, c_int, c_int, POINTER(ASMlpWeights), c_int, c_float, c_float,
                                      c_void_p, c_int, c_void_p, c_int, c_uint, POINTER(ASMlpDebug),
                                      c_void_p, c_size_t, c_void_p]),
+    "as_sparse_swiglu_mlp_noalloc": (c_int, [c_void_p, c_int, c_int, POINTER(ASMlpWeights), c_int, c_float,
+                                             c_float, c_void_p, c_int, c_void_p, c_int, c_uint, POINTER(ASMlpDebug),
+                                             c_void_p]),
     "as_topk_mask_ws_size": (c_size_t, [c_int, c_int, c_int]),
     "as_topk_mask": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
                              c_void_p, c_size_t, c_void_p]),

@@ -197,6 +197,20 @@ def as_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float = float("-in
     return (out, dd) if debug else out
 
 
+def as_sparse_swiglu_mlp_noalloc(X: torch.Tensor, w: MLPWeights, Y: torch.Tensor, t_x: float = float("-inf"),
+                                 t_h: float = float("-inf"), neuron_idx: torch.Tensor | None = None, flags: int = 0):
+    """as_sparse_swiglu_mlp on the library's static per-device scratch (no workspace
+    argument; the C call allocates nothing).  The caller passes the output Y."""
+    X2 = X.reshape(1, -1) if X.dim() == 1 else X
+    _need_cuda(X2, w.w_gate_up, w.w_down, neuron_idx, Y)
+    ws_ = w.struct()
+    n_active = 0 if neuron_idx is None else neuron_idx.numel()
+    L.check(L.load().as_sparse_swiglu_mlp_noalloc(_ptr(X2), _dt(X2), X2.shape[0], ctypes.byref(ws_), w.mode,
+                                                  float(t_x), float(t_h), _ptr(neuron_idx), n_active, _ptr(Y), _dt(Y),
+                                                  flags, None, _stream(X.device)), "as_sparse_swiglu_mlp_noalloc")
+    return Y
+
+
 def as_topk_mask(score: torch.Tensor, k: int, prior: torch.Tensor | None = None, lam: float = 0.5,
                  mode: int | None = None, want_mask: bool = True, want_idx: bool = True):
     """Exact top-k per row (value mode, or the GLASS rank blend when ``prior`` is

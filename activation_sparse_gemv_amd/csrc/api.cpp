@@ -27,6 +27,13 @@ as_status fail(as_status s, const char* fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+// Error reporting for the entry points defined in other source files.
+as_status as::report_error(as_status s, const char* msg) { return fail(s, "%s", msg); }
+
+namespace {
+
 as_status hip_check(hipError_t e, const char* what) {
   if (e == hipSuccess) return AS_OK;
   return fail(AS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

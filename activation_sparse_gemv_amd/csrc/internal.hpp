@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include "../../include/actsparse.h"
+
 namespace as {
 
 enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_RANGE = 4, IN_PARTS = 5 };
@@ -147,6 +149,9 @@ int attention_max_chunks();
 // GLASS local signal (see glass.hip).
 hipError_t launch_local_signal(const uint16_t* X, int P, int d, const uint16_t* W, long ld_neuron, long up_off,
                                int d_ff, float* local, hipStream_t s);
+
+// Sets the calling thread's last-error text (as_last_error) and returns s.
+as_status report_error(as_status s, const char* msg);
 
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

@@ -196,6 +196,23 @@ as_status as_sparse_swiglu_mlp(const void *X, as_dtype x_dt, int M, const as_mlp
                                void *Y, as_dtype y_dt, unsigned flags, as_mlp_debug *dbg,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Allocation-free as_sparse_swiglu_mlp, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The workspace is a static device array of 16 MiB (enough for up to 8
+ * tokens at d_model 4096, d_ff 14336) that every GPU the library runs on holds until
+ * the process ends; the call allocates nothing.  Arguments, results and errors are
+ * those of as_sparse_swiglu_mlp, which it runs on that memory (the same kernels and
+ * bits); UNSUPPORTED when the call needs a larger workspace than the array (see
+ * as_sparse_swiglu_mlp_ws_size).  The bytes a call uses are cleared (one fill kernel
+ * on `stream`) on a device's first call and whenever the shapes change.  Every call
+ * on a GPU shares that GPU's array: calls that overlap on one GPU (from several
+ * streams or threads) race. */
+as_status as_sparse_swiglu_mlp_noalloc(const void *X, as_dtype x_dt, int M, const as_mlp_weights *w,
+                                       as_mlp_mode mode, float t_x, float t_h,
+                                       const int32_t *neuron_idx, int n_active,
+                                       void *Y, as_dtype y_dt, unsigned flags, as_mlp_debug *dbg,
+                                       hipStream_t stream);
+
 /* ------------------------------------------------------------ top-k neuron masks */
 typedef enum { AS_TOPK_VALUE = 0, AS_TOPK_RANK_BLEND = 1 } as_topk_mode;
 
