@@ -104,6 +104,7 @@ SIGNATURES = {
                                  c_size_t, c_void_p]),
     "as_glass_local_signal": (c_int, [c_void_p, c_int, c_int, POINTER(ASMlpWeights), c_void_p, c_void_p]),
     "as_bench_flush": (c_int, [c_void_p, c_size_t, c_void_p]),
+    "as_bench_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
 }
 
 _lib = None

@@ -541,6 +541,12 @@ def as_bench_flush(buf: torch.Tensor):
             "as_bench_flush")
 
 
+def as_bench_read(buf: torch.Tensor, sink: torch.Tensor):
+    _need_cuda(buf, sink)
+    L.check(L.load().as_bench_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf.device)),
+            "as_bench_read")
+
+
 def unpack_bits(bits: torch.Tensor, n: int) -> torch.Tensor:
     """[M, words] int64 bitmask -> [M, n] bool (bit i%64 of word i//64)."""
     b = bits.cpu().view(torch.int64)

@@ -275,6 +275,14 @@ as_status as_bench_flush(void* buf, size_t bytes, hipStream_t stream) {
   return hip_check(launch_fill_pattern(buf, bytes, 0x9e3779b9u * salt.fetch_add(1u), stream), "as_bench_flush");
 }
 
+as_status as_bench_read(const void* buf, size_t bytes, unsigned* sink, hipStream_t stream) {
+  if (bytes == 0) return AS_OK;
+  if (!buf || !sink) return fail(AS_ERR_INVALID_ARG, "as_bench_read: NULL pointer");
+  if (!aligned16(buf) || bytes % 16 != 0)
+    return fail(AS_ERR_INVALID_ARG, "as_bench_read: buf must be 16-byte aligned and bytes a multiple of 16");
+  return hip_check(launch_read_probe(buf, bytes, sink, num_cus(), stream), "as_bench_read");
+}
+
 size_t as_calibrate_threshold_ws_size(int64_t n) { return n < 1 ? 0 : up256(calibrate_ws_bytes()); }
 
 as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64_t p_num, int64_t p_den,

@@ -156,6 +156,7 @@ as_status report_error(as_status s, const char* msg);
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);
+hipError_t launch_read_probe(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t s);
 size_t calibrate_ws_bytes();
 hipError_t launch_calibrate(const void* pool, int dt, int64_t n, int64_t rank, float* t_out, unsigned* ghist,
                             hipStream_t s);

@@ -35,6 +35,39 @@ hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s)
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) { return launch_fill_pattern(p, bytes, 0u, s); }
 
+// Streaming read of n16 16-byte vectors (benchmark probe of the achievable HBM read
+// bandwidth): every thread keeps eight nontemporal loads in flight and folds them
+// into a running XOR; the result is stored only when it equals a value no input is
+// meant to produce, so the loads are kept but nothing is written in practice.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* p, size_t n16, unsigned* sink) {
+  constexpr int kU = 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  u32x4 acc{0u, 0u, 0u, 0u};
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += stride * kU) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t j = i + u * stride;
+      v[u] = j < n16 ? __builtin_nontemporal_load(p + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc ^= v[u];
+  }
+  const unsigned r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (r == 0x9e3779b9u) atomicAdd(sink, 1u);
+}
+
+hipError_t launch_read_probe(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (size_t)cus * 8;
+  const size_t need = (n16 + 255) / 256;
+  if (blocks > need) blocks = need;
+  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const u32x4*>(p),
+                     n16, sink);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- calibration
 // TEAL slides, method slide: t_p is decided from calibration data for the target
 // sparsity.  Nearest-rank order statistic of |pool| by an MSB-first radix select

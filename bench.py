@@ -11,14 +11,19 @@ weight buffers, so no layer is still resident in the 256 MB Infinity Cache when
 it runs again).  value = achieved GB/s of active-row bytes (the weight rows of
 surviving inputs only) over the whole sparse MLP.
 
-Also reported, each with the fp64 CPU oracle timed on a bounded sample beside it:
-the dense baseline (same kernels over every row), the dominant kernel's roofline
-from HIP events recorded around it on its own stream, a sparsity sweep, and one
-entry per hot-path step (calibration, threshold GEMV, top-k / rank blend, GLASS
-local signal + static-mask MLP, MoE router + routed + shared experts, 16-token
-batches on the matrix cores, the full decoder block, the small fp16 MLP).
-Sub-benchmarks are timed as HIP-graph replays of sequences rotating over weight
-copies (launch overhead excluded, caches not reused across a copy's uses).
+Also reported: the per-step distribution (p10 / p50 / p90 of us per layer), the
+dense baseline (same kernels over every row), a streaming-read probe of the
+achievable HBM bandwidth (as_bench_read over 4 GiB) and the fractions of it
+reached, the dominant kernel's roofline from HIP events recorded around it on its
+own stream (and from the committed rocprofv3 trace when it matches the sources), a
+sparsity sweep, and one entry per hot-path step (calibration, threshold GEMV,
+top-k / rank blend, GLASS local signal + static-mask MLP, MoE router + routed +
+shared experts, 16-token batches on the matrix cores, the 32-block decode step,
+the small fp16 MLP cold and warm), each with the fp64 CPU oracle timed on a
+bounded sample beside it (the CPU baseline leg, which also checks the parity of a
+few headline tokens stage by stage).  Sub-benchmarks are timed as HIP-graph
+replays of sequences rotating over weight copies (launch overhead excluded, at
+least about 1 GB of other weights between two uses of a copy's bytes).
 """
 from __future__ import annotations
 
@@ -154,29 +159,33 @@ def headline(a, C):
         return out
 
     def run(t_x, t_h, flags, steps, warmup, per_kernel):
+        """Times `steps` steps of a.layers MLP calls; returns the total ms, the per-kernel
+        event times (per_kernel), the tokens used and the per-step us per layer."""
         evs = [[L.HipEvent() for _ in range(3)] for _ in range(steps * a.layers)] if per_kernel else []
         Y = torch.empty((1, d), dtype=torch.float32, device=dev)
         warm = [asg.api.prepare_sparse_swiglu_mlp(toks[(s * a.layers + l) % n_tok], w, t_x, t_h, Y, flags=flags)
                 for s in range(warmup) for l, w in enumerate(layers)]
-        calls = [asg.api.prepare_sparse_swiglu_mlp(toks[(s * a.layers + l) % n_tok], w, t_x, t_h, Y, flags=flags,
-                                                   events=evs[s * a.layers + l] if per_kernel else None)
-                 for s in range(steps) for l, w in enumerate(layers)]
+        calls = [[asg.api.prepare_sparse_swiglu_mlp(toks[(s * a.layers + l) % n_tok], w, t_x, t_h, Y, flags=flags,
+                                                    events=evs[s * a.layers + l] if per_kernel else None)
+                  for l, w in enumerate(layers)] for s in range(steps)]
         for c in warm:
             c()
         torch.cuda.synchronize()
-        e0, e1 = L.HipEvent(), L.HipEvent()
-        e0.record(C.stream)
-        for c in calls:
-            c()
-        e1.record(C.stream)
+        marks = [L.HipEvent() for _ in range(steps + 1)]
+        marks[0].record(C.stream)
+        for s_, step in enumerate(calls):
+            for c in step:
+                c()
+            marks[s_ + 1].record(C.stream)
         torch.cuda.synchronize()
-        total_ms = e0.elapsed_ms(e1)
+        total_ms = marks[0].elapsed_ms(marks[-1])
+        per_step = np.array([marks[i].elapsed_ms(marks[i + 1]) for i in range(steps)]) * 1e3 / a.layers
         k1 = k2 = None
         if per_kernel:
             k1 = np.array([e[0].elapsed_ms(e[1]) for e in evs]) * 1e3
             k2 = np.array([e[1].elapsed_ms(e[2]) for e in evs]) * 1e3
         used = [(s * a.layers + l) % n_tok for s in range(steps) for l in range(a.layers)]
-        return total_ms, k1, k2, used
+        return total_ms, k1, k2, used, per_step
 
     res = {}
     sweep = SWEEP if not a.no_sweep else (a.sparsity,)
@@ -185,36 +194,49 @@ def headline(a, C):
     for s in sweep:
         t_x, t_h = calibrate(s)
         ab = active_bytes(t_x, t_h)
-        total_ms, _, _, used = run(t_x, t_h, a.flags, a.steps, a.warmup, per_kernel=False)
+        total_ms, _, _, used, per_step = run(t_x, t_h, a.flags, a.steps, a.warmup, per_kernel=False)
         calls = a.steps * a.layers
         bytes_tot = sum(ab[t][0] + ab[t][1] for t in used)
         r = dict(sparsity=s, t_x=t_x, t_h=t_h, us_per_layer=total_ms * 1e3 / calls,
                  gbs=bytes_tot / (total_ms * 1e-3) / 1e9,
                  realized_sparsity_x=1 - np.mean([ab[t][2] for t in used]) / d,
                  realized_sparsity_h=1 - np.mean([ab[t][3] for t in used]) / f,
-                 active_mb_per_layer=bytes_tot / calls / 1e6, total_ms=total_ms)
+                 active_mb_per_layer=bytes_tot / calls / 1e6, total_ms=total_ms,
+                 us_p10=float(np.percentile(per_step, 10)), us_p50=float(np.median(per_step)),
+                 us_p90=float(np.percentile(per_step, 90)))
         if abs(s - a.sparsity) < 1e-9:
-            _, k1, k2, used_k = run(t_x, t_h, a.flags, a.steps, 2, per_kernel=True)
+            _, k1, k2, used_k, _ = run(t_x, t_h, a.flags, a.steps, 2, per_kernel=True)
             b1 = np.array([ab[t][0] for t in used_k], dtype=np.float64)
             r["stage1_us"], r["stage2_us"] = float(k1.mean()), float(k2.mean())
             r["stage1_gbs"] = float(b1.sum() / (k1.sum() * 1e-6) / 1e9)
             r["stage1_bytes_per_launch"] = float(b1.mean())
             # the same step with the down stage's slices adding into Y atomically (no
             # deterministic combine); reported beside the headline, not as it
-            at_ms, _, _, _ = run(t_x, t_h, a.flags | L.AS_FLAG_ATOMIC_SPLITK, a.steps, a.warmup, per_kernel=False)
+            at_ms, _, _, _, _ = run(t_x, t_h, a.flags | L.AS_FLAG_ATOMIC_SPLITK, a.steps, a.warmup, per_kernel=False)
             r["atomic_us_per_layer"] = at_ms * 1e3 / calls
             r["atomic_gbs"] = bytes_tot / (at_ms * 1e-3) / 1e9
         res[s] = r
         log(f"s={s:.2f} {r['us_per_layer']:.2f} us/layer {r['gbs']:.0f} GB/s (active {r['active_mb_per_layer']:.1f} MB)")
-    dense_ms, _, _, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE, a.steps, a.warmup, per_kernel=False)
-    _, dk1, dk2, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE, a.steps, 2, per_kernel=True)
+    dense_ms, _, _, _, dense_steps = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE, a.steps, a.warmup,
+                                         per_kernel=False)
+    _, dk1, dk2, _, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE, a.steps, 2, per_kernel=True)
     dense_us = dense_ms * 1e3 / (a.steps * a.layers)
-    dense_at_ms, _, _, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK, a.steps, a.warmup,
-                               per_kernel=False)
+    dense_at_ms, _, _, _, _ = run(0.0, 0.0, a.flags | L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK, a.steps,
+                                  a.warmup, per_kernel=False)
     dense_at_us = dense_at_ms * 1e3 / (a.steps * a.layers)
     dense_bytes = d * row_gu + f * row_d
     log(f"dense {dense_us:.2f} us/layer {dense_bytes / (dense_us * 1e-6) / 1e9:.0f} GB/s")
     m = res[a.sparsity]
+    probe = read_probe(C)
+    log(f"streaming-read probe {probe:.0f} GB/s")
+    # GPU exports of a few tokens for the parity summary (compared with the oracle in the CPU leg)
+    samples = []
+    for i in range(4):
+        y, dbg = asg.as_sparse_swiglu_mlp(toks[i:i + 1], w0, m["t_x"], m["t_h"], debug=True)
+        samples.append(dict(x=toks[i].float().cpu(), y=y[0].cpu(), h=dbg["h"][0].cpu(),
+                            x_bits=dbg["x_mask"]["bits"][0].cpu(), x_nnz=int(dbg["x_mask"]["nnz"][0]),
+                            h_bits=dbg["h_mask"]["bits"][0].cpu(), h_nnz=int(dbg["h_mask"]["nnz"][0])))
+    trace_us = kernel_trace_us()
     out = {
         "metric": METRIC,
         "value": round(m["gbs"], 1),
@@ -233,7 +255,11 @@ def headline(a, C):
                    "d_model": d, "d_ff": f, "weights": "bf16", "sparsity": a.sparsity,
                    "layers_per_step": a.layers, "tokens": n_tok},
         "us_per_layer": round(m["us_per_layer"], 3),
+        "us_per_layer_p10_p50_p90": [round(m["us_p10"], 3), round(m["us_p50"], 3), round(m["us_p90"], 3)],
         "dense_us_per_layer": round(dense_us, 3),
+        "dense_us_per_layer_p10_p50_p90": [round(float(np.percentile(dense_steps, q)), 3) for q in (10, 50, 90)],
+        "read_probe_gbs": round(probe, 1),
+        "frac_of_probe_layer": round(m["gbs"] / probe, 4),
         "dense_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
         "speedup_vs_dense": round(dense_us / m["us_per_layer"], 3),
         "frac_of_peak_layer": round(m["gbs"] / PEAK_HBM_GBS, 4),
@@ -247,7 +273,13 @@ def headline(a, C):
         "roofline": {"bound": "hbm", "kernel": "gather_gemv_kernel: gate/up row gather (split-K partials left for the down prologue, which applies SwiGLU)",
                      "achieved": round(m["stage1_gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(m["stage1_gbs"] / PEAK_HBM_GBS, 4),
+                     "timing": "HIP events recorded on the launch stream right before and after each gate/up "
+                               "launch (the time includes the launch's dispatch gap)",
                      "bytes_per_launch": m["stage1_bytes_per_launch"], "us_per_launch": round(m["stage1_us"], 3),
+                     "frac_of_probe": round(m["stage1_gbs"] / probe, 4),
+                     "kernel_trace_us": trace_us,
+                     "frac_kernel_trace": (round(m["stage1_bytes_per_launch"] / (trace_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                                           if trace_us else None),
                      "traffic": traffic_from_profiles()},
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in res[s].items()
                    if k in ("sparsity", "us_per_layer", "gbs", "realized_sparsity_x", "realized_sparsity_h",
@@ -255,7 +287,53 @@ def headline(a, C):
     }
     del layers, w0
     torch.cuda.empty_cache()
-    return out, m["t_x"], m["t_h"]
+    return out, m["t_x"], m["t_h"], samples
+
+
+def read_probe(C, gib: int = 4, reps: int = 5) -> float:
+    """Achievable streaming-read bandwidth (GB/s): as_bench_read over a 4 GiB buffer."""
+    torch, asg = C.torch, C.asg
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=C.dev)
+    asg.as_bench_flush(buf)
+    sink = torch.zeros(1, dtype=torch.int32, device=C.dev)
+    for _ in range(2):
+        asg.as_bench_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = C.L.HipEvent(), C.L.HipEvent()
+    e0.record(C.stream)
+    for _ in range(reps):
+        asg.as_bench_read(buf, sink)
+    e1.record(C.stream)
+    torch.cuda.synchronize()
+    gbs = buf.numel() * reps / (e0.elapsed_ms(e1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def kernel_trace_us():
+    """Average rocprofv3 duration (us) of the dominant kernel's timed dispatches, from the
+    committed trace summary, when it was taken on the current kernel sources (else null)."""
+    p = os.path.join(HERE, "profiles", "gather_gemv_llama_mlp_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+        if rec.get("source_sha256") != kernel_source_hash():
+            return None
+        return rec.get("gate_up_kernel_trace_us")
+    except Exception:
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def traffic_from_profiles():
@@ -280,7 +358,7 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def cpu_baseline_headline(t_x, t_h, seconds):
+def cpu_baseline_headline(t_x, t_h, seconds, samples):
     import torch
     from activation_sparse_gemv_amd import datagen
     from oracle import teal
@@ -298,7 +376,29 @@ def cpu_baseline_headline(t_x, t_h, seconds):
         active[0] += int(r["m1"].sum()) * 2 * shape.d_ff * 2 + int(r["m2"].sum()) * shape.d_model * 2
 
     us, n, el = cpu_time(one, seconds, max_n=100000)
+    # parity of the GPU's sample tokens, stage by stage (masks on the GPU's own tensors)
+    par = dict(tokens=len(samples), x_masks_exact=True, h_masks_exact=True, nnz_exact=True, h_max_rel_err=0.0,
+               y_max_rel_err_given_h=0.0, e2e_max_rel_err=0.0, h_mask_flips_vs_fp64=0)
+    for smp in samples:
+        X = smp["x"].double().numpy()
+        r = teal.swiglu_mlp_threshold(X, Wg, Wu, Wd, t_x, t_h)
+        xb = ((smp["x_bits"].view(torch.int64).numpy()[:, None].astype(np.uint64) >> np.arange(64, dtype=np.uint64))
+              & np.uint64(1)).astype(bool).reshape(-1)[:X.size]
+        h = smp["h"].double().numpy()
+        m2 = teal.magnitude_mask(h, t_h)
+        hb = ((smp["h_bits"].view(torch.int64).numpy()[:, None].astype(np.uint64) >> np.arange(64, dtype=np.uint64))
+              & np.uint64(1)).astype(bool).reshape(-1)[:h.size]
+        par["x_masks_exact"] &= bool(np.array_equal(xb, r["m1"]))
+        par["h_masks_exact"] &= bool(np.array_equal(hb, m2))
+        par["nnz_exact"] &= smp["x_nnz"] == int(r["m1"].sum()) and smp["h_nnz"] == int(m2.sum())
+        err = lambda a, b: float(np.abs(a - b).max() / np.abs(b).max())  # noqa: E731
+        par["h_max_rel_err"] = max(par["h_max_rel_err"], err(h, r["h"]))
+        par["y_max_rel_err_given_h"] = max(par["y_max_rel_err_given_h"],
+                                           err(smp["y"].double().numpy(), teal.down_stage(h, Wd, t_h)))
+        par["e2e_max_rel_err"] = max(par["e2e_max_rel_err"], err(smp["y"].double().numpy(), r["y"]))
+        par["h_mask_flips_vs_fp64"] += int((m2 != r["m2"]).sum())
     return {"value": round(active[0] / el / 1e9, 3), "unit": "GB/s", "cores": cores(), "kind": "oracle",
+            "cpu_model": cpu_model(), "parity": par,
             "us_per_layer": round(us, 1),
             "sample": f"{n} decode tokens through one 4096->14336->4096 threshold MLP (fp64 numpy, same "
                       f"thresholds and tokens as the GPU run), {el:.1f} s; value = the active-row bytes "
@@ -449,19 +549,22 @@ def row_moe(C, cpu):
         return asg.MoEWeights(src["w_gate_up"], src["w_down"], src["w_router"],
                               asg.MLPWeights(src["s_gate_up"], src["s_down"]))
     dev0 = {k: v.to(C.dev) for k, v in w.items()}
-    copies = [mk(dev0)] + [mk({k: v.clone() for k, v in dev0.items()}) for _ in range(2)]
+    # nine weight copies (1.26 GB each, about 104 MB touched per one-token call): a
+    # copy's bytes come back only after about 0.9 GB of other copies at one token,
+    # well past the 256 MB Infinity Cache
+    copies = [mk(dev0)] + [mk({k: v.clone() for k, v in dev0.items()}) for _ in range(8)]
     cases = []
     for T in c["tokens"]:
         X = datagen.student_t((T, d), datagen.seed_for(5, T, "decode")).to(C.dev)
-        fs = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"]) for ww in copies * 2]
+        fs = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"]) for ww in copies]
         fd = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"], flags=L.AS_FLAG_FORCE_DENSE)
-              for ww in copies * 2]
+              for ww in copies]
         fa = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"], flags=L.AS_FLAG_ATOMIC_SPLITK)
-              for ww in copies * 2]
+              for ww in copies]
         us, usd = C.graph_us(fs, reps=10), C.graph_us(fd, reps=10)
         fda = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"],
                                            flags=L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK)
-               for ww in copies * 2]
+               for ww in copies]
         usa, usda = C.graph_us(fa, reps=10), C.graph_us(fda, reps=10)
         _, dbg = asg.moe_layer(X, copies[0], c["top"], c["keep"], debug=True)
         ids = dbg["ids"].cpu().numpy()
@@ -481,7 +584,8 @@ def row_moe(C, cpu):
         log(f"moe T={T}: {us:.1f} us (dense {usd:.1f}); atomic split-K {usa:.1f} (dense {usda:.1f})")
     r = {"step": "a8+a9 MoE layer: router GEMV + top-8/softmax, dense shared expert, routed experts "
                  "(dense gate/up scoring, exact top-77 of 768, gathered down rows)",
-         "shape": "128 experts, d_model 2048, d_ff_e 768, shared d_ff 4096, bf16", "cases": cases}
+         "shape": "128 experts, d_model 2048, d_ff_e 768, shared d_ff 4096, bf16",
+         "rotation": "9 weight copies of 1.26 GB, cycled", "cases": cases}
     if cpu:
         from oracle import moe as omoe
         ow = {"w_router": w["w_router"].double().numpy(), "w_gate_up": _LazyF64(w["w_gate_up"]),
@@ -526,58 +630,99 @@ def row_batch16(C, cpu, t_x, t_h):
 
 
 def row_block(C, cpu):
+    """a11: the 32-block Llama-3-8B-shaped decode step (sparsity 30% -> 60% with depth).
+
+    Every block has its own weights and KV cache (14 GB in all, so no block's bytes
+    are still cached when the next token reaches it).  Thresholds: 256 synthetic
+    calibration vectors enter block 0, each block's four pools are taken in order
+    with the earlier thresholds applied, and the block's outputs are the next
+    block's calibration vectors.  A decode step is one token through the 32 blocks
+    (each block's output is the next block's input), timed as HIP-graph replays of
+    8 steps and, eagerly with events between blocks, per block."""
     torch, asg, L, datagen = C.torch, C.asg, C.L, C.datagen
-    from oracle import block as oblock, teal
-    out = []
-    for layer in (0, 31):
-        s = datagen.cfg3_sparsity(layer)
+    nbk = datagen.CFG3_ATTN["n_blocks"]
+    d, f = 4096, datagen.CFG2.d_ff
+    t0 = time.time()
+    blocks = []
+    for layer in range(nbk):
         wqkv, wo = datagen.attn_weights(3, layer)
         wgu, wd = datagen.mlp_weights_input_major(3, layer, datagen.CFG2)
         kc, vc = datagen.kv_cache(3, layer)
-        bw = asg.BlockWeights(wqkv.to(C.dev), wo.to(C.dev), asg.MLPWeights(wgu.to(C.dev), wd.to(C.dev)))
-        bw2 = asg.BlockWeights(bw.w_qkv.clone(), bw.w_o.clone(),
-                               asg.MLPWeights(bw.mlp.w_gate_up.clone(), bw.mlp.w_down.clone()))
-        kcd, vcd = kc.to(C.dev), vc.to(C.dev)
-        # thresholds: GPU calibration on 64 synthetic vectors, pools taken sequentially through the block
-        calib = datagen.student_t((64, 4096), datagen.seed_for(3, layer, "calib")).to(C.dev)
-        t = dict(qkv=float("-inf"), o=float("-inf"), gate_up=float("-inf"), down=float("-inf"))
-        for key, pk in (("qkv", "xn"), ("o", "o"), ("gate_up", "xn2"), ("down", "h")):
-            pool = torch.stack([asg.as_decoder_block(calib[i], bw, kcd, vcd, t, debug=True)[1][pk]
-                                for i in range(64)])
-            t[key] = float(asg.as_calibrate_threshold(pool, s).item())
-        x = datagen.student_t((8, 4096), datagen.seed_for(3, layer, "decode")).to(C.dev)
-        Y = torch.empty(4096, dtype=torch.float32, device=C.dev)
-        fs = [lambda w=w, i=i: asg.as_decoder_block(x[i % 8], w, kcd, vcd, t, Y=Y) for i, w in enumerate([bw, bw2] * 3)]
-        fd = [lambda w=w, i=i: asg.as_decoder_block(x[i % 8], w, kcd, vcd, t, flags=L.AS_FLAG_FORCE_DENSE, Y=Y)
-              for i, w in enumerate([bw, bw2] * 3)]
-        us, usd = C.graph_us(fs), C.graph_us(fd)
-        # active bytes from the GPU's own intermediates of one token
-        _, g = asg.as_decoder_block(x[0], bw, kcd, vcd, t, debug=True)
-        nx = int((g["xn"].abs() > t["qkv"]).sum().item())
-        no = int((g["o"].abs() > t["o"]).sum().item())
-        nx2 = int((g["xn2"].abs() > t["gate_up"]).sum().item())
-        nh = int((g["h"].abs() > t["down"]).sum().item())
-        ab = (nx * 6144 + no * 4096 + nx2 * 2 * 14336 + nh * 4096) * 2 + 2 * kc.numel() * 2
-        dense_b = (4096 * 6144 + 4096 * 4096 + 4096 * 28672 + 14336 * 4096) * 2 + 2 * kc.numel() * 2
-        r = {"layer": layer, "sparsity": r4(s), "us": r4(us), "dense_us": r4(usd), "speedup": r4(usd / us),
-             "active_mb_incl_kv": r4(ab / 1e6), "dense_mb": r4(dense_b / 1e6),
-             "gbs": r4(ab / (us * 1e-6) / 1e9), "frac_hbm": r4(ab / (us * 1e-6) / 8e12)}
-        if cpu:
-            W = dict(wqkv=wqkv.double().numpy(), wo=wo.double().numpy(), wgu=wgu.double().numpy(),
-                     wd=wd.double().numpy(), kc=kc.double().numpy(), vc=vc.double().numpy())
-            X = x.cpu().double().numpy()
-            to = dict(qkv=t["qkv"], o=t["o"], gu=t["gate_up"], d=t["down"])
-            cu, _, _ = cpu_time(lambda i: oblock.decoder_block(X[i % 8], W["wqkv"], W["wo"], W["wgu"], W["wd"],
-                                                               W["kc"], W["vc"], to), 4.0, 50)
-            r.update(cpu_oracle_us=r4(cu), cpu_cores=cores())
-            del W
-        out.append(r)
-        log(f"block layer {layer}: {us:.1f} us (dense {usd:.1f})")
-        del bw, bw2
-        torch.cuda.empty_cache()
-    return {"step": "a11 decoder block (RMSNorm, thresholded qkv / o / MLP projections, dense GQA attention "
-                    "over 2048 cached keys)", "shape": "Llama-3-8B block, 32/8 heads, bf16, batch 1",
-            "cases": out, "model_step_estimate_us": r4(np.mean([c["us"] for c in out]) * 32)}
+        blocks.append((asg.BlockWeights(wqkv.to(C.dev), wo.to(C.dev), asg.MLPWeights(wgu.to(C.dev), wd.to(C.dev))),
+                       kc.to(C.dev), vc.to(C.dev)))
+        del wqkv, wo, wgu, wd, kc, vc
+    log(f"32 blocks ready in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    xc = datagen.student_t((datagen.N_CALIB, d), datagen.seed_for(3, 0, "calib")).to(C.dev)
+    ts = []
+    for layer, (bw, kc, vc) in enumerate(blocks):
+        t, xc, _ = asg.calibrate_decoder_block(xc, bw, kc, vc, datagen.cfg3_sparsity(layer, nbk))
+        ts.append(t)
+    del xc
+    log(f"32 blocks calibrated (256 vectors, block to block) in {time.time() - t0:.1f}s")
+    toks = datagen.student_t((8, d), datagen.seed_for(3, 0, "decode")).to(C.dev)
+    ping = [torch.empty(d, dtype=torch.float32, device=C.dev) for _ in range(2)]
+
+    def step_calls(i, flags):
+        calls, x = [], toks[i]
+        for layer, (bw, kc, vc) in enumerate(blocks):
+            y = ping[layer % 2]
+            calls.append(lambda x=x, bw=bw, kc=kc, vc=vc, t=ts[layer], y=y:
+                         asg.as_decoder_block(x, bw, kc, vc, t, flags=flags, Y=y))
+            x = y
+        return calls
+
+    us_blk = C.graph_us([c for i in range(8) for c in step_calls(i, 0)], reps=3)
+    us_blk_d = C.graph_us([c for i in range(8) for c in step_calls(i, L.AS_FLAG_FORCE_DENSE)], reps=3)
+    # per block, eager, events between the blocks of each token's step
+    per = np.zeros((8, nbk))
+    for i in range(8):
+        evs = [L.HipEvent() for _ in range(nbk + 1)]
+        evs[0].record(C.stream)
+        for layer, c in enumerate(step_calls(i, 0)):
+            c()
+            evs[layer + 1].record(C.stream)
+        torch.cuda.synchronize()
+        per[i] = [evs[k].elapsed_ms(evs[k + 1]) * 1e3 for k in range(nbk)]
+    # active bytes of one token's step, from the masks the GPU applied
+    act, x = [], toks[0]
+    kv_b = 2 * blocks[0][1].numel() * 2
+    for layer, (bw, kc, vc) in enumerate(blocks):
+        y, g = asg.as_decoder_block(x, bw, kc, vc, ts[layer], debug=True)
+        nx, no = int(g["qkv_in"]["nnz"][0]), int(g["o_in"]["nnz"][0])
+        nx2, nh = int(g["gate_up_in"]["nnz"][0]), int(g["down_in"]["nnz"][0])
+        act.append((nx * 6144 + no * 4096 + nx2 * 2 * f + nh * d) * 2 + kv_b)
+        x = y
+    dense_b = (d * 6144 + 4096 * d + d * 2 * f + f * d) * 2 + kv_b
+    step_us, step_us_d = us_blk * nbk, us_blk_d * nbk
+    ab = float(np.sum(act))
+    r = {"step": "a11 32-block decode step (RMSNorm, thresholded qkv / o / MLP projections, dense GQA attention "
+                 "over 2048 cached keys), thresholds calibrated block to block on 256 vectors",
+         "shape": "32 Llama-3-8B blocks, 32/8 heads, bf16, batch 1, sparsity 0.30 -> 0.60",
+         "step_us": r4(step_us), "dense_step_us": r4(step_us_d), "speedup": r4(step_us_d / step_us),
+         "us_per_block": r4(us_blk), "dense_us_per_block": r4(us_blk_d),
+         "active_gb_per_step_incl_kv": r4(ab / 1e9), "dense_gb_per_step": r4(dense_b * nbk / 1e9),
+         "gbs": r4(ab / (step_us * 1e-6) / 1e9), "frac_hbm": r4(ab / (step_us * 1e-6) / 8e12),
+         "eager_block_us_p50": {"layer0": r4(np.median(per[:, 0])), "layer31": r4(np.median(per[:, -1])),
+                                "all": r4(np.median(per))},
+         "timing": "graph replays of 8 decode steps (8 tokens x 32 blocks); eager per-block times from events "
+                   "between consecutive blocks (include the launch gaps)"}
+    log(f"32-block step: {step_us:.0f} us ({us_blk:.1f} us/block), dense {step_us_d:.0f} us")
+    if cpu:
+        from oracle import block as oblock
+        bw, kc, vc = blocks[0]
+        W = dict(wqkv=bw.w_qkv.cpu().double().numpy(), wo=bw.w_o.cpu().double().numpy(),
+                 wgu=bw.mlp.w_gate_up.cpu().double().numpy(), wd=bw.mlp.w_down.cpu().double().numpy(),
+                 kc=kc.cpu().double().numpy(), vc=vc.cpu().double().numpy())
+        X = toks.cpu().double().numpy()
+        to = dict(qkv=ts[0]["qkv"], o=ts[0]["o"], gu=ts[0]["gate_up"], d=ts[0]["down"])
+        cu, _, _ = cpu_time(lambda i: oblock.decoder_block(X[i % 8], W["wqkv"], W["wo"], W["wgu"], W["wd"],
+                                                           W["kc"], W["vc"], to), 4.0, 50)
+        r.update(cpu_oracle_us_per_block=r4(cu), cpu_cores=cores())
+        del W
+    del blocks
+    torch.cuda.empty_cache()
+    return r
 
 
 def row_small(C, cpu):
@@ -595,8 +740,27 @@ def row_small(C, cpu):
                      for i in range(16)])
     usd = C.graph_us([lambda i=i: asg.as_sparse_swiglu_mlp(toks[i], w, flags=L.AS_FLAG_FORCE_DENSE, Y=Y)
                       for i in range(16)])
+
+    def cold(flags, tx, th, n=20):
+        # each call after a 1 GiB overwrite (Infinity Cache and L2 evicted), events around the call only
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=C.dev)
+        ts = []
+        for i in range(n):
+            asg.as_bench_flush(flush)
+            e0, e1 = C.L.HipEvent(), C.L.HipEvent()
+            e0.record(C.stream)
+            asg.as_sparse_swiglu_mlp(toks[i % 64], w, tx, th, flags=flags, Y=Y)
+            e1.record(C.stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_ms(e1) * 1e3)
+        del flush
+        return float(np.median(ts))
+    uc, udc = cold(0, float(t_x), float(t_h)), cold(L.AS_FLAG_FORCE_DENSE, 0.0, 0.0)
     r = {"step": "small SwiGLU 512->2048->512, fp16 weights, 50%/50% (latency bound: 6.3 MB dense)",
-         "us": r4(us), "dense_us": r4(usd), "speedup": r4(usd / us)}
+         "us": r4(us), "dense_us": r4(usd), "speedup": r4(usd / us),
+         "warm": "HIP-graph replays on the same weights (6.3 MB stay in the Infinity Cache)",
+         "cold_us": r4(uc), "cold_dense_us": r4(udc), "cold_speedup": r4(udc / uc),
+         "cold": "median of 20 calls, each timed by events after a 1 GiB overwrite of device memory"}
     if cpu:
         Wg, Wu, Wd = (wgu[:, 0, :].double().numpy(), wgu[:, 1, :].double().numpy(), wd.double().numpy())
         T = toks.cpu().double().numpy()
@@ -656,7 +820,7 @@ def main():
     if a.traffic_run:
         traffic_run(C)
         return
-    out, t_x, t_h = headline(a, C)
+    out, t_x, t_h, samples = headline(a, C)
     cpu = not a.no_cpu_baseline
     if not a.headline_only:
         rows = {}
@@ -672,7 +836,8 @@ def main():
             log(f"row {name} done in {time.time() - t0:.1f}s")
         out["rows"] = rows
     if cpu:
-        out["cpu_baseline"] = cpu_baseline_headline(t_x, t_h, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_headline(t_x, t_h, a.cpu_seconds, samples)
+        out["parity"] = out["cpu_baseline"]["parity"]
     print(json.dumps(out), flush=True)
 
 

@@ -423,6 +423,14 @@ as_status as_decoder_block(const void *X, as_dtype x_dt, const as_block_weights 
  * Infinity Cache and L2 between timed calls. */
 as_status as_bench_flush(void *buf, size_t bytes, hipStream_t stream);
 
+/* Read `bytes` of device memory at `buf` with 16-byte nontemporal loads, eight in
+ * flight per thread over a grid of eight workgroups per CU: a probe of the
+ * achievable streaming-read bandwidth, against which the kernels' rates are also
+ * reported.  buf 16-byte aligned, bytes a multiple of 16; *sink (one device
+ * unsigned) is written only in the unlikely case that the loaded data fold to one
+ * particular value.  Errors: INVALID_ARG for NULL pointers or misalignment. */
+as_status as_bench_read(const void *buf, size_t bytes, unsigned *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

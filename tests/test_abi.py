@@ -205,6 +205,10 @@ def test_workspace_init_and_flush_validation(lib):
     assert lib.as_workspace_init(None, 64, None) == L.AS_ERR_INVALID_ARG
     assert lib.as_workspace_init(None, 0, None) == L.AS_OK
     assert lib.as_bench_flush(None, 64, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_bench_read(None, 64, _p(), None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_bench_read(_p(), 60, _p(), None) == L.AS_ERR_INVALID_ARG      # not whole 16-byte vectors
+    assert lib.as_bench_read(_p(4100), 64, _p(), None) == L.AS_ERR_INVALID_ARG  # misaligned
+    assert lib.as_bench_read(None, 0, None, None) == L.AS_OK
 
 
 def test_binding_refuses_cpu_tensors():
