@@ -943,13 +943,18 @@ as_status as_rmsnorm(const void* X, as_dtype x_dt, int rows, int d, float eps, f
 }
 
 namespace {
+// Key chunks per kv head: chunks of about 64 keys, at most about one workgroup per
+// CU, but never more than attention_max_keys() keys in a chunk (0 when the context
+// needs more than attention_max_chunks() chunks).
 int attn_chunks(int n_ctx, int n_kv) {
-  int c = (n_ctx + 1 + 63) / 64;
+  const int n_keys = n_ctx + 1;
+  int c = (n_keys + 63) / 64;
   const int max_c = (num_cus() + n_kv - 1) / n_kv;       // about one workgroup per CU
   if (c > max_c) c = max_c;
-  if (c > attention_max_chunks()) c = attention_max_chunks();
+  const int min_c = (n_keys + attention_max_keys() - 1) / attention_max_keys();
+  if (c < min_c) c = min_c;
   if (c < 1) c = 1;
-  return c;
+  return c > attention_max_chunks() ? 0 : c;
 }
 struct AttnWs {
   float* part_o;
@@ -985,6 +990,9 @@ as_status as_gqa_decode_attention(const float* q, const float* k_new, const floa
     return fail(AS_ERR_INVALID_ARG, "%s: n_ctx=%d n_q=%d n_kv=%d hd=%d", fn, n_ctx, n_q, n_kv, head_dim);
   if (n_q / n_kv > attention_max_group() || head_dim != attention_head_dim())
     return fail(AS_ERR_UNSUPPORTED, "%s: group %d (max 8) or head_dim %d (must be 128)", fn, n_q / n_kv, head_dim);
+  if (attn_chunks(n_ctx, n_kv) == 0)
+    return fail(AS_ERR_UNSUPPORTED, "%s: n_ctx=%d above %d", fn, n_ctx,
+                attention_max_chunks() * attention_max_keys() - 1);
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return fail(AS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   Carver c{reinterpret_cast<char*>(ws)};

@@ -28,7 +28,14 @@
 namespace as {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
+// Rows whose weight loads a lane keeps in flight per main-loop step: one token
+// has room for sixteen (the loop is bound by loads in flight per CU: measured on
+// the 4096 x 2 x 14336 gather, 8 rows per lane left it ~15% below the rate that
+// 16 rows reach); several tokens keep eight (their accumulators take the room).
+template <int MT>
+struct Unroll {
+  static constexpr int value = MT == 1 ? 16 : 8;
+};
 
 template <int LPR>
 struct TileShape {
@@ -323,8 +330,12 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
       *inv_out = inv;
 #pragma unroll
       for (int e = 0; e < CEV; ++e) v0[e] *= inv;
-      if (export_xn && p.xn_out != nullptr)
-        for (int e = 0; e < n; ++e) p.xn_out[c0 + e] = v0[e];
+      if (export_xn && p.xn_out != nullptr) {
+        // constant trip count: v0 stays in registers
+#pragma unroll
+        for (int e = 0; e < CEV; ++e)
+          if (e < n) p.xn_out[c0 + e] = v0[e];
+      }
     }
     const bool keep_all = p.keep_all != 0;
 #pragma unroll
@@ -813,6 +824,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
   // Lanes past a ragged column edge read column 0 of the same rows (their sums are
   // discarded), and rows past the end of the slice repeat its last row with x = 0,
   // so every load below is unconditional and all kUnroll loads issue back to back.
+  constexpr int kUnroll = Unroll<MT>::value;
   const uint16_t* Wc = p.W + (valid ? wcol : 0);
   const long ldw = p.ldw;
 

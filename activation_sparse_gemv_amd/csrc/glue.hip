@@ -41,27 +41,31 @@ hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, f
 }
 
 // ---------------------------------------------------------------- attention
-// One decode token.  Workgroup (kv head g, key chunk c) scores its chunk of
-// keys against the n_q / n_kv query heads of the group, keeps the chunk's
-// running max and exp-sum, and its unnormalised partial output; the last chunk
-// of a kv head to finish merges the chunks in chunk order (deterministic).
-// Loads are 16-byte: four lanes share one 256-byte key row for the scores, and
-// sixteen lanes one value row for the output.
+// One decode token.  Workgroup (kv head g, key chunk c) takes at most kMaxKeys
+// keys: every K and V row of its chunk (16 lanes per 256-byte row, 16 rows per
+// workgroup step, so at most 8 rows of each per thread) is loaded at entry, before
+// the query, so the chunk costs one round trip to memory.  Scores: each lane dots
+// its 8 dimensions with the group's query heads and the 16 lanes of a row add
+// theirs up with DPP row operations; the chunk's softmax statistics (max, sum of
+// exponentials) per head come from LDS; the unnormalised partial output sums the
+// value rows held in registers, reduced over the 16 rows in LDS in row order.  The
+// last chunk of a kv head to finish merges the chunks in chunk order
+// (deterministic).
 constexpr int kAttThreads = 256;
 constexpr int kMaxGroup = 8;      // query heads per kv head
 constexpr int kAttHd = 128;       // head dimension of the vectorised path
-constexpr int kMaxChunks = 64;
+constexpr int kMaxChunks = 256;   // chunks per kv head
+constexpr int kMaxKeys = 128;     // keys per chunk: 8 row steps of 16
+constexpr int kSteps = kMaxKeys / 16;
 
-__device__ __forceinline__ void kv_row8(const uint16_t* cache, const float* fresh, bool from_cache, long off,
-                                        float v[8]) {
-  if (from_cache) {
-    unpack8<DT_BF16>(*reinterpret_cast<const u32x4*>(cache + off), v);
-  } else {
+// Sum over the 16 lanes of each row (every lane of the row gets the row's sum).
+__device__ __forceinline__ float row16_sum(float v) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = fresh[off + e];
-  }
+  for (int s = 0; s < 4; ++s) v += dppf(v, s);
+  return v;
 }
 
+template <int GM>
 __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams p) {
   extern __shared__ __align__(16) float sm[];
   constexpr int hd = kAttHd;
@@ -69,46 +73,76 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   const int g = blockIdx.x, c = blockIdx.y, C = gridDim.y;
   const int n_keys = p.n_ctx + 1;
   const int j0 = (int)((long)c * n_keys / C), j1 = (int)((long)(c + 1) * n_keys / C);
-  const int nk = j1 - j0;
-  float* qs = sm;                          // [grp][hd]  (pre-scaled)
-  float* sc = qs + grp * hd;               // [grp][nk]
-  float* red = sc + grp * ((nk + 3) & ~3); // [16][grp][hd] output partials per key group
+  const int nk = j1 - j0;                  // <= kMaxKeys (the host sizes C)
+  float* qs = sm;                          // [GM][hd] query heads of the group, pre-scaled
+  float* sc = qs + GM * hd;                // [GM][kMaxKeys] scores, then exp(score - max)
+  float* red = sc + GM * kMaxKeys;         // [16][GM][hd] per key-row partial outputs
   __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
   __shared__ float s_ml[kMaxChunks * kMaxGroup * 2];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float scale = 1.0f / sqrtf((float)hd);
-  for (int i = tid; i < grp * hd; i += kAttThreads) {
-    const int qh = g * grp + i / hd, dd = i % hd;
-    qs[i] = p.q[(long)qh * hd + dd] * scale;
+  const int ks = tid >> 4, l16 = tid & 15;   // key row slot 0..15, 8 dimensions 8 l16 ..
+  const int dd0 = 8 * l16;
+
+  // every K and V row of the chunk, issued together (rows past the chunk repeat its
+  // last row; the current token's own row is fp32 and taken apart below)
+  u32x4 kr[kSteps], vr[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    int jj = ks + 16 * s;
+    jj = jj < nk ? jj : nk - 1;
+    int j = j0 + jj;
+    j = j < p.n_ctx ? j : (p.n_ctx > 0 ? p.n_ctx - 1 : 0);
+    const long off = ((long)j * p.n_kv + g) * hd + dd0;
+    if (p.n_ctx > 0) {
+      kr[s] = *reinterpret_cast<const u32x4*>(p.k_cache + off);
+      vr[s] = *reinterpret_cast<const u32x4*>(p.v_cache + off);
+    } else {
+      kr[s] = u32x4{0u, 0u, 0u, 0u};
+      vr[s] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
+  const bool has_fresh = j1 == n_keys;     // this chunk holds the current token's key
+  float kf[8], vf[8];
+  if (has_fresh) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = p.k_new[(long)g * hd + dd0 + e];
+      vf[e] = p.v_new[(long)g * hd + dd0 + e];
+    }
+  }
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int i = tid; i < grp * hd; i += kAttThreads) qs[i] = p.q[(long)(g * grp) * hd + i] * scale;
   __syncthreads();
-  // scores: four lanes per key, 32 dimensions (four 16-byte loads) each
-  {
-    const int part = tid & 3, d0 = part * 32;
-    for (int jj = tid >> 2; jj < nk; jj += kAttThreads / 4) {
-      const int j = j0 + jj;
-      const bool fromc = j < p.n_ctx;
-      const long off = fromc ? ((long)j * p.n_kv + g) * hd + d0 : (long)g * hd + d0;
-      float acc[kMaxGroup];
+
+  // scores
 #pragma unroll
-      for (int a = 0; a < kMaxGroup; ++a) acc[a] = 0.f;
+  for (int s = 0; s < kSteps; ++s) {
+    const int jj = ks + 16 * s;
+    if (16 * s < nk) {                     // uniform over the workgroup
+      float kv[8];
+      if (has_fresh && j0 + jj == p.n_ctx) {
 #pragma unroll
-      for (int v8 = 0; v8 < 4; ++v8) {
-        float kv[8];
-        kv_row8(p.k_cache, p.k_new, fromc, off + v8 * 8, kv);
-#pragma unroll
-        for (int a = 0; a < kMaxGroup; ++a)
-          if (a < grp)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[a] = fmaf(qs[a * hd + d0 + v8 * 8 + e], kv[e], acc[a]);
+        for (int e = 0; e < 8; ++e) kv[e] = kf[e];
+      } else {
+        unpack8<DT_BF16>(kr[s], kv);
       }
 #pragma unroll
-      for (int a = 0; a < kMaxGroup; ++a) {
-        float v = acc[a];
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
-        if (part == 0 && a < grp) sc[a * nk + jj] = v;
+      for (int a = 0; a < GM; ++a) {
+        if (a < grp) {
+          const float4 q0 = *reinterpret_cast<const float4*>(qs + a * hd + dd0);
+          const float4 q1 = *reinterpret_cast<const float4*>(qs + a * hd + dd0 + 4);
+          float v = q0.x * kv[0];
+          v = fmaf(q0.y, kv[1], v);
+          v = fmaf(q0.z, kv[2], v);
+          v = fmaf(q0.w, kv[3], v);
+          v = fmaf(q1.x, kv[4], v);
+          v = fmaf(q1.y, kv[5], v);
+          v = fmaf(q1.z, kv[6], v);
+          v = fmaf(q1.w, kv[7], v);
+          v = row16_sum(v);
+          if (l16 == 0 && jj < nk) sc[a * kMaxKeys + jj] = v;
+        }
       }
     }
   }
@@ -116,52 +150,58 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   // chunk softmax statistics per query head (one wave per head)
   for (int a = wave; a < grp; a += kAttThreads / 64) {
     float m = -INFINITY;
-    for (int t = lane; t < nk; t += 64) m = fmaxf(m, sc[a * nk + t]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    for (int t = lane; t < nk; t += 64) m = fmaxf(m, sc[a * kMaxKeys + t]);
+    m = wave_max(m);
     float l = 0.f;
     for (int t = lane; t < nk; t += 64) {
-      const float e = expf(sc[a * nk + t] - m);
-      sc[a * nk + t] = e;
+      const float e = expf(sc[a * kMaxKeys + t] - m);
+      sc[a * kMaxKeys + t] = e;
       l += e;
     }
     l = wave_sum(l);
     if (lane == 0) { s_m[a] = m; s_l[a] = l; }
   }
   __syncthreads();
-  // unnormalised partial outputs: thread = (key group kg of 16, 8 dims dg of 16)
+  // unnormalised partial outputs of this thread's rows and 8 dimensions
   {
-    const int dg = tid & 15, kg = tid >> 4;
-    float acc[kMaxGroup][8];
+    float acc[GM][8];
 #pragma unroll
-    for (int a = 0; a < kMaxGroup; ++a)
+    for (int a = 0; a < GM; ++a)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
-    for (int jj = kg; jj < nk; jj += 16) {
-      const int j = j0 + jj;
-      const bool fromc = j < p.n_ctx;
-      const long off = fromc ? ((long)j * p.n_kv + g) * hd + dg * 8 : (long)g * hd + dg * 8;
-      float vv[8];
-      kv_row8(p.v_cache, p.v_new, fromc, off, vv);
 #pragma unroll
-      for (int a = 0; a < kMaxGroup; ++a)
-        if (a < grp) {
-          const float pa = sc[a * nk + jj];
+    for (int s = 0; s < kSteps; ++s) {
+      const int jj = ks + 16 * s;
+      if (jj < nk) {
+        float vv[8];
+        if (has_fresh && j0 + jj == p.n_ctx) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(pa, vv[e], acc[a][e]);
+          for (int e = 0; e < 8; ++e) vv[e] = vf[e];
+        } else {
+          unpack8<DT_BF16>(vr[s], vv);
         }
+#pragma unroll
+        for (int a = 0; a < GM; ++a)
+          if (a < grp) {
+            const float pa = sc[a * kMaxKeys + jj];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(pa, vv[e], acc[a][e]);
+          }
+      }
     }
 #pragma unroll
-    for (int a = 0; a < kMaxGroup; ++a)
-      if (a < grp)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[(kg * grp + a) * hd + dg * 8 + e] = acc[a][e];
+    for (int a = 0; a < GM; ++a)
+      if (a < grp) {
+        float4* dst = reinterpret_cast<float4*>(red + (ks * GM + a) * hd + dd0);
+        dst[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+        dst[1] = make_float4(acc[a][4], acc[a][5], acc[a][6], acc[a][7]);
+      }
   }
   __syncthreads();
   for (int i = tid; i < grp * hd; i += kAttThreads) {
     const int a = i / hd, dd = i % hd;
     float o = 0.f;
-    for (int kg = 0; kg < 16; ++kg) o += red[(kg * grp + a) * hd + dd];
+    for (int r = 0; r < 16; ++r) o += red[(r * GM + a) * hd + dd];
     const long base = ((long)g * C + c) * grp + a;          // partial record index
     store_coherent(p.part_o + base * hd + dd, o);
     if (dd == 0) {
@@ -183,7 +223,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   // the chunk statistics are waited for; the weights exp(m_c - M) and the sums L
   // depend on (chunk, head) only and are formed once in LDS.  Chunks are merged in
   // chunk order.
-  constexpr int kOut = kMaxGroup * kAttHd / kAttThreads;
+  constexpr int kOut = (GM * kAttHd + kAttThreads - 1) / kAttThreads;
   const int n_out = (grp * hd + kAttThreads - 1) / kAttThreads;      // in use (uniform)
   float ov[kOut][32];
   auto load_ov = [&](int c0) {
@@ -243,23 +283,31 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   }
 }
 
-hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s) {
-  const int grp = p.n_q / p.n_kv;
-  const int n_keys = p.n_ctx + 1;
-  const int max_chunk = (n_keys + chunks - 1) / chunks;
-  const size_t smem = size_t(grp) * kAttHd * 4 + size_t(grp) * ((max_chunk + 3) & ~3) * 4 +
-                      size_t(16) * grp * kAttHd * 4;
+template <int GM>
+hipError_t launch_attention_g(const AttnParams& p, int chunks, hipStream_t s) {
+  const size_t smem = (size_t(GM) * kAttHd + size_t(GM) * kMaxKeys + size_t(16) * GM * kAttHd) * 4;
+  auto k = attention_kernel<GM>;
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(smem));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attention_kernel, dim3(p.n_kv, chunks), dim3(kAttThreads), smem, s, p);
+  hipLaunchKernelGGL(k, dim3(p.n_kv, chunks), dim3(kAttThreads), smem, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s) {
+  const int grp = p.n_q / p.n_kv;
+  if (chunks < 1 || chunks > kMaxChunks || (p.n_ctx + 1 + chunks - 1) / chunks > kMaxKeys) return hipErrorInvalidValue;
+  if (grp <= 1) return launch_attention_g<1>(p, chunks, s);
+  if (grp <= 2) return launch_attention_g<2>(p, chunks, s);
+  if (grp <= 4) return launch_attention_g<4>(p, chunks, s);
+  return launch_attention_g<8>(p, chunks, s);
 }
 
 int attention_max_group() { return kMaxGroup; }
 int attention_head_dim() { return kAttHd; }
 int attention_max_chunks() { return kMaxChunks; }
+int attention_max_keys() { return kMaxKeys; }
 
 }  // namespace as

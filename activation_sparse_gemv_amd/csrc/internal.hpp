@@ -145,6 +145,7 @@ hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s);
 int attention_max_group();
 int attention_head_dim();
 int attention_max_chunks();
+int attention_max_keys();
 
 // GLASS local signal (see glass.hip).
 hipError_t launch_local_signal(const uint16_t* X, int P, int d, const uint16_t* W, long ld_neuron, long up_off,
