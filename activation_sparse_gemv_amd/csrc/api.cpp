@@ -10,6 +10,9 @@
 #include <string>
 
 #include "internal.hpp"
+#ifdef AS_PHASE_TIMELINE
+#include "../../include/actsparse_timeline.h"
+#endif
 
 using namespace as;
 
@@ -51,18 +54,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return na > 0 && nb > 0 && x < y + nb && y < x + na;
 }
 
-int num_cus() {
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-      cus = prop.multiProcessorCount;
-    else
-      cus = 256;
-  }
-  return cus;
-}
+int num_cus() { return device_cus(); }
 
 // Launch plan of one row-gather GEMV over at most `rows` rows and `cols` output
 // columns (paired gate/up: `cols` neurons, 2*cols columns).
@@ -205,6 +197,10 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     // tokens, IN_PARTS)
     const int hard = (kLdsBytes - kLdsReserve) / (4 + 8 * mt);
     int S = mp.p2.S;
+    // a whole number of workgroups per CU (two) where the tiles allow it: with 1.75
+    // per CU the CUs holding two workgroups set the finish (measured on MI355X for
+    // the 14336 -> 4096 down projection)
+    if ((2 * num_cus()) % mp.p2.n_tiles == 0) S = 2 * num_cus() / mp.p2.n_tiles;
     if (S > units / 2) S = units / 2 > 1 ? units / 2 : 1;      // ranges of at least 128 rows
     while (S < units && ((units + S - 1) / S) * 64 > hard) ++S;
     mp.s2_range = S;
@@ -445,6 +441,18 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
                           unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream,
                           const GemvFuse* fz);
 
+#ifdef AS_PHASE_TIMELINE
+static std::atomic<unsigned long long*> g_phase_buf{nullptr};
+static std::atomic<size_t> g_phase_words{0};
+
+as_status as_phase_timeline_arm(uint64_t* buf, size_t words) {
+  if (buf == nullptr || words < 32) return fail(AS_ERR_INVALID_ARG, "as_phase_timeline_arm: NULL buffer or < 32 words");
+  g_phase_words.store(words);
+  g_phase_buf.store(reinterpret_cast<unsigned long long*>(buf));
+  return AS_OK;
+}
+#endif
+
 as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp_weights* w, as_mlp_mode mode,
                                float t_x, float t_h, const int32_t* neuron_idx, int n_active, void* Y,
                                as_dtype y_dt, unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes,
@@ -483,6 +491,12 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   if (dbg && mode == AS_MLP_NEURON_SET && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz || dbg->h_mask.bits))
     return fail(AS_ERR_UNSUPPORTED, "%s: mask exports exist in THRESHOLD mode only", fn);
 
+#ifdef AS_PHASE_TIMELINE
+  // an armed timeline buffer is taken by this call (first half: gate/up launch,
+  // second half: down launch)
+  unsigned long long* tl_buf = g_phase_buf.exchange(nullptr);
+  const size_t tl_half = g_phase_words.load() / 2;
+#endif
   const MlpPlan mp = plan_mlp(M, w, mode, dense);
   if ((long)mp.p1.S * M * 2L * w->d_ff >= (1L << 31) || (long)mp.parts2 * M * w->d_model >= (1L << 31))
     return fail(AS_ERR_UNSUPPORTED, "%s: split-K partials exceed 2^31 elements", fn);
@@ -549,6 +563,9 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
     if (gu_range) p.cap = mp.cap1_range;
     // the down stage adds into Y: the gate/up launch clears it (Y does not alias X)
     if (clear_y) { p.zero_y = reinterpret_cast<float*>(Y); p.zero_n = long(M) * d; }
+#ifdef AS_PHASE_TIMELINE
+    if (tl_buf != nullptr && (size_t)p.n_tiles * p.S * 16 <= tl_half) p.phase_tl = tl_buf;
+#endif
     if ((st = hip_check(launch_gather_gemv(c1, p, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
     // stage 2: down projection over the surviving h rows; each slice masks its
@@ -593,6 +610,9 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   p2.y = Y; p2.y_dt = int(y_dt); p2.ldy = d; p2.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   p2.atomic_y = atomic ? 1 : 0;
   if (fz != nullptr) { p2.res = fz->res; p2.res_dt = fz->res_dt; p2.ldres = d; }
+#ifdef AS_PHASE_TIMELINE
+  if (tl_buf != nullptr && (size_t)p2.n_tiles * p2.S * 16 <= tl_half) p2.phase_tl = tl_buf + tl_half;
+#endif
   if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;
   return rec(2);
 }

@@ -293,16 +293,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sm, int* total) {
   int inc = wave_incl_scan(v);
   if (l == 63) sm[w] = inc;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < NW; ++i) { int c = sm[i]; sm[i] = run; run += c; }
-    sm[NW] = run;
+  // every wave adds up the wave totals itself (no serial step by one thread)
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int c = sm[i];
+    base += i < w ? c : 0;
+    tot += c;
   }
-  __syncthreads();
-  int r = sm[w] + inc - v;
-  *total = sm[NW];
-  __syncthreads();
-  return r;
+  *total = tot;
+  __syncthreads();   // sm may be reused as soon as this returns
+  return base + inc - v;
 }
 
 }  // namespace as

@@ -7,6 +7,17 @@ namespace as {
 
 constexpr int kThreadsHost = 256;
 
+int device_cus() {
+  static const int cus = [] {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      return prop.multiProcessorCount;
+    return 256;
+  }();
+  return cus;
+}
+
 size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
   auto a16 = [](size_t b) { return (b + 15) & ~size_t(15); };
   const int nslot = 4 * (64 / c.lpr), tn = c.lpr * 8;

@@ -21,6 +21,7 @@
 //     (atomic_y) a y-storing launch skips that combine instead: every slice adds
 //     its tile into an fp32 y with atomic adds, in no fixed order.
 #pragma once
+#include <atomic>
 #include "common.hpp"
 #include "internal.hpp"
 #include "topk.hpp"
@@ -32,6 +33,31 @@ constexpr int kThreads = 256;
 // has room for sixteen (the loop is bound by loads in flight per CU: measured on
 // the 4096 x 2 x 14336 gather, 8 rows per lane left it ~15% below the rate that
 // 16 rows reach); several tokens keep eight (their accumulators take the room).
+// Phase timeline, compiled into libactsparse_timeline.so only (AS_PHASE_TIMELINE):
+// thread 0 of each workgroup writes the device's 100 MHz constant clock into slot
+// `slot` of its 16 words at phase boundaries.  Slots: 0 entry, 1 prologue done,
+// 2 main loop done (thread 0's wave), 3 slot reduction done, 4 partial tile stored
+// and complete, 5 tile counter returned, 6 output written (last workgroup of a
+// tile), 7 rows gathered (a count, not a time), 8 input of the prologue arrived, 9
+// prologue scan (IN_THRESH) or SwiGLU staging (IN_PARTS) done, 10 h exports done.
+#ifdef AS_PHASE_TIMELINE
+#define AS_PHASE(p, slot)                                                                    \
+  do {                                                                                       \
+    if ((p).phase_tl != nullptr && threadIdx.x == 0)                                         \
+      (p).phase_tl[(long)blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime();       \
+  } while (0)
+#define AS_PHASE_VAL(p, slot, v)                                                             \
+  do {                                                                                       \
+    if ((p).phase_tl != nullptr && threadIdx.x == 0) (p).phase_tl[(long)blockIdx.x * 16 + (slot)] = (v); \
+  } while (0)
+// orders a stamp after the arrival of `v` (the empty asm reads its register)
+#define AS_PHASE_AFTER(v) asm volatile("" ::"v"(v))
+#else
+#define AS_PHASE(p, slot) do {} while (0)
+#define AS_PHASE_VAL(p, slot, v) do {} while (0)
+#define AS_PHASE_AFTER(v) do {} while (0)
+#endif
+
 template <int MT>
 struct Unroll {
   static constexpr int value = MT == 1 ? 16 : 8;
@@ -341,6 +367,8 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
 #pragma unroll
     for (int e = 0; e < CEV; ++e) ubits |= (uint64_t)(e < n && (keep_all || fabsf(v0[e]) > t)) << e;
     c = __popcll(ubits);
+    AS_PHASE_AFTER(c);
+    AS_PHASE(p, 8);
   } else if constexpr (NV > 0) {
     if (n == CEV && p.x_dt != DT_F32) {
       // the chunks of up to 8 tokens are loaded before any is used
@@ -429,6 +457,7 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
   }
   int nnz;
   const int off = block_excl_scan<kThreads>(c, s_scan, &nnz);
+  AS_PHASE(p, 9);
   const int lo = split ? split_point(sl, nnz, S) : 0;
   const int hi = split ? split_point(sl + 1, nnz, S) : nnz;
   *lo_out = lo;
@@ -476,38 +505,52 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
 }
 
 // Compaction of a range [i0, i0 + L) whose values sit in LDS (stage: [MT][L]
-// fp32): each thread takes a contiguous chunk for the union mask over tokens
-// (|v| > t for any token, or every row with keep_all), a workgroup scan places the
-// chunks, and the kept rows' values are copied (a token's value is 0 where its own
-// |v| <= t).  Returns the number of kept rows; synchronises before returning.
+// fp32).  The range is cut into units of 64 rows and wave w takes a contiguous run
+// of units, lane l row l of each unit: the union mask over tokens (|v| > t for any
+// token, or every row with keep_all) is a ballot per unit, so a wave counts its
+// kept rows without a loop over bits; one barrier exchanges the four wave totals,
+// then each wave writes its kept rows in ascending order (a token's value is 0
+// where its own |v| <= t).  Returns the number of kept rows; synchronises before
+// returning.
 template <int MT>
 __device__ __forceinline__ int compact_stage(const float* stage, int L, int i0, float t, bool keep_all, int* s_idx,
                                              float* s_val, int cap, int* s_scan) {
-  const int tid = threadIdx.x;
-  const int CE = (L + kThreads - 1) / kThreads;
-  const int c0 = min(tid * CE, L), n = max(0, min(CE, L - c0));
-  int c = 0;
-  for (int e = 0; e < n; ++e) {
+  constexpr int NW = kThreads / 64;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int units = (L + 63) / 64;
+  const int u0 = split_point(w, units, NW), u1 = split_point(w + 1, units, NW);
+  auto keep = [&](int e) {
+    if (e >= L) return false;
     bool a = keep_all;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
-    c += a;
+    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + e]) > t;
+    return a;
+  };
+  int cnt = 0;
+  for (int u = u0; u < u1; ++u) cnt += __popcll(__ballot(keep(u * 64 + lane)));
+  if (lane == 0) s_scan[w] = cnt;
+  __syncthreads();
+  int r = 0, nnz = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    const int c = s_scan[k];
+    r += k < w ? c : 0;
+    nnz += c;
   }
-  int nnz;
-  int r = block_excl_scan<kThreads>(c, s_scan, &nnz);
-  for (int e = 0; e < n; ++e) {
-    bool a = keep_all;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) a |= fabsf(stage[m * L + c0 + e]) > t;
+  for (int u = u0; u < u1; ++u) {
+    const int e = u * 64 + lane;
+    const bool a = keep(e);
+    const uint64_t bits = __ballot(a);
     if (a) {
-      s_idx[r] = i0 + c0 + e;
+      const int pos = r + lanes_below(bits);
+      s_idx[pos] = i0 + e;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const float xv = stage[m * L + c0 + e];
-        s_val[m * cap + r] = (keep_all || fabsf(xv) > t) ? xv : 0.f;
+        const float xv = stage[m * L + e];
+        s_val[m * cap + pos] = (keep_all || fabsf(xv) > t) ? xv : 0.f;
       }
-      ++r;
     }
+    r += __popcll(bits);
   }
   __syncthreads();
   return nnz;
@@ -619,15 +662,87 @@ __device__ __forceinline__ int compact_range_staged(const GemvParams& p, int i0,
   return compact_stage<MT>(stage, L, i0, t, false, s_idx, s_val, cap, s_scan);
 }
 
+// Sum of the gate and up partials of four consecutive rows (offset `off` of slice
+// 0) over the S1 gate/up slices, in slice order from 0: batches of up to kB slices
+// are loaded together (one round trip per batch).
+__device__ __forceinline__ void sum_parts4(const float* P, int off, int S1, int slice_ld, int up, f32x4_t& g,
+                                           f32x4_t& u) {
+  constexpr int kB = 8;
+  g = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S1; s0 += kB) {
+    f32x4_t tg[kB], tu[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      // the slice count is uniform: a batch past the last slice issues no loads
+      if (s0 + k < S1) {
+        const float* ps = P + (s0 + k) * slice_ld + off;
+        tg[k] = *reinterpret_cast<const f32x4_t*>(ps);
+        tu[k] = *reinterpret_cast<const f32x4_t*>(ps + up);
+      } else {
+        tg[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        tu[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (s0 + k < S1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g[e] += tg[k][e];
+          u[e] += tu[k][e];
+        }
+      }
+  }
+}
+
+// One token, a range of at most 4 * kThreads rows, no h exports: thread j owns rows
+// 4j..4j+3 and keeps their h values in registers; a workgroup scan of the per-thread
+// kept counts places the rows, which go from registers straight to the row list (no
+// LDS staging, no second pass).  The same rows, order and values as the staged path.
+__device__ __forceinline__ int compact_parts_regs(const GemvParams& p, int i0, int L, int* s_idx, float* s_val,
+                                                  int* s_scan) {
+  const int tid = threadIdx.x;
+  const int nq = L / 4;
+  const bool live = tid < nq;
+  f32x4_t h = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    f32x4_t g, u;
+    sum_parts4(reinterpret_cast<const float*>(p.x), i0 + 4 * tid, p.x_parts, (int)p.ldx, (int)p.x_up, g, u);
+    AS_PHASE_AFTER(g[0]);
+    AS_PHASE_AFTER(u[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = silu_f32(g[e]) * u[e];
+  }
+  AS_PHASE(p, 8);
+  const bool keep_all = p.keep_all != 0;
+  unsigned kb = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) kb |= (unsigned)(live && (keep_all || fabsf(h[e]) > p.t)) << e;
+  AS_PHASE(p, 9);
+  AS_PHASE(p, 10);
+  int nnz;
+  int r = block_excl_scan<kThreads>(__popc(kb), s_scan, &nnz);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if ((kb >> e) & 1u) {
+      s_idx[r] = i0 + 4 * tid + e;
+      s_val[r] = h[e];
+      ++r;
+    }
+  __syncthreads();
+  return nnz;
+}
+
 // The input of a down projection is h = silu(g) * u of a paired gate/up launch
 // that stored its split-K partials without summing them (OUT_PARTS).  Slice sl
 // owns the 64-aligned range [i0, i1) of h: for each token and each group of four
-// rows, the gate and up partials of every gate/up slice are loaded together (up
-// to 8 slices per round trip, 16-byte vectors) and summed in slice order starting
-// from 0, which is exactly the sum the gate/up launch's own combine would form;
-// h goes to the stage ([MT][L] fp32), then the range is masked and compacted.
-// With `exports`, h and its mask bits are also written out (one workgroup per
-// range does this).
+// rows, the gate and up partials of every gate/up slice are summed in slice order
+// starting from 0 (sum_parts4), which is exactly the sum the gate/up launch's own
+// combine would form; h goes to the stage ([MT][L] fp32), then the range is masked
+// and compacted.  With `exports`, h and its mask bits are also written out (one
+// workgroup per range does this).  One token without exports takes the register
+// path above.
 template <int MT>
 __device__ __forceinline__ int compact_parts(const GemvParams& p, int i0, int i1, int* s_idx, float* s_val, int cap,
                                              float* stage, int* s_scan, bool exports) {
@@ -635,33 +750,22 @@ __device__ __forceinline__ int compact_parts(const GemvParams& p, int i0, int i1
   const float t = p.t;
   const int L = max(0, i1 - i0);            // a multiple of 64 (K is)
   const int nq = L / 4;                     // groups of four rows per token
+  const bool exporting = exports && (p.h != nullptr || p.h_bits != nullptr || p.h_nnz != nullptr);
+  if constexpr (MT == 1) {
+    if (!exporting && nq <= kThreads) return compact_parts_regs(p, i0, L, s_idx, s_val, s_scan);
+  }
   const int tot = nq * MT;
-  const int S1 = p.x_parts;
   const float* P = reinterpret_cast<const float*>(p.x);
   // 32-bit offsets: the partials buffer holds fewer than 2^31 floats
   const int tok_ld = (int)p.ldx, slice_ld = M * tok_ld, up = (int)p.x_up;
-  constexpr int kB = 8;
   for (int j = tid; j < tot; j += kThreads) {
     const int m = j / nq, q = j % nq;
-    const int off = (m < M ? m : M - 1) * tok_ld + i0 + 4 * q;
-    f32x4_t g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S1; s0 += kB) {
-      f32x4_t tg[kB], tu[kB];
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const float* ps = P + min(s0 + k, S1 - 1) * slice_ld + off;
-        tg[k] = *reinterpret_cast<const f32x4_t*>(ps);
-        tu[k] = *reinterpret_cast<const f32x4_t*>(ps + up);
-      }
-#pragma unroll
-      for (int k = 0; k < kB; ++k)
-        if (s0 + k < S1) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            g[e] += tg[k][e];
-            u[e] += tu[k][e];
-          }
-        }
+    f32x4_t g, u;
+    sum_parts4(P, (m < M ? m : M - 1) * tok_ld + i0 + 4 * q, p.x_parts, slice_ld, up, g, u);
+    if (j == tid) {
+      AS_PHASE_AFTER(g[0]);
+      AS_PHASE_AFTER(u[3]);
+      AS_PHASE(p, 8);
     }
     f32x4_t h;
 #pragma unroll
@@ -669,7 +773,8 @@ __device__ __forceinline__ int compact_parts(const GemvParams& p, int i0, int i1
     *reinterpret_cast<f32x4_t*>(stage + m * L + 4 * q) = h;
   }
   __syncthreads();
-  if (exports) {
+  AS_PHASE(p, 9);
+  if (exporting) {
     if (p.h != nullptr)
       for (int j = tid; j < M * L; j += kThreads) p.h[(j / L) * p.ldh + i0 + j % L] = stage[j];
     if (p.h_bits != nullptr || p.h_nnz != nullptr) {
@@ -685,6 +790,7 @@ __device__ __forceinline__ int compact_parts(const GemvParams& p, int i0, int i1
       }
     }
   }
+  AS_PHASE(p, 10);
   return compact_stage<MT>(stage, L, i0, t, p.keep_all != 0, s_idx, s_val, cap, s_scan);
 }
 
@@ -719,6 +825,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
   const int tid = threadIdx.x;
   const int S = p.S;
   const int M = p.M;
+  AS_PHASE(p, 0);
 
   // ------------------------------------------------------------ prologue
   int cnt = 0;
@@ -792,6 +899,8 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     }
   }
   __syncthreads();
+  AS_PHASE(p, 1);
+  AS_PHASE_VAL(p, 7, (unsigned long long)cnt);
 
   constexpr int CPT = (TN + kThreads - 1) / kThreads;   // tile columns per thread
   float res[MT][CPT];
@@ -855,6 +964,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     }
   }
 
+  AS_PHASE(p, 2);
   // ------------------------------------------------------------ slot reduction
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -875,6 +985,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
 
   }
 
+  AS_PHASE(p, 3);
   // tile-local column c -> (validity, partial/output column)
   auto col_of = [&](int c, bool& ok) -> long {
     if constexpr (GU) {
@@ -904,6 +1015,10 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     // one workgroup clears the y that the next launch adds into
     if (p.zero_y != nullptr && tile == 0 && part == 0)
       for (long i = tid; i < p.zero_n; i += kThreads) p.zero_y[i] = 0.f;
+#ifdef AS_PHASE_TIMELINE
+    if (p.phase_tl != nullptr && tid == 0) wait_vmem();
+#endif
+    AS_PHASE(p, 4);
     return;
   }
 
@@ -946,12 +1061,14 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     }
     wait_vmem();
     __syncthreads();
+    AS_PHASE(p, 4);
     if (tid == 0) {
       const unsigned prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       s_flag = (prev == unsigned(n_parts - 1));
     }
     __syncthreads();
+    AS_PHASE(p, 5);
     if (!s_flag) return;
     if (tid == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // Batches of slices are loaded together for every token (one round trip per
@@ -1020,6 +1137,10 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
             store_elem(p.y, p.y_dt, m * p.ldy + gc, v);
           }
     }
+#ifdef AS_PHASE_TIMELINE
+    if (p.phase_tl != nullptr && tid == 0) wait_vmem();
+#endif
+    AS_PHASE(p, 6);
   } else if constexpr (OUT == OUT_ROUTER) {
     // the logits of every token (the grid has this one column tile): stored, staged
     // in LDS, and each token routed by one wave
@@ -1109,9 +1230,16 @@ template <int WDT, int MT, int LPR, int IN, int OUT, bool GU, bool NT, int NV>
 hipError_t launch_one(const GemvParams& p, size_t smem, hipStream_t s) {
   auto k = gather_gemv_kernel<WDT, MT, LPR, IN, OUT, GU, NT, NV>;
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-    if (e != hipSuccess) return e;
+    // raised per instantiation only when a launch asks for more than before
+    static std::atomic<size_t> allowed{64 * 1024};
+    if (smem > allowed.load(std::memory_order_acquire)) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+      if (e != hipSuccess) return e;
+      size_t cur = allowed.load(std::memory_order_relaxed);
+      while (cur < smem && !allowed.compare_exchange_weak(cur, smem, std::memory_order_acq_rel)) {
+      }
+    }
   }
   hipLaunchKernelGGL(k, dim3(p.n_tiles * p.S), dim3(kThreads), smem, s, p);
   return hipGetLastError();

@@ -63,6 +63,8 @@ struct GemvParams {
   // OUT_ROUTER (one column tile holding all N logits): y = logits, then per token
   // the top route_top experts and their softmax weights
   int route_top; int* route_ids; float* route_wts;
+  // phase timeline (libactsparse_timeline.so only): 16 words per workgroup
+  unsigned long long* phase_tl;
 };
 
 struct GemvConfig {
@@ -77,6 +79,8 @@ struct GemvConfig {
 };
 
 size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt);
+// Compute units of the current device (read once per process).
+int device_cus();
 
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s);
 int pick_chunk_vectors(const void* x, int x_dt, int K, long ldx);

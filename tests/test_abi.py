@@ -247,3 +247,18 @@ def test_moe_layer_limits_and_validation(lib):
     assert call(flags=L.AS_FLAG_NO_NT_LOADS) == L.AS_ERR_UNSUPPORTED
     assert call(logits=None) == L.AS_ERR_INVALID_ARG
     assert call(ws_bytes=nb - 1) == L.AS_ERR_WORKSPACE
+
+
+def test_phase_timeline_only_in_the_opt_in_build(lib):
+    """The phase-timeline entry point (include/actsparse_timeline.h) exists only in
+    libactsparse_timeline.so; the product library's kernels carry no timeline code.
+    The opt-in build, when present, rejects a NULL or too-small buffer."""
+    assert not hasattr(lib, "as_phase_timeline_arm")
+    tl_path = os.path.join(ROOT, "activation_sparse_gemv_amd", "libactsparse_timeline.so")
+    if not os.path.exists(tl_path):
+        pytest.skip("libactsparse_timeline.so not built (python -m activation_sparse_gemv_amd.build --timeline)")
+    tl = ctypes.CDLL(tl_path)
+    tl.as_phase_timeline_arm.restype = ctypes.c_int
+    tl.as_phase_timeline_arm.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    assert tl.as_phase_timeline_arm(None, 1024) == L.AS_ERR_INVALID_ARG
+    assert tl.as_phase_timeline_arm(ctypes.c_void_p(16), 8) == L.AS_ERR_INVALID_ARG
