@@ -39,7 +39,9 @@ constexpr int kThreads = 256;
 // 2 main loop done (thread 0's wave), 3 slot reduction done, 4 partial tile stored
 // and complete, 5 tile counter returned, 6 output written (last workgroup of a
 // tile), 7 rows gathered (a count, not a time), 8 input of the prologue arrived, 9
-// prologue scan (IN_THRESH) or SwiGLU staging (IN_PARTS) done, 10 h exports done.
+// prologue scan (IN_THRESH) or SwiGLU staging (IN_PARTS) done, 10 h exports done,
+// 11 split points (IN_THRESH), 12 row list written by thread 0's wave, 13 barrier
+// after the row list passed.
 #ifdef AS_PHASE_TIMELINE
 #define AS_PHASE(p, slot)                                                                    \
   do {                                                                                       \
@@ -461,18 +463,23 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
   const int lo = split ? split_point(sl, nnz, S) : 0;
   const int hi = split ? split_point(sl + 1, nnz, S) : nnz;
   *lo_out = lo;
+  AS_PHASE_AFTER(hi);
+  AS_PHASE(p, 11);
   if (off < hi && off + c > lo) {
     if constexpr (NV > 0) {
-      int r = off - lo;
+      // each kept input's place is its rank among the thread's kept inputs (a
+      // popcount of the lower bits), so the writes carry no chain of dependent adds
+      const int base = off - lo;
       const unsigned span = (unsigned)(hi - lo);
 #pragma unroll
       for (int e = 0; e < CEV; ++e) {
-        const bool k = (ubits >> e) & 1;
-        if (k && (unsigned)r < span) {
+        int r;
+        if constexpr (CEV <= 32) r = base + __popc((uint32_t)ubits & ((1u << e) - 1u));
+        else r = base + __popcll(ubits & ((uint64_t(1) << e) - 1u));
+        if (((ubits >> e) & 1u) && (unsigned)r < span) {
           s_idx[r] = c0 + e;
           if constexpr (MT == 1) s_val[r] = v0[e];
         }
-        r += k;
       }
     } else {
       int r = off;
@@ -492,7 +499,9 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
       }
     }
   }
+  AS_PHASE(p, 12);
   __syncthreads();
+  AS_PHASE(p, 13);
   const int cnt = hi - lo;
   if constexpr (MT == 1) return cnt;
   for (int r = tid; r < cnt; r += kThreads) {

@@ -32,7 +32,10 @@ GU_PHASES = [
     ("start after the first workgroup", lambda g, t0: g[:, 0] - t0),
     ("x arrived (load of the whole input)", lambda g, t0: g[:, 8] - g[:, 0]),
     ("mask scan over the input", lambda g, t0: g[:, 9] - g[:, 8]),
-    ("row list written to LDS", lambda g, t0: g[:, 1] - g[:, 9]),
+    ("split points of the list", lambda g, t0: g[:, 11] - g[:, 9]),
+    ("row list written (thread 0's wave)", lambda g, t0: g[:, 12] - g[:, 11]),
+    ("barrier after the list", lambda g, t0: g[:, 13] - g[:, 12]),
+    ("second barrier (prologue end)", lambda g, t0: g[:, 1] - g[:, 13]),
     ("main loop (row gather)", lambda g, t0: g[:, 2] - g[:, 1]),
     ("slot reduction", lambda g, t0: g[:, 3] - g[:, 2]),
     ("partial tile stored", lambda g, t0: g[:, 4] - g[:, 3]),
@@ -153,7 +156,7 @@ def main(argv=None):
             c = asg.prepare_sparse_swiglu_mlp(toks[5 + rep], layers[(3 + rep) % 8], tx, th, Y)
             for c2 in calls[:8]:
                 c2()
-            torch.cuda.synchronize()
+            # arming is host-side: the armed call queues behind the eight in flight
             L.check(lib.as_phase_timeline_arm(ctypes.c_void_p(buf.data_ptr()), words), "as_phase_timeline_arm")
             c()
             torch.cuda.synchronize()

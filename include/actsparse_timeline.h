@@ -34,7 +34,9 @@ extern "C" {
  *     3 slot reduction done; 4 partial tile stored and complete; 5 tile counter
  *     returned; 6 output written (last workgroup of a column tile);
  *     7 rows gathered (a count); 8 prologue input arrived; 9 prologue scan done
- *     (gate/up) or SwiGLU staged (down); 10 h exports done (down).
+ *     (gate/up) or SwiGLU staged (down); 10 h exports done (down); 11 split
+ *     points of the row list (gate/up); 12 row list written by thread 0's wave;
+ *     13 barrier after the row list passed (gate/up).
  * Returns AS_ERR_INVALID_ARG for a NULL buffer or words < 32.  The buffer is owned
  * by the caller and must stay valid until the armed call's launches complete. */
 as_status as_phase_timeline_arm(uint64_t* buf, size_t words);
