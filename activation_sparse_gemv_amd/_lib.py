@@ -18,7 +18,7 @@ AS_FLAG_ATOMIC_SPLITK = 1 << 1
 AS_FLAG_NO_NT_LOADS = 1 << 2
 AS_FLAG_FORCE_DENSE = 1 << 3
 AS_FLAG_NO_FUSION = 1 << 4
-AS_MLP_THRESHOLD, AS_MLP_NEURON_SET = 0, 1
+AS_MLP_THRESHOLD, AS_MLP_NEURON_SET, AS_MLP_GATE_SCORE = 0, 1, 2
 AS_TOPK_VALUE, AS_TOPK_RANK_BLEND = 0, 1
 
 
@@ -56,7 +56,8 @@ class ASBlockDebug(ctypes.Structure):
 
 
 class ASMlpDebug(ctypes.Structure):
-    _fields_ = [("h", c_void_p), ("x_mask", ASMaskOut), ("h_mask", ASMaskOut), ("ev", c_void_p * 3)]
+    _fields_ = [("h", c_void_p), ("x_mask", ASMaskOut), ("h_mask", ASMaskOut), ("ev", c_void_p * 3),
+                ("a", c_void_p)]
 
 
 # name -> (restype, argtypes); every symbol declared in include/actsparse.h

@@ -134,7 +134,8 @@ def as_dense_gemv(X: torch.Tensor, W: torch.Tensor, y_dtype=torch.float32, flags
 @dataclass
 class MLPWeights:
     """THRESHOLD: w_gate_up [d_model, 2, d_ff], w_down [d_ff, d_model].
-    NEURON_SET: w_gate_up [d_ff, 3, d_model] (gate, up, down rows per neuron), w_down None."""
+    NEURON_SET and GATE_SCORE: w_gate_up [d_ff, 3, d_model] (gate, up, down rows per
+    neuron), w_down None."""
     w_gate_up: torch.Tensor
     w_down: Optional[torch.Tensor]
     mode: int = L.AS_MLP_THRESHOLD
@@ -155,8 +156,9 @@ class MLPWeights:
 def as_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float = float("-inf"), t_h: float = float("-inf"),
                          neuron_idx: torch.Tensor | None = None, y_dtype=torch.float32, flags: int = 0,
                          debug: bool = False, events=None, Y: torch.Tensor | None = None):
-    """Sparse SwiGLU MLP (THRESHOLD or NEURON_SET per ``w.mode``).  With ``debug``
-    returns (Y, dict(h=..., x_mask=..., h_mask=...))."""
+    """Sparse SwiGLU MLP (THRESHOLD, NEURON_SET or GATE_SCORE per ``w.mode``; in
+    GATE_SCORE ``t_h`` is the threshold on |silu(g)|).  With ``debug`` returns
+    (Y, dict(h=..., x_mask=..., h_mask=..., a=...)) as the mode exports them."""
     squeeze = X.dim() == 1
     X2 = X.reshape(1, -1) if squeeze else X
     _need_cuda(X2, w.w_gate_up, w.w_down, neuron_idx, Y)
@@ -177,7 +179,7 @@ def as_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float = float("-in
         dbg = L.ASMlpDebug()
         if debug:
             dense = bool(flags & L.AS_FLAG_FORCE_DENSE)
-            nh = f if (w.mode == L.AS_MLP_THRESHOLD) else (f if dense else n_active)
+            nh = f if (w.mode != L.AS_MLP_NEURON_SET) else (f if dense else n_active)
             dd = dict(h=torch.zeros((M, max(nh, 1)), dtype=torch.float32, device=X.device))
             dbg.h = _ptr(dd["h"])
             if w.mode == L.AS_MLP_THRESHOLD:
@@ -186,6 +188,13 @@ def as_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float = float("-in
                                     nnz=torch.zeros(M, dtype=torch.int32, device=X.device))
                 dbg.x_mask = _mask_struct(dd["x_mask"])
                 dbg.h_mask = _mask_struct(dd["h_mask"])
+            elif w.mode == L.AS_MLP_GATE_SCORE:
+                dd["a"] = torch.zeros((M, f), dtype=torch.float32, device=X.device)
+                dbg.a = _ptr(dd["a"])
+                if not dense:
+                    dd["h_mask"] = dict(bits=torch.zeros((M, (f + 63) // 64), dtype=torch.int64, device=X.device),
+                                        nnz=torch.zeros(M, dtype=torch.int32, device=X.device))
+                    dbg.h_mask = _mask_struct(dd["h_mask"])
         if events is not None:
             for i, e in enumerate(events):
                 dbg.ev[i] = e.ev if e is not None else None

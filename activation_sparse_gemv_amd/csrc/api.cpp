@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <atomic>
 #include <string>
 
@@ -159,6 +160,10 @@ struct MlpPlan {
   int cap1_range;            // gate/up stage masking x by range (several tokens): max range length
 };
 
+// Gate-score mode: neurons per workgroup of the scoring launch (four waves, four
+// neurons each: small workgroups that the hardware refills as they finish).
+constexpr int kGateScoreNpb = 16;
+
 MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
   MlpPlan mp;
   if (mode == AS_MLP_THRESHOLD) {
@@ -177,6 +182,11 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     }
     mp.n_lt = mp.p1.n_tiles;
     mp.lt_stride = mp.p1.lpr * 4;   // tile neurons = tile columns / 2
+  } else if (mode == AS_MLP_GATE_SCORE) {
+    // one list tile per gate-score workgroup of kGateScoreNpb neurons
+    mp.p1 = Plan{0, 0, 1, 0};
+    mp.n_lt = gate_score_grid(w->d_ff, kGateScoreNpb);
+    mp.lt_stride = kGateScoreNpb;
   } else {
     mp.p1 = Plan{0, 0, 1, 0};
     mp.n_lt = 1;
@@ -220,8 +230,9 @@ MlpWs carve_mlp(Carver& c, const MlpPlan& mp, int M, const as_mlp_weights* w, as
   ws.g2 = carve_gemv(c, p2, M, w->d_model);
   ws.h = c.take<float>(size_t(M) * w->d_ff);
   ws.l_cnt = c.take<int>(mp.n_lt);
-  ws.l_idx = c.take<int>(w->d_ff);
-  ws.l_val = c.take<float>(size_t(w->d_ff) * M);
+  const size_t list_len = std::max(size_t(w->d_ff), size_t(mp.n_lt) * mp.lt_stride);
+  ws.l_idx = c.take<int>(list_len);
+  ws.l_val = c.take<float>(list_len * M);
   return ws;
 }
 
@@ -422,6 +433,8 @@ static as_status check_mlp_weights(const as_mlp_weights* w, as_mlp_mode mode, co
   if (mode == AS_MLP_THRESHOLD) {
     if (!w->w_down) return fail(AS_ERR_INVALID_ARG, "%s: w_down is NULL", fn);
     if (!aligned16(w->w_down)) return fail(AS_ERR_INVALID_ARG, "%s: w_down not 16-byte aligned", fn);
+  } else if (mode == AS_MLP_GATE_SCORE) {
+    if (w->d_model > 8192) return fail(AS_ERR_UNSUPPORTED, "%s: GATE_SCORE needs d_model <= 8192", fn);
   } else if (mode != AS_MLP_NEURON_SET) {
     return fail(AS_ERR_INVALID_ARG, "%s: bad mode %d", fn, int(mode));
   }
@@ -489,7 +502,15 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   if (dbg && dbg->h_mask.idx) return fail(AS_ERR_UNSUPPORTED, "%s: the h mask exports bits and nnz only", fn);
   if (dbg && dbg->x_mask.idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: x mask idx export needs M == 1", fn);
   if (dbg && mode == AS_MLP_NEURON_SET && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz || dbg->h_mask.bits))
-    return fail(AS_ERR_UNSUPPORTED, "%s: mask exports exist in THRESHOLD mode only", fn);
+    return fail(AS_ERR_UNSUPPORTED, "%s: NEURON_SET exports no masks", fn);
+  if (mode == AS_MLP_GATE_SCORE) {
+    if (M > 8) return fail(AS_ERR_UNSUPPORTED, "%s: GATE_SCORE takes at most 8 tokens", fn);
+    if (!(t_x == -INFINITY)) return fail(AS_ERR_UNSUPPORTED, "%s: GATE_SCORE does not threshold X (t_x must be -inf)", fn);
+    if (dbg && (dbg->x_mask.bits || dbg->x_mask.idx || dbg->x_mask.nnz))
+      return fail(AS_ERR_UNSUPPORTED, "%s: GATE_SCORE has no input mask", fn);
+  }
+  if (dbg && mode != AS_MLP_GATE_SCORE && dbg->a)
+    return fail(AS_ERR_UNSUPPORTED, "%s: the gate activation export exists in GATE_SCORE mode only", fn);
 
 #ifdef AS_PHASE_TIMELINE
   // an armed timeline buffer is taken by this call (first half: gate/up launch,
@@ -584,6 +605,29 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
       c2.in = IN_RANGE;
       p2.x = hbuf; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = t_h;
     }
+  } else if (mode == AS_MLP_GATE_SCORE) {
+    // stage 1: dense gate over every neuron, |silu(g)| > t_h, up over the kept ones;
+    // the kept neurons' h values go out as one list tile per workgroup
+    if (clear_y && (st = hip_check(launch_fill_zero(Y, size_t(M) * d * sizeof(float), stream), fn)) != AS_OK)
+      return st;
+    const bool want_bits = dbg && !dense && dbg->h_mask.bits;
+    const bool want_nnz = dbg && !dense && dbg->h_mask.nnz;
+    if (want_bits && (st = hip_check(launch_fill_zero(dbg->h_mask.bits, size_t(M) * ((f + 63) / 64) * 8, stream), fn)) != AS_OK)
+      return st;
+    if (want_nnz && (st = hip_check(launch_fill_zero(dbg->h_mask.nnz, size_t(M) * sizeof(int), stream), fn)) != AS_OK)
+      return st;
+    GateScoreParams q;
+    memset(&q, 0, sizeof q);
+    q.x = X; q.x_dt = int(x_dt); q.M = M; q.ldx = d; q.d_model = d; q.d_ff = f;
+    q.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); q.ld_neuron = 3L * d; q.up_off = d;
+    q.t = t_h; q.keep_all = dense ? 1 : 0; q.npb = kGateScoreNpb;
+    q.o_cnt = mw.l_cnt; q.o_idx = mw.l_idx; q.o_val = mw.l_val;
+    q.a_dbg = dbg ? dbg->a : nullptr; q.h_dbg = dbg ? dbg->h : nullptr; q.ld_dbg = f;
+    q.bits = want_bits ? dbg->h_mask.bits : nullptr; q.bits_ld = (f + 63) / 64;
+    q.nnz = want_nnz ? dbg->h_mask.nnz : nullptr;
+    if ((st = hip_check(launch_gate_score(int(w->w_dt), mt, nt, q, stream), fn)) != AS_OK) return st;
+    if ((st = rec(1)) != AS_OK) return st;
+    p2.W = reinterpret_cast<const uint16_t*>(w->w_gate_up) + 2L * d; p2.ldw = 3L * d;
   } else {
     // stage 1: gate/up dot products of the listed neurons (neuron-major rows)
     if (clear_y && (st = hip_check(launch_fill_zero(Y, size_t(M) * d * sizeof(float), stream), fn)) != AS_OK)

@@ -866,34 +866,64 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     const int r1 = rr1 >= 0 ? rr1 : min(p.K, split_point(sl + 1, units, S) * 64);
     cnt = compact_parts<MT>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan, tile == 0);
   } else if constexpr (IN == IN_LISTS) {
+    // Tile counts: up to kLB batches of 256 tiles are loaded together (one round
+    // trip), then scanned batch by batch into the prefix table s_pref.
+    constexpr int kLB = MT >= 8 ? 2 : MT >= 4 ? 4 : 8;   // batch per thread (registers)
     int run = 0;
-    for (int base = 0; base < n_lt; base += kThreads) {
-      const int q = base + tid;
-      const int v = q < n_lt ? p.list_cnt[lt0 + q] : 0;
-      int tot;
-      const int off = block_excl_scan<kThreads>(v, s_scan, &tot);
-      if (q < n_lt) s_pref[q] = run + off;
-      run += tot;
+    for (int base0 = 0; base0 < n_lt; base0 += kLB * kThreads) {
+      int v[kLB];
+#pragma unroll
+      for (int k = 0; k < kLB; ++k) {
+        const int q = base0 + k * kThreads + tid;
+        v[k] = q < n_lt ? p.list_cnt[lt0 + q] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < kLB; ++k) {
+        if (base0 + k * kThreads >= n_lt) break;         // uniform
+        const int q = base0 + k * kThreads + tid;
+        int tot;
+        const int off = block_excl_scan<kThreads>(v[k], s_scan, &tot);
+        if (q < n_lt) s_pref[q] = run + off;
+        run += tot;
+      }
     }
     if (tid == 0) s_pref[n_lt] = run;
     __syncthreads();
     const int nnz = run;
     const int lo = split_point(sl, nnz, S), hi = split_point(sl + 1, nnz, S);
     cnt = hi - lo;
-    for (int r = tid; r < cnt; r += kThreads) {
-      const int g = lo + r;
-      int a = 0, b = n_lt;            // largest q with s_pref[q] <= g
-      while (b - a > 1) {
-        const int mid = (a + b) >> 1;
-        if (s_pref[mid] <= g) a = mid; else b = mid;
+    // Entries: a batch of up to kLB entries per thread is located in the prefix
+    // table first (binary searches in LDS), then all its loads issue together.
+    for (int r0 = tid; r0 < cnt; r0 += kLB * kThreads) {
+      long e[kLB];
+#pragma unroll
+      for (int k = 0; k < kLB; ++k) {
+        const int r = r0 + k * kThreads;
+        const int g = lo + min(r, cnt - 1);
+        int a = 0, b = n_lt;            // largest q with s_pref[q] <= g
+        while (b - a > 1) {
+          const int mid = (a + b) >> 1;
+          if (s_pref[mid] <= g) a = mid; else b = mid;
+        }
+        e[k] = (long)(lt0 + a) * p.lt_stride + (g - s_pref[a]);
       }
-      const long e = (long)(lt0 + a) * p.lt_stride + (g - s_pref[a]);
-      float xv[MT];
-      s_idx[r] = p.list_idx[e];
+      int idx[kLB];
+      float xv[kLB][MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) xv[m] = p.list_val[e * M + (m < M ? m : M - 1)];
+      for (int k = 0; k < kLB; ++k) {
+        idx[k] = p.list_idx[e[k]];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? xv[m] : 0.f;
+        for (int m = 0; m < MT; ++m) xv[k][m] = p.list_val[e[k] * M + (m < M ? m : M - 1)];
+      }
+#pragma unroll
+      for (int k = 0; k < kLB; ++k) {
+        const int r = r0 + k * kThreads;
+        if (r < cnt) {
+          s_idx[r] = idx[k];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) s_val[m * cap + r] = m < M ? xv[k][m] : 0.f;
+        }
+      }
     }
   } else {  // IN_ALL: every row, no mask (dense baseline)
     const int K = p.K;

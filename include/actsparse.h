@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AS_VERSION 200
+#define AS_VERSION 201
 
 typedef enum {
   AS_OK = 0,
@@ -151,13 +151,13 @@ as_status as_dense_gemv(const void *X, as_dtype x_dt, int M, int K,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ sparse SwiGLU MLP */
-typedef enum { AS_MLP_THRESHOLD = 0, AS_MLP_NEURON_SET = 1 } as_mlp_mode;
+typedef enum { AS_MLP_THRESHOLD = 0, AS_MLP_NEURON_SET = 1, AS_MLP_GATE_SCORE = 2 } as_mlp_mode;
 
 typedef struct {
   const void *w_gate_up;  /* THRESHOLD: [d_model, 2, d_ff] input-major (row i = gate row i
-                             then up row i).  NEURON_SET: [d_ff, 3, d_model] neuron-major
-                             (gate row, up row, down row of neuron j adjacent). */
-  const void *w_down;     /* THRESHOLD: [d_ff, d_model] input-major.  NEURON_SET: NULL. */
+                             then up row i).  NEURON_SET and GATE_SCORE: [d_ff, 3, d_model]
+                             neuron-major (gate row, up row, down row of neuron j adjacent). */
+  const void *w_down;     /* THRESHOLD: [d_ff, d_model] input-major.  Otherwise NULL. */
   as_dtype w_dt;          /* AS_F16 or AS_BF16 */
   int d_model;            /* multiple of 8, at most 2^24 */
   int d_ff;               /* multiple of 64, at most 2^24 */
@@ -165,12 +165,15 @@ typedef struct {
 
 typedef struct {
   float *h;               /* THRESHOLD: [M, d_ff] fp32 intermediate silu(g)*u of every
-                             neuron.  NEURON_SET: [M, n_active] for the listed neurons. */
+                             neuron.  NEURON_SET: [M, n_active] for the listed neurons.
+                             GATE_SCORE: [M, d_ff], 0 where the token drops the neuron. */
   as_mask_out x_mask;     /* input mask |X| > t_x (THRESHOLD only; see as_threshold_gemv) */
-  as_mask_out h_mask;     /* |h| > t_h (THRESHOLD only): bits [M, ceil(d_ff/64)] and nnz [M];
-                             idx must be NULL */
+  as_mask_out h_mask;     /* THRESHOLD: |h| > t_h; GATE_SCORE: the keep mask |silu(g)| > t_h.
+                             bits [M, ceil(d_ff/64)] and nnz [M]; idx must be NULL */
   hipEvent_t ev[3];       /* if non-NULL: recorded before stage 1, between the stages,
                              and after stage 2 (per-kernel timing) */
+  float *a;               /* GATE_SCORE only: [M, d_ff] fp32 gate activation silu(g) of
+                             every neuron (the score the keep mask thresholds) */
 } as_mlp_debug;
 
 /* THRESHOLD (TEAL slides, method slide; every projection input thresholded):
@@ -180,6 +183,14 @@ typedef struct {
  * through decode): the same SwiGLU restricted to neurons
  * neuron_idx[0 .. n_active) (int32, device, ascending, distinct, < d_ff);
  * t_x and t_h are ignored.
+ * GATE_SCORE (Intra-expert summary, system implementation: dense gate projection,
+ * one threshold pass over the scores, up and down over the active neurons only;
+ * TEAL slides, slides 5-6: the CATS score |SiLU(x W_gate)|):
+ *   g = X Wg (every neuron);  a = silu(g);  token m keeps neuron j iff |a[m,j]| > t_h
+ *   h[m,j] = a[m,j] * (X[m] . Wu[j]) where kept, else 0;  Y = h Wd
+ * The up and down rows of a neuron are read once if any token keeps it.  t_x
+ * must be -INFINITY (X is not thresholded; UNSUPPORTED otherwise); M <= 8;
+ * d_model <= 8192; neuron_idx is ignored.  AS_FLAG_FORCE_DENSE keeps every neuron.
  * X: [M, d_model] (f16/bf16/f32), 1 <= M <= 16 (M > 8: THRESHOLD mode with bf16
  * weights, on the matrix cores); Y: [M, d_model].
  * silu(z) = z / (1 + exp(-z)).  AS_FLAG_FORCE_DENSE: dense SwiGLU over all
