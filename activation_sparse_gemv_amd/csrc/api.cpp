@@ -182,11 +182,6 @@ MlpPlan plan_mlp(int M, const as_mlp_weights* w, as_mlp_mode mode, bool dense) {
     }
     mp.n_lt = mp.p1.n_tiles;
     mp.lt_stride = mp.p1.lpr * 4;   // tile neurons = tile columns / 2
-  } else if (mode == AS_MLP_GATE_SCORE) {
-    // one list tile per gate-score workgroup of kGateScoreNpb neurons
-    mp.p1 = Plan{0, 0, 1, 0};
-    mp.n_lt = gate_score_grid(w->d_ff, kGateScoreNpb);
-    mp.lt_stride = kGateScoreNpb;
   } else {
     mp.p1 = Plan{0, 0, 1, 0};
     mp.n_lt = 1;
@@ -616,18 +611,22 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
       return st;
     if (want_nnz && (st = hip_check(launch_fill_zero(dbg->h_mask.nnz, size_t(M) * sizeof(int), stream), fn)) != AS_OK)
       return st;
+    float* hg = (dbg && dbg->h) ? dbg->h : mw.h;
     GateScoreParams q;
     memset(&q, 0, sizeof q);
     q.x = X; q.x_dt = int(x_dt); q.M = M; q.ldx = d; q.d_model = d; q.d_ff = f;
     q.W = reinterpret_cast<const uint16_t*>(w->w_gate_up); q.ld_neuron = 3L * d; q.up_off = d;
     q.t = t_h; q.keep_all = dense ? 1 : 0; q.npb = kGateScoreNpb;
-    q.o_cnt = mw.l_cnt; q.o_idx = mw.l_idx; q.o_val = mw.l_val;
-    q.a_dbg = dbg ? dbg->a : nullptr; q.h_dbg = dbg ? dbg->h : nullptr; q.ld_dbg = f;
+    q.h = hg; q.ldh = f; q.a_dbg = dbg ? dbg->a : nullptr;
     q.bits = want_bits ? dbg->h_mask.bits : nullptr; q.bits_ld = (f + 63) / 64;
     q.nnz = want_nnz ? dbg->h_mask.nnz : nullptr;
     if ((st = hip_check(launch_gate_score(int(w->w_dt), mt, nt, q, stream), fn)) != AS_OK) return st;
     if ((st = rec(1)) != AS_OK) return st;
+    // stage 2: down rows of the neurons with a nonzero h; each slice compacts its own
+    // range of h (a dropped neuron's h is exactly 0; the dense baseline reads every row)
     p2.W = reinterpret_cast<const uint16_t*>(w->w_gate_up) + 2L * d; p2.ldw = 3L * d;
+    p2.x = hg; p2.x_dt = AS_F32; p2.K = f; p2.ldx = f; p2.t = 0.0f;
+    c2.in = dense ? IN_ALL : IN_RANGE;
   } else {
     // stage 1: gate/up dot products of the listed neurons (neuron-major rows)
     if (clear_y && (st = hip_check(launch_fill_zero(Y, size_t(M) * d * sizeof(float), stream), fn)) != AS_OK)

@@ -12,9 +12,9 @@
 // in LDS as fp32) across the wave, and only if some token keeps the neuron
 // (|silu(g)| > t) streams the up row.  Many small workgroups (four waves, a few
 // neurons each) keep the CUs full: the hardware refills a CU as its workgroups
-// finish, which balances the uneven kept counts.  Each workgroup writes its kept
-// neurons, in neuron order, as one tile of the list the down projection (the
-// row-gather GEMV over the kept neurons' down rows) reads.
+// finish, which balances the uneven kept counts.  h goes out densely ([M, d_ff],
+// exactly 0 for a dropped neuron): the down projection is then the row-gather GEMV
+// whose slices each compact their own range of h (its nonzero rows).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -66,7 +66,6 @@ __device__ __forceinline__ void gs_reduce(const u32x4 (&v)[NK], const float* xs,
 template <int WDT, int MT, int NK, bool NT>
 __global__ __launch_bounds__(kGsThreads) void gate_score_kernel(const GateScoreParams p) {
   extern __shared__ __align__(16) float xs[];          // [MT][d_model] fp32
-  __shared__ float s_h[MT][kGsMaxNpb];
   __shared__ uint32_t s_keep[kGsMaxNpb];               // bit m: token m keeps the neuron
   const int d = p.d_model, M = p.M;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -128,40 +127,25 @@ __global__ __launch_bounds__(kGsThreads) void gate_score_kernel(const GateScoreP
     if (lane == 0) {
       s_keep[q] = keep;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        s_h[m][q] = h[m];
+      for (int m = 0; m < MT; ++m)
         if (m < M) {
-          if (p.a_dbg != nullptr) p.a_dbg[m * p.ld_dbg + j] = a[m];
-          if (p.h_dbg != nullptr) p.h_dbg[m * p.ld_dbg + j] = h[m];
+          p.h[m * p.ldh + j] = h[m];
+          if (p.a_dbg != nullptr) p.a_dbg[m * p.ldh + j] = a[m];
         }
-      }
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    // the tile's kept neurons (kept by any token) in neuron order; a token's value
-    // is 0 where it drops the neuron
-    const uint32_t kb = lane < nloc ? s_keep[lane] : 0u;
-    const uint64_t any = __ballot(kb != 0u);
-    if (kb != 0u) {
-      const int pos = j0 + lanes_below(any);
-      p.o_idx[pos] = j0 + lane;
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) p.o_val[(long)pos * M + m] = s_h[m][lane];
-    }
-    if (lane == 0) p.o_cnt[blockIdx.x] = __popcll(any);
+  if (wave == 0 && (p.bits != nullptr || p.nnz != nullptr)) {
     // per-token keep masks: npb divides 64, so a tile's bits of one token land in
     // one 64-bit word (cleared by the host; several tiles share a word)
-    if (p.bits != nullptr || p.nnz != nullptr) {
-      for (int m = 0; m < M; ++m) {
-        const uint64_t b = __ballot((kb >> m) & 1u);
-        if (lane == 0 && b != 0) {
-          if (p.bits != nullptr)
-            atomicOr(reinterpret_cast<unsigned long long*>(p.bits + m * p.bits_ld + j0 / 64),
-                     (unsigned long long)(b << (j0 % 64)));
-          if (p.nnz != nullptr) atomicAdd(p.nnz + m, (int)__popcll(b));
-        }
+    const uint32_t kb = lane < nloc ? s_keep[lane] : 0u;
+    for (int m = 0; m < M; ++m) {
+      const uint64_t b = __ballot((kb >> m) & 1u);
+      if (lane == 0 && b != 0) {
+        if (p.bits != nullptr)
+          atomicOr(reinterpret_cast<unsigned long long*>(p.bits + m * p.bits_ld + j0 / 64),
+                   (unsigned long long)(b << (j0 % 64)));
+        if (p.nnz != nullptr) atomicAdd(p.nnz + m, (int)__popcll(b));
       }
     }
   }

@@ -97,16 +97,16 @@ struct NeuronGuParams {
 hipError_t launch_neuron_gu(int wdt, int mt, bool nt, const NeuronGuParams& p, hipStream_t s);
 
 // Gate-score neuron selection (dense gate, |silu(g)| > t, up over the kept):
-// workgroup b scores neurons [b * npb, (b + 1) * npb) and writes its kept ones as
-// list tile b (o_cnt[b] entries at o_idx / o_val [b * npb ...], values [M] each).
+// workgroup b scores neurons [b * npb, (b + 1) * npb) and writes h[m * ldh + j]
+// for each of them (0 where token m drops neuron j).
 constexpr int kGsMaxNpb = 64;
 struct GateScoreParams {
   const void* x; int x_dt; int M; long ldx; int d_model; int d_ff;
   const uint16_t* W; long ld_neuron; long up_off;    // gate row of neuron j at W + j*ld_neuron, up at + up_off
   float t; int keep_all;
   int npb;                                            // neurons per workgroup, divides 64
-  int* o_cnt; int* o_idx; float* o_val;
-  float* a_dbg; float* h_dbg; long ld_dbg;            // optional [M, d_ff] silu(g) and h
+  float* h; long ldh;                                 // [M, d_ff] output
+  float* a_dbg;                                       // optional [M, d_ff] silu(g) (stride ldh)
   uint64_t* bits; long bits_ld; int* nnz;             // optional keep masks (cleared by the host)
 };
 int gate_score_grid(int d_ff, int npb);

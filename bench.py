@@ -525,6 +525,67 @@ def row_glass(C, cpu):
     return r
 
 
+def row_gate(C, cpu):
+    """NEXT-1 gate-score MLP: dense gate, |silu(g)| > t, up and down over the kept."""
+    torch, asg, L, datagen = C.torch, C.asg, C.L, C.datagen
+    d, f = 4096, 14336
+    W = datagen.mlp_weights_neuron_major(6, 0, d, f)
+    Wd = W.to(C.dev)
+    # four 352 MB copies rotate (1.4 GB between reuses of one copy)
+    gs = [asg.MLPWeights(Wd, None, L.AS_MLP_GATE_SCORE)] + \
+         [asg.MLPWeights(Wd.clone(), None, L.AS_MLP_GATE_SCORE) for _ in range(3)]
+    ns = [asg.MLPWeights(w.w_gate_up, None, L.AS_MLP_NEURON_SET) for w in gs]
+    calib = datagen.student_t((64, d), datagen.seed_for(6, 0, "calib")).to(C.dev)
+    toks = datagen.student_t((16, d), datagen.seed_for(6, 0, "decode")).to(C.dev)
+    pool = []
+    for b in range(0, 64, 8):
+        _, dd = asg.as_sparse_swiglu_mlp(calib[b:b + 8], gs[0], float("-inf"), float("-inf"), debug=True)
+        pool.append(dd["a"].clone())
+    pool = torch.cat(pool)
+    Y = torch.empty((1, d), dtype=torch.float32, device=C.dev)
+    ninf = float("-inf")
+    fd_gs = [lambda w=w, i=i: asg.as_sparse_swiglu_mlp(toks[i % 16], w, ninf, ninf, flags=L.AS_FLAG_FORCE_DENSE, Y=Y)
+             for i, w in enumerate(gs * 3)]
+    fd_ns = [lambda w=w, i=i: asg.as_sparse_swiglu_mlp(toks[i % 16], w, flags=L.AS_FLAG_FORCE_DENSE, Y=Y)
+             for i, w in enumerate(ns * 3)]
+    us_dense_gs, us_dense_ns = C.graph_us(fd_gs), C.graph_us(fd_ns)
+    out = {"step": "NEXT-1 gate-score MLP: dense gate (every neuron), one threshold pass on |silu(g)|, "
+                   "up and down rows of the kept neurons only (neuron-major [d_ff, 3, d_model])",
+           "shape": "d_model 4096, d_ff 14336, bf16, batch 1, t calibrated on 64 tokens' gate activations",
+           "dense_same_kernels_us": r4(us_dense_gs),
+           "dense_neuron_major_us": r4(us_dense_ns),
+           "note": "dense_neuron_major: gate and up rows of every neuron read together (one round trip per "
+                   "neuron), then the down rows: the fastest dense SwiGLU on this layout",
+           "points": []}
+    for p in (0.5, 0.7, 0.9):
+        t = float(asg.as_calibrate_threshold(pool, p).item())
+        fs = [lambda w=w, i=i: asg.as_sparse_swiglu_mlp(toks[i % 16], w, ninf, t, Y=Y)
+              for i, w in enumerate(gs * 3)]
+        us = C.graph_us(fs)
+        kept = []
+        for i in range(16):
+            _, dd = asg.as_sparse_swiglu_mlp(toks[i], gs[0], ninf, t, debug=True)
+            kept.append(int(dd["h_mask"]["nnz"][0].item()))
+        kmean = float(np.mean(kept))
+        ab = (f + 2 * kmean) * d * 2                 # gate of every neuron, up and down of the kept
+        out["points"].append({"sparsity": p, "t": t, "kept_mean": r4(kmean), "us": r4(us),
+                              "active_mb": r4(ab / 1e6), "gbs": r4(ab / (us * 1e-6) / 1e9),
+                              "frac_hbm": r4(ab / (us * 1e-6) / 8e12),
+                              "speedup_vs_dense_same_kernels": r4(us_dense_gs / us),
+                              "speedup_vs_dense_neuron_major": r4(us_dense_ns / us),
+                              "ideal_speedup_bytes": r4(3 * f / (f + 2 * kmean))})
+    if cpu:
+        from oracle import gate
+        Wg, Wu, Wdn = (W[:, j].to(torch.float64).numpy() for j in range(3))
+        T = toks.cpu().double().numpy()
+        t = out["points"][0]["t"]
+        cu, _, _ = cpu_time(lambda i: gate.gate_score_mlp(T[i % 16], Wg, Wu, Wdn, t=np.float32(t)), 4.0, 100)
+        out.update(cpu_oracle_us=r4(cu), cpu_cores=cores())
+    del gs, ns, Wd
+    torch.cuda.empty_cache()
+    return out
+
+
 class _LazyF64:
     """Index-on-demand fp64 view of a stacked bf16 expert tensor (oracle sample only)."""
 
@@ -826,6 +887,7 @@ def main():
         rows = {}
         for name, fn in (("a1_calibrate", lambda: row_calibrate(C, cpu)), ("a2_a3_gemv", lambda: row_gemv(C, cpu)),
                          ("a6_topk", lambda: row_topk(C, cpu)), ("a7_glass", lambda: row_glass(C, cpu)),
+                         ("next1_gate_score", lambda: row_gate(C, cpu)),
                          ("a8_a9_moe", lambda: row_moe(C, cpu)),
                          ("a10_batch16_mfma", lambda: row_batch16(C, cpu, t_x, t_h)),
                          ("a11_block", lambda: row_block(C, cpu)), ("small_mlp_fp16", lambda: row_small(C, cpu))):
