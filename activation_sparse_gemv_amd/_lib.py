@@ -106,6 +106,7 @@ SIGNATURES = {
     "as_glass_local_signal": (c_int, [c_void_p, c_int, c_int, POINTER(ASMlpWeights), c_void_p, c_void_p]),
     "as_bench_flush": (c_int, [c_void_p, c_size_t, c_void_p]),
     "as_bench_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "as_greedy_sparsity": (c_int, [c_void_p, c_int, c_int, c_void_p, ctypes.c_double, ctypes.c_double, c_void_p]),
 }
 
 _lib = None

@@ -596,3 +596,18 @@ def prepare_sparse_swiglu_mlp(X: torch.Tensor, w: MLPWeights, t_x: float, t_h: f
             _ptr(neuron_idx), n_active, _ptr(Y), _dt(Y), flags,
             ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream(X.device))
     return PreparedCall(lib.as_sparse_swiglu_mlp, args, "as_sparse_swiglu_mlp", (ws_, dbg, ws, X2, Y))
+
+
+def as_greedy_sparsity(err, weights, step: float, target: float):
+    """Block-wise greedy sparsity levels (host arrays): ``err`` [n_blocks, n_levels]
+    (error at sparsity level * step), ``weights`` [n_blocks]; returns int32 levels."""
+    import numpy as np
+    e = np.ascontiguousarray(err, dtype=np.float64)
+    w = np.ascontiguousarray(weights, dtype=np.float64)
+    if e.ndim != 2 or w.shape != (e.shape[0],):
+        raise ValueError("err must be [n_blocks, n_levels] and weights [n_blocks]")
+    out = np.zeros(e.shape[0], dtype=np.int32)
+    lib = L.load()
+    L.check(lib.as_greedy_sparsity(e.ctypes.data, e.shape[0], e.shape[1], w.ctypes.data, float(step), float(target),
+                                   out.ctypes.data), "as_greedy_sparsity")
+    return out

@@ -660,6 +660,41 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
   return rec(2);
 }
 
+// ------------------------------------------------------------------ greedy allocation
+as_status as_greedy_sparsity(const double* err, int n_blocks, int n_levels, const double* weights, double step,
+                             double target, int32_t* levels) {
+  const char* fn = "as_greedy_sparsity";
+  if (!err || !weights || !levels) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (n_blocks < 1 || n_levels < 1) return fail(AS_ERR_INVALID_ARG, "%s: n_blocks=%d n_levels=%d", fn, n_blocks, n_levels);
+  if (!(step > 0.0) || !std::isfinite(step)) return fail(AS_ERR_INVALID_ARG, "%s: step must be > 0", fn);
+  if (!(target >= 0.0 && target <= 1.0)) return fail(AS_ERR_INVALID_ARG, "%s: target outside [0, 1]", fn);
+  double wsum = 0.0;
+  for (int b = 0; b < n_blocks; ++b) {
+    if (!(weights[b] > 0.0) || !std::isfinite(weights[b])) return fail(AS_ERR_INVALID_ARG, "%s: weight %d", fn, b);
+    wsum += weights[b];
+    for (int l = 0; l < n_levels; ++l)
+      if (!std::isfinite(err[(size_t)b * n_levels + l])) return fail(AS_ERR_INVALID_ARG, "%s: err[%d][%d]", fn, b, l);
+  }
+  for (int b = 0; b < n_blocks; ++b) levels[b] = 0;
+  auto overall = [&]() {
+    double s = 0.0;
+    for (int b = 0; b < n_blocks; ++b) s += weights[b] * levels[b] * step;
+    return s / wsum;
+  };
+  while (overall() < target * (1.0 - 1e-12)) {
+    int best_b = -1;
+    double best = 0.0;
+    for (int b = 0; b < n_blocks; ++b) {
+      if (levels[b] + 1 >= n_levels) continue;
+      const double inc = err[(size_t)b * n_levels + levels[b] + 1] - err[(size_t)b * n_levels + levels[b]];
+      if (best_b < 0 || inc < best) { best = inc; best_b = b; }
+    }
+    if (best_b < 0) break;
+    ++levels[best_b];
+  }
+  return AS_OK;
+}
+
 // ------------------------------------------------------------------ top-k
 size_t as_topk_mask_ws_size(int rows, int n, as_topk_mode mode) {
   if (mode != AS_TOPK_RANK_BLEND || rows < 1 || n < 1) return 0;

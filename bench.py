@@ -586,6 +586,49 @@ def row_gate(C, cpu):
     return out
 
 
+def row_greedy(C, cpu):
+    """NEXT-4 (offline part): block-wise greedy sparsity allocation over synthetic
+    blocks, from error curves measured with this library's sparse and dense paths."""
+    torch, asg, L, datagen = C.torch, C.asg, C.L, C.datagen
+    d, f, nb = 1024, 4096, 8
+    shape = datagen.MLPShape(d, f, "bf16")
+    levels = np.round(np.arange(0, 0.91, 0.1), 2)
+    err = np.zeros((nb, len(levels)))
+    for b in range(nb):
+        wgu, wd = datagen.mlp_weights_input_major(7, b, shape)
+        w = asg.MLPWeights(wgu.to(C.dev), wd.to(C.dev))
+        # later blocks see heavier-tailed inputs (Student-t with fewer degrees of freedom)
+        nu = 8.0 - 0.75 * b
+        calib = datagen.student_t((64, d), datagen.seed_for(7, b, "calib"), nu=nu).to(C.dev)
+        ev = datagen.student_t((16, d), datagen.seed_for(7, b, "eval"), nu=nu).to(C.dev)
+        yd = asg.as_sparse_swiglu_mlp(ev, w, flags=L.AS_FLAG_FORCE_DENSE).double()
+        for li, p in enumerate(levels):
+            if p == 0:
+                continue
+            tx = float(asg.as_calibrate_threshold(calib, p).item())
+            _, dd = asg.as_sparse_swiglu_mlp(calib, w, tx, float("-inf"), debug=True)
+            th = float(asg.as_calibrate_threshold(dd["h"], p).item())
+            ys = asg.as_sparse_swiglu_mlp(ev, w, tx, th).double()
+            err[b, li] = float(((ys - yd) ** 2).sum() / (yd ** 2).sum())
+        del w
+    wts = np.ones(nb)
+    lev = asg.as_greedy_sparsity(err, wts, 0.1, 0.5)
+    uni = int(round(0.5 / 0.1))
+    out = {"step": "NEXT-4 block-wise greedy allocation (offline): per-block l2 error of the sparse MLP output "
+                   "vs dense at sparsities 0..0.9, then as_greedy_sparsity to a 50% model-wide target",
+           "shape": f"{nb} synthetic SwiGLU blocks {d}->{f}->{d} bf16, Student-t inputs, nu from 8.0 down to 2.75",
+           "levels": [float(round(v * 0.1, 2)) for v in lev],
+           "greedy_total_rel_sq_err": float(f"{sum(err[b, lev[b]] for b in range(nb)):.4g}"),
+           "uniform_total_rel_sq_err": float(f"{err[:, uni].sum():.4g}"),
+           "err_curves": [[float(f"{v:.4g}") for v in row] for row in err]}
+    if cpu:
+        from oracle import greedy
+        assert greedy.greedy_allocate(err, wts, 0.1, 0.5).tolist() == lev.tolist()
+        out["oracle_levels_equal"] = True
+    torch.cuda.empty_cache()
+    return out
+
+
 class _LazyF64:
     """Index-on-demand fp64 view of a stacked bf16 expert tensor (oracle sample only)."""
 
@@ -888,6 +931,7 @@ def main():
         for name, fn in (("a1_calibrate", lambda: row_calibrate(C, cpu)), ("a2_a3_gemv", lambda: row_gemv(C, cpu)),
                          ("a6_topk", lambda: row_topk(C, cpu)), ("a7_glass", lambda: row_glass(C, cpu)),
                          ("next1_gate_score", lambda: row_gate(C, cpu)),
+                         ("next4_greedy", lambda: row_greedy(C, cpu)),
                          ("a8_a9_moe", lambda: row_moe(C, cpu)),
                          ("a10_batch16_mfma", lambda: row_batch16(C, cpu, t_x, t_h)),
                          ("a11_block", lambda: row_block(C, cpu)), ("small_mlp_fp16", lambda: row_small(C, cpu))):

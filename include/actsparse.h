@@ -369,6 +369,29 @@ as_status as_moe_layer(const void *X, as_dtype x_dt, int T, const as_moe_layer_w
                        float *h_dbg, int32_t *keep_dbg,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------ offline sparsity allocation
+ * Block-wise greedy sparsity allocation (TEAL slides, slide 10): under a
+ * model-wide sparsity target, every block starts at sparsity 0 and, one step at
+ * a time, the block whose error would grow least is raised one level, until the
+ * target is met.  Host-side (it runs once, offline; inference then uses the
+ * fixed per-block levels).
+ *   err      host, [n_blocks][n_levels] doubles: block b's l2 activation error at
+ *            sparsity l * step (measured beforehand, e.g. with the sparse and dense
+ *            paths of this library on calibration inputs)
+ *   weights  host, [n_blocks] doubles > 0: each block's share of the model-wide
+ *            sparsity (e.g. its count of thresholded inputs); the overall sparsity
+ *            is the weighted mean of step * level
+ *   step     > 0: sparsity per level; target in [0, 1]
+ *   levels   host, [n_blocks] int32 output
+ * A step raises the block with the least error increase err[b][l+1] - err[b][l]
+ * (ties to the smaller index; blocks at level n_levels - 1 are not raised); the
+ * loop stops at the first step whose overall sparsity reaches target (relative
+ * slack 1e-12) or when no block can be raised.
+ * Errors: INVALID_ARG for NULL pointers, n_blocks < 1, n_levels < 1, a weight
+ * <= 0 or not finite, step <= 0, target outside [0, 1], a non-finite error. */
+as_status as_greedy_sparsity(const double *err, int n_blocks, int n_levels, const double *weights,
+                             double step, double target, int32_t *levels);
+
 /* ------------------------------------------------------------ decoder-block glue
  * TEAL slides, method slide: every projection input of the attention and MLP
  * blocks is thresholded; the attention core stays dense.  Readings (the pages

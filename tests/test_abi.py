@@ -262,3 +262,32 @@ def test_phase_timeline_only_in_the_opt_in_build(lib):
     tl.as_phase_timeline_arm.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     assert tl.as_phase_timeline_arm(None, 1024) == L.AS_ERR_INVALID_ARG
     assert tl.as_phase_timeline_arm(ctypes.c_void_p(16), 8) == L.AS_ERR_INVALID_ARG
+
+
+def test_greedy_sparsity_matches_the_oracle(lib):
+    """The C allocation takes the oracle's steps exactly (integer levels), on convex
+    and on non-monotone curves, with ties and weights; bad arguments are rejected."""
+    import numpy as np
+    from oracle import greedy
+    import activation_sparse_gemv_amd as asg
+    rng = np.random.default_rng(12)
+    for trial in range(40):
+        nb, nl = int(rng.integers(1, 9)), int(rng.integers(1, 12))
+        err = np.round(rng.standard_normal((nb, nl)).cumsum(axis=1), 1)     # ties and non-monotone steps
+        w = rng.choice([1.0, 2.0, 0.5, 3.0], nb)
+        step = float(rng.choice([0.05, 0.1, 0.125]))
+        target = float(rng.uniform(0, 1))
+        got = asg.as_greedy_sparsity(err, w, step, target)
+        assert got.tolist() == greedy.greedy_allocate(err, w, step, target).tolist()
+    e = np.zeros((2, 3))
+    p = e.ctypes.data
+    wv = np.ones(2)
+    lv = np.zeros(2, dtype=np.int32)
+    assert lib.as_greedy_sparsity(None, 2, 3, wv.ctypes.data, 0.1, 0.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
+    assert lib.as_greedy_sparsity(p, 0, 3, wv.ctypes.data, 0.1, 0.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
+    assert lib.as_greedy_sparsity(p, 2, 3, wv.ctypes.data, 0.0, 0.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
+    assert lib.as_greedy_sparsity(p, 2, 3, wv.ctypes.data, 0.1, 1.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
+    wbad = np.array([1.0, -1.0])
+    assert lib.as_greedy_sparsity(p, 2, 3, wbad.ctypes.data, 0.1, 0.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
+    enan = np.array([[0.0, np.nan, 1.0], [0.0, 1.0, 2.0]])
+    assert lib.as_greedy_sparsity(enan.ctypes.data, 2, 3, wv.ctypes.data, 0.1, 0.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
