@@ -12,7 +12,7 @@ LIB_PATH = os.environ.get("ACTSPARSE_LIB",
                           os.path.join(os.path.dirname(os.path.abspath(__file__)), "libactsparse.so"))
 
 AS_OK, AS_ERR_INVALID_ARG, AS_ERR_UNSUPPORTED, AS_ERR_WORKSPACE, AS_ERR_HIP = range(5)
-AS_F16, AS_BF16, AS_F32 = 0, 1, 2
+AS_F16, AS_BF16, AS_F32, AS_I8 = 0, 1, 2, 3
 AS_FLAG_ACCUMULATE = 1 << 0
 AS_FLAG_ATOMIC_SPLITK = 1 << 1
 AS_FLAG_NO_NT_LOADS = 1 << 2
@@ -107,6 +107,9 @@ SIGNATURES = {
     "as_bench_flush": (c_int, [c_void_p, c_size_t, c_void_p]),
     "as_bench_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "as_greedy_sparsity": (c_int, [c_void_p, c_int, c_int, c_void_p, ctypes.c_double, ctypes.c_double, c_void_p]),
+    "as_threshold_gemv_i8_ws_size": (c_size_t, [c_int, c_int]),
+    "as_threshold_gemv_i8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_float, c_void_p, c_int,
+                                     c_uint, c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None

@@ -611,3 +611,22 @@ def as_greedy_sparsity(err, weights, step: float, target: float):
     L.check(lib.as_greedy_sparsity(e.ctypes.data, e.shape[0], e.shape[1], w.ctypes.data, float(step), float(target),
                                    out.ctypes.data), "as_greedy_sparsity")
     return out
+
+
+def as_threshold_gemv_i8(X: torch.Tensor, Wq: torch.Tensor, row_scale: torch.Tensor, t: float,
+                         y_dtype=torch.float32, flags: int = 0, Y: torch.Tensor | None = None):
+    """One token over int8 rows with a per-row scale:
+    y = sum_{i: |x_i| > t} x_i * row_scale[i] * Wq[i, :].  X [K] or [1, K]; Wq [K, N] int8."""
+    x = X.reshape(-1)
+    _need_cuda(x, Wq, row_scale, Y)
+    if Wq.dtype != torch.int8 or row_scale.dtype != torch.float32:
+        raise ValueError("Wq must be int8 and row_scale float32")
+    K, N = Wq.shape
+    if Y is None:
+        Y = torch.empty((N,), dtype=y_dtype, device=X.device)
+    lib = L.load()
+    nb = lib.as_threshold_gemv_i8_ws_size(K, N)
+    ws = workspace(("gemv_i8", K, N), nb, X.device)
+    L.check(lib.as_threshold_gemv_i8(_ptr(x), _dt(x), K, _ptr(Wq), _ptr(row_scale), N, float(t), _ptr(Y), _dt(Y),
+                                     flags, _ptr(ws), ws.numel(), _stream(X.device)), "as_threshold_gemv_i8")
+    return Y

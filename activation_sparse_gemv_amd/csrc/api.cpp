@@ -120,6 +120,27 @@ Plan plan_gemv(int rows, int cols, bool gu, int mt) {
   return Plan{lpr, n_tiles, S, cap};
 }
 
+// int8 rows (one token): twice the lanes per row segment of the 16-bit plan, so a
+// workgroup's piece of a row is as many bytes, and the slices re-chosen for the
+// halved tile count (the same ~1.75 workgroups per CU).
+Plan plan_gemv_i8(int rows, int cols) {
+  Plan pl = plan_gemv(rows, cols, false, 1);
+  if (pl.lpr >= 64) return pl;
+  pl.lpr *= 2;
+  pl.n_tiles = (cols + pl.lpr * 8 - 1) / (pl.lpr * 8);
+  const int target = (7 * num_cus()) / 4;
+  int S = (target + pl.n_tiles - 1) / pl.n_tiles;
+  const int smax = rows / 128 > 1 ? rows / 128 : 1;
+  if (S > smax) S = smax;
+  if (S > 256) S = 256;
+  if (S < 1) S = 1;
+  const int hard_cap = (kLdsBytes - kLdsReserve) / 8;
+  if ((rows + S - 1) / S > hard_cap) S = (rows + hard_cap - 1) / hard_cap;
+  pl.S = S;
+  pl.cap = (((rows + S - 1) / S) + 7) & ~7;
+  return pl;
+}
+
 struct Carver {
   char* base;
   size_t off = 0;
@@ -304,6 +325,14 @@ as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64
 }
 
 // ------------------------------------------------------------------ GEMV
+size_t as_threshold_gemv_i8_ws_size(int K, int N) {
+  if (K < 1 || N < 1) return 0;
+  const Plan pl = plan_gemv_i8(K, N);
+  Carver c{nullptr};
+  carve_gemv(c, pl, 1, N);
+  return c.off;
+}
+
 size_t as_threshold_gemv_ws_size(int M, int K, int N) {
   if (M < 1 || K < 1 || N < 1) return 0;
   const Plan pl = plan_gemv(K, N, false, mt_for(M));
@@ -332,16 +361,25 @@ static bool can_norm_in_prologue(const void* X, as_dtype x_dt, int K) {
 static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N,
                              float t, void* Y, as_dtype y_dt, unsigned flags, as_mask_out* mo, void* ws,
                              size_t ws_bytes, hipStream_t stream, bool dense, const char* fn,
-                             const GemvFuse* fz = nullptr) {
+                             const GemvFuse* fz = nullptr, const float* row_scale = nullptr) {
   if (!X || !W || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, W or Y", fn);
-  if (!is_dt(x_dt) || !is_wdt(w_dt) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  const bool i8 = w_dt == AS_I8;
+  if (!is_dt(x_dt) || !(is_wdt(w_dt) || i8) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (i8) {
+    if (!row_scale) return fail(AS_ERR_INVALID_ARG, "%s: row_scale is NULL", fn);
+    if (!aligned16(row_scale)) return fail(AS_ERR_INVALID_ARG, "%s: row_scale not 16-byte aligned", fn);
+    if (M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: int8 weights take one token", fn);
+    if (!aligned16(X) || (K % 8) != 0) return fail(AS_ERR_UNSUPPORTED, "%s: int8 weights need a 16-byte aligned X and K %% 8 == 0", fn);
+    if (mo && (mo->bits || mo->idx || mo->nnz)) return fail(AS_ERR_UNSUPPORTED, "%s: int8 weights export no mask", fn);
+    if (fz != nullptr) return fail(AS_ERR_UNSUPPORTED, "%s: int8 weights take no fused work", fn);
+  }
   if (M < 1 || M > 16) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d outside 1..16", fn, M);
   if (M > 8 && w_dt != AS_BF16) return fail(AS_ERR_UNSUPPORTED, "%s: M > 8 (MFMA path) needs bf16 weights", fn);
   if (K < 1 || N < 8 || N % 8 != 0) return fail(AS_ERR_INVALID_ARG, "%s: K=%d N=%d (N must be a multiple of 8)", fn, K, N);
   if (K > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "%s: K=%d above %d", fn, K, kMaxRows);
   if (!aligned16(W)) return fail(AS_ERR_INVALID_ARG, "%s: W not 16-byte aligned", fn);
   if (mo && mo->idx && M != 1) return fail(AS_ERR_UNSUPPORTED, "%s: mask idx export needs M == 1", fn);
-  const Plan pl = plan_gemv(K, N, false, mt_for(M));
+  const Plan pl = i8 ? plan_gemv_i8(K, N) : plan_gemv(K, N, false, mt_for(M));
   if ((long)pl.S * M * N >= (1L << 31))
     return fail(AS_ERR_UNSUPPORTED, "%s: split-K partials of %d x %d x %d exceed 2^31 elements", fn, pl.S, M, N);
   Carver c{reinterpret_cast<char*>(ws)};
@@ -374,6 +412,7 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   }
   p.partials = gw.partials; p.counters = gw.counters; p.part_ld = N;
   p.y = Y; p.y_dt = int(y_dt); p.ldy = N; p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
+  p.row_scale = row_scale;
   if (mo && !dense) {
     p.x_bits = mo->bits; p.x_bits_ld = (K + 63) / 64; p.x_idx = mo->idx; p.x_nnz = mo->nnz;
   }
@@ -407,6 +446,14 @@ as_status as_threshold_gemv(const void* X, as_dtype x_dt, int M, int K, const vo
   const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
   return gemv_common(X, x_dt, M, K, W, w_dt, N, t, Y, y_dt, flags, mask_out, ws, ws_bytes, stream, dense,
                      "as_threshold_gemv");
+}
+
+as_status as_threshold_gemv_i8(const void* X, as_dtype x_dt, int K, const int8_t* W, const float* row_scale,
+                               int N, float t, void* Y, as_dtype y_dt, unsigned flags, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
+  return gemv_common(X, x_dt, 1, K, W, AS_I8, N, dense ? -INFINITY : t, Y, y_dt, flags, nullptr, ws, ws_bytes,
+                     stream, dense, "as_threshold_gemv_i8", nullptr, row_scale);
 }
 
 as_status as_dense_gemv(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N, void* Y,

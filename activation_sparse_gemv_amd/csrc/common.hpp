@@ -8,7 +8,7 @@
 
 namespace as {
 
-enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_I8 = 3 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -53,6 +53,27 @@ __device__ __forceinline__ u32x4 load_w16(const uint16_t* p) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
   if constexpr (NT) return __builtin_nontemporal_load(q);
   else return *q;
+}
+
+// Eight int8 weights (one 8-byte piece of a row), plain or nontemporal.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ u32x2 load_w8(const int8_t* p) {
+  const u32x2* q = reinterpret_cast<const u32x2*>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
+}
+
+// Eight int8 weights (four per dword, lowest byte first) to fp32: the sign bit is
+// flipped so each byte reads as an unsigned value biased by 128 (one byte-to-float
+// conversion and one subtraction per weight, both exact).
+__device__ __forceinline__ void unpack8_i8(const u32x2 v, float w[8]) {
+  const uint32_t a = v.x ^ 0x80808080u, b = v.y ^ 0x80808080u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    w[k] = (float)((a >> (8 * k)) & 0xffu) - 128.f;
+    w[4 + k] = (float)((b >> (8 * k)) & 0xffu) - 128.f;
+  }
 }
 
 // Unpack 8 weights (two per dword, low half first) to fp32.

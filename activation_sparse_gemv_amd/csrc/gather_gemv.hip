@@ -74,6 +74,7 @@ hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStrea
       if (cc.mt > 1 && cc.nv > 2) cc.nv = 0;     // wide register chunks only for one token
     }
   }
+  if (cc.wdt == DT_I8) return launch_gemv_i8_m1(cc, p, smem, s);
   const bool bf = cc.wdt == DT_BF16;
   switch (cc.mt) {
     case 1: return bf ? launch_gemv_bf16_m1(cc, p, smem, s) : launch_gemv_f16_m1(cc, p, smem, s);

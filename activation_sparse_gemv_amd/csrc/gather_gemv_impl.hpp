@@ -324,7 +324,7 @@ __device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s
 // keeps it; a workgroup scan of the per-thread counts places the chunks.  One
 // token's values stay in registers; for several tokens every kept row's values
 // are gathered afterwards in one pass of independent loads.
-template <int MT, int NV>
+template <int MT, int NV, bool WDT_SCALED = false>
 __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i1, bool split, int sl, int S,
                                               int* s_idx, float* s_val, int cap, int* s_scan, int* lo_out,
                                               bool export_xn, float* inv_out) {
@@ -339,6 +339,15 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
   float v0[CEV];            // MT == 1, NV > 0: the chunk's values
   int c = 0;
   if constexpr (NV > 0 && MT == 1) {
+    // int8 rows: the chunk's row scales load together with its inputs
+    float4 sc[WDT_SCALED ? CEV / 4 : 1];
+    if constexpr (WDT_SCALED) {
+      if (n == CEV) {
+        const float4* q = reinterpret_cast<const float4*>(p.row_scale + c0);
+#pragma unroll
+        for (int k = 0; k < CEV / 4; ++k) sc[k] = q[k];
+      }
+    }
     load_chunk<CEV>(p.x, p.x_dt, c0, n, v0);
     if (p.norm_x && split) {
       // RMS of the whole input (the chunks of all threads cover it): per-thread sum
@@ -369,6 +378,19 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
 #pragma unroll
     for (int e = 0; e < CEV; ++e) ubits |= (uint64_t)(e < n && (keep_all || fabsf(v0[e]) > t)) << e;
     c = __popcll(ubits);
+    if constexpr (WDT_SCALED) {
+      // int8 rows: the kept value is x_i * row_scale[i] (the mask stays on x)
+      if (n == CEV) {
+#pragma unroll
+        for (int k = 0; k < CEV / 4; ++k) {
+          v0[4 * k] *= sc[k].x; v0[4 * k + 1] *= sc[k].y; v0[4 * k + 2] *= sc[k].z; v0[4 * k + 3] *= sc[k].w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < CEV; ++e)
+          if (e < n) v0[e] *= p.row_scale[c0 + e];
+      }
+    }
     AS_PHASE_AFTER(c);
     AS_PHASE(p, 8);
   } else if constexpr (NV > 0) {
@@ -855,8 +877,8 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
                 ? compact_range_regs<MT>(p, r0, r1, s_idx, s_val, cap, s_scan)
                 : compact_range_staged<MT, NV>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan);
     else
-      cnt = compact_chunks<MT, NV>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo, tile == 0 && sl == 0,
-                                   &inv_scale);
+      cnt = compact_chunks<MT, NV, WDT == DT_I8>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo,
+                                                 tile == 0 && sl == 0, &inv_scale);
     if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
       thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0, inv_scale);
   } else if constexpr (IN == IN_PARTS) {
@@ -933,6 +955,11 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       s_idx[r] = lo + r;
       float xv[MT];
       load_tokens<MT>(p.x, p.x_dt, p.ldx, lo + r, M, xv);
+      if constexpr (WDT == DT_I8) {
+        const float sc = p.row_scale[lo + r];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xv[m] *= sc;
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m) s_val[m * cap + r] = xv[m];
     }
@@ -982,6 +1009,32 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[m][j] = 0.f;
 
+  if constexpr (WDT == DT_I8) {
+    // int8 rows: 8-byte pieces (eight columns per lane, as for 16-bit weights), twice
+    // as many rows in flight for the same bytes; the row scale is in s_val
+    constexpr int kU8 = 2 * kUnroll;
+    const int8_t* W8 = reinterpret_cast<const int8_t*>(p.W) + (valid ? wcol : 0);
+    for (int r = slot; r < cnt; r += NSLOT * kU8) {
+      int row[kU8];
+#pragma unroll
+      for (int u = 0; u < kU8; ++u) row[u] = s_idx[min(r + u * NSLOT, cnt - 1)];
+      u32x2 w[kU8];
+#pragma unroll
+      for (int u = 0; u < kU8; ++u) w[u] = load_w8<NT>(W8 + (long)row[u] * ldw);
+#pragma unroll
+      for (int u = 0; u < kU8; ++u) {
+        const int rr = r + u * NSLOT;
+        float wf[8];
+        unpack8_i8(w[u], wf);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float xv = rr < cnt ? s_val[m * cap + rr] : 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[m][j] = fmaf(xv, wf[j], acc[m][j]);
+        }
+      }
+    }
+  } else
   for (int r = slot; r < cnt; r += NSLOT * kUnroll) {
     int row[kUnroll];
 #pragma unroll
@@ -1334,6 +1387,29 @@ hipError_t pick_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipS
     return hipErrorInvalidValue;
   }
   return pick_nt<WDT, MT, LPR, IN_ALL, OUT_Y, false>(c, p, smem, s);
+}
+
+// int8 weights: one token, the threshold prologue (16-byte chunks) or every row.
+template <int LPR>
+hipError_t pick_i8_mode(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s) {
+  if (c.gu || c.out != OUT_Y) return hipErrorInvalidValue;
+  if (c.in == IN_THRESH) {
+    if (c.nv == 2) return c.nt ? launch_one<DT_I8, 1, LPR, IN_THRESH, OUT_Y, false, true, 2>(p, smem, s)
+                               : launch_one<DT_I8, 1, LPR, IN_THRESH, OUT_Y, false, false, 2>(p, smem, s);
+    if (c.nv == 8) return c.nt ? launch_one<DT_I8, 1, LPR, IN_THRESH, OUT_Y, false, true, 8>(p, smem, s)
+                               : launch_one<DT_I8, 1, LPR, IN_THRESH, OUT_Y, false, false, 8>(p, smem, s);
+    return hipErrorInvalidValue;
+  }
+  if (c.in == IN_RANGE) {
+    if (c.nv == 2) return c.nt ? launch_one<DT_I8, 1, LPR, IN_RANGE, OUT_Y, false, true, 2>(p, smem, s)
+                               : launch_one<DT_I8, 1, LPR, IN_RANGE, OUT_Y, false, false, 2>(p, smem, s);
+    if (c.nv == 8) return c.nt ? launch_one<DT_I8, 1, LPR, IN_RANGE, OUT_Y, false, true, 8>(p, smem, s)
+                               : launch_one<DT_I8, 1, LPR, IN_RANGE, OUT_Y, false, false, 8>(p, smem, s);
+    return hipErrorInvalidValue;
+  }
+  if (c.in == IN_ALL) return c.nt ? launch_one<DT_I8, 1, LPR, IN_ALL, OUT_Y, false, true, 0>(p, smem, s)
+                                  : launch_one<DT_I8, 1, LPR, IN_ALL, OUT_Y, false, false, 0>(p, smem, s);
+  return hipErrorInvalidValue;
 }
 
 template <int WDT, int MT>

@@ -65,6 +65,8 @@ struct GemvParams {
   int route_top; int* route_ids; float* route_wts;
   // phase timeline (libactsparse_timeline.so only): 16 words per workgroup
   unsigned long long* phase_tl;
+  // int8 weights (DT_I8): row i is W[i, :] * row_scale[i] (fp32, K entries)
+  const float* row_scale;
 };
 
 struct GemvConfig {
@@ -83,6 +85,9 @@ size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt);
 int device_cus();
 
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s);
+// int8 weights with a per-row scale: one token, IN_THRESH (16-byte aligned x) or
+// IN_ALL, OUT_Y.
+hipError_t launch_gemv_i8_m1(const GemvConfig& c, const GemvParams& p, size_t smem, hipStream_t s);
 int pick_chunk_vectors(const void* x, int x_dt, int K, long ldx);
 
 // Neuron-major gate/up dot products for a neuron list (static neuron set).

@@ -600,14 +600,17 @@ def row_greedy(C, cpu):
         # later blocks see heavier-tailed inputs (Student-t with fewer degrees of freedom)
         nu = 8.0 - 0.75 * b
         calib = datagen.student_t((64, d), datagen.seed_for(7, b, "calib"), nu=nu).to(C.dev)
-        ev = datagen.student_t((16, d), datagen.seed_for(7, b, "eval"), nu=nu).to(C.dev)
+        ev = datagen.student_t((16, d), datagen.seed_for(7, b, "decode"), nu=nu).to(C.dev)
         yd = asg.as_sparse_swiglu_mlp(ev, w, flags=L.AS_FLAG_FORCE_DENSE).double()
         for li, p in enumerate(levels):
             if p == 0:
                 continue
             tx = float(asg.as_calibrate_threshold(calib, p).item())
-            _, dd = asg.as_sparse_swiglu_mlp(calib, w, tx, float("-inf"), debug=True)
-            th = float(asg.as_calibrate_threshold(dd["h"], p).item())
+            hs = []
+            for c0 in range(0, 64, 16):
+                _, dd = asg.as_sparse_swiglu_mlp(calib[c0:c0 + 16], w, tx, float("-inf"), debug=True)
+                hs.append(dd["h"].clone())
+            th = float(asg.as_calibrate_threshold(torch.cat(hs), p).item())
             ys = asg.as_sparse_swiglu_mlp(ev, w, tx, th).double()
             err[b, li] = float(((ys - yd) ** 2).sum() / (yd ** 2).sum())
         del w
@@ -626,6 +629,38 @@ def row_greedy(C, cpu):
         assert greedy.greedy_allocate(err, wts, 0.1, 0.5).tolist() == lev.tolist()
         out["oracle_levels_equal"] = True
     torch.cuda.empty_cache()
+    return out
+
+
+def row_int8(C, cpu):
+    """NEXT-4 (kernel part): the sparse GEMV over int8 rows with a per-row scale."""
+    torch, asg, L, datagen = C.torch, C.asg, C.L, C.datagen
+    out = {"step": "NEXT-4 int8 rows (per-row fp32 scale) under the activation mask: one-token sparse GEMV "
+                   "(x is thresholded, kept rows read at 1 byte per weight) vs the bf16 sparse and dense GEMVs",
+           "points": []}
+    for K, N in ((4096, 14336), (14336, 4096)):
+        # eight weight copies of each dtype rotate (>= 0.9 GB between reuses)
+        g = torch.Generator().manual_seed(K)
+        qs = [torch.randint(-127, 128, (K, N), generator=g, dtype=torch.int8).to(C.dev) for _ in range(8)]
+        sc = (torch.rand(K, generator=g) * 0.01 + 0.001).to(C.dev)
+        wb = [datagen.normal((K, N), 900 + K).to(C.dev)] * 1
+        wb = wb + [wb[0].clone() for _ in range(7)]
+        xs = datagen.student_t((16, K), datagen.seed_for(8, 0, K)).to(C.dev)
+        t = float(asg.as_calibrate_threshold(xs, 0.5).item())
+        Y = torch.empty((N,), dtype=torch.float32, device=C.dev)
+        Y2 = torch.empty((1, N), dtype=torch.float32, device=C.dev)
+        fi = [lambda i=i: asg.as_threshold_gemv_i8(xs[i % 16], qs[i % 8], sc, t, Y=Y) for i in range(24)]
+        fb = [lambda i=i: asg.as_threshold_gemv(xs[i % 16:i % 16 + 1], wb[i % 8], t, Y=Y2) for i in range(24)]
+        fd = [lambda i=i: asg.as_dense_gemv(xs[i % 16:i % 16 + 1], wb[i % 8], Y=Y2) for i in range(24)]
+        ui, ub, ud = C.graph_us(fi), C.graph_us(fb), C.graph_us(fd)
+        kept = float((xs.float().abs() > t).sum(dim=1).float().mean().item())
+        ab8 = kept * N
+        out["points"].append({"K": K, "N": N, "sparsity": 0.5, "kept_rows_mean": r4(kept),
+                              "int8_us": r4(ui), "bf16_sparse_us": r4(ub), "bf16_dense_us": r4(ud),
+                              "int8_gbs": r4(ab8 / (ui * 1e-6) / 1e9), "int8_frac_hbm": r4(ab8 / (ui * 1e-6) / 8e12),
+                              "speedup_vs_bf16_sparse": r4(ub / ui), "speedup_vs_bf16_dense": r4(ud / ui)})
+        del qs, wb
+        torch.cuda.empty_cache()
     return out
 
 
@@ -932,6 +967,7 @@ def main():
                          ("a6_topk", lambda: row_topk(C, cpu)), ("a7_glass", lambda: row_glass(C, cpu)),
                          ("next1_gate_score", lambda: row_gate(C, cpu)),
                          ("next4_greedy", lambda: row_greedy(C, cpu)),
+                         ("next4_int8", lambda: row_int8(C, cpu)),
                          ("a8_a9_moe", lambda: row_moe(C, cpu)),
                          ("a10_batch16_mfma", lambda: row_batch16(C, cpu, t_x, t_h)),
                          ("a11_block", lambda: row_block(C, cpu)), ("small_mlp_fp16", lambda: row_small(C, cpu))):

@@ -68,7 +68,7 @@ typedef enum {
   AS_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed          */
 } as_status;
 
-typedef enum { AS_F16 = 0, AS_BF16 = 1, AS_F32 = 2 } as_dtype;
+typedef enum { AS_F16 = 0, AS_BF16 = 1, AS_F32 = 2, AS_I8 = 3 } as_dtype;   /* AS_I8: as_threshold_gemv_i8 weights only */
 
 enum {
   AS_FLAG_ACCUMULATE = 1u << 0,   /* Y += result instead of Y = result                   */
@@ -142,6 +142,22 @@ as_status as_threshold_gemv(const void *X, as_dtype x_dt, int M, int K,
                             const void *W, as_dtype w_dt, int N, float t,
                             void *Y, as_dtype y_dt, unsigned flags, as_mask_out *mask_out,
                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Sparse GEMV over int8 weight rows with a per-row scale (attribution notes,
+ * discussion: activation sparsity combined with weight quantization such as W8A8
+ * or INT4 compounds the byte savings):
+ *   Y[0, :] = sum over i with |X[0, i]| > t of X[0, i] * row_scale[i] * W[i, :]
+ * One token.  X: [K] (f16/bf16/f32, 16-byte aligned, K % 8 == 0); W: [K, N] int8
+ * input-major (16-byte aligned, N % 8 == 0); row_scale: [K] fp32 (16-byte aligned);
+ * Y: [N] (f16/bf16/f32).  The mask is on X, not on X * row_scale.  Each kept row
+ * reads N bytes instead of 2N.  Flags as
+ * for as_threshold_gemv (AS_FLAG_FORCE_DENSE: every row).  Errors: INVALID_ARG for
+ * NULL or misaligned pointers or a bad N; UNSUPPORTED for an unaligned X or K % 8.
+ * ws: as_threshold_gemv_i8_ws_size(K, N) bytes (zero-filled once, left zeroed). */
+size_t as_threshold_gemv_i8_ws_size(int K, int N);
+as_status as_threshold_gemv_i8(const void *X, as_dtype x_dt, int K, const int8_t *W, const float *row_scale,
+                               int N, float t, void *Y, as_dtype y_dt, unsigned flags,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Dense GEMV baseline Y = X W over every row (the speedup denominator): the
  * same kernel and launch shape as as_threshold_gemv without the mask. */
