@@ -108,6 +108,12 @@ SIGNATURES = {
     "as_bench_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "as_greedy_sparsity": (c_int, [c_void_p, c_int, c_int, c_void_p, ctypes.c_double, ctypes.c_double, c_void_p]),
     "as_threshold_gemv_i8_ws_size": (c_size_t, [c_int, c_int]),
+    "as_corrected_gxo": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p]),
+    "as_top_fraction_count": (c_int, [c_int, c_int, c_int]),
+    "as_select_top_fraction": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "as_head_masked_gemv_ws_size": (c_size_t, [c_int, c_int, c_int]),
+    "as_head_masked_gemv": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_int, c_int,
+                                    c_void_p, c_int, c_uint, c_void_p, c_size_t, c_void_p]),
     "as_threshold_gemv_i8": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_float, c_void_p, c_int,
                                      c_uint, c_void_p, c_size_t, c_void_p]),
 }

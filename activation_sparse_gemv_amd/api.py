@@ -630,3 +630,49 @@ def as_threshold_gemv_i8(X: torch.Tensor, Wq: torch.Tensor, row_scale: torch.Ten
     L.check(lib.as_threshold_gemv_i8(_ptr(x), _dt(x), K, _ptr(Wq), _ptr(row_scale), N, float(t), _ptr(Y), _dt(Y),
                                      flags, _ptr(ws), ws.numel(), _stream(X.device)), "as_threshold_gemv_i8")
     return Y
+
+
+def as_corrected_gxo(x: torch.Tensor, grad: torch.Tensor) -> torch.Tensor:
+    """Corrected GxO attribution score per row (layer): grad*x + |x| * ||grad|| / 2."""
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    g2 = grad.reshape(x2.shape)
+    _need_cuda(x2, g2)
+    if x2.dtype != torch.float32 or g2.dtype != torch.float32:
+        raise ValueError("x and grad must be float32")
+    out = torch.empty_like(x2)
+    L.check(L.load().as_corrected_gxo(_ptr(x2), _ptr(g2), x2.shape[0], x2.shape[1], _ptr(out), _stream(x.device)),
+            "as_corrected_gxo")
+    return out
+
+
+def as_select_top_fraction(score: torch.Tensor, ar_num: int, ar_den: int):
+    """Per-row top fraction ar_num/ar_den of the scores: (bitmask [rows, words], idx [rows, k])."""
+    s2 = score.reshape(1, -1) if score.dim() == 1 else score
+    _need_cuda(s2)
+    rows, n = s2.shape
+    lib = L.load()
+    k = lib.as_top_fraction_count(n, int(ar_num), int(ar_den))
+    if k < 0:
+        raise ValueError(f"ratio {ar_num}/{ar_den} outside [0, 1]")
+    mask = torch.zeros((rows, (n + 63) // 64), dtype=torch.int64, device=score.device)
+    idx = torch.zeros((rows, max(k, 1)), dtype=torch.int32, device=score.device)
+    L.check(lib.as_select_top_fraction(_ptr(s2), rows, n, int(ar_num), int(ar_den), _ptr(mask), _ptr(idx),
+                                       _stream(score.device)), "as_select_top_fraction")
+    return mask, idx[:, :k]
+
+
+def as_head_masked_gemv(X: torch.Tensor, W: torch.Tensor, heads: torch.Tensor, n_heads: int, head_dim: int,
+                        y_dtype=torch.float32, flags: int = 0, Y: torch.Tensor | None = None):
+    """One token's output projection over the listed heads' row blocks of W."""
+    x = X.reshape(-1)
+    _need_cuda(x, W, heads, Y)
+    N = W.shape[1]
+    if Y is None:
+        Y = torch.empty((N,), dtype=y_dtype, device=X.device)
+    lib = L.load()
+    nb = lib.as_head_masked_gemv_ws_size(n_heads, head_dim, N)
+    ws = workspace(("head_gemv", n_heads, head_dim, N), nb, X.device)
+    L.check(lib.as_head_masked_gemv(_ptr(x), _dt(x), n_heads, head_dim, _ptr(heads), heads.numel(), _ptr(W), _dt(W),
+                                    N, _ptr(Y), _dt(Y), flags, _ptr(ws), ws.numel(), _stream(X.device)),
+            "as_head_masked_gemv")
+    return Y

@@ -361,7 +361,8 @@ static bool can_norm_in_prologue(const void* X, as_dtype x_dt, int K) {
 static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N,
                              float t, void* Y, as_dtype y_dt, unsigned flags, as_mask_out* mo, void* ws,
                              size_t ws_bytes, hipStream_t stream, bool dense, const char* fn,
-                             const GemvFuse* fz = nullptr, const float* row_scale = nullptr) {
+                             const GemvFuse* fz = nullptr, const float* row_scale = nullptr,
+                             const int32_t* heads = nullptr, int n_keep = 0, int head_dim = 0) {
   if (!X || !W || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, W or Y", fn);
   const bool i8 = w_dt == AS_I8;
   if (!is_dt(x_dt) || !(is_wdt(w_dt) || i8) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
@@ -413,6 +414,10 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   p.partials = gw.partials; p.counters = gw.counters; p.part_ld = N;
   p.y = Y; p.y_dt = int(y_dt); p.ldy = N; p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   p.row_scale = row_scale;
+  if (head_dim > 0) {
+    // every input of a listed head is kept (zeros and NaN too), no other row
+    p.heads = heads; p.n_heads_keep = n_keep; p.head_dim = head_dim; p.n_heads = K / head_dim; p.keep_all = 1;
+  }
   if (mo && !dense) {
     p.x_bits = mo->bits; p.x_bits_ld = (K + 63) / 64; p.x_idx = mo->idx; p.x_nnz = mo->nnz;
   }
@@ -705,6 +710,55 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
 #endif
   if ((st = hip_check(launch_gather_gemv(c2, p2, stream), fn)) != AS_OK) return st;
   return rec(2);
+}
+
+// ------------------------------------------------------------------ attribution selection
+as_status as_corrected_gxo(const float* x, const float* grad, int rows, int n, float* score, hipStream_t stream) {
+  const char* fn = "as_corrected_gxo";
+  if (!x || !grad || !score) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (rows < 1 || n < 1) return fail(AS_ERR_INVALID_ARG, "%s: rows=%d n=%d", fn, rows, n);
+  return hip_check(launch_corrected_gxo(x, grad, rows, n, score, stream), fn);
+}
+
+int as_top_fraction_count(int n, int ar_num, int ar_den) {
+  if (n < 0 || ar_den <= 0 || ar_num < 0 || ar_num > ar_den) return -1;
+  const unsigned __int128 a = (unsigned __int128)(unsigned)ar_num * (unsigned)n;
+  return (int)((a + (unsigned)ar_den - 1) / (unsigned)ar_den);
+}
+
+as_status as_select_top_fraction(const float* score, int rows, int n, int ar_num, int ar_den, uint64_t* mask,
+                                 int32_t* idx, hipStream_t stream) {
+  const char* fn = "as_select_top_fraction";
+  if (!score) return fail(AS_ERR_INVALID_ARG, "%s: score is NULL", fn);
+  if (!mask && !idx) return fail(AS_ERR_INVALID_ARG, "%s: both outputs are NULL", fn);
+  if (rows < 1 || n < 1) return fail(AS_ERR_INVALID_ARG, "%s: rows=%d n=%d", fn, rows, n);
+  const int k = as_top_fraction_count(n, ar_num, ar_den);
+  if (k < 0) return fail(AS_ERR_INVALID_ARG, "%s: ratio %d/%d outside [0, 1]", fn, ar_num, ar_den);
+  return hip_check(launch_topk_value(score, rows, n, k, mask, idx, stream), fn);
+}
+
+size_t as_head_masked_gemv_ws_size(int n_heads, int head_dim, int N) {
+  if (n_heads < 1 || head_dim < 1 || N < 1) return 0;
+  return as_threshold_gemv_ws_size(1, n_heads * head_dim, N);
+}
+
+as_status as_head_masked_gemv(const void* X, as_dtype x_dt, int n_heads, int head_dim, const int32_t* heads,
+                              int n_keep, const void* W, as_dtype w_dt, int N, void* Y, as_dtype y_dt,
+                              unsigned flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "as_head_masked_gemv";
+  if (!X || !W || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, W or Y", fn);
+  if (n_heads < 1 || n_heads > 1024 || head_dim < 1) return fail(AS_ERR_INVALID_ARG, "%s: n_heads=%d head_dim=%d", fn, n_heads, head_dim);
+  if (n_keep < 0 || n_keep > n_heads || (n_keep > 0 && !heads)) return fail(AS_ERR_INVALID_ARG, "%s: n_keep=%d", fn, n_keep);
+  if (!is_dt(x_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad x dtype", fn);
+  if (flags & (AS_FLAG_FORCE_DENSE | AS_FLAG_ACCUMULATE))
+    return fail(AS_ERR_UNSUPPORTED, "%s: flags other than AS_FLAG_ATOMIC_SPLITK / AS_FLAG_NO_NT_LOADS", fn);
+  const int K = n_heads * head_dim;
+  if (!aligned16(X) || (K % 8) != 0)
+    return fail(AS_ERR_UNSUPPORTED, "%s: needs a 16-byte aligned X and n_heads * head_dim %% 8 == 0", fn);
+  // one launch: every slice masks its range of X by the head list (t = -inf: all of
+  // a kept head's inputs, zeros and NaN included) and reads only the kept rows
+  return gemv_common(X, x_dt, 1, K, W, w_dt, N, -INFINITY, Y, y_dt, flags, nullptr, ws, ws_bytes, stream, false,
+                     fn, nullptr, nullptr, heads, n_keep, head_dim);
 }
 
 // ------------------------------------------------------------------ greedy allocation

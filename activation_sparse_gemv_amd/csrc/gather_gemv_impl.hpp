@@ -327,7 +327,8 @@ __device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s
 template <int MT, int NV, bool WDT_SCALED = false>
 __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i1, bool split, int sl, int S,
                                               int* s_idx, float* s_val, int cap, int* s_scan, int* lo_out,
-                                              bool export_xn, float* inv_out) {
+                                              bool export_xn, float* inv_out,
+                                              const unsigned char* head_on = nullptr) {
   const int tid = threadIdx.x;
   const int M = p.M;
   const float t = p.t;
@@ -377,6 +378,13 @@ __device__ __forceinline__ int compact_chunks(const GemvParams& p, int i0, int i
     const bool keep_all = p.keep_all != 0;
 #pragma unroll
     for (int e = 0; e < CEV; ++e) ubits |= (uint64_t)(e < n && (keep_all || fabsf(v0[e]) > t)) << e;
+    if (p.head_dim > 0) {
+      // only rows of the listed heads
+      uint64_t hb = 0;
+#pragma unroll
+      for (int e = 0; e < CEV; ++e) hb |= (uint64_t)(e < n && head_on[(c0 + e) / p.head_dim]) << e;
+      ubits &= hb;
+    }
     c = __popcll(ubits);
     if constexpr (WDT_SCALED) {
       // int8 rows: the kept value is x_i * row_scale[i] (the mask stays on x)
@@ -852,6 +860,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
   (void)n_lt;
   __shared__ int s_scan[kThreads / 64 + 1];
   __shared__ int s_flag;
+  __shared__ unsigned char s_head_on[MT == 1 ? 1024 : 1];
 
   const int tid = threadIdx.x;
   const int S = p.S;
@@ -864,6 +873,18 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     // IN_THRESH: the whole input, split into S equal parts of the compacted list.
     // IN_RANGE: slice sl owns the inputs of its 64-aligned range and keeps all of them.
     const bool split = IN == IN_THRESH;
+    if constexpr (MT == 1) {
+      if (p.head_dim > 0) {
+        // head mask: the listed heads' flags in LDS before the range is masked
+        for (int h = tid; h < p.n_heads; h += kThreads) s_head_on[h] = 0;
+        __syncthreads();
+        for (int q = tid; q < p.n_heads_keep; q += kThreads) {
+          const int h = p.heads[q];
+          if (h >= 0 && h < p.n_heads) s_head_on[h] = 1;
+        }
+        __syncthreads();
+      }
+    }
     int r0 = 0, r1 = p.K;
     if (!split) {
       const int units = (p.K + 63) / 64;
@@ -878,7 +899,7 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
                 : compact_range_staged<MT, NV>(p, r0, r1, s_idx, s_val, cap, reinterpret_cast<float*>(s_w), s_scan);
     else
       cnt = compact_chunks<MT, NV, WDT == DT_I8>(p, r0, r1, split, sl, S, s_idx, s_val, cap, s_scan, &lo,
-                                                 tile == 0 && sl == 0, &inv_scale);
+                                                 tile == 0 && sl == 0, &inv_scale, s_head_on);
     if (split && (p.x_bits != nullptr || p.x_nnz != nullptr || p.x_idx != nullptr))
       thresh_exports<MT>(p, s_idx, s_scan, tid, tile, lo, cnt, tile == 0 && sl == 0, inv_scale);
   } else if constexpr (IN == IN_PARTS) {

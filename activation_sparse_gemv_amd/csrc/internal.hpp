@@ -67,6 +67,10 @@ struct GemvParams {
   unsigned long long* phase_tl;
   // int8 weights (DT_I8): row i is W[i, :] * row_scale[i] (fp32, K entries)
   const float* row_scale;
+  // head mask (IN_RANGE / IN_THRESH, one token; on when head_dim > 0): only rows of
+  // the listed heads (row i belongs to head i / head_dim) are kept, besides the
+  // threshold
+  const int* heads; int n_heads_keep; int head_dim; int n_heads;
 };
 
 struct GemvConfig {
@@ -181,6 +185,7 @@ as_status report_error(as_status s, const char* msg);
 
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_corrected_gxo(const float* x, const float* g, int rows, int n, float* score, hipStream_t s);
 hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_read_probe(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t s);
 size_t calibrate_ws_bytes();

@@ -195,4 +195,33 @@ hipError_t launch_calibrate(const void* pool, int dt, int64_t n, int64_t rank, f
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- attribution scores
+// Corrected GxO (attribution notes, correction term): per row (layer),
+// score_i = grad_i * x_i + 1/2 |x_i| * ||grad||_2.  One workgroup per row: the
+// squared gradient is summed per thread over a fixed stride, then per wave, then
+// the four wave sums in wave order (the same bits on every call).
+constexpr int kGxoThreads = 256;
+__global__ __launch_bounds__(kGxoThreads) void corrected_gxo_kernel(const float* x, const float* g, int n,
+                                                                    float* score) {
+  __shared__ float s_w[kGxoThreads / 64];
+  const long r = blockIdx.x;
+  const float* xr = x + r * n;
+  const float* gr = g + r * n;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n; i += kGxoThreads) ss = fmaf(gr[i], gr[i], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kGxoThreads / 64; ++w) tot += s_w[w];
+  const float half_norm = 0.5f * sqrtf(tot);
+  for (int i = threadIdx.x; i < n; i += kGxoThreads) score[r * n + i] = fmaf(gr[i], xr[i], fabsf(xr[i]) * half_norm);
+}
+
+hipError_t launch_corrected_gxo(const float* x, const float* g, int rows, int n, float* score, hipStream_t s) {
+  hipLaunchKernelGGL(corrected_gxo_kernel, dim3(rows), dim3(kGxoThreads), 0, s, x, g, n, score);
+  return hipGetLastError();
+}
+
 }  // namespace as

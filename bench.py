@@ -664,6 +664,39 @@ def row_int8(C, cpu):
     return out
 
 
+def row_attrib(C, cpu):
+    """NEXT-3: external-score selection (Corrected GxO -> per-layer top fraction) and
+    the head-masked output projection."""
+    torch, asg, L, datagen = C.torch, C.asg, C.L, C.datagen
+    nh, hd, N = 32, 128, 4096
+    K = nh * hd
+    Ws = [datagen.normal((K, N), 950).to(C.dev)]
+    Ws += [Ws[0].clone() for _ in range(31)]            # 32 copies (1 GiB)
+    xs = datagen.student_t((16, K), 951).to(C.dev)
+    Y = torch.empty((N,), dtype=torch.float32, device=C.dev)
+    Y2 = torch.empty((1, N), dtype=torch.float32, device=C.dev)
+    fd = [lambda i=i: asg.as_dense_gemv(xs[i % 16:i % 16 + 1], Ws[i % 32], Y=Y2) for i in range(64)]
+    ud = C.graph_us(fd)
+    out = {"step": "NEXT-3 attribution selection: Corrected GxO scores (32 layers x 14336), per-layer top "
+                   "fraction, and the o-proj over the kept heads' 128-row blocks (32 heads, 4096 -> 4096, bf16)",
+           "o_proj_dense_us": r4(ud), "points": []}
+    for kept in (24, 16, 8):
+        heads = torch.arange(0, 32, 32 // kept, dtype=torch.int32, device=C.dev)[:kept].contiguous()
+        fh = [lambda i=i: asg.as_head_masked_gemv(xs[i % 16], Ws[i % 32], heads, nh, hd, Y=Y) for i in range(64)]
+        uh = C.graph_us(fh)
+        ab = kept * hd * N * 2
+        out["points"].append({"heads_kept": kept, "us": r4(uh), "speedup_vs_dense": r4(ud / uh),
+                              "active_mb": r4(ab / 1e6), "gbs": r4(ab / (uh * 1e-6) / 1e9)})
+    x = datagen.student_t((32, 14336), 952, dtype="f32").to(C.dev)
+    g = datagen.normal((32, 14336), 953, std=1e-3, dtype="f32").to(C.dev)
+    out["gxo_us_32x14336"] = r4(C.graph_us([lambda: asg.as_corrected_gxo(x, g)] * 8))
+    sc = asg.as_corrected_gxo(x, g)
+    out["top_fraction_us_32x14336_ratio_0.4"] = r4(C.graph_us([lambda: asg.as_select_top_fraction(sc, 2, 5)] * 8))
+    del Ws
+    torch.cuda.empty_cache()
+    return out
+
+
 class _LazyF64:
     """Index-on-demand fp64 view of a stacked bf16 expert tensor (oracle sample only)."""
 
@@ -968,6 +1001,7 @@ def main():
                          ("next1_gate_score", lambda: row_gate(C, cpu)),
                          ("next4_greedy", lambda: row_greedy(C, cpu)),
                          ("next4_int8", lambda: row_int8(C, cpu)),
+                         ("next3_attribution", lambda: row_attrib(C, cpu)),
                          ("a8_a9_moe", lambda: row_moe(C, cpu)),
                          ("a10_batch16_mfma", lambda: row_batch16(C, cpu, t_x, t_h)),
                          ("a11_block", lambda: row_block(C, cpu)), ("small_mlp_fp16", lambda: row_small(C, cpu))):

@@ -385,6 +385,56 @@ as_status as_moe_layer(const void *X, as_dtype x_dt, int T, const as_moe_layer_w
                        float *h_dbg, int32_t *keep_dbg,
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------ attribution-based selection
+ * Attribution notes (Attribution-based Sparse Activation in LLMs): neurons are
+ * ranked by an attribution score rather than by their output magnitude, and each
+ * layer keeps a fixed fraction of its neurons (Approach 1); in attention the
+ * neuron is a head.  The scores come from outside the decode path (a backward pass
+ * on representative data, or a predictor trained on it); the calls below turn them
+ * into kept sets and use those sets. */
+
+/* Corrected GxO score (attribution notes, correction term), per row (layer):
+ *   score[r, i] = grad[r, i] * x[r, i] + 0.5 * |x[r, i]| * sqrt(sum_k grad[r, k]^2)
+ * x, grad, score: device [rows, n] fp32.  The squared-gradient sum is formed in a
+ * fixed order (the same bits on every call).  Errors: INVALID_ARG for NULL
+ * pointers, rows < 1 or n < 1. */
+as_status as_corrected_gxo(const float *x, const float *grad, int rows, int n, float *score,
+                           hipStream_t stream);
+
+/* Number of neurons a layer of n keeps at activation ratio ar_num / ar_den:
+ * ceil(ar_num * n / ar_den), computed exactly; -1 for n < 0, ar_den <= 0 or a
+ * ratio outside [0, 1]. */
+int as_top_fraction_count(int n, int ar_num, int ar_den);
+
+/* Approach 1: per row (layer), the k = as_top_fraction_count(n, ar_num, ar_den)
+ * neurons with the largest score[r, :] (by value: a negative attribution ranks
+ * lowest; ties to the smaller index; NaN ranks below every number), as a bitmask
+ * [rows, ceil(n/64)] and/or ascending indices [rows, k] (either output nullable).
+ * The kept indices feed AS_MLP_NEURON_SET (MLP neurons) or as_head_masked_gemv
+ * (attention heads).  Errors: INVALID_ARG for NULL score or both outputs NULL,
+ * rows < 1, n < 1, a ratio outside [0, 1]. */
+as_status as_select_top_fraction(const float *score, int rows, int n, int ar_num, int ar_den,
+                                 uint64_t *mask, int32_t *idx, hipStream_t stream);
+
+/* Output projection over the kept heads only (attribution notes: a deactivated
+ * head's weights are zeroed; here its head_dim-row block of W is not read):
+ *   Y[0, :] = sum over listed heads h of X[h*hd .. h*hd+hd) W[h*hd .. h*hd+hd, :]
+ * One token.  X: [n_heads * head_dim] (f16/bf16/f32); heads: device int32 [n_keep]
+ * (indices outside [0, n_heads) are ignored, repeats count once); W: [n_heads *
+ * head_dim, N] input-major (f16/bf16, 16-byte aligned, N % 8 == 0); Y: [N].  One
+ * launch: each row slice marks the listed heads in LDS and gathers only their
+ * rows (every input of a kept head counts, zeros and NaN included).
+ * ws: as_head_masked_gemv_ws_size bytes, zero-filled once.  flags:
+ * AS_FLAG_ATOMIC_SPLITK, AS_FLAG_NO_NT_LOADS (others UNSUPPORTED).
+ * Errors: INVALID_ARG for NULL pointers, n_heads outside 1..1024, n_keep outside
+ * 0..n_heads, bad dtypes or N; UNSUPPORTED for an X not 16-byte aligned or
+ * n_heads * head_dim not a multiple of 8. */
+size_t as_head_masked_gemv_ws_size(int n_heads, int head_dim, int N);
+as_status as_head_masked_gemv(const void *X, as_dtype x_dt, int n_heads, int head_dim,
+                              const int32_t *heads, int n_keep, const void *W, as_dtype w_dt, int N,
+                              void *Y, as_dtype y_dt, unsigned flags, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* ------------------------------------------------------------ offline sparsity allocation
  * Block-wise greedy sparsity allocation (TEAL slides, slide 10): under a
  * model-wide sparsity target, every block starts at sparsity 0 and, one step at

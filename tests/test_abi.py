@@ -291,3 +291,23 @@ def test_greedy_sparsity_matches_the_oracle(lib):
     assert lib.as_greedy_sparsity(p, 2, 3, wbad.ctypes.data, 0.1, 0.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
     enan = np.array([[0.0, np.nan, 1.0], [0.0, 1.0, 2.0]])
     assert lib.as_greedy_sparsity(enan.ctypes.data, 2, 3, wv.ctypes.data, 0.1, 0.5, lv.ctypes.data) == L.AS_ERR_INVALID_ARG
+
+
+def test_attribution_selection_validation(lib):
+    assert lib.as_top_fraction_count(10, 3, 10) == 3
+    assert lib.as_top_fraction_count(10, 31, 100) == 4
+    assert lib.as_top_fraction_count(14336, 2, 5) == 5735
+    assert lib.as_top_fraction_count(7, 0, 1) == 0 and lib.as_top_fraction_count(7, 1, 1) == 7
+    assert lib.as_top_fraction_count(7, 2, 1) == -1 and lib.as_top_fraction_count(7, 1, 0) == -1
+    assert lib.as_top_fraction_count(2**31 - 1, 2**31 - 2, 2**31 - 1) == 2**31 - 2
+    assert lib.as_corrected_gxo(None, _p(), 1, 4, _p(), None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_corrected_gxo(_p(), _p(), 0, 4, _p(), None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_select_top_fraction(_p(), 1, 10, 3, 2, _p(), None, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_select_top_fraction(_p(), 1, 10, 1, 2, None, None, None) == L.AS_ERR_INVALID_ARG
+    assert lib.as_head_masked_gemv_ws_size(32, 128, 4096) > 32 * 128 * 4
+    st = lib.as_head_masked_gemv(_p(), L.AS_BF16, 32, 128, _p(), 33, _p(), L.AS_BF16, 4096, _p(), L.AS_F32, 0,
+                                 _p(), 1 << 30, None)
+    assert st == L.AS_ERR_INVALID_ARG
+    st = lib.as_head_masked_gemv(_p(), L.AS_BF16, 32, 128, _p(), 8, _p(), L.AS_BF16, 4096, _p(), L.AS_F32,
+                                 L.AS_FLAG_FORCE_DENSE, _p(), 1 << 30, None)
+    assert st == L.AS_ERR_UNSUPPORTED
