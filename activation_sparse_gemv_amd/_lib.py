@@ -18,6 +18,8 @@ AS_FLAG_ATOMIC_SPLITK = 1 << 1
 AS_FLAG_NO_NT_LOADS = 1 << 2
 AS_FLAG_FORCE_DENSE = 1 << 3
 AS_FLAG_NO_FUSION = 1 << 4
+AS_FLAG_AUTO = 1 << 5
+AS_AUTO_DENSE_MIN_TOKENS = 8
 AS_MLP_THRESHOLD, AS_MLP_NEURON_SET, AS_MLP_GATE_SCORE = 0, 1, 2
 AS_TOPK_VALUE, AS_TOPK_RANK_BLEND = 0, 1
 
@@ -108,6 +110,7 @@ SIGNATURES = {
     "as_bench_read": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "as_greedy_sparsity": (c_int, [c_void_p, c_int, c_int, c_void_p, ctypes.c_double, ctypes.c_double, c_void_p]),
     "as_threshold_gemv_i8_ws_size": (c_size_t, [c_int, c_int]),
+    "as_pack_neuron_set": (c_int, [POINTER(ASMlpWeights), c_void_p, c_int, c_void_p, c_void_p, c_void_p]),
     "as_corrected_gxo": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p]),
     "as_top_fraction_count": (c_int, [c_int, c_int, c_int]),
     "as_select_top_fraction": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]),

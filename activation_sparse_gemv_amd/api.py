@@ -676,3 +676,20 @@ def as_head_masked_gemv(X: torch.Tensor, W: torch.Tensor, heads: torch.Tensor, n
                                     N, _ptr(Y), _dt(Y), flags, _ptr(ws), ws.numel(), _stream(X.device)),
             "as_head_masked_gemv")
     return Y
+
+
+def as_pack_neuron_set(w: MLPWeights, idx: torch.Tensor) -> MLPWeights:
+    """Compact THRESHOLD-layout copy of the neurons idx (int32, device): gate/up
+    [d_model, 2, k] and down [k, d_model]; run it with AS_FLAG_FORCE_DENSE for the
+    static-set SwiGLU of a batch."""
+    if w.mode != L.AS_MLP_THRESHOLD:
+        raise ValueError("pack from THRESHOLD-layout weights")
+    idx = idx.reshape(-1).contiguous()
+    _need_cuda(w.w_gate_up, w.w_down, idx)
+    k = idx.numel()
+    gu = torch.empty((w.d_model, 2, k), dtype=w.w_gate_up.dtype, device=idx.device)
+    dn = torch.empty((k, w.d_model), dtype=w.w_down.dtype, device=idx.device)
+    ws_ = w.struct()
+    L.check(L.load().as_pack_neuron_set(ctypes.byref(ws_), _ptr(idx), k, _ptr(gu), _ptr(dn), _stream(idx.device)),
+            "as_pack_neuron_set")
+    return MLPWeights(gu, dn, L.AS_MLP_THRESHOLD)

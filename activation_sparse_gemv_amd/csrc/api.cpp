@@ -490,6 +490,11 @@ static as_status check_mlp_weights(const as_mlp_weights* w, as_mlp_mode mode, co
 
 size_t as_sparse_swiglu_mlp_ws_size(int M, const as_mlp_weights* w, as_mlp_mode mode) {
   if (M < 1 || !w || w->d_model < 1 || w->d_ff < 1) return 0;
+  if (M > 16 && mode == AS_MLP_THRESHOLD) {
+    // groups of 16 tokens: one region for the full groups, one for a partial last group
+    const size_t full = up256(as_sparse_swiglu_mlp_ws_size(16, w, mode));
+    return M % 16 ? full + as_sparse_swiglu_mlp_ws_size(M % 16, w, mode) : full;
+  }
   const MlpPlan mp = plan_mlp(M, w, mode, false);
   Carver c{nullptr};
   carve_mlp(c, mp, M, w, mode);
@@ -517,8 +522,52 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
                                float t_x, float t_h, const int32_t* neuron_idx, int n_active, void* Y,
                                as_dtype y_dt, unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
+  const char* fn = "as_sparse_swiglu_mlp";
+  if (flags & AS_FLAG_AUTO) {
+    if (mode != AS_MLP_THRESHOLD) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_AUTO is for THRESHOLD mode", fn);
+    flags &= ~unsigned(AS_FLAG_AUTO);
+    if (M >= AS_AUTO_DENSE_MIN_TOKENS) flags |= AS_FLAG_FORCE_DENSE;
+  }
+  if (M > 16 && mode == AS_MLP_THRESHOLD) {
+    // consecutive groups of 16 tokens on one stream, each a call of its own (the
+    // workspace is reused in stream order; every call leaves its counters at zero)
+    if (M > 256) return fail(AS_ERR_UNSUPPORTED, "%s: M=%d above 256", fn, M);
+    if (dbg) return fail(AS_ERR_UNSUPPORTED, "%s: debug exports take at most 16 tokens", fn);
+    if (!X || !Y || !w) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, Y or weights", fn);
+    if (!is_dt(x_dt) || !is_dt(y_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
+    const size_t xr = size_t(w->d_model) * dt_bytes(x_dt), yr = size_t(w->d_model) * dt_bytes(y_dt);
+    // the full groups use the first region of the workspace and a partial last group
+    // its own second region, so each region always holds one carve-up
+    const size_t ws16 = up256(as_sparse_swiglu_mlp_ws_size(16, w, mode));
+    if (ws_bytes < as_sparse_swiglu_mlp_ws_size(M, w, mode))
+      return fail(AS_ERR_WORKSPACE, "%s: workspace too small for %d tokens", fn, M);
+    for (int m0 = 0; m0 < M; m0 += 16) {
+      const int mg = M - m0 < 16 ? M - m0 : 16;
+      char* wsg = reinterpret_cast<char*>(ws) + (mg == 16 ? 0 : ws16);
+      const size_t wsb = mg == 16 ? ws16 : ws_bytes - ws16;
+      const as_status st = mlp_impl(reinterpret_cast<const char*>(X) + m0 * xr, x_dt, mg, w, mode, t_x, t_h,
+                                    neuron_idx, n_active, reinterpret_cast<char*>(Y) + m0 * yr, y_dt, flags, nullptr,
+                                    wsg, wsb, stream, nullptr);
+      if (st != AS_OK) return st;
+    }
+    return AS_OK;
+  }
   return mlp_impl(X, x_dt, M, w, mode, t_x, t_h, neuron_idx, n_active, Y, y_dt, flags, dbg, ws, ws_bytes, stream,
                   nullptr);
+}
+
+as_status as_pack_neuron_set(const as_mlp_weights* w, const int32_t* idx, int k, void* gate_up_out,
+                             void* down_out, hipStream_t stream) {
+  const char* fn = "as_pack_neuron_set";
+  as_status st = check_mlp_weights(w, AS_MLP_THRESHOLD, fn);
+  if (st != AS_OK) return st;
+  if (!idx || !gate_up_out || !down_out) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (k < 64 || k % 64 != 0 || k > w->d_ff) return fail(AS_ERR_INVALID_ARG, "%s: k=%d (multiple of 64, <= d_ff)", fn, k);
+  if (!aligned16(gate_up_out) || !aligned16(down_out)) return fail(AS_ERR_INVALID_ARG, "%s: outputs not 16-byte aligned", fn);
+  return hip_check(launch_pack_neuron_set(reinterpret_cast<const uint16_t*>(w->w_gate_up),
+                                          reinterpret_cast<const uint16_t*>(w->w_down), w->d_model, w->d_ff, idx, k,
+                                          reinterpret_cast<uint16_t*>(gate_up_out),
+                                          reinterpret_cast<uint16_t*>(down_out), stream), fn);
 }
 
 // fz (nullable): the input normalised in the gate/up prologue and/or a residual

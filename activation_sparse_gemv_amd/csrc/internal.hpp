@@ -185,6 +185,8 @@ as_status report_error(as_status s, const char* msg);
 
 // Misc kernels.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_pack_neuron_set(const uint16_t* gu, const uint16_t* dn, int d, int f, const int* idx, int k,
+                                  uint16_t* gu_out, uint16_t* dn_out, hipStream_t s);
 hipError_t launch_corrected_gxo(const float* x, const float* g, int rows, int n, float* score, hipStream_t s);
 hipError_t launch_fill_pattern(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_read_probe(const void* p, size_t bytes, unsigned* sink, int cus, hipStream_t s);

@@ -697,6 +697,46 @@ def row_attrib(C, cpu):
     return out
 
 
+def row_batch_static(C, cpu):
+    """NEXT-2: batched decode with a static neuron set (compact packed weights) and the
+    batch-size switch between the sparse and dense threshold paths."""
+    torch, asg, L, datagen = C.torch, C.asg, C.L, C.datagen
+    d, f, k = 4096, 14336, 7168
+    wgu, wd = datagen.mlp_weights_input_major(10, 0, datagen.MLPShape(d, f, "bf16"))
+    full = [asg.MLPWeights(wgu.to(C.dev), wd.to(C.dev))]
+    full += [asg.MLPWeights(full[0].w_gate_up.clone(), full[0].w_down.clone()) for _ in range(3)]
+    del wgu, wd
+    idx = torch.from_numpy(np.sort(np.random.default_rng(0).choice(f, k, replace=False)).astype(np.int32)).to(C.dev)
+    packed = [asg.as_pack_neuron_set(w, idx) for w in full]
+    torch.cuda.synchronize()
+    out = {"step": "NEXT-2 static neuron set for a batch: the kept 7168 of 14336 neurons packed once into compact "
+                   "input-major matrices (as_pack_neuron_set), then the dense SwiGLU on them for 1..64 tokens, "
+                   "vs the dense SwiGLU on the full matrices; and the threshold path's batch-size switch",
+           "shape": "d_model 4096, d_ff 14336 -> 7168 kept, bf16; four weight copies rotate (1.4 GB full, 0.7 GB packed)",
+           "points": [], "switch": []}
+    for M in (1, 8, 16, 32, 64):
+        X = datagen.student_t((M, d), 960 + M).to(C.dev)
+        Y = torch.empty((M, d), dtype=torch.float32, device=C.dev)
+        fp = [lambda w=w: asg.as_sparse_swiglu_mlp(X, w, flags=L.AS_FLAG_FORCE_DENSE, Y=Y) for w in packed * 3]
+        ff = [lambda w=w: asg.as_sparse_swiglu_mlp(X, w, flags=L.AS_FLAG_FORCE_DENSE, Y=Y) for w in full * 3]
+        up, uf = C.graph_us(fp), C.graph_us(ff)
+        out["points"].append({"tokens": M, "packed_us": r4(up), "full_dense_us": r4(uf), "speedup": r4(uf / up),
+                              "packed_tokens_per_s": r4(M / (up * 1e-6))})
+    for M in (1, 2, 4, 8, 16):
+        X = datagen.student_t((M, d), 970 + M).to(C.dev)
+        Y = torch.empty((M, d), dtype=torch.float32, device=C.dev)
+        t_x = float(asg.as_calibrate_threshold(X, 0.5).item())
+        fs = [lambda w=w: asg.as_sparse_swiglu_mlp(X, w, t_x, 0.01, Y=Y) for w in full * 3]
+        fd = [lambda w=w: asg.as_sparse_swiglu_mlp(X, w, t_x, 0.01, flags=L.AS_FLAG_FORCE_DENSE, Y=Y) for w in full * 3]
+        us, ud = C.graph_us(fs), C.graph_us(fd)
+        union = float((X.float().abs() > t_x).any(dim=0).float().mean().item())
+        out["switch"].append({"tokens": M, "x_union_density": r4(union), "sparse_us": r4(us), "dense_us": r4(ud),
+                              "auto_takes": "dense" if M >= L.AS_AUTO_DENSE_MIN_TOKENS else "sparse"})
+    del full, packed
+    torch.cuda.empty_cache()
+    return out
+
+
 class _LazyF64:
     """Index-on-demand fp64 view of a stacked bf16 expert tensor (oracle sample only)."""
 
@@ -1002,6 +1042,7 @@ def main():
                          ("next4_greedy", lambda: row_greedy(C, cpu)),
                          ("next4_int8", lambda: row_int8(C, cpu)),
                          ("next3_attribution", lambda: row_attrib(C, cpu)),
+                         ("next2_batch_static", lambda: row_batch_static(C, cpu)),
                          ("a8_a9_moe", lambda: row_moe(C, cpu)),
                          ("a10_batch16_mfma", lambda: row_batch16(C, cpu, t_x, t_h)),
                          ("a11_block", lambda: row_block(C, cpu)), ("small_mlp_fp16", lambda: row_small(C, cpu))):

@@ -77,9 +77,16 @@ enum {
                                       reproducible (see the GEMV and MLP calls)           */
   AS_FLAG_NO_NT_LOADS = 1u << 2,  /* plain (cached) weight loads instead of nontemporal  */
   AS_FLAG_FORCE_DENSE = 1u << 3,  /* ignore thresholds / neuron lists: dense baseline   */
-  AS_FLAG_NO_FUSION = 1u << 4     /* decoder block: RMS normalisations and residual adds as
+  AS_FLAG_NO_FUSION = 1u << 4,    /* decoder block: RMS normalisations and residual adds as
                                      launches of their own (seven instead of five)       */
+  AS_FLAG_AUTO = 1u << 5          /* as_sparse_swiglu_mlp, THRESHOLD: the batch-size switch
+                                     (dense from AS_AUTO_DENSE_MIN_TOKENS tokens on)     */
 };
+
+/* Tokens from which AS_FLAG_AUTO runs the dense path (measured on MI355X: from
+ * eight tokens on, the union of the tokens' threshold masks keeps nearly every
+ * row and the sparse launches cost more than the dense ones). */
+#define AS_AUTO_DENSE_MIN_TOKENS 8
 
 /* Verification exports of a mask (every field may be NULL).
    bits: [M, ceil(n/64)] uint64, bit i%64 of word i/64 set when element i is kept.
@@ -208,7 +215,13 @@ typedef struct {
  * must be -INFINITY (X is not thresholded; UNSUPPORTED otherwise); M <= 8;
  * d_model <= 8192; neuron_idx is ignored.  AS_FLAG_FORCE_DENSE keeps every neuron.
  * X: [M, d_model] (f16/bf16/f32), 1 <= M <= 16 (M > 8: THRESHOLD mode with bf16
- * weights, on the matrix cores); Y: [M, d_model].
+ * weights, on the matrix cores); THRESHOLD mode without debug exports also takes
+ * 16 < M <= 256, run as consecutive groups of 16 tokens on `stream` (the full
+ * groups and a partial last group each use a region of the workspace of their
+ * own, as as_sparse_swiglu_mlp_ws_size(M) sizes it).  Y: [M, d_model].
+ * AS_FLAG_AUTO (THRESHOLD; Intra-expert summary, system implementation: the sparse
+ * path for low latency, the dense one for throughput, switched by batch size):
+ * the call runs as AS_FLAG_FORCE_DENSE when M >= AS_AUTO_DENSE_MIN_TOKENS.
  * silu(z) = z / (1 + exp(-z)).  AS_FLAG_FORCE_DENSE: dense SwiGLU over all
  * neurons and inputs (the baseline).  AS_FLAG_ATOMIC_SPLITK (fp32 Y only): the
  * down projection's row slices add into Y with fp32 atomic adds (as in
@@ -222,6 +235,20 @@ as_status as_sparse_swiglu_mlp(const void *X, as_dtype x_dt, int M, const as_mlp
                                const int32_t *neuron_idx, int n_active,
                                void *Y, as_dtype y_dt, unsigned flags, as_mlp_debug *dbg,
                                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Compact packing of a static neuron set (GLASS summary, section 2.2 and its
+ * edge-deployment discussion: a static mask keeps one compact subset of the
+ * weights resident for the whole decode).  From THRESHOLD-layout weights w (gate/up
+ * [d_model, 2, d_ff], down [d_ff, d_model]) and the kept neurons idx[0..k) (device
+ * int32, each < d_ff), writes gate_up_out [d_model, 2, k] (columns idx of every
+ * input row) and down_out [k, d_model] (rows idx), in w->w_dt.  The packed pair is
+ * an ordinary THRESHOLD-layout MLP with d_ff = k: as_sparse_swiglu_mlp on it with
+ * AS_FLAG_FORCE_DENSE (or t_x = t_h = -INFINITY) is the static-set SwiGLU of a
+ * whole batch, each packed row read once per 16 tokens.  k must be a multiple of 64
+ * (the MLP's d_ff rule) and at most d_ff; both outputs 16-byte aligned.
+ * Errors: INVALID_ARG for NULL pointers, a bad k or misaligned outputs. */
+as_status as_pack_neuron_set(const as_mlp_weights *w, const int32_t *idx, int k,
+                             void *gate_up_out, void *down_out, hipStream_t stream);
 
 /* Allocation-free as_sparse_swiglu_mlp, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
