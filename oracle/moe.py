@@ -6,7 +6,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .teal import silu, dense_mlp
+from .teal import silu, dense_mlp, magnitude_mask
 from .topk import value_topk
 
 
@@ -50,6 +50,58 @@ def expert_sparse(x, Wgu_e, Wd_e, keep: int):
     kidx = value_topk(np.abs(h), keep)
     y = h[kidx] @ np.asarray(Wd_e, dtype=np.float64)[kidx]
     return y, h, kidx
+
+
+def expert_gate_score(x, Wgu_e, Wd_e, t):
+    """One routed expert on one token with the gate-score keep rule.
+
+    Intra-expert summary, system implementation: the gate projection runs densely
+    and scores every neuron, one O(n) threshold pass masks the scores (no top-k
+    sort), and only the active neurons' weights enter the up and down work.  TEAL
+    slides, slides 5-6 (CATS): the score is |SiLU(x W_gate)|; W_up and W_down are
+    pruned, the gate is not.
+
+    Steps: ``g = W_gate x``, ``a = silu(g)``, keep j iff ``|a_j| > t`` (strict, t
+    as fp32); for kept j ``u_j = W_up[j] . x`` and ``h_j = a_j u_j``; h is 0
+    elsewhere; ``y_e = sum over kept j of h_j W_down[j]``.
+
+    Wgu_e: ``[d_ff_e, 2, d_model]`` neuron-major; Wd_e: ``[d_ff_e, d_model]``.
+    Returns (y_e, h, a, keep_idx).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(Wgu_e, dtype=np.float64)
+    a = silu(W[:, 0, :] @ x)
+    kidx = np.flatnonzero(magnitude_mask(a, t))
+    h = np.zeros(W.shape[0])
+    h[kidx] = a[kidx] * (W[kidx, 1, :] @ x)        # up rows of the kept neurons only
+    y = h[kidx] @ np.asarray(Wd_e, dtype=np.float64)[kidx]
+    return y, h, a, kidx
+
+
+def moe_layer_gate_score(x, w: dict, top: int, t):
+    """The routed MoE layer of ``moe_layer`` with every routed expert under the
+    gate-score keep rule (``expert_gate_score`` with threshold ``t``); the shared
+    expert stays dense.  Returns (out, info) with per-token ids, weights, and per
+    slot h, a and the kept neuron indices."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    T, d = x.shape
+    out = np.zeros((T, d))
+    info = []
+    sgu = np.asarray(w["s_gate_up"], dtype=np.float64)
+    for i in range(T):
+        ids, wts, logits = router(x[i], w["w_router"], top)
+        y = np.zeros(d)
+        hs, as_, ks = [], [], []
+        for e, we in zip(ids, wts):
+            ye, h, a, kidx = expert_gate_score(x[i], w["w_gate_up"][e], w["w_down"][e], t)
+            y += we * ye
+            hs.append(h)
+            as_.append(a)
+            ks.append(kidx)
+        y += dense_mlp(x[i], sgu[:, 0, :], sgu[:, 1, :], w["s_down"])
+        out[i] = y
+        info.append(dict(ids=ids, weights=wts, logits=logits, h=hs, a=as_, keep=ks))
+    return out, info
 
 
 def moe_layer(x, w: dict, top: int, keep: int):

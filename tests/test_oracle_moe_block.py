@@ -84,6 +84,70 @@ def test_moe_single_expert_weight_one():
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-15)
 
 
+# ------------------------------------------------------------ gate-score experts
+def test_expert_gate_score_hand_values():
+    """d_model 2, three neurons, values worked by hand: g = (2, 0, -3); silu(2) =
+    2/(1+e^-2) = 1.7616, silu(0) = 0, silu(-3) = -3/(1+e^3) = -0.1423; t = 0.1 keeps
+    neurons 0 and 2; u = (1, -, 0.5); y = 1.7616 * 1 * Wd[0] - 0.1423 * 0.5 * Wd[2]."""
+    x = np.array([1.0, 2.0])
+    Wgu = np.array([[[2.0, 0.0], [1.0, 0.0]],
+                    [[0.0, 0.0], [9.0, 9.0]],
+                    [[-1.0, -1.0], [0.5, 0.0]]])
+    Wd = np.array([[1.0, 0.0], [5.0, 5.0], [0.0, 2.0]])
+    y, h, a, kidx = moe.expert_gate_score(x, Wgu, Wd, 0.1)
+    s2, s3 = 2.0 / (1.0 + np.exp(-2.0)), -3.0 / (1.0 + np.exp(3.0))
+    assert kidx.tolist() == [0, 2]
+    np.testing.assert_allclose(a, [s2, 0.0, s3], rtol=1e-15)
+    np.testing.assert_allclose(h, [s2, 0.0, 0.5 * s3], rtol=1e-15)
+    np.testing.assert_allclose(y, [s2, 2.0 * 0.5 * s3], rtol=1e-15)
+    # t between |silu(-3)| and silu(2) keeps neuron 0 only
+    y1, _, _, k1 = moe.expert_gate_score(x, Wgu, Wd, 0.5)
+    assert k1.tolist() == [0] and np.allclose(y1, [s2, 0.0], rtol=1e-15)
+
+
+def test_expert_gate_score_limits_and_pruned_rows():
+    """t = -inf is the dense SwiGLU expert; t = +inf drops every neuron (y = 0);
+    at a median t the output equals the dense SwiGLU with the dropped neurons' up
+    and down rows zeroed (the gate row is not pruned), and the kept set is exactly
+    the neurons whose |silu(g)| exceeds t."""
+    w = _small_moe()
+    x = _f64(datagen.student_t((64,), 17))
+    e = 5
+    Wgu, Wd = w["w_gate_up"][e], w["w_down"][e]
+    ref = _torch_swiglu(x, Wgu[:, 0, :].T, Wgu[:, 1, :].T, Wd)
+    y, h, a, kidx = moe.expert_gate_score(x, Wgu, Wd, float("-inf"))
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-15)
+    assert kidx.tolist() == list(range(48))
+    y, h, a, kidx = moe.expert_gate_score(x, Wgu, Wd, float("inf"))
+    assert kidx.size == 0 and np.all(h == 0) and np.all(y == 0)
+    g = torch.from_numpy(Wgu[:, 0, :] @ x)
+    act = F.silu(g).numpy()
+    t = float(np.float32(np.median(np.abs(act))))
+    y, h, a, kidx = moe.expert_gate_score(x, Wgu, Wd, t)
+    m = np.abs(act) > t
+    assert kidx.tolist() == np.flatnonzero(m).tolist()
+    Wu0, Wd0 = Wgu[:, 1, :].copy(), Wd.copy()
+    Wu0[~m] = 0.0
+    Wd0[~m] = 0.0
+    np.testing.assert_allclose(y, _torch_swiglu(x, Wgu[:, 0, :].T, Wu0.T, Wd0), rtol=1e-11, atol=1e-15)
+
+
+def test_moe_layer_gate_score_dense_limit_and_shared_only():
+    """t = -inf equals the dense MoE layer (keep = d_ff_e); t = +inf leaves the
+    shared expert alone; routing is the same as the top-k layer's."""
+    w = _small_moe()
+    X = _f64(datagen.student_t((3, 64), 19))
+    out_d, info_d = moe.moe_layer(X, w, top=2, keep=48)
+    out_g, info_g = moe.moe_layer_gate_score(X, w, top=2, t=float("-inf"))
+    np.testing.assert_allclose(out_g, out_d, rtol=1e-12, atol=1e-15)
+    for a, b in zip(info_d, info_g):
+        assert a["ids"].tolist() == b["ids"].tolist()
+    out_s, _ = moe.moe_layer_gate_score(X, w, top=2, t=float("inf"))
+    for i in range(3):
+        ref = _torch_swiglu(X[i], w["s_gate_up"][:, 0, :], w["s_gate_up"][:, 1, :], w["s_down"])
+        np.testing.assert_allclose(out_s[i], ref, rtol=1e-12, atol=1e-15)
+
+
 # ------------------------------------------------------------ static neuron set
 def test_neuron_set_full_is_dense_and_subset_is_masked():
     d, f = 64, 96
