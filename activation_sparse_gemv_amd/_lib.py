@@ -94,6 +94,12 @@ SIGNATURES = {
     "as_sparse_moe_expert": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, POINTER(ASMoeWeights),
                                      c_int, c_void_p, c_int, c_uint, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),
+    "as_sparse_moe_expert_gate": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, POINTER(ASMoeWeights),
+                                          c_float, c_void_p, c_int, c_uint, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_size_t, c_void_p]),
+    "as_moe_layer_gate": (c_int, [c_void_p, c_int, c_int, POINTER(ASMoeLayerWeights), c_int, c_float, c_void_p,
+                                  c_uint, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                  c_void_p]),
     "as_moe_layer_ws_size": (c_size_t, [c_int, c_int, POINTER(ASMoeLayerWeights)]),
     "as_moe_layer": (c_int, [c_void_p, c_int, c_int, POINTER(ASMoeLayerWeights), c_int, c_int, c_void_p, c_uint,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -319,6 +319,33 @@ def as_sparse_moe_expert(X: torch.Tensor, w: MoEWeights, ids: torch.Tensor, wts:
     return (Y, dict(h=h, keep=keep)) if debug else Y
 
 
+def as_sparse_moe_expert_gate(X: torch.Tensor, w: MoEWeights, ids: torch.Tensor, wts: torch.Tensor, t_gate: float,
+                              y_dtype=torch.float32, flags: int = 0, Y: torch.Tensor | None = None,
+                              debug: bool = False, y_ready: "L.HipEvent | None" = None):
+    """Routed experts under the gate-score keep rule (|silu(g)| > t_gate, up and
+    down over the kept neurons); otherwise as as_sparse_moe_expert.  debug adds h
+    and a ([T, top, d_ff_e] fp32)."""
+    _need_cuda(X, w.w_gate_up, w.w_down, ids, wts, Y)
+    T, d = X.shape
+    top = ids.shape[1]
+    E, f = w.w_gate_up.shape[0], w.w_gate_up.shape[1]
+    if Y is None:
+        Y = torch.empty((T, d), dtype=y_dtype, device=X.device)
+    lib = L.load()
+    st = w.struct()
+    nb = lib.as_sparse_moe_expert_ws_size(T, top, ctypes.byref(st))
+    ws = workspace(("moe", T, top, E, d, f), nb, X.device)
+    h = a = None
+    if debug:
+        h = torch.zeros((T, top, f), dtype=torch.float32, device=X.device)
+        a = torch.zeros((T, top, f), dtype=torch.float32, device=X.device)
+    L.check(lib.as_sparse_moe_expert_gate(_ptr(X), _dt(X), T, _ptr(ids), _ptr(wts), top, ctypes.byref(st),
+                                          float(t_gate), _ptr(Y), _dt(Y), flags, _ptr(h), _ptr(a),
+                                          y_ready.ev if y_ready is not None else None, _ptr(ws), ws.numel(),
+                                          _stream(X.device)), "as_sparse_moe_expert_gate")
+    return (Y, dict(h=h, a=a)) if debug else Y
+
+
 def _moe_layer_struct(w: MoEWeights) -> "L.ASMoeLayerWeights | None":
     if w.w_router is None or w.shared is None or w.w_router.dtype != torch.bfloat16:
         return None
@@ -356,6 +383,36 @@ def as_moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags:
     return Y
 
 
+def as_moe_layer_gate(X: torch.Tensor, w: MoEWeights, top_k: int, t_gate: float, flags: int = 0,
+                      debug: bool = False):
+    """as_moe_layer with the routed experts under the gate-score keep rule
+    (|silu(g)| > t_gate).  Returns Y [T, d] fp32 (and logits, ids, wts, h, a when
+    debug)."""
+    _need_cuda(X, w.w_gate_up, w.w_down, w.w_router)
+    T, d = X.shape
+    E, f = w.w_gate_up.shape[0], w.w_gate_up.shape[1]
+    lib = L.load()
+    st = _moe_layer_struct(w)
+    if st is None:
+        raise ValueError("as_moe_layer_gate: needs a bf16 router and a shared expert")
+    nb = lib.as_moe_layer_ws_size(T, top_k, ctypes.byref(st))
+    ws = workspace(("moe_layer", T, top_k, E, d, f, w.shared.d_ff), nb, X.device)
+    Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=X.device)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=X.device)
+    wts = torch.empty((T, top_k), dtype=torch.float32, device=X.device)
+    h = a = None
+    if debug:
+        h = torch.zeros((T, top_k, f), dtype=torch.float32, device=X.device)
+        a = torch.zeros((T, top_k, f), dtype=torch.float32, device=X.device)
+    L.check(lib.as_moe_layer_gate(_ptr(X), _dt(X), T, ctypes.byref(st), top_k, float(t_gate), _ptr(Y), flags,
+                                  _ptr(logits), _ptr(ids), _ptr(wts), _ptr(h), _ptr(a), _ptr(ws), ws.numel(),
+                                  _stream(X.device)), "as_moe_layer_gate")
+    if debug:
+        return Y, dict(logits=logits, ids=ids, wts=wts, h=h, a=a)
+    return Y
+
+
 def moe_layer_one_stream_ok(X: torch.Tensor, w: MoEWeights, top_k: int, flags: int = 0) -> bool:
     """Whether as_moe_layer takes this call (shapes within its limits, bf16 weights)."""
     if flags & ~(L.AS_FLAG_FORCE_DENSE | L.AS_FLAG_ATOMIC_SPLITK):
@@ -387,16 +444,19 @@ def _side_event(device: torch.device) -> "L.HipEvent":
 
 
 def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: int = 0, debug: bool = False,
-              overlap: bool = True, one_stream: bool = True):
+              overlap: bool = True, one_stream: bool = True, t_gate: float | None = None):
     """One MoE layer: router logits (dense GEMV), router top-k + softmax, the dense
     shared expert, then the routed experts accumulated on top.  Where as_moe_layer
     takes the shapes (and `one_stream`), the layer is that one call: three launches
     on the current stream.  Otherwise it is composed from the separate entry points;
     with `overlap`, the shared expert then runs on a second stream while the router
     and the routed experts' gate/up stage run, and their down stage waits for it,
-    since it accumulates into its output.  Returns Y [T, d] fp32 (and intermediates
-    when debug)."""
+    since it accumulates into its output.  With `t_gate`, the routed experts keep
+    the neurons with |silu(g)| > t_gate instead of the top keep_k (keep_k unused).
+    Returns Y [T, d] fp32 (and intermediates when debug)."""
     if one_stream and moe_layer_one_stream_ok(X, w, top_k, flags):
+        if t_gate is not None:
+            return as_moe_layer_gate(X, w, top_k, t_gate, flags=flags, debug=debug)
         return as_moe_layer(X, w, top_k, keep_k, flags=flags, debug=debug)
     T, d = X.shape
     Y = torch.empty((T, d), dtype=torch.float32, device=X.device)
@@ -427,8 +487,12 @@ def moe_layer(X: torch.Tensor, w: MoEWeights, top_k: int, keep_k: int, flags: in
         shared()
     # the routed experts' down stage waits for the shared expert (it accumulates
     # into Y); their grouping and gate/up stage overlap it
-    r = as_sparse_moe_expert(X, w, ids, wts, keep_k, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug,
-                             y_ready=ready)
+    if t_gate is not None:
+        r = as_sparse_moe_expert_gate(X, w, ids, wts, t_gate, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug,
+                                      y_ready=ready)
+    else:
+        r = as_sparse_moe_expert(X, w, ids, wts, keep_k, flags=flags | L.AS_FLAG_ACCUMULATE, Y=Y, debug=debug,
+                                 y_ready=ready)
     if debug:
         return Y, dict(logits=logits, ids=ids, wts=wts, **r[1])
     return Y

@@ -970,11 +970,19 @@ size_t as_sparse_moe_expert_ws_size(int T, int top_k, const as_moe_weights* w) {
   return c.off;
 }
 
-as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_t* expert_ids,
-                               const float* expert_w, int top_k, const as_moe_weights* w, int keep_k, void* Y,
-                               as_dtype y_dt, unsigned flags, float* h_dbg, int32_t* keep_dbg,
-                               hipEvent_t y_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "as_sparse_moe_expert";
+namespace {
+// Keep rule of the routed experts: the exact top keep_k of |h| per (token, slot), or
+// (gate) the neurons with |silu(g)| > t_gate.
+struct MoeKeepRule {
+  bool gate;
+  float t_gate;
+  float* a_dbg;
+};
+
+as_status moe_expert_impl(const char* fn, const void* X, as_dtype x_dt, int T, const int32_t* expert_ids,
+                          const float* expert_w, int top_k, const as_moe_weights* w, int keep_k,
+                          const MoeKeepRule& rule, void* Y, as_dtype y_dt, unsigned flags, float* h_dbg,
+                          int32_t* keep_dbg, hipEvent_t y_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!X || !expert_ids || !expert_w || !w || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!w->w_gate_up || !w->w_down) return fail(AS_ERR_INVALID_ARG, "%s: NULL weights", fn);
   if (!is_dt(x_dt) || !is_dt(y_dt) || !is_wdt(w->w_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
@@ -999,6 +1007,13 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   p.h = m.h; p.h_dbg = h_dbg; p.keep_dbg = (flags & AS_FLAG_FORCE_DENSE) ? nullptr : keep_dbg;
   p.partials = m.partials; p.counters = m.counters; p.n_tiles = moe_down_tiles(w->d_model);
   if (moe_select_in_gu(T * top_k, w->d_ff_e, false)) { p.gu_cnt = m.gu_cnt; p.keep = m.keep; p.kval = m.kval; }
+  if (rule.gate) {
+    // every neuron's h is written (0 where dropped); the down stage keeps the nonzero
+    p.gate_mode = 1;
+    p.gate_t = (flags & AS_FLAG_FORCE_DENSE) ? -INFINITY : rule.t_gate;
+    p.a_dbg = rule.a_dbg;
+    p.keep_k = 0; p.keep_dbg = nullptr; p.keep = nullptr; p.kval = nullptr; p.gu_cnt = nullptr;
+  }
   p.y = Y; p.y_dt = int(y_dt); p.accumulate = (flags & AS_FLAG_ACCUMULATE) ? 1 : 0;
   p.neurons_per_block = moe_npb(T * top_k);
   if (flags & AS_FLAG_ATOMIC_SPLITK) {
@@ -1015,6 +1030,26 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
   }
   const int max_unique = T * top_k < w->n_experts ? T * top_k : w->n_experts;
   return hip_check(launch_moe(int(w->w_dt), p, max_unique, y_ready, stream), fn);
+}
+}  // namespace
+
+as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_t* expert_ids,
+                               const float* expert_w, int top_k, const as_moe_weights* w, int keep_k, void* Y,
+                               as_dtype y_dt, unsigned flags, float* h_dbg, int32_t* keep_dbg,
+                               hipEvent_t y_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const MoeKeepRule rule{false, 0.f, nullptr};
+  return moe_expert_impl("as_sparse_moe_expert", X, x_dt, T, expert_ids, expert_w, top_k, w, keep_k, rule, Y, y_dt,
+                         flags, h_dbg, keep_dbg, y_ready, ws, ws_bytes, stream);
+}
+
+as_status as_sparse_moe_expert_gate(const void* X, as_dtype x_dt, int T, const int32_t* expert_ids,
+                                    const float* expert_w, int top_k, const as_moe_weights* w, float t_gate,
+                                    void* Y, as_dtype y_dt, unsigned flags, float* h_dbg, float* a_dbg,
+                                    hipEvent_t y_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (std::isnan(t_gate)) return fail(AS_ERR_INVALID_ARG, "as_sparse_moe_expert_gate: t_gate is NaN");
+  const MoeKeepRule rule{true, t_gate, a_dbg};
+  return moe_expert_impl("as_sparse_moe_expert_gate", X, x_dt, T, expert_ids, expert_w, top_k, w, 0, rule, Y, y_dt,
+                         flags, h_dbg, nullptr, y_ready, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ MoE layer (one stream)
@@ -1086,10 +1121,11 @@ size_t as_moe_layer_ws_size(int T, int top_k, const as_moe_layer_weights* w) {
   return c.off;
 }
 
-as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_weights* w, int top_k, int keep_k,
-                       float* Y, unsigned flags, float* logits, int32_t* ids, float* weights, float* h_dbg,
-                       int32_t* keep_dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "as_moe_layer";
+namespace {
+as_status moe_layer_impl(const char* fn, const void* X, as_dtype x_dt, int T, const as_moe_layer_weights* w,
+                         int top_k, int keep_k, const MoeKeepRule& rule, float* Y, unsigned flags, float* logits,
+                         int32_t* ids, float* weights, float* h_dbg, int32_t* keep_dbg, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   if (!X || !w || !Y || !logits || !ids || !weights) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!w->w_router || !w->experts.w_gate_up || !w->experts.w_down)
     return fail(AS_ERR_INVALID_ARG, "%s: NULL router or expert weights", fn);
@@ -1147,6 +1183,12 @@ as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_w
   pm.h = m.moe.h; pm.h_dbg = h_dbg; pm.keep_dbg = dense ? nullptr : keep_dbg;
   pm.partials = m.moe.partials; pm.counters = m.moe.counters; pm.n_tiles = moe_down_tiles(d);
   if (moe_select_in_gu(T * top_k, ew.d_ff_e, true)) { pm.gu_cnt = m.moe.gu_cnt; pm.keep = m.moe.keep; pm.kval = m.moe.kval; }
+  if (rule.gate) {
+    pm.gate_mode = 1;
+    pm.gate_t = dense ? -INFINITY : rule.t_gate;
+    pm.a_dbg = rule.a_dbg;
+    pm.keep_k = 0; pm.keep_dbg = nullptr; pm.keep = nullptr; pm.kval = nullptr; pm.gu_cnt = nullptr;
+  }
   pm.y = Y; pm.y_dt = AS_F32; pm.accumulate = 1;
   pm.atomic_y = (flags & AS_FLAG_ATOMIC_SPLITK) ? 1 : 0;
   pm.neurons_per_block = moe_npb(T * top_k);
@@ -1176,8 +1218,26 @@ as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_w
   }
   if ((st = hip_check(launch_moe_route_gu(lp.cfg, pr, pg, sm1, stream), fn)) != AS_OK) return st;
   if ((st = hip_check(launch_moe_gu_down(lp.cfg, pm, n_u, n_gu, pd, sm2, stream), fn)) != AS_OK) return st;
-  // launch 3: routed down stage, exact top keep_k per (token, slot), added onto Y
+  // launch 3: routed down stage over each (token, slot)'s keep set, added onto Y
   return hip_check(launch_moe_down(int(AS_BF16), pm, stream), fn);
+}
+}  // namespace
+
+as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_weights* w, int top_k, int keep_k,
+                       float* Y, unsigned flags, float* logits, int32_t* ids, float* weights, float* h_dbg,
+                       int32_t* keep_dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const MoeKeepRule rule{false, 0.f, nullptr};
+  return moe_layer_impl("as_moe_layer", X, x_dt, T, w, top_k, keep_k, rule, Y, flags, logits, ids, weights, h_dbg,
+                        keep_dbg, ws, ws_bytes, stream);
+}
+
+as_status as_moe_layer_gate(const void* X, as_dtype x_dt, int T, const as_moe_layer_weights* w, int top_k,
+                            float t_gate, float* Y, unsigned flags, float* logits, int32_t* ids, float* weights,
+                            float* h_dbg, float* a_dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (std::isnan(t_gate)) return fail(AS_ERR_INVALID_ARG, "as_moe_layer_gate: t_gate is NaN");
+  const MoeKeepRule rule{true, t_gate, a_dbg};
+  return moe_layer_impl("as_moe_layer_gate", X, x_dt, T, w, top_k, 0, rule, Y, flags, logits, ids, weights, h_dbg,
+                        nullptr, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ block glue

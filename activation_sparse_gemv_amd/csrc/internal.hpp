@@ -140,6 +140,9 @@ struct MoeParams {
   // finished neuron blocks per touched expert [256], kept indices and their h
   // [T * top][keep_k]; else the down stage selects them itself
   unsigned* gu_cnt; int* keep; float* kval;
+  // gate-score mode: keep neuron n of an item iff |silu(g_n)| > gate_t, up row read
+  // only for kept neurons (h = 0 elsewhere); the down stage keeps the nonzero h
+  int gate_mode; float gate_t; float* a_dbg;
 };
 hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s);
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s);

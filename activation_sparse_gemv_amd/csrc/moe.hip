@@ -6,7 +6,10 @@
 // remaining neurons' weights are gathered for the rest of the expert.  Here the
 // score of neuron n is |silu(g_n) * u_n| (gate and up dense), the keep_k best
 // neurons (ties to the smaller index) reach the down projection, and only their
-// down rows (one contiguous d_model row each) are read.
+// down rows (one contiguous d_model row each) are read.  Gate-score mode (TEAL
+// slides, slides 5-6, CATS): the score is |silu(g_n)| alone, the neurons above a
+// threshold are kept, the up row is read only for them, and the down stage takes
+// the nonzero h of each (token, slot) in neuron order.
 //
 // Kernels (one call):
 //   gate/up: (touched expert, neuron block) workgroups; each derives its expert's
@@ -59,10 +62,12 @@ static_assert(kDnTile % 256 == 0, "the combine takes whole columns per thread");
 template <int WDT>
 __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int* keep = reinterpret_cast<int*>(smem);                        // [keep_k]
-  float* kval = reinterpret_cast<float*>(smem + 4 * ((p.keep_k + 3) & ~3));
-  float* red = kval + ((p.keep_k + 3) & ~3);                       // [4][kDnTile]
-  float* hs = red + 4 * kDnTile;                                   // [d_ff] when d_ff > 1024
+  // keep-set capacity: keep_k, or every neuron in gate-score mode
+  const int kcap = p.gate_mode ? p.d_ff : p.keep_k;
+  int* keep = reinterpret_cast<int*>(smem);                        // [kcap]
+  float* kval = reinterpret_cast<float*>(smem + 4 * ((kcap + 3) & ~3));
+  float* red = kval + ((kcap + 3) & ~3);                           // [4][kDnTile]
+  float* hs = red + 4 * kDnTile;                   // [d_ff] when d_ff > 1024 (top-k mode only)
   __shared__ TopkSmem sm;
   __shared__ int s_last;
   const int item = blockIdx.x;                  // t * top + j
@@ -72,11 +77,33 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   int e = p.ids[item];
   const bool valid_e = e >= 0 && e < p.E;
   if (!valid_e) e = 0;
-  const int kk = valid_e ? p.keep_k : 0;
+  int kk = valid_e ? p.keep_k : 0;
   // the item's keep set by wave 0 (every tile's workgroup selects the same set);
   // an item with an invalid expert keeps nothing
   int* dbg = (p.keep_dbg != nullptr && tile == 0) ? p.keep_dbg + (long)item * p.keep_k : nullptr;
-  if (p.keep != nullptr) {
+  __shared__ int s_kk;
+  if (p.gate_mode) {
+    // gate-score mode: the item's nonzero h, in neuron order (wave 0: one ballot per
+    // 64 neurons)
+    if (threadIdx.x < 64) {
+      const float* h = p.h + (long)item * f;
+      int run = 0;
+      for (int i0 = 0; valid_e && i0 < f; i0 += 64) {
+        const int i = i0 + (int)threadIdx.x;
+        const float v = i < f ? h[i] : 0.f;
+        const uint64_t b = __ballot(v != 0.f);
+        if (v != 0.f) {
+          const int pos = run + lanes_below(b);
+          keep[pos] = i;
+          kval[pos] = v;
+        }
+        run += __popcll(b);
+      }
+      if (threadIdx.x == 0) s_kk = run;
+    }
+    __syncthreads();
+    kk = s_kk;
+  } else if (p.keep != nullptr) {
     // chosen by the gate/up stage
     for (int r = threadIdx.x; r < kk; r += kDnThreads) {
       keep[r] = p.keep[(long)item * p.keep_k + r];
@@ -195,9 +222,15 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
 }
 
 hipError_t launch_moe_down(int wdt, const MoeParams& p, hipStream_t s) {
-  const size_t sm2 = size_t(8) * ((p.keep_k + 3) & ~3) + size_t(4) * kDnTile * 4 +
-                     (p.d_ff > 1024 ? size_t(p.d_ff) * 4 : 0);
+  const int kcap = p.gate_mode ? p.d_ff : p.keep_k;
+  const size_t sm2 = size_t(8) * ((kcap + 3) & ~3) + size_t(4) * kDnTile * 4 +
+                     (p.d_ff > 1024 && !p.gate_mode ? size_t(p.d_ff) * 4 : 0);
   auto k2 = wdt == DT_BF16 ? expert_down_kernel<DT_BF16> : expert_down_kernel<DT_F16>;
+  if (sm2 > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k2), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(sm2));
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k2, dim3(p.T * p.top, p.n_tiles), dim3(kDnThreads), sm2, s, p);
   return hipGetLastError();
 }

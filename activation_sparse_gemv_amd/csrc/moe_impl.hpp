@@ -4,7 +4,9 @@
 // Intra-expert summary, system implementation: inside each routed expert the gate
 // and up projections are run densely to score the neurons.  One wave per neuron
 // computes both dot products for the tokens routed to the expert and writes
-// h = silu(g) * u per (token, slot) item.
+// h = silu(g) * u per (token, slot) item.  In gate-score mode the gate dot
+// products come first, and the up row is read only when some item's
+// |silu(g)| passes the threshold (h = 0 for the items that drop the neuron).
 #pragma once
 #include "topk.hpp"
 #include "internal.hpp"
@@ -83,6 +85,65 @@ __device__ __forceinline__ void expert_neurons_reg(const MoeParams& p, const uin
       const int c = lane * 8 + k * 512;
       load_chunk<8>(p.x, p.x_dt, row + (c < d ? c : 0), (m < ng && c < d) ? 8 : 0, xr[m][k]);
     }
+  }
+  if (p.gate_mode) {
+    // gate-score mode: the gate row first; the up row only if some item keeps n
+    for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
+      const uint16_t* wg = W + (long)n * 2 * d;
+      u32x4 vg[NK];
+#pragma unroll
+      for (int k = 0; k < NK; ++k) vg[k] = load_w16<true>(wg + min(lane * 8 + k * 512, d - 8));
+      float g[TK];
+#pragma unroll
+      for (int m = 0; m < TK; ++m) g[m] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+        if (lane * 8 + k * 512 < d) {
+          float fg[8];
+          unpack8<WDT>(vg[k], fg);
+#pragma unroll
+          for (int m = 0; m < TK; ++m)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) g[m] = fmaf(xr[m][k][q], fg[q], g[m]);
+        }
+      float a[TK];
+      uint32_t keep = 0;
+#pragma unroll
+      for (int m = 0; m < TK; ++m) {
+        a[m] = silu_f32(wave_sum(g[m]));
+        keep |= (uint32_t)(m < ng && fabsf(a[m]) > p.gate_t) << m;
+      }
+      float uu[TK];
+#pragma unroll
+      for (int m = 0; m < TK; ++m) uu[m] = 0.f;
+      if (keep != 0) {                                   // uniform across the wave
+        u32x4 vu[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) vu[k] = load_w16<true>(wg + d + min(lane * 8 + k * 512, d - 8));
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+          if (lane * 8 + k * 512 < d) {
+            float fu[8];
+            unpack8<WDT>(vu[k], fu);
+#pragma unroll
+            for (int m = 0; m < TK; ++m)
+#pragma unroll
+              for (int q = 0; q < 8; ++q) uu[m] = fmaf(xr[m][k][q], fu[q], uu[m]);
+          }
+#pragma unroll
+        for (int m = 0; m < TK; ++m) uu[m] = wave_sum(uu[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < TK; ++m)
+        if (lane == 0 && m < ng) {
+          const int it = items[g0 + m];
+          const float h = ((keep >> m) & 1u) ? a[m] * uu[m] : 0.f;
+          store_coherent(p.h + (long)it * f + n, h);
+          if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
+          if (p.a_dbg != nullptr) p.a_dbg[(long)it * f + n] = a[m];
+        }
+    }
+    return;
   }
   for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
     const uint16_t* wg = W + (long)n * 2 * d;
@@ -234,6 +295,60 @@ __device__ __forceinline__ void expert_gu_block(const MoeParams& p, int u, int n
       }
     }
     __syncthreads();
+    if (p.gate_mode) {
+      // gate-score mode over the staged tokens: gate dot products first, the up
+      // row only if some item keeps the neuron
+      for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
+        const uint16_t* wg = W + (long)n * 2 * d;
+        float g[kGuTok], uu[kGuTok];
+#pragma unroll
+        for (int m = 0; m < kGuTok; ++m) { g[m] = 0.f; uu[m] = 0.f; }
+        auto dots = [&](const uint16_t* wr, float (&acc)[kGuTok]) {
+          for (int c0 = lane * 8; c0 < d; c0 += 64 * 8 * 4) {
+            u32x4 vw[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vw[k] = load_w16<true>(wr + min(c0 + k * 512, d - 8));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int c = c0 + k * 512;
+              if (c < d) {
+                float fw[8];
+                unpack8<WDT>(vw[k], fw);
+#pragma unroll
+                for (int m = 0; m < kGuTok; ++m) {
+                  const float4 xa = *reinterpret_cast<const float4*>(xs + m * d + c);
+                  const float4 xb = *reinterpret_cast<const float4*>(xs + m * d + c + 4);
+                  const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                  for (int q = 0; q < 8; ++q) acc[m] = fmaf(xv[q], fw[q], acc[m]);
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < kGuTok; ++m) acc[m] = wave_sum(acc[m]);
+        };
+        dots(wg, g);
+        float a[kGuTok];
+        uint32_t keep = 0;
+#pragma unroll
+        for (int m = 0; m < kGuTok; ++m) {
+          a[m] = silu_f32(g[m]);
+          keep |= (uint32_t)(m < ng && fabsf(a[m]) > p.gate_t) << m;
+        }
+        if (keep != 0) dots(wg + d, uu);                 // uniform across the wave
+#pragma unroll
+        for (int m = 0; m < kGuTok; ++m)
+          if (lane == 0 && m < ng) {
+            const int it = items[g0 + m];
+            const float h = ((keep >> m) & 1u) ? a[m] * uu[m] : 0.f;
+            store_coherent(p.h + (long)it * f + n, h);
+            if (p.h_dbg != nullptr) p.h_dbg[(long)it * f + n] = h;
+            if (p.a_dbg != nullptr) p.a_dbg[(long)it * f + n] = a[m];
+          }
+      }
+      continue;
+    }
     for (int n = n0 + wave; n < n1; n += kGuThreads / 64) {
       const uint16_t* wg = W + (long)n * 2 * d;
       const uint16_t* wu = wg + d;

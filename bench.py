@@ -766,6 +766,11 @@ def row_moe(C, cpu):
     # well past the 256 MB Infinity Cache
     copies = [mk(dev0)] + [mk({k: v.clone() for k, v in dev0.items()}) for _ in range(8)]
     cases = []
+    # gate-score threshold for 85% of the routed neurons dropped: nearest rank over
+    # the gate activations of 8 calibration tokens' routed experts
+    Xc = datagen.student_t((8, d), datagen.seed_for(5, 0, "calib")).to(C.dev)
+    _, dc = asg.as_moe_layer_gate(Xc, copies[0], c["top"], float("-inf"), debug=True)
+    t_gate = float(asg.as_calibrate_threshold(dc["a"].reshape(-1, c["d_ff_e"]), 0.85).item())
     for T in c["tokens"]:
         X = datagen.student_t((T, d), datagen.seed_for(5, T, "decode")).to(C.dev)
         fs = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], c["keep"]) for ww in copies]
@@ -788,14 +793,30 @@ def row_moe(C, cpu):
         ab = touched * e_gu + down_rows * d * 2 + (2 * d * c["d_ff_shared"] + c["d_ff_shared"] * d) * 2 + \
             d * c["n_experts"] * 2
         dense_b = touched * (e_gu + c["d_ff_e"] * d * 2) + (3 * d * c["d_ff_shared"]) * 2 + d * c["n_experts"] * 2
+        fg = [lambda ww=ww: asg.moe_layer(X, ww, c["top"], 0, t_gate=t_gate) for ww in copies]
+        usg = C.graph_us(fg, reps=10)
+        _, dg = asg.moe_layer(X, copies[0], c["top"], 0, t_gate=t_gate, debug=True)
+        hg = dg["h"].reshape(T, c["top"], c["d_ff_e"]).cpu().numpy()
+        g_rows = 0
+        for e in np.unique(ids):
+            sel = [(t, j) for t in range(T) for j in range(c["top"]) if ids[t, j] == e]
+            g_rows += int(np.any(np.stack([hg[t, j] != 0 for t, j in sel]), axis=0).sum())
+        gb = touched * c["d_ff_e"] * d * 2 + g_rows * 2 * d * 2 + \
+            (2 * d * c["d_ff_shared"] + c["d_ff_shared"] * d) * 2 + d * c["n_experts"] * 2
+        gate_case = {"t_gate": r4(t_gate), "kept_frac": r4(float((hg != 0).mean())), "us": r4(usg),
+                     "speedup_vs_dense": r4(usd / usg), "active_mb": r4(gb / 1e6),
+                     "gbs": r4(gb / (usg * 1e-6) / 1e9)}
         cases.append({"tokens": T, "experts_touched": touched, "us": r4(us), "dense_us": r4(usd),
-                      "speedup": r4(usd / us),
+                      "speedup": r4(usd / us), "gate_score": gate_case,
                       "atomic_splitk": {"us": r4(usa), "dense_us": r4(usda), "speedup": r4(usda / usa)},
                       "active_mb": r4(ab / 1e6), "dense_mb": r4(dense_b / 1e6),
                       "gbs": r4(ab / (us * 1e-6) / 1e9), "frac_hbm": r4(ab / (us * 1e-6) / 8e12)})
-        log(f"moe T={T}: {us:.1f} us (dense {usd:.1f}); atomic split-K {usa:.1f} (dense {usda:.1f})")
+        log(f"moe T={T}: {us:.1f} us (dense {usd:.1f}); atomic split-K {usa:.1f} (dense {usda:.1f}); "
+            f"gate-score {usg:.1f}")
     r = {"step": "a8+a9 MoE layer: router GEMV + top-8/softmax, dense shared expert, routed experts "
-                 "(dense gate/up scoring, exact top-77 of 768, gathered down rows)",
+                 "(dense gate/up scoring, exact top-77 of 768, gathered down rows); gate_score: NEXT-1 for "
+                 "the routed experts (dense gate, |silu(g)| > t at 85% calibrated sparsity, up and down rows "
+                 "of the kept neurons only)",
          "shape": "128 experts, d_model 2048, d_ff_e 768, shared d_ff 4096, bf16",
          "rotation": "9 weight copies of 1.26 GB, cycled", "cases": cases}
     if cpu:

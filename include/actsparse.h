@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define AS_VERSION 201
+#define AS_VERSION 202
 
 typedef enum {
   AS_OK = 0,
@@ -370,6 +370,27 @@ as_status as_sparse_moe_expert(const void *X, as_dtype x_dt, int T,
                                float *h_dbg, int32_t *keep_dbg, hipEvent_t y_ready,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Routed experts with the gate-score keep rule (TEAL slides, slides 5-6, CATS;
+ * intra-expert summary, system implementation: the gate projection runs densely
+ * to score the neurons, one threshold pass masks them, only the active neurons'
+ * weights are read for the rest):
+ *   a = silu(x_t Wg_e^T) over all d_ff_e neurons (fp32),
+ *   keep(t, j) = { n : |a_n| > t_gate } (strict),
+ *   h_n = a_n * (x_t . Wu_e[n]) for kept n (the up row read only where some token
+ *   routed to the expert keeps n), h_n = 0 otherwise,
+ *   Y[t, :] (+)= sum_j expert_w[t, j] * sum over n with h_n != 0 of h_n Wd_e[n, :].
+ * Arguments, layouts, workspace (as_sparse_moe_expert_ws_size), y_ready and the
+ * flags AS_FLAG_ACCUMULATE / AS_FLAG_ATOMIC_SPLITK / AS_FLAG_FORCE_DENSE (t_gate
+ * taken as -inf) as for as_sparse_moe_expert.  Debug exports (nullable): h_dbg
+ * [T, top_k, d_ff_e] (exactly 0 where dropped) and a_dbg [T, top_k, d_ff_e] fp32.
+ * Errors: those of as_sparse_moe_expert; INVALID_ARG for a NaN t_gate. */
+as_status as_sparse_moe_expert_gate(const void *X, as_dtype x_dt, int T,
+                                    const int32_t *expert_ids, const float *expert_w, int top_k,
+                                    const as_moe_weights *w, float t_gate,
+                                    void *Y, as_dtype y_dt, unsigned flags,
+                                    float *h_dbg, float *a_dbg, hipEvent_t y_ready,
+                                    void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* One MoE layer for up to 8 tokens on `stream` alone, in three launches
  * (intra-expert summary, system implementation: the router and the shared expert
  * are unchanged; the routed experts score their neurons densely and read only the
@@ -411,6 +432,17 @@ as_status as_moe_layer(const void *X, as_dtype x_dt, int T, const as_moe_layer_w
                        float *logits, int32_t *ids, float *weights,
                        float *h_dbg, int32_t *keep_dbg,
                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* as_moe_layer with the routed experts under the gate-score keep rule of
+ * as_sparse_moe_expert_gate (threshold t_gate on |silu(g)|; the shared expert
+ * stays dense).  Same launches, workspace (as_moe_layer_ws_size), limits and
+ * flags; h_dbg and a_dbg [T * top_k, d_ff_e] as in as_sparse_moe_expert_gate.
+ * Errors: those of as_moe_layer; INVALID_ARG for a NaN t_gate. */
+as_status as_moe_layer_gate(const void *X, as_dtype x_dt, int T, const as_moe_layer_weights *w,
+                            int top_k, float t_gate, float *Y, unsigned flags,
+                            float *logits, int32_t *ids, float *weights,
+                            float *h_dbg, float *a_dbg,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------ attribution-based selection
  * Attribution notes (Attribution-based Sparse Activation in LLMs): neurons are

@@ -49,7 +49,7 @@ def test_enum_values_match_the_header():
 
 
 def test_version_and_strings(lib):
-    assert lib.as_version() == 201
+    assert lib.as_version() == 202
     assert lib.as_status_string(L.AS_ERR_WORKSPACE) == b"AS_ERR_WORKSPACE"
 
 
