@@ -14,76 +14,146 @@ namespace as {
 
 constexpr int kTopkThreads = 1024;
 
+// One workgroup per row; rows up to kValueLdsMax keys are staged in LDS once
+// (eight loads in flight per thread), longer rows are read from memory by every
+// pass of the selection.
+constexpr int kValueLdsMax = 16384;
+
+template <bool SLDS>
 __global__ __launch_bounds__(kTopkThreads) void topk_value_kernel(const float* score, int n, int k, uint64_t* mask,
                                                                   int* idx) {
   __shared__ TopkSmem sm;
+  extern __shared__ __align__(16) uint32_t kl[];
   const long r = blockIdx.x;
   const float* s = score + r * n;
-  block_topk<kTopkThreads>([=](int i) { return float_key(s[i]); }, n, k,
-                           mask ? mask + r * ((n + 63) / 64) : nullptr, idx ? idx + r * (long)k : nullptr, sm);
+  uint64_t* mk = mask ? mask + r * ((n + 63) / 64) : nullptr;
+  int* ix = idx ? idx + r * (long)k : nullptr;
+  if constexpr (SLDS) {
+    constexpr int kB = 8;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kB * kTopkThreads) {
+      float v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) v[u] = i0 + u * kTopkThreads < n ? s[i0 + u * kTopkThreads] : 0.f;
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (i0 + u * kTopkThreads < n) kl[i0 + u * kTopkThreads] = float_key(v[u]);
+    }
+    __syncthreads();
+    block_topk<kTopkThreads>([=](int i) { return kl[i]; }, n, k, mk, ix, sm);
+  } else {
+    block_topk<kTopkThreads>([=](int i) { return float_key(s[i]); }, n, k, mk, ix, sm);
+  }
 }
 
-// Ordinal ranks by counting: rank_j - 1 = #{i : v_i < v_j or (v_i == v_j and
-// i > j)}, accumulated over chunks of i into cnt[r][sig][j] (atomically; the blend
-// kernel clears it), where sig 0 ranks score[r] and sig 1 ranks prior[r].
-// The chunk's keys sit in LDS and are read four at a time; each thread ranks
-// kRankJ consecutive values, so one LDS read feeds 16 comparisons.  A wave's
-// values span a window of 256 indices: chunk keys below the window are strictly
-// smaller-index (ties do not count), keys past it are larger-index (ties count),
-// and only keys inside the window take the exact index comparison.
-constexpr int kRankThreads = 256;
-constexpr int kRankJ = 4;
+// Ordinal ranks: rank_j - 1 = #{i : v_i < v_j or (v_i == v_j and i > j)}, the
+// number of entries before j in the order (key ascending, index descending).
+// (1) chunk_sort_kernel: every chunk of 256 consecutive entries is sorted in that
+//     order (each entry's place in its chunk by counting over the chunk in LDS,
+//     four threads per entry) into the workspace as (key, index) pairs;
+// (2) rank_search_kernel: for each j and each sorted chunk, the entries of the
+//     chunk that come before j form a prefix of it, found by a binary search
+//     (nine steps); a workgroup takes 256 values of j against a batch of up to
+//     kRankBatch chunks staged in LDS and adds its counts into cnt (cleared by
+//     the blend kernel after use).
+// Both launches spread over the chip: n/256 workgroups per signal for (1) and
+// (n/256) * ceil(n/256/kRankBatch) for (2).
+constexpr int kRankChunk = 256;
+constexpr int kRankBatch = 16;
 
-__global__ __launch_bounds__(kRankThreads) void rank_count_kernel(const float* score, const float* prior, int n,
-                                                                  int chunks, unsigned* part) {
-  extern __shared__ __align__(16) uint32_t keys[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int chunk = blockIdx.y;
-  const int r = blockIdx.z >> 1, sig = blockIdx.z & 1;
+__device__ __forceinline__ bool rank_before(uint32_t ke, uint32_t ie, uint32_t kj, uint32_t j) {
+  return ke < kj || (ke == kj && ie > j);
+}
+
+// Four threads per entry, each counting over a quarter of the chunk.
+constexpr int kSortParts = 4;
+
+__global__ __launch_bounds__(kRankChunk * kSortParts) void chunk_sort_kernel(const float* score, const float* prior,
+                                                                             int n, uint32_t* skey, uint32_t* sidx) {
+  __shared__ __align__(16) uint32_t k_s[kRankChunk];
+  __shared__ int s_part[kSortParts][kRankChunk];
+  const int t = threadIdx.x & (kRankChunk - 1), part = threadIdx.x / kRankChunk, c = blockIdx.x;
+  const int r = blockIdx.y >> 1, sig = blockIdx.y & 1;
   const float* v = (sig == 0 ? score : prior) + (long)r * n;
-  const int i0 = split_point(chunk, n, chunks), i1 = split_point(chunk + 1, n, chunks);
-  const int len = i1 - i0;
-  for (int t = tid; t < len; t += kRankThreads) keys[t] = float_key(v[i0 + t]);
+  const int i0 = c * kRankChunk, len = min(kRankChunk, n - i0);
+  if (part == 0) k_s[t] = t < len ? float_key(v[i0 + t]) : 0u;
   __syncthreads();
-  const int j0 = (blockIdx.x * kRankThreads + tid) * kRankJ;
-  uint32_t kj[kRankJ];
-  unsigned c[kRankJ];
-#pragma unroll
-  for (int q = 0; q < kRankJ; ++q) {
-    kj[q] = j0 + q < n ? float_key(v[j0 + q]) : 0u;
-    c[q] = 0u;
+  const uint32_t kt = k_s[t];
+  // entries u of [u0, u1) that come before t: smaller key, or equal key and larger index
+  constexpr int kQ = kRankChunk / kSortParts;
+  const int u0 = part * kQ, u1 = min(u0 + kQ, len);
+  int pos = 0;
+  if (u1 - u0 == kQ) {
+#pragma unroll 4
+    for (int u = u0; u < u1; u += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(k_s + u);
+      pos += (int)(q.x < kt || (q.x == kt && u > t)) + (int)(q.y < kt || (q.y == kt && u + 1 > t)) +
+             (int)(q.z < kt || (q.z == kt && u + 2 > t)) + (int)(q.w < kt || (q.w == kt && u + 3 > t));
+    }
+  } else {
+    for (int u = u0; u < u1; ++u) {
+      const uint32_t ku = k_s[u];
+      pos += (int)(ku < kt || (ku == kt && u > t));
+    }
   }
-  // chunk-local bounds of the wave's index window [jw0, jw0 + 64 * kRankJ)
-  const int jw0 = j0 - lane * kRankJ;
-  const int len4 = len & ~3;
-  const int wa = min(max(jw0 - i0, 0), len), wb = min(max(jw0 + 64 * kRankJ - i0, 0), len);
-  const int sa = min(wa & ~3, len4);                 // [0, sa): every key is below the window
-  const int sb = max(min((wb + 3) & ~3, len4), sa);  // [sb, len4): every key is past it
-  for (int t = 0; t < sa; t += 4) {
-    const uint4 q4 = *reinterpret_cast<const uint4*>(keys + t);
+  s_part[part][t] = pos;
+  __syncthreads();
+  if (part != 0 || t >= len) return;
+  pos = s_part[0][t] + s_part[1][t] + s_part[2][t] + s_part[3][t];
+  const long o = ((long)r * 2 + sig) * n + i0 + pos;
+  skey[o] = kt;
+  sidx[o] = (uint32_t)(i0 + t);
+}
+
+__global__ __launch_bounds__(kRankChunk) void rank_search_kernel(const float* score, const float* prior, int n,
+                                                                 const uint32_t* skey, const uint32_t* sidx,
+                                                                 unsigned* cnt) {
+  __shared__ uint2 bp[kRankBatch * kRankChunk];        // (key, index) of the batch's sorted chunks
+  const int t = threadIdx.x;
+  const int r = blockIdx.z >> 1, sig = blockIdx.z & 1;
+  const long row = ((long)r * 2 + sig) * n;
+  const int nch = (n + kRankChunk - 1) / kRankChunk;
+  const int c0 = blockIdx.y * kRankBatch, c1 = min(c0 + kRankBatch, nch);
+  const int e0 = c0 * kRankChunk, e1 = min(c1 * kRankChunk, n);
+  {
+    // the batch's sorted pairs, every load of a thread issued before the first is used
+    uint32_t lk[kRankBatch], li[kRankBatch];
 #pragma unroll
-    for (int q = 0; q < kRankJ; ++q)
-      c[q] += (unsigned)(q4.x < kj[q]) + (unsigned)(q4.y < kj[q]) + (unsigned)(q4.z < kj[q]) + (unsigned)(q4.w < kj[q]);
+    for (int u = 0; u < kRankBatch; ++u) {
+      const int e = e0 + t + u * kRankChunk;
+      lk[u] = e < e1 ? skey[row + e] : 0u;
+      li[u] = e < e1 ? sidx[row + e] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kRankBatch; ++u)
+      if (e0 + t + u * kRankChunk < e1) bp[t + u * kRankChunk] = make_uint2(lk[u], li[u]);
   }
-  for (int t = sb; t < len4; t += 4) {
-    const uint4 q4 = *reinterpret_cast<const uint4*>(keys + t);
+  const float* v = (sig == 0 ? score : prior) + (long)r * n;
+  const int j = blockIdx.x * kRankChunk + t;
+  const uint32_t kj = j < n ? float_key(v[j]) : 0u;
+  __syncthreads();
+  if (j >= n) return;
+  // the batch's binary searches side by side: kRankBatch independent LDS reads per step
+  int pos[kRankBatch], len[kRankBatch];
 #pragma unroll
-    for (int q = 0; q < kRankJ; ++q)
-      c[q] += (unsigned)(q4.x <= kj[q]) + (unsigned)(q4.y <= kj[q]) + (unsigned)(q4.z <= kj[q]) +
-              (unsigned)(q4.w <= kj[q]);
+  for (int c = 0; c < kRankBatch; ++c) {
+    pos[c] = 0;
+    len[c] = c0 + c < c1 ? min(kRankChunk, n - (c0 + c) * kRankChunk) : 0;
   }
-  auto exact = [&](int t) {
-    const uint32_t ki = keys[t];
-    const int i = i0 + t;
 #pragma unroll
-    for (int q = 0; q < kRankJ; ++q) c[q] += (unsigned)((ki < kj[q]) | ((ki == kj[q]) & (i > j0 + q)));
-  };
-  for (int t = sa; t < sb; ++t) exact(t);
-  for (int t = max(sb, len4); t < len; ++t) exact(t);
-  unsigned* out = part + ((long)r * 2 + sig) * n;
+  for (int step = kRankChunk; step > 0; step >>= 1) {
 #pragma unroll
-  for (int q = 0; q < kRankJ; ++q)
-    if (j0 + q < n && c[q]) atomicAdd(out + j0 + q, c[q]);
+    for (int c = 0; c < kRankBatch; ++c) {
+      const int q = pos[c] + step;
+      if (q <= len[c]) {
+        const uint2 e = bp[c * kRankChunk + q - 1];
+        if (rank_before(e.x, e.y, kj, (uint32_t)j)) pos[c] = q;
+      }
+    }
+  }
+  unsigned tot = 0u;
+#pragma unroll
+  for (int c = 0; c < kRankBatch; ++c) tot += (unsigned)pos[c];
+  atomicAdd(cnt + row + j, tot);
 }
 
 // Blended score S_j = (65536 - lq) R^(l)_j + lq R^(g)_j (ranks = counts + 1; fits
@@ -100,10 +170,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_blend_kernel(unsigned* cnt,
   uint32_t* S = SLDS ? s_lds : s_glob + r * n;
   const uint32_t* Sg = s_glob + r * n;
   const uint32_t wl = 65536u - lq;
-  for (int j = threadIdx.x; j < n; j += kTopkThreads) {
-    S[j] = wl * (cl[j] + 1u) + lq * (cg[j] + 1u);
-    cl[j] = 0u;
-    cg[j] = 0u;
+  constexpr int kB = 8;                                // loads in flight per thread
+  for (int j0 = threadIdx.x; j0 < n; j0 += kB * kTopkThreads) {
+    uint32_t a[kB], b[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int j = j0 + u * kTopkThreads;
+      a[u] = j < n ? cl[j] : 0u;
+      b[u] = j < n ? cg[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int j = j0 + u * kTopkThreads;
+      if (j < n) {
+        S[j] = wl * (a[u] + 1u) + lq * (b[u] + 1u);
+        cl[j] = 0u;
+        cg[j] = 0u;
+      }
+    }
   }
   __syncthreads();
   uint64_t* mk = mask ? mask + r * ((n + 63) / 64) : nullptr;
@@ -112,23 +196,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_blend_kernel(unsigned* cnt,
   else block_topk<kTopkThreads>([=](int i) { return Sg[i]; }, n, k, mk, ix, sm);
 }
 
+
 constexpr int kBlendLdsMax = 32768;   // blended scores staged in LDS up to this n
 
-// Chunks of the counting grid: about 512 workgroups in all, chunks of >= 64 keys.
-int rank_chunks(int rows, int n) {
-  const long jb = (n + kRankThreads * kRankJ - 1) / (kRankThreads * kRankJ);
-  long c = (512 + jb * 2 * rows - 1) / (jb * 2 * rows);
-  if (c > 64) c = 64;
-  if (c > n / 64) c = n / 64;
-  return c < 1 ? 1 : (int)c;
-}
-
+// counts [rows][2][n], blended scores [rows][n], then the sorted chunks' keys and
+// indices [rows][2][n] each
 size_t topk_blend_ws_bytes(int rows, int n) {
-  return (size_t(rows) * 2 * n + size_t(rows) * n) * sizeof(unsigned);
+  return (size_t(rows) * 2 * n * 3 + size_t(rows) * n) * sizeof(unsigned);
 }
 
 hipError_t launch_topk_value(const float* score, int rows, int n, int k, uint64_t* mask, int* idx, hipStream_t s) {
-  hipLaunchKernelGGL(topk_value_kernel, dim3(rows), dim3(kTopkThreads), 0, s, score, n, k, mask, idx);
+  if (n <= kValueLdsMax) {
+    const size_t smem = size_t(n) * 4;
+    if (smem > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_value_kernel<true>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(topk_value_kernel<true>, dim3(rows), dim3(kTopkThreads), smem, s, score, n, k, mask, idx);
+  } else {
+    hipLaunchKernelGGL(topk_value_kernel<false>, dim3(rows), dim3(kTopkThreads), 0, s, score, n, k, mask, idx);
+  }
   return hipGetLastError();
 }
 
@@ -136,12 +224,15 @@ hipError_t launch_topk_blend(const float* score, const float* prior, int rows, i
                              uint64_t* mask, int* idx, unsigned* ws, hipStream_t s) {
   unsigned* cnt = ws;                                // [rows][2][n], zero between calls
   uint32_t* s_glob = ws + size_t(rows) * 2 * n;
+  uint32_t* skey = s_glob + size_t(rows) * n;
+  uint32_t* sidx = skey + size_t(rows) * 2 * n;
   hipError_t e;
-  const int chunks = rank_chunks(rows, n);
-  const int maxlen = (n + chunks - 1) / chunks;
-  const size_t smem1 = (size_t(maxlen) * 4 + 15) & ~size_t(15);
-  const dim3 grid((n + kRankThreads * kRankJ - 1) / (kRankThreads * kRankJ), chunks, rows * 2);
-  hipLaunchKernelGGL(rank_count_kernel, grid, dim3(kRankThreads), smem1, s, score, prior, n, chunks, cnt);
+  const int nch = (n + kRankChunk - 1) / kRankChunk;
+  hipLaunchKernelGGL(chunk_sort_kernel, dim3(nch, rows * 2), dim3(kRankChunk * kSortParts), 0, s, score, prior, n,
+                     skey, sidx);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(rank_search_kernel, dim3(nch, (nch + kRankBatch - 1) / kRankBatch, rows * 2),
+                     dim3(kRankChunk), 0, s, score, prior, n, skey, sidx, cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (n <= kBlendLdsMax) {
     const size_t smem = size_t(n) * 4;

@@ -26,11 +26,9 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 struct TopkSmem {
   unsigned hist[256];
-  int wave_cnt[32];
   uint32_t prefix;
   int krem;
   int sel_bin, sel_krem;
-  int run_eq, run_sel;
 };
 
 // Select the k largest of n keys (key(i) for i < n), ties to the smaller index.
@@ -68,50 +66,52 @@ __device__ void block_topk(KeyFn key, int n, int k, uint64_t* mask, int* idx, To
     T = sm.prefix;
     take_eq = sm.krem;
   }
-  if (tid == 0) { sm.run_eq = 0; sm.run_sel = 0; }
-  __syncthreads();
-  for (int base = 0; base < n; base += NT) {
-    const int i = base + tid;
-    bool sel = false, eq = false;
-    if (i < n) {
-      if (all) sel = true;
-      else if (!none) {
-        const uint32_t kk = key(i);
-        sel = kk > T;
-        eq = kk == T;
-      }
-    }
-    // rank of this key among the keys equal to T, in index order
-    const uint64_t eqb = __ballot(eq);
-    if (lane == 0) sm.wave_cnt[w] = __popcll(eqb);
-    __syncthreads();
-    int eq_before = sm.run_eq;
-    for (int v = 0; v < w; ++v) eq_before += sm.wave_cnt[v];
-    eq_before += lanes_below(eqb);
-    if (eq && eq_before < take_eq) sel = true;
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int v = 0; v < NW; ++v) tot += sm.wave_cnt[v];
-      sm.run_eq += tot;
-    }
-    const uint64_t sb = __ballot(sel);
-    if (mask != nullptr && lane == 0 && (base + w * 64) < n) mask[(base + w * 64) >> 6] = sb;
-    __syncthreads();
-    if (lane == 0) sm.wave_cnt[w] = __popcll(sb);
-    __syncthreads();
-    int pos = sm.run_sel;
-    for (int v = 0; v < w; ++v) pos += sm.wave_cnt[v];
-    pos += lanes_below(sb);
-    if (sel && idx != nullptr) idx[pos] = i;
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int v = 0; v < NW; ++v) tot += sm.wave_cnt[v];
-      sm.run_sel += tot;
+  // Emission.  The kept keys equal to T are the first take_eq of them in index
+  // order, i.e. those at or below the index i_cut of the take_eq-th; thread t owns
+  // the run [t R, t R + R) of R = ceil(n / NT) consecutive indices, and two
+  // workgroup scans over the runs find i_cut and each run's first output slot.
+  // The mask words come from ballots over 64 consecutive indices.
+  __shared__ int s_scan[NW + 1];
+  __shared__ int s_cut;
+  const int R = (n + NT - 1) / NT;
+  const int ra = min(tid * R, n), rb = min(ra + R, n);
+  int i_cut = -1;
+  if (!all && !none) {
+    int ce = 0;
+    for (int i = ra; i < rb; ++i) ce += (int)(key(i) == T);
+    int tot;
+    const int before = block_excl_scan<NT>(ce, s_scan, &tot);
+    if (before < take_eq && take_eq <= before + ce) {
+      int c = before;
+      for (int i = ra; i < rb; ++i)
+        if (key(i) == T && ++c == take_eq) {
+          s_cut = i;
+          break;
+        }
     }
     __syncthreads();
+    i_cut = s_cut;
   }
+  auto selected = [&](int i) -> bool {
+    if (all) return true;
+    if (none) return false;
+    const uint32_t kk = key(i);
+    return kk > T || (kk == T && i <= i_cut);
+  };
+  if (idx != nullptr) {
+    int cs = 0;
+    for (int i = ra; i < rb; ++i) cs += (int)selected(i);
+    int tot;
+    int pos = block_excl_scan<NT>(cs, s_scan, &tot);
+    for (int i = ra; i < rb; ++i)
+      if (selected(i)) idx[pos++] = i;
+  }
+  if (mask != nullptr)
+    for (int i0 = w * 64; i0 < n; i0 += NT) {
+      const int i = i0 + lane;
+      const uint64_t sb = __ballot(i < n && selected(i));
+      if (lane == 0) mask[i0 >> 6] = sb;
+    }
 }
 
 // The same selection by a single wave, without workgroup barriers (only the

@@ -465,7 +465,8 @@ def row_topk(C, cpu):
     uv = C.graph_us([lambda: asg.as_topk_mask(h, 77) for _ in range(4)])
     r = {"step": "a6 exact top-k (LDS radix select, index tie-break) and GLASS rank blend",
          "blend_n14336_k7168_us": r4(ub), "value_128rows_n768_k77_us": r4(uv),
-         "note": "blend = two ordinal rankings (chunked counting, four values per thread) + LDS-staged radix select; once per prompt"}
+         "note": "blend = two ordinal rankings (256-key chunks sorted in LDS, then per value a binary search "
+                 "in every sorted chunk) + LDS-staged radix select; once per prompt"}
     if cpu:
         from oracle import topk
         L64, P64 = loc.cpu().double().numpy(), prior.cpu().double().numpy()
