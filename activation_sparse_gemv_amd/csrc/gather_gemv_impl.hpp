@@ -1162,6 +1162,27 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     // atomic stores) and the wave waits for their completion before the counter
     // increment; the last workgroup reads them back with coherent loads.  No
     // L2 writeback/invalidate fence is needed on any workgroup.
+    //
+    // Memory-ordering argument.  Under the HIP/C++ model alone this is not enough:
+    // relaxed atomics order nothing, and the portable form is a release on the
+    // counter increment and an acquire on the last workgroup's side.  At agent scope
+    // on this chip those fences become a writeback of the XCD's whole L2 and an
+    // invalidate of it, microseconds on every workgroup.  The protocol relies
+    // instead on what the AMDGPU memory model (LLVM AMDGPUUsage, gfx942/gfx950
+    // memory model) gives these operations on this target:
+    //  (1) an agent-scope atomic store/load is a global store/load with the cache
+    //      policy bits that make it coherent across the XCDs (no stale line in a
+    //      non-coherent per-XCD L2 can satisfy or absorb it);
+    //  (2) wait_vmem() (s_waitcnt vmcnt(0)) returns only after those stores are
+    //      acknowledged, i.e. performed at that coherent level;
+    //  (3) the __syncthreads() then orders every wave's completed stores before
+    //      thread 0's counter fetch-add, itself an agent-scope atomic performed at
+    //      the same level;
+    //  (4) the last workgroup issues its loads only after the fetch-add's returned
+    //      value is known (s_flag through LDS and a barrier), and those loads are
+    //      agent-scope atomic loads, so they read the coherent level.
+    // Every value written before (2) is therefore visible to the loads in (4).
+    // The bitwise run-twice tests and the integer-valued exact tests exercise it.
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int c = tid + q * kThreads;
