@@ -42,15 +42,16 @@ hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, f
 
 // ---------------------------------------------------------------- attention
 // One decode token.  Workgroup (kv head g, key chunk c) takes at most kMaxKeys
-// keys: every K and V row of its chunk (16 lanes per 256-byte row, 16 rows per
-// workgroup step, so at most 8 rows of each per thread) is loaded at entry, before
-// the query, so the chunk costs one round trip to memory.  Scores: each lane dots
-// its 8 dimensions with the group's query heads and the 16 lanes of a row add
+// keys: the group's query heads, then every K row and then every V row of its
+// chunk (16 lanes per 256-byte row, 16 rows per workgroup step, so at most 8 rows
+// of each per thread) are loaded at entry, so the chunk costs one round trip to
+// memory and the scores overlap the V rows still in flight.  Scores: each lane
+// dots its 8 dimensions with the group's query heads and the 16 lanes of a row add
 // theirs up with DPP row operations; the chunk's softmax statistics (max, sum of
 // exponentials) per head come from LDS; the unnormalised partial output sums the
 // value rows held in registers, reduced over the 16 rows in LDS in row order.  The
 // last chunk of a kv head to finish merges the chunks in chunk order
-// (deterministic).
+// (deterministic), in registers.
 constexpr int kAttThreads = 256;
 constexpr int kMaxGroup = 8;      // query heads per kv head
 constexpr int kAttHd = 128;       // head dimension of the vectorised path
@@ -78,29 +79,21 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   float* sc = qs + GM * hd;                // [GM][kMaxKeys] scores, then exp(score - max)
   float* red = sc + GM * kMaxKeys;         // [16][GM][hd] per key-row partial outputs
   __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
-  __shared__ float s_ml[kMaxChunks * kMaxGroup * 2];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ks = tid >> 4, l16 = tid & 15;   // key row slot 0..15, 8 dimensions 8 l16 ..
   const int dd0 = 8 * l16;
 
-  // every K and V row of the chunk, issued together (rows past the chunk repeat its
+  // the group's query heads first (small, read by every key row), then every K row
+  // and then every V row of the chunk, issued together: the scores start as the K
+  // rows arrive while the V rows are still in flight (rows past the chunk repeat its
   // last row; the current token's own row is fp32 and taken apart below)
-  u32x4 kr[kSteps], vr[kSteps];
+  constexpr int kQPer = (GM * kAttHd + kAttThreads - 1) / kAttThreads;
+  float qv[kQPer];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    int jj = ks + 16 * s;
-    jj = jj < nk ? jj : nk - 1;
-    int j = j0 + jj;
-    j = j < p.n_ctx ? j : (p.n_ctx > 0 ? p.n_ctx - 1 : 0);
-    const long off = ((long)j * p.n_kv + g) * hd + dd0;
-    if (p.n_ctx > 0) {
-      kr[s] = *reinterpret_cast<const u32x4*>(p.k_cache + off);
-      vr[s] = *reinterpret_cast<const u32x4*>(p.v_cache + off);
-    } else {
-      kr[s] = u32x4{0u, 0u, 0u, 0u};
-      vr[s] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int u = 0; u < kQPer; ++u) {
+    const int i = tid + u * kAttThreads;
+    qv[u] = i < grp * hd ? p.q[(long)(g * grp) * hd + i] : 0.f;
   }
   const bool has_fresh = j1 == n_keys;     // this chunk holds the current token's key
   float kf[8], vf[8];
@@ -111,8 +104,28 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
       vf[e] = p.v_new[(long)g * hd + dd0 + e];
     }
   }
+  u32x4 kr[kSteps], vr[kSteps];
+  long roff[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    int jj = ks + 16 * s;
+    jj = jj < nk ? jj : nk - 1;
+    int j = j0 + jj;
+    j = j < p.n_ctx ? j : (p.n_ctx > 0 ? p.n_ctx - 1 : 0);
+    roff[s] = ((long)j * p.n_kv + g) * hd + dd0;
+  }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+    kr[s] = p.n_ctx > 0 ? *reinterpret_cast<const u32x4*>(p.k_cache + roff[s]) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+    vr[s] = p.n_ctx > 0 ? *reinterpret_cast<const u32x4*>(p.v_cache + roff[s]) : u32x4{0u, 0u, 0u, 0u};
   const float scale = 1.0f / sqrtf((float)hd);
-  for (int i = tid; i < grp * hd; i += kAttThreads) qs[i] = p.q[(long)(g * grp) * hd + i] * scale;
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int i = tid + u * kAttThreads;
+    if (i < grp * hd) qs[i] = qv[u] * scale;
+  }
   __syncthreads();
 
   // scores
@@ -218,69 +231,67 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   }
   __syncthreads();
   if (!s_last) return;
-  // merge: O = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c.  The partial outputs
-  // of 32 chunks of every output of this thread are loaded together, issued before
-  // the chunk statistics are waited for; the weights exp(m_c - M) and the sums L
-  // depend on (chunk, head) only and are formed once in LDS.  Chunks are merged in
-  // chunk order.
-  constexpr int kOut = (GM * kAttHd + kAttThreads - 1) / kAttThreads;
-  const int n_out = (grp * hd + kAttThreads - 1) / kAttThreads;      // in use (uniform)
-  float ov[kOut][32];
-  auto load_ov = [&](int c0) {
+  // merge: O = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c per query head, M the
+  // largest chunk maximum, chunks in chunk order.  Thread t takes kPer consecutive
+  // outputs of one head; the statistics and partial outputs of a batch of chunks
+  // are loaded at once (one round trip per batch) and everything else stays in
+  // registers (no LDS, no barrier).  Over several batches the running sums are
+  // rescaled to the new maximum; with one batch (C <= kB) the arithmetic is the
+  // two-pass formula.
+  constexpr int kPer = GM * kAttHd >= kAttThreads ? GM * kAttHd / kAttThreads : 1;
+  constexpr int kB = GM >= 8 ? 16 : 32;
+  const int i0 = tid * kPer;
+  if (i0 >= grp * hd) return;
+  const int a = i0 / hd;
+  float M = -INFINITY, L = 0.f, O[kPer];
 #pragma unroll
-    for (int u = 0; u < kOut; ++u) {
-      if (u < n_out) {
-        const int i = min(tid + u * kAttThreads, grp * hd - 1), a = i / hd, dd = i % hd;
+  for (int u = 0; u < kPer; ++u) O[u] = 0.f;
+  for (int c0 = 0; c0 < C; c0 += kB) {
+    float mc[kB], lc[kB], ov[kPer][kB];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
-          const int cc = min(c0 + k, C - 1);
-          ov[u][k] = load_coherent(p.part_o + (((long)g * C + cc) * grp + a) * hd + dd);
+    for (int k = 0; k < kB; ++k) {
+      const long rec = ((long)g * C + min(c0 + k, C - 1)) * grp + a;
+      // (m, l) and the kPer outputs are adjacent: 8-byte coherent loads
+      const uint64_t ml = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p.part_ml + rec * 2),
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mc[k] = __uint_as_float((uint32_t)ml);
+      lc[k] = __uint_as_float((uint32_t)(ml >> 32));
+      const float* po = p.part_o + rec * hd + i0 % hd;
+      if constexpr (kPer % 2 == 0) {
+#pragma unroll
+        for (int u = 0; u < kPer; u += 2) {
+          const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(po + u), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          ov[u][k] = __uint_as_float((uint32_t)v);
+          ov[u + 1][k] = __uint_as_float((uint32_t)(v >> 32));
         }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) ov[u][k] = load_coherent(po + u);
       }
     }
-  };
-  load_ov(0);
-  for (int i = tid; i < C * grp * 2; i += kAttThreads) s_ml[i] = load_coherent(p.part_ml + (long)g * C * grp * 2 + i);
-  __syncthreads();
-  __shared__ float s_M[kMaxGroup], s_L[kMaxGroup];
-  __shared__ float s_w[kMaxChunks * kMaxGroup];                     // [C][grp] merge weights
-  if (tid < grp) {
-    float M = -INFINITY;
-    for (int cc = 0; cc < C; ++cc) M = fmaxf(M, s_ml[(cc * grp + tid) * 2]);
-    s_M[tid] = M;
-  }
-  __syncthreads();
-  for (int i = tid; i < C * grp; i += kAttThreads) s_w[i] = expf(s_ml[i * 2] - s_M[i % grp]);
-  __syncthreads();
-  if (tid < grp) {
-    float L = 0.f;
-    for (int cc = 0; cc < C; ++cc) L = fmaf(s_w[cc * grp + tid], s_ml[(cc * grp + tid) * 2 + 1], L);
-    s_L[tid] = L;
-  }
-  __syncthreads();
-  float O[kOut];
+    float Mb = M;
 #pragma unroll
-  for (int u = 0; u < kOut; ++u) O[u] = 0.f;
-  for (int c0 = 0; c0 < C; c0 += 32) {
-    if (c0 > 0) load_ov(c0);
+    for (int k = 0; k < kB; ++k)
+      if (c0 + k < C) Mb = fmaxf(Mb, mc[k]);
+    if (M != -INFINITY) {
+      const float r = expf(M - Mb);
+      L *= r;
 #pragma unroll
-    for (int u = 0; u < kOut; ++u) {
-      if (u < n_out) {
-        const int a = min(tid + u * kAttThreads, grp * hd - 1) / hd;
+      for (int u = 0; u < kPer; ++u) O[u] *= r;
+    }
 #pragma unroll
-        for (int k = 0; k < 32; ++k)
-          if (c0 + k < C) O[u] = fmaf(s_w[(c0 + k) * grp + a], ov[u][k], O[u]);
+    for (int k = 0; k < kB; ++k)
+      if (c0 + k < C) {
+        const float w = expf(mc[k] - Mb);
+        L = fmaf(w, lc[k], L);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) O[u] = fmaf(w, ov[u][k], O[u]);
       }
-    }
+    M = Mb;
   }
 #pragma unroll
-  for (int u = 0; u < kOut; ++u) {
-    const int i = tid + u * kAttThreads;
-    if (u < n_out && i < grp * hd) {
-      const int a = i / hd;
-      p.o[(long)(g * grp + a) * hd + i % hd] = O[u] / s_L[a];
-    }
-  }
+  for (int u = 0; u < kPer; ++u) p.o[(long)(g * grp + a) * hd + (i0 + u) % hd] = O[u] / L;
 }
 
 template <int GM>

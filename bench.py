@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--rows", default="", help="comma-separated row names to run (default: all)")
     ap.add_argument("--traffic-run", action="store_true",
                     help="counter run: a 256 MiB device copy (known bytes) then 16 headline sparse-MLP calls")
+    ap.add_argument("--trace-run", action="store_true",
+                    help="kernel-trace run: only the headline's timed sparse loop (warmup + steps, no debug, "
+                         "atomic or dense calls), for rocprofv3 --kernel-trace")
     return ap.parse_args()
 
 
@@ -187,6 +190,15 @@ def headline(a, C):
         used = [(s * a.layers + l) % n_tok for s in range(steps) for l in range(a.layers)]
         return total_ms, k1, k2, used, per_step
 
+    if a.trace_run:
+        # the headline's sparse gate/up kernel is dispatched here only by the timed loop
+        # (warmup first); calibration runs 16-token calls, which take other kernels
+        t_x, t_h = calibrate(a.sparsity)
+        total_ms, _, _, _, _ = run(t_x, t_h, a.flags, a.steps, a.warmup, per_kernel=False)
+        print(json.dumps({"trace_run": True, "warmup_calls": a.warmup * a.layers, "timed_calls": a.steps * a.layers,
+                          "us_per_layer": r4(total_ms * 1e3 / (a.steps * a.layers)),
+                          "kernel_source_sha256": kernel_source_hash()}), flush=True)
+        return None
     res = {}
     sweep = SWEEP if not a.no_sweep else (a.sparsity,)
     if a.sparsity not in sweep:
@@ -1053,6 +1065,9 @@ def main():
     C = Ctx(torch, asg, L, datagen, dev)
     if a.traffic_run:
         traffic_run(C)
+        return
+    if a.trace_run:
+        headline(a, C)
         return
     out, t_x, t_h, samples = headline(a, C)
     cpu = not a.no_cpu_baseline
