@@ -944,7 +944,7 @@ MoeWs carve_moe(Carver& c, int T, int top, const as_moe_weights* w) {
   MoeWs m;
   m.h = c.take<float>(size_t(T) * top * w->d_ff_e);
   m.partials = c.take<float>(size_t(T) * top * w->d_model);
-  m.counters = c.take<unsigned>(size_t(T) * moe_down_tiles(w->d_model));
+  m.counters = c.take<unsigned>(size_t(T) * moe_down_tiles(w->d_model, T * top));
   m.gu_cnt = c.take<unsigned>(256);
   m.keep = c.take<int>(size_t(T) * top * w->d_ff_e);
   m.kval = c.take<float>(size_t(T) * top * w->d_ff_e);
@@ -1005,7 +1005,7 @@ as_status moe_expert_impl(const char* fn, const void* X, as_dtype x_dt, int T, c
   p.ids = expert_ids; p.wts = expert_w;
   p.w_gu = reinterpret_cast<const uint16_t*>(w->w_gate_up); p.w_down = reinterpret_cast<const uint16_t*>(w->w_down);
   p.h = m.h; p.h_dbg = h_dbg; p.keep_dbg = (flags & AS_FLAG_FORCE_DENSE) ? nullptr : keep_dbg;
-  p.partials = m.partials; p.counters = m.counters; p.n_tiles = moe_down_tiles(w->d_model);
+  p.partials = m.partials; p.counters = m.counters; p.n_tiles = moe_down_tiles(w->d_model, T * top_k);
   if (moe_select_in_gu(T * top_k, w->d_ff_e, false)) { p.gu_cnt = m.gu_cnt; p.keep = m.keep; p.kval = m.kval; }
   if (rule.gate) {
     // every neuron's h is written (0 where dropped); the down stage keeps the nonzero
@@ -1181,7 +1181,7 @@ as_status moe_layer_impl(const char* fn, const void* X, as_dtype x_dt, int T, co
   pm.ids = ids; pm.wts = weights;
   pm.w_gu = reinterpret_cast<const uint16_t*>(ew.w_gate_up); pm.w_down = reinterpret_cast<const uint16_t*>(ew.w_down);
   pm.h = m.moe.h; pm.h_dbg = h_dbg; pm.keep_dbg = dense ? nullptr : keep_dbg;
-  pm.partials = m.moe.partials; pm.counters = m.moe.counters; pm.n_tiles = moe_down_tiles(d);
+  pm.partials = m.moe.partials; pm.counters = m.moe.counters; pm.n_tiles = moe_down_tiles(d, T * top_k);
   if (moe_select_in_gu(T * top_k, ew.d_ff_e, true)) { pm.gu_cnt = m.moe.gu_cnt; pm.keep = m.moe.keep; pm.kval = m.moe.kval; }
   if (rule.gate) {
     pm.gate_mode = 1;

@@ -147,7 +147,7 @@ struct MoeParams {
 hipError_t launch_router(const float* logits, int T, int E, int top, int* ids, float* wts, hipStream_t s);
 hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_ready, hipStream_t s);
 hipError_t launch_moe_down(int wdt, const MoeParams& p, hipStream_t s);
-int moe_down_tiles(int d_model);
+int moe_down_tiles(int d_model, int items);   // column tiles of the routed down stage
 // Launch shape of the routed gate/up stage (register chunks NK, neuron blocks, LDS).
 int moe_gu_nk_of(const MoeParams& p);
 int moe_gu_blocks_of(const MoeParams& p);

@@ -55,19 +55,30 @@ __global__ __launch_bounds__(kGuThreads) void expert_gu_kernel(const MoeParams p
 
 // ---------------------------------------------------------------- down
 constexpr int kDnThreads = 256;
-constexpr int kDnLpr = 64;                 // one wave covers 512 columns of one row
-constexpr int kDnTile = kDnLpr * 8;
-static_assert(kDnTile % 256 == 0, "the combine takes whole columns per thread");
+constexpr int kDnWaves = kDnThreads / 64;
+constexpr int kDnRed = kDnWaves * 512;     // floats of the row-slot reduction buffer, any tile width
 
-template <int WDT>
+// Column tile of the down stage: LPR lanes cover 8 * LPR columns of a row, so a wave
+// takes 64 / LPR rows at once.  512 columns (LPR 64) for many (token, slot) items;
+// 128 columns (LPR 16) for at most 32 items, which would otherwise leave most CUs idle
+// (one token: 8 items x 16 tiles instead of 8 x 4 workgroups, each loading a quarter
+// of the kept rows' bytes).  Measured on the 128-expert, d_model 2048 layer: one
+// token 38.1 us (was 40.9), four tokens 68.5 (69.1); sixteen tokens keep 512 columns.
+int moe_down_lpr(int items) { return items <= 32 ? 16 : 64; }
+
+template <int WDT, int LPR>
 __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams p) {
+  constexpr int TILE = LPR * 8;            // columns per workgroup
+  constexpr int RG = 64 / LPR;             // rows a wave takes at once
+  constexpr int NS = kDnWaves * RG;        // row slots of the workgroup
+  static_assert(NS * TILE == kDnRed, "the reduction buffer holds every slot's tile");
   extern __shared__ __align__(16) unsigned char smem[];
   // keep-set capacity: keep_k, or every neuron in gate-score mode
   const int kcap = p.gate_mode ? p.d_ff : p.keep_k;
   int* keep = reinterpret_cast<int*>(smem);                        // [kcap]
   float* kval = reinterpret_cast<float*>(smem + 4 * ((kcap + 3) & ~3));
-  float* red = kval + ((kcap + 3) & ~3);                           // [4][kDnTile]
-  float* hs = red + 4 * kDnTile;                   // [d_ff] when d_ff > 1024 (top-k mode only)
+  float* red = kval + ((kcap + 3) & ~3);                           // [NS][TILE]
+  float* hs = red + kDnRed;                        // [d_ff] when d_ff > 1024 (top-k mode only)
   __shared__ TopkSmem sm;
   __shared__ int s_last;
   const int item = blockIdx.x;                  // t * top + j
@@ -129,22 +140,23 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c0 = tile * kDnTile + lane * 8;
+  const int slot = wave * RG + lane / LPR, cl = lane % LPR;
+  const int c0 = tile * TILE + cl * 8;
   const bool cvalid = c0 < d;
   const uint16_t* Wd = p.w_down + (long)e * f * d + (cvalid ? c0 : 0);
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  // up to 24 kept rows per wave in one batch of independent loads (77 rows: one
-  // round trip for the four waves)
-  constexpr int U = 24;
-  for (int r = wave; r < kk; r += 4 * U) {
+  // 96 kept rows per workgroup in one batch of independent loads (77 rows: one
+  // round trip)
+  constexpr int U = 24 / RG;
+  for (int r = slot; r < kk; r += NS * U) {
     u32x4 w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = load_w16<true>(Wd + (long)keep[min(r + 4 * u, kk - 1)] * d);
+    for (int u = 0; u < U; ++u) w[u] = load_w16<true>(Wd + (long)keep[min(r + NS * u, kk - 1)] * d);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int rr = r + 4 * u;
+      const int rr = r + NS * u;
       const float hv = rr < kk ? kval[rr] : 0.f;
       float wf[8];
       unpack8<WDT>(w[u], wf);
@@ -153,29 +165,30 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
     }
   }
 #pragma unroll
-  for (int q = 0; q < 8; ++q) red[wave * kDnTile + lane * 8 + q] = acc[q];
+  for (int q = 0; q < 8; ++q) red[slot * TILE + cl * 8 + q] = acc[q];
   __syncthreads();
+  // the row slots' sums of column c, in slot order
+  auto slot_sum = [&](int c) {
+    float v = red[c];
+#pragma unroll
+    for (int sl = 1; sl < NS; ++sl) v += red[sl * TILE + c];
+    return v;
+  };
   const float wt = valid_e ? p.wts[item] : 0.f;
   if (p.atomic_y) {
     // w_tj * sum over kept neurons added straight into y (fp32, written or cleared
     // before this launch); no slot partials, no counter, no combine
     if (valid_e)
-      for (int c = threadIdx.x; c < kDnTile; c += kDnThreads) {
-        const int gc = tile * kDnTile + c;
-        if (gc < d) {
-          const float v = red[c] + red[kDnTile + c] + red[2 * kDnTile + c] + red[3 * kDnTile + c];
-          unsafeAtomicAdd(reinterpret_cast<float*>(p.y) + (long)t * d + gc, wt * v);
-        }
+      for (int c = threadIdx.x; c < TILE; c += kDnThreads) {
+        const int gc = tile * TILE + c;
+        if (gc < d) unsafeAtomicAdd(reinterpret_cast<float*>(p.y) + (long)t * d + gc, wt * slot_sum(c));
       }
     return;
   }
   // partial of this (token, slot): w_tj * sum over kept neurons, coherent store
-  for (int c = threadIdx.x; c < kDnTile; c += kDnThreads) {
-    const int gc = tile * kDnTile + c;
-    if (gc < d) {
-      const float v = red[c] + red[kDnTile + c] + red[2 * kDnTile + c] + red[3 * kDnTile + c];
-      store_coherent(p.partials + (long)item * d + gc, wt * v);
-    }
+  for (int c = threadIdx.x; c < TILE; c += kDnThreads) {
+    const int gc = tile * TILE + c;
+    if (gc < d) store_coherent(p.partials + (long)item * d + gc, wt * slot_sum(c));
   }
   wait_vmem();
   __syncthreads();
@@ -190,13 +203,14 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   (void)j;
   // both columns of a thread at once: the y values and eight slots' partials of
   // each column are loaded before any is added (one round trip for eight slots)
-  constexpr int kCols = kDnTile / kDnThreads;
+  constexpr int kCols = (TILE + kDnThreads - 1) / kDnThreads;
   const int top = p.top;
   int gcs[kCols];
   float v[kCols], yv[kCols];
 #pragma unroll
   for (int u = 0; u < kCols; ++u) {
-    gcs[u] = tile * kDnTile + threadIdx.x + u * kDnThreads;
+    const int cc = threadIdx.x + u * kDnThreads;
+    gcs[u] = cc < TILE ? tile * TILE + cc : d;              // d: not a column of this tile
     v[u] = 0.f;
     yv[u] = p.accumulate ? load_elem(p.y, p.y_dt, (long)t * d + (gcs[u] < d ? gcs[u] : 0)) : 0.f;
   }
@@ -223,9 +237,12 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
 
 hipError_t launch_moe_down(int wdt, const MoeParams& p, hipStream_t s) {
   const int kcap = p.gate_mode ? p.d_ff : p.keep_k;
-  const size_t sm2 = size_t(8) * ((kcap + 3) & ~3) + size_t(4) * kDnTile * 4 +
+  const size_t sm2 = size_t(8) * ((kcap + 3) & ~3) + size_t(kDnRed) * 4 +
                      (p.d_ff > 1024 && !p.gate_mode ? size_t(p.d_ff) * 4 : 0);
-  auto k2 = wdt == DT_BF16 ? expert_down_kernel<DT_BF16> : expert_down_kernel<DT_F16>;
+  const int lpr = moe_down_lpr(p.T * p.top);
+  if (p.n_tiles != moe_down_tiles(p.d_model, p.T * p.top)) return hipErrorInvalidValue;
+  auto k2 = lpr == 16 ? (wdt == DT_BF16 ? expert_down_kernel<DT_BF16, 16> : expert_down_kernel<DT_F16, 16>)
+                      : (wdt == DT_BF16 ? expert_down_kernel<DT_BF16, 64> : expert_down_kernel<DT_F16, 64>);
   if (sm2 > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k2), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(sm2));
@@ -258,7 +275,10 @@ hipError_t launch_moe(int wdt, const MoeParams& p, int max_unique, hipEvent_t y_
   return launch_moe_down(wdt, p, s);
 }
 
-int moe_down_tiles(int d_model) { return (d_model + kDnTile - 1) / kDnTile; }
+int moe_down_tiles(int d_model, int items) {
+  const int tile = moe_down_lpr(items) * 8;
+  return (d_model + tile - 1) / tile;
+}
 int moe_gu_nk_of(const MoeParams& p) { return moe_gu_nk(p); }
 int moe_gu_blocks_of(const MoeParams& p) { return moe_gu_blocks(p); }
 size_t moe_gu_smem_of(const MoeParams& p) { return moe_gu_smem(p); }
