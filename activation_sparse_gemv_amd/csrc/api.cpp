@@ -423,7 +423,8 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
   if (mo && !dense) {
     p.x_bits = mo->bits; p.x_bits_ld = (K + 63) / 64; p.x_idx = mo->idx; p.x_nnz = mo->nnz;
   }
-  int in = dense ? IN_ALL : (range ? IN_RANGE : IN_THRESH);
+  // a head list: the dense prologue over the listed heads' rows (equal shares per slice)
+  int in = (dense || head_dim > 0) ? IN_ALL : (range ? IN_RANGE : IN_THRESH);
   if (fz != nullptr) {
     if (norm) {
       // the whole vector is read by every workgroup; the dense baseline keeps every row

@@ -968,16 +968,50 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
         }
       }
     }
-  } else {  // IN_ALL: every row, no mask (dense baseline)
-    const int K = p.K;
+  } else {  // IN_ALL: every row, no mask (dense baseline); with a head list, every row of the listed heads
+    int K = p.K;
+    const int* hl = nullptr;
+    if constexpr (MT == 1) {
+      if (p.head_dim > 0) {
+        // the listed heads (entries outside [0, n_heads) ignored, repeats once) in
+        // ascending order, kept in the reduction buffer (unused until the main loop
+        // ends); the slices then take equal shares of those heads' rows
+        int* s_hl = reinterpret_cast<int*>(s_red);
+        for (int h = tid; h < p.n_heads; h += kThreads) s_head_on[h] = 0;
+        __syncthreads();
+        for (int q = tid; q < p.n_heads_keep; q += kThreads) {
+          const int h = p.heads[q];
+          if (h >= 0 && h < p.n_heads) s_head_on[h] = 1;
+        }
+        __syncthreads();
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int h = 4 * tid + e;
+          c += (h < p.n_heads && s_head_on[h]) ? 1 : 0;
+        }
+        int tot;
+        int off = block_excl_scan<kThreads>(c, s_scan, &tot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int h = 4 * tid + e;
+          if (h < p.n_heads && s_head_on[h]) s_hl[off++] = h;
+        }
+        __syncthreads();
+        K = tot * p.head_dim;
+        hl = s_hl;
+      }
+    }
     const int lo = split_point(sl, K, S), hi = split_point(sl + 1, K, S);
     cnt = hi - lo;
     for (int r = tid; r < cnt; r += kThreads) {
-      s_idx[r] = lo + r;
+      const int g = lo + r;
+      const int row = hl != nullptr ? hl[g / p.head_dim] * p.head_dim + g % p.head_dim : g;
+      s_idx[r] = row;
       float xv[MT];
-      load_tokens<MT>(p.x, p.x_dt, p.ldx, lo + r, M, xv);
+      load_tokens<MT>(p.x, p.x_dt, p.ldx, row, M, xv);
       if constexpr (WDT == DT_I8) {
-        const float sc = p.row_scale[lo + r];
+        const float sc = p.row_scale[row];
 #pragma unroll
         for (int m = 0; m < MT; ++m) xv[m] *= sc;
       }
