@@ -481,8 +481,9 @@ as_status as_select_top_fraction(const float *score, int rows, int n, int ar_num
  * One token.  X: [n_heads * head_dim] (f16/bf16/f32); heads: device int32 [n_keep]
  * (indices outside [0, n_heads) are ignored, repeats count once); W: [n_heads *
  * head_dim, N] input-major (f16/bf16, 16-byte aligned, N % 8 == 0); Y: [N].  One
- * launch: each row slice marks the listed heads in LDS and gathers only their
- * rows (every input of a kept head counts, zeros and NaN included).
+ * launch: each workgroup marks the listed heads in LDS, lists them in ascending
+ * order and gathers an equal share of their rows (every input of a kept head
+ * counts, zeros and NaN included).
  * ws: as_head_masked_gemv_ws_size bytes, zero-filled once.  flags:
  * AS_FLAG_ATOMIC_SPLITK, AS_FLAG_NO_NT_LOADS (others UNSUPPORTED).
  * Errors: INVALID_ARG for NULL pointers, n_heads outside 1..1024, n_keep outside
