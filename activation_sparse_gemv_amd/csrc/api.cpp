@@ -159,7 +159,7 @@ struct GemvWs {
 };
 GemvWs carve_gemv(Carver& c, const Plan& pl, int M, long part_ld) {
   GemvWs w;
-  w.counters = c.take<unsigned>(pl.n_tiles);
+  w.counters = c.take<unsigned>(size_t(pl.n_tiles) * kCounterStride);
   w.partials = c.take<float>(size_t(pl.S) * M * part_ld);
   return w;
 }
@@ -947,8 +947,8 @@ MoeWs carve_moe(Carver& c, int T, int top, const as_moe_weights* w) {
   MoeWs m;
   m.h = c.take<float>(size_t(T) * top * w->d_ff_e);
   m.partials = c.take<float>(size_t(T) * top * w->d_model);
-  m.counters = c.take<unsigned>(size_t(T) * moe_down_tiles(w->d_model, T * top));
-  m.gu_cnt = c.take<unsigned>(256);
+  m.counters = c.take<unsigned>(size_t(T) * moe_down_tiles(w->d_model, T * top) * kCounterStride);
+  m.gu_cnt = c.take<unsigned>(size_t(256) * kCounterStride);
   m.keep = c.take<int>(size_t(T) * top * w->d_ff_e);
   m.kval = c.take<float>(size_t(T) * top * w->d_ff_e);
   return m;
@@ -1254,15 +1254,15 @@ as_status as_rmsnorm(const void* X, as_dtype x_dt, int rows, int d, float eps, f
 }
 
 namespace {
-// Key chunks per kv head: chunks of about 64 keys, at most about one workgroup per
-// CU, but never more than attention_max_keys() keys in a chunk (0 when the context
-// needs more than attention_max_chunks() chunks).
+// Chunks of cached keys per kv head: about 64 keys each, at most about one
+// workgroup per CU, but never more than attention_max_keys() keys in a chunk (0
+// when the context needs more than attention_max_chunks() chunks).  The current
+// token's key rides with the last chunk.
 int attn_chunks(int n_ctx, int n_kv) {
-  const int n_keys = n_ctx + 1;
-  int c = (n_keys + 63) / 64;
+  int c = (n_ctx + 63) / 64;
   const int max_c = (num_cus() + n_kv - 1) / n_kv;       // about one workgroup per CU
   if (c > max_c) c = max_c;
-  const int min_c = (n_keys + attention_max_keys() - 1) / attention_max_keys();
+  const int min_c = (n_ctx + attention_max_keys() - 1) / attention_max_keys();
   if (c < min_c) c = min_c;
   if (c < 1) c = 1;
   return c > attention_max_chunks() ? 0 : c;
@@ -1278,7 +1278,7 @@ AttnWs carve_attn(Carver& c, int n_ctx, int n_q, int n_kv, int hd) {
   const int grp = n_q / n_kv;
   a.part_o = c.take<float>(size_t(n_kv) * C * grp * hd);
   a.part_ml = c.take<float>(size_t(n_kv) * C * grp * 2);
-  a.counters = c.take<unsigned>(size_t(n_kv));
+  a.counters = c.take<unsigned>(size_t(n_kv) * kCounterStride);
   return a;
 }
 }  // namespace
@@ -1304,7 +1304,7 @@ as_status as_gqa_decode_attention(const float* q, const float* k_new, const floa
   if (attn_chunks(n_ctx, n_kv) == 0)
     return fail(AS_ERR_UNSUPPORTED, "%s: n_ctx=%d above %d", fn, n_ctx,
                 attention_max_chunks() * attention_max_keys() - 1);
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return fail(AS_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   Carver c{reinterpret_cast<char*>(ws)};
   AttnWs a = carve_attn(c, n_ctx, n_q, n_kv, head_dim);

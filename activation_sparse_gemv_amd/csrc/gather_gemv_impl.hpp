@@ -1231,14 +1231,14 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
     __syncthreads();
     AS_PHASE(p, 4);
     if (tid == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
+      const unsigned prev = __hip_atomic_fetch_add(p.counters + (long)tile * kCounterStride, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       s_flag = (prev == unsigned(n_parts - 1));
     }
     __syncthreads();
     AS_PHASE(p, 5);
     if (!s_flag) return;
-    if (tid == 0) __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(p.counters + (long)tile * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // Batches of slices are loaded together for every token (one round trip per
     // batch, at most 128 values in flight per thread), then summed in slice order.
     constexpr int kBudget = 128 / (MT * CPT);

@@ -41,23 +41,31 @@ hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, f
 }
 
 // ---------------------------------------------------------------- attention
-// One decode token.  Workgroup (kv head g, key chunk c) takes at most kMaxKeys
-// keys: the group's query heads, then every K row and then every V row of its
-// chunk (16 lanes per 256-byte row, 16 rows per workgroup step, so at most 8 rows
-// of each per thread) are loaded at entry, so the chunk costs one round trip to
-// memory and the scores overlap the V rows still in flight.  Scores: each lane
-// dots its 8 dimensions with the group's query heads and the 16 lanes of a row add
-// theirs up with DPP row operations; the chunk's softmax statistics (max, sum of
-// exponentials) per head come from LDS; the unnormalised partial output sums the
-// value rows held in registers, reduced over the 16 rows in LDS in row order.  The
-// last chunk of a kv head to finish merges the chunks in chunk order
-// (deterministic), in registers.
-constexpr int kAttThreads = 256;
+// One decode token.  The n_ctx cached keys of each kv head are cut into C equal
+// chunks of at most 32 * KS keys; the current token's own key (fp32) rides with the
+// last chunk as one extra row.  Workgroup (kv head g, chunk c): 32 row slots of 16
+// lanes (one 256-byte row per slot and step, 8 dimensions per lane; two waves per
+// SIMD, so the dependent score and value chains of one wave hide behind the
+// other's); the group's
+// query heads go straight from memory into registers, every K row and then every V
+// row of the chunk are issued at entry, so the chunk costs one round trip and the
+// scores overlap the V rows still in flight.  Scores: 8-dimension dot products
+// summed over the 16 lanes of a row by DPP, kept in registers; the chunk maximum
+// per head from the 32 slot maxima (one barrier); exponentials (base 2: the query
+// scale carries log2(e), so every exponential is one hardware exp2) and the value
+// sums in registers; the 32 slots' partial outputs added in slot order through LDS
+// (second barrier).  Slot maxima and sums are combined within the wave first (one
+// entry per wave and head in LDS).  The chunk's (max, sum, output) record is stored
+// device-coherently and counted; the last chunk of a kv head to arrive merges
+// every record of the head in one round trip: the statistics give each chunk its
+// weight 2^(m_c - M) (M the largest chunk maximum), the weighted outputs are
+// added in chunk order and divided by sum_c 2^(m_c - M) l_c (deterministic).
+constexpr int kAttThreads = 512;
+constexpr int kSlots = kAttThreads / 16;   // row slots
 constexpr int kMaxGroup = 8;      // query heads per kv head
 constexpr int kAttHd = 128;       // head dimension of the vectorised path
 constexpr int kMaxChunks = 256;   // chunks per kv head
-constexpr int kMaxKeys = 128;     // keys per chunk: 8 row steps of 16
-constexpr int kSteps = kMaxKeys / 16;
+constexpr int kMaxKeys = 128;     // cached keys per chunk: 4 row steps of 32
 
 // Sum over the 16 lanes of each row (every lane of the row gets the row's sum).
 __device__ __forceinline__ float row16_sum(float v) {
@@ -66,239 +74,298 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-template <int GM>
+__device__ __forceinline__ float dot8(const float (&q)[8], const float (&k)[8]) {
+  float v = q[0] * k[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) v = fmaf(q[e], k[e], v);
+  return v;
+}
+
+// Two adjacent fp32 values read device-coherently (one 8-byte load).
+__device__ __forceinline__ float2 load_coherent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+template <int GM, int KS>
 __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams p) {
-  extern __shared__ __align__(16) float sm[];
+  extern __shared__ __align__(16) float red[];   // [kSlots][GM][hd] slot partial outputs; merge weights later
+  constexpr int NWV = kAttThreads / 64;
+  __shared__ __align__(16) float s_mx[NWV * GM];
+  __shared__ float s_ls[NWV * GM], s_L[GM];
+  __shared__ int s_last;
   constexpr int hd = kAttHd;
   const int grp = p.n_q / p.n_kv;
   const int g = blockIdx.x, c = blockIdx.y, C = gridDim.y;
-  const int n_keys = p.n_ctx + 1;
-  const int j0 = (int)((long)c * n_keys / C), j1 = (int)((long)(c + 1) * n_keys / C);
-  const int nk = j1 - j0;                  // <= kMaxKeys (the host sizes C)
-  float* qs = sm;                          // [GM][hd] query heads of the group, pre-scaled
-  float* sc = qs + GM * hd;                // [GM][kMaxKeys] scores, then exp(score - max)
-  float* red = sc + GM * kMaxKeys;         // [16][GM][hd] per key-row partial outputs
-  __shared__ float s_m[kMaxGroup], s_l[kMaxGroup];
-  __shared__ int s_last;
+  const int j0 = (int)((long)c * p.n_ctx / C), j1 = (int)((long)(c + 1) * p.n_ctx / C);
+  const int nk = j1 - j0;                  // cached keys of the chunk, <= kSlots * KS (the host sizes C)
+  const bool has_fresh = c == C - 1;       // the current token's key and value
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ks = tid >> 4, l16 = tid & 15;   // key row slot 0..15, 8 dimensions 8 l16 ..
+  const int ks = tid >> 4, l16 = tid & 15;   // row slot 0..31, dimensions 8 l16 .. 8 l16 + 7
   const int dd0 = 8 * l16;
 
-  // the group's query heads first (small, read by every key row), then every K row
-  // and then every V row of the chunk, issued together: the scores start as the K
-  // rows arrive while the V rows are still in flight (rows past the chunk repeat its
-  // last row; the current token's own row is fp32 and taken apart below)
-  constexpr int kQPer = (GM * kAttHd + kAttThreads - 1) / kAttThreads;
-  float qv[kQPer];
+  // this lane's 8 dimensions of every query head of the group, scaled by
+  // log2(e) / sqrt(hd): the scores are in base-2 units
+  const float scale = 1.4426950408889634f / sqrtf((float)hd);
+  float qv[GM][8];
 #pragma unroll
-  for (int u = 0; u < kQPer; ++u) {
-    const int i = tid + u * kAttThreads;
-    qv[u] = i < grp * hd ? p.q[(long)(g * grp) * hd + i] : 0.f;
+  for (int a = 0; a < GM; ++a) {
+    if (a < grp) {
+      const float4* qp = reinterpret_cast<const float4*>(p.q + (long)(g * grp + a) * hd + dd0);
+      const float4 x0 = qp[0], x1 = qp[1];
+      qv[a][0] = x0.x * scale; qv[a][1] = x0.y * scale; qv[a][2] = x0.z * scale; qv[a][3] = x0.w * scale;
+      qv[a][4] = x1.x * scale; qv[a][5] = x1.y * scale; qv[a][6] = x1.z * scale; qv[a][7] = x1.w * scale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[a][e] = 0.f;
+    }
   }
-  const bool has_fresh = j1 == n_keys;     // this chunk holds the current token's key
   float kf[8], vf[8];
   if (has_fresh) {
+    const float4* kp = reinterpret_cast<const float4*>(p.k_new + (long)g * hd + dd0);
+    const float4* vp = reinterpret_cast<const float4*>(p.v_new + (long)g * hd + dd0);
+    const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+    kf[0] = k0.x; kf[1] = k0.y; kf[2] = k0.z; kf[3] = k0.w; kf[4] = k1.x; kf[5] = k1.y; kf[6] = k1.z; kf[7] = k1.w;
+    vf[0] = v0.x; vf[1] = v0.y; vf[2] = v0.z; vf[3] = v0.w; vf[4] = v1.x; vf[5] = v1.y; vf[6] = v1.z; vf[7] = v1.w;
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kf[e] = p.k_new[(long)g * hd + dd0 + e];
-      vf[e] = p.v_new[(long)g * hd + dd0 + e];
-    }
+    for (int e = 0; e < 8; ++e) kf[e] = vf[e] = 0.f;
   }
-  u32x4 kr[kSteps], vr[kSteps];
-  long roff[kSteps];
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    int jj = ks + 16 * s;
-    jj = jj < nk ? jj : nk - 1;
-    int j = j0 + jj;
-    j = j < p.n_ctx ? j : (p.n_ctx > 0 ? p.n_ctx - 1 : 0);
-    roff[s] = ((long)j * p.n_kv + g) * hd + dd0;
-  }
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s)
-    kr[s] = p.n_ctx > 0 ? *reinterpret_cast<const u32x4*>(p.k_cache + roff[s]) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s)
-    vr[s] = p.n_ctx > 0 ? *reinterpret_cast<const u32x4*>(p.v_cache + roff[s]) : u32x4{0u, 0u, 0u, 0u};
-  const float scale = 1.0f / sqrtf((float)hd);
-#pragma unroll
-  for (int u = 0; u < kQPer; ++u) {
-    const int i = tid + u * kAttThreads;
-    if (i < grp * hd) qs[i] = qv[u] * scale;
-  }
-  __syncthreads();
 
-  // scores
+  // K rows, then V rows (slots past the chunk re-read its last row; their weights
+  // are 0 and they are skipped in the value sums)
+  u32x4 kr[KS], vr[KS];
+  if (nk > 0) {
+    long roff[KS];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int jj = ks + 16 * s;
-    if (16 * s < nk) {                     // uniform over the workgroup
+    for (int s = 0; s < KS; ++s) roff[s] = ((long)(j0 + min(ks + kSlots * s, nk - 1)) * p.n_kv + g) * hd + dd0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kr[s] = *reinterpret_cast<const u32x4*>(p.k_cache + roff[s]);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) vr[s] = *reinterpret_cast<const u32x4*>(p.v_cache + roff[s]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kr[s] = vr[s] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // scores: sc[s][a] for the row of slot ks at step s; step KS is the current
+  // token's key, held by slot 0 of the last chunk (-inf marks no row)
+  float sc[KS + 1][GM];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const bool valid = ks + kSlots * s < nk;
+    if (kSlots * s < nk) {                 // uniform over the workgroup
       float kv[8];
-      if (has_fresh && j0 + jj == p.n_ctx) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kv[e] = kf[e];
-      } else {
-        unpack8<DT_BF16>(kr[s], kv);
-      }
+      unpack8<DT_BF16>(kr[s], kv);
 #pragma unroll
       for (int a = 0; a < GM; ++a) {
+        float v = -INFINITY;
         if (a < grp) {
-          const float4 q0 = *reinterpret_cast<const float4*>(qs + a * hd + dd0);
-          const float4 q1 = *reinterpret_cast<const float4*>(qs + a * hd + dd0 + 4);
-          float v = q0.x * kv[0];
-          v = fmaf(q0.y, kv[1], v);
-          v = fmaf(q0.z, kv[2], v);
-          v = fmaf(q0.w, kv[3], v);
-          v = fmaf(q1.x, kv[4], v);
-          v = fmaf(q1.y, kv[5], v);
-          v = fmaf(q1.z, kv[6], v);
-          v = fmaf(q1.w, kv[7], v);
-          v = row16_sum(v);
-          if (l16 == 0 && jj < nk) sc[a * kMaxKeys + jj] = v;
+          v = row16_sum(dot8(qv[a], kv));
+          v = valid ? v : -INFINITY;
         }
+        sc[s][a] = v;
       }
+    } else {
+#pragma unroll
+      for (int a = 0; a < GM; ++a) sc[s][a] = -INFINITY;
     }
   }
+#pragma unroll
+  for (int a = 0; a < GM; ++a) {
+    float v = -INFINITY;
+    if (has_fresh && a < grp) {
+      v = row16_sum(dot8(qv[a], kf));
+      v = ks == 0 ? v : -INFINITY;
+    }
+    sc[KS][a] = v;
+  }
+  // chunk maximum per head: the wave's maximum over its 4 row slots (every lane of
+  // a slot holds the slot's value), one entry per wave in LDS
+#pragma unroll
+  for (int a = 0; a < GM; ++a) {
+    float m = sc[0][a];
+#pragma unroll
+    for (int s = 1; s <= KS; ++s) m = fmaxf(m, sc[s][a]);
+    m = fmaxf(fmaxf(readlane_f(m, 0), readlane_f(m, 16)), fmaxf(readlane_f(m, 32), readlane_f(m, 48)));
+    if (lane == 0) s_mx[wave * GM + a] = m;
+  }
   __syncthreads();
-  // chunk softmax statistics per query head (one wave per head)
-  for (int a = wave; a < grp; a += kAttThreads / 64) {
-    float m = -INFINITY;
-    for (int t = lane; t < nk; t += 64) m = fmaxf(m, sc[a * kMaxKeys + t]);
-    m = wave_max(m);
+  float l_loc[GM];
+  float Mx[GM];
+#pragma unroll
+  for (int a = 0; a < GM; ++a) Mx[a] = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    if constexpr (GM % 4 == 0) {
+#pragma unroll
+      for (int a = 0; a < GM; a += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(s_mx + w * GM + a);
+        Mx[a] = fmaxf(Mx[a], v.x); Mx[a + 1] = fmaxf(Mx[a + 1], v.y);
+        Mx[a + 2] = fmaxf(Mx[a + 2], v.z); Mx[a + 3] = fmaxf(Mx[a + 3], v.w);
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < GM; ++a) Mx[a] = fmaxf(Mx[a], s_mx[w * GM + a]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < GM; ++a) {
+    const float M = Mx[a];
     float l = 0.f;
-    for (int t = lane; t < nk; t += 64) {
-      const float e = expf(sc[a * kMaxKeys + t] - m);
-      sc[a * kMaxKeys + t] = e;
+#pragma unroll
+    for (int s = 0; s <= KS; ++s) {
+      const float e = sc[s][a] == -INFINITY ? 0.f : exp2f(sc[s][a] - M);
+      sc[s][a] = e;
       l += e;
     }
-    l = wave_sum(l);
-    if (lane == 0) { s_m[a] = m; s_l[a] = l; }
+    l_loc[a] = (readlane_f(l, 0) + readlane_f(l, 16)) + (readlane_f(l, 32) + readlane_f(l, 48));
   }
-  __syncthreads();
-  // unnormalised partial outputs of this thread's rows and 8 dimensions
-  {
-    float acc[GM][8];
+  // unnormalised partial outputs of this slot's rows, 8 dimensions
+  float acc[GM][8];
 #pragma unroll
-    for (int a = 0; a < GM; ++a)
+  for (int a = 0; a < GM; ++a)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int jj = ks + 16 * s;
-      if (jj < nk) {
-        float vv[8];
-        if (has_fresh && j0 + jj == p.n_ctx) {
+  for (int s = 0; s < KS; ++s) {
+    if (ks + kSlots * s < nk) {
+      float vv[8];
+      unpack8<DT_BF16>(vr[s], vv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vv[e] = vf[e];
-        } else {
-          unpack8<DT_BF16>(vr[s], vv);
-        }
+      for (int a = 0; a < GM; ++a)
+        if (a < grp)
 #pragma unroll
-        for (int a = 0; a < GM; ++a)
-          if (a < grp) {
-            const float pa = sc[a * kMaxKeys + jj];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(pa, vv[e], acc[a][e]);
-          }
-      }
+          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(sc[s][a], vv[e], acc[a][e]);
     }
+  }
+  if (has_fresh && ks == 0) {
 #pragma unroll
     for (int a = 0; a < GM; ++a)
-      if (a < grp) {
-        float4* dst = reinterpret_cast<float4*>(red + (ks * GM + a) * hd + dd0);
-        dst[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
-        dst[1] = make_float4(acc[a][4], acc[a][5], acc[a][6], acc[a][7]);
-      }
+      if (a < grp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(sc[KS][a], vf[e], acc[a][e]);
+  }
+#pragma unroll
+  for (int a = 0; a < GM; ++a) {
+    if (a < grp) {
+      float4* dst = reinterpret_cast<float4*>(red + (ks * GM + a) * hd + dd0);
+      dst[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+      dst[1] = make_float4(acc[a][4], acc[a][5], acc[a][6], acc[a][7]);
+      if (lane == 0) s_ls[wave * GM + a] = l_loc[a];
+    }
   }
   __syncthreads();
+  // the chunk's record: outputs summed over the slots in slot order, (max, sum)
   for (int i = tid; i < grp * hd; i += kAttThreads) {
     const int a = i / hd, dd = i % hd;
     float o = 0.f;
-    for (int r = 0; r < 16; ++r) o += red[(r * GM + a) * hd + dd];
-    const long base = ((long)g * C + c) * grp + a;          // partial record index
-    store_coherent(p.part_o + base * hd + dd, o);
-    if (dd == 0) {
-      store_coherent(p.part_ml + base * 2, s_m[a]);
-      store_coherent(p.part_ml + base * 2 + 1, s_l[a]);
-    }
+#pragma unroll
+    for (int r = 0; r < kSlots; ++r) o += red[(r * GM + a) * hd + dd];
+    const long rec = ((long)g * C + c) * grp + a;
+    store_coherent(p.part_o + rec * hd + dd, o);
+  }
+  if (tid < grp) {
+    float M = s_mx[tid], l = 0.f;
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) M = fmaxf(M, s_mx[w * GM + tid]);
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) l += s_ls[w * GM + tid];
+    const long rec = ((long)g * C + c) * grp + tid;
+    store_coherent(p.part_ml + rec * 2, M);
+    store_coherent(p.part_ml + rec * 2 + 1, l);
   }
   wait_vmem();
   __syncthreads();
   if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(p.counters + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev = __hip_atomic_fetch_add(p.counters + (long)g * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == unsigned(C - 1);
-    if (s_last) __hip_atomic_store(p.counters + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (s_last) __hip_atomic_store(p.counters + (long)g * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last) return;
-  // merge: O = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c per query head, M the
-  // largest chunk maximum, chunks in chunk order.  Thread t takes kPer consecutive
-  // outputs of one head; the statistics and partial outputs of a batch of chunks
-  // are loaded at once (one round trip per batch) and everything else stays in
-  // registers (no LDS, no barrier).  Over several batches the running sums are
-  // rescaled to the new maximum; with one batch (C <= kB) the arithmetic is the
-  // two-pass formula.
-  constexpr int kPer = GM * kAttHd >= kAttThreads ? GM * kAttHd / kAttThreads : 1;
-  constexpr int kB = GM >= 8 ? 16 : 32;
-  const int i0 = tid * kPer;
-  if (i0 >= grp * hd) return;
-  const int a = i0 / hd;
-  float M = -INFINITY, L = 0.f, O[kPer];
+
+  // merge.  Wave w takes head a = w % GM and the w / GM-th of NWV / GM equal runs of
+  // chunks; a record (128 floats) is one 512-byte load instruction of the wave,
+  // lane l holding dimensions 2l, 2l + 1.  Every wave first loads its head's
+  // statistics (lane c: chunks c, c + 64, ..), then a batch of up to kB records;
+  // the chunk weights 2^(m_c - M) go to LDS while the records are in flight.  The
+  // runs are added in order through LDS at the end.
+  constexpr int WPH = NWV / GM;            // waves per head
+  constexpr int kB = 16;
+  const int a = min(wave % GM, grp - 1), run = wave / GM;
+  const bool live = wave % GM < grp;
+  const int cb = run * C / WPH, ce = (run + 1) * C / WPH;
+  float2 ml[4];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) O[u] = 0.f;
-  for (int c0 = 0; c0 < C; c0 += kB) {
-    float mc[kB], lc[kB], ov[kPer][kB];
-#pragma unroll
-    for (int k = 0; k < kB; ++k) {
-      const long rec = ((long)g * C + min(c0 + k, C - 1)) * grp + a;
-      // (m, l) and the kPer outputs are adjacent: 8-byte coherent loads
-      const uint64_t ml = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p.part_ml + rec * 2),
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      mc[k] = __uint_as_float((uint32_t)ml);
-      lc[k] = __uint_as_float((uint32_t)(ml >> 32));
-      const float* po = p.part_o + rec * hd + i0 % hd;
-      if constexpr (kPer % 2 == 0) {
-#pragma unroll
-        for (int u = 0; u < kPer; u += 2) {
-          const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(po + u), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-          ov[u][k] = __uint_as_float((uint32_t)v);
-          ov[u + 1][k] = __uint_as_float((uint32_t)(v >> 32));
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) ov[u][k] = load_coherent(po + u);
-      }
-    }
-    float Mb = M;
-#pragma unroll
-    for (int k = 0; k < kB; ++k)
-      if (c0 + k < C) Mb = fmaxf(Mb, mc[k]);
-    if (M != -INFINITY) {
-      const float r = expf(M - Mb);
-      L *= r;
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) O[u] *= r;
-    }
-#pragma unroll
-    for (int k = 0; k < kB; ++k)
-      if (c0 + k < C) {
-        const float w = expf(mc[k] - Mb);
-        L = fmaf(w, lc[k], L);
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) O[u] = fmaf(w, ov[u][k], O[u]);
-      }
-    M = Mb;
+  for (int u = 0; u < 4; ++u) {
+    const int cc = min(lane + 64 * u, C - 1);
+    ml[u] = load_coherent2(p.part_ml + (((long)g * C + cc) * grp + a) * 2);
   }
+  float2 ob[kB];
+  const float* rec0 = p.part_o + ((long)g * C * grp + a) * hd + 2 * lane;
+  const long rec_ld = (long)grp * hd;      // floats between the records of consecutive chunks
+  auto load_batch = [&](int c0) {
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) p.o[(long)(g * grp + a) * hd + (i0 + u) % hd] = O[u] / L;
+    for (int k = 0; k < kB; ++k) ob[k] = load_coherent2(rec0 + (long)min(c0 + k, C - 1) * rec_ld);
+  };
+  load_batch(cb);
+  float Mh = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (lane + 64 * u < C) Mh = fmaxf(Mh, ml[u].x);
+  Mh = wave_max(Mh);
+  float lsum = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int cc = lane + 64 * u;
+    if (cc < C) {
+      const float w = ml[u].x == -INFINITY ? 0.f : exp2f(ml[u].x - Mh);
+      if (live && run == 0) red[a * C + cc] = w;
+      lsum = fmaf(w, ml[u].y, lsum);
+    }
+  }
+  lsum = wave_sum(lsum);
+  if (live && run == 0 && lane == 0) s_L[a] = lsum;
+  __syncthreads();
+  float2 O = make_float2(0.f, 0.f);
+  for (int c0 = cb; c0 < ce; c0 += kB) {
+    if (c0 != cb) load_batch(c0);
+#pragma unroll
+    for (int k = 0; k < kB; ++k)
+      if (c0 + k < ce) {
+        const float w = red[a * C + c0 + k];
+        O.x = fmaf(w, ob[k].x, O.x);
+        O.y = fmaf(w, ob[k].y, O.y);
+      }
+  }
+  // runs of one head added in run order (LDS past the weights)
+  float2* s_run = reinterpret_cast<float2*>(red + ((GM * C + 1) & ~1));
+  if constexpr (WPH > 1) {
+    if (live && run > 0) s_run[((run - 1) * GM + a) * 64 + lane] = O;
+    __syncthreads();
+    if (run == 0) {
+#pragma unroll
+      for (int r = 1; r < WPH; ++r) {
+        const float2 v = s_run[((r - 1) * GM + a) * 64 + lane];
+        O.x += v.x;
+        O.y += v.y;
+      }
+    }
+  }
+  if (live && run == 0) {
+    const float L = s_L[a];
+    float* dst = p.o + (long)(g * grp + a) * hd + 2 * lane;
+    dst[0] = O.x / L;
+    dst[1] = O.y / L;
+  }
 }
 
-template <int GM>
+template <int GM, int KS>
 hipError_t launch_attention_g(const AttnParams& p, int chunks, hipStream_t s) {
-  const size_t smem = (size_t(GM) * kAttHd + size_t(GM) * kMaxKeys + size_t(16) * GM * kAttHd) * 4;
-  auto k = attention_kernel<GM>;
-  if (smem > 64 * 1024) {
+  const size_t smem = size_t(kSlots) * GM * kAttHd * 4;
+  auto k = attention_kernel<GM, KS>;
+  if (smem > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(smem));
     if (e != hipSuccess) return e;
@@ -307,13 +374,20 @@ hipError_t launch_attention_g(const AttnParams& p, int chunks, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s) {
+template <int KS>
+hipError_t launch_attention_ks(const AttnParams& p, int chunks, hipStream_t s) {
   const int grp = p.n_q / p.n_kv;
-  if (chunks < 1 || chunks > kMaxChunks || (p.n_ctx + 1 + chunks - 1) / chunks > kMaxKeys) return hipErrorInvalidValue;
-  if (grp <= 1) return launch_attention_g<1>(p, chunks, s);
-  if (grp <= 2) return launch_attention_g<2>(p, chunks, s);
-  if (grp <= 4) return launch_attention_g<4>(p, chunks, s);
-  return launch_attention_g<8>(p, chunks, s);
+  if (grp <= 1) return launch_attention_g<1, KS>(p, chunks, s);
+  if (grp <= 2) return launch_attention_g<2, KS>(p, chunks, s);
+  if (grp <= 4) return launch_attention_g<4, KS>(p, chunks, s);
+  return launch_attention_g<8, KS>(p, chunks, s);
+}
+
+hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s) {
+  if (chunks < 1 || chunks > kMaxChunks || p.n_q / p.n_kv > kMaxGroup) return hipErrorInvalidValue;
+  const int longest = (p.n_ctx + chunks - 1) / chunks;     // cached keys of the longest chunk
+  if (longest > kMaxKeys) return hipErrorInvalidValue;
+  return longest <= 2 * kSlots ? launch_attention_ks<2>(p, chunks, s) : launch_attention_ks<4>(p, chunks, s);
 }
 
 int attention_max_group() { return kMaxGroup; }

@@ -9,6 +9,11 @@
 
 namespace as {
 
+// Arrival counters (split-K tiles, MoE down tiles, attention kv heads) sit
+// kCounterStride uints apart, one 256-byte line each: counters that share a line
+// have every workgroup's atomic queue on that one line.
+constexpr int kCounterStride = 64;
+
 enum { IN_THRESH = 0, IN_LISTS = 1, IN_ALL = 2, IN_RANGE = 4, IN_PARTS = 5 };
 enum { OUT_Y = 0, OUT_SWIGLU = 1, OUT_PARTS = 2, OUT_ROUTER = 3 };
 

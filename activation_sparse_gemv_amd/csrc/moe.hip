@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_kernel(const MoeParams
   wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned* cnt = p.counters + (long)t * p.n_tiles + tile;
+    unsigned* cnt = p.counters + ((long)t * p.n_tiles + tile) * kCounterStride;
     const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == unsigned(p.top - 1);
     if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -406,9 +406,9 @@ __device__ __forceinline__ void expert_gu_block(const MoeParams& p, int u, int n
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned nblk = (unsigned)((f + p.neurons_per_block - 1) / p.neurons_per_block);
-    const unsigned prev = __hip_atomic_fetch_add(p.gu_cnt + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev = __hip_atomic_fetch_add(p.gu_cnt + (long)u * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == nblk - 1;
-    if (s_last) __hip_atomic_store(p.gu_cnt + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (s_last) __hip_atomic_store(p.gu_cnt + (long)u * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last || p.keep_k <= 0) return;

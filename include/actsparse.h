@@ -535,7 +535,11 @@ as_status as_rmsnorm(const void *X, as_dtype x_dt, int rows, int d, float eps,
  * of kv head h / (n_q / n_kv) followed by the current token's k_new / v_new.
  * q: [n_q, hd] fp32; k_new, v_new: [n_kv, hd] fp32; caches: [n_ctx, n_kv, hd]
  * (AS_BF16 only); o: [n_q, hd] fp32.  n_q % n_kv == 0, n_q / n_kv <= 8,
- * head_dim == 128, 0 <= n_ctx <= 32767 (UNSUPPORTED above). */
+ * head_dim == 128, 0 <= n_ctx <= 32767 (UNSUPPORTED above).  q, k_new, v_new
+ * and the caches 16-byte aligned (INVALID_ARG otherwise).  The cached keys of a
+ * kv head are split into up to 256 chunks reduced side by side and merged in
+ * chunk order by the last one to finish (bitwise reproducible); the workspace
+ * holds the chunk records and one counter per kv head, zero between calls. */
 size_t as_gqa_decode_attention_ws_size(int n_ctx, int n_q, int n_kv, int head_dim);
 as_status as_gqa_decode_attention(const float *q, const float *k_new, const float *v_new,
                                   const void *k_cache, const void *v_cache, as_dtype kv_dt,
