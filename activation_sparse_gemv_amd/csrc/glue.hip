@@ -51,11 +51,12 @@ hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, f
 // row of the chunk are issued at entry, so the chunk costs one round trip and the
 // scores overlap the V rows still in flight.  Scores: 8-dimension dot products
 // summed over the 16 lanes of a row by DPP, kept in registers; the chunk maximum
-// per head from the 32 slot maxima (one barrier); exponentials (base 2: the query
+// per head from the slot maxima (one barrier); exponentials (base 2: the query
 // scale carries log2(e), so every exponential is one hardware exp2) and the value
-// sums in registers; the 32 slots' partial outputs added in slot order through LDS
-// (second barrier).  Slot maxima and sums are combined within the wave first (one
-// entry per wave and head in LDS).  The chunk's (max, sum, output) record is stored
+// sums in registers; the partial outputs of the wave's four slots added by
+// cross-row lane swaps, then the eight waves' through LDS in wave order (second
+// barrier).  Slot maxima and sums are likewise combined within the wave first
+// (one entry per wave and head in LDS).  The chunk's (max, sum, output) record is stored
 // device-coherently and counted; the last chunk of a kv head to arrive merges
 // every record of the head in one round trip: the statistics give each chunk its
 // weight 2^(m_c - M) (M the largest chunk maximum), the weighted outputs are
@@ -81,6 +82,11 @@ __device__ __forceinline__ float dot8(const float (&q)[8], const float (&k)[8]) 
   return v;
 }
 
+// 2^x by the hardware instruction alone (no range fix-up: arguments below -126,
+// whose results would be subnormal, give 0 or a subnormal; softmax weights that
+// small do not change a sum of weights of which the largest is 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Two adjacent fp32 values read device-coherently (one 8-byte load).
 __device__ __forceinline__ float2 load_coherent2(const float* p) {
   const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
@@ -90,7 +96,7 @@ __device__ __forceinline__ float2 load_coherent2(const float* p) {
 
 template <int GM, int KS>
 __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams p) {
-  extern __shared__ __align__(16) float red[];   // [kSlots][GM][hd] slot partial outputs; merge weights later
+  extern __shared__ __align__(16) float red[];   // [NWV][GM][hd] wave partial outputs; merge weights later
   constexpr int NWV = kAttThreads / 64;
   __shared__ __align__(16) float s_mx[NWV * GM];
   __shared__ float s_ls[NWV * GM], s_L[GM];
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     float l = 0.f;
 #pragma unroll
     for (int s = 0; s <= KS; ++s) {
-      const float e = sc[s][a] == -INFINITY ? 0.f : exp2f(sc[s][a] - M);
+      const float e = sc[s][a] == -INFINITY ? 0.f : fast_exp2(sc[s][a] - M);
       sc[s][a] = e;
       l += e;
     }
@@ -246,22 +252,42 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(sc[KS][a], vf[e], acc[a][e]);
   }
+  // The wave's four row slots are summed with cross-row lane swaps: four values
+  // (A, B, E, F) become one register whose row r holds the slot sum of the value
+  // 4q + {0, 2, 1, 3}[r], i.e. (A.R0 + A.R2) + (A.R1 + A.R3) etc. (fixed order).
+  constexpr int NQ = GM * 8 / 4;
+  float outq[NQ];
 #pragma unroll
-  for (int a = 0; a < GM; ++a) {
-    if (a < grp) {
-      float4* dst = reinterpret_cast<float4*>(red + (ks * GM + a) * hd + dd0);
-      dst[0] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
-      dst[1] = make_float4(acc[a][4], acc[a][5], acc[a][6], acc[a][7]);
-      if (lane == 0) s_ls[wave * GM + a] = l_loc[a];
+  for (int q = 0; q < NQ; ++q) {
+    const int v = 4 * q;
+    const float A = acc[v / 8][v % 8], B = acc[(v + 1) / 8][(v + 1) % 8];
+    const float E = acc[(v + 2) / 8][(v + 2) % 8], F = acc[(v + 3) / 8][(v + 3) % 8];
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(A), __float_as_uint(B), false, false);
+    const float Cq = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(E), __float_as_uint(F), false, false);
+    const float Dq = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(Cq), __float_as_uint(Dq), false, false);
+    outq[q] = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+  }
+  {
+    const int rr = lane >> 4;
+    const int pr = rr == 1 ? 2 : (rr == 2 ? 1 : rr);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int v = 4 * q + pr, a = v >> 3, e = v & 7;
+      red[(wave * GM + a) * hd + dd0 + e] = outq[q];
     }
+#pragma unroll
+    for (int a = 0; a < GM; ++a)
+      if (a < grp && lane == 0) s_ls[wave * GM + a] = l_loc[a];
   }
   __syncthreads();
-  // the chunk's record: outputs summed over the slots in slot order, (max, sum)
+  // the chunk's record: outputs summed over the waves in wave order, (max, sum)
   for (int i = tid; i < grp * hd; i += kAttThreads) {
     const int a = i / hd, dd = i % hd;
     float o = 0.f;
 #pragma unroll
-    for (int r = 0; r < kSlots; ++r) o += red[(r * GM + a) * hd + dd];
+    for (int w = 0; w < NWV; ++w) o += red[(w * GM + a) * hd + dd];
     const long rec = ((long)g * C + c) * grp + a;
     store_coherent(p.part_o + rec * hd + dd, o);
   }
@@ -320,7 +346,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   for (int u = 0; u < 4; ++u) {
     const int cc = lane + 64 * u;
     if (cc < C) {
-      const float w = ml[u].x == -INFINITY ? 0.f : exp2f(ml[u].x - Mh);
+      const float w = ml[u].x == -INFINITY ? 0.f : fast_exp2(ml[u].x - Mh);
       if (live && run == 0) red[a * C + cc] = w;
       lsum = fmaf(w, ml[u].y, lsum);
     }
@@ -363,7 +389,11 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
 
 template <int GM, int KS>
 hipError_t launch_attention_g(const AttnParams& p, int chunks, hipStream_t s) {
-  const size_t smem = size_t(kSlots) * GM * kAttHd * 4;
+  constexpr int NWV = kAttThreads / 64, WPH = NWV / GM;
+  // wave partial outputs, or the merge's chunk weights and run sums
+  const size_t chunk_f = size_t(NWV) * GM * kAttHd;
+  const size_t merge_f = size_t(GM) * kMaxChunks + 2 + size_t(WPH - 1) * GM * 128;
+  const size_t smem = (chunk_f > merge_f ? chunk_f : merge_f) * 4;
   auto k = attention_kernel<GM, KS>;
   if (smem > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
