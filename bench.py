@@ -930,6 +930,13 @@ def row_block(C, cpu):
             evs[layer + 1].record(C.stream)
         torch.cuda.synchronize()
         per[i] = [evs[k].elapsed_ms(evs[k + 1]) * 1e3 for k in range(nbk)]
+    # decode attention alone (n_ctx 2048, 32/8 heads) over the 32 blocks' own caches
+    gq = torch.Generator(device="cpu").manual_seed(7)
+    qa = torch.randn((32, 128), generator=gq).to(C.dev)
+    kna = torch.randn((8, 128), generator=gq).to(C.dev)
+    vna = torch.randn((8, 128), generator=gq).to(C.dev)
+    us_att = C.graph_us([lambda kc=kc, vc=vc: asg.as_gqa_decode_attention(qa, kna, vna, kc, vc)
+                         for (_, kc, vc) in blocks], reps=10)
     # active bytes of one token's step, from the masks the GPU applied
     act, x = [], toks[0]
     kv_b = 2 * blocks[0][1].numel() * 2
@@ -949,6 +956,8 @@ def row_block(C, cpu):
          "us_per_block": r4(us_blk), "dense_us_per_block": r4(us_blk_d),
          "active_gb_per_step_incl_kv": r4(ab / 1e9), "dense_gb_per_step": r4(dense_b * nbk / 1e9),
          "gbs": r4(ab / (step_us * 1e-6) / 1e9), "frac_hbm": r4(ab / (step_us * 1e-6) / 8e12),
+         "attention_us": r4(us_att), "attention_kv_mb": r4(kv_b / 1e6),
+         "attention_frac_hbm": r4(kv_b / (us_att * 1e-6) / 8e12),
          "eager_block_us_p50": {"layer0": r4(np.median(per[:, 0])), "layer31": r4(np.median(per[:, -1])),
                                 "all": r4(np.median(per))},
          "timing": "graph replays of 8 decode steps (8 tokens x 32 blocks); eager per-block times from events "
