@@ -510,6 +510,17 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
                           const GemvFuse* fz);
 
 #ifdef AS_PHASE_TIMELINE
+static std::atomic<unsigned long long*> g_attn_phase_buf{nullptr};
+static std::atomic<size_t> g_attn_phase_words{0};
+
+as_status as_attention_timeline_arm(uint64_t* buf, size_t words) {
+  if (buf == nullptr || words < 32)
+    return fail(AS_ERR_INVALID_ARG, "as_attention_timeline_arm: NULL buffer or < 32 words");
+  g_attn_phase_words.store(words);
+  g_attn_phase_buf.store(reinterpret_cast<unsigned long long*>(buf));
+  return AS_OK;
+}
+
 static std::atomic<unsigned long long*> g_phase_buf{nullptr};
 static std::atomic<size_t> g_phase_words{0};
 
@@ -1315,7 +1326,14 @@ as_status as_gqa_decode_attention(const float* q, const float* k_new, const floa
   p.k_cache = reinterpret_cast<const uint16_t*>(k_cache); p.v_cache = reinterpret_cast<const uint16_t*>(v_cache);
   p.n_ctx = n_ctx; p.n_q = n_q; p.n_kv = n_kv; p.head_dim = head_dim;
   p.o = o; p.part_o = a.part_o; p.part_ml = a.part_ml; p.counters = a.counters;
-  return hip_check(launch_attention(p, attn_chunks(n_ctx, n_kv), stream), fn);
+  const int C = attn_chunks(n_ctx, n_kv);
+#ifdef AS_PHASE_TIMELINE
+  {
+    unsigned long long* tl = g_attn_phase_buf.exchange(nullptr);
+    if (tl != nullptr && size_t(n_kv) * C * 16 <= g_attn_phase_words.load()) p.phase_tl = tl;
+  }
+#endif
+  return hip_check(launch_attention(p, C, stream), fn);
 }
 
 namespace {

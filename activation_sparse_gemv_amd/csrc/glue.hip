@@ -82,6 +82,20 @@ __device__ __forceinline__ float dot8(const float (&q)[8], const float (&k)[8]) 
   return v;
 }
 
+// Phase timeline (libactsparse_timeline.so only): thread 0 of each workgroup writes
+// the device's 100 MHz clock at the phase boundaries listed with
+// as_attention_timeline_arm.
+#ifdef AS_PHASE_TIMELINE
+#define AS_ATT_PHASE(p, slot)                                                                           \
+  do {                                                                                                  \
+    if ((p).phase_tl != nullptr && threadIdx.x == 0)                                                    \
+      (p).phase_tl[((long)blockIdx.x + (long)gridDim.x * blockIdx.y) * 16 + (slot)] =                   \
+          __builtin_amdgcn_s_memrealtime();                                                              \
+  } while (0)
+#else
+#define AS_ATT_PHASE(p, slot) do {} while (0)
+#endif
+
 // 2^x by the hardware instruction alone (no range fix-up: arguments below -126,
 // whose results would be subnormal, give 0 or a subnormal; softmax weights that
 // small do not change a sum of weights of which the largest is 1).
@@ -110,6 +124,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ks = tid >> 4, l16 = tid & 15;   // row slot 0..31, dimensions 8 l16 .. 8 l16 + 7
   const int dd0 = 8 * l16;
+  AS_ATT_PHASE(p, 0);
 
   // this lane's 8 dimensions of every query head of the group, scaled by
   // log2(e) / sqrt(hd): the scores are in base-2 units
@@ -186,6 +201,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     }
     sc[KS][a] = v;
   }
+  AS_ATT_PHASE(p, 1);
   // chunk maximum per head: the wave's maximum over its 4 row slots (every lane of
   // a slot holds the slot's value), one entry per wave in LDS
 #pragma unroll
@@ -197,6 +213,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     if (lane == 0) s_mx[wave * GM + a] = m;
   }
   __syncthreads();
+  AS_ATT_PHASE(p, 2);
   float l_loc[GM];
   float Mx[GM];
 #pragma unroll
@@ -282,6 +299,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
       if (a < grp && lane == 0) s_ls[wave * GM + a] = l_loc[a];
   }
   __syncthreads();
+  AS_ATT_PHASE(p, 3);
   // the chunk's record: outputs summed over the waves in wave order, (max, sum)
   for (int i = tid; i < grp * hd; i += kAttThreads) {
     const int a = i / hd, dd = i % hd;
@@ -302,6 +320,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     store_coherent(p.part_ml + rec * 2 + 1, l);
   }
   wait_vmem();
+  AS_ATT_PHASE(p, 4);
   __syncthreads();
   if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(p.counters + (long)g * kCounterStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -309,6 +328,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     if (s_last) __hip_atomic_store(p.counters + (long)g * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  AS_ATT_PHASE(p, 5);
   if (!s_last) return;
 
   // merge.  Wave w takes head a = w % GM and the w / GM-th of NWV / GM equal runs of
@@ -354,6 +374,7 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   lsum = wave_sum(lsum);
   if (live && run == 0 && lane == 0) s_L[a] = lsum;
   __syncthreads();
+  AS_ATT_PHASE(p, 6);
   float2 O = make_float2(0.f, 0.f);
   for (int c0 = cb; c0 < ce; c0 += kB) {
     if (c0 != cb) load_batch(c0);
@@ -385,6 +406,10 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     dst[0] = O.x / L;
     dst[1] = O.y / L;
   }
+#ifdef AS_PHASE_TIMELINE
+  if (p.phase_tl != nullptr && tid == 0) wait_vmem();
+#endif
+  AS_ATT_PHASE(p, 7);
 }
 
 template <int GM, int KS>

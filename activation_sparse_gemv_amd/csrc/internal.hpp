@@ -176,6 +176,7 @@ struct AttnParams {
   const uint16_t* k_cache; const uint16_t* v_cache;            // bf16 [n_ctx, n_kv, head_dim]
   int n_ctx, n_q, n_kv, head_dim;
   float* o; float* part_o; float* part_ml; unsigned* counters;
+  unsigned long long* phase_tl = nullptr;   // timeline build only: per-workgroup stamps
 };
 hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, float* y, float* copy, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int chunks, hipStream_t s);

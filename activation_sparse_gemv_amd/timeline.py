@@ -1,7 +1,9 @@
-"""Phase timeline of the one-token sparse SwiGLU MLP (Llama-3-8B shape).
+"""Phase timelines of the one-token sparse SwiGLU MLP (Llama-3-8B shape) and of
+the decode attention (n_ctx 2048, 32 query / 8 kv heads).
 
     python -m activation_sparse_gemv_amd.build --timeline
     python -m activation_sparse_gemv_amd.timeline [--sparsity 0.5] [--reps 8] [--out FILE]
+    python -m activation_sparse_gemv_amd.timeline --attention [--reps 8] [--out FILE]
 
 Loads libactsparse_timeline.so (the opt-in build whose kernels write the device's
 100 MHz clock at phase boundaries, include/actsparse_timeline.h) instead of
@@ -99,7 +101,10 @@ def main(argv=None):
     ap.add_argument("--sparsity", type=float, default=0.5)
     ap.add_argument("--reps", type=int, default=8)
     ap.add_argument("--out", default=None, help="also write the markdown summary here")
+    ap.add_argument("--attention", action="store_true", help="time the decode attention's phases instead")
     a = ap.parse_args(argv)
+    if a.attention:
+        return attention_main(a, argv)
     if not os.path.exists(LIB_TL):
         raise SystemExit(f"{LIB_TL} not built: python -m activation_sparse_gemv_amd.build --timeline")
     L.LIB_PATH = LIB_TL
@@ -176,6 +181,96 @@ def main(argv=None):
                   f"combine of the last workgroup per tile {np.median(ex['combine']) * TICK_US:.2f} us", ""]
         lines += table("gate/up phase", gu) + [""] + table("down phase", dn) + [""]
         print("\n".join(lines[-(len(gu) + len(dn) + 14):]), flush=True)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+
+ATT_PHASES = [
+    ("workgroup start (after the first)", lambda g, t0: g[:, 0] - t0),
+    ("scores computed (query and K rows arrived)", lambda g, t0: g[:, 1] - t0),
+    ("chunk maximum known (first barrier)", lambda g, t0: g[:, 2] - t0),
+    ("wave partial outputs in LDS (second barrier)", lambda g, t0: g[:, 3] - t0),
+    ("chunk record stored and complete", lambda g, t0: g[:, 4] - t0),
+    ("arrival counter returned", lambda g, t0: g[:, 5] - t0),
+]
+ATT_MERGE = [
+    ("merge weights ready (statistics loaded)", lambda g, t0: g[:, 6] - t0),
+    ("output stored", lambda g, t0: g[:, 7] - t0),
+]
+
+
+def attention_main(a, argv):
+    """Decode attention at n_ctx 2048, 32/8 heads, head_dim 128: per-workgroup phase
+    times from the first workgroup's entry, for calls on one cache (its 8.4 MB stay
+    in the last-level cache) and on 40 rotating caches (336 MB, from HBM)."""
+    if not os.path.exists(LIB_TL):
+        raise SystemExit(f"{LIB_TL} not built: python -m activation_sparse_gemv_amd.build --timeline")
+    L.LIB_PATH = LIB_TL
+    import torch
+    from . import api as asg
+    from . import datagen
+    lib = L.load()
+    lib.as_attention_timeline_arm.restype = ctypes.c_int
+    lib.as_attention_timeline_arm.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    dev = "cuda:0"
+    c3 = datagen.CFG3_ATTN
+    n_q, n_kv, hd, n_ctx = c3["n_q"], c3["n_kv"], c3["head_dim"], c3["n_ctx"]
+    caches = []
+    for i in range(40):
+        kc, vc = datagen.kv_cache(3, i, n_ctx=n_ctx, n_kv=n_kv, head_dim=hd)
+        caches.append((kc.to(dev), vc.to(dev)))
+    q = datagen.normal((n_q, hd), datagen.seed_for(3, 0, 91), std=1.0, dtype="f32").to(dev)
+    kn = datagen.normal((n_kv, hd), datagen.seed_for(3, 0, 92), std=1.0, dtype="f32").to(dev)
+    vn = datagen.normal((n_kv, hd), datagen.seed_for(3, 0, 93), std=1.0, dtype="f32").to(dev)
+    words = 16 * 4096
+    buf = torch.zeros(words, dtype=torch.int64, device=dev)
+    lines = ["# Phase timeline: decode attention, n_ctx 2048, 32 query / 8 kv heads, head_dim 128 (MI355X)", "",
+             "Command (from the repository root):", "", "```",
+             "python -m activation_sparse_gemv_amd.build --timeline",
+             "python -m activation_sparse_gemv_amd.timeline " + " ".join(argv if argv is not None else sys.argv[1:]),
+             "```", "",
+             "Times in us from the first workgroup's entry (100 MHz device clock stamped by thread 0 of every "
+             f"workgroup), pooled over {a.reps} single calls, each issued behind 8 calls on other caches. "
+             "The last two rows are the merging workgroup of each kv head only.", ""]
+    for name, rot in (("one cache (warm: last-level cache)", False), ("40 rotating caches (cold: HBM)", True)):
+        for i in range(8):
+            asg.as_gqa_decode_attention(q, kn, vn, *caches[i])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(64):
+            asg.as_gqa_decode_attention(q, kn, vn, *caches[(i % 40) if rot else 0])
+        e1.record()
+        torch.cuda.synchronize()
+        per_call = e0.elapsed_time(e1) * 1e3 / 64
+        chunk, merge = {k: [] for k, _ in ATT_PHASES}, {k: [] for k, _ in ATT_MERGE}
+        n_wg = 0
+        for rep in range(a.reps):
+            buf.zero_()
+            for i in range(8):
+                asg.as_gqa_decode_attention(q, kn, vn, *caches[(8 + rep * 3 + i) % 40 if rot else 0])
+            L.check(lib.as_attention_timeline_arm(ctypes.c_void_p(buf.data_ptr()), words),
+                    "as_attention_timeline_arm")
+            asg.as_gqa_decode_attention(q, kn, vn, *caches[(rep * 5) % 40 if rot else 0])
+            torch.cuda.synchronize()
+            g = buf.cpu().numpy().reshape(-1, 16)
+            g = g[g[:, 0] > 0].astype(np.float64)
+            n_wg = len(g)
+            t0 = g[:, 0].min()
+            for k, f in ATT_PHASES:
+                chunk[k].append(f(g, t0))
+            m = g[g[:, 7] > 0]
+            for k, f in ATT_MERGE:
+                merge[k].append(f(m, t0))
+        cat = lambda v: np.concatenate([np.asarray(x, dtype=np.float64) for x in v])
+        st = {k: _stats(cat(v)) for k, v in chunk.items()}
+        st.update({k: _stats(cat(v)) for k, v in merge.items()})
+        lines += [f"## {name}", "",
+                  f"- {n_wg} workgroups (8 kv heads x chunks of 64 cached keys); eager back-to-back calls "
+                  f"(events; host-bound, the binding's per-call work included): {per_call:.2f} us per call", ""]
+        lines += table("phase (us from the first entry)", st) + [""]
+        print("\n".join(lines[-(len(st) + 6):]), flush=True)
     if a.out:
         with open(a.out, "w") as f:
             f.write("\n".join(lines) + "\n")

@@ -1,4 +1,5 @@
-/* actsparse_timeline.h -- phase timeline of the sparse SwiGLU MLP.
+/* actsparse_timeline.h -- phase timelines of the sparse SwiGLU MLP and of the
+ * decode attention.
  *
  * Declared only for libactsparse_timeline.so, the opt-in build of libactsparse
  * made by `python -m activation_sparse_gemv_amd.build --timeline` (the kernels
@@ -40,6 +41,18 @@ extern "C" {
  * Returns AS_ERR_INVALID_ARG for a NULL buffer or words < 32.  The buffer is owned
  * by the caller and must stay valid until the armed call's launches complete. */
 as_status as_phase_timeline_arm(uint64_t* buf, size_t words);
+
+/* Arms a timeline buffer for the next as_gqa_decode_attention call (the decoder
+ * block's attention launch included) made on any thread of the process; that call
+ * disarms it.  Workgroup (kv head g, chunk c) of a grid of n_kv x C writes its 16
+ * words at buf[16 * (g + n_kv * c) ...]; a grid needing more than `words` words is
+ * not recorded.  Slots (10 ns ticks; 0: not reached): 0 entry; 1 scores computed
+ * (query and K rows arrived); 2 chunk maximum known (first barrier passed); 3 wave
+ * partial outputs in LDS (second barrier passed); 4 chunk record stored and
+ * complete; 5 arrival counter returned; for the last chunk of a kv head only:
+ * 6 merge weights ready (statistics loaded, third barrier passed); 7 output
+ * stored.  Errors and ownership as for as_phase_timeline_arm. */
+as_status as_attention_timeline_arm(uint64_t* buf, size_t words);
 
 #ifdef __cplusplus
 }

@@ -253,15 +253,18 @@ def test_phase_timeline_only_in_the_opt_in_build(lib):
     """The phase-timeline entry point (include/actsparse_timeline.h) exists only in
     libactsparse_timeline.so; the product library's kernels carry no timeline code.
     The opt-in build, when present, rejects a NULL or too-small buffer."""
-    assert not hasattr(lib, "as_phase_timeline_arm")
+    for name in ("as_phase_timeline_arm", "as_attention_timeline_arm"):
+        assert not hasattr(lib, name)
     tl_path = os.path.join(ROOT, "activation_sparse_gemv_amd", "libactsparse_timeline.so")
     if not os.path.exists(tl_path):
         pytest.skip("libactsparse_timeline.so not built (python -m activation_sparse_gemv_amd.build --timeline)")
     tl = ctypes.CDLL(tl_path)
-    tl.as_phase_timeline_arm.restype = ctypes.c_int
-    tl.as_phase_timeline_arm.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-    assert tl.as_phase_timeline_arm(None, 1024) == L.AS_ERR_INVALID_ARG
-    assert tl.as_phase_timeline_arm(ctypes.c_void_p(16), 8) == L.AS_ERR_INVALID_ARG
+    for name in ("as_phase_timeline_arm", "as_attention_timeline_arm"):
+        f = getattr(tl, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        assert f(None, 1024) == L.AS_ERR_INVALID_ARG
+        assert f(ctypes.c_void_p(16), 8) == L.AS_ERR_INVALID_ARG
 
 
 def test_greedy_sparsity_matches_the_oracle(lib):
