@@ -89,6 +89,33 @@ def summarize(runs):
             len(runs[0][1][runs[0][1][:, 0] > 0]))
 
 
+def breakdown(runs):
+    """Main-loop medians of each launch by XCD (workgroup index mod 8: the hardware
+    deals workgroups to the eight XCDs in turn) and by dispatch half (the first half
+    of a launch's workgroups take the CUs first; the second half share those CUs as
+    younger waves), and the launch's streaming rate: rows gathered x row bytes over
+    the span from the first main-loop start to the last main-loop end."""
+    out = []
+    for k, (name, row_bytes) in enumerate((("gate/up", 2 * 14336 * 2 // 56), ("down", 4096 * 2 // 32))):
+        mains, idx, rate = [], [], []
+        for r in runs:
+            g = r[k]
+            live = g[:, 0] > 0
+            g = g[live]
+            ids = np.nonzero(live)[0]
+            mains.append((g[:, 2] - g[:, 1]) * TICK_US)
+            idx.append(ids)
+            span = (g[:, 2].max() - g[:, 1].min()) * TICK_US
+            rate.append(g[:, 7].sum() * row_bytes / (span * 1e-6) / 1e12)
+        m, i = np.concatenate(mains), np.concatenate(idx)
+        n = int(i.max()) + 1
+        xcd = " / ".join(f"{np.median(m[i % 8 == x]):.2f}" for x in range(8))
+        half = f"{np.median(m[i < n // 2]):.2f} / {np.median(m[i >= n // 2]):.2f}"
+        out.append(f"- {name} main loop, median µs by XCD 0..7: {xcd}; by dispatch half (first / second): "
+                   f"{half}; rows x row bytes over the main-loop span: {np.median(rate):.2f} TB/s")
+    return out
+
+
 def table(title, stats):
     out = [f"| {title} | median us | p10 | p90 | max |", "|---|---|---|---|---|"]
     for k, (m, a, b, c) in stats.items():
@@ -168,6 +195,7 @@ def main(argv=None):
             tl = buf.cpu().numpy().reshape(2, words // 32, 16)
             runs.append((tl[0].copy(), tl[1].copy()))
         gu, dn, ex, n1, n2 = summarize(runs)
+        br = breakdown(runs)
         lines += [f"## {name}", "",
                   f"- layer time of this build: {np.median(per_layer):.2f} us (median of 5 x 48 back-to-back calls)",
                   f"- one call from the first gate/up workgroup to the last down workgroup: median "
@@ -179,8 +207,8 @@ def main(argv=None):
                   f"- down launch: {n2} workgroups, rows per workgroup median {np.median(ex['dn_rows']):.0f}; "
                   f"last main loop ends at {np.median(ex['dn_main_last']) * TICK_US:.2f} us; "
                   f"combine of the last workgroup per tile {np.median(ex['combine']) * TICK_US:.2f} us", ""]
-        lines += table("gate/up phase", gu) + [""] + table("down phase", dn) + [""]
-        print("\n".join(lines[-(len(gu) + len(dn) + 14):]), flush=True)
+        lines += table("gate/up phase", gu) + [""] + table("down phase", dn) + [""] + br + [""]
+        print("\n".join(lines[-(len(gu) + len(dn) + len(br) + 15):]), flush=True)
     if a.out:
         with open(a.out, "w") as f:
             f.write("\n".join(lines) + "\n")
