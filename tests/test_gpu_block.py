@@ -33,10 +33,13 @@ def test_rmsnorm():
 
 @pytest.mark.parametrize("n_ctx,n_q,n_kv,hd", [(2048, 32, 8, 128), (0, 4, 2, 128), (1, 8, 8, 128),
                                                (300, 16, 2, 128), (5000, 32, 8, 128), (70, 8, 1, 128),
-                                               (5000, 8, 1, 128), (2100, 16, 2, 128)])
+                                               (5000, 8, 1, 128), (2100, 16, 2, 128), (4096, 64, 8, 128),
+                                               (20000, 4, 4, 128), (9000, 32, 16, 128), (32767, 8, 8, 128)])
 def test_attention(n_ctx, n_q, n_kv, hd):
-    """Decode attention against the fp64 oracle; the shapes cover 1 to 64 key chunks per kv
-    head (64 with one kv head and 5001 keys; 33 with two and 2101) and groups of 1 to 8."""
+    """Decode attention against the fp64 oracle; the shapes cover 1 to 256 key chunks per kv
+    head, chunks of up to 64 and up to 128 cached keys (two and four row steps), groups of 1
+    to 8 query heads per kv head in both chunk sizes, the longest context (32767), and a
+    second call bit-identical to the first (the chunk merge runs in a fixed order)."""
     announce(f"attention n_ctx={n_ctx}")
     rng = np.random.default_rng(n_ctx + n_q)
     q = torch.from_numpy(rng.standard_normal((n_q, hd)).astype(np.float32))
@@ -46,6 +49,8 @@ def test_attention(n_ctx, n_q, n_kv, hd):
     o = asg.as_gqa_decode_attention(q.to(DEV), kn.to(DEV), vn.to(DEV), kc.to(DEV), vc.to(DEV))
     ref = block.gqa_decode_attention(f64(q), f64(kc), f64(vc), f64(kn), f64(vn)).reshape(n_q, hd)
     assert rel_err(o, ref) < 1e-4
+    o2 = asg.as_gqa_decode_attention(q.to(DEV), kn.to(DEV), vn.to(DEV), kc.to(DEV), vc.to(DEV))
+    assert torch.equal(o, o2)
     # q = 0: equal scores -> the mean of the group's values
     o0 = asg.as_gqa_decode_attention(torch.zeros_like(q).to(DEV), kn.to(DEV), vn.to(DEV), kc.to(DEV), vc.to(DEV))
     Vall = np.concatenate([f64(vc), f64(vn)[None]], 0)
