@@ -234,40 +234,43 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   }
 #pragma unroll
   for (int a = 0; a < GM; ++a) {
-    const float M = Mx[a];
+    // a row without a key has score -inf and weight 2^-inf = 0; a chunk maximum of
+    // -inf (no finite score) is taken as 0 so that -inf - M is not NaN
+    const float M = Mx[a] == -INFINITY ? 0.f : Mx[a];
     float l = 0.f;
 #pragma unroll
     for (int s = 0; s <= KS; ++s) {
-      const float e = sc[s][a] == -INFINITY ? 0.f : fast_exp2(sc[s][a] - M);
+      const float e = fast_exp2(sc[s][a] - M);
       sc[s][a] = e;
       l += e;
     }
     l_loc[a] = (readlane_f(l, 0) + readlane_f(l, 16)) + (readlane_f(l, 32) + readlane_f(l, 48));
   }
-  // unnormalised partial outputs of this slot's rows, 8 dimensions
+  // unnormalised partial outputs of this slot's rows, 8 dimensions.  Every step is
+  // summed without a branch: a slot past the chunk (weight 0) has its re-read row
+  // replaced by zeros, so it adds exactly 0 whatever that row holds; heads past the
+  // group have weight 0 and are never read out.
   float acc[GM][8];
 #pragma unroll
-  for (int a = 0; a < GM; ++a)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
-#pragma unroll
   for (int s = 0; s < KS; ++s) {
-    if (ks + kSlots * s < nk) {
-      float vv[8];
-      unpack8<DT_BF16>(vr[s], vv);
+    const bool valid = ks + kSlots * s < nk;
+    u32x4 v = vr[s];
+    v.x = valid ? v.x : 0u;
+    v.y = valid ? v.y : 0u;
+    v.z = valid ? v.z : 0u;
+    v.w = valid ? v.w : 0u;
+    float vv[8];
+    unpack8<DT_BF16>(v, vv);
 #pragma unroll
-      for (int a = 0; a < GM; ++a)
-        if (a < grp)
+    for (int a = 0; a < GM; ++a)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(sc[s][a], vv[e], acc[a][e]);
-    }
+      for (int e = 0; e < 8; ++e) acc[a][e] = s == 0 ? sc[0][a] * vv[e] : fmaf(sc[s][a], vv[e], acc[a][e]);
   }
   if (has_fresh && ks == 0) {
 #pragma unroll
     for (int a = 0; a < GM; ++a)
-      if (a < grp)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(sc[KS][a], vf[e], acc[a][e]);
+      for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(sc[KS][a], vf[e], acc[a][e]);
   }
   // The wave's four row slots are summed with cross-row lane swaps: four values
   // (A, B, E, F) become one register whose row r holds the slot sum of the value
@@ -362,11 +365,12 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
     if (lane + 64 * u < C) Mh = fmaxf(Mh, ml[u].x);
   Mh = wave_max(Mh);
   float lsum = 0.f;
+  if (Mh == -INFINITY) Mh = 0.f;           // no finite chunk maximum: weights 2^-inf = 0
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int cc = lane + 64 * u;
     if (cc < C) {
-      const float w = ml[u].x == -INFINITY ? 0.f : fast_exp2(ml[u].x - Mh);
+      const float w = fast_exp2(ml[u].x - Mh);
       if (live && run == 0) red[a * C + cc] = w;
       lsum = fmaf(w, ml[u].y, lsum);
     }
@@ -378,13 +382,15 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   float2 O = make_float2(0.f, 0.f);
   for (int c0 = cb; c0 < ce; c0 += kB) {
     if (c0 != cb) load_batch(c0);
+    // chunks past the run (re-read records) are selected away, not branched over
 #pragma unroll
-    for (int k = 0; k < kB; ++k)
-      if (c0 + k < ce) {
-        const float w = red[a * C + c0 + k];
-        O.x = fmaf(w, ob[k].x, O.x);
-        O.y = fmaf(w, ob[k].y, O.y);
-      }
+    for (int k = 0; k < kB; ++k) {
+      const bool in = c0 + k < ce;
+      const float w = red[a * C + min(c0 + k, C - 1)];
+      const float x = fmaf(w, ob[k].x, O.x), y = fmaf(w, ob[k].y, O.y);
+      O.x = in ? x : O.x;
+      O.y = in ? y : O.y;
+    }
   }
   // runs of one head added in run order (LDS past the weights)
   float2* s_run = reinterpret_cast<float2*>(red + ((GM * C + 1) & ~1));
