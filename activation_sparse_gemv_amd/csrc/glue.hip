@@ -172,34 +172,29 @@ __global__ __launch_bounds__(kAttThreads) void attention_kernel(const AttnParams
   // scores: sc[s][a] for the row of slot ks at step s; step KS is the current
   // token's key, held by slot 0 of the last chunk (-inf marks no row)
   float sc[KS + 1][GM];
+  // every head and step is computed (no branch per head: the heads' dot products and
+  // DPP sums are independent chains the compiler can interleave); heads past the
+  // group (zero queries) and slots past the chunk are masked to -inf by selects
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const bool valid = ks + kSlots * s < nk;
-    if (kSlots * s < nk) {                 // uniform over the workgroup
-      float kv[8];
-      unpack8<DT_BF16>(kr[s], kv);
+    float kv[8];
+    unpack8<DT_BF16>(kr[s], kv);
 #pragma unroll
-      for (int a = 0; a < GM; ++a) {
-        float v = -INFINITY;
-        if (a < grp) {
-          v = row16_sum(dot8(qv[a], kv));
-          v = valid ? v : -INFINITY;
-        }
-        sc[s][a] = v;
-      }
-    } else {
-#pragma unroll
-      for (int a = 0; a < GM; ++a) sc[s][a] = -INFINITY;
+    for (int a = 0; a < GM; ++a) {
+      const float v = row16_sum(dot8(qv[a], kv));
+      sc[s][a] = (valid && a < grp) ? v : -INFINITY;
     }
   }
+  if (has_fresh) {                         // uniform over the workgroup
 #pragma unroll
-  for (int a = 0; a < GM; ++a) {
-    float v = -INFINITY;
-    if (has_fresh && a < grp) {
-      v = row16_sum(dot8(qv[a], kf));
-      v = ks == 0 ? v : -INFINITY;
+    for (int a = 0; a < GM; ++a) {
+      const float v = row16_sum(dot8(qv[a], kf));
+      sc[KS][a] = (ks == 0 && a < grp) ? v : -INFINITY;
     }
-    sc[KS][a] = v;
+  } else {
+#pragma unroll
+    for (int a = 0; a < GM; ++a) sc[KS][a] = -INFINITY;
   }
   AS_ATT_PHASE(p, 1);
   // chunk maximum per head: the wave's maximum over its 4 row slots (every lane of
