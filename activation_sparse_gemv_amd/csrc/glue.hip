@@ -46,21 +46,21 @@ hipError_t launch_rmsnorm(const void* x, int x_dt, int rows, int d, float eps, f
 // last chunk as one extra row.  Workgroup (kv head g, chunk c): 32 row slots of 16
 // lanes (one 256-byte row per slot and step, 8 dimensions per lane; two waves per
 // SIMD, so the dependent score and value chains of one wave hide behind the
-// other's); the group's
-// query heads go straight from memory into registers, every K row and then every V
-// row of the chunk are issued at entry, so the chunk costs one round trip and the
-// scores overlap the V rows still in flight.  Scores: 8-dimension dot products
-// summed over the 16 lanes of a row by DPP, kept in registers; the chunk maximum
-// per head from the slot maxima (one barrier); exponentials (base 2: the query
-// scale carries log2(e), so every exponential is one hardware exp2) and the value
-// sums in registers; the partial outputs of the wave's four slots added by
-// cross-row lane swaps, then the eight waves' through LDS in wave order (second
-// barrier).  Slot maxima and sums are likewise combined within the wave first
-// (one entry per wave and head in LDS).  The chunk's (max, sum, output) record is stored
-// device-coherently and counted; the last chunk of a kv head to arrive merges
-// every record of the head in one round trip: the statistics give each chunk its
-// weight 2^(m_c - M) (M the largest chunk maximum), the weighted outputs are
-// added in chunk order and divided by sum_c 2^(m_c - M) l_c (deterministic).
+// other's).  The group's query heads go straight from memory into registers, then
+// every K row and every V row of the chunk are issued, so the chunk costs one round
+// trip and the scores overlap the V rows still in flight.  Scores: 8-dimension dot
+// products summed over the 16 lanes of a row by DPP, kept in registers; the chunk
+// maximum per head from per-wave maxima through LDS (first barrier); exponentials
+// (base 2: the query scale carries log2(e), so every exponential is one hardware
+// exp2) and the value sums in registers; the partial outputs of a wave's four slots
+// added by cross-row lane swaps, then the eight waves' through LDS in wave order
+// (second barrier).  These phases are bound by instructions and latency, so heads
+// past the group and slots past the chunk are masked by selects, never branched
+// over.  The chunk's (max, sum, output) record is stored device-coherently and
+// counted; the last chunk of a kv head to arrive merges every record of the head
+// in one round trip: the statistics give each chunk its weight 2^(m_c - M) (M the
+// largest chunk maximum), the weighted outputs are added in chunk order and divided
+// by sum_c 2^(m_c - M) l_c (deterministic).
 constexpr int kAttThreads = 512;
 constexpr int kSlots = kAttThreads / 16;   // row slots
 constexpr int kMaxGroup = 8;      // query heads per kv head
