@@ -931,10 +931,9 @@ def row_block(C, cpu):
         torch.cuda.synchronize()
         per[i] = [evs[k].elapsed_ms(evs[k + 1]) * 1e3 for k in range(nbk)]
     # decode attention alone (n_ctx 2048, 32/8 heads) over the 32 blocks' own caches
-    gq = torch.Generator(device="cpu").manual_seed(7)
-    qa = torch.randn((32, 128), generator=gq).to(C.dev)
-    kna = torch.randn((8, 128), generator=gq).to(C.dev)
-    vna = torch.randn((8, 128), generator=gq).to(C.dev)
+    qa = datagen.normal((32, 128), datagen.seed_for(3, 0, 91), std=1.0, dtype="f32").to(C.dev)
+    kna = datagen.normal((8, 128), datagen.seed_for(3, 0, 92), std=1.0, dtype="f32").to(C.dev)
+    vna = datagen.normal((8, 128), datagen.seed_for(3, 0, 93), std=1.0, dtype="f32").to(C.dev)
     us_att = C.graph_us([lambda kc=kc, vc=vc: asg.as_gqa_decode_attention(qa, kna, vna, kc, vc)
                          for (_, kc, vc) in blocks], reps=10)
     # active bytes of one token's step, from the masks the GPU applied
