@@ -11,6 +11,7 @@
 #include <string>
 
 #include "internal.hpp"
+#include "api_range.hpp"
 #ifdef AS_PHASE_TIMELINE
 #include "../../include/actsparse_timeline.h"
 #endif
@@ -312,6 +313,7 @@ size_t as_calibrate_threshold_ws_size(int64_t n) { return n < 1 ? 0 : up256(cali
 
 as_status as_calibrate_threshold(const void* pool, as_dtype dt, int64_t n, int64_t p_num, int64_t p_den,
                                  float* t_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   if (!pool || !t_out) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: NULL pointer");
   if (!is_dt(dt)) return fail(AS_ERR_INVALID_ARG, "as_calibrate_threshold: bad dtype %d", int(dt));
   if (n < 1 || n > 2147483647LL || p_den < 1 || p_num < 0 || p_num > p_den)
@@ -451,6 +453,7 @@ static as_status gemv_common(const void* X, as_dtype x_dt, int M, int K, const v
 as_status as_threshold_gemv(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N,
                             float t, void* Y, as_dtype y_dt, unsigned flags, as_mask_out* mask_out, void* ws,
                             size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
   return gemv_common(X, x_dt, M, K, W, w_dt, N, t, Y, y_dt, flags, mask_out, ws, ws_bytes, stream, dense,
                      "as_threshold_gemv");
@@ -459,6 +462,7 @@ as_status as_threshold_gemv(const void* X, as_dtype x_dt, int M, int K, const vo
 as_status as_threshold_gemv_i8(const void* X, as_dtype x_dt, int K, const int8_t* W, const float* row_scale,
                                int N, float t, void* Y, as_dtype y_dt, unsigned flags, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
+  AS_API_RANGE();
   const bool dense = (flags & AS_FLAG_FORCE_DENSE) != 0;
   return gemv_common(X, x_dt, 1, K, W, AS_I8, N, dense ? -INFINITY : t, Y, y_dt, flags, nullptr, ws, ws_bytes,
                      stream, dense, "as_threshold_gemv_i8", nullptr, row_scale);
@@ -466,6 +470,7 @@ as_status as_threshold_gemv_i8(const void* X, as_dtype x_dt, int K, const int8_t
 
 as_status as_dense_gemv(const void* X, as_dtype x_dt, int M, int K, const void* W, as_dtype w_dt, int N, void* Y,
                         as_dtype y_dt, unsigned flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   return gemv_common(X, x_dt, M, K, W, w_dt, N, -INFINITY, Y, y_dt, flags, nullptr, ws, ws_bytes, stream, true,
                      "as_dense_gemv");
 }
@@ -536,6 +541,7 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
                                float t_x, float t_h, const int32_t* neuron_idx, int n_active, void* Y,
                                as_dtype y_dt, unsigned flags, as_mlp_debug* dbg, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_sparse_swiglu_mlp";
   if (flags & AS_FLAG_AUTO) {
     if (mode != AS_MLP_THRESHOLD) return fail(AS_ERR_UNSUPPORTED, "%s: AS_FLAG_AUTO is for THRESHOLD mode", fn);
@@ -572,6 +578,7 @@ as_status as_sparse_swiglu_mlp(const void* X, as_dtype x_dt, int M, const as_mlp
 
 as_status as_pack_neuron_set(const as_mlp_weights* w, const int32_t* idx, int k, void* gate_up_out,
                              void* down_out, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_pack_neuron_set";
   as_status st = check_mlp_weights(w, AS_MLP_THRESHOLD, fn);
   if (st != AS_OK) return st;
@@ -777,6 +784,7 @@ static as_status mlp_impl(const void* X, as_dtype x_dt, int M, const as_mlp_weig
 
 // ------------------------------------------------------------------ attribution selection
 as_status as_corrected_gxo(const float* x, const float* grad, int rows, int n, float* score, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_corrected_gxo";
   if (!x || !grad || !score) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (rows < 1 || n < 1) return fail(AS_ERR_INVALID_ARG, "%s: rows=%d n=%d", fn, rows, n);
@@ -791,6 +799,7 @@ int as_top_fraction_count(int n, int ar_num, int ar_den) {
 
 as_status as_select_top_fraction(const float* score, int rows, int n, int ar_num, int ar_den, uint64_t* mask,
                                  int32_t* idx, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_select_top_fraction";
   if (!score) return fail(AS_ERR_INVALID_ARG, "%s: score is NULL", fn);
   if (!mask && !idx) return fail(AS_ERR_INVALID_ARG, "%s: both outputs are NULL", fn);
@@ -808,6 +817,7 @@ size_t as_head_masked_gemv_ws_size(int n_heads, int head_dim, int N) {
 as_status as_head_masked_gemv(const void* X, as_dtype x_dt, int n_heads, int head_dim, const int32_t* heads,
                               int n_keep, const void* W, as_dtype w_dt, int N, void* Y, as_dtype y_dt,
                               unsigned flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_head_masked_gemv";
   if (!X || !W || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL X, W or Y", fn);
   if (n_heads < 1 || n_heads > 1024 || head_dim < 1) return fail(AS_ERR_INVALID_ARG, "%s: n_heads=%d head_dim=%d", fn, n_heads, head_dim);
@@ -827,6 +837,7 @@ as_status as_head_masked_gemv(const void* X, as_dtype x_dt, int n_heads, int hea
 // ------------------------------------------------------------------ greedy allocation
 as_status as_greedy_sparsity(const double* err, int n_blocks, int n_levels, const double* weights, double step,
                              double target, int32_t* levels) {
+  AS_API_RANGE();
   const char* fn = "as_greedy_sparsity";
   if (!err || !weights || !levels) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (n_blocks < 1 || n_levels < 1) return fail(AS_ERR_INVALID_ARG, "%s: n_blocks=%d n_levels=%d", fn, n_blocks, n_levels);
@@ -867,6 +878,7 @@ size_t as_topk_mask_ws_size(int rows, int n, as_topk_mode mode) {
 
 as_status as_topk_mask(const float* score, const float* prior, int rows, int n, int k, as_topk_mode mode,
                        float lambda, uint64_t* mask, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_topk_mask";
   if (!score) return fail(AS_ERR_INVALID_ARG, "%s: score is NULL", fn);
   if (!mask && !idx) return fail(AS_ERR_INVALID_ARG, "%s: both outputs are NULL", fn);
@@ -887,6 +899,7 @@ as_status as_topk_mask(const float* score, const float* prior, int rows, int n, 
 // ------------------------------------------------------------------ MoE
 as_status as_moe_router(const float* logits, int T, int E, int top_k, int32_t* ids, float* weights,
                         hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_moe_router";
   if (!logits || !ids || !weights) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (T < 1 || E < 1 || E > 1024) return fail(AS_ERR_INVALID_ARG, "%s: T=%d E=%d", fn, T, E);
@@ -916,6 +929,7 @@ size_t as_moe_router_gemv_ws_size(int T, int d_model, int E) {
 as_status as_moe_router_gemv(const void* X, as_dtype x_dt, int T, const void* w_router, as_dtype w_dt, int d_model,
                              int E, int top_k, float* logits, int32_t* ids, float* weights, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_moe_router_gemv";
   if (!X || !w_router || !logits || !ids || !weights) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!is_dt(x_dt) || !is_wdt(w_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
@@ -1051,6 +1065,7 @@ as_status as_sparse_moe_expert(const void* X, as_dtype x_dt, int T, const int32_
                                const float* expert_w, int top_k, const as_moe_weights* w, int keep_k, void* Y,
                                as_dtype y_dt, unsigned flags, float* h_dbg, int32_t* keep_dbg,
                                hipEvent_t y_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const MoeKeepRule rule{false, 0.f, nullptr};
   return moe_expert_impl("as_sparse_moe_expert", X, x_dt, T, expert_ids, expert_w, top_k, w, keep_k, rule, Y, y_dt,
                          flags, h_dbg, keep_dbg, y_ready, ws, ws_bytes, stream);
@@ -1060,6 +1075,7 @@ as_status as_sparse_moe_expert_gate(const void* X, as_dtype x_dt, int T, const i
                                     const float* expert_w, int top_k, const as_moe_weights* w, float t_gate,
                                     void* Y, as_dtype y_dt, unsigned flags, float* h_dbg, float* a_dbg,
                                     hipEvent_t y_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   if (std::isnan(t_gate)) return fail(AS_ERR_INVALID_ARG, "as_sparse_moe_expert_gate: t_gate is NaN");
   const MoeKeepRule rule{true, t_gate, a_dbg};
   return moe_expert_impl("as_sparse_moe_expert_gate", X, x_dt, T, expert_ids, expert_w, top_k, w, 0, rule, Y, y_dt,
@@ -1240,6 +1256,7 @@ as_status moe_layer_impl(const char* fn, const void* X, as_dtype x_dt, int T, co
 as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_weights* w, int top_k, int keep_k,
                        float* Y, unsigned flags, float* logits, int32_t* ids, float* weights, float* h_dbg,
                        int32_t* keep_dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const MoeKeepRule rule{false, 0.f, nullptr};
   return moe_layer_impl("as_moe_layer", X, x_dt, T, w, top_k, keep_k, rule, Y, flags, logits, ids, weights, h_dbg,
                         keep_dbg, ws, ws_bytes, stream);
@@ -1248,6 +1265,7 @@ as_status as_moe_layer(const void* X, as_dtype x_dt, int T, const as_moe_layer_w
 as_status as_moe_layer_gate(const void* X, as_dtype x_dt, int T, const as_moe_layer_weights* w, int top_k,
                             float t_gate, float* Y, unsigned flags, float* logits, int32_t* ids, float* weights,
                             float* h_dbg, float* a_dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   if (std::isnan(t_gate)) return fail(AS_ERR_INVALID_ARG, "as_moe_layer_gate: t_gate is NaN");
   const MoeKeepRule rule{true, t_gate, a_dbg};
   return moe_layer_impl("as_moe_layer_gate", X, x_dt, T, w, top_k, 0, rule, Y, flags, logits, ids, weights, h_dbg,
@@ -1257,6 +1275,7 @@ as_status as_moe_layer_gate(const void* X, as_dtype x_dt, int T, const as_moe_la
 // ------------------------------------------------------------------ block glue
 as_status as_rmsnorm(const void* X, as_dtype x_dt, int rows, int d, float eps, float* Y, float* copy,
                      hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_rmsnorm";
   if (!X || !Y) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!is_dt(x_dt)) return fail(AS_ERR_INVALID_ARG, "%s: bad dtype", fn);
@@ -1304,6 +1323,7 @@ size_t as_gqa_decode_attention_ws_size(int n_ctx, int n_q, int n_kv, int head_di
 as_status as_gqa_decode_attention(const float* q, const float* k_new, const float* v_new, const void* k_cache,
                                   const void* v_cache, as_dtype kv_dt, int n_ctx, int n_q, int n_kv, int head_dim,
                                   float* o, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_gqa_decode_attention";
   if (!q || !k_new || !v_new || !o) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (n_ctx > 0 && (!k_cache || !v_cache)) return fail(AS_ERR_INVALID_ARG, "%s: NULL cache", fn);
@@ -1373,6 +1393,7 @@ size_t as_decoder_block_ws_size(const as_block_weights* w, int n_ctx) {
 as_status as_decoder_block(const void* X, as_dtype x_dt, const as_block_weights* w, const void* k_cache,
                            const void* v_cache, int n_ctx, const as_block_thresholds* t, float* Y, unsigned flags,
                            as_block_debug* dbg, void* ws, size_t ws_bytes, hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_decoder_block";
   if (!X || !w || !t || !Y || !w->w_qkv || !w->w_o) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   as_status st = check_mlp_weights(&w->mlp, AS_MLP_THRESHOLD, fn);
@@ -1447,6 +1468,7 @@ as_status as_decoder_block(const void* X, as_dtype x_dt, const as_block_weights*
 // ------------------------------------------------------------------ GLASS local signal
 as_status as_glass_local_signal(const void* X, as_dtype x_dt, int P, const as_mlp_weights* w, float* local,
                                 hipStream_t stream) {
+  AS_API_RANGE();
   const char* fn = "as_glass_local_signal";
   if (!X || !w || !w->w_gate_up || !local) return fail(AS_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (P < 1 || w->d_model < 32 || w->d_ff < 16) return fail(AS_ERR_INVALID_ARG, "%s: P=%d d=%d d_ff=%d", fn, P, w->d_model, w->d_ff);

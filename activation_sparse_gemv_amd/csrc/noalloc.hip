@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "internal.hpp"
+#include "api_range.hpp"
 
 namespace {
 
@@ -39,6 +40,7 @@ extern "C" as_status as_sparse_swiglu_mlp_noalloc(const void* X, as_dtype x_dt, 
                                                   as_mlp_mode mode, float t_x, float t_h, const int32_t* neuron_idx,
                                                   int n_active, void* Y, as_dtype y_dt, unsigned flags,
                                                   as_mlp_debug* dbg, hipStream_t stream) {
+  AS_API_RANGE();
   char msg[256];
   if (!w || M < 1) return as::report_error(AS_ERR_INVALID_ARG, "as_sparse_swiglu_mlp_noalloc: NULL weights or M < 1");
   const size_t need = as_sparse_swiglu_mlp_ws_size(M, w, mode);

@@ -49,7 +49,7 @@ def build_sanitized() -> str:
                         if os.path.basename(o) != "api.cpp.o"]
     tmp = LIB + ".tmp"
     link_cmd = [CLANG, "-shared", "-fPIC", *SAN, "-shared-libasan", "-o", tmp, *objs,
-                "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+                "-L/opt/rocm/lib", "-lamdhip64", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(link_cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"sanitized link failed:\n{r.stdout}\n{r.stderr}")
