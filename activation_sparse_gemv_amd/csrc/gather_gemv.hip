@@ -61,6 +61,30 @@ int pick_chunk_vectors(const void* x, int x_dt, int len, long ldx) {
 }
 
 
+// y[m][c] = sum over slices s = 0, 1, ... of partials[s][m][c], in that order from
+// 0, then + y (accumulate), then + res: the additions of the in-kernel last-workgroup
+// combine, so results are bitwise the same.  One thread per output element, the
+// slices' loads issued in batches of eight.
+__global__ __launch_bounds__(kThreadsHost) void sum_slices_kernel(const GemvParams p) {
+  const long i = (long)blockIdx.x * kThreadsHost + threadIdx.x;
+  if (i >= (long)p.M * p.N) return;
+  const int m = (int)(i / p.N), c = (int)(i % p.N);
+  const float* src = p.partials + (long)m * p.part_ld + c;
+  const long stride = (long)p.M * p.part_ld;
+  float v = 0.f;
+  for (int s0 = 0; s0 < p.S; s0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[k] = src[(long)min(s0 + k, p.S - 1) * stride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < p.S) v += t[k];
+  }
+  if (p.accumulate) v += load_elem(p.y, p.y_dt, m * p.ldy + c);
+  if (p.res != nullptr) v += load_elem(p.res, p.res_dt, m * p.ldres + c);
+  store_elem(p.y, p.y_dt, m * p.ldy + c, v);
+}
+
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s) {
   const size_t smem = gemv_smem_bytes(c, p.cap, p.n_lt);
   GemvConfig cc = c;
@@ -81,7 +105,24 @@ hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStrea
     case 2: return bf ? launch_gemv_bf16_m2(cc, p, smem, s) : launch_gemv_f16_m2(cc, p, smem, s);
     case 4: return bf ? launch_gemv_bf16_m4(cc, p, smem, s) : launch_gemv_f16_m4(cc, p, smem, s);
     case 8: return bf ? launch_gemv_bf16_m8(cc, p, smem, s) : launch_gemv_f16_m8(cc, p, smem, s);
-    case 16: return bf ? launch_gemv_bf16_m16(cc, p, smem, s) : hipErrorInvalidValue;
+    case 16: {
+      if (!bf) return hipErrorInvalidValue;
+      // 9..16 tokens, split rows, deterministic sum: a 16-token tile of every slice
+      // is 16x larger than one token's, and one workgroup per tile loading all of
+      // them sets the launch's tail; the slices are summed by a launch of its own
+      // that spreads the loads over the chip
+      if (cc.out == OUT_Y && p.S > 1 && !p.atomic_y) {
+        GemvParams q = p;
+        q.defer_sum = 1;
+        hipError_t e = launch_gemv_bf16_m16(cc, q, smem, s);
+        if (e != hipSuccess) return e;
+        const long n = (long)p.M * p.N;
+        hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n + kThreadsHost - 1) / kThreadsHost)),
+                           dim3(kThreadsHost), 0, s, p);
+        return hipGetLastError();
+      }
+      return launch_gemv_bf16_m16(cc, p, smem, s);
+    }
     default: return hipErrorInvalidValue;
   }
 }

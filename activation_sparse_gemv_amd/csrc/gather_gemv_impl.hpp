@@ -1190,6 +1190,22 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       }
       return;
     }
+    if (n_parts > 1 && p.defer_sum) {
+      // the next launch sums the slices in slice order (its kernel boundary makes
+      // these stores visible): no counter, and no one workgroup loading every
+      // slice's tile
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int c = tid + q * kThreads;
+        bool ok;
+        const long pc = col_of(c, ok);
+        if (c < TN && ok)
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            if (m < M) p.partials[((long)part * M + m) * p.part_ld + pc] = res[m][q];
+      }
+      return;
+    }
   }
   if (n_parts > 1) {
     // Partials are written through to the device-coherent level (relaxed agent-scope
