@@ -85,6 +85,51 @@ __global__ __launch_bounds__(kThreadsHost) void sum_slices_kernel(const GemvPara
   store_elem(p.y, p.y_dt, m * p.ldy + c, v);
 }
 
+// The SwiGLU epilogue of a gate/up launch whose slices stored their partials: for
+// token m = blockIdx.y and neuron n, g and u are the slice-order sums of the gate
+// (column n) and up (column N + n) partials, h = silu(g) * u, and the |h| > t_h
+// mask bits and counts are exported when asked for; the y the next launch adds into
+// is cleared.  The same operations in the same order as the in-kernel epilogue.
+__global__ __launch_bounds__(kThreadsHost) void sum_swiglu_kernel(const GemvParams p) {
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * kThreadsHost + threadIdx.x;
+  const bool valid = n < p.N;
+  if (p.zero_y != nullptr) {
+    const long nth = (long)gridDim.x * gridDim.y * kThreadsHost;
+    for (long i = ((long)blockIdx.y * gridDim.x + blockIdx.x) * kThreadsHost + threadIdx.x; i < p.zero_n; i += nth)
+      p.zero_y[i] = 0.f;
+  }
+  const int nc = valid ? n : 0;
+  const float* src = p.partials + (long)m * p.part_ld;
+  const long stride = (long)p.M * p.part_ld;
+  float g = 0.f, u = 0.f;
+  for (int s0 = 0; s0 < p.S; s0 += 8) {
+    float tg[8], tu[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float* ps = src + (long)min(s0 + k, p.S - 1) * stride;
+      tg[k] = ps[nc];
+      tu[k] = ps[(long)p.N + nc];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < p.S) {
+        g += tg[k];
+        u += tu[k];
+      }
+  }
+  const float hv = valid ? silu_f32(g) * u : 0.f;
+  if (valid) p.h[(long)m * p.ldh + n] = hv;
+  if (p.h_bits != nullptr || p.h_nnz != nullptr) {
+    const uint64_t bits = __ballot(valid && fabsf(hv) > p.t_h);
+    if ((threadIdx.x & 63) == 0 && valid) {
+      if (p.h_bits != nullptr) p.h_bits[(long)m * p.h_bits_ld + n / 64] = bits;
+      // the mask's count: integer adds, exact in any order (cleared by the host)
+      if (p.h_nnz != nullptr && bits) atomicAdd(p.h_nnz + m, (int)__popcll(bits));
+    }
+  }
+}
+
 hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStream_t s) {
   const size_t smem = gemv_smem_bytes(c, p.cap, p.n_lt);
   GemvConfig cc = c;
@@ -118,6 +163,17 @@ hipError_t launch_gather_gemv(const GemvConfig& c, const GemvParams& p, hipStrea
         if (e != hipSuccess) return e;
         const long n = (long)p.M * p.N;
         hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n + kThreadsHost - 1) / kThreadsHost)),
+                           dim3(kThreadsHost), 0, s, p);
+        return hipGetLastError();
+      }
+      // the gate/up stage likewise, unless it writes per-tile row lists
+      if (cc.out == OUT_SWIGLU && p.S > 1 && p.o_cnt == nullptr) {
+        GemvParams q = p;
+        q.defer_sum = 1;
+        q.zero_y = nullptr;
+        hipError_t e = launch_gemv_bf16_m16(cc, q, smem, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(sum_swiglu_kernel, dim3((unsigned)((p.N + kThreadsHost - 1) / kThreadsHost), (unsigned)p.M),
                            dim3(kThreadsHost), 0, s, p);
         return hipGetLastError();
       }

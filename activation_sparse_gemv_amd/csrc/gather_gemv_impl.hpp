@@ -1190,6 +1190,8 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int sl,
       }
       return;
     }
+  }
+  if constexpr (OUT == OUT_Y || OUT == OUT_SWIGLU) {
     if (n_parts > 1 && p.defer_sum) {
       // the next launch sums the slices in slice order (its kernel boundary makes
       // these stores visible): no counter, and no one workgroup loading every

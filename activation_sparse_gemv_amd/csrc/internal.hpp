@@ -46,8 +46,9 @@ struct GemvParams {
   // OUT_Y with split rows: each slice adds its partial tile into y (fp32) with
   // atomic adds (slice 0 also adds res) instead of the last-workgroup combine
   int atomic_y;
-  // OUT_Y with split rows: the slices store their partial tiles and end; the next
-  // launch on the stream (sum_slices_kernel) sums them in slice order
+  // OUT_Y / OUT_SWIGLU with split rows: the slices store their partial tiles and
+  // end; the next launch on the stream (sum_slices_kernel, sum_swiglu_kernel) sums
+  // them in slice order
   int defer_sum;
   // OUT_PARTS / OUT_SWIGLU: when set, one workgroup (column tile 0) clears zero_n
   // floats at zero_y (the y that the next launch adds into)
