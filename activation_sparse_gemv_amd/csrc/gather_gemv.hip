@@ -32,7 +32,7 @@ size_t gemv_smem_bytes(const GemvConfig& c, int cap, int n_lt) {
   if ((c.in == IN_RANGE && c.mt > 1) || c.in == IN_PARTS) stage = size_t(cap) * c.mt * 4;
   if (c.mt == 16) {
     const size_t rows = size_t(32) * (512 / tn);
-    const size_t chunk = rows * (tn + 4) * 2, out = size_t(16) * tn * 4;
+    const size_t chunk = size_t(tn) * (rows + 8) * 2, out = size_t(16) * tn * 4;
     const size_t m = chunk > out ? chunk : out;
     if (m > stage) stage = m;
   }

@@ -174,12 +174,15 @@ __device__ __forceinline__ void copy2_to_lds(T* d1, const T* s1, int n1, U* d2, 
 // Batches of 9..16 tokens: the per-row FMA count outgrows the VALU, so the
 // contraction runs on the matrix cores (v_mfma_f32_16x16x32_bf16).  MFMA wants
 // the reduction (row) index contiguous per lane, while input-major rows are
-// contiguous along the output columns, so each chunk of CR rows (32 KB of bf16
-// weights whatever the tile width) is staged through LDS (rows padded by 4
-// elements, which spreads the four lane groups of a transposed read over
-// distinct banks) and read back column-wise.  Two chunks are in flight per
-// workgroup: the loads of chunk c + 2 are issued as soon as chunk c has been
-// written to LDS, into the register buffer chunk c came from.
+// contiguous along the output columns.  Each chunk of CR rows (32 KB of bf16
+// weights whatever the tile width) is therefore split into 8x8 blocks, one per
+// thread: the thread loads 8 rows of 8 consecutive columns (16 bytes each),
+// transposes the block in registers and writes each column's 8 rows as one
+// 16-byte vector into a K-major LDS chunk (column pitch CR + 8 elements, so the
+// 16 columns of a fragment read fall on distinct banks); a B fragment is then a
+// single 16-byte LDS read.  Two chunks are in flight per workgroup: the loads of
+// chunk c + 2 are issued as soon as chunk c has been written to LDS, into the
+// register buffer chunk c came from.
 // Activations are fp32 in LDS; each is split into bf16 hi + bf16 lo (x - hi),
 // two MFMAs per fragment, which keeps fp32 inputs (h, normalised x) to ~2^-16
 // relative precision while bf16 inputs stay exact.
@@ -189,10 +192,11 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <int TN>
 struct MfmaShape {
   static constexpr int CR = 32 * (512 / TN);          // rows per staged chunk
-  static constexpr int LDW = TN + 4;                   // LDS row pitch (elements)
+  static constexpr int LDK = CR + 8;                   // K-major LDS column pitch (elements)
   static constexpr int KS = CR / 32;                   // MFMA k-steps per chunk
-  static constexpr int VPT = CR * TN / 8 / kThreads;   // 16-byte vectors per thread per chunk
-  static constexpr size_t kBytes = size_t(CR) * LDW * 2;
+  static constexpr int NRG = CR / 8;                   // 8-row groups per chunk
+  static constexpr int VPT = 8;                        // one 8x8 block (8 row vectors) per thread
+  static constexpr size_t kBytes = size_t(TN) * LDK * 2;
 };
 
 template <int LPR, bool GU, bool NT>
@@ -200,53 +204,60 @@ __device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s
                                int cnt, int tile, float* s_out /* [16][TN], aliases s_w */) {
   constexpr int TN = LPR * 8, TB = TN / 2;
   using MS = MfmaShape<TN>;
-  constexpr int CR = MS::CR, LDW = MS::LDW, KS = MS::KS, VPT = MS::VPT, VPR = TN / 8;
+  constexpr int CR = MS::CR, LDK = MS::LDK, KS = MS::KS, VPT = MS::VPT, NRG = MS::NRG;
   constexpr int NB = TN / 16;              // 16-column blocks in the tile
   constexpr int NBW = NB / 4;              // blocks per wave
-  static_assert(VPT * kThreads * 8 == CR * TN, "chunk must split evenly over the threads");
+  static_assert(NRG * (TN / 8) == kThreads, "one 8x8 block per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, li = lane & 15;
   f32x4_t acc[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // global source of each of this thread's vectors: chunk row and tile column (multiple of 8)
-  int vrow[VPT], vcol[VPT];
-  long vsrc[VPT];
-#pragma unroll
-  for (int q = 0; q < VPT; ++q) {
-    const int v = tid + q * kThreads;
-    vrow[q] = v / VPR;
-    vcol[q] = (v % VPR) * 8;
+  // this thread's block: chunk rows 8 * rg .. 8 * rg + 7, tile columns vcol .. vcol + 7
+  // (consecutive threads take consecutive row groups, so a wave's LDS writes spread
+  // over the banks; each of its loads covers NRG rows)
+  const int rg = tid % NRG, vcol = (tid / NRG) * 8;
+  long vsrc;
+  {
     long gc;
     bool ok;
     if constexpr (GU) {
-      const int n = tile * TB + (vcol[q] % TB);
+      const int n = tile * TB + (vcol % TB);
       ok = n < p.N;
-      gc = vcol[q] < TB ? (long)n : p.gu_off + n;
+      gc = vcol < TB ? (long)n : p.gu_off + n;
     } else {
-      const int n = tile * TN + vcol[q];
+      const int n = tile * TN + vcol;
       ok = n < p.N;
       gc = n;
     }
-    vsrc[q] = ok ? gc : 0;
+    vsrc = ok ? gc : 0;
   }
   const int nch = (cnt + CR - 1) / CR;
   // rows past the end of the list repeat its last row (their activations are 0)
   auto fetch = [&](int ch, u32x4 (&buf)[VPT]) {
 #pragma unroll
     for (int q = 0; q < VPT; ++q) {
-      const int row = s_idx[min(ch * CR + vrow[q], cnt - 1)];
-      buf[q] = load_w16<NT>(p.W + (long)row * p.ldw + vsrc[q]);
+      const int row = s_idx[min(ch * CR + rg * 8 + q, cnt - 1)];
+      buf[q] = load_w16<NT>(p.W + (long)row * p.ldw + vsrc);
     }
   };
   // refill: issue the loads of chunk ch + 2 into buf once chunk ch is in LDS
   auto step = [&](int ch, u32x4 (&buf)[VPT], bool refill) {
     __syncthreads();                       // every wave is done reading the previous chunk
+    // transpose the 8x8 block while writing it: word m of row q holds columns 2m
+    // (low half) and 2m + 1 (high half); word n of column c's vector holds rows
+    // 2n (low half) and 2n + 1 (high half)
 #pragma unroll
-    for (int q = 0; q < VPT; ++q) {
-      uint64_t* dst = reinterpret_cast<uint64_t*>(s_w + vrow[q] * LDW + vcol[q]);
-      dst[0] = (uint64_t)buf[q].x | ((uint64_t)buf[q].y << 32);
-      dst[1] = (uint64_t)buf[q].z | ((uint64_t)buf[q].w << 32);
+    for (int m = 0; m < 4; ++m) {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const unsigned a = buf[2 * n][m], b = buf[2 * n + 1][m];
+        lo[n] = (a & 0xffffu) | (b << 16);
+        hi[n] = (a >> 16) | (b & 0xffff0000u);
+      }
+      *reinterpret_cast<u32x4*>(s_w + (vcol + 2 * m) * LDK + rg * 8) = lo;
+      *reinterpret_cast<u32x4*>(s_w + (vcol + 2 * m + 1) * LDK + rg * 8) = hi;
     }
     __syncthreads();
     if (refill) fetch(ch + 2, buf);
@@ -268,10 +279,9 @@ __device__ __forceinline__ void mfma_main_loop(const GemvParams& p, const int* s
       }
 #pragma unroll
       for (int b = 0; b < NBW; ++b) {
+        // B fragment: column col, rows 8g .. 8g+7 of this k-step, one 16-byte read
         const int col = (wave * NBW + b) * 16 + li;
-        bf16x8_t bw;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bw[e] = __builtin_bit_cast(__bf16, s_w[(ks * 32 + 8 * g + e) * LDW + col]);
+        const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(s_w + col * LDK + ks * 32 + 8 * g);
         acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bw, acc[b], 0, 0, 0);
         acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bw, acc[b], 0, 0, 0);
       }
